@@ -1,0 +1,438 @@
+"""Pins of the CPU oracle against what the mathematics fixes (no GPU).
+
+Each test checks the oracle against something other than itself: closed forms derived in exact
+arithmetic (tests/golden/closed_forms.json), library routines on special cases (numpy's eigh,
+float16 conversion, Chebyshev interpolation), brute force on 4x4 blocks, defining invariants and
+limits of each iteration, and exact integer arithmetic.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import dash_inputs as di
+import oracle
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))
+
+
+def rel(a, b):
+    return np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(np.asarray(b))
+
+
+def spd(seed, n, lam_min, lam_max):
+    A, Q, lam = di.known_spectrum_stack(seed, 1, n, lam_min, lam_max)
+    return A[0], Q[0], lam[0]
+
+
+# ----------------------------------------------------------------------------------------------
+# elementary routines
+# ----------------------------------------------------------------------------------------------
+
+def test_matmul_matches_library_product():
+    g = di.rng(11)
+    X, Y = g.standard_normal((7, 7)), g.standard_normal((7, 7))
+    assert rel(oracle.matmul(X, Y), X @ Y) < 1e-14
+    # non-commuting operands: a swapped operand order would fail
+    assert rel(oracle.matmul(X, Y), Y @ X) > 1e-3
+
+
+def test_round_binary16_matches_numpy():
+    g = di.rng(12)
+    vals = list(g.standard_normal(2000) * np.exp(g.uniform(-20, 12, 2000)))
+    ulp1 = 2.0 ** -10
+    vals += [0.0, -0.0, 1.0, 1 + ulp1 / 2, 1 + 3 * ulp1 / 2, 2049.0, 2051.0, 65504.0, 65519.99, 65520.0, 7e4,
+             2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 * (1 - 2.0 ** -11), 6.1e-5, -5.96e-8, 1e-9]
+    x = np.array(vals)
+    got = oracle.round_binary16(x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, want)
+    assert math.isnan(oracle.round_binary16(np.array([np.nan]))[0])
+
+
+# ----------------------------------------------------------------------------------------------
+# c1: exact root by Jacobi eigendecomposition
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fx", GOLDEN["inverse_roots"], ids=lambda f: f["name"])
+def test_power_evd_closed_forms(fx):
+    A = np.array(fx["A"])
+    assert rel(oracle.inverse_root_evd(A), fx["inv_fourth_root"]) < 1e-13
+    assert rel(oracle.power_evd(A, 0.5), fx["sqrt"]) < 1e-13
+
+
+def test_jacobi_diagonal_is_exact():
+    d = np.array([3.0, -1.0, 7.5, 0.25, 2.0])
+    w, Q, sweeps = oracle.jacobi_eigh(np.diag(d))
+    assert sweeps == 0
+    assert np.array_equal(w, d) and np.array_equal(Q, np.eye(5))
+
+
+def test_jacobi_known_spectrum_and_invariants():
+    A, Q, lam = spd(21, 40, 1e-3, 2.0)
+    w, V, sweeps = oracle.jacobi_eigh(A)
+    assert 0 < sweeps < 20
+    assert np.max(np.abs(np.sort(w) - np.sort(lam))) < 1e-13 * np.linalg.norm(A)
+    assert np.max(np.abs(V.T @ V - np.eye(40))) < 1e-13
+    assert np.max(np.abs(A @ V - V * w[None, :])) < 1e-12
+
+
+def test_jacobi_matches_numpy_eigh():
+    g = di.rng(22)
+    M = g.standard_normal((48, 48))
+    A = M + M.T
+    w, _, _ = oracle.jacobi_eigh(A)
+    assert np.max(np.abs(np.sort(w) - np.linalg.eigvalsh(A))) < 1e-12 * np.abs(A).max() * 48
+
+
+def _det_leibniz(M):
+    n = len(M)
+    tot = 0.0
+    for perm in itertools.permutations(range(n)):
+        sign = 1
+        for i in range(n):
+            for j in range(i + 1, n):
+                if perm[i] > perm[j]:
+                    sign = -sign
+        prod = 1.0
+        for i in range(n):
+            prod *= M[i][perm[i]]
+        tot += sign * prod
+    return tot
+
+
+def _brute_eigs_4x4(A):
+    """Eigenvalues of a symmetric 4x4 by bisection on det(A - x I) (Leibniz determinant)."""
+    radius = max(sum(abs(v) for v in row) for row in A)  # Gershgorin bound
+    f = lambda x: _det_leibniz([[A[i][j] - (x if i == j else 0.0) for j in range(4)] for i in range(4)])
+    grid = np.linspace(-radius - 1, radius + 1, 4001)
+    vals = [f(x) for x in grid]
+    roots = []
+    for a, b, fa, fb in zip(grid[:-1], grid[1:], vals[:-1], vals[1:]):
+        if fa == 0.0:
+            roots.append(a)
+        elif fa * fb < 0:
+            for _ in range(200):
+                m = 0.5 * (a + b)
+                fm = f(m)
+                if fa * fm <= 0:
+                    b = m
+                else:
+                    a, fa = m, fm
+            roots.append(0.5 * (a + b))
+    return np.array(sorted(roots))
+
+
+def _inverse_cofactor(A):
+    n = len(A)
+    det = _det_leibniz(A)
+    inv = np.empty((n, n))
+    for i in range(n):
+        for j in range(n):
+            minor = [[A[r][c] for c in range(n) if c != j] for r in range(n) if r != i]
+            inv[j][i] = (-1) ** (i + j) * _det_leibniz(minor) / det
+    return inv
+
+
+def test_brute_force_4x4():
+    g = di.rng(23)
+    for _ in range(3):
+        M = g.standard_normal((4, 4))
+        A = M @ M.T + 0.5 * np.eye(4)  # SPD with well separated-enough eigenvalues
+        w, _, _ = oracle.jacobi_eigh(A)
+        assert np.max(np.abs(np.sort(w) - _brute_eigs_4x4(A.tolist()))) < 1e-10
+        X = oracle.inverse_root_evd(A)
+        X4 = X @ X @ X @ X
+        assert rel(X4, _inverse_cofactor(A.tolist())) < 1e-12
+        assert np.max(np.abs(X - X.T)) < 1e-14 and np.min(np.linalg.eigvalsh(X)) > 0
+
+
+def test_power_evd_rejects_indefinite():
+    with pytest.raises(ValueError):
+        oracle.inverse_root_evd(np.diag([1.0, -0.5, 2.0]))
+
+
+# ----------------------------------------------------------------------------------------------
+# c2: Frobenius scale
+# ----------------------------------------------------------------------------------------------
+
+def test_frobenius_pins():
+    assert oracle.frobenius(np.eye(64)) == 8.0
+    A, _, lam = spd(24, 32, 1e-2, 3.0)
+    s = oracle.frobenius(A)
+    assert s == 0.25 * oracle.frobenius(-4.0 * A)
+    assert s >= lam.max()
+    assert abs(s - math.sqrt(np.sum(lam ** 2))) < 1e-13 * s  # ||A||_F^2 = sum of squared eigenvalues
+    st = oracle.frobenius(np.stack([np.eye(16), 2 * np.eye(16)]))
+    assert np.array_equal(st, [4.0, 8.0])
+
+
+# ----------------------------------------------------------------------------------------------
+# c3: Multi-Power-Iteration
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fx", GOLDEN["power_iteration"], ids=lambda f: "T%d_n%d" % (f["T"], len(f["lam"])))
+def test_mpi_closed_form_fixtures(fx):
+    A = np.diag(fx["lam"])
+    s, mu = oracle.mpi(A, np.array(fx["V0"]), fx["T"])
+    assert np.max(np.abs(mu - fx["mu"]) / np.abs(fx["mu"])) < 1e-14
+    assert abs(s - fx["s"]) <= 1e-14 * fx["s"]
+
+
+def test_mpi_closed_form_known_spectrum():
+    A, Q, lam = spd(25, 48, 1e-3, 1.0)
+    V0 = di.start_vectors(48, 8, seed=26).astype(np.float64)
+    U = Q.T @ V0
+    for T in (1, 3, 10):
+        s, mu = oracle.mpi(A, V0, T)
+        want = (lam[:, None] ** (2 * T - 1) * U ** 2).sum(0) / (lam[:, None] ** (2 * T - 2) * U ** 2).sum(0)
+        assert np.max(np.abs(mu - want) / want) < 1e-12
+        assert s == mu.max()
+
+
+def test_mpi_bounds_monotone_and_identity():
+    A, _, lam = spd(27, 64, 1e-4, 1.0)
+    V0 = di.start_vectors(64, 32, seed=28)
+    prev = 0.0
+    for T in range(1, 12):
+        s, mu = oracle.mpi(A, V0, T)
+        assert np.all(mu <= lam.max() * (1 + 1e-14))
+        assert s >= prev * (1 - 1e-14)  # Rayleigh quotients of the power iteration never decrease
+        prev = s
+    s, _ = oracle.mpi(3.25 * np.eye(32), di.start_vectors(32, 4, seed=29), 10)
+    assert abs(s - 3.25) < 1e-15 * 3.25
+
+
+def test_mpi_half_precision():
+    # A = 2^m I: the binary16 operand is exactly I, every Rayleigh quotient is exactly 1, s = 2^m
+    s, mu = oracle.mpi(np.eye(32) * 2.0 ** -7, di.start_vectors(32, 5, seed=30), 6, half=True)
+    assert s == 2.0 ** -7 and np.all(mu == 2.0 ** -7)
+    # close to the fp64 estimate on a well conditioned block (binary16 storage of A and V)
+    A = di.tiny_stack()[0].astype(np.float64)
+    V0 = di.start_vectors(64, 32)
+    s64, _ = oracle.mpi(A, V0, 10)
+    s16, _ = oracle.mpi(A, V0, 10, half=True)
+    assert abs(s16 - s64) / s64 < 2e-3
+    # zero block: no positive diagonal, scale 0
+    assert oracle.mpi(np.zeros((8, 8)), np.ones((8, 2)), 3, half=True)[0] == 0.0
+
+
+# ----------------------------------------------------------------------------------------------
+# c4 / c5: Newton-Denman-Beavers
+# ----------------------------------------------------------------------------------------------
+
+def test_ndb_identity_is_fixed_point():
+    Y, Z, mon = oracle.ndb(np.eye(16), 5)
+    assert np.array_equal(Y, np.eye(16)) and np.array_equal(Z, np.eye(16)) and np.all(mon == 0)
+
+
+def test_ndb_limits_and_coupling_invariant():
+    M, _, _ = spd(31, 32, 0.02, 1.0)
+    R = oracle.power_evd(M, 0.5)
+    Ri = oracle.power_evd(M, -0.5)
+    for T in (1, 2, 4):
+        Y, Z, _ = oracle.ndb(M, T)
+        # coupled Denman-Beavers iterates satisfy Y_k = M Z_k and commute
+        assert rel(Y, M @ Z) < 1e-13
+        assert rel(Y @ Z, Z @ Y) < 1e-13
+    Y, Z, mon = oracle.ndb(M, 25)
+    assert rel(Y, R) < 1e-12 and rel(Z, Ri) < 1e-12
+    assert rel(Y @ Y, M) < 1e-12 and rel(Y @ Z, np.eye(32)) < 1e-12
+    # quadratic convergence of the monitor ||P - I||/sqrt(B) once it is small
+    k = int(np.argmax(mon < 1e-2))
+    assert mon[k + 1] < 10 * mon[k] ** 2
+
+
+def test_ndb_stable_at_kappa_1e4():
+    """The operand order (P = Z Y, Y' = Y S, Z' = S Z) stays converged long after convergence."""
+    M, _, _ = spd(32, 64, 1e-4, 1.0)
+    R = oracle.power_evd(M, 0.5)
+    Y, Z, mon = oracle.ndb(M, 80)
+    assert rel(Y, R) < 1e-10
+    assert mon[-1] < 1e-12
+
+
+def _ndb_numpy_swapped(M, T):
+    """A planted mistake (for the test above to catch): Y' = S Y instead of Y S."""
+    Y, Z = M.copy(), np.eye(len(M))
+    for _ in range(T):
+        S = 1.5 * np.eye(len(M)) - 0.5 * (Z @ Y)
+        Y, Z = S @ Y, S @ Z
+    return Y
+
+
+def test_ndb_stability_pin_catches_swapped_order():
+    M, _, _ = spd(32, 64, 1e-4, 1.0)
+    R = oracle.power_evd(M, 0.5)
+    with np.errstate(all="ignore"):
+        bad = _ndb_numpy_swapped(M, 80)
+    assert not np.all(np.isfinite(bad)) or rel(bad, R) > 1e-6
+
+
+@pytest.mark.parametrize("fx", GOLDEN["inverse_roots"], ids=lambda f: f["name"])
+def test_ndb_inverse_root_closed_forms(fx):
+    A = np.array(fx["A"])
+    X, R, mon = oracle.ndb_inverse_root(A, fx["lambda_max"], 30, 30, want_sqrt=True)
+    assert rel(X, fx["inv_fourth_root"]) < 1e-12
+    assert rel(R, fx["sqrt"]) < 1e-12
+    assert mon.shape == (60,)
+
+
+def test_ndb_inverse_root_tiny_stack_and_scale_equivariance():
+    A = di.tiny_stack().astype(np.float64)
+    s, _ = oracle.mpi(A, di.start_vectors(64, 32), 10)
+    X, _, _ = oracle.ndb_inverse_root(A, s, 20, 20)
+    assert rel(X, oracle.inverse_root_evd(A)) < 1e-10
+    X16, _, _ = oracle.ndb_inverse_root(16 * A, 16 * s, 20, 20)
+    assert rel(2 * X16, X) < 1e-15
+
+
+# ----------------------------------------------------------------------------------------------
+# c6: Coupled Newton, p = 4
+# ----------------------------------------------------------------------------------------------
+
+def test_cn_identity():
+    X, mon = oracle.cn_inverse_root(16.0 * np.eye(8), 16.0, 4)
+    assert np.array_equal(X, 0.5 * np.eye(8)) and np.all(mon == 0)
+    Xh, _ = oracle.cn_inverse_root(16.0 * np.eye(8), 16.0, 4, half_storage=True)
+    assert np.array_equal(Xh, 0.5 * np.eye(8))
+
+
+def test_cn_monitor_is_residual_and_limit():
+    A, _, _ = spd(41, 32, 1e-3, 1.0)
+    exact = oracle.inverse_root_evd(A)
+    for T in (1, 2, 3, 5):
+        X, mon = oracle.cn_inverse_root(A, 1.0, T)
+        # in exact arithmetic M_k = X_k^4 A_s, so the monitor of step T (one more step) is the residual
+        X2, mon2 = oracle.cn_inverse_root(A, 1.0, T + 1)
+        r = np.linalg.norm(X @ X @ X @ X @ A - np.eye(32)) / math.sqrt(32)
+        assert abs(mon2[T] - r) < 1e-10 * max(r, 1e-3)
+    X, mon = oracle.cn_inverse_root(A, 1.0, 40)
+    assert rel(X, exact) < 1e-10
+
+
+@pytest.mark.parametrize("fx", GOLDEN["inverse_roots"], ids=lambda f: f["name"])
+def test_cn_closed_forms(fx):
+    A = np.array(fx["A"])
+    X, _ = oracle.cn_inverse_root(A, fx["lambda_max"], 40)
+    assert rel(X, fx["inv_fourth_root"]) < 1e-12
+
+
+def test_cn_half_storage_residual():
+    A = di.tiny_stack()[:2].astype(np.float64)
+    s, _ = oracle.mpi(A, di.start_vectors(64, 32), 10)
+    X, _ = oracle.cn_inverse_root(A, s, 8, half_storage=True)
+    for b in range(2):
+        r = np.linalg.norm(np.linalg.matrix_power(X[b], 4) @ A[b] - np.eye(64)) / 8.0
+        assert r < 5e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# c7: Chebyshev / Clenshaw
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fx", GOLDEN["chebyshev"], ids=lambda f: "%g_%g" % (f["lo"], f["hi"]))
+def test_cheb_coeffs_x2_closed_form(fx):
+    c = oracle.cheb_coeffs(2, fx["lo"], fx["hi"], 2.0)
+    assert np.max(np.abs(c - fx["coeffs"])) < 1e-13 * max(1.0, np.abs(fx["coeffs"]).max())
+    c5 = oracle.cheb_coeffs(5, fx["lo"], fx["hi"], 2.0)
+    assert np.max(np.abs(c5[:3] - fx["coeffs"])) < 1e-12 * max(1.0, np.abs(fx["coeffs"]).max())
+    assert np.max(np.abs(c5[3:])) < 1e-12 * max(1.0, np.abs(fx["coeffs"]).max())
+
+
+def test_cheb_coeffs_match_numpy_interpolant():
+    lo, hi, d = 1e-3, 1.25, 24
+    c = oracle.cheb_coeffs(d, lo, hi, -0.25)
+    ref = np.polynomial.chebyshev.chebinterpolate(lambda t: (((hi - lo) * t + hi + lo) / 2) ** -0.25, d)
+    assert np.max(np.abs(c - ref)) < 1e-12 * np.abs(ref).max()
+    # interpolation property at the nodes
+    j = np.arange(d + 1)
+    t = np.cos(np.pi * (j + 0.5) / (d + 1))
+    x = ((hi - lo) * t + hi + lo) / 2
+    assert np.max(np.abs(np.polynomial.chebyshev.chebval(t, c) / x ** -0.25 - 1)) < 1e-12
+
+
+def test_clenshaw_scalar_and_x2():
+    lo, hi = 0.1, 1.3
+    c = oracle.cheb_coeffs(9, lo, hi, -0.25)
+    for a in (0.1, 0.37, 1.0, 1.3):
+        t = (2 * a - lo - hi) / (hi - lo)
+        want = sum(ck * math.cos(k * math.acos(t)) for k, ck in enumerate(c))
+        assert abs(oracle.clenshaw(np.array([[a]]), c, lo, hi)[0, 0] - want) < 1e-14
+    A, _, _ = spd(51, 24, 0.05, 1.0)
+    c2 = oracle.cheb_coeffs(3, 0.0, 1.0, 2.0)
+    assert rel(oracle.clenshaw(A, c2, 0.0, 1.0), A @ A) < 1e-13
+
+
+def test_clenshaw_known_spectrum_and_cheb_root_error():
+    A, Q, lam = spd(52, 32, 0.05, 1.0)
+    lo, hi, d = 0.04, 1.1, 12
+    c = oracle.cheb_coeffs(d, lo, hi, -0.25)
+    P = oracle.clenshaw(A, c, lo, hi)
+    p = np.polynomial.chebyshev.chebval((2 * lam - lo - hi) / (hi - lo), c)
+    assert rel(P, (Q * p[None, :]) @ Q.T) < 1e-13
+    # spectral-norm error of the matrix function equals the scalar error on the spectrum
+    X = oracle.cheb_inverse_root(2.0 * A, 2.0, d, lo, hi)
+    E = X - oracle.inverse_root_evd(2.0 * A)
+    scalar = np.max(np.abs(p - lam ** -0.25)) * 2.0 ** -0.25
+    assert abs(np.linalg.norm(E, 2) - scalar) < 1e-12
+
+
+# ----------------------------------------------------------------------------------------------
+# c8, c9, stacking
+# ----------------------------------------------------------------------------------------------
+
+def test_update_stats_exact_integers():
+    g = di.rng(61)
+    n = 12
+    G = g.integers(-3, 4, (n, n)).astype(np.int64)
+    L0 = g.integers(-5, 6, (n, n)).astype(np.int64)
+    L0 = L0 + L0.T
+    R0 = g.integers(-5, 6, (n, n)).astype(np.int64)
+    R0 = R0 + R0.T
+    L, R = oracle.update_stats(G, 0.5, L0, R0)
+    assert np.array_equal(2 * L, L0 + G @ G.T)   # beta = 1/2 keeps every value exact
+    assert np.array_equal(2 * R, R0 + G.T @ G)
+    assert np.array_equal(L, L.T) and np.array_equal(R, R.T)
+    # R(G) = L(G^T)
+    L_t, _ = oracle.update_stats(G.T, 0.5, R0, L0)
+    assert np.array_equal(L_t, R)
+
+
+def test_apply_identity_and_integers():
+    g = di.rng(62)
+    G = g.standard_normal((3, 16, 16))
+    I = np.broadcast_to(np.eye(16), G.shape)
+    assert np.array_equal(oracle.apply(I, G, I), G)
+    XL = g.integers(-3, 4, (3, 16, 16)).astype(np.int64)
+    XR = g.integers(-3, 4, (3, 16, 16)).astype(np.int64)
+    Gi = g.integers(-3, 4, (3, 16, 16)).astype(np.int64)
+    assert np.array_equal(oracle.apply(XL, Gi, XR), XL @ Gi @ XR)
+    assert not np.array_equal(oracle.apply(XL, Gi, XR), XR @ Gi @ XL)
+
+
+def test_stack_order_and_round_trip():
+    B = 4
+    shapes = [(8, 12), (4, 4), (12, 8)]
+    g = di.rng(63)
+    W = [g.standard_normal(s) for s in shapes]
+    S = oracle.stack(W, B)
+    assert S.shape == (6 + 1 + 6, B, B)
+    # tile (tr, tc) of weight w sits at offset(w) + tr * (cols / B) + tc
+    assert np.array_equal(S[0], W[0][0:4, 0:4])
+    assert np.array_equal(S[2], W[0][0:4, 8:12])
+    assert np.array_equal(S[3], W[0][4:8, 0:4])
+    assert np.array_equal(S[6], W[1])
+    assert np.array_equal(S[7 + 2 * 2 + 1], W[2][8:12, 4:8])
+    back = oracle.unstack(S, shapes, B)
+    assert all(np.array_equal(a, b) for a, b in zip(back, W))
+    with pytest.raises(ValueError):
+        oracle.stack([np.zeros((6, 8))], B)
+
+
+def test_llama_shapes_give_1536_tiles():
+    assert di.num_tiles(di.llama_weight_shapes(), 1024) == 1536
