@@ -1,0 +1,155 @@
+/*
+ * dash.h -- C ABI of the MI355X (gfx950) batched inverse-fourth-root library.
+ *
+ * The library computes, for a stack of N independent symmetric positive-definite B x B blocks held
+ * as one (N, B, B) tensor, the inverse fourth root A^{-1/4} that Shampoo needs, plus the steps
+ * around it: stacking weight gradients into B x B tiles, the L/R statistic update, spectral
+ * scaling, and applying the preconditioned update L^{-1/4} G R^{-1/4}.
+ *
+ * Pages cited (by title and section):
+ *   [PT] "Resumo Técnico: DASH – Shampoo Mais Rápido via Pré-condicionamento de Blocos em Lote e
+ *        Solvers de Raiz Inversa Eficientes" (gist.science/pt/paper/2602.02016)
+ *   [TG] quant_prune_distill post 646 (tgviewer.app), commentary on DASH
+ *   [AB] arxivdaily.com/papers/2602.02016, English abstract
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless marked [host].  Matrices are contiguous row-major fp32
+ *   (fp16 appears only inside the library), 16-byte aligned; a stack of N blocks is N*B*B floats
+ *   with block i at offset i*B*B.
+ * - B % 64 == 0 and 64 <= B <= 8192; N >= 1.
+ * - Ownership: the caller allocates and owns every buffer.  The library never allocates device
+ *   memory, never synchronises the device or the stream and keeps no mutable global state.
+ *   Scratch memory is the caller's `ws` of `ws_bytes` bytes (256-byte aligned), sized by
+ *   dash_workspace_size(); its contents are undefined on return.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ * - Errors: argument, shape and workspace errors are detected on the host before anything is
+ *   enqueued (nothing is launched); DASH_ERR_DEVICE reports a failed launch.  Numerical trouble
+ *   never synchronises: per-block problems are reported in the optional `status[N]` array
+ *   (bit 0: the scale s_i is not finite or not > 0, the block's output is NaN;
+ *    bit 1: the block's output contains a non-finite value).  Other blocks are unaffected.
+ * - Outputs must not alias inputs unless stated.
+ */
+#ifndef DASH_H_
+#define DASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DASH_ABI_VERSION 1
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad count, parameter out of range */
+  DASH_ERR_SHAPE = 2,       /* B not a multiple of 64 or out of range, weight not divisible by B */
+  DASH_ERR_WORKSPACE = 3,   /* ws too small or misaligned */
+  DASH_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement (e.g. p != 4) */
+  DASH_ERR_DEVICE = 5       /* a HIP launch failed */
+} dash_status;
+
+typedef enum { DASH_FP32 = 0, DASH_FP16 = 1 } dash_prec; /* operand precision; accumulation is fp32 */
+
+typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
+
+typedef enum {
+  DASH_OP_SCALE = 0,
+  DASH_OP_NDB = 1,
+  DASH_OP_CN = 2,
+  DASH_OP_CHEB = 3,
+  DASH_OP_APPLY = 4
+} dash_op;
+
+/* A row-major fp32 weight gradient (device memory): element (r, c) at ptr[r * ld + c]. */
+typedef struct {
+  float* ptr;
+  int64_t rows, cols, ld;
+} dash_mat;
+
+/* Blockify: copy the B x B tiles of n weight gradients into G_stack, weight-major, then tile row,
+ * then tile column ([PT] Metodologia, item 1: gradient blocks G_ij are stacked into an (N, B, B)
+ * tensor so one batched call processes them all).
+ * grads [host]: n descriptors; every rows and cols must be divisible by B (else DASH_ERR_SHAPE),
+ * ld >= cols, ptr and ld*4 16-byte aligned.  G_stack: sum_w (rows_w/B)(cols_w/B) blocks. */
+dash_status dash_stack(const dash_mat* grads, int32_t n, int32_t B, float* G_stack, void* stream);
+
+/* Inverse of dash_stack: scatter the tiles of U_stack back into n weight-shaped outputs [host]. */
+dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, int32_t n, void* stream);
+
+/* Shampoo statistics ([TG] body: L and R are kept from products of the gradient):
+ *   L_t <- beta L_t + (1 - beta) G_t G_t^T,   R_t <- beta R_t + (1 - beta) G_t^T G_t,
+ * for the NG gradient tiles G_stack[NG,B,B].  A is the stacked preconditioner statistic
+ * [2*NG, B, B] updated IN PLACE: L blocks at [0, NG), R blocks at [NG, 2 NG) ([TG] body: the L and R
+ * preconditioners are stacked into one tensor).  Only the upper triangle of each input block is
+ * read; every output block is exactly symmetric.  0 <= beta <= 1. */
+dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float beta, float* A, void* stream);
+
+/* Per-block scale s[N] ([PT] Definição do Problema, item 3, and Metodologia, item 2,
+ * "Multi-Power-Iteration"; [TG] body: Rayleigh-quotient estimate of the spectral norm).
+ *   DASH_SCALE_FROBENIUS: s_i = ||A_i||_F   (k, steps, V0 and prec ignored; ws may be NULL).
+ *   DASH_SCALE_POWER:     k start vectors (columns of V0[B,k], shared by all blocks, 1 <= k <= 32)
+ *     run `steps` >= 1 power-iteration steps in parallel: each step forms W = A_i V, the Rayleigh
+ *     quotient of every column comes from the last step, each column is renormalised between
+ *     steps, and s_i = max over columns.  prec == DASH_FP16 streams A_i in binary16 prescaled by
+ *     2^-ceil(log2 max_j A_i[j][j]) and keeps V in binary16; accumulation stays fp32.
+ * A block whose scale comes out non-finite or <= 0 is flagged later by the solver. */
+dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream);
+
+/* Inverse fourth root by two Newton-Denman-Beavers calls ([PT] Metodologia, item 2,
+ * "Iteração de Newton-Denman-Beavers": one call gives the square root and the inverse square root;
+ * the first step skips the products that the identity start makes redundant).
+ * One call on M: Y_0 = M, Z_0 = I; per step P = Z Y, S = (3I - P)/2, Y <- Y S, Z <- S Z.
+ * Call 1 runs iters1 steps on A_i / s_i giving Y ~ (A_i/s_i)^{1/2}; call 2 runs iters2 steps on
+ * that Y giving Z ~ (A_i/s_i)^{-1/4}; X_i = s_i^{-1/4} Z.  3*iters - 3 products per call.
+ * fp32 only.  iters1, iters2 >= 1.
+ * sqrt_out: NULL or [N,B,B] receives s_i^{1/2} Y (the square root of A_i).
+ * monitor:  NULL or [N, iters1 + iters2] receives ||P_k - I||_F / sqrt(B) per step.
+ * status:   NULL or [N]. */
+dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                  int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Inverse p-th root by the Coupled-Newton iteration, p = 4 ([PT] Definição do Problema, item 2;
+ * [TG] body, "CN - Coupled Newton Iteration"; fp16 operands per [PT] Resultados Experimentais).
+ * On M_0 = A_i / s_i, X_0 = I: S = (5I - M)/4, X <- X S, M <- M S^4 (S^4 = (S S)(S S));
+ * X_i = s_i^{-1/4} X_iters.  4*iters - 4 products.  prec == DASH_FP16 stores every iterate in
+ * binary16 and accumulates in fp32; X is always written in fp32.  p != 4 -> DASH_ERR_UNSUPPORTED.
+ * monitor: NULL or [N, iters] receives ||M_k - I||_F / sqrt(B) before step k. */
+dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
+                                 dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* Inverse fourth root by a Chebyshev approximation evaluated with Clenshaw's recurrence
+ * ([PT] Metodologia, item 2, "Aproximações de Polinômios de Chebyshev").  The degree-`degree`
+ * interpolant p of x^{-1/4} at the Chebyshev points of the first kind on [lo, hi] is applied to
+ * A_i / s_i; X_i = s_i^{-1/4} p(A_i / s_i).  degree - 1 products.  1 <= degree <= 64, 0 < lo < hi.
+ * fp32 only. */
+dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,
+                                   double hi, float* X, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* Preconditioned update U_t = (XL_t G_t) XR_t for t < NG ([TG] body: the -1/4 powers of L and R
+ * precondition the gradient).  XL, XR, G_stack, U_stack are [NG,B,B]; U_stack must not alias the
+ * inputs.  ws holds one [NG,B,B] intermediate. */
+dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B, float* U_stack,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for an operation.  k_or_degree: the number of start vectors for
+ * DASH_OP_SCALE (power iteration; Frobenius needs 0), ignored otherwise.  bytes [host]. */
+dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t k_or_degree,
+                                size_t* bytes);
+
+/* Number of B x B products a solver call enqueues per block (host-side count, no GPU work). */
+int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2);
+
+const char* dash_status_string(dash_status status);
+int32_t dash_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H_ */

@@ -1,0 +1,613 @@
+// api.hip -- the C ABI of include/dash.h: host-side validation, workspace carving and the solver
+// drivers that enqueue the kernels of gemm.hip, scale.hip and elementwise.hip on the caller's stream.
+//
+// Nothing here allocates device memory or synchronises: every intermediate lives in the caller's
+// workspace, and per-block scalars derived from s stay on the device (coefficient table).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "dash_internal.hpp"
+
+using namespace dash;
+
+namespace {
+
+#define TRY(x)                                              \
+  do {                                                      \
+    if ((x) != hipSuccess) return DASH_ERR_DEVICE;          \
+  } while (0)
+
+constexpr int64_t MAX_N = (int64_t)1 << 31;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool valid_B(int32_t B) { return B >= 64 && B <= 8192 && B % 64 == 0; }
+bool valid_N(int64_t N) { return N >= 1 && N <= MAX_N; }
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+size_t elem_size(dash_prec p) { return p == DASH_FP16 ? 2 : 4; }
+size_t stack_bytes(int64_t N, int B, dash_prec p) { return align_up((size_t)N * B * B * elem_size(p), 256); }
+size_t coef_bytes(int64_t N) { return align_up((size_t)N * COEF_STRIDE * sizeof(float), 256); }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  char* p;
+  size_t left;
+  void* take(size_t n) {
+    n = align_up(n, 256);
+    if (n > left) return nullptr;
+    void* r = p;
+    p += n;
+    left -= n;
+    return r;
+  }
+};
+
+// Stack-sized buffers of the caller's workspace handed out to a solver's iterates.
+struct Pool {
+  std::vector<void*> free_list;
+  void* get() {
+    void* r = free_list.back();
+    free_list.pop_back();
+    return r;
+  }
+  void put(void* p) { free_list.push_back(p); }
+};
+
+size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32); }
+size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + 5 * stack_bytes(N, B, p); }
+size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
+size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
+size_t ws_scale(int64_t N, int B, dash_prec p, int k) { return k == 0 ? 0 : power_workspace_bytes(N, B, p); }
+
+Product prod(const void* X, const void* Y, void* D, const float* C = nullptr, const float* E = nullptr,
+             void* D2 = nullptr) {
+  Product p;
+  p.X = X;
+  p.Y = Y;
+  p.D = D;
+  p.C = C;
+  p.E = E;
+  p.D2 = D2;
+  return p;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Newton-Denman-Beavers: one call on M (optionally M = A / s via the coefficient table).
+// Returns the buffer holding the wanted iterate (Y when !want_z) or writes Z into `final_out`
+// scaled by coef[final_idx] (when want_z).
+// ------------------------------------------------------------------------------------------------
+struct NdbCtx {
+  int64_t N;
+  int B;
+  const float* coef;
+  float* monitor;  // base of [N, mon_cols] or null
+  int mon_cols;
+  int32_t* status;
+  hipStream_t st;
+  Pool* pool;
+};
+
+dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool scaled, int T, int mon_col,
+                     bool want_z, float* final_out, float** y_out) {
+  // step 0: Z_0 = I so P_0 = M and S_0 = (3I - M)/2; Y_1 = M S_0 = 1.5 M - 0.5 M^2, Z_1 = S_0.
+  const bool last = (T == 1);
+  float* Z = nullptr;
+  float* Y = nullptr;
+  {
+    Affine s0;
+    s0.X = M;
+    s0.a = -0.5f;
+    s0.ia = scaled ? CO_R1 : CO_NONE;
+    s0.g = 1.5f;
+    s0.coef = c.coef;
+    if (c.monitor) {  // ||P_0 - I||^2 = 4 ||S_0 - I||^2
+      s0.monitor = c.monitor + mon_col;
+      s0.mon_stride = c.mon_cols;
+      s0.mon_mul = 4.f;
+    }
+    if (!last || want_z) {
+      Z = (float*)c.pool->get();
+      s0.D = Z;
+      TRY(launch_affine(s0, c.N, c.B, c.st));
+    } else if (c.monitor) {  // only the monitor is wanted from S_0: write it to a scratch buffer
+      float* tmp = (float*)c.pool->get();
+      s0.D = tmp;
+      TRY(launch_affine(s0, c.N, c.B, c.st));
+      c.pool->put(tmp);
+    }
+  }
+  if (!last || !want_z) {
+    Y = (float*)c.pool->get();
+    Epilogue e;
+    e.alpha = -0.5f;
+    e.ia = scaled ? CO_R2 : CO_NONE;
+    e.beta = 1.5f;
+    e.ib = scaled ? CO_R1 : CO_NONE;
+    e.coef = c.coef;
+    Product p = prod(M, M, Y, M);
+    TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+  }
+  if (m_from_pool) c.pool->put((void*)M);
+  if (last) {
+    if (want_z) {
+      Affine fin;  // X = u Z_1
+      fin.X = Z;
+      fin.D = final_out;
+      fin.a = 1.f;
+      fin.ia = CO_U;
+      fin.coef = c.coef;
+      fin.status = c.status;
+      TRY(launch_affine(fin, c.N, c.B, c.st));
+      c.pool->put(Z);
+    } else {
+      *y_out = Y;
+    }
+    return DASH_OK;
+  }
+  for (int k = 1; k < T; ++k) {
+    // S = (3I - Z Y) / 2, monitor ||Z Y - I|| = 2 ||S - I||
+    float* S = (float*)c.pool->get();
+    {
+      Epilogue e;
+      e.alpha = -0.5f;
+      e.gamma = 1.5f;
+      if (c.monitor) {
+        e.monitor = c.monitor + mon_col + k;
+        e.mon_stride = c.mon_cols;
+        e.mon_mul = 4.f;
+      }
+      Product p = prod(Z, Y, S);
+      TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+    }
+    if (k == T - 1) {
+      if (want_z) {  // Z_T = S Z, unscaled into the output
+        Epilogue e;
+        e.alpha = 1.f;
+        e.ia = CO_U;
+        e.coef = c.coef;
+        e.status = c.status;
+        Product p = prod(S, Z, final_out);
+        TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+        c.pool->put(Y);
+        c.pool->put(Z);
+      } else {  // Y_T = Y S
+        float* Yn = (float*)c.pool->get();
+        Epilogue e;
+        Product p = prod(Y, S, Yn);
+        TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+        c.pool->put(Y);
+        c.pool->put(Z);
+        *y_out = Yn;
+      }
+      c.pool->put(S);
+      return DASH_OK;
+    }
+    float* Yn = (float*)c.pool->get();
+    float* Zn = (float*)c.pool->get();
+    Epilogue e;
+    Product p[2] = {prod(Y, S, Yn), prod(S, Z, Zn)};
+    TRY(launch_gemm(p, 2, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+    c.pool->put(Y);
+    c.pool->put(Z);
+    c.pool->put(S);
+    Y = Yn;
+    Z = Zn;
+  }
+  return DASH_OK;
+}
+
+// Chebyshev interpolation coefficients of x^{-1/4} on [lo, hi] at the d+1 Chebyshev points of the
+// first kind (the interpolant in the Chebyshev basis of t = (2x - lo - hi)/(hi - lo)).
+void cheb_coefficients(int d, double lo, double hi, std::vector<double>& c) {
+  const double pi = std::acos(-1.0);
+  c.assign(d + 1, 0.0);
+  for (int j = 0; j <= d; ++j) {
+    const double theta = pi * (j + 0.5) / (d + 1);
+    const double x = 0.5 * ((hi - lo) * std::cos(theta) + hi + lo);
+    const double fx = 1.0 / std::sqrt(std::sqrt(x));
+    for (int k = 0; k <= d; ++k) c[k] += fx * std::cos(k * theta);
+  }
+  for (int k = 0; k <= d; ++k) c[k] *= 2.0 / (d + 1);
+  c[0] *= 0.5;
+}
+
+dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) {
+  if (!m || n < 1) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  int64_t t = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!m[i].ptr || !aligned(m[i].ptr, 16) || m[i].ld % 4 != 0) return DASH_ERR_INVALID_ARG;
+    if (m[i].rows < 1 || m[i].cols < 1 || m[i].ld < m[i].cols) return DASH_ERR_INVALID_ARG;
+    if (m[i].rows % B || m[i].cols % B) return DASH_ERR_SHAPE;
+    t += (m[i].rows / B) * (m[i].cols / B);
+  }
+  *tiles = t;
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dash_abi_version(void) { return DASH_ABI_VERSION; }
+
+const char* dash_status_string(dash_status s) {
+  switch (s) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARG: return "invalid argument";
+    case DASH_ERR_SHAPE: return "unsupported shape";
+    case DASH_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case DASH_ERR_UNSUPPORTED: return "unsupported request";
+    case DASH_ERR_DEVICE: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2) {
+  switch (op) {
+    case DASH_OP_NDB:
+      if (iters1 < 1 || iters2 < 1) return -1;
+      return (iters1 == 1 ? 1 : 3 * (int64_t)iters1 - 3) + (3 * (int64_t)iters2 - 3);
+    case DASH_OP_CN:
+      if (iters1 < 1) return -1;
+      return iters1 == 1 ? 0 : 4 * (int64_t)iters1 - 4;
+    case DASH_OP_CHEB:
+      if (iters1 < 1) return -1;
+      return iters1 < 2 ? 0 : (int64_t)iters1 - 1;
+    default: return -1;
+  }
+}
+
+dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t k_or_degree,
+                                size_t* bytes) {
+  if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  switch (op) {
+    case DASH_OP_SCALE:
+      if (k_or_degree < 0 || k_or_degree > 32) return DASH_ERR_INVALID_ARG;
+      *bytes = ws_scale(N, B, prec, k_or_degree);
+      return DASH_OK;
+    case DASH_OP_NDB: *bytes = ws_ndb(N, B); return DASH_OK;
+    case DASH_OP_CN: *bytes = ws_cn(N, B, prec); return DASH_OK;
+    case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
+    case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
+  }
+  return DASH_ERR_INVALID_ARG;
+}
+
+dash_status dash_stack(const dash_mat* grads, int32_t n, int32_t B, float* G_stack, void* stream) {
+  int64_t tiles = 0;
+  dash_status st = check_mats(grads, n, B, &tiles);
+  if (st != DASH_OK) return st;
+  if (!G_stack || !aligned(G_stack, 16)) return DASH_ERR_INVALID_ARG;
+  int64_t first = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    TRY(launch_tile_copy(grads[i], B, G_stack, first, true, nullptr, as_stream(stream)));
+    first += (grads[i].rows / B) * (grads[i].cols / B);
+  }
+  return DASH_OK;
+}
+
+dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, int32_t n, void* stream) {
+  int64_t tiles = 0;
+  dash_status st = check_mats(outs, n, B, &tiles);
+  if (st != DASH_OK) return st;
+  if (!U_stack || !aligned(U_stack, 16)) return DASH_ERR_INVALID_ARG;
+  int64_t first = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    TRY(launch_tile_copy(outs[i], B, nullptr, first, false, U_stack, as_stream(stream)));
+    first += (outs[i].rows / B) * (outs[i].cols / B);
+  }
+  return DASH_OK;
+}
+
+dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float beta, float* A, void* stream) {
+  if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
+  if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
+  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  float* L = A;
+  float* R = A + NG * (int64_t)B * B;
+  Epilogue e;
+  e.alpha = 1.f - beta;
+  e.beta = beta;
+  Product pl = prod(G_stack, G_stack, L, L);  // G G^T : Y read transposed
+  TRY(launch_gemm(&pl, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NT, true, e, as_stream(stream)));
+  Product pr = prod(G_stack, G_stack, R, R);  // G^T G : X read transposed
+  TRY(launch_gemm(&pr, 1, NG, B, DASH_FP32, DASH_FP32, Trans::TN, true, e, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !s || !aligned(A, 16) || !aligned(s, 4) || !valid_N(N)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (how == DASH_SCALE_FROBENIUS) {
+    TRY(launch_frobenius(A, N, B, s, as_stream(stream)));
+    return DASH_OK;
+  }
+  if (how != DASH_SCALE_POWER) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !V0 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) || ws_bytes < power_workspace_bytes(N, B, prec)) return DASH_ERR_WORKSPACE;
+  Carver cv{(char*)ws, ws_bytes};
+  PowerPlan p;
+  p.N = N;
+  p.B = B;
+  p.k = k;
+  p.steps = steps;
+  p.prec = prec;
+  p.A = A;
+  p.V0 = V0;
+  p.s = s;
+  const int RB = B / 64;
+  for (int q = 0; q < 2; ++q) p.W[q] = (float*)cv.take((size_t)N * B * 32 * sizeof(float));
+  for (int q = 0; q < 2; ++q) p.part[q] = (float*)cv.take((size_t)N * RB * 3 * 32 * sizeof(float));
+  p.v0inv = (float*)cv.take(256);
+  p.coef = (float*)cv.take((size_t)N * COEF_STRIDE * sizeof(float));
+  p.Ah = prec == DASH_FP16 ? (_Float16*)cv.take((size_t)N * B * B * sizeof(_Float16)) : nullptr;
+  TRY(launch_power_iteration(p, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                  int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (sqrt_out && (!aligned(sqrt_out, 16) || sqrt_out == A || sqrt_out == X)) return DASH_ERR_INVALID_ARG;
+  if (X == A || iters1 < 1 || iters2 < 1 || iters1 > 1000 || iters2 > 1000) return DASH_ERR_INVALID_ARG;
+  if (monitor && !aligned(monitor, 4)) return DASH_ERR_INVALID_ARG;
+  if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_ndb(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  Pool pool;
+  for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, DASH_FP32)));
+  const int cols = iters1 + iters2;
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  if (monitor) TRY(launch_fill_f32(monitor, N * cols, 0.f, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
+  float* Y = nullptr;
+  dash_status r = ndb_call(c, A, false, true, iters1, 0, false, nullptr, &Y);
+  if (r != DASH_OK) return r;
+  if (sqrt_out) {
+    Affine sq;
+    sq.X = Y;
+    sq.D = sqrt_out;
+    sq.a = 1.f;
+    sq.ia = CO_SQ;
+    sq.coef = coef;
+    TRY(launch_affine(sq, N, B, st));
+  }
+  r = ndb_call(c, Y, true, false, iters2, iters1, true, X, nullptr);
+  if (r != DASH_OK) return r;
+  if (monitor) TRY(launch_monitor_finish(monitor, N * cols, B, st));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
+                                 dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (X == A || iters < 1 || iters > 1000) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (monitor && !aligned(monitor, 4)) return DASH_ERR_INVALID_ARG;
+  if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (p != 4) return DASH_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_cn(N, B, prec)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  Pool pool;
+  for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, prec)));
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  const int T = iters;
+  // step 0: M_0 = A/s, S_0 = (5I - M_0)/4, X_1 = S_0;  ||M_0 - I||^2 = 16 ||S_0 - I||^2
+  void* S = pool.get();
+  void* M = pool.get();
+  {
+    Affine s0;
+    s0.X = A;
+    s0.D = S;
+    s0.d_prec = prec;
+    s0.a = -0.25f;
+    s0.ia = CO_R1;
+    s0.g = 1.25f;
+    s0.coef = coef;
+    if (T > 1) {
+      s0.D2 = M;
+      s0.d2_prec = prec;
+      s0.a2 = 1.f;
+      s0.ia2 = CO_R1;
+    }
+    if (monitor) {
+      s0.monitor = monitor;
+      s0.mon_stride = T;
+      s0.mon_mul = 16.f;
+    }
+    TRY(launch_affine(s0, N, B, st));
+  }
+  if (T == 1) {  // X = s^{-1/4} S_0, straight from A
+    Affine fin;
+    fin.X = A;
+    fin.D = X;
+    fin.a = -0.25f;
+    fin.ia = CO_R1U;
+    fin.g = 1.25f;
+    fin.ig = CO_U;
+    fin.coef = coef;
+    fin.status = status;
+    TRY(launch_affine(fin, N, B, st));
+    if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
+    return DASH_OK;
+  }
+  void* Xk = S;  // X_1 = S_0 shares the buffer (both are read-only from here on)
+  for (int k = 0; k < T; ++k) {
+    if (k == T - 1) {  // X_T = s^{-1/4} X_{T-1} S_{T-1}
+      Epilogue e;
+      e.ia = CO_U;
+      e.coef = coef;
+      e.status = status;
+      Product pr = prod(Xk, S, X);
+      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, false, e, st));
+      break;
+    }
+    void* S2 = pool.get();
+    if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
+      Product pr = prod(S, S, S2);
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+    } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
+      void* Xn = pool.get();
+      Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
+      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+      pool.put(Xk);
+      pool.put(S);
+      Xk = Xn;
+    }
+    void* S4 = pool.get();
+    {
+      Product pr = prod(S2, S2, S4);
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+    }
+    pool.put(S2);
+    // M_{k+1} = M_k S^4 and S_{k+1} = (5I - M_{k+1})/4 from the same accumulator
+    void* Sn = pool.get();
+    Epilogue e;
+    if (monitor) {
+      e.monitor = monitor + (k + 1);
+      e.mon_stride = T;
+    }
+    if (k + 1 == T - 1) {  // M_T is never needed: write S only, monitor from it
+      e.alpha = -0.25f;
+      e.gamma = 1.25f;
+      e.mon_mul = 16.f;
+      Product pr = prod(M, S4, Sn);
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st));
+      pool.put(M);
+      M = nullptr;
+    } else {
+      void* Mn = pool.get();
+      e.alpha = 1.f;
+      e.alpha2 = -0.25f;
+      e.gamma2 = 1.25f;
+      Product pr = prod(M, S4, Mn, nullptr, nullptr, Sn);
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st));
+      pool.put(M);
+      M = Mn;
+    }
+    pool.put(S4);
+    S = Sn;
+  }
+  if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,
+                                   double hi, float* X, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (X == A || degree < 1 || degree > 64) return DASH_ERR_INVALID_ARG;
+  if (!(std::isfinite(lo) && std::isfinite(hi) && lo > 0.0 && hi > lo)) return DASH_ERR_INVALID_ARG;
+  if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_cheb(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  float* b1 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
+  float* b2 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  std::vector<double> c;
+  cheb_coefficients(degree, lo, hi, c);
+  const int d = degree;
+  const double w = hi - lo, m = hi + lo;
+  if (d == 1) {  // X = u (c0 I + c1 T),  T = (2 A/s - m I)/w
+    Affine fin;
+    fin.X = A;
+    fin.D = X;
+    fin.a = (float)(2.0 * c[1] / w);
+    fin.ia = CO_R1U;
+    fin.g = (float)(c[0] - c[1] * m / w);
+    fin.ig = CO_U;
+    fin.coef = coef;
+    fin.status = status;
+    TRY(launch_affine(fin, N, B, st));
+    return DASH_OK;
+  }
+  // b_d = c_d I,  b_{d-1} = c_{d-1} I + 2 T b_d = c_{d-1} I + c_d (4 A/s - 2 m I)/w
+  {
+    Affine init;
+    init.X = A;
+    init.D = b1;
+    init.a = (float)(4.0 * c[d] / w);
+    init.ia = CO_R1;
+    init.g = (float)(c[d - 1] - 2.0 * c[d] * m / w);
+    init.D2 = b2;
+    init.a2 = 0.f;
+    init.g2 = (float)c[d];
+    init.coef = coef;
+    TRY(launch_affine(init, N, B, st));
+  }
+  // b_k = c_k I + 2 T b_{k+1} - b_{k+2}, written over b_{k+2}
+  for (int k = d - 2; k >= 1; --k) {
+    Epilogue e;
+    e.alpha = (float)(4.0 / w);
+    e.ia = CO_R1;
+    e.beta = (float)(-2.0 * m / w);
+    e.delta = -1.f;
+    e.gamma = (float)c[k];
+    e.coef = coef;
+    Product pr = prod(A, b1, b2, b1, b2);
+    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, e, st));
+    float* t = b1;
+    b1 = b2;
+    b2 = t;
+  }
+  // X = u (c_0 I + T b_1 - b_2)
+  Epilogue e;
+  e.alpha = (float)(2.0 / w);
+  e.ia = CO_R1U;
+  e.beta = (float)(-m / w);
+  e.ib = CO_U;
+  e.delta = -1.f;
+  e.id = CO_U;
+  e.gamma = (float)c[0];
+  e.ig = CO_U;
+  e.coef = coef;
+  e.status = status;
+  Product pr = prod(A, b1, X, b1, b2);
+  TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, e, st));
+  return DASH_OK;
+}
+
+dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B, float* U_stack,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (!XL || !XR || !G_stack || !U_stack || !valid_N(NG)) return DASH_ERR_INVALID_ARG;
+  if (!aligned(XL, 16) || !aligned(XR, 16) || !aligned(G_stack, 16) || !aligned(U_stack, 16))
+    return DASH_ERR_INVALID_ARG;
+  if (U_stack == XL || U_stack == XR || U_stack == G_stack) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_apply(NG, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  float* T = (float*)ws;
+  Product p1 = prod(XL, G_stack, T);
+  TRY(launch_gemm(&p1, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+  Product p2 = prod(T, XR, U_stack);
+  TRY(launch_gemm(&p2, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+  return DASH_OK;
+}
+
+}  // extern "C"

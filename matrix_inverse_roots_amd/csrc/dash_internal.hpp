@@ -1,0 +1,122 @@
+// dash_internal.hpp -- internal declarations shared by the HIP translation units of libdash.
+//
+// Everything here is private to the library; the public surface is include/dash.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/dash.h"
+
+namespace dash {
+
+// ------------------------------------------------------------------------------------------------
+// Per-block coefficient table.  One row of COEF_STRIDE floats per block, computed on the device
+// from the scale s_i so that the host never reads s (no synchronisation).
+// ------------------------------------------------------------------------------------------------
+enum CoefIdx : int {
+  CO_R1 = 0,    // 1 / s
+  CO_R2 = 1,    // 1 / s^2
+  CO_U = 2,     // s^{-1/4}        (final unscaling of an inverse fourth root)
+  CO_SQ = 3,    // s^{1/2}         (unscaling of a square root)
+  CO_R1U = 4,   // s^{-1} s^{-1/4}
+  CO_P2 = 5,    // 2^-e: binary16 prescale of the power iteration
+  CO_P2INV = 6, // 2^e
+  CO_NONE = -1
+};
+constexpr int COEF_STRIDE = 8;
+
+// Epilogue of a batched product acc = X_b Y_b (fp32 accumulation):
+//   D  = alpha_b acc + beta_b C + delta_b E + gamma_b I        (C, E optional fp32 stacks)
+//   D2 = alpha2_b acc + gamma2_b I                             (optional second output)
+// with every coefficient = scalar * (idx >= 0 ? coef[b * COEF_STRIDE + idx] : 1).
+// monitor (optional): monitor[b * mon_stride] += mon_mul * sum over the block of (D - I)^2
+//   (accumulated with atomics; the caller zero-fills it and takes sqrt/ sqrt(B) afterwards).
+// status (optional): status[b] |= 2 when D or D2 holds a non-finite value.
+struct Epilogue {
+  float alpha = 1.f, beta = 0.f, delta = 0.f, gamma = 0.f, alpha2 = 0.f, gamma2 = 0.f;
+  int8_t ia = CO_NONE, ib = CO_NONE, id = CO_NONE, ig = CO_NONE, ia2 = CO_NONE, ig2 = CO_NONE;
+  const float* coef = nullptr;
+  float* monitor = nullptr;
+  int32_t mon_stride = 0;
+  float mon_mul = 1.f;
+  int32_t* status = nullptr;
+};
+
+// One batched product over N blocks: D_b = epi(X_b Y_b).  X/Y element type is `in_prec`,
+// D/D2 element type is `out_prec`; C/E are fp32.  Stride between blocks: B*B elements.
+struct Product {
+  const void* X = nullptr;
+  const void* Y = nullptr;
+  const float* C = nullptr;
+  const float* E = nullptr;
+  void* D = nullptr;
+  void* D2 = nullptr;
+};
+
+enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed
+
+// Enqueue one or two batched products sharing shape, precision and epilogue scalars (two problems
+// in one launch fill the GPU better).  sym: compute only the upper-triangle tiles and mirror them
+// (exactly symmetric output; C read from the upper triangle).
+hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_prec in_prec, dash_prec out_prec,
+                       Trans trans, bool sym, const Epilogue& epi, hipStream_t stream);
+
+// D_b = a_b X_b + g_b I (and optionally D2_b = a2_b X_b + g2_b I), elementwise, X fp32.
+// X may be NULL (then D = g_b I).  Output precisions per output.  Optional monitor/status as above
+// (monitor from D).
+struct Affine {
+  const float* X = nullptr;
+  void* D = nullptr;
+  dash_prec d_prec = DASH_FP32;
+  float a = 0.f, g = 0.f;
+  int8_t ia = CO_NONE, ig = CO_NONE;
+  void* D2 = nullptr;
+  dash_prec d2_prec = DASH_FP32;
+  float a2 = 0.f, g2 = 0.f;
+  int8_t ia2 = CO_NONE, ig2 = CO_NONE;
+  const float* coef = nullptr;
+  float* monitor = nullptr;
+  int32_t mon_stride = 0;
+  float mon_mul = 1.f;
+  int32_t* status = nullptr;
+};
+hipError_t launch_affine(const Affine& op, int64_t N, int B, hipStream_t stream);
+
+// coef[b] from s[b]; status[b] bit 0 when s_b is not finite or not > 0 (all coefficients NaN).
+hipError_t launch_coef(const float* s, int64_t N, float* coef, int32_t* status, hipStream_t stream);
+
+// Fill n floats / int32 with a value (a kernel, never a memset node).
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+// monitor[i] <- sqrt(monitor[i]) / sqrt(B)
+hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t stream);
+
+// Scaling kernels.
+hipError_t launch_frobenius(const float* A, int64_t N, int B, float* s, hipStream_t stream);
+struct PowerPlan {
+  int64_t N;
+  int B, k, steps;
+  dash_prec prec;
+  const float* A;
+  const float* V0;
+  float* s;
+  // workspace pieces
+  float* W[2];       // [N, B, 32] fp32 iterates
+  float* part[2];    // [N, B/128, 3, 32] partial column sums
+  float* v0inv;      // [32] inverse norms of the start vectors
+  float* coef;       // [N, COEF_STRIDE] (prescale for binary16)
+  _Float16* Ah;      // [N, B, B] binary16 operand (prec == DASH_FP16)
+};
+hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
+size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
+
+// Stack / unstack one weight: tiles (rows/B) x (cols/B) into consecutive blocks starting at `first`.
+hipError_t launch_tile_copy(const dash_mat& w, int B, float* stack, int64_t first, bool to_stack,
+                            const float* from_stack, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace dash

@@ -1,0 +1,190 @@
+// elementwise.hip -- HBM-bound kernels around the products: per-block coefficients, affine
+// identity combinations (solver start terms, casts, unscaling), fills, and stack/unstack copies.
+//
+// All of them stream 16-byte vectors with consecutive lanes on consecutive addresses.
+#include <hip/hip_runtime.h>
+
+#include "dash_internal.hpp"
+
+namespace dash {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// coef row of block b from s_b.  The roots are taken in double so that a power-of-two change of
+// s changes every coefficient by the exact power of two (scale equivariance of the solvers).
+__global__ void coef_kernel(const float* s, int64_t N, float* coef, int32_t* status) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= N) return;
+  const float sv = s[b];
+  float* c = coef + b * COEF_STRIDE;
+  if (!(isfinite(sv) && sv > 0.f)) {
+    const float nan = __builtin_nanf("");
+    for (int q = 0; q < COEF_STRIDE; ++q) c[q] = nan;
+    if (status) atomicOr(&status[b], 1);
+    return;
+  }
+  const double sd = (double)sv;
+  const double r1 = 1.0 / sd;
+  const double u = 1.0 / sqrt(sqrt(sd));
+  c[CO_R1] = (float)r1;
+  c[CO_R2] = (float)(r1 * r1);
+  c[CO_U] = (float)u;
+  c[CO_SQ] = (float)sqrt(sd);
+  c[CO_R1U] = (float)(r1 * u);
+  c[CO_P2] = 1.f;
+  c[CO_P2INV] = 1.f;
+  c[7] = 0.f;
+}
+
+__device__ __forceinline__ float co(const float* coef, int idx, int64_t b) {
+  return idx >= 0 ? coef[b * COEF_STRIDE + idx] : 1.f;
+}
+
+__device__ __forceinline__ void store4(void* D, dash_prec p, int64_t e, f32x4 v) {
+  if (p == DASH_FP32) {
+    *(f32x4*)((float*)D + e) = v;
+  } else {
+    f16x4 hv;
+    hv[0] = (_Float16)v[0];
+    hv[1] = (_Float16)v[1];
+    hv[2] = (_Float16)v[2];
+    hv[3] = (_Float16)v[3];
+    *(f16x4*)((_Float16*)D + e) = hv;
+  }
+}
+
+// One workgroup = 256 threads x 4 vectors of 4 = 4096 consecutive elements of one block.
+constexpr int AFF_CHUNK = 4096;
+
+__global__ __launch_bounds__(256) void affine_kernel(Affine op, int64_t N, int B) {
+  const int64_t chunks = (int64_t)B * B / AFF_CHUNK;
+  const int64_t b = blockIdx.x / chunks;
+  const int64_t c = blockIdx.x - b * chunks;
+  const int64_t base = b * (int64_t)B * B + c * AFF_CHUNK;
+  const float a = op.a * co(op.coef, op.ia, b), g = op.g * co(op.coef, op.ig, b);
+  const float a2 = op.a2 * co(op.coef, op.ia2, b), g2 = op.g2 * co(op.coef, op.ig2, b);
+  float mon = 0.f;
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t e = base + 4 * (threadIdx.x + 256 * r);   // element index within the stack
+    const int64_t in_blk = e - b * (int64_t)B * B;
+    const int row = (int)(in_blk / B), col = (int)(in_blk % B);
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (op.X) x = *(const f32x4*)(op.X + e);
+    f32x4 v, v2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool diag = (row == col + q);
+      v[q] = (op.X ? a * x[q] : 0.f) + (diag ? g : 0.f);
+      v2[q] = (op.X ? a2 * x[q] : 0.f) + (diag ? g2 : 0.f);
+      bad |= !isfinite(v[q]);
+      if (op.monitor) {
+        const float d = v[q] - (diag ? 1.f : 0.f);
+        mon += d * d;
+      }
+    }
+    store4(op.D, op.d_prec, e, v);
+    if (op.D2) {
+      store4(op.D2, op.d2_prec, e, v2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bad |= !isfinite(v2[q]);
+    }
+  }
+  if (op.monitor) {
+    mon = wave_sum(mon);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&op.monitor[b * op.mon_stride], op.mon_mul * mon);
+  }
+  if (op.status && bad) atomicOr(&op.status[b], 2);
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void monitor_finish_kernel(float* m, int64_t n, float inv_sqrt_b) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) m[i] = sqrtf(m[i]) * inv_sqrt_b;
+}
+
+// Copy one weight's tiles to (to_stack) or from the stack.  Workgroup = 8 rows of one tile.
+__global__ __launch_bounds__(256) void tile_copy_kernel(float* w, int64_t rows, int64_t cols, int64_t ld, int B,
+                                                        float* stack, const float* from_stack, int64_t first,
+                                                        int to_stack) {
+  const int64_t tiles_c = cols / B;
+  const int row_groups = B / 8;
+  const int64_t t = blockIdx.x / row_groups;
+  const int rg = (int)(blockIdx.x - t * row_groups);
+  const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
+  const int vec_per_row = B / 4;
+  for (int v = threadIdx.x; v < 8 * vec_per_row; v += 256) {
+    const int r = rg * 8 + v / vec_per_row;
+    const int c4 = v % vec_per_row;
+    float* wp = w + (tr * B + r) * ld + tc * B + 4 * c4;
+    const int64_t so = (first + t) * (int64_t)B * B + (int64_t)r * B + 4 * c4;
+    if (to_stack)
+      *(f32x4*)(stack + so) = *(const f32x4*)wp;
+    else
+      *(f32x4*)wp = *(const f32x4*)(from_stack + so);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_coef(const float* s, int64_t N, float* coef, int32_t* status, hipStream_t stream) {
+  hipLaunchKernelGGL(coef_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, s, N, coef, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_affine(const Affine& op, int64_t N, int B, hipStream_t stream) {
+  const int64_t grid = N * ((int64_t)B * B / AFF_CHUNK);
+  if ((int64_t)B * B % AFF_CHUNK != 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(affine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, op, N, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(monitor_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, monitor, n,
+                     (float)(1.0 / sqrt((double)B)));
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_copy(const dash_mat& w, int B, float* stack, int64_t first, bool to_stack,
+                            const float* from_stack, hipStream_t stream) {
+  const int64_t tiles = (w.rows / B) * (w.cols / B);
+  if (tiles == 0) return hipSuccess;
+  const int64_t grid = tiles * (B / 8);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w.ptr, w.rows, w.cols, w.ld, B,
+                     stack, from_stack, first, to_stack ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace dash

@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU parity tests (host-side arithmetic is fp64 numpy, never the GPU path)."""
+import numpy as np
+import torch
+
+import matrix_inverse_roots_amd as dash
+
+DEV = torch.device("cuda:0")
+
+# gates (fp32: residual 1e-3 and iterate parity 1e-4; fp16 operands: residual 5e-3)
+R_FP32 = 1e-3
+R_FP16 = 5e-3
+ITERATE_TOL = 1e-4
+
+
+def to_dev(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def to_host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rel_err(X, R):
+    """per-block ||X - R||_F / ||R||_F"""
+    X, R = np.asarray(X, np.float64), np.asarray(R, np.float64)
+    if X.ndim == 2:
+        X, R = X[None], R[None]
+    return np.linalg.norm(X - R, axis=(1, 2)) / np.linalg.norm(R, axis=(1, 2))
+
+
+def residual(X, A):
+    """per-block ||X^4 A - I||_F / sqrt(B), in fp64 on the host"""
+    X, A = np.asarray(X, np.float64), np.asarray(A, np.float64)
+    if X.ndim == 2:
+        X, A = X[None], A[None]
+    B = A.shape[-1]
+    X2 = X @ X
+    return np.linalg.norm(X2 @ X2 @ A - np.eye(B), axis=(1, 2)) / np.sqrt(B)
+
+
+def power_scale(A, V0, steps=10, prec=dash.DASH_FP32):
+    N, B = A.shape[0], A.shape[1]
+    s = torch.empty(N, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, prec, V0.shape[1], device=DEV)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prec, V0.shape[1], steps, V0, s, ws)
+    return s
+
+
+def frob_scale(A):
+    N, B = A.shape[0], A.shape[1]
+    s = torch.empty(N, device=DEV)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None)
+    return s
+
+
+def ndb(A, s, it1, it2, want_sqrt=False, want_monitor=False):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    R = torch.empty_like(A) if want_sqrt else None
+    mon = torch.empty((N, it1 + it2), device=DEV) if want_monitor else None
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=DEV)
+    dash.dash_inverse_root_ndb(A, s, N, B, it1, it2, X, sqrt_out=R, monitor=mon, status=status, ws=ws)
+    return X, R, mon, status
+
+
+def cn(A, s, iters, prec=dash.DASH_FP32, want_monitor=False):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    mon = torch.empty((N, iters), device=DEV) if want_monitor else None
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=DEV)
+    dash.dash_inverse_root_cn(A, s, N, B, 4, iters, prec, X, monitor=mon, status=status, ws=ws)
+    return X, mon, status
+
+
+def cheb(A, s, degree, lo, hi):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=DEV)
+    dash.dash_inverse_root_cheb(A, s, N, B, degree, lo, hi, X, status=status, ws=ws)
+    return X, status

@@ -1,0 +1,160 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every declared call, and
+rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_inverse_roots_amd as dash
+from matrix_inverse_roots_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dash.h")
+
+# fake, well aligned device addresses: argument checks run before any use of them
+P = 1 << 20
+P2 = 2 << 20
+P3 = 3 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dash_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_call():
+    lib = ctypes.CDLL(_lib.library_path)
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(dash, n), n  # the binding mirrors every name
+
+
+def test_version_and_status_strings():
+    assert dash.dash_abi_version() == 1
+    for code in range(6):
+        assert dash.dash_status_string(code)
+    assert dash.dash_status_string(99) == "unknown status"
+
+
+def test_product_counts():
+    assert dash.dash_solver_products(dash.DASH_OP_NDB, 6, 6) == 30
+    assert dash.dash_solver_products(dash.DASH_OP_NDB, 1, 1) == 1
+    assert dash.dash_solver_products(dash.DASH_OP_CN, 5) == 16
+    assert dash.dash_solver_products(dash.DASH_OP_CN, 1) == 0
+    assert dash.dash_solver_products(dash.DASH_OP_CHEB, 24) == 23
+    assert dash.dash_solver_products(dash.DASH_OP_NDB, 0, 3) == -1
+
+
+def test_workspace_sizes():
+    N, B = 16, 256
+    stack32 = N * B * B * 4
+    assert dash.dash_workspace_size(dash.DASH_OP_NDB, N, B) >= 5 * stack32
+    assert dash.dash_workspace_size(dash.DASH_OP_CN, N, B, dash.DASH_FP16) >= 5 * stack32 // 2
+    assert dash.dash_workspace_size(dash.DASH_OP_CN, N, B, dash.DASH_FP16) < 5 * stack32
+    assert dash.dash_workspace_size(dash.DASH_OP_CHEB, N, B) >= 2 * stack32
+    assert dash.dash_workspace_size(dash.DASH_OP_APPLY, N, B) >= stack32
+    assert dash.dash_workspace_size(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 0) == 0
+    assert dash.dash_workspace_size(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, 32) > N * B * B * 2
+    for bad_B in (0, 32, 100, 8256):
+        with pytest.raises(dash.DashError) as ei:
+            dash.dash_workspace_size(dash.DASH_OP_NDB, N, bad_B)
+        assert ei.value.status == _lib.DASH_ERR_SHAPE
+    with pytest.raises(dash.DashError):
+        dash.dash_workspace_size(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 33)
+
+
+def _status_of(fn, *args, **kw):
+    with pytest.raises(dash.DashError) as ei:
+        fn(*args, stream=0, **kw)
+    return ei.value.status
+
+
+class FakeWs:
+    """Stands in for a workspace tensor: a pointer and a byte count."""
+
+    def __init__(self, ptr, nbytes):
+        self.ptr, self.n = ptr, nbytes
+
+    def data_ptr(self):
+        return self.ptr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def test_ndb_argument_errors():
+    N, B = 4, 64
+    ws = FakeWs(P3, dash.dash_workspace_size(dash.DASH_OP_NDB, N, B))
+    f = dash.dash_inverse_root_ndb
+    assert _status_of(f, None, P2, N, B, 5, 5, P, ws=ws) == _lib.DASH_ERR_INVALID_ARG      # null A
+    assert _status_of(f, P + 4, P2, N, B, 5, 5, P, ws=ws) == _lib.DASH_ERR_INVALID_ARG     # misaligned
+    assert _status_of(f, P, P2, N, B, 5, 5, P, ws=ws) == _lib.DASH_ERR_INVALID_ARG         # X aliases A
+    assert _status_of(f, P, P2, N, B, 0, 5, P3, ws=ws) == _lib.DASH_ERR_INVALID_ARG        # iters < 1
+    assert _status_of(f, P, P2, 0, B, 5, 5, P3, ws=ws) == _lib.DASH_ERR_INVALID_ARG        # N < 1
+    assert _status_of(f, P, P2, N, 96, 5, 5, P3, ws=ws) == _lib.DASH_ERR_SHAPE             # B % 64
+    small = FakeWs(P3, ws.n - 1)
+    assert _status_of(f, P, P2, N, B, 5, 5, 5 * P, ws=small) == _lib.DASH_ERR_WORKSPACE
+    assert _status_of(f, P, P2, N, B, 5, 5, 5 * P, ws=FakeWs(P3 + 16, ws.n)) == _lib.DASH_ERR_WORKSPACE
+
+
+def test_cn_cheb_scale_apply_stats_argument_errors():
+    N, B = 4, 64
+    ws = FakeWs(P3, 1 << 30)
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 2, 5, dash.DASH_FP32, 5 * P,
+                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                   # p != 4
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 0, dash.DASH_FP32, 5 * P,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 3, 7, 5 * P,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG                                   # bad precision
+    f = dash.dash_inverse_root_cheb
+    assert _status_of(f, P, P2, N, B, 0, 0.1, 1.0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, N, B, 65, 0.1, 1.0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, N, B, 8, 0.0, 1.0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, N, B, 8, 1.0, 1.0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, N, B, 8, 0.1, float("inf"), 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    g = dash.dash_scale
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 33, 10, P2, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG                                   # k > 32
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 0, 10, P2, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 0, P2, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 10, None, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG                                   # V0 missing
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 10, P2, P3,
+                      ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
+    assert _status_of(g, P, N, B, 5, dash.DASH_FP32, 8, 10, P2, P3, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    a = dash.dash_apply
+    assert _status_of(a, P, P2, P3, N, B, P, ws=ws) == _lib.DASH_ERR_INVALID_ARG            # U aliases XL
+    assert _status_of(a, P, P2, P3, N, B, 5 * P, ws=FakeWs(8 * P, 10)) == _lib.DASH_ERR_WORKSPACE
+    u = dash.dash_update_stats
+    assert _status_of(u, P, N, B, 1.5, P2) == _lib.DASH_ERR_INVALID_ARG                     # beta > 1
+    assert _status_of(u, P, N, B, float("nan"), P2) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(u, P, N, 48, 0.9, P2) == _lib.DASH_ERR_SHAPE
+
+
+class FakeMat:
+    def __init__(self, ptr, rows, cols, ld=None):
+        self.ptr, self.shape, self._ld = ptr, (rows, cols), ld if ld is not None else cols
+
+    def data_ptr(self):
+        return self.ptr
+
+    def stride(self, d):
+        return self._ld if d == 0 else 1
+
+
+def test_stack_argument_errors():
+    B = 64
+    assert _status_of(dash.dash_stack, [FakeMat(P, 128, 96)], B, P2) == _lib.DASH_ERR_SHAPE
+    assert _status_of(dash.dash_stack, [FakeMat(P, 128, 128, ld=64)], B, P2) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_stack, [FakeMat(P + 8, 128, 128)], B, P2) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_stack, [FakeMat(P, 128, 128)], B, None) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_unstack, P2, B, [FakeMat(P, 64, 130, ld=132)]) == _lib.DASH_ERR_SHAPE

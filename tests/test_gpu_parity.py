@@ -1,0 +1,307 @@
+"""GPU parity of every hot-path call against the CPU oracle, on the tiny (4 x 64 x 64) and the
+conditioned (16 x 256 x 256, kappa 1e4) stacks, plus ragged tile shapes and edge cases.
+
+Gates: fp32 iterate parity max_i ||X_gpu - X_oracle||_F / ||X_oracle||_F <= 1e-4 with the SAME scale
+s fed to both sides; residual ||X^4 A - I||_F / sqrt(B) <= 1e-3 (fp32) and <= 5e-3 (fp16 operands)
+evaluated in fp64 on the host.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dash_inputs as di
+import matrix_inverse_roots_amd as dash
+import oracle
+from gpu_helpers import (DEV, ITERATE_TOL, R_FP16, R_FP32, cheb, cn, frob_scale, ndb, power_scale, rel_err,
+                         residual, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    A = di.tiny_stack()
+    return A, to_dev(A)
+
+
+@pytest.fixture(scope="module")
+def conditioned():
+    A, Q, lam = di.conditioned_stack()
+    return A, to_dev(A)
+
+
+# ------------------------------------------------------------------------------------------------
+# scaling
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k,steps", [(32, 10), (7, 3), (1, 1), (32, 1)])
+def test_power_scale_tiny(tiny, k, steps):
+    A, Ad = tiny
+    V0 = di.start_vectors(A.shape[1], k)
+    s = to_host(power_scale(Ad, to_dev(V0), steps))
+    s_ref, _ = oracle.mpi(A, V0, steps)
+    assert np.max(np.abs(s - s_ref) / s_ref) < 1e-5
+
+
+def test_power_scale_conditioned_fp32_and_fp16(conditioned):
+    A, Ad = conditioned
+    V0 = di.start_vectors(256, 32)
+    s = to_host(power_scale(Ad, to_dev(V0), 10))
+    s_ref, _ = oracle.mpi(A, V0, 10)
+    assert np.max(np.abs(s - s_ref) / s_ref) < 1e-5
+    s16 = to_host(power_scale(Ad, to_dev(V0), 10, dash.DASH_FP16))
+    s16_ref, _ = oracle.mpi(A, V0, 10, half=True)
+    assert np.max(np.abs(s16 - s16_ref) / s16_ref) < 2e-3
+    assert np.max(np.abs(s16 - s_ref) / s_ref) < 2e-3
+
+
+def test_frobenius(tiny, conditioned):
+    for A, Ad in (tiny, conditioned):
+        s = to_host(frob_scale(Ad))
+        assert np.max(np.abs(s - oracle.frobenius(A)) / oracle.frobenius(A)) < 1e-6
+
+
+# ------------------------------------------------------------------------------------------------
+# Newton-Denman-Beavers
+# ------------------------------------------------------------------------------------------------
+
+def test_ndb_tiny_full_stack(tiny):
+    A, Ad = tiny
+    V0 = di.start_vectors(64, 32)
+    s = power_scale(Ad, to_dev(V0), 10)
+    X, R, mon, status = ndb(Ad, s, 20, 20, want_sqrt=True, want_monitor=True)
+    s_h = to_host(s)
+    X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, s_h, 20, 20, want_sqrt=True)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(rel_err(to_host(R), R_ref)) < ITERATE_TOL
+    assert np.max(residual(to_host(X), A)) < R_FP32
+    assert np.all(to_host(status) == 0)
+    m = to_host(mon)
+    big = mon_ref > 1e-3  # below that the monitor is at fp32 rounding level
+    assert np.max(np.abs(m[big] - mon_ref[big]) / mon_ref[big]) < 1e-3
+    assert np.all(m[~big] < 2e-3)
+
+
+@pytest.mark.parametrize("scaling", ["power", "frobenius"])
+def test_ndb_conditioned(conditioned, scaling):
+    A, Ad = conditioned
+    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    T = 16 if scaling == "power" else 18
+    X, _, _, status = ndb(Ad, s, T, T)
+    X_ref, _, _ = oracle.ndb_inverse_root(A, to_host(s), T, T)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(residual(to_host(X), A)) < R_FP32
+    assert np.all(to_host(status) == 0)
+
+
+@pytest.mark.parametrize("it1,it2", [(1, 1), (1, 3), (2, 1), (3, 2)])
+def test_ndb_few_steps_match_oracle_iterates(tiny, it1, it2):
+    A, Ad = tiny
+    s = frob_scale(Ad)
+    X, R, mon, _ = ndb(Ad, s, it1, it2, want_sqrt=True, want_monitor=True)
+    X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, to_host(s), it1, it2, want_sqrt=True)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(rel_err(to_host(R), R_ref)) < ITERATE_TOL
+    assert np.max(np.abs(to_host(mon) - mon_ref) / mon_ref) < 1e-3
+
+
+# ------------------------------------------------------------------------------------------------
+# Coupled Newton
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scaling", ["power", "frobenius"])
+def test_cn_conditioned(conditioned, scaling):
+    A, Ad = conditioned
+    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    T = 16
+    X, mon, status = cn(Ad, s, T, want_monitor=True)
+    X_ref, mon_ref = oracle.cn_inverse_root(A, to_host(s), T)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(residual(to_host(X), A)) < R_FP32
+    assert np.all(to_host(status) == 0)
+    m = to_host(mon)
+    big = mon_ref > 1e-3
+    assert np.max(np.abs(m[big] - mon_ref[big]) / mon_ref[big]) < 1e-3
+
+
+@pytest.mark.parametrize("iters", [1, 2, 3, 6])
+def test_cn_few_steps_match_oracle_iterates(tiny, iters):
+    A, Ad = tiny
+    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10)
+    X, mon, _ = cn(Ad, s, iters, want_monitor=True)
+    X_ref, mon_ref = oracle.cn_inverse_root(A, to_host(s), iters)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(np.abs(to_host(mon) - mon_ref) / mon_ref) < 1e-3
+
+
+def test_cn_fp16_tiny(tiny):
+    A, Ad = tiny
+    V0 = to_dev(di.start_vectors(64, 32))
+    s = power_scale(Ad, V0, 10, dash.DASH_FP16)
+    X, _, status = cn(Ad, s, 8, dash.DASH_FP16)
+    Xh = to_host(X)
+    assert np.max(residual(Xh, A)) < R_FP16
+    X_emul, _ = oracle.cn_inverse_root(A, to_host(s), 8, half_storage=True)
+    assert np.max(rel_err(Xh, X_emul)) < 5e-3
+    assert np.all(to_host(status) == 0)
+
+
+# ------------------------------------------------------------------------------------------------
+# Chebyshev / Clenshaw
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("degree", [1, 2, 3, 8, 24])
+def test_cheb_tiny(tiny, degree):
+    A, Ad = tiny
+    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10)
+    lo, hi = 0.02, 1.25
+    X, status = cheb(Ad, s, degree, lo, hi)
+    X_ref = oracle.cheb_inverse_root(A, to_host(s), degree, lo, hi)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.all(to_host(status) == 0)
+
+
+def test_cheb_known_spectrum_accuracy():
+    A64, Q, lam = di.known_spectrum_stack(81, 4, 128, 0.05, 1.0)
+    A = A64.astype(np.float32)
+    Ad = to_dev(A)
+    s = torch.ones(4, device=DEV)
+    X, _ = cheb(Ad, s, 24, 0.04, 1.1)
+    X_ref = oracle.cheb_inverse_root(A, 1.0, 24, 0.04, 1.1)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(residual(to_host(X), A)) < R_FP32
+
+
+# ------------------------------------------------------------------------------------------------
+# statistics, apply, stacking (ragged tile shapes: B = 64, 192, 320 use the 64-wide tiles)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [64, 128, 192, 320])
+def test_apply_matches_oracle(B):
+    NG = 3
+    XL, XR, G = (di.gaussian((NG, B, B), seed) for seed in (91, 92, 93))
+    U = torch.empty((NG, B, B), device=DEV)
+    ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
+    dash.dash_apply(to_dev(XL), to_dev(XR), to_dev(G), NG, B, U, ws)
+    U_ref = oracle.apply(XL, G, XR)
+    assert np.max(rel_err(to_host(U), U_ref)) < 1e-5
+
+
+def test_apply_identity_is_exact():
+    NG, B = 2, 128
+    G = di.gaussian((NG, B, B), 94)
+    I = torch.eye(B, device=DEV).expand(NG, B, B).contiguous()
+    U = torch.empty((NG, B, B), device=DEV)
+    ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
+    dash.dash_apply(I, I, to_dev(G), NG, B, U, ws)
+    assert np.array_equal(to_host(U), G.astype(np.float64))
+
+
+@pytest.mark.parametrize("B", [64, 192, 256])
+def test_update_stats_integers_exact_and_symmetric(B):
+    NG = 2
+    g = di.rng(95)
+    G = g.integers(-3, 4, (NG, B, B)).astype(np.float32)
+    L0 = g.integers(-4, 5, (NG, B, B)).astype(np.float32)
+    L0 = L0 + L0.transpose(0, 2, 1)
+    R0 = g.integers(-4, 5, (NG, B, B)).astype(np.float32)
+    R0 = R0 + R0.transpose(0, 2, 1)
+    A = to_dev(np.concatenate([L0, R0]))
+    dash.dash_update_stats(to_dev(G), NG, B, 0.5, A)
+    out = to_host(A)
+    L_ref, R_ref = oracle.update_stats(G, 0.5, L0, R0)
+    assert np.array_equal(out[:NG], L_ref) and np.array_equal(out[NG:], R_ref)
+
+
+def test_update_stats_gaussian():
+    NG, B = 3, 256
+    G = di.gaussian((NG, B, B), 96, 1e-3)
+    L0 = di.tiny_stack(seed=97, N=NG, B=B) * 1e-6
+    R0 = di.tiny_stack(seed=98, N=NG, B=B) * 1e-6
+    A = to_dev(np.concatenate([L0, R0]))
+    dash.dash_update_stats(to_dev(G), NG, B, 0.95, A)
+    out = to_host(A)
+    L_ref, R_ref = oracle.update_stats(G, 0.95, L0, R0)
+    assert np.max(rel_err(out[:NG], L_ref)) < 1e-5 and np.max(rel_err(out[NG:], R_ref)) < 1e-5
+    assert np.array_equal(out, out.transpose(0, 2, 1))
+
+
+def test_stack_unstack_round_trip():
+    B = 64
+    shapes = [(128, 192), (64, 64), (192, 128)]
+    W = [di.gaussian(s, 100 + i) for i, s in enumerate(shapes)]
+    Wd = [to_dev(w) for w in W]
+    n = di.num_tiles(shapes, B)
+    S = torch.empty((n, B, B), device=DEV)
+    dash.dash_stack(Wd, B, S)
+    assert np.array_equal(to_host(S), oracle.stack(W, B).astype(np.float64))
+    outs = [torch.zeros(s, device=DEV) for s in shapes]
+    dash.dash_unstack(S, B, outs)
+    for o, w in zip(outs, W):
+        assert np.array_equal(to_host(o), w.astype(np.float64))
+
+
+def test_stack_strided_rows():
+    B = 64
+    big = to_dev(di.gaussian((128, 256), 110))
+    view = big[:, 64:192]  # ld = 256, cols = 128
+    S = torch.empty((4, B, B), device=DEV)
+    dash.dash_stack([view], B, S)
+    assert np.array_equal(to_host(S), oracle.stack([to_host(view)], B))
+
+
+# ------------------------------------------------------------------------------------------------
+# invariants: scale equivariance, batch independence, determinism, per-block failure reporting
+# ------------------------------------------------------------------------------------------------
+
+def test_scale_equivariance_bitwise(tiny):
+    A, Ad = tiny
+    s = frob_scale(Ad)
+    X1, _, _, _ = ndb(Ad, s, 6, 6)
+    X16, _, _, _ = ndb(16 * Ad, 16 * s, 6, 6)
+    assert torch.equal(X16 * 2, X1)
+    C1, _, _ = cn(Ad, s, 6)
+    C16, _, _ = cn(16 * Ad, 16 * s, 6)
+    assert torch.equal(C16 * 2, C1)
+    H1, _ = cheb(Ad, s, 12, 0.02, 1.25)
+    H16, _ = cheb(16 * Ad, 16 * s, 12, 0.02, 1.25)
+    assert torch.equal(H16 * 2, H1)
+
+
+def test_batch_independence_and_determinism(conditioned):
+    _, Ad = conditioned
+    s = frob_scale(Ad)
+    X, _, _, _ = ndb(Ad, s, 8, 8)
+    X2, _, _, _ = ndb(Ad, s, 8, 8)
+    assert torch.equal(X, X2)
+    for i in (0, 7, 15):
+        Xi, _, _, _ = ndb(Ad[i:i + 1].contiguous(), s[i:i + 1].contiguous(), 8, 8)
+        assert torch.equal(Xi[0], X[i])
+    perm = torch.tensor([3, 1, 15, 0, 2, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14], device=DEV)
+    Xp, _, _ = cn(Ad[perm].contiguous(), s[perm].contiguous(), 6)
+    Xc, _, _ = cn(Ad, s, 6)
+    assert torch.equal(Xp, Xc[perm])
+
+
+def test_bad_blocks_are_flagged_and_isolated(tiny):
+    A, Ad = tiny
+    s = frob_scale(Ad).clone()
+    s[1] = 0.0
+    s[2] = float("nan")
+    X, _, _, status = ndb(Ad, s, 6, 6)
+    st = to_host(status).astype(int)
+    Xh = to_host(X)
+    assert st[0] == 0 and st[3] == 0
+    assert st[1] & 1 and st[2] & 1
+    assert np.all(np.isnan(Xh[1])) and np.all(np.isnan(Xh[2]))
+    X_ok, _, _, _ = ndb(Ad[[0, 3]].contiguous(), s[[0, 3]].contiguous(), 6, 6)
+    assert np.array_equal(to_host(X_ok), Xh[[0, 3]])
+    Xc, _, stc = cn(Ad, s, 5)
+    assert np.array_equal(to_host(stc).astype(int) & 1, [0, 1, 1, 0])
+    Xh, sth = cheb(Ad, s, 8, 0.02, 1.25)
+    assert np.array_equal(to_host(sth).astype(int) & 1, [0, 1, 1, 0])
+    # a non-finite input block: flagged as a non-finite output, neighbours untouched
+    bad = Ad.clone()
+    bad[0, 3, 5] = float("inf")
+    _, _, _, st2 = ndb(bad, frob_scale(Ad), 4, 4)
+    assert np.array_equal(to_host(st2).astype(int) & 2, [2, 0, 0, 0])
