@@ -112,8 +112,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   const int li = lane & 31, h = lane >> 5;
   float mon = 0.f;
   bool bad = false;
+  // One row of MFMA tiles at a time: all C/E loads of the chunk are issued before any store, so
+  // their latency is paid once per chunk (D may alias E: a lane reads and writes only its own
+  // elements, so loading the chunk first is still exact).
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+    float cv[MT][16], ev[MT][16];
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = tc.ti * TILE + wm * WT + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = tc.tj * TILE + wn * WT + nt * 32 + li;
+        const int64_t idx = (int64_t)i * B + j;
+        cv[nt][r] = C ? C[idx] : 0.f;
+        ev[nt][r] = E ? E[idx] : 0.f;
+      }
 #pragma unroll
     for (int nt = 0; nt < MT; ++nt)
 #pragma unroll
@@ -123,9 +137,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
         if (SYM && tc.ti == tc.tj && i > j) continue;
         const int64_t idx = (int64_t)i * B + j;
         const float x = acc[mt][nt][r];
-        float v = al * x;
-        if (C) v += be * C[idx];
-        if (E) v += de * E[idx];
+        float v = al * x + be * cv[nt][r] + de * ev[nt][r];
         if (i == j) v += ga;
         D[idx] = cvt_out<TO>(v);
         if (SYM && i != j) D[(int64_t)j * B + i] = cvt_out<TO>(v);
@@ -140,6 +152,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           mon += dd * dd;
         }
       }
+  }
   if (e.monitor) {
     mon = wave_sum(mon);
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
