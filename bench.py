@@ -48,6 +48,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
+    p.add_argument("--only", choices=["step", "cheb"], default="step",
+                   help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
+                        "(the run that HBM traffic counters are collected on)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
 
 
@@ -78,6 +83,8 @@ def traffic_record():
 
 def main():
     args = parse()
+    if args.traffic_from:
+        return traffic_from_counters(*args.traffic_from)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every block of the stack is independent, and multi-GPU runs "
               "are not part of this build (run with --gpus 1)", file=sys.stderr)
@@ -91,6 +98,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "cheb":
+        return only_cheb(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -161,13 +170,17 @@ def main():
     launch_ms = phase_ms["cheb"] / cheb_products
     achieved = flop_per_launch / (launch_ms * 1e-3) / 1e12
     rec = traffic_record()
-    traffic = None
+    traffic, traffic_detail = None, None
     if rec is not None:
-        traffic = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
-                   "algorithmic_bytes": 4.0 * B * B * N * 5, "source": "profiles/traffic.json"}
+        # algorithmic bytes of one Clenshaw product launch: read A, b_{k+1} (operand and C), b_{k+2};
+        # write b_k -- four fp32 stacks
+        traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        traffic_detail = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
+                          "algorithmic_bytes": 4.0 * B * B * N * 4, "source": "profiles/traffic.json"}
     roofline = {"kernel": PRODUCT_KERNEL, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                "traffic": traffic, "flop_per_launch": flop_per_launch, "avg_launch_ms": round(launch_ms, 3)}
+                "traffic": traffic, "traffic_detail": traffic_detail, "flop_per_launch": flop_per_launch,
+                "avg_launch_ms": round(launch_ms, 3)}
 
     step_flop = (cheb_products * 2.0 * B ** 3 * N          # Clenshaw products
                  + 2 * NG * B * B * (B + 64)                # triangle-only statistics, 128-wide tiles
@@ -217,6 +230,68 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+REF_COPY_BYTES = 4 << 30  # dash_stack of 64 weights of 4096 x 4096 fp32: reads and writes 4 GiB
+
+
+def only_cheb(dash, di, torch, dev):
+    """The run that HBM traffic counters are collected on: a plain copy of known size (dash_stack of
+    4 GiB, float4 loads and stores like the product kernel) and then one degree-24 Clenshaw solve on
+    the N=3072, B=1024 stack."""
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    s = torch.empty(N, device=dev)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    lo = BETA * EPS / float(s.max().item())
+    del ws
+    X = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=dev)
+    ref = [torch.ones((4096, 4096), device=dev) for _ in range(REF_COPY_BYTES // (4096 * 4096 * 4))]
+    ref_stack = torch.empty((REF_COPY_BYTES // (B * B * 4), B, B), device=dev)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    dash.dash_stack(ref, B, ref_stack)
+    e[1].record()
+    dash.dash_inverse_root_cheb(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, X, ws=ws)
+    e[2].record()
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "cheb", "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
+                      "ref_copy_ms": round(e[0].elapsed_time(e[1]), 3), "cheb_ms": round(e[1].elapsed_time(e[2]), 3),
+                      "products": dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)}), flush=True)
+
+
+def traffic_from_counters(fetch_csv, write_csv):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of `bench.py --only cheb`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads for
+    the 4 GiB reference copy (the tile_copy dispatches of dash_stack in the same run)."""
+    import csv
+
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        ref = sum(float(r["Counter_Value"]) for r in rows if "tile_copy_kernel" in r["Kernel_Name"]) * 1024
+        gemm = [float(r["Counter_Value"]) * 1024 for r in rows
+                if "gemm_f32_kernel<128, 0, 0, false, float>" in r["Kernel_Name"]]
+        factor = REF_COPY_BYTES / ref
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[key + "_raw_bytes_per_launch"] = sum(gemm) / len(gemm)
+        out[key + "_scale_factor"] = factor
+        out[key + "_bytes_per_launch"] = factor * sum(gemm) / len(gemm)
+        out[key + "_launches"] = len(gemm)
+    src = os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", "gemm.hip")
+    out["gemm_source_sha256"] = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    out["kernel"] = PRODUCT_KERNEL
+    out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb; "
+                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
@@ -281,7 +356,7 @@ def cpu_baseline(di, np, torch, A, V0, lo, args):
     import oracle
 
     threads = cpu_threads()
-    K = args.cpu_blocks or threads
+    K = args.cpu_blocks or 2 * threads
     idx = np.linspace(0, A.shape[0] - 1, K).astype(int)
     A_h = A[torch.from_numpy(idx).to(A.device)].cpu().numpy().astype(np.float64)
     V0_h = V0.cpu().numpy().astype(np.float64)

@@ -1,0 +1,142 @@
+"""GPU checks at the full benchmark size (N=3072 blocks of 1024 x 1024, the launch configuration that
+bench.py times): sampled blocks against the oracle one by one, plus properties that hold for every
+block (the residual ||X^4 A - I||_F / sqrt(B), checked on the GPU with torch products)."""
+import numpy as np
+import pytest
+import torch
+
+import dash_inputs as di
+import matrix_inverse_roots_amd as dash
+import oracle
+from gpu_helpers import DEV, ITERATE_TOL, R_FP16, R_FP32, rel_err, residual
+
+pytestmark = pytest.mark.gpu
+
+B = 1024
+SHAPES = di.llama_weight_shapes()
+NG = di.num_tiles(SHAPES, B)
+N = 2 * NG
+SAMPLE = [0, 1535, 1536, 3071]       # first/last L block, first/last R block
+ORACLE_SAMPLE = [17, 2900]            # blocks recomputed by the fp64 oracle
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def residual_all(X, A, chunk=128):
+    """max over all blocks of ||X^4 A - I||_F / sqrt(B), computed with torch fp32 products."""
+    worst = 0.0
+    eye = torch.eye(B, device=DEV)
+    for i in range(0, X.shape[0], chunk):
+        x = X[i:i + chunk]
+        x2 = torch.matmul(x, x)
+        r = torch.matmul(torch.matmul(x2, x2), A[i:i + chunk]) - eye
+        worst = max(worst, float((torch.linalg.matrix_norm(r) / B ** 0.5).max()))
+        del x2, r
+    return worst
+
+
+@pytest.fixture(scope="module")
+def stack():
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=DEV)
+    V0 = torch.from_numpy(di.start_vectors(B, 32)).to(DEV)
+    yield A, V0
+    del A
+    torch.cuda.empty_cache()
+
+
+def scale(A, V0, prec):
+    s = torch.empty(N, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, prec, 32, device=DEV)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prec, 32, 10, V0, s, ws)
+    return s
+
+
+def test_full_ndb_fp32(stack):
+    A, V0 = stack
+    s = scale(A, V0, dash.DASH_FP32)
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=DEV)
+    dash.dash_inverse_root_ndb(A, s, N, B, 6, 6, X, status=status, ws=ws)
+    del ws
+    torch.cuda.empty_cache()
+    assert int(status.abs().sum()) == 0
+    idx = SAMPLE + ORACLE_SAMPLE
+    A_h = host(A[idx])
+    s_h = host(s)[idx]
+    s_ref, _ = oracle.mpi(A_h, host(V0), 10)
+    assert np.max(np.abs(s_h - s_ref) / s_ref) < 1e-5
+    X_h = host(X[idx])
+    assert np.max(residual(X_h, A_h)) < R_FP32
+    k = len(SAMPLE)
+    X_ref, _, _ = oracle.ndb_inverse_root(A_h[k:], s_h[k:], 6, 6)
+    assert np.max(rel_err(X_h[k:], X_ref)) < ITERATE_TOL
+    assert residual_all(X, A) < R_FP32
+    del X
+    torch.cuda.empty_cache()
+
+
+def test_full_cn_fp16(stack):
+    A, V0 = stack
+    s = scale(A, V0, dash.DASH_FP16)
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_FP16, device=DEV)
+    dash.dash_inverse_root_cn(A, s, N, B, 4, 5, dash.DASH_FP16, X, status=status, ws=ws)
+    del ws
+    torch.cuda.empty_cache()
+    assert int(status.abs().sum()) == 0
+    idx = SAMPLE + ORACLE_SAMPLE
+    A_h = host(A[idx])
+    s_h = host(s)[idx]
+    s_ref, _ = oracle.mpi(A_h, host(V0), 10, half=True)
+    assert np.max(np.abs(s_h - s_ref) / s_ref) < 2e-3
+    assert np.max(residual(host(X[idx]), A_h)) < R_FP16
+    assert residual_all(X, A) < R_FP16
+    del X
+    torch.cuda.empty_cache()
+
+
+def test_full_step_chebyshev(stack):
+    """stack -> EMA stats -> power scale -> Chebyshev d=24 -> apply -> unstack on the full workload."""
+    A0, V0 = stack
+    A = A0.clone()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(di.SEED_GRADS)
+    grads = [torch.randn(sh, generator=gen, device=DEV) * 1e-3 for sh in SHAPES]
+    G = torch.empty((NG, B, B), device=DEV)
+    dash.dash_stack(grads, B, G)
+    # stacking: tile (tr, tc) of weight w sits at offset(w) + tr * cols/B + tc
+    assert torch.equal(G[0], grads[0][:B, :B]) and torch.equal(G[NG - 1], grads[-1][B:, -B:])
+    sample_t = [0, 700, NG - 1]
+    L_prev, R_prev = host(A[sample_t]), host(A[[NG + t for t in sample_t]])
+    dash.dash_update_stats(G, NG, B, 0.95, A)
+    L_ref, R_ref = oracle.update_stats(host(G[sample_t]), 0.95, L_prev, R_prev)
+    assert np.max(rel_err(host(A[sample_t]), L_ref)) < 1e-5
+    assert np.max(rel_err(host(A[[NG + t for t in sample_t]]), R_ref)) < 1e-5
+    s = scale(A, V0, dash.DASH_FP32)
+    lo = 0.95e-6 / float(s.max())
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=DEV)
+    dash.dash_inverse_root_cheb(A, s, N, B, 24, lo, 1.25, X, status=status, ws=ws)
+    del ws
+    assert int(status.abs().sum()) == 0
+    idx = ORACLE_SAMPLE
+    X_ref = oracle.cheb_inverse_root(host(A[idx]), host(s)[idx], 24, lo, 1.25)
+    assert np.max(rel_err(host(X[idx]), X_ref)) < ITERATE_TOL
+    U = torch.empty((NG, B, B), device=DEV)
+    ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
+    dash.dash_apply(X[:NG], X[NG:], G, NG, B, U, ws)
+    del ws
+    t = [3, NG - 2]
+    U_ref = oracle.apply(host(X[t]), host(G[t]), host(X[[NG + i for i in t]]))
+    assert np.max(rel_err(host(U[t]), U_ref)) < 1e-5
+    outs = [torch.empty(sh, device=DEV) for sh in SHAPES]
+    dash.dash_unstack(U, B, outs)
+    assert torch.equal(outs[0][:B, :B], U[0]) and torch.equal(outs[-1][B:, -B:], U[NG - 1])
+    del A, X, U, G, grads, outs
+    torch.cuda.empty_cache()
