@@ -92,9 +92,9 @@ __device__ __forceinline__ TO cvt_out(float v) {
 
 // Shared epilogue for a wave holding MT x MT accumulators of 32 x 32 (layout of the 32x32 MFMA
 // family: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32).
-template <int MT, int WT, bool SYM, typename TO>
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_CE = true>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
-                                         const f32x16 (&acc)[MT][MT], int wm, int wn, int lane, int TILE) {
+                                         const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, int TILE) {
   const Epilogue& e = a.epi;
   const int B = a.B;
   const int64_t b = tc.b;
@@ -116,24 +116,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   // their latency is paid once per chunk (D may alias E: a lane reads and writes only its own
   // elements, so loading the chunk first is still exact).
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float cv[MT][16], ev[MT][16];
+  for (int mt = 0; mt < MTM; ++mt) {
+    float cv[MTN][16], ev[MTN][16];
 #pragma unroll
-    for (int nt = 0; nt < MT; ++nt)
+    for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = tc.ti * TILE + wm * WT + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int j = tc.tj * TILE + wn * WT + nt * 32 + li;
+        const int i = tc.ti * TILE + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = tc.tj * TILE + wn * WTN + nt * 32 + li;
         const int64_t idx = (int64_t)i * B + j;
-        cv[nt][r] = C ? C[idx] : 0.f;
-        ev[nt][r] = E ? E[idx] : 0.f;
+        cv[nt][r] = (HAS_CE && C) ? C[idx] : 0.f;
+        ev[nt][r] = (HAS_CE && E) ? E[idx] : 0.f;
       }
 #pragma unroll
-    for (int nt = 0; nt < MT; ++nt)
+    for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = tc.ti * TILE + wm * WT + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int j = tc.tj * TILE + wn * WT + nt * 32 + li;
+        const int i = tc.ti * TILE + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = tc.tj * TILE + wn * WTN + nt * 32 + li;
         if (SYM && tc.ti == tc.tj && i > j) continue;
         const int64_t idx = (int64_t)i * B + j;
         const float x = acc[mt][nt][r];
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, WT, SYM, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+  epilogue<MT, MT, WT, WT, SYM, TO>(a, tc, P, acc, wm, wn, lane, TILE);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -350,14 +350,116 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, WT, false, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+  epilogue<MT, MT, WT, WT, false, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+}
+
+
+// ------------------------------------------------------------------------------------------------
+// fp16 operands, 256 x 256 macro tile (B % 256 == 0).  Four waves as 2 x 2, wave tile 128 x 128
+// (4 x 4 accumulators of 32 x 32, held in the accumulation registers at one wave per SIMD).  Every
+// thread stages 8 pieces of the X slice (256 rows x 64 k, 16-byte loads) and one 8 (k) x 8 (n)
+// sub-block of the Y slice, loaded as eight 16-byte row pieces and transposed in registers, so both
+// LDS tiles hold rows of 64 consecutive k.  LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+// (row ^ row/8) & 7, which keeps both the MFMA reads (8 consecutive rows, one chunk) and the
+// transposed writes (rows 8 apart, one chunk) free of bank conflicts.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row ^ (row >> 3))) & 7; }
+
+template <typename TO>
+__global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
+  constexpr int TILE = 256, BK = 64, MT = 4, WT = 128;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][TILE * BK];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TILE * BK];
+
+  const TileCoord tc = decode_tile(a, false);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const _Float16* X = (const _Float16*)P.X + off;
+  const _Float16* Y = (const _Float16*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int kb = tid >> 5, nb = tid & 31;  // this thread's 8 x 8 sub-block of the Y slice
+
+  // X slice: 8 pieces of 16 bytes, piece c = tid + 256 r -> row c / 8, chunk c % 8.
+  // Y slice: k rows 8 kb .. 8 kb + 7, n columns 8 nb .. 8 nb + 7, transposed in registers.
+  f16x8 lx[8], ly[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      lx[r] = *(const f16x8*)(X + (int64_t)(i0 + (c >> 3)) * B + k0 + 8 * (c & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ly[q] = *(const f16x8*)(Y + (int64_t)(k0 + 8 * kb + q) * B + j0 + 8 * nb);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c >> 3;
+      *(f16x8*)&As[buf][row * BK + 8 * swz(row, c & 7)] = lx[r];
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      f16x8 col;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) col[q] = ly[q][n];
+      const int row = 8 * nb + n;
+      *(f16x8*)&Bs[buf][row * BK + 8 * swz(row, kb)] = col;
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int KT = B / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const _Float16* as = As[buf];
+    const _Float16* bs = Bs[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int chunk = 4 * h + s;
+      f16x8 av[MT], bv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * WT + mt * 32 + li;
+        av[mt] = *(const f16x8*)&as[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int nt = 0; nt < MT; ++nt) {
+        const int row = wn * WT + nt * 32 + li;
+        bv[nt] = *(const f16x8*)&bs[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<MT, MT, WT, WT, false, TO, false>(a, tc, P, acc, wm, wn, lane, TILE);
 }
 
 template <typename K>
-hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream, int threads = 256) {
   const int64_t grid = (int64_t)a.nprob * a.N * a.tiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -393,6 +495,12 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   a.N = N;
   a.B = B;
   a.epi = epi;
+  if (in_prec == DASH_FP16 && B % 256 == 0 && trans == Trans::NN && !sym) {
+    a.tdim = B / 256;
+    a.tiles = a.tdim * a.tdim;
+    if (out_prec == DASH_FP16) return launch(gemm_f16_big_kernel<_Float16>, a, stream);
+    return launch(gemm_f16_big_kernel<float>, a, stream);
+  }
   if (B % 128 == 0) return dispatch<128>(a, in_prec, out_prec, trans, sym, stream);
   return dispatch<64>(a, in_prec, out_prec, trans, sym, stream);
 }

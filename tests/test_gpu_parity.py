@@ -146,6 +146,23 @@ def test_cn_fp16_tiny(tiny):
     assert np.all(to_host(status) == 0)
 
 
+@pytest.mark.parametrize("B", [256, 512])
+def test_cn_fp16_wide_tiles(B):
+    """B % 256 == 0 runs the 256 x 256 fp16 product tile; compare with the binary16-storage oracle."""
+    A64, _, _ = di.known_spectrum_stack(120 + B, 3, B, 0.2, 1.0)  # kappa 5, like the Gram stacks
+    A = A64.astype(np.float32)
+    Ad = to_dev(A)
+    s = power_scale(Ad, to_dev(di.start_vectors(B, 32)), 10, dash.DASH_FP16)
+    X, mon, status = cn(Ad, s, 9, dash.DASH_FP16, want_monitor=True)
+    Xh = to_host(X)
+    assert np.max(residual(Xh, A)) < R_FP16
+    X_emul, mon_ref = oracle.cn_inverse_root(A, to_host(s), 9, half_storage=True)
+    assert np.max(rel_err(Xh, X_emul)) < 5e-3
+    assert np.all(to_host(status) == 0)
+    m = to_host(mon)
+    assert np.max(np.abs(m[:, :4] - mon_ref[:, :4]) / mon_ref[:, :4]) < 1e-2
+
+
 # ------------------------------------------------------------------------------------------------
 # Chebyshev / Clenshaw
 # ------------------------------------------------------------------------------------------------
