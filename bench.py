@@ -68,15 +68,24 @@ def cpu_threads():
     return max(1, n)
 
 
+PRODUCT_SOURCES = ("gemm_common.hpp", "gemm_f32.hip")
+
+
+def product_source_sha():
+    """sha256 over the sources of the fp32 product kernel (its epilogue and its body)."""
+    h = hashlib.sha256()
+    for name in PRODUCT_SOURCES:
+        h.update(open(os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record():
     """Measured HBM bytes per product launch, if recorded for the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", "gemm.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != sha:
+    if rec.get("product_source_sha256") != product_source_sha():
         return None
     return rec
 
@@ -283,8 +292,7 @@ def traffic_from_counters(fetch_csv, write_csv):
         out[key + "_scale_factor"] = factor
         out[key + "_bytes_per_launch"] = factor * sum(gemm) / len(gemm)
         out[key + "_launches"] = len(gemm)
-    src = os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", "gemm.hip")
-    out["gemm_source_sha256"] = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    out["product_source_sha256"] = product_source_sha()
     out["kernel"] = PRODUCT_KERNEL
     out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb; "
                       "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb")

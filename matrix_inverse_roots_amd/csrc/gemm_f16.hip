@@ -1,0 +1,215 @@
+// gemm_f16.hip -- batched B x B products with binary16 operands and fp32 accumulation on the
+// 32x32x16 fp16 MFMA (coupled Newton in half precision).
+#include <hip/hip_runtime.h>
+
+#include "gemm_common.hpp"
+
+namespace dash {
+namespace gemm {
+namespace {
+
+template <int TILE, typename TO>
+__global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
+  constexpr int BK = 64;
+  constexpr int WT = TILE / 2;
+  constexpr int MT = WT / 32;
+  constexpr int LD = BK + 8;  // As[m][k], Bs[n][k] (Y tile transposed)
+  constexpr int NL = TILE * BK / 8 / 256;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][TILE * LD];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TILE * LD];
+
+  const TileCoord tc = decode_tile(a, false);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const _Float16* X = (const _Float16*)P.X + off;
+  const _Float16* Y = (const _Float16*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+
+  f16x8 ra[NL], rb[NL];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int f = tid + 256 * r;
+      const int row = f / (BK / 8), c8 = f % (BK / 8);
+      ra[r] = *(const f16x8*)(X + (int64_t)(i0 + row) * B + k0 + 8 * c8);
+      const int krow = f / (TILE / 8), n8 = f % (TILE / 8);
+      rb[r] = *(const f16x8*)(Y + (int64_t)(k0 + krow) * B + j0 + 8 * n8);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int f = tid + 256 * r;
+      const int row = f / (BK / 8), c8 = f % (BK / 8);
+      *(f16x8*)&As[buf][row * LD + 8 * c8] = ra[r];
+      const int krow = f / (TILE / 8), n8 = f % (TILE / 8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Bs[buf][(8 * n8 + q) * LD + krow] = rb[r][q];
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int KT = B / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const _Float16* as = As[buf];
+    const _Float16* bs = Bs[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 av[MT], bv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) av[mt] = *(const f16x8*)&as[(wm * WT + mt * 32 + li) * LD + h * 32 + 8 * s];
+#pragma unroll
+      for (int nt = 0; nt < MT; ++nt) bv[nt] = *(const f16x8*)&bs[(wn * WT + nt * 32 + li) * LD + h * 32 + 8 * s];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<MT, MT, WT, WT, false, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+}
+
+
+// ------------------------------------------------------------------------------------------------
+// fp16 operands, 256 x 256 macro tile (B % 256 == 0).  Four waves as 2 x 2, wave tile 128 x 128
+// (4 x 4 accumulators of 32 x 32, held in the accumulation registers at one wave per SIMD).  Every
+// thread stages 8 pieces of the X slice (256 rows x 64 k, 16-byte loads) and one 8 (k) x 8 (n)
+// sub-block of the Y slice, loaded as eight 16-byte row pieces and transposed in registers, so both
+// LDS tiles hold rows of 64 consecutive k.  LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+// (row ^ row/8) & 7, which keeps both the MFMA reads (8 consecutive rows, one chunk) and the
+// transposed writes (rows 8 apart, one chunk) free of bank conflicts.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row ^ (row >> 3))) & 7; }
+
+template <typename TO>
+__global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
+  constexpr int TILE = 256, BK = 64, MT = 4, WT = 128;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][TILE * BK];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TILE * BK];
+
+  const TileCoord tc = decode_tile(a, false);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const _Float16* X = (const _Float16*)P.X + off;
+  const _Float16* Y = (const _Float16*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int kb = tid >> 5, nb = tid & 31;  // this thread's 8 x 8 sub-block of the Y slice
+
+  // X slice: 8 pieces of 16 bytes, piece c = tid + 256 r -> row c / 8, chunk c % 8.
+  // Y slice: k rows 8 kb .. 8 kb + 7, n columns 8 nb .. 8 nb + 7, transposed in registers.
+  f16x8 lx[8], ly[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      lx[r] = *(const f16x8*)(X + (int64_t)(i0 + (c >> 3)) * B + k0 + 8 * (c & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ly[q] = *(const f16x8*)(Y + (int64_t)(k0 + 8 * kb + q) * B + j0 + 8 * nb);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c >> 3;
+      *(f16x8*)&As[buf][row * BK + 8 * swz(row, c & 7)] = lx[r];
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      f16x8 col;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) col[q] = ly[q][n];
+      const int row = 8 * nb + n;
+      *(f16x8*)&Bs[buf][row * BK + 8 * swz(row, kb)] = col;
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int KT = B / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const _Float16* as = As[buf];
+    const _Float16* bs = Bs[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int chunk = 4 * h + s;
+      f16x8 av[MT], bv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * WT + mt * 32 + li;
+        av[mt] = *(const f16x8*)&as[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int nt = 0; nt < MT; ++nt) {
+        const int row = wn * WT + nt * 32 + li;
+        bv[nt] = *(const f16x8*)&bs[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<MT, MT, WT, WT, false, TO, false>(a, tc, P, acc, wm, wn, lane, TILE);
+}
+
+}  // namespace
+
+hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, hipStream_t stream) {
+  if (a.B % 256 == 0) {  // 256 x 256 tiles
+    a.tdim = a.B / 256;
+    a.tiles = a.tdim * a.tdim;
+    if (out_prec == DASH_FP16) return launch(gemm_f16_big_kernel<_Float16>, a, stream);
+    return launch(gemm_f16_big_kernel<float>, a, stream);
+  }
+  if (a.B % 128 == 0) {
+    a.tdim = a.B / 128;
+    a.tiles = a.tdim * a.tdim;
+    if (out_prec == DASH_FP16) return launch(gemm_f16_kernel<128, _Float16>, a, stream);
+    return launch(gemm_f16_kernel<128, float>, a, stream);
+  }
+  a.tdim = a.B / 64;
+  a.tiles = a.tdim * a.tdim;
+  if (out_prec == DASH_FP16) return launch(gemm_f16_kernel<64, _Float16>, a, stream);
+  return launch(gemm_f16_kernel<64, float>, a, stream);
+}
+
+}  // namespace gemm
+}  // namespace dash

@@ -1,0 +1,145 @@
+// gemm_f32.hip -- batched fp32 B x B products on the 32x32x2 fp32 MFMA.
+//
+// Workgroup = 4 waves (256 threads), macro tile TILE x TILE (128, or 64 when B is not a multiple of
+// 128), wave tile (TILE/2)^2, k-step 32, LDS double buffer with register prefetch of the next
+// k-slice.  Within one k-step, lane half h of an MFMA takes k = h*16 + s at step s, so each lane
+// reads 16 consecutive k of its X row with 128-bit LDS loads; the Y operand is a single float per
+// lane read straight from a row of the Y tile.  The statistics products read one operand
+// transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them.
+#include <hip/hip_runtime.h>
+
+#include "gemm_common.hpp"
+
+namespace dash {
+namespace gemm {
+namespace {
+
+template <int TILE, int TX, int TY, bool SYM, typename TO>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  constexpr int BK = 32;
+  constexpr int WT = TILE / 2;
+  constexpr int MT = WT / 32;
+  constexpr int LDA = BK + 4;    // As[m][k]
+  constexpr int LDB = TILE + 4;  // Bs[k][n]
+  constexpr int NL = TILE * BK / 4 / 256;
+  __shared__ __attribute__((aligned(16))) float As[2][TILE * LDA];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+
+  const TileCoord tc = decode_tile(a, SYM);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const float* X = (const float*)P.X + off;
+  const float* Y = (const float*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+
+  f32x4 ra[NL], rb[NL];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int f = tid + 256 * r;
+      if (!TX) {
+        const int row = f / (BK / 4), c4 = f % (BK / 4);
+        ra[r] = *(const f32x4*)(X + (int64_t)(i0 + row) * B + k0 + 4 * c4);
+      } else {  // X[i][k] = G[k][i]
+        const int krow = f / (TILE / 4), c4 = f % (TILE / 4);
+        ra[r] = *(const f32x4*)(X + (int64_t)(k0 + krow) * B + i0 + 4 * c4);
+      }
+      if (!TY) {
+        const int krow = f / (TILE / 4), c4 = f % (TILE / 4);
+        rb[r] = *(const f32x4*)(Y + (int64_t)(k0 + krow) * B + j0 + 4 * c4);
+      } else {  // Y[k][j] = G[j][k]
+        const int row = f / (BK / 4), c4 = f % (BK / 4);
+        rb[r] = *(const f32x4*)(Y + (int64_t)(j0 + row) * B + k0 + 4 * c4);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) {
+      const int f = tid + 256 * r;
+      if (!TX) {
+        const int row = f / (BK / 4), c4 = f % (BK / 4);
+        *(f32x4*)&As[buf][row * LDA + 4 * c4] = ra[r];
+      } else {
+        const int krow = f / (TILE / 4), c4 = f % (TILE / 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) As[buf][(4 * c4 + q) * LDA + krow] = ra[r][q];
+      }
+      if (!TY) {
+        const int krow = f / (TILE / 4), c4 = f % (TILE / 4);
+        *(f32x4*)&Bs[buf][krow * LDB + 4 * c4] = rb[r];
+      } else {
+        const int row = f / (BK / 4), c4 = f % (BK / 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[buf][(4 * c4 + q) * LDB + row] = rb[r][q];
+      }
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int KT = B / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const float* as = As[buf];
+    const float* bs = Bs[buf];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      f32x4 av[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) av[mt] = *(const f32x4*)&as[(wm * WT + mt * 32 + li) * LDA + h * 16 + 4 * s4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = h * 16 + 4 * s4 + q;
+        float bv[MT];
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt) bv[nt] = bs[kk * LDB + wn * WT + nt * 32 + li];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < MT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][q], bv[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  epilogue<MT, MT, WT, WT, SYM, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+}
+
+template <int TILE>
+hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
+  a.tdim = a.B / TILE;
+  a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
+  if (trans == Trans::NN) {
+    if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float>, a, stream);
+    return launch(gemm_f32_kernel<TILE, 0, 0, false, float>, a, stream);
+  }
+  if (!sym) return hipErrorInvalidValue;
+  if (trans == Trans::NT) return launch(gemm_f32_kernel<TILE, 0, 1, true, float>, a, stream);
+  return launch(gemm_f32_kernel<TILE, 1, 0, true, float>, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
+  if (a.B % 128 == 0) return dispatch_f32<128>(a, trans, sym, stream);
+  return dispatch_f32<64>(a, trans, sym, stream);
+}
+
+}  // namespace gemm
+}  // namespace dash
