@@ -37,7 +37,7 @@ CN_ITERS = 5       # 16 products per block
 FP32_PEAK_TFLOPS = 157.3
 FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-PRODUCT_KERNEL = "gemm_f32_kernel<128, 0, 0, false, float>"
+PRODUCT_KERNEL = "gemm_f32_kernel<128, 0, 0, true, float>"
 
 
 def parse():
@@ -173,28 +173,31 @@ def main():
     value = N / (wall / args.steps)
 
     # dominant kernel: the fp32 product of the Clenshaw solve (d-1 launches per call, each one
-    # batched product over all N blocks); its launch time from the events around the solve
+    # batched triangle-only product over all N blocks); its launch time from the events around the
+    # solve.  Flops are counted per computed tile (dash_flops).
     cheb_products = dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)
-    flop_per_launch = 2.0 * B ** 3 * N
+    cheb_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32, CHEB_DEGREE, 0)
+    flop_per_launch = cheb_flop / cheb_products
+    tri = flop_per_launch / (2.0 * B ** 3 * N)
     launch_ms = phase_ms["cheb"] / cheb_products
     achieved = flop_per_launch / (launch_ms * 1e-3) / 1e12
     rec = traffic_record()
     traffic, traffic_detail = None, None
     if rec is not None:
-        # algorithmic bytes of one Clenshaw product launch: read A, b_{k+1} (operand and C), b_{k+2};
-        # write b_k -- four fp32 stacks
+        # algorithmic bytes of one Clenshaw product launch: read A and b_{k+1} (operands), the upper
+        # triangle of b_{k+2}, write b_k (both triangles) -- fp32 stacks
         traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
         traffic_detail = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
-                          "algorithmic_bytes": 4.0 * B * B * N * 4, "source": "profiles/traffic.json"}
+                          "algorithmic_bytes": 4.0 * B * B * N * (3 + tri), "source": "profiles/traffic.json"}
     roofline = {"kernel": PRODUCT_KERNEL, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
                 "traffic": traffic, "traffic_detail": traffic_detail, "flop_per_launch": flop_per_launch,
-                "avg_launch_ms": round(launch_ms, 3)}
+                "tiles_computed_fraction": round(tri, 4), "avg_launch_ms": round(launch_ms, 3)}
 
-    step_flop = (cheb_products * 2.0 * B ** 3 * N          # Clenshaw products
-                 + 2 * NG * B * B * (B + 64)                # triangle-only statistics, 128-wide tiles
-                 + 2 * 2.0 * B ** 3 * NG                    # apply
-                 + MPI_STEPS * 2.0 * B * B * K_VEC * N)     # power iteration
+    step_flop = (cheb_flop
+                 + dash.dash_flops(dash.DASH_OP_STATS, NG, B, dash.DASH_FP32, 0, 0)
+                 + dash.dash_flops(dash.DASH_OP_APPLY, NG, B, dash.DASH_FP32, 0, 0)
+                 + dash.dash_flops(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, MPI_STEPS, 0))
     mpi_bytes = MPI_STEPS * 4.0 * B * B * N
     breakdown = {
         "phase_ms": {k: round(v, 3) for k, v in phase_ms.items()},
@@ -284,8 +287,7 @@ def traffic_from_counters(fetch_csv, write_csv):
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         ref = sum(float(r["Counter_Value"]) for r in rows if "tile_copy_kernel" in r["Kernel_Name"]) * 1024
-        gemm = [float(r["Counter_Value"]) * 1024 for r in rows
-                if "gemm_f32_kernel<128, 0, 0, false, float>" in r["Kernel_Name"]]
+        gemm = [float(r["Counter_Value"]) * 1024 for r in rows if PRODUCT_KERNEL in r["Kernel_Name"]]
         factor = REF_COPY_BYTES / ref
         key = "fetch" if counter == "FETCH_SIZE" else "write"
         out[key + "_raw_bytes_per_launch"] = sum(gemm) / len(gemm)
@@ -330,12 +332,10 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     del ws
     torch.cuda.empty_cache()
     prods = dash.dash_solver_products(dash.DASH_OP_NDB, NDB_ITERS, NDB_ITERS)
+    fl = dash.dash_flops(dash.DASH_OP_NDB, N, B, dash.DASH_FP32, NDB_ITERS, NDB_ITERS) / (ndb_ms * 1e-3) / 1e12
     res["ndb_fp32"] = {"iters": [NDB_ITERS, NDB_ITERS], "products_per_block": prods, "ms": round(ndb_ms, 2),
-                       "blocks_per_s": round(N / (ndb_ms * 1e-3), 1),
-                       "tflops": round(prods * 2.0 * B ** 3 * N / (ndb_ms * 1e-3) / 1e12, 2),
-                       "frac_fp32_peak": round(prods * 2.0 * B ** 3 * N / (ndb_ms * 1e-3) / 1e12
-                                               / FP32_PEAK_TFLOPS, 4),
-                       "scale_ms": round(scale_ms, 2)}
+                       "blocks_per_s": round(N / (ndb_ms * 1e-3), 1), "tflops": round(fl, 2),
+                       "frac_fp32_peak": round(fl / FP32_PEAK_TFLOPS, 4), "scale_ms": round(scale_ms, 2)}
     # CN fp16 after binary16 power-iteration scaling
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, K_VEC, device=dev)
     scale16_ms = timed(lambda: dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP16, K_VEC,
@@ -346,7 +346,7 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     del ws
     torch.cuda.empty_cache()
     prods = dash.dash_solver_products(dash.DASH_OP_CN, CN_ITERS, 0)
-    fl = prods * 2.0 * B ** 3 * N / (cn_ms * 1e-3) / 1e12
+    fl = dash.dash_flops(dash.DASH_OP_CN, N, B, dash.DASH_FP16, CN_ITERS, 0) / (cn_ms * 1e-3) / 1e12
     half_bytes = 2.0 * B * B * N * (1 + MPI_STEPS) + 4.0 * B * B * N  # cast (read fp32, write fp16) + T reads
     res["cn_fp16"] = {"iters": CN_ITERS, "products_per_block": prods, "ms": round(cn_ms, 2),
                       "blocks_per_s": round(N / (cn_ms * 1e-3), 1), "tflops": round(fl, 2),

@@ -60,7 +60,8 @@ typedef enum {
   DASH_OP_NDB = 1,
   DASH_OP_CN = 2,
   DASH_OP_CHEB = 3,
-  DASH_OP_APPLY = 4
+  DASH_OP_APPLY = 4,
+  DASH_OP_STATS = 5
 } dash_op;
 
 /* A row-major fp32 weight gradient (device memory): element (r, c) at ptr[r * ld + c]. */
@@ -118,6 +119,8 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
  * On M_0 = A_i / s_i, X_0 = I: S = (5I - M)/4, X <- X S, M <- M S^4 (S^4 = (S S)(S S));
  * X_i = s_i^{-1/4} X_iters.  4*iters - 4 products.  prec == DASH_FP16 stores every iterate in
  * binary16 and accumulates in fp32; X is always written in fp32.  p != 4 -> DASH_ERR_UNSUPPORTED.
+ * Every iterate is a polynomial in A_i, so A_i must be symmetric: each product computes only its
+ * upper-triangle tiles and mirrors them, and X_i comes out exactly symmetric.
  * monitor: NULL or [N, iters] receives ||M_k - I||_F / sqrt(B) before step k. */
 dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
                                  dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
@@ -127,7 +130,8 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
  * ([PT] Metodologia, item 2, "Aproximações de Polinômios de Chebyshev").  The degree-`degree`
  * interpolant p of x^{-1/4} at the Chebyshev points of the first kind on [lo, hi] is applied to
  * A_i / s_i; X_i = s_i^{-1/4} p(A_i / s_i).  degree - 1 products.  1 <= degree <= 64, 0 < lo < hi.
- * fp32 only. */
+ * fp32 only.  A_i must be symmetric: the recurrence terms are polynomials in A_i, so each product
+ * computes only its upper-triangle tiles and mirrors them; X_i comes out exactly symmetric. */
 dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,
                                    double hi, float* X, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
@@ -142,8 +146,17 @@ dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, i
 dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t k_or_degree,
                                 size_t* bytes);
 
-/* Number of B x B products a solver call enqueues per block (host-side count, no GPU work). */
+/* Number of B x B products a solver call enqueues per block (host-side count, no GPU work).
+ * op: DASH_OP_NDB (iters1, iters2), DASH_OP_CN (iters1), DASH_OP_CHEB (iters1 = degree). -1 if invalid. */
 int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2);
+
+/* Floating-point operations one call executes on the matrix cores, counted per computed output tile
+ * (host-side, no GPU work).  The Coupled-Newton, Chebyshev and statistics products compute only the
+ * upper-triangle tiles of their symmetric results, so they count tdim(tdim+1)/2 of the tdim^2
+ * tiles of each product.  op and a1/a2: DASH_OP_NDB (iters1, iters2), DASH_OP_CN (iters, -),
+ * DASH_OP_CHEB (degree, -), DASH_OP_APPLY (-, -; N = tiles), DASH_OP_STATS (-, -; N = tiles),
+ * DASH_OP_SCALE (steps of power iteration, -).  Returns -1 for invalid arguments. */
+double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2);
 
 const char* dash_status_string(dash_status status);
 int32_t dash_abi_version(void);

@@ -13,11 +13,13 @@ from ._lib import (  # noqa: F401
     DASH_OP_CN,
     DASH_OP_NDB,
     DASH_OP_SCALE,
+    DASH_OP_STATS,
     DASH_SCALE_FROBENIUS,
     DASH_SCALE_POWER,
     DashError,
     dash_abi_version,
     dash_apply,
+    dash_flops,
     dash_inverse_root_cheb,
     dash_inverse_root_cn,
     dash_inverse_root_ndb,

@@ -15,7 +15,7 @@ library_path = os.path.join(_HERE, "libdash.so")
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
 DASH_FP32, DASH_FP16 = 0, 1
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
-DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY = range(5)
+DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS = range(6)
 
 
 class DashError(RuntimeError):
@@ -53,6 +53,7 @@ def library() -> ctypes.CDLL:
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
+            "dash_flops": (f64, [st, i64, i32, st, i32, i32]),
             "dash_status_string": (ctypes.c_char_p, [st]),
             "dash_abi_version": (i32, []),
         }
@@ -101,6 +102,10 @@ def dash_abi_version() -> int:
 
 def dash_solver_products(op: int, iters1: int, iters2: int = 0) -> int:
     return library().dash_solver_products(op, iters1, iters2)
+
+
+def dash_flops(op: int, N: int, B: int, prec: int = DASH_FP32, a1: int = 0, a2: int = 0) -> float:
+    return library().dash_flops(op, N, B, prec, a1, a2)
 
 
 def dash_workspace_size(op: int, N: int, B: int, prec: int = DASH_FP32, k_or_degree: int = 0) -> int:

@@ -261,6 +261,33 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2) {
   }
 }
 
+double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2) {
+  if (!valid_N(N) || !valid_B(B) || (prec != DASH_FP32 && prec != DASH_FP16)) return -1.0;
+  const double full = 2.0 * B * B * (double)B * (double)N;
+  // fraction of the tiles a triangle-only product computes, for the tile width the kernels use
+  auto tri = [&](dash_prec p) {
+    const int tile = (p == DASH_FP16 && B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64);
+    const double t = B / tile;
+    return (t * (t + 1) / 2) / (t * t);
+  };
+  int64_t n;
+  switch (op) {
+    case DASH_OP_NDB:
+      n = dash_solver_products(op, a1, a2);
+      return n < 0 ? -1.0 : n * full;
+    case DASH_OP_CN:
+      n = dash_solver_products(op, a1, 0);
+      return n < 0 ? -1.0 : n * full * tri(prec);
+    case DASH_OP_CHEB:
+      n = dash_solver_products(op, a1, 0);
+      return n < 0 ? -1.0 : n * full * tri(DASH_FP32);
+    case DASH_OP_APPLY: return 2.0 * full;
+    case DASH_OP_STATS: return 2.0 * full * tri(DASH_FP32);
+    case DASH_OP_SCALE: return a1 < 1 ? -1.0 : 2.0 * B * (double)B * 32.0 * a1 * (double)N;
+  }
+  return -1.0;
+}
+
 dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t k_or_degree,
                                 size_t* bytes) {
   if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
@@ -275,6 +302,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
     case DASH_OP_CN: *bytes = ws_cn(N, B, prec); return DASH_OK;
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
+    case DASH_OP_STATS: *bytes = 0; return DASH_OK;
   }
   return DASH_ERR_INVALID_ARG;
 }
@@ -461,17 +489,17 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.coef = coef;
       e.status = status;
       Product pr = prod(Xk, S, X);
-      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, false, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, true, e, st));
       break;
     }
     void* S2 = pool.get();
     if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
       Product pr = prod(S, S, S2);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
       Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
-      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
       pool.put(Xk);
       pool.put(S);
       Xk = Xn;
@@ -479,7 +507,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     void* S4 = pool.get();
     {
       Product pr = prod(S2, S2, S4);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
     }
     pool.put(S2);
     // M_{k+1} = M_k S^4 and S_{k+1} = (5I - M_{k+1})/4 from the same accumulator
@@ -489,12 +517,28 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.monitor = monitor + (k + 1);
       e.mon_stride = T;
     }
-    if (k + 1 == T - 1) {  // M_T is never needed: write S only, monitor from it
+    if (prec == DASH_FP16) {
+      // binary16: M_{k+1} is stored first and S_{k+1} formed from the stored M in an elementwise
+      // pass (binary16 products carry no second output)
+      void* Mn = pool.get();
+      Product pr = prod(M, S4, Mn);
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
+      Affine sn;
+      sn.X = Mn;
+      sn.x_prec = DASH_FP16;
+      sn.D = Sn;
+      sn.d_prec = DASH_FP16;
+      sn.a = -0.25f;
+      sn.g = 1.25f;
+      TRY(launch_affine(sn, N, B, st));
+      pool.put(M);
+      M = Mn;
+    } else if (k + 1 == T - 1) {  // M_T is never needed: write S only, monitor from it
       e.alpha = -0.25f;
       e.gamma = 1.25f;
       e.mon_mul = 16.f;
       Product pr = prod(M, S4, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
       pool.put(M);
       M = nullptr;
     } else {
@@ -503,7 +547,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.alpha2 = -0.25f;
       e.gamma2 = 1.25f;
       Product pr = prod(M, S4, Mn, nullptr, nullptr, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
       pool.put(M);
       M = Mn;
     }
@@ -571,7 +615,7 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
     e.gamma = (float)c[k];
     e.coef = coef;
     Product pr = prod(A, b1, b2, b1, b2);
-    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, e, st));
+    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, e, st));
     float* t = b1;
     b1 = b2;
     b2 = t;
@@ -589,7 +633,7 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
   e.coef = coef;
   e.status = status;
   Product pr = prod(A, b1, X, b1, b2);
-  TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, e, st));
+  TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, e, st));
   return DASH_OK;
 }
 

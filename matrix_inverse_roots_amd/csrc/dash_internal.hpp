@@ -64,11 +64,12 @@ enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transpose
 hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_prec in_prec, dash_prec out_prec,
                        Trans trans, bool sym, const Epilogue& epi, hipStream_t stream);
 
-// D_b = a_b X_b + g_b I (and optionally D2_b = a2_b X_b + g2_b I), elementwise, X fp32.
-// X may be NULL (then D = g_b I).  Output precisions per output.  Optional monitor/status as above
-// (monitor from D).
+// D_b = a_b X_b + g_b I (and optionally D2_b = a2_b X_b + g2_b I), elementwise; X is fp32 or
+// binary16 (x_prec).  X may be NULL (then D = g_b I).  Output precisions per output.  Optional
+// monitor/status as above (monitor from D).
 struct Affine {
-  const float* X = nullptr;
+  const void* X = nullptr;
+  dash_prec x_prec = DASH_FP32;
   void* D = nullptr;
   dash_prec d_prec = DASH_FP32;
   float a = 0.f, g = 0.f;

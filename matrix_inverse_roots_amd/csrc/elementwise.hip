@@ -79,7 +79,14 @@ __global__ __launch_bounds__(256) void affine_kernel(Affine op, int64_t N, int B
     const int64_t in_blk = e - b * (int64_t)B * B;
     const int row = (int)(in_blk / B), col = (int)(in_blk % B);
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (op.X) x = *(const f32x4*)(op.X + e);
+    if (op.X) {
+      if (op.x_prec == DASH_FP32) {
+        x = *(const f32x4*)((const float*)op.X + e);
+      } else {
+        const f16x4 hx = *(const f16x4*)((const _Float16*)op.X + e);
+        x = f32x4{(float)hx[0], (float)hx[1], (float)hx[2], (float)hx[3]};
+      }
+    }
     f32x4 v, v2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -32,12 +32,18 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   a.N = N;
   a.B = B;
   a.epi = epi;
+  // a mirrored second output is re-derived from D: D must be the bare accumulator
+  if (sym && nprob >= 1 && (probs[0].D2 || (nprob > 1 && probs[1].D2)) &&
+      (epi.alpha != 1.f || epi.ia != CO_NONE || epi.gamma != 0.f || epi_uses_ce(probs, nprob)))
+    return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);
   }
-  if (trans != Trans::NN || sym || epi_uses_ce(probs, nprob)) return hipErrorInvalidValue;
-  return gemm::launch_f16(a, out_prec, stream);
+  if (trans != Trans::NN || epi_uses_ce(probs, nprob)) return hipErrorInvalidValue;
+  // binary16 outputs are staged through LDS for wide stores and carry no second output
+  if (out_prec == DASH_FP16 && (probs[0].D2 || (nprob > 1 && probs[1].D2))) return hipErrorInvalidValue;
+  return gemm::launch_f16(a, out_prec, sym, stream);
 }
 
 }  // namespace dash

@@ -8,17 +8,19 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, typename TO>
+template <int TILE, bool SYM, typename TO>
 __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int WT = TILE / 2;
   constexpr int MT = WT / 32;
   constexpr int LD = BK + 8;  // As[m][k], Bs[n][k] (Y tile transposed)
   constexpr int NL = TILE * BK / 8 / 256;
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][TILE * LD];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TILE * LD];
+  constexpr int SMEM_BYTES = 2 * 2 * TILE * LD * 2;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  _Float16(*As)[TILE * LD] = reinterpret_cast<_Float16(*)[TILE * LD]>(smem);
+  _Float16(*Bs)[TILE * LD] = reinterpret_cast<_Float16(*)[TILE * LD]>(smem + 2 * TILE * LD * 2);
 
-  const TileCoord tc = decode_tile(a, false);
+  const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -85,7 +87,10 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, MT, WT, WT, false, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+  if constexpr (sizeof(TO) == 2)
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+  else
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 
@@ -100,13 +105,18 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row ^ (row >> 3))) & 7; }
 
-template <typename TO>
+template <bool SYM, typename TO>
 __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 64, MT = 4, WT = 128;
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][TILE * BK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][TILE * BK];
+  // double-buffered X and Y slices (128 KiB); a little more so a mirrored binary16 tile fits whole
+  constexpr int MAIN_BYTES = 2 * 2 * TILE * BK * 2;
+  constexpr int STAGE_BYTES = TILE * (TILE + 8) * 2;  // binary16 output tile staged for 16-byte stores
+  constexpr int SMEM_BYTES = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  _Float16(*As)[TILE * BK] = reinterpret_cast<_Float16(*)[TILE * BK]>(smem);
+  _Float16(*Bs)[TILE * BK] = reinterpret_cast<_Float16(*)[TILE * BK]>(smem + 2 * TILE * BK * 2);
 
-  const TileCoord tc = decode_tile(a, false);
+  const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -187,28 +197,32 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, MT, WT, WT, false, TO, false>(a, tc, P, acc, wm, wn, lane, TILE);
+  if constexpr (sizeof(TO) == 2)
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+  else
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+}
+
+template <bool SYM>
+hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, hipStream_t stream) {
+  const int tile = a.B % 256 == 0 ? 256 : (a.B % 128 == 0 ? 128 : 64);
+  a.tdim = a.B / tile;
+  a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
+  const bool half_out = out_prec == DASH_FP16;
+  if (tile == 256)
+    return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16>, a, stream)
+                    : launch(gemm_f16_big_kernel<SYM, float>, a, stream);
+  if (tile == 128)
+    return half_out ? launch(gemm_f16_kernel<128, SYM, _Float16>, a, stream)
+                    : launch(gemm_f16_kernel<128, SYM, float>, a, stream);
+  return half_out ? launch(gemm_f16_kernel<64, SYM, _Float16>, a, stream)
+                  : launch(gemm_f16_kernel<64, SYM, float>, a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, hipStream_t stream) {
-  if (a.B % 256 == 0) {  // 256 x 256 tiles
-    a.tdim = a.B / 256;
-    a.tiles = a.tdim * a.tdim;
-    if (out_prec == DASH_FP16) return launch(gemm_f16_big_kernel<_Float16>, a, stream);
-    return launch(gemm_f16_big_kernel<float>, a, stream);
-  }
-  if (a.B % 128 == 0) {
-    a.tdim = a.B / 128;
-    a.tiles = a.tdim * a.tdim;
-    if (out_prec == DASH_FP16) return launch(gemm_f16_kernel<128, _Float16>, a, stream);
-    return launch(gemm_f16_kernel<128, float>, a, stream);
-  }
-  a.tdim = a.B / 64;
-  a.tiles = a.tdim * a.tdim;
-  if (out_prec == DASH_FP16) return launch(gemm_f16_kernel<64, _Float16>, a, stream);
-  return launch(gemm_f16_kernel<64, float>, a, stream);
+hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, hipStream_t stream) {
+  return sym ? dispatch_f16<true>(a, out_prec, stream) : dispatch_f16<false>(a, out_prec, stream);
 }
 
 }  // namespace gemm

@@ -22,8 +22,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   constexpr int LDA = BK + 4;    // As[m][k]
   constexpr int LDB = TILE + 4;  // Bs[k][n]
   constexpr int NL = TILE * BK / 4 / 256;
-  __shared__ __attribute__((aligned(16))) float As[2][TILE * LDA];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+  constexpr int SMEM_BYTES = (2 * TILE * LDA + 2 * BK * LDB) * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  float(*As)[TILE * LDA] = reinterpret_cast<float(*)[TILE * LDA]>(smem);
+  float(*Bs)[BK * LDB] = reinterpret_cast<float(*)[BK * LDB]>(smem + 2 * TILE * LDA * 4);
 
   const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, MT, WT, WT, SYM, TO>(a, tc, P, acc, wm, wn, lane, TILE);
+  epilogue<MT, MT, WT, WT, SYM, TO, true, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <int TILE>

@@ -119,9 +119,10 @@ def test_cn_conditioned(conditioned, scaling):
     assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
     assert np.max(residual(to_host(X), A)) < R_FP32
     assert np.all(to_host(status) == 0)
+    # the monitor ||M_k - I||/sqrt(B) differences O(1) fp32 entries: near convergence its error has
+    # an absolute floor of fp32 rounding accumulated in M over the steps
     m = to_host(mon)
-    big = mon_ref > 1e-3
-    assert np.max(np.abs(m[big] - mon_ref[big]) / mon_ref[big]) < 1e-3
+    assert np.all(np.abs(m - mon_ref) <= 1e-3 * mon_ref + 2e-5)
 
 
 @pytest.mark.parametrize("iters", [1, 2, 3, 6])
