@@ -15,7 +15,7 @@ namespace gemm {
 namespace {
 
 template <int TILE, int TX, int TY, bool SYM, typename TO>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BK = 32;
   constexpr int WT = TILE / 2;
   constexpr int MT = WT / 32;
