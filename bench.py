@@ -48,9 +48,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb"], default="step",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb"], default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
-                        "(the run that HBM traffic counters are collected on)")
+                        "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
+                        "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
@@ -109,6 +110,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.only == "cheb":
         return only_cheb(dash, di, torch, dev)
+    if args.only in ("cn16", "ndb"):
+        return only_solver(dash, di, torch, dev, args.only)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -275,6 +278,33 @@ def only_cheb(dash, di, torch, dev):
     print(json.dumps({"mode": "cheb", "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
                       "ref_copy_ms": round(e[0].elapsed_time(e[1]), 3), "cheb_ms": round(e[1].elapsed_time(e[2]), 3),
                       "products": dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)}), flush=True)
+
+
+def only_solver(dash, di, torch, dev, which):
+    """One scaled solve on the N=3072, B=1024 stack: CN p=4 fp16 (5 steps) or NDB fp32 (6+6 steps)."""
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    s = torch.empty(N, device=dev)
+    prec = dash.DASH_FP16 if which == "cn16" else dash.DASH_FP32
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, prec, K_VEC, device=dev)
+    X = torch.empty_like(A)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prec, K_VEC, MPI_STEPS, V0, s, ws)
+    e[1].record()
+    if which == "cn16":
+        ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=dev)
+        dash.dash_inverse_root_cn(A, s, N, B, 4, CN_ITERS, prec, X, ws=ws)
+    else:
+        ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=dev)
+        dash.dash_inverse_root_ndb(A, s, N, B, NDB_ITERS, NDB_ITERS, X, ws=ws)
+    e[2].record()
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": which, "N": N, "B": B, "scale_ms": round(e[0].elapsed_time(e[1]), 3),
+                      "solve_ms": round(e[1].elapsed_time(e[2]), 3)}), flush=True)
 
 
 def traffic_from_counters(fetch_csv, write_csv):

@@ -119,8 +119,10 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
  * On M_0 = A_i / s_i, X_0 = I: S = (5I - M)/4, X <- X S, M <- M S^4 (S^4 = (S S)(S S));
  * X_i = s_i^{-1/4} X_iters.  4*iters - 4 products.  prec == DASH_FP16 stores every iterate in
  * binary16 and accumulates in fp32; X is always written in fp32.  p != 4 -> DASH_ERR_UNSUPPORTED.
- * Every iterate is a polynomial in A_i, so A_i must be symmetric: each product computes only its
- * upper-triangle tiles and mirrors them, and X_i comes out exactly symmetric.
+ * Only the upper triangle of A_i is read (the start terms are built from it, mirrored).  With
+ * binary16 operands every iterate (a polynomial in A_i) is kept exactly symmetric: each product
+ * computes only its upper-triangle tiles and mirrors them, and X_i comes out exactly symmetric.
+ * fp32 runs full products, which keep the fp32 rounding floor lowest at high condition numbers.
  * monitor: NULL or [N, iters] receives ||M_k - I||_F / sqrt(B) before step k. */
 dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
                                  dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
@@ -153,7 +155,7 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2);
 /* Floating-point operations one call executes on the matrix cores, counted per computed output tile
  * (host-side, no GPU work).  The Coupled-Newton, Chebyshev and statistics products compute only the
  * upper-triangle tiles of their symmetric results, so they count tdim(tdim+1)/2 of the tdim^2
- * tiles of each product.  op and a1/a2: DASH_OP_NDB (iters1, iters2), DASH_OP_CN (iters, -),
+ * tiles of each product (Coupled-Newton only with binary16 operands).  op and a1/a2: DASH_OP_NDB (iters1, iters2), DASH_OP_CN (iters, -),
  * DASH_OP_CHEB (degree, -), DASH_OP_APPLY (-, -; N = tiles), DASH_OP_STATS (-, -; N = tiles),
  * DASH_OP_SCALE (steps of power iteration, -).  Returns -1 for invalid arguments. */
 double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2);

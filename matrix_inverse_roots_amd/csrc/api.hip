@@ -277,7 +277,7 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
       return n < 0 ? -1.0 : n * full;
     case DASH_OP_CN:
       n = dash_solver_products(op, a1, 0);
-      return n < 0 ? -1.0 : n * full * tri(prec);
+      return n < 0 ? -1.0 : n * full * (prec == DASH_FP16 ? tri(prec) : 1.0);
     case DASH_OP_CHEB:
       n = dash_solver_products(op, a1, 0);
       return n < 0 ? -1.0 : n * full * tri(DASH_FP32);
@@ -442,6 +442,10 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   const int T = iters;
+  // binary16: triangle-only products (the iterates are symmetric polynomials in A and the error
+  // floor is set by binary16 storage); fp32: full products, which keep the fp32 rounding floor of
+  // the iteration lowest at high condition numbers
+  const bool tri = (prec == DASH_FP16);
   // step 0: M_0 = A/s, S_0 = (5I - M_0)/4, X_1 = S_0;  ||M_0 - I||^2 = 16 ||S_0 - I||^2
   void* S = pool.get();
   void* M = pool.get();
@@ -465,7 +469,8 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       s0.mon_stride = T;
       s0.mon_mul = 16.f;
     }
-    TRY(launch_affine(s0, N, B, st));
+    // built from the upper triangle of A: every later right operand is then exactly symmetric
+    TRY(launch_sym_affine(s0, N, B, st));
   }
   if (T == 1) {  // X = s^{-1/4} S_0, straight from A
     Affine fin;
@@ -476,8 +481,13 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     fin.g = 1.25f;
     fin.ig = CO_U;
     fin.coef = coef;
-    fin.status = status;
-    TRY(launch_affine(fin, N, B, st));
+    TRY(launch_sym_affine(fin, N, B, st));
+    Affine chk;  // finite check of the output (status bit 1)
+    chk.X = X;
+    chk.D = X;
+    chk.a = 1.f;
+    chk.status = status;
+    if (status) TRY(launch_affine(chk, N, B, st));
     if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
     return DASH_OK;
   }
@@ -489,17 +499,17 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.coef = coef;
       e.status = status;
       Product pr = prod(Xk, S, X);
-      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, true, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, tri, e, st, true));
       break;
     }
     void* S2 = pool.get();
     if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
       Product pr = prod(S, S, S2);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
       Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
-      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
+      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
       pool.put(Xk);
       pool.put(S);
       Xk = Xn;
@@ -507,7 +517,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     void* S4 = pool.get();
     {
       Product pr = prod(S2, S2, S4);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, Epilogue(), st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
     }
     pool.put(S2);
     // M_{k+1} = M_k S^4 and S_{k+1} = (5I - M_{k+1})/4 from the same accumulator
@@ -522,7 +532,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       // pass (binary16 products carry no second output)
       void* Mn = pool.get();
       Product pr = prod(M, S4, Mn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
       Affine sn;
       sn.X = Mn;
       sn.x_prec = DASH_FP16;
@@ -538,7 +548,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.gamma = 1.25f;
       e.mon_mul = 16.f;
       Product pr = prod(M, S4, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
       pool.put(M);
       M = nullptr;
     } else {
@@ -547,7 +557,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.alpha2 = -0.25f;
       e.gamma2 = 1.25f;
       Product pr = prod(M, S4, Mn, nullptr, nullptr, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, true, e, st));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
       pool.put(M);
       M = Mn;
     }

@@ -60,9 +60,10 @@ enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transpose
 
 // Enqueue one or two batched products sharing shape, precision and epilogue scalars (two problems
 // in one launch fill the GPU better).  sym: compute only the upper-triangle tiles and mirror them
-// (exactly symmetric output; C read from the upper triangle).
+// (exactly symmetric output; C read from the upper triangle).  y_sym: every right operand Y is
+// exactly symmetric (Y^T == Y bitwise), so binary16 kernels may read its columns as rows.
 hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_prec in_prec, dash_prec out_prec,
-                       Trans trans, bool sym, const Epilogue& epi, hipStream_t stream);
+                       Trans trans, bool sym, const Epilogue& epi, hipStream_t stream, bool y_sym = false);
 
 // D_b = a_b X_b + g_b I (and optionally D2_b = a2_b X_b + g2_b I), elementwise; X is fp32 or
 // binary16 (x_prec).  X may be NULL (then D = g_b I).  Output precisions per output.  Optional
@@ -85,6 +86,9 @@ struct Affine {
   int32_t* status = nullptr;
 };
 hipError_t launch_affine(const Affine& op, int64_t N, int B, hipStream_t stream);
+// The same map applied to the symmetric matrix built from the upper triangle of X (fp32 X, no
+// status): D and D2 come out exactly symmetric.
+hipError_t launch_sym_affine(const Affine& op, int64_t N, int B, hipStream_t stream);
 
 // coef[b] from s[b]; status[b] bit 0 when s_b is not finite or not > 0 (all coefficients NaN).
 hipError_t launch_coef(const float* s, int64_t N, float* coef, int32_t* status, hipStream_t stream);

@@ -113,6 +113,69 @@ __global__ __launch_bounds__(256) void affine_kernel(Affine op, int64_t N, int B
   if (op.status && bad) atomicOr(&op.status[b], 2);
 }
 
+// Affine map of the symmetric matrix built from the upper triangle of X (fp32):
+// Xu[i][j] = X[min(i,j)][max(i,j)].  One workgroup per pair of 64 x 64 tiles (ti <= tj): the upper
+// tile is staged in LDS and both it and its mirror are written, so D (and D2) come out exactly
+// symmetric whatever the lower triangle of X holds.
+__global__ __launch_bounds__(256) void sym_affine_kernel(Affine op, int64_t N, int B) {
+  constexpr int T = 64;
+  __shared__ float U[T][T + 1];
+  const int nt = B / T;
+  const int64_t pairs = (int64_t)nt * (nt + 1) / 2;
+  const int64_t b = blockIdx.x / pairs;
+  int t = (int)(blockIdx.x - b * pairs);
+  int ti = 0;
+  while (t >= nt - ti) {
+    t -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + t;
+  const float* X = (const float*)op.X + b * (int64_t)B * B;
+  const float a = op.a * co(op.coef, op.ia, b), g = op.g * co(op.coef, op.ig, b);
+  const float a2 = op.a2 * co(op.coef, op.ia2, b), g2 = op.g2 * co(op.coef, op.ig2, b);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // 64 x 64 floats = 1024 float4, 4 per thread
+    const int f = threadIdx.x + 256 * q;
+    const int r = f >> 4, c4 = f & 15;
+    const f32x4 v = *(const f32x4*)(X + (int64_t)(ti * T + r) * B + tj * T + 4 * c4);
+    U[r][4 * c4 + 0] = v[0];
+    U[r][4 * c4 + 1] = v[1];
+    U[r][4 * c4 + 2] = v[2];
+    U[r][4 * c4 + 3] = v[3];
+  }
+  __syncthreads();
+  float mon = 0.f;
+  for (int m = 0; m < (ti == tj ? 1 : 2); ++m) {  // m = 0: tile (ti, tj); m = 1: its mirror (tj, ti)
+    const int R0 = (m ? tj : ti) * T, C0 = (m ? ti : tj) * T;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = threadIdx.x + 256 * q;
+      const int r = f >> 4, c4 = f & 15;
+      f32x4 v, v2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * c4 + e;
+        // value at (R0 + r, C0 + c) from the upper triangle
+        const float x = (m == 0 && (ti < tj || r <= c)) ? U[r][c] : U[c][r];
+        const bool diag = (R0 + r == C0 + c);
+        v[e] = a * x + (diag ? g : 0.f);
+        v2[e] = a2 * x + (diag ? g2 : 0.f);
+        if (op.monitor) {
+          const float d = v[e] - (diag ? 1.f : 0.f);
+          mon += d * d;
+        }
+      }
+      const int64_t idx = b * (int64_t)B * B + (int64_t)(R0 + r) * B + C0 + 4 * c4;
+      store4(op.D, op.d_prec, idx, v);
+      if (op.D2) store4(op.D2, op.d2_prec, idx, v2);
+    }
+  }
+  if (op.monitor) {
+    mon = wave_sum(mon);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&op.monitor[b * op.mon_stride], op.mon_mul * mon);
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -161,6 +224,14 @@ hipError_t launch_affine(const Affine& op, int64_t N, int B, hipStream_t stream)
   const int64_t grid = N * ((int64_t)B * B / AFF_CHUNK);
   if ((int64_t)B * B % AFF_CHUNK != 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(affine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, op, N, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_sym_affine(const Affine& op, int64_t N, int B, hipStream_t stream) {
+  const int nt = B / 64;
+  const int64_t grid = N * (int64_t)nt * (nt + 1) / 2;
+  if (B % 64 != 0 || op.x_prec != DASH_FP32 || !op.X || op.status || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sym_affine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, op, N, B);
   return hipGetLastError();
 }
 

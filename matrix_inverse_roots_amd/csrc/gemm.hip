@@ -23,7 +23,7 @@ bool epi_uses_ce(const Product* p, int n) {
 }  // namespace
 
 hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_prec in_prec, dash_prec out_prec,
-                       Trans trans, bool sym, const Epilogue& epi, hipStream_t stream) {
+                       Trans trans, bool sym, const Epilogue& epi, hipStream_t stream, bool y_sym) {
   if (nprob < 1 || nprob > 2 || N < 1 || B % 64 != 0) return hipErrorInvalidValue;
   gemm::GemmArgs a;
   a.p0 = probs[0];
@@ -43,7 +43,7 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   if (trans != Trans::NN || epi_uses_ce(probs, nprob)) return hipErrorInvalidValue;
   // binary16 outputs are staged through LDS for wide stores and carry no second output
   if (out_prec == DASH_FP16 && (probs[0].D2 || (nprob > 1 && probs[1].D2))) return hipErrorInvalidValue;
-  return gemm::launch_f16(a, out_prec, sym, stream);
+  return gemm::launch_f16(a, out_prec, sym, y_sym, stream);
 }
 
 }  // namespace dash

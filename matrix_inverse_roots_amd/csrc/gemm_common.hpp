@@ -82,16 +82,54 @@ __device__ __forceinline__ TO cvt_out(float v) {
 //   D  = alpha acc + beta C + delta E + gamma I,   D2 = alpha2 acc + gamma2 I   (per-block coefficients)
 //
 // SYM (triangle-only products): only tiles ti <= tj run, and within a diagonal tile only i <= j is
-// kept.  Each kept element is stored at (i, j) directly and at (j, i) through LDS: the values are
-// written transposed into `smem` and read back row by row, so the mirrored stores are as coalesced
-// as the direct ones.  When the whole transposed tile fits in `smem` (ONE_PASS) it is filled while
-// D is stored; otherwise the tile is mirrored in passes of R rows from D's values kept in acc, and
-// a second output D2 is then re-derived from D, which requires alpha = 1, gamma = 0 and no C/E
-// (enforced on the host).  The monitor counts off-diagonal kept elements twice under SYM.
+// kept.  Each kept element is stored at (i, j) directly and at (j, i) through LDS.  In the 32x32
+// accumulator layout a lane's 4 consecutive r are 4 consecutive rows of one column, i.e. 4
+// consecutive entries of a row of the transposed tile, so the transposed tile T[jl][il] is filled
+// with one vector LDS store per 4 values and read back in 16-byte row pieces.  When T fits in
+// `smem` whole (ONE_PASS) it is filled while D is stored; otherwise the tile is mirrored in passes
+// of R rows, recomputed from the products in acc (or from D's values kept in acc when C/E enter
+// D; a second output D2 is then re-derived from D, which requires alpha = 1, gamma = 0 and no C/E,
+// enforced on the host).  The monitor counts off-diagonal
+// kept elements twice under SYM.
+template <typename TO>
+struct Vec4;
+template <>
+struct Vec4<float> {
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct Vec4<_Float16> {
+  typedef _Float16 type __attribute__((ext_vector_type(4)));
+};
+
+// read back R rows-worth of the transposed tile T (pitch PITCH) into Dst rows j0 + jl, columns
+// i0 + p R + c; a diagonal tile writes only its strict lower part (c + p R < jl)
+template <typename TO, int TILE, int R, int PITCH>
+__device__ __forceinline__ void mirror_readback(TO* Dst, const TO* T, int B, int i0, int j0, int p, bool diag_tile) {
+  constexpr int PER16 = 16 / (int)sizeof(TO);  // elements per 16-byte piece
+  typedef TO v16 __attribute__((ext_vector_type(PER16)));
+  for (int g = threadIdx.x; g < TILE * R / PER16; g += blockDim.x) {
+    const int jl = g / (R / PER16), c = (g - jl * (R / PER16)) * PER16;
+    const int il = p * R + c;
+    TO* dst = Dst + (int64_t)(j0 + jl) * B + i0 + il;
+    if (!diag_tile || il + PER16 - 1 < jl) {
+      *(v16*)dst = *(const v16*)&T[jl * PITCH + c];
+    } else if (il < jl) {
+      for (int q = 0; il + q < jl; ++q) dst[q] = T[jl * PITCH + c + q];
+    }
+  }
+}
+
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_CE, int TILE, int SMEM_BYTES>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, char* smem) {
-  constexpr bool ONE_PASS = TILE * (TILE + 1) * (int)sizeof(TO) <= SMEM_BYTES;
+  typedef typename Vec4<TO>::type v4;
+  constexpr int PAD = 16 / (int)sizeof(TO);  // keeps every T row 16-byte aligned
+  constexpr bool ONE_PASS = TILE * (TILE + PAD) * (int)sizeof(TO) <= SMEM_BYTES;
+  constexpr int R1 = ONE_PASS ? TILE : (TILE * (TILE / 2 + PAD) * (int)sizeof(TO) <= SMEM_BYTES ? TILE / 2 : TILE / 4);
+  constexpr int R = R1;
+  constexpr int PITCH = R + PAD;
+  static_assert(TILE * PITCH * (int)sizeof(TO) <= SMEM_BYTES, "mirror staging does not fit in LDS");
   const Epilogue& e = a.epi;
   const int B = a.B;
   const int64_t b = tc.b;
@@ -110,7 +148,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const bool diag_tile = SYM && tc.ti == tc.tj;
   TO* T = (TO*)smem;
-  const int nthreads = blockDim.x;
   float mon = 0.f;
   bool bad = false;
   // One row of MFMA tiles at a time: all C/E loads of the chunk are issued before any store, so
@@ -132,28 +169,35 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
 #pragma unroll
     for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3 of the tile
         const int jl = wn * WTN + nt * 32 + li;
-        const int i = i0 + il, j = j0 + jl;
-        const float x = acc[mt][nt][r];
-        float v = al * x + be * cv[nt][r] + de * ev[nt][r];
-        if (i == j) v += ga;
-        if (SYM && ONE_PASS) T[jl * (TILE + 1) + il] = cvt_out<TO>(v);
-        if (SYM && !ONE_PASS) acc[mt][nt][r] = v;
-        if (diag_tile && i > j) continue;
-        const int64_t idx = (int64_t)i * B + j;
-        D[idx] = cvt_out<TO>(v);
-        bad |= !isfinite(v);
-        if (D2) {
-          const float v2 = al2 * x + (i == j ? ga2 : 0.f);
-          D2[idx] = cvt_out<TO>(v2);
-          bad |= !isfinite(v2);
+        v4 pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * r4 + q;
+          const int il = il0 + q;
+          const int i = i0 + il, j = j0 + jl;
+          const float x = acc[mt][nt][r];
+          float v = al * x + be * cv[nt][r] + de * ev[nt][r];
+          if (i == j) v += ga;
+          pk[q] = cvt_out<TO>(v);
+          if (SYM && !ONE_PASS && HAS_CE) acc[mt][nt][r] = v;  // C/E are not re-read by the passes
+          if (diag_tile && i > j) continue;
+          const int64_t idx = (int64_t)i * B + j;
+          D[idx] = cvt_out<TO>(v);
+          bad |= !isfinite(v);
+          if (D2) {
+            const float v2 = al2 * x + (i == j ? ga2 : 0.f);
+            D2[idx] = cvt_out<TO>(v2);
+            bad |= !isfinite(v2);
+          }
+          if (e.monitor) {
+            const float dd = v - (i == j ? 1.f : 0.f);
+            mon += (SYM && i != j) ? 2.f * dd * dd : dd * dd;
+          }
         }
-        if (e.monitor) {
-          const float dd = v - (i == j ? 1.f : 0.f);
-          mon += (SYM && i != j) ? 2.f * dd * dd : dd * dd;
-        }
+        if (SYM && ONE_PASS) *(v4*)&T[jl * PITCH + il0] = pk;
       }
   }
   if (e.monitor) {
@@ -164,36 +208,31 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   if (!SYM) return;
 
   if (ONE_PASS) {
-    for (int out = 0; out < (D2 ? 2 : 1); ++out) {
-      if (out) {  // refill the staging tile with D2's values (acc still holds the products)
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              const int jl = wn * WTN + nt * 32 + li;
-              const float v2 = al2 * acc[mt][nt][r] + (il + i0 == jl + j0 ? ga2 : 0.f);
-              T[jl * (TILE + 1) + il] = cvt_out<TO>(v2);
-            }
-      }
+    __syncthreads();
+    mirror_readback<TO, TILE, R, PITCH>(D, T, B, i0, j0, 0, diag_tile);
+    if (D2) {  // refill T with D2's values (acc still holds the products)
       __syncthreads();
-      TO* Dst = out ? D2 : D;
-      for (int g = threadIdx.x; g < TILE * TILE; g += nthreads) {
-        const int jl = g / TILE, il = g - jl * TILE;
-        if (diag_tile && il >= jl) continue;  // only the strict lower part is a mirror
-        Dst[(int64_t)(j0 + jl) * B + i0 + il] = T[jl * (TILE + 1) + il];
-      }
+#pragma unroll
+      for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;
+            const int jl = wn * WTN + nt * 32 + li;
+            v4 pk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              pk[q] = cvt_out<TO>(al2 * acc[mt][nt][4 * r4 + q] + (il0 + q + i0 == jl + j0 ? ga2 : 0.f));
+            *(v4*)&T[jl * PITCH + il0] = pk;
+          }
+      __syncthreads();
+      mirror_readback<TO, TILE, R, PITCH>(D2, T, B, i0, j0, 0, diag_tile);
     }
     return;
   }
 
-  // multi-pass mirror: pass p covers tile rows [p R, p R + R), stored transposed T[jl][il - p R]
-  constexpr int R0 = SMEM_BYTES / (int)sizeof(TO) / TILE - 1;  // largest R with TILE (R+1) fitting
-  constexpr int R = R0 >= TILE / 2 ? TILE / 2 : (R0 >= TILE / 4 ? TILE / 4 : TILE / 8);
-  static_assert(ONE_PASS || TILE * (R + 1) * (int)sizeof(TO) <= SMEM_BYTES, "mirror staging does not fit");
+  // multi-pass mirror: pass p covers tile rows [p R, p R + R), T[jl][il - p R]
   constexpr int PASSES = TILE / R;
   for (int out = 0; out < (D2 ? 2 : 1); ++out) {
     TO* Dst = out ? D2 : D;
@@ -204,36 +243,42 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
 #pragma unroll
         for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;
             const int jl = wn * WTN + nt * 32 + li;
-            if (il / R != p) continue;
-            const float v = acc[mt][nt][r];
-            const float w = out ? al2 * v + (il + i0 == jl + j0 ? ga2 : 0.f) : v;
-            T[jl * (R + 1) + (il - p * R)] = cvt_out<TO>(w);
+            if (il0 / R != p) continue;
+            v4 pk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool dg = (il0 + q + i0 == jl + j0);
+              const float x = acc[mt][nt][4 * r4 + q];  // D's value (HAS_CE) or the product
+              float w;
+              if (out)
+                w = al2 * x + (dg ? ga2 : 0.f);  // with HAS_CE, D2 requires D = acc (host check)
+              else
+                w = HAS_CE ? x : al * x + (dg ? ga : 0.f);
+              pk[q] = cvt_out<TO>(w);
+            }
+            *(v4*)&T[jl * PITCH + (il0 - p * R)] = pk;
           }
       __syncthreads();
-      for (int g = threadIdx.x; g < TILE * R; g += nthreads) {
-        const int jl = g / R, c = g - jl * R;
-        const int il = p * R + c;
-        if (diag_tile && il >= jl) continue;
-        Dst[(int64_t)(j0 + jl) * B + i0 + il] = T[jl * (R + 1) + c];
-      }
+      mirror_readback<TO, TILE, R, PITCH>(Dst, T, B, i0, j0, p, diag_tile);
     }
   }
 }
 
-// Epilogue for binary16 outputs (no C/E operands, no second output): the tile is staged in LDS
-// (row pitch TILE + 8 halves) and written back with 16-byte row stores instead of one 2-byte store
-// per element.  SYM: a diagonal tile is made exactly symmetric inside LDS (each kept upper element
-// is written at (i, j) and (j, i)) and stored in one pass; an off-diagonal tile is stored, then
-// staged again transposed -- from the binary16 values packed in registers during the first pass,
-// so the accumulators are read once -- and stored at (tj, ti).  Monitor and status as in `epilogue`.
-// smem: TILE * (TILE + 8) halves.
+// Epilogue for binary16 outputs (no C/E operands, no second output).  Kept elements are stored
+// straight from the accumulators with 2-byte stores (lanes 0-31 cover 64 contiguous bytes of a
+// row).  SYM mirrors through LDS: in the 32x32 accumulator layout a lane's 4 consecutive r are 4
+// consecutive rows of one column, i.e. 4 consecutive halves of a row of the transposed tile, so
+// the transposed tile T[jl][il] is written with one 8-byte LDS store per 4 values and read back as
+// 16-byte rows (a diagonal tile mirrors its strict upper part only).  Monitor and status as in
+// `epilogue`.  smem: TILE * (TILE + 8) halves when SYM.
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE>
 __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                                     const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                                     char* smem) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   constexpr int PITCH = TILE + 8;
   const Epilogue& e = a.epi;
   const int B = a.B;
@@ -244,72 +289,54 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
   const int li = lane & 31, h = lane >> 5;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const bool diag_tile = SYM && tc.ti == tc.tj;
-  _Float16* S = (_Float16*)smem;
-  _Float16* Dst = (_Float16*)P.D + off;
-  const int nthreads = blockDim.x;
+  _Float16* T = (_Float16*)smem;
+  _Float16* D = (_Float16*)P.D + off;
   float mon = 0.f;
   bool bad = false;
-  uint32_t pk[MTM][MTN][8];  // the staged values, two halves per register (rows r and r + 1)
-
-  auto store_tile = [&](int r0, int c0) {
-    __syncthreads();
-    for (int g = threadIdx.x; g < TILE * TILE / 8; g += nthreads) {
-      const int row = g / (TILE / 8), c8 = g - row * (TILE / 8);
-      *(f16x8*)(Dst + (int64_t)(r0 + row) * B + c0 + 8 * c8) = *(const f16x8*)&S[row * PITCH + 8 * c8];
-    }
-  };
-
-  // pass 0: tile (ti, tj)
 #pragma unroll
   for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
     for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3
         const int jl = wn * WTN + nt * 32 + li;
-        const bool on_diag = (i0 + il == j0 + jl);
-        const float v = al * acc[mt][nt][r] + (on_diag ? ga : 0.f);
-        const _Float16 hv = (_Float16)v;
-        const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, hv);
-        if (r & 1)
-          pk[mt][nt][r >> 1] |= bits << 16;
-        else
-          pk[mt][nt][r >> 1] = bits;
-        if (diag_tile) {
-          if (il > jl) continue;
-          S[il * PITCH + jl] = hv;
-          S[jl * PITCH + il] = hv;
-        } else {
-          S[il * PITCH + jl] = hv;
+        f16x4 pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int il = il0 + q;
+          const bool on_diag = (i0 + il == j0 + jl);
+          const float v = al * acc[mt][nt][4 * r4 + q] + (on_diag ? ga : 0.f);
+          const _Float16 hv = (_Float16)v;
+          pk[q] = hv;
+          if (diag_tile && il > jl) continue;
+          D[(int64_t)(i0 + il) * B + j0 + jl] = hv;
+          bad |= !isfinite(v);
+          if (e.monitor) {
+            const float dd = v - (on_diag ? 1.f : 0.f);
+            mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
+          }
         }
-        bad |= !isfinite(v);
-        if (e.monitor) {
-          const float dd = v - (on_diag ? 1.f : 0.f);
-          mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
-        }
+        if (SYM) *(f16x4*)&T[jl * PITCH + il0] = pk;
       }
-  store_tile(i0, j0);
-  if (SYM && !diag_tile) {  // pass 1: the mirror tile (tj, ti) from the packed values
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int jl = wn * WTN + nt * 32 + li;
-          const uint16_t bits = (uint16_t)((r & 1) ? (pk[mt][nt][r >> 1] >> 16) : (pk[mt][nt][r >> 1] & 0xffffu));
-          S[jl * PITCH + il] = __builtin_bit_cast(_Float16, bits);
-        }
-    store_tile(j0, i0);
-  }
   if (e.monitor) {
     mon = wave_sum(mon);
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
   if (e.status && bad) atomicOr(&e.status[b], 2);
+  if (!SYM) return;
+  __syncthreads();
+  const int nthreads = blockDim.x;
+  for (int g = threadIdx.x; g < TILE * TILE / 8; g += nthreads) {
+    const int jl = g / (TILE / 8), c8 = g - jl * (TILE / 8);
+    const int il = 8 * c8;
+    _Float16* dst = D + (int64_t)(j0 + jl) * B + i0 + il;  // mirror element (j, i) = value at (i, j)
+    if (!diag_tile || il + 7 < jl) {
+      *(f16x8*)dst = *(const f16x8*)&T[jl * PITCH + il];
+    } else if (il < jl) {  // the chunk crossing the diagonal: strict upper part only
+      for (int q = 0; il + q < jl; ++q) dst[q] = T[jl * PITCH + il + q];
+    }
+  }
 }
 
 template <typename K>
@@ -322,7 +349,7 @@ hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream, int threads =
 
 // kernel launchers of the two precisions
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
-hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, hipStream_t stream);
+hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

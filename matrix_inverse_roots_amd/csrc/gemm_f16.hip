@@ -2,6 +2,8 @@
 // 32x32x16 fp16 MFMA (coupled Newton in half precision).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace dash {
@@ -203,12 +205,150 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
     epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
+// ------------------------------------------------------------------------------------------------
+// fp16 operands with an exactly symmetric right operand Y (Y^T = Y bitwise), 256 x 256 macro tile.
+// Then column j of Y is row j of Y, so both slices are read as rows of consecutive k with 16-byte
+// loads and no transposition.  The k-step is 32 and the global slices run DEPTH = 4 k-steps ahead
+// of the MFMAs through a ring of registers (two LDS buffers), so each workgroup keeps 128 KiB of
+// loads in flight: the products of the coupled-Newton iteration are latency-bound otherwise (one
+// workgroup per CU, and the first touch of every operand panel misses L2).
+// LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled by row/2 so that the MFMA reads
+// (8 consecutive rows, one chunk) and the stores (2 rows x 4 chunks) are free of bank conflicts.
+// ------------------------------------------------------------------------------------------------
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+__device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 1)) & 3; }
+
+template <bool SYM, typename TO>
+__global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
+  constexpr int TILE = 256, BK = 32, MT = 4, WT = 128, DEPTH = 4;
+  constexpr int SLICE = TILE * BK;  // halves of one operand slice
+  constexpr int MAIN_BYTES = 2 * 2 * SLICE * 2;
+  constexpr int STAGE_BYTES = TILE * (TILE + 8) * 2;  // binary16 output tile staged for 16-byte stores
+  constexpr int SMEM_BYTES = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  _Float16* Xs = (_Float16*)smem;  // [2][SLICE]
+  _Float16* Ys = Xs + 2 * SLICE;   // [2][SLICE]
+
+  const TileCoord tc = decode_tile(a, SYM);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const _Float16* X = (const _Float16*)P.X + off;
+  const _Float16* Y = (const _Float16*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+
+  // per k-step each thread moves 4 pieces of 16 bytes of each slice: piece c = tid + 256 r -> row
+  // c / 4, chunk c % 4 (rows i0.. of X and rows j0.. of Y, k0 .. k0 + 31)
+  f16x8 rx[DEPTH][4], ry[DEPTH][4];
+  auto gload = [&](auto slot_c, int k0) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c >> 2, ch = c & 3;
+      rx[slot][r] = *(const f16x8*)(X + (int64_t)(i0 + row) * B + k0 + 8 * ch);
+      ry[slot][r] = *(const f16x8*)(Y + (int64_t)(j0 + row) * B + k0 + 8 * ch);
+    }
+  };
+  auto sstore = [&](auto slot_c, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c >> 2, ch = c & 3;
+      const int o = buf * SLICE + row * BK + 8 * swz4(row, ch);
+      *(f16x8*)&Xs[o] = rx[slot][r];
+      *(f16x8*)&Ys[o] = ry[slot][r];
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  auto compute = [&](int buf) {
+    const _Float16* xs = Xs + buf * SLICE;
+    const _Float16* ys = Ys + buf * SLICE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int chunk = 2 * h + s;
+      f16x8 av[MT], bv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * WT + mt * 32 + li;
+        av[mt] = *(const f16x8*)&xs[row * BK + 8 * swz4(row, chunk)];
+      }
+#pragma unroll
+      for (int nt = 0; nt < MT; ++nt) {
+        const int row = wn * WT + nt * 32 + li;
+        bv[nt] = *(const f16x8*)&ys[row * BK + 8 * swz4(row, chunk)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+
+  const int KT = B / BK;  // a multiple of 8 (B % 256 == 0)
+  // Steady state: the loads of k-step kt + DEPTH go into the registers that k-step kt vacated, the
+  // MFMAs consume kt from LDS, then k-step kt + 1 moves from registers to the other LDS buffer.
+  // The loads are unconditional here (the tail below has none), so the compiler's wait before the
+  // LDS store counts only k-step kt + 1's loads and leaves the later ones in flight.
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int slot = decltype(slot_c)::value;  // == kt % DEPTH
+    gload(slot_c, (kt + DEPTH) * BK);
+    compute(slot & 1);
+    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    __syncthreads();
+  };
+  auto tail_step = [&](auto slot_c, bool store_next) {
+    constexpr int slot = decltype(slot_c)::value;
+    compute(slot & 1);
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    __syncthreads();
+  };
+  gload(IC<0>{}, 0);
+  gload(IC<1>{}, BK);
+  gload(IC<2>{}, 2 * BK);
+  gload(IC<3>{}, 3 * BK);
+  sstore(IC<0>{}, 0);
+  __syncthreads();
+  for (int kt = 0; kt + DEPTH < KT; kt += DEPTH) {
+    step(IC<0>{}, kt);
+    step(IC<1>{}, kt + 1);
+    step(IC<2>{}, kt + 2);
+    step(IC<3>{}, kt + 3);
+  }
+  tail_step(IC<0>{}, true);
+  tail_step(IC<1>{}, true);
+  tail_step(IC<2>{}, true);
+  tail_step(IC<3>{}, false);
+  if constexpr (sizeof(TO) == 2)
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+  else
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+}
+
 template <bool SYM>
-hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, hipStream_t stream) {
+hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t stream) {
   const int tile = a.B % 256 == 0 ? 256 : (a.B % 128 == 0 ? 128 : 64);
   a.tdim = a.B / tile;
   a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool half_out = out_prec == DASH_FP16;
+  if (tile == 256 && y_sym)
+    return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16>, a, stream)
+                    : launch(gemm_f16_ysym_kernel<SYM, float>, a, stream);
   if (tile == 256)
     return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16>, a, stream)
                     : launch(gemm_f16_big_kernel<SYM, float>, a, stream);
@@ -221,8 +361,8 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, hipStream_t stream) {
-  return sym ? dispatch_f16<true>(a, out_prec, stream) : dispatch_f16<false>(a, out_prec, stream);
+hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream) {
+  return sym ? dispatch_f16<true>(a, out_prec, y_sym, stream) : dispatch_f16<false>(a, out_prec, y_sym, stream);
 }
 
 }  // namespace gemm

@@ -147,6 +147,25 @@ def test_cn_fp16_tiny(tiny):
     assert np.all(to_host(status) == 0)
 
 
+@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP16])
+def test_cn_reads_only_the_upper_triangle(prec):
+    """CN builds its start terms from the upper triangle of A: garbage below the diagonal is ignored."""
+    A64, _, _ = di.known_spectrum_stack(130, 2, 256, 0.2, 1.0)
+    A = A64.astype(np.float32)
+    noisy = A.copy()
+    low = np.tril_indices(256, -1)
+    noisy[:, low[0], low[1]] += di.gaussian((2, len(low[0])), 131, 0.05)
+    s = torch.ones(2, device=DEV)
+    X_clean, _, _ = cn(to_dev(A), s, 6, prec)
+    X_noisy, _, _ = cn(to_dev(noisy), s, 6, prec)
+    assert torch.equal(X_clean, X_noisy)
+    Xh = to_host(X_noisy)
+    if prec == dash.DASH_FP16:  # triangle-only products: exactly symmetric
+        assert np.array_equal(Xh, Xh.transpose(0, 2, 1))
+    else:
+        assert np.max(np.abs(Xh - Xh.transpose(0, 2, 1))) < 1e-5 * np.abs(Xh).max()
+
+
 @pytest.mark.parametrize("B", [256, 512])
 def test_cn_fp16_wide_tiles(B):
     """B % 256 == 0 runs the 256 x 256 fp16 product tile; compare with the binary16-storage oracle."""
