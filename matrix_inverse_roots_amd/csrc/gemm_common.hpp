@@ -24,6 +24,9 @@ struct GemmArgs {
   Epilogue epi;
 };
 
+// the monitor / status code of the epilogues is compiled only into the launches that ask for it
+inline bool wants_checks(const Epilogue& e) { return e.monitor || e.status; }
+
 __device__ __forceinline__ float coef_of(const Epilogue& e, int idx, int64_t b) {
   return idx >= 0 ? e.coef[b * COEF_STRIDE + idx] : 1.f;
 }
@@ -82,7 +85,9 @@ __device__ __forceinline__ TO cvt_out(float v) {
 //   D  = alpha acc + beta C + delta E + gamma I,   D2 = alpha2 acc + gamma2 I   (per-block coefficients)
 //
 // SYM (triangle-only products): only tiles ti <= tj run, and within a diagonal tile only i <= j is
-// kept.  Each kept element is stored at (i, j) directly and at (j, i) through LDS.  In the 32x32
+// kept.  Each kept element is stored at (i, j) directly and at (j, i) through LDS (a diagonal tile
+// stores all its elements directly and the mirror then overwrites the strict lower part: stores of
+// one workgroup before and after the barrier are ordered).  In the 32x32
 // accumulator layout a lane's 4 consecutive r are 4 consecutive rows of one column, i.e. 4
 // consecutive entries of a row of the transposed tile, so the transposed tile T[jl][il] is filled
 // with one vector LDS store per 4 values and read back in 16-byte row pieces.  When T fits in
@@ -120,7 +125,8 @@ __device__ __forceinline__ void mirror_readback(TO* Dst, const TO* T, int B, int
   }
 }
 
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_CE, int TILE, int SMEM_BYTES>
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_CE, int TILE, int SMEM_BYTES,
+          bool CHECKS>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, char* smem) {
   typedef typename Vec4<TO>::type v4;
@@ -183,28 +189,30 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           if (i == j) v += ga;
           pk[q] = cvt_out<TO>(v);
           if (SYM && !ONE_PASS && HAS_CE) acc[mt][nt][r] = v;  // C/E are not re-read by the passes
-          if (diag_tile && i > j) continue;
+          // a diagonal tile stores its lower part too; the mirror overwrites it after the barrier
           const int64_t idx = (int64_t)i * B + j;
           D[idx] = cvt_out<TO>(v);
-          bad |= !isfinite(v);
+          float v2 = 0.f;
           if (D2) {
-            const float v2 = al2 * x + (i == j ? ga2 : 0.f);
+            v2 = al2 * x + (i == j ? ga2 : 0.f);
             D2[idx] = cvt_out<TO>(v2);
-            bad |= !isfinite(v2);
           }
-          if (e.monitor) {
-            const float dd = v - (i == j ? 1.f : 0.f);
-            mon += (SYM && i != j) ? 2.f * dd * dd : dd * dd;
+          if (CHECKS && !(diag_tile && i > j)) {
+            bad |= !isfinite(v) || (D2 && !isfinite(v2));
+            if (e.monitor) {
+              const float dd = v - (i == j ? 1.f : 0.f);
+              mon += (SYM && i != j) ? 2.f * dd * dd : dd * dd;
+            }
           }
         }
         if (SYM && ONE_PASS) *(v4*)&T[jl * PITCH + il0] = pk;
       }
   }
-  if (e.monitor) {
+  if (CHECKS && e.monitor) {
     mon = wave_sum(mon);
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
-  if (e.status && bad) atomicOr(&e.status[b], 2);
+  if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
   if (!SYM) return;
 
   if (ONE_PASS) {
@@ -272,9 +280,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
 // row).  SYM mirrors through LDS: in the 32x32 accumulator layout a lane's 4 consecutive r are 4
 // consecutive rows of one column, i.e. 4 consecutive halves of a row of the transposed tile, so
 // the transposed tile T[jl][il] is written with one 8-byte LDS store per 4 values and read back as
-// 16-byte rows (a diagonal tile mirrors its strict upper part only).  Monitor and status as in
-// `epilogue`.  smem: TILE * (TILE + 8) halves when SYM.
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE>
+// 16-byte rows (a diagonal tile stores everything directly and the mirror then overwrites its
+// strict lower part).  Monitor and status (CHECKS) as in `epilogue`.  smem: TILE * (TILE + 8)
+// halves when SYM.
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE, bool CHECKS>
 __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                                     const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                                     char* smem) {
@@ -309,21 +318,23 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
           const float v = al * acc[mt][nt][4 * r4 + q] + (on_diag ? ga : 0.f);
           const _Float16 hv = (_Float16)v;
           pk[q] = hv;
-          if (diag_tile && il > jl) continue;
+          // a diagonal tile stores its lower part too; the mirror overwrites it after the barrier
           D[(int64_t)(i0 + il) * B + j0 + jl] = hv;
-          bad |= !isfinite(v);
-          if (e.monitor) {
-            const float dd = v - (on_diag ? 1.f : 0.f);
-            mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
+          if (CHECKS && !(diag_tile && il > jl)) {
+            bad |= !isfinite(v);
+            if (e.monitor) {
+              const float dd = v - (on_diag ? 1.f : 0.f);
+              mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
+            }
           }
         }
         if (SYM) *(f16x4*)&T[jl * PITCH + il0] = pk;
       }
-  if (e.monitor) {
+  if (CHECKS && e.monitor) {
     mon = wave_sum(mon);
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
-  if (e.status && bad) atomicOr(&e.status[b], 2);
+  if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
   if (!SYM) return;
   __syncthreads();
   const int nthreads = blockDim.x;

@@ -10,7 +10,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, bool SYM, typename TO>
+template <int TILE, bool SYM, typename TO, bool CHECKS>
 __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int WT = TILE / 2;
@@ -90,9 +90,9 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
     __syncthreads();
   }
   if constexpr (sizeof(TO) == 2)
-    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row ^ (row >> 3))) & 7; }
 
-template <bool SYM, typename TO>
+template <bool SYM, typename TO, bool CHECKS>
 __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 64, MT = 4, WT = 128;
   // double-buffered X and Y slices (128 KiB); a little more so a mirrored binary16 tile fits whole
@@ -200,9 +200,9 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
     __syncthreads();
   }
   if constexpr (sizeof(TO) == 2)
-    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -220,7 +220,7 @@ using IC = std::integral_constant<int, V>;
 
 __device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 1)) & 3; }
 
-template <bool SYM, typename TO>
+template <bool SYM, typename TO, bool CHECKS>
 __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 32, MT = 4, WT = 128, DEPTH = 4;
   constexpr int SLICE = TILE * BK;  // halves of one operand slice
@@ -335,34 +335,36 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   tail_step(IC<2>{}, true);
   tail_step(IC<3>{}, false);
   if constexpr (sizeof(TO) == 2)
-    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
-template <bool SYM>
+template <bool SYM, bool CHECKS>
 hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t stream) {
   const int tile = a.B % 256 == 0 ? 256 : (a.B % 128 == 0 ? 128 : 64);
   a.tdim = a.B / tile;
   a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool half_out = out_prec == DASH_FP16;
   if (tile == 256 && y_sym)
-    return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16>, a, stream)
-                    : launch(gemm_f16_ysym_kernel<SYM, float>, a, stream);
+    return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS>, a, stream)
+                    : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS>, a, stream);
   if (tile == 256)
-    return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16>, a, stream)
-                    : launch(gemm_f16_big_kernel<SYM, float>, a, stream);
+    return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16, CHECKS>, a, stream)
+                    : launch(gemm_f16_big_kernel<SYM, float, CHECKS>, a, stream);
   if (tile == 128)
-    return half_out ? launch(gemm_f16_kernel<128, SYM, _Float16>, a, stream)
-                    : launch(gemm_f16_kernel<128, SYM, float>, a, stream);
-  return half_out ? launch(gemm_f16_kernel<64, SYM, _Float16>, a, stream)
-                  : launch(gemm_f16_kernel<64, SYM, float>, a, stream);
+    return half_out ? launch(gemm_f16_kernel<128, SYM, _Float16, CHECKS>, a, stream)
+                    : launch(gemm_f16_kernel<128, SYM, float, CHECKS>, a, stream);
+  return half_out ? launch(gemm_f16_kernel<64, SYM, _Float16, CHECKS>, a, stream)
+                  : launch(gemm_f16_kernel<64, SYM, float, CHECKS>, a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream) {
-  return sym ? dispatch_f16<true>(a, out_prec, y_sym, stream) : dispatch_f16<false>(a, out_prec, y_sym, stream);
+  if (wants_checks(a.epi))
+    return sym ? dispatch_f16<true, true>(a, out_prec, y_sym, stream) : dispatch_f16<false, true>(a, out_prec, y_sym, stream);
+  return sym ? dispatch_f16<true, false>(a, out_prec, y_sym, stream) : dispatch_f16<false, false>(a, out_prec, y_sym, stream);
 }
 
 }  // namespace gemm

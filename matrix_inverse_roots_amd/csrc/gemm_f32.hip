@@ -14,7 +14,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, int TX, int TY, bool SYM, typename TO>
+template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BK = 32;
   constexpr int WT = TILE / 2;
@@ -120,27 +120,29 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
-  epilogue<MT, MT, WT, WT, SYM, TO, true, TILE, SMEM_BYTES>(a, tc, P, acc, wm, wn, lane, smem);
+  epilogue<MT, MT, WT, WT, SYM, TO, true, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
-template <int TILE>
+template <int TILE, bool CHECKS>
 hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
   a.tdim = a.B / TILE;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   if (trans == Trans::NN) {
-    if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float>, a, stream);
-    return launch(gemm_f32_kernel<TILE, 0, 0, false, float>, a, stream);
+    if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS>, a, stream);
+    return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS>, a, stream);
   }
   if (!sym) return hipErrorInvalidValue;
-  if (trans == Trans::NT) return launch(gemm_f32_kernel<TILE, 0, 1, true, float>, a, stream);
-  return launch(gemm_f32_kernel<TILE, 1, 0, true, float>, a, stream);
+  if (trans == Trans::NT) return launch(gemm_f32_kernel<TILE, 0, 1, true, float, CHECKS>, a, stream);
+  return launch(gemm_f32_kernel<TILE, 1, 0, true, float, CHECKS>, a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
-  if (a.B % 128 == 0) return dispatch_f32<128>(a, trans, sym, stream);
-  return dispatch_f32<64>(a, trans, sym, stream);
+  const bool checks = wants_checks(a.epi);
+  if (a.B % 128 == 0)
+    return checks ? dispatch_f32<128, true>(a, trans, sym, stream) : dispatch_f32<128, false>(a, trans, sym, stream);
+  return checks ? dispatch_f32<64, true>(a, trans, sym, stream) : dispatch_f32<64, false>(a, trans, sym, stream);
 }
 
 }  // namespace gemm
