@@ -312,11 +312,7 @@ dash_status dash_stack(const dash_mat* grads, int32_t n, int32_t B, float* G_sta
   dash_status st = check_mats(grads, n, B, &tiles);
   if (st != DASH_OK) return st;
   if (!G_stack || !aligned(G_stack, 16)) return DASH_ERR_INVALID_ARG;
-  int64_t first = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    TRY(launch_tile_copy(grads[i], B, G_stack, first, true, nullptr, as_stream(stream)));
-    first += (grads[i].rows / B) * (grads[i].cols / B);
-  }
+  TRY(launch_tile_copy(grads, n, B, G_stack, true, as_stream(stream)));
   return DASH_OK;
 }
 
@@ -325,11 +321,7 @@ dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, 
   dash_status st = check_mats(outs, n, B, &tiles);
   if (st != DASH_OK) return st;
   if (!U_stack || !aligned(U_stack, 16)) return DASH_ERR_INVALID_ARG;
-  int64_t first = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    TRY(launch_tile_copy(outs[i], B, nullptr, first, false, U_stack, as_stream(stream)));
-    first += (outs[i].rows / B) * (outs[i].cols / B);
-  }
+  TRY(launch_tile_copy(outs, n, B, const_cast<float*>(U_stack), false, as_stream(stream)));
   return DASH_OK;
 }
 

@@ -118,9 +118,18 @@ struct PowerPlan {
 hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
 size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
 
-// Stack / unstack one weight: tiles (rows/B) x (cols/B) into consecutive blocks starting at `first`.
-hipError_t launch_tile_copy(const dash_mat& w, int B, float* stack, int64_t first, bool to_stack,
-                            const float* from_stack, hipStream_t stream);
+// Stack / unstack n weights: the (rows/B) x (cols/B) tiles of each, in order, into consecutive
+// blocks of `stack` (to_stack) or back out of it.  One launch per COPY_GROUP weights.
+constexpr int COPY_GROUP = 32;
+struct CopyGroup {
+  float* ptr[COPY_GROUP];
+  int64_t ld[COPY_GROUP];
+  int64_t row_base[COPY_GROUP + 1];  // first stack row (tile * B + r) of weight i in this launch
+  int32_t wg_base[COPY_GROUP + 1];   // first workgroup of weight i
+  int32_t tiles_c[COPY_GROUP];       // tile columns of weight i
+  int32_t n;
+};
+hipError_t launch_tile_copy(const dash_mat* w, int n, int B, float* stack, bool to_stack, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -192,24 +192,44 @@ __global__ void monitor_finish_kernel(float* m, int64_t n, float inv_sqrt_b) {
 }
 
 // Copy one weight's tiles to (to_stack) or from the stack.  Workgroup = 8 rows of one tile.
-__global__ __launch_bounds__(256) void tile_copy_kernel(float* w, int64_t rows, int64_t cols, int64_t ld, int B,
-                                                        float* stack, const float* from_stack, int64_t first,
-                                                        int to_stack) {
-  const int64_t tiles_c = cols / B;
-  const int row_groups = B / 8;
-  const int64_t t = blockIdx.x / row_groups;
-  const int rg = (int)(blockIdx.x - t * row_groups);
-  const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
-  const int vec_per_row = B / 4;
-  for (int v = threadIdx.x; v < 8 * vec_per_row; v += 256) {
-    const int r = rg * 8 + v / vec_per_row;
-    const int c4 = v % vec_per_row;
-    float* wp = w + (tr * B + r) * ld + tc * B + 4 * c4;
-    const int64_t so = (first + t) * (int64_t)B * B + (int64_t)r * B + 4 * c4;
-    if (to_stack)
-      *(f32x4*)(stack + so) = *(const f32x4*)wp;
-    else
-      *(f32x4*)wp = *(const f32x4*)(from_stack + so);
+// Stack / unstack.  The stack side of a copy is one linear stream, so each workgroup moves
+// COPY_VEC * 256 consecutive float4 of it and gathers them from (or scatters them to) the rows of
+// the weight they belong to.  All loads of a thread are issued before its stores, and both are
+// non-temporal: the data is streamed once and is far larger than the caches.  A launch covers up
+// to COPY_GROUP weights; the weight of a workgroup comes from the prefix table in the arguments.
+constexpr int COPY_VEC = 4;
+
+template <bool TO_STACK>
+__global__ __launch_bounds__(256) void tile_copy_kernel(CopyGroup g, int B, float* stack) {
+  const int wg = blockIdx.x;
+  int wi = 0;
+  while (wi + 1 < g.n && wg >= g.wg_base[wi + 1]) ++wi;
+  const unsigned vpr = (unsigned)B / 4;  // float4 per tile row
+  const int64_t total = (g.row_base[wi + 1] - g.row_base[wi]) * vpr;
+  const int64_t q0 = (int64_t)(wg - g.wg_base[wi]) * (256 * COPY_VEC);
+  const int64_t row0 = q0 / vpr;
+  const unsigned c0 = (unsigned)(q0 - row0 * vpr);
+  const int64_t t0 = row0 / B;
+  const unsigned r0 = (unsigned)(row0 - t0 * B);
+  const unsigned tiles_c = (unsigned)g.tiles_c[wi];
+  const int64_t ld = g.ld[wi];
+  f32x4* lin = (f32x4*)(stack + g.row_base[wi] * B) + q0;
+  f32x4* wp[COPY_VEC];
+  f32x4 v[COPY_VEC];
+#pragma unroll
+  for (int i = 0; i < COPY_VEC; ++i) {
+    const unsigned d = i * 256 + threadIdx.x;
+    const unsigned dr = (c0 + d) / vpr, c4 = c0 + d - dr * vpr;
+    const unsigned rr = r0 + dr, tt = rr / (unsigned)B, r = rr - tt * (unsigned)B;
+    const unsigned t = (unsigned)t0 + tt;  // tiles per weight < 2^31 (checked on the host)
+    const unsigned tr = t / tiles_c, tc = t - tr * tiles_c;
+    wp[i] = (f32x4*)(g.ptr[wi] + ((int64_t)tr * B + r) * ld + (int64_t)tc * B) + c4;
+    if (q0 + d < total) v[i] = __builtin_nontemporal_load(TO_STACK ? wp[i] : lin + d);
+  }
+#pragma unroll
+  for (int i = 0; i < COPY_VEC; ++i) {
+    const unsigned d = i * 256 + threadIdx.x;
+    if (q0 + d < total) __builtin_nontemporal_store(v[i], TO_STACK ? lin + d : wp[i]);
   }
 }
 
@@ -254,15 +274,37 @@ hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_tile_copy(const dash_mat& w, int B, float* stack, int64_t first, bool to_stack,
-                            const float* from_stack, hipStream_t stream) {
-  const int64_t tiles = (w.rows / B) * (w.cols / B);
-  if (tiles == 0) return hipSuccess;
-  const int64_t grid = tiles * (B / 8);
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tile_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w.ptr, w.rows, w.cols, w.ld, B,
-                     stack, from_stack, first, to_stack ? 1 : 0);
-  return hipGetLastError();
+hipError_t launch_tile_copy(const dash_mat* w, int n, int B, float* stack, bool to_stack, hipStream_t stream) {
+  const int64_t f4_per_wg = 256 * COPY_VEC;
+  for (int i0 = 0; i0 < n; i0 += COPY_GROUP) {
+    CopyGroup g{};
+    g.n = n - i0 < COPY_GROUP ? n - i0 : COPY_GROUP;
+    int64_t wgs = 0;
+    g.row_base[0] = 0;
+    g.wg_base[0] = 0;
+    for (int j = 0; j < g.n; ++j) {
+      const dash_mat& m = w[i0 + j];
+      const int64_t tiles = (m.rows / B) * (m.cols / B);
+      if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+      g.ptr[j] = m.ptr;
+      g.ld[j] = m.ld;
+      g.tiles_c[j] = (int32_t)(m.cols / B);
+      g.row_base[j + 1] = g.row_base[j] + tiles * B;
+      wgs += (tiles * B * (B / 4) + f4_per_wg - 1) / f4_per_wg;
+      if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+      g.wg_base[j + 1] = (int32_t)wgs;
+    }
+    if (wgs > 0) {
+      if (to_stack)
+        hipLaunchKernelGGL(tile_copy_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, stream, g, B, stack);
+      else
+        hipLaunchKernelGGL(tile_copy_kernel<false>, dim3((unsigned)wgs), dim3(256), 0, stream, g, B, stack);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    stack += g.row_base[g.n] * B;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dash

@@ -278,6 +278,24 @@ def test_stack_unstack_round_trip():
         assert np.array_equal(to_host(o), w.astype(np.float64))
 
 
+@pytest.mark.parametrize("B", [64, 192])
+def test_stack_many_weights(B):
+    # 37 weights: more than one launch takes (32); with B = 192 a workgroup's chunk of the stack
+    # straddles tile rows and tiles.  Unstack writes into strided views; the rest stays untouched.
+    shapes = [(B * (1 + i % 3), B * (1 + (i * 7) % 4)) for i in range(37)]
+    W = [di.gaussian(s, 200 + i) for i, s in enumerate(shapes)]
+    n = di.num_tiles(shapes, B)
+    S = torch.empty((n, B, B), device=DEV)
+    dash.dash_stack([to_dev(w) for w in W], B, S)
+    assert np.array_equal(to_host(S), oracle.stack(W, B).astype(np.float64))
+    bigs = [torch.full((r, c + 64), -7.0, device=DEV) for r, c in shapes]
+    dash.dash_unstack(S, B, [b[:, 32:32 + c] for b, (r, c) in zip(bigs, shapes)])
+    for b, w, (r, c) in zip(bigs, W, shapes):
+        h = to_host(b)
+        assert np.array_equal(h[:, 32:32 + c], w.astype(np.float64))
+        assert np.all(h[:, :32] == -7.0) and np.all(h[:, 32 + c:] == -7.0)
+
+
 def test_stack_strided_rows():
     B = 64
     big = to_dev(di.gaussian((128, 256), 110))
