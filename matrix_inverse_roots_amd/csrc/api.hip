@@ -367,7 +367,7 @@ dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, d
   const int RB = B / 64;
   for (int q = 0; q < 2; ++q) p.W[q] = (float*)cv.take((size_t)N * B * 32 * sizeof(float));
   for (int q = 0; q < 2; ++q) p.part[q] = (float*)cv.take((size_t)N * RB * 3 * 32 * sizeof(float));
-  p.v0inv = (float*)cv.take(256);
+  p.V0p = (float*)cv.take((size_t)B * 32 * sizeof(float));
   p.coef = (float*)cv.take((size_t)N * COEF_STRIDE * sizeof(float));
   p.Ah = prec == DASH_FP16 ? (_Float16*)cv.take((size_t)N * B * B * sizeof(_Float16)) : nullptr;
   TRY(launch_power_iteration(p, as_stream(stream)));

@@ -111,7 +111,7 @@ struct PowerPlan {
   // workspace pieces
   float* W[2];       // [N, B, 32] fp32 iterates
   float* part[2];    // [N, B/128, 3, 32] partial column sums
-  float* v0inv;      // [32] inverse norms of the start vectors
+  float* V0p;        // [B, 32] normalised start vectors, zero columns from k on
   float* coef;       // [N, COEF_STRIDE] (prescale for binary16)
   _Float16* Ah;      // [N, B, B] binary16 operand (prec == DASH_FP16)
 };

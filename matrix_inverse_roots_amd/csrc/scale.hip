@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "dash_internal.hpp"
 
@@ -63,20 +64,31 @@ __global__ __launch_bounds__(1024) void frobenius_kernel(const float* A, int B, 
 // Power iteration
 // ------------------------------------------------------------------------------------------------
 
-// inverse column norms of the shared start vectors V0[B, k]; zero for padding columns j >= k
-__global__ void v0_inverse_norms_kernel(const float* V0, int B, int k, float* inv) {
-  const int j = threadIdx.x;
-  if (j >= KV) return;
-  if (j >= k) {
-    inv[j] = 0.f;
-    return;
-  }
+// Start vectors: V0p[B, KV] = V0[:, j] / ||V0[:, j]|| for j < k, zero columns after (so every step
+// reads a [B, KV] iterate with 16-byte loads).  One workgroup: 32 threads per column reduce in
+// double, then all threads write the normalised copy.
+__global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, int B, int k, float* V0p) {
+  const int j = threadIdx.x % KV, part = threadIdx.x / KV;
+  __shared__ double sq[32][KV];
+  __shared__ float inv[KV];
   double acc = 0.0;
-  for (int i = 0; i < B; ++i) {
-    const double v = V0[(int64_t)i * k + j];
-    acc += v * v;
+  if (j < k)
+    for (int i = part; i < B; i += 32) {
+      const double v = V0[(int64_t)i * k + j];
+      acc += v * v;
+    }
+  sq[part][j] = acc;
+  __syncthreads();
+  if (threadIdx.x < KV) {
+    double t = 0.0;
+    for (int q = 0; q < 32; ++q) t += sq[q][threadIdx.x];
+    inv[threadIdx.x] = threadIdx.x < k ? (float)(1.0 / sqrt(t)) : 0.f;
   }
-  inv[j] = (float)(1.0 / sqrt(acc));
+  __syncthreads();
+  for (int e = threadIdx.x; e < B * KV; e += 1024) {
+    const int i = e / KV, jj = e % KV;
+    V0p[e] = jj < k ? V0[(int64_t)i * k + jj] * inv[jj] : 0.f;
+  }
 }
 
 // binary16 prescale per block: coef[P2] = 2^-e, coef[P2INV] = 2^e, e = ceil(log2 max diag)
@@ -109,36 +121,75 @@ __global__ void half_prescale_kernel(const float* A, int64_t N, int B, float* co
 template <typename TI>
 struct PowerStepArgs {
   const TI* A;          // [N, B, B]
-  const float* Vsrc;    // [*, B, vld]: block stride vstride (0: shared start vectors)
+  const float* Vsrc;    // [*, B, KV] iterate: block stride vstride (0: the prepared start vectors)
   int64_t vstride;
-  int vld;
-  const float* v0inv;   // inverse norms of the shared start vectors (first step), or null
-  const float* part_in; // partials of the previous step [N, RB, 3, KV] (later steps)
+  const float* part_in; // partials of the previous step [N, RB, 3, KV], or null on the first step
   float* W;             // [N, B, KV]
   float* part_out;      // [N, RB, 3, KV]
   int B, k, RB;         // RB = row blocks per block
 };
 
-// inverse norm of column j of the current V for block b
+// inverse norm of column j of the current V for block b (the start vectors come normalised)
 template <typename TI>
 __device__ __forceinline__ float col_inv_norm(const PowerStepArgs<TI>& a, int64_t b, int j) {
   if (j >= a.k) return 0.f;
-  if (a.v0inv) return a.v0inv[j];
+  if (!a.part_in) return 1.f;
   const float* p = a.part_in + b * (int64_t)a.RB * 3 * KV;
   double ww = 0.0;
   for (int rb = 0; rb < a.RB; ++rb) ww += p[rb * 3 * KV + j];
   return (float)(1.0 / sqrt(ww));
 }
 
-template <typename TI>
-__device__ __forceinline__ float stage_v(float v) {
-  return (float)(TI)v;  // binary16 rounding of the iterate when TI is _Float16
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Column partial sums (w.w, v.w, v.v) of this workgroup's rows of W = A V, and the W rows
+// themselves.  acc: the wave's 32 x 32 MFMA tile (rows wave*32.., column li).
+template <int WAVES, bool HALF>
+__device__ __forceinline__ void power_epilogue(const float* V, float* W, float* part_out, const f32x16& acc, int r0,
+                                               int wave, int lane, float invj, int k, float (*red)[3][KV]) {
+  const int li = lane & 31, h = lane >> 5, j = li;
+  float ww = 0.f, vw = 0.f, vv = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = r0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+    const float w = acc[r];
+    W[(int64_t)i * KV + j] = w;
+    float v = (j < k) ? V[(int64_t)i * KV + j] * invj : 0.f;
+    if (HALF) v = (float)(_Float16)v;  // the binary16 iterate the product used
+    ww += w * w;
+    vw += v * w;
+    vv += v * v;
+  }
+  ww += __shfl_xor(ww, 32, 64);
+  vw += __shfl_xor(vw, 32, 64);
+  vv += __shfl_xor(vv, 32, 64);
+  if (h == 0) {
+    red[wave][0][j] = ww;
+    red[wave][1][j] = vw;
+    red[wave][2][j] = vv;
+  }
+  __syncthreads();
+  const int tid = wave * 64 + lane;
+  if (tid < 3 * KV) {
+    const int q = tid / KV, jj = tid % KV;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += red[w][q][jj];
+    part_out[q * KV + jj] = t;
+  }
 }
 
-// WAVES waves, each 32 rows x 32 columns; the workgroup covers RT = 32 * WAVES rows of block b.
-template <int WAVES>
+// One power step W = A_b V_b (fp32 operands).  WAVES waves, each 32 rows x 32 columns; the
+// workgroup covers RT = 32 * WAVES rows of block b and streams them in k-slices of BK = 32.
+// Slices are loaded DEPTH slices ahead into a register ring (DEPTH divides B / BK), so up to
+// DEPTH * 16 KiB of A per workgroup is in flight while the MFMAs run on the slice in LDS.
+template <int WAVES, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float> a) {
+  constexpr int NT = 64 * WAVES;
   constexpr int RT = 32 * WAVES, BK = 32, LDA = BK + 4, LDV = KV + 4;
+  constexpr int NLA = RT * BK / 4 / NT;  // float4 loads of the A slice per thread (4)
+  constexpr int NLV = BK * KV / 4 / NT;  // float4 loads of the V slice per thread (1 or 2)
   __shared__ __attribute__((aligned(16))) float As[2][RT * LDA];
   __shared__ __attribute__((aligned(16))) float Vs[2][BK * LDV];
   __shared__ float inv_s[KV];
@@ -151,51 +202,45 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float
   const float* A = a.A + b * (int64_t)B * B;
   const float* V = a.Vsrc + b * a.vstride;
   if (tid < KV) inv_s[tid] = col_inv_norm(a, b, tid);
-  __syncthreads();
 
-  constexpr int NLA = RT * BK / 4 / (64 * WAVES);  // float4 loads of the A slice per thread (= 4)
-  f32x4 ra[NLA];
-  float rv[BK * KV / (64 * WAVES)];
-  constexpr int NV = BK * KV / (64 * WAVES);
-  auto gload = [&](int k0) {
+  f32x4 ra[DEPTH][NLA], rv[DEPTH][NLV];
+  auto gload = [&](auto slot_c, int k0) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < NLA; ++r) {
-      const int f = tid + 64 * WAVES * r;
+      const int f = tid + NT * r;
       const int row = f / (BK / 4), c4 = f % (BK / 4);
-      ra[r] = *(const f32x4*)(A + (int64_t)(r0 + row) * B + k0 + 4 * c4);
+      ra[slot][r] = *(const f32x4*)(A + (int64_t)(r0 + row) * B + k0 + 4 * c4);
     }
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int f = tid + 64 * WAVES * r;
-      const int kr = f / KV, j = f % KV;
-      rv[r] = (j < a.k) ? V[(int64_t)(k0 + kr) * a.vld + j] : 0.f;
+    for (int r = 0; r < NLV; ++r) {
+      const int f = tid + NT * r;
+      const int kr = f / (KV / 4), c4 = f % (KV / 4);
+      rv[slot][r] = *(const f32x4*)(V + (int64_t)(k0 + kr) * KV + 4 * c4);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](auto slot_c, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < NLA; ++r) {
-      const int f = tid + 64 * WAVES * r;
+      const int f = tid + NT * r;
       const int row = f / (BK / 4), c4 = f % (BK / 4);
-      *(f32x4*)&As[buf][row * LDA + 4 * c4] = ra[r];
+      *(f32x4*)&As[buf][row * LDA + 4 * c4] = ra[slot][r];
     }
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int f = tid + 64 * WAVES * r;
-      const int kr = f / KV, j = f % KV;
-      Vs[buf][kr * LDV + j] = rv[r] * inv_s[j];
+    for (int r = 0; r < NLV; ++r) {
+      const int f = tid + NT * r;
+      const int kr = f / (KV / 4), c4 = f % (KV / 4);
+      f32x4 v = rv[slot][r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= inv_s[4 * c4 + e];
+      *(f32x4*)&Vs[buf][kr * LDV + 4 * c4] = v;
     }
   };
-
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int KT = B / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const f32x4 av = *(const f32x4*)&As[buf][(wave * 32 + li) * LDA + h * 16 + 4 * s4];
@@ -205,48 +250,65 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv, acc, 0, 0, 0);
       }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+  const int KT = B / BK;
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int slot = decltype(slot_c)::value;
+    gload(slot_c, (kt + DEPTH) * BK);  // slot held slice kt, already in LDS
+    compute(kt & 1);
+    sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
+  };
+  auto tail_step = [&](auto slot_c, int kt, bool store_next) {
+    constexpr int slot = decltype(slot_c)::value;
+    compute(kt & 1);
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
+    __syncthreads();
+  };
+  gload(IC<0>{}, 0);
+  if constexpr (DEPTH > 1) gload(IC<1>{}, BK);
+  if constexpr (DEPTH > 2) {
+    gload(IC<2>{}, 2 * BK);
+    gload(IC<3>{}, 3 * BK);
   }
-
-  // epilogue: W rows, column partial sums of this workgroup's rows
-  const int j = li;
-  const float invj = inv_s[j];
-  float ww = 0.f, vw = 0.f, vv = 0.f;
-  float* Wb = a.W + b * (int64_t)B * KV;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = r0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    const float w = acc[r];
-    Wb[(int64_t)i * KV + j] = w;
-    const float v = (j < a.k) ? V[(int64_t)i * a.vld + j] * invj : 0.f;
-    ww += w * w;
-    vw += v * w;
-    vv += v * v;
-  }
-  ww += __shfl_xor(ww, 32, 64);
-  vw += __shfl_xor(vw, 32, 64);
-  vv += __shfl_xor(vv, 32, 64);
-  if (h == 0) {
-    red[wave][0][j] = ww;
-    red[wave][1][j] = vw;
-    red[wave][2][j] = vv;
-  }
+  __syncthreads();  // inv_s
+  sstore(IC<0>{}, 0);
   __syncthreads();
-  if (tid < 3 * KV) {
-    const int q = tid / KV, jj = tid % KV;
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) t += red[w][q][jj];
-    a.part_out[(b * a.RB + rb) * 3 * KV + q * KV + jj] = t;
+  int kt = 0;
+  // steady state: DEPTH divides KT, so the loop and the tail cover every slice exactly once
+  for (; kt + DEPTH < KT; kt += DEPTH) {
+    step(IC<0>{}, kt);
+    if constexpr (DEPTH > 1) step(IC<1>{}, kt + 1);
+    if constexpr (DEPTH > 2) {
+      step(IC<2>{}, kt + 2);
+      step(IC<3>{}, kt + 3);
+    }
   }
+  if constexpr (DEPTH == 1) {
+    tail_step(IC<0>{}, kt, false);
+  } else if constexpr (DEPTH == 2) {
+    tail_step(IC<0>{}, kt, true);
+    tail_step(IC<1>{}, kt + 1, false);
+  } else {
+    tail_step(IC<0>{}, kt, true);
+    tail_step(IC<1>{}, kt + 1, true);
+    tail_step(IC<2>{}, kt + 2, true);
+    tail_step(IC<3>{}, kt + 3, false);
+  }
+  power_epilogue<WAVES, false>(V, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0,
+                               wave, lane, inv_s[li], a.k, red);
 }
 
-template <int WAVES>
+// Binary16 operands: A_b prescaled in binary16, V rounded to binary16 as it is staged (transposed,
+// Vs[j][k]); k-slices of BK = 64; fp32 accumulation.  Same ring as the fp32 step.
+template <int WAVES, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Float16> a) {
+  constexpr int NT = 64 * WAVES;
   constexpr int RT = 32 * WAVES, BK = 64, LDA = BK + 8, LDV = BK + 8;
+  constexpr int NLA = RT * BK / 8 / NT;  // 16-byte loads of the A slice per thread (4)
+  constexpr int NLV = BK * KV / 4 / NT;  // float4 loads of the V slice per thread (2 or 4)
   __shared__ __attribute__((aligned(16))) _Float16 As[2][RT * LDA];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KV * LDV];  // transposed: Vs[j][k]
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KV * LDV];
   __shared__ float inv_s[KV];
   __shared__ float red[WAVES][3][KV];
   const int64_t b = blockIdx.x / a.RB;
@@ -257,91 +319,96 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Floa
   const _Float16* A = a.A + b * (int64_t)B * B;
   const float* V = a.Vsrc + b * a.vstride;
   if (tid < KV) inv_s[tid] = col_inv_norm(a, b, tid);
-  __syncthreads();
 
-  constexpr int NLA = RT * BK / 8 / (64 * WAVES);  // 16-byte loads of the A slice per thread (= 4)
-  constexpr int NV = BK * KV / (64 * WAVES);
-  f16x8 ra[NLA];
-  float rv[NV];
-  auto gload = [&](int k0) {
+  f16x8 ra[DEPTH][NLA];
+  f32x4 rv[DEPTH][NLV];
+  auto gload = [&](auto slot_c, int k0) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < NLA; ++r) {
-      const int f = tid + 64 * WAVES * r;
+      const int f = tid + NT * r;
       const int row = f / (BK / 8), c8 = f % (BK / 8);
-      ra[r] = *(const f16x8*)(A + (int64_t)(r0 + row) * B + k0 + 8 * c8);
+      ra[slot][r] = *(const f16x8*)(A + (int64_t)(r0 + row) * B + k0 + 8 * c8);
     }
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int f = tid + 64 * WAVES * r;
-      const int kr = f / KV, j = f % KV;
-      rv[r] = (j < a.k) ? V[(int64_t)(k0 + kr) * a.vld + j] : 0.f;
+    for (int r = 0; r < NLV; ++r) {
+      const int f = tid + NT * r;
+      const int kr = f / (KV / 4), c4 = f % (KV / 4);
+      rv[slot][r] = *(const f32x4*)(V + (int64_t)(k0 + kr) * KV + 4 * c4);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](auto slot_c, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < NLA; ++r) {
-      const int f = tid + 64 * WAVES * r;
+      const int f = tid + NT * r;
       const int row = f / (BK / 8), c8 = f % (BK / 8);
-      *(f16x8*)&As[buf][row * LDA + 8 * c8] = ra[r];
+      *(f16x8*)&As[buf][row * LDA + 8 * c8] = ra[slot][r];
     }
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int f = tid + 64 * WAVES * r;
-      const int kr = f / KV, j = f % KV;
-      Vs[buf][j * LDV + kr] = (_Float16)(rv[r] * inv_s[j]);
+    for (int r = 0; r < NLV; ++r) {
+      const int f = tid + NT * r;
+      const int kr = f / (KV / 4), c4 = f % (KV / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Vs[buf][(4 * c4 + e) * LDV + kr] = (_Float16)(rv[slot][r][e] * inv_s[4 * c4 + e]);
     }
   };
-
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int KT = B / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const f16x8 av = *(const f16x8*)&As[buf][(wave * 32 + li) * LDA + h * 32 + 8 * s];
       const f16x8 bv = *(const f16x8*)&Vs[buf][li * LDV + h * 32 + 8 * s];
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+  const int KT = B / BK;
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int slot = decltype(slot_c)::value;
+    gload(slot_c, (kt + DEPTH) * BK);
+    compute(kt & 1);
+    sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
+  };
+  auto tail_step = [&](auto slot_c, int kt, bool store_next) {
+    constexpr int slot = decltype(slot_c)::value;
+    compute(kt & 1);
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
+    __syncthreads();
+  };
+  gload(IC<0>{}, 0);
+  if constexpr (DEPTH > 1) gload(IC<1>{}, BK);
+  if constexpr (DEPTH > 2) {
+    gload(IC<2>{}, 2 * BK);
+    gload(IC<3>{}, 3 * BK);
   }
-
-  const int j = li;
-  const float invj = inv_s[j];
-  float ww = 0.f, vw = 0.f, vv = 0.f;
-  float* Wb = a.W + b * (int64_t)B * KV;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = r0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    const float w = acc[r];
-    Wb[(int64_t)i * KV + j] = w;
-    const float v = (j < a.k) ? stage_v<_Float16>(V[(int64_t)i * a.vld + j] * invj) : 0.f;
-    ww += w * w;
-    vw += v * w;
-    vv += v * v;
-  }
-  ww += __shfl_xor(ww, 32, 64);
-  vw += __shfl_xor(vw, 32, 64);
-  vv += __shfl_xor(vv, 32, 64);
-  if (h == 0) {
-    red[wave][0][j] = ww;
-    red[wave][1][j] = vw;
-    red[wave][2][j] = vv;
-  }
+  __syncthreads();  // inv_s
+  sstore(IC<0>{}, 0);
   __syncthreads();
-  if (tid < 3 * KV) {
-    const int q = tid / KV, jj = tid % KV;
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) t += red[w][q][jj];
-    a.part_out[(b * a.RB + rb) * 3 * KV + q * KV + jj] = t;
+  int kt = 0;
+  for (; kt + DEPTH < KT; kt += DEPTH) {
+    step(IC<0>{}, kt);
+    if constexpr (DEPTH > 1) step(IC<1>{}, kt + 1);
+    if constexpr (DEPTH > 2) {
+      step(IC<2>{}, kt + 2);
+      step(IC<3>{}, kt + 3);
+    }
   }
+  if constexpr (DEPTH == 1) {
+    tail_step(IC<0>{}, kt, false);
+  } else if constexpr (DEPTH == 2) {
+    tail_step(IC<0>{}, kt, true);
+    tail_step(IC<1>{}, kt + 1, false);
+  } else {
+    tail_step(IC<0>{}, kt, true);
+    tail_step(IC<1>{}, kt + 1, true);
+    tail_step(IC<2>{}, kt + 2, true);
+    tail_step(IC<3>{}, kt + 3, false);
+  }
+  power_epilogue<WAVES, true>(V, a.W + b * (int64_t)B * KV,
+                              a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave, lane, inv_s[li], a.k, red);
 }
 
 // s_b = scale_b * max_{j<k} (v.w / v.v) from the last step's partials
@@ -378,7 +445,7 @@ size_t power_workspace_bytes(int64_t N, int B, dash_prec prec) {
   size_t bytes = 0;
   bytes += 2 * align_up((size_t)N * B * KV * sizeof(float), 256);
   bytes += 2 * align_up((size_t)N * RB * 3 * KV * sizeof(float), 256);
-  bytes += 256;                                                  // v0 inverse norms
+  bytes += align_up((size_t)B * KV * sizeof(float), 256);       // prepared start vectors
   bytes += align_up((size_t)N * COEF_STRIDE * sizeof(float), 256);
   if (prec == DASH_FP16) bytes += align_up((size_t)N * B * B * sizeof(_Float16), 256);
   return bytes;
@@ -390,6 +457,30 @@ hipError_t launch_frobenius(const float* A, int64_t N, int B, float* s, hipStrea
   return hipGetLastError();
 }
 
+// Ring depth for a k-loop of KT slices: the largest of 4, 2, 1 that divides KT and is <= max_depth.
+// (binary16 steps run best at 2: the 4-deep ring costs them a wave per SIMD.)
+inline int ring_depth(int KT, int max_depth) {
+  return (max_depth >= 4 && KT % 4 == 0) ? 4 : (KT % 2 == 0 ? 2 : 1);
+}
+
+template <typename TI, int WAVES, int DEPTH>
+void launch_step(dim3 grid, hipStream_t stream, const PowerStepArgs<TI>& a) {
+  if constexpr (sizeof(TI) == 4)
+    hipLaunchKernelGGL((power_step_f32<WAVES, DEPTH>), grid, dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((power_step_f16<WAVES, DEPTH>), grid, dim3(64 * WAVES), 0, stream, a);
+}
+
+template <typename TI, int WAVES>
+void launch_step_depth(int depth, dim3 grid, hipStream_t stream, const PowerStepArgs<TI>& a) {
+  if (depth == 4)
+    launch_step<TI, WAVES, 4>(grid, stream, a);
+  else if (depth == 2)
+    launch_step<TI, WAVES, 2>(grid, stream, a);
+  else
+    launch_step<TI, WAVES, 1>(grid, stream, a);
+}
+
 hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   const bool wide = (p.B % 128 == 0);
   const int RT = wide ? 128 : 64;
@@ -397,7 +488,7 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   const int64_t grid = p.N * RB;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err;
-  hipLaunchKernelGGL(v0_inverse_norms_kernel, dim3(1), dim3(64), 0, stream, p.V0, p.B, p.k, p.v0inv);
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.B, p.k, p.V0p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const float* coef = nullptr;
   if (p.prec == DASH_FP16) {
@@ -413,42 +504,36 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
     if ((err = launch_affine(cast, p.N, p.B, stream)) != hipSuccess) return err;
     coef = p.coef;
   }
+  // fp32 slices are 32 wide, binary16 slices 64 wide
+  const int depth = p.prec == DASH_FP32 ? ring_depth(p.B / 32, 4) : ring_depth(p.B / 64, 2);
   for (int t = 0; t < p.steps; ++t) {
     const int cur = t & 1;
+    auto fill = [&](auto& a) {
+      a.Vsrc = t == 0 ? p.V0p : p.W[cur ^ 1];
+      a.vstride = t == 0 ? 0 : (int64_t)p.B * KV;
+      a.part_in = t == 0 ? nullptr : p.part[cur ^ 1];
+      a.W = p.W[cur];
+      a.part_out = p.part[cur];
+      a.B = p.B;
+      a.k = p.k;
+      a.RB = RB;
+    };
     if (p.prec == DASH_FP32) {
       PowerStepArgs<float> a;
       a.A = p.A;
-      a.Vsrc = t == 0 ? p.V0 : p.W[cur ^ 1];
-      a.vstride = t == 0 ? 0 : (int64_t)p.B * KV;
-      a.vld = t == 0 ? p.k : KV;
-      a.v0inv = t == 0 ? p.v0inv : nullptr;
-      a.part_in = t == 0 ? nullptr : p.part[cur ^ 1];
-      a.W = p.W[cur];
-      a.part_out = p.part[cur];
-      a.B = p.B;
-      a.k = p.k;
-      a.RB = RB;
+      fill(a);
       if (wide)
-        hipLaunchKernelGGL(power_step_f32<4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        launch_step_depth<float, 4>(depth, dim3((unsigned)grid), stream, a);
       else
-        hipLaunchKernelGGL(power_step_f32<2>, dim3((unsigned)grid), dim3(128), 0, stream, a);
+        launch_step_depth<float, 2>(depth, dim3((unsigned)grid), stream, a);
     } else {
       PowerStepArgs<_Float16> a;
       a.A = p.Ah;
-      a.Vsrc = t == 0 ? p.V0 : p.W[cur ^ 1];
-      a.vstride = t == 0 ? 0 : (int64_t)p.B * KV;
-      a.vld = t == 0 ? p.k : KV;
-      a.v0inv = t == 0 ? p.v0inv : nullptr;
-      a.part_in = t == 0 ? nullptr : p.part[cur ^ 1];
-      a.W = p.W[cur];
-      a.part_out = p.part[cur];
-      a.B = p.B;
-      a.k = p.k;
-      a.RB = RB;
+      fill(a);
       if (wide)
-        hipLaunchKernelGGL(power_step_f16<4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        launch_step_depth<_Float16, 4>(depth, dim3((unsigned)grid), stream, a);
       else
-        hipLaunchKernelGGL(power_step_f16<2>, dim3((unsigned)grid), dim3(128), 0, stream, a);
+        launch_step_depth<_Float16, 2>(depth, dim3((unsigned)grid), stream, a);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

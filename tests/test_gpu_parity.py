@@ -55,6 +55,22 @@ def test_power_scale_conditioned_fp32_and_fp16(conditioned):
     assert np.max(np.abs(s16 - s_ref) / s_ref) < 2e-3
 
 
+@pytest.mark.parametrize("B", [64, 128, 192, 320])
+def test_power_scale_ring_depths(B):
+    """k-loops of 1, 2 and 4 register-ring slices (fp32 slices are 32 wide, binary16 slices 64) on
+    64- and 128-row workgroups; k = 5 start vectors leave 27 zero columns."""
+    A64, _, _ = di.known_spectrum_stack(150 + B, 2, B, 0.05, 1.0)
+    A = A64.astype(np.float32)
+    for k in (32, 5):
+        V0 = di.start_vectors(B, k)
+        s = to_host(power_scale(to_dev(A), to_dev(V0), 10))
+        s_ref, _ = oracle.mpi(A, V0, 10)
+        assert np.max(np.abs(s - s_ref) / s_ref) < 1e-5
+        s16 = to_host(power_scale(to_dev(A), to_dev(V0), 10, dash.DASH_FP16))
+        s16_ref, _ = oracle.mpi(A, V0, 10, half=True)
+        assert np.max(np.abs(s16 - s16_ref) / s16_ref) < 2e-3
+
+
 def test_frobenius(tiny, conditioned):
     for A, Ad in (tiny, conditioned):
         s = to_host(frob_scale(Ad))
