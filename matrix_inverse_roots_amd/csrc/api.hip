@@ -613,6 +613,9 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
     e.alpha = (float)(4.0 / w);
     e.ia = CO_R1;
     e.beta = (float)(-2.0 * m / w);
+    e.fold_c = true;  // beta / alpha = -(m / 2) s
+    e.c_over_a = (float)(-0.5 * m);
+    e.ic = CO_S;
     e.delta = -1.f;
     e.gamma = (float)c[k];
     e.coef = coef;
@@ -628,6 +631,9 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
   e.ia = CO_R1U;
   e.beta = (float)(-m / w);
   e.ib = CO_U;
+  e.fold_c = true;  // beta / alpha = (-m/w) s^{-1/4} / ((2/w) s^{-5/4}) = -(m / 2) s
+  e.c_over_a = (float)(-0.5 * m);
+  e.ic = CO_S;
   e.delta = -1.f;
   e.id = CO_U;
   e.gamma = (float)c[0];

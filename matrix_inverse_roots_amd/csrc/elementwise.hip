@@ -41,7 +41,7 @@ __global__ void coef_kernel(const float* s, int64_t N, float* coef, int32_t* sta
   c[CO_R1U] = (float)(r1 * u);
   c[CO_P2] = 1.f;
   c[CO_P2INV] = 1.f;
-  c[7] = 0.f;
+  c[CO_S] = sv;
 }
 
 __device__ __forceinline__ float co(const float* coef, int idx, int64_t b) {

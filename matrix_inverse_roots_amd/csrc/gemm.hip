@@ -36,6 +36,10 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   if (sym && nprob >= 1 && (probs[0].D2 || (nprob > 1 && probs[1].D2)) &&
       (epi.alpha != 1.f || epi.ia != CO_NONE || epi.gamma != 0.f || epi_uses_ce(probs, nprob)))
     return hipErrorInvalidValue;
+  // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
+  if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || probs[0].C != probs[0].Y ||
+                     (nprob > 1 && probs[1].C != probs[1].Y) || !probs[0].C))
+    return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);

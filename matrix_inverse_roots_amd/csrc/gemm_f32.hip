@@ -6,6 +6,9 @@
 // reads 16 consecutive k of its X row with 128-bit LDS loads; the Y operand is a single float per
 // lane read straight from a row of the Y tile.  The statistics products read one operand
 // transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them.
+// CY: the epilogue's C operand is the right operand Y itself (Clenshaw's b_{k+1}), so the C tile
+// rows [i0, i0 + TILE) pass through LDS as k-slices of Y; each wave adds (beta/alpha) C to its
+// accumulators from those slices and the epilogue reads no C from memory.
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
@@ -14,7 +17,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS>
+template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS, bool CY>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BK = 32;
   constexpr int WT = TILE / 2;
@@ -28,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   float(*Bs)[BK * LDB] = reinterpret_cast<float(*)[BK * LDB]>(smem + 2 * TILE * LDA * 4);
 
   const TileCoord tc = decode_tile(a, SYM);
-  const Product P = tc.prob ? a.p1 : a.p0;
+  Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
   const float* X = (const float*)P.X + off;
@@ -117,32 +120,53 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][q], bv[nt], acc[mt][nt], 0, 0, 0);
       }
     }
+    if constexpr (CY) {
+      // this slice holds Y rows kt*BK .. kt*BK + 31, i.e. C rows of the tile when they fall in
+      // [i0, i0 + TILE); BK = 32 rows are exactly one row of 32 x 32 accumulators
+      const int s_rel = kt * BK - i0;
+      if (s_rel >= 0 && s_rel < TILE) {
+        const float fc = a.epi.c_over_a * coef_of(a.epi, a.epi.ic, tc.b);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (wm * WT + mt * 32 != s_rel) continue;
+#pragma unroll
+          for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[mt][nt][r] += fc * bs[(8 * (r >> 2) + 4 * h + (r & 3)) * LDB + wn * WT + nt * 32 + li];
+        }
+      }
+    }
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
+  if (CY) P.C = nullptr;  // already in the accumulators
   epilogue<MT, MT, WT, WT, SYM, TO, true, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <int TILE, bool CHECKS>
-hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
+hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, bool c_is_y, hipStream_t stream) {
   a.tdim = a.B / TILE;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   if (trans == Trans::NN) {
-    if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS>, a, stream);
-    return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS>, a, stream);
+    if (sym && c_is_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true>, a, stream);
+    if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, false>, a, stream);
+    return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false>, a, stream);
   }
   if (!sym) return hipErrorInvalidValue;
-  if (trans == Trans::NT) return launch(gemm_f32_kernel<TILE, 0, 1, true, float, CHECKS>, a, stream);
-  return launch(gemm_f32_kernel<TILE, 1, 0, true, float, CHECKS>, a, stream);
+  if (trans == Trans::NT) return launch(gemm_f32_kernel<TILE, 0, 1, true, float, CHECKS, false>, a, stream);
+  return launch(gemm_f32_kernel<TILE, 1, 0, true, float, CHECKS, false>, a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream) {
   const bool checks = wants_checks(a.epi);
+  const bool cy = a.epi.fold_c;
   if (a.B % 128 == 0)
-    return checks ? dispatch_f32<128, true>(a, trans, sym, stream) : dispatch_f32<128, false>(a, trans, sym, stream);
-  return checks ? dispatch_f32<64, true>(a, trans, sym, stream) : dispatch_f32<64, false>(a, trans, sym, stream);
+    return checks ? dispatch_f32<128, true>(a, trans, sym, cy, stream)
+                  : dispatch_f32<128, false>(a, trans, sym, cy, stream);
+  return checks ? dispatch_f32<64, true>(a, trans, sym, cy, stream) : dispatch_f32<64, false>(a, trans, sym, cy, stream);
 }
 
 }  // namespace gemm
