@@ -36,10 +36,10 @@ constexpr int COEF_STRIDE = 8;
 // monitor (optional): monitor[b * mon_stride] += mon_mul * sum over the block of (D - I)^2
 //   (accumulated with atomics; the caller zero-fills it and takes sqrt/ sqrt(B) afterwards).
 // status (optional): status[b] |= 2 when D or D2 holds a non-finite value.
-// fold_c (fp32 triangle-only NN products whose C is their right operand Y, i.e. Clenshaw's
-// b_{k+1}): D = alpha_b (acc + c_over_a_b C) + delta_b E + gamma_b I, with C added from the staged
-// Y slices inside the product; c_over_a_b = c_over_a * coef[ic] must equal beta_b / alpha_b, and
-// beta/ib are then unused.
+// fold_c (fp32 triangle-only NN products whose C is their right operand Y and that carry E, i.e.
+// Clenshaw's b_{k+1} and b_{k+2}): D = alpha_b (acc + c_over_a_b C) + delta_b E + gamma_b I, with C
+// added from the staged Y slices inside the product and E loaded during its last k-slice;
+// c_over_a_b = c_over_a * coef[ic] must equal beta_b / alpha_b, and beta/ib are then unused.
 struct Epilogue {
   float alpha = 1.f, beta = 0.f, delta = 0.f, gamma = 0.f, alpha2 = 0.f, gamma2 = 0.f;
   int8_t ia = CO_NONE, ib = CO_NONE, id = CO_NONE, ig = CO_NONE, ia2 = CO_NONE, ig2 = CO_NONE;

@@ -38,7 +38,8 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     return hipErrorInvalidValue;
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
   if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || probs[0].C != probs[0].Y ||
-                     (nprob > 1 && probs[1].C != probs[1].Y) || !probs[0].C))
+                     (nprob > 1 && probs[1].C != probs[1].Y) || !probs[0].C || !probs[0].E ||
+                     (nprob > 1 && !probs[1].E)))
     return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;

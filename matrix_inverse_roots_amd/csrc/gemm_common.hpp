@@ -125,10 +125,35 @@ __device__ __forceinline__ void mirror_readback(TO* Dst, const TO* T, int B, int
   }
 }
 
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_CE, int TILE, int SMEM_BYTES,
-          bool CHECKS>
+// E values of a lane's accumulator elements, loaded ahead of the epilogue (E_PRE) so that their
+// latency overlaps the last k-slice of the product.
+template <int MTM, int MTN, int WTM, int WTN, int TILE>
+__device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, const Product& P, int wm, int wn,
+                                       int lane, float (&ev)[MTM][MTN][16]) {
+  const int B = a.B;
+  const float* E = P.E + tc.b * (int64_t)B * B;
+  const int li = lane & 31, h = lane >> 5;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+#pragma unroll
+  for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = j0 + wn * WTN + nt * 32 + li;
+        ev[mt][nt][r] = E[(int64_t)i * B + j];
+      }
+}
+
+// HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
+// that E_PRE takes E's values from ev_pre, loaded by load_e).
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE,
+          int SMEM_BYTES, bool CHECKS, bool E_PRE = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
-                                         f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, char* smem) {
+                                         f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, char* smem,
+                                         const float (*ev_pre)[MTN][16] = nullptr) {
+  constexpr bool HAS_CE = HAS_C || HAS_E;
   typedef typename Vec4<TO>::type v4;
   constexpr int PAD = 16 / (int)sizeof(TO);  // keeps every T row 16-byte aligned
   constexpr bool ONE_PASS = TILE * (TILE + PAD) * (int)sizeof(TO) <= SMEM_BYTES;
@@ -169,8 +194,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
         const int i = i0 + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int j = j0 + wn * WTN + nt * 32 + li;
         const int64_t idx = (int64_t)i * B + j;
-        cv[nt][r] = (HAS_CE && C) ? C[idx] : 0.f;
-        ev[nt][r] = (HAS_CE && E) ? E[idx] : 0.f;
+        cv[nt][r] = (HAS_C && C) ? C[idx] : 0.f;
+        if (E_PRE)
+          ev[nt][r] = ev_pre[mt][nt][r];
+        else
+          ev[nt][r] = (HAS_E && E) ? E[idx] : 0.f;
       }
 #pragma unroll
     for (int nt = 0; nt < MTN; ++nt)

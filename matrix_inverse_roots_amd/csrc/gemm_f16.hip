@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <bool SYM, bool CHECKS>

@@ -94,14 +94,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
   const int KT = B / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const float* as = As[buf];
-    const float* bs = Bs[buf];
+  auto compute = [&](int kt) {
+    const float* as = As[kt & 1];
+    const float* bs = Bs[kt & 1];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       f32x4 av[MT];
@@ -137,11 +132,37 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
         }
       }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  float ev[CY ? MT : 1][MT][16];
+  if constexpr (CY) {
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      gload((kt + 1) * BK);
+      compute(kt);
+      sstore((kt + 1) & 1);
+      __syncthreads();
+    }
+    // last k-slice: a Clenshaw launch (always with E) loads its E values first, so that their
+    // latency overlaps this slice's MFMAs
+    load_e<MT, MT, WT, WT, TILE>(a, tc, P, wm, wn, lane, ev);
+    compute(KT - 1);
     __syncthreads();
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) gload((kt + 1) * BK);
+      compute(kt);
+      if (kt + 1 < KT) sstore((kt + 1) & 1);
+      __syncthreads();
+    }
   }
   if (CY) P.C = nullptr;  // already in the accumulators
-  epilogue<MT, MT, WT, WT, SYM, TO, true, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+  if constexpr (CY)
+    epilogue<MT, MT, WT, WT, SYM, TO, false, true, TILE, SMEM_BYTES, CHECKS, true>(a, tc, P, acc, wm, wn, lane, smem,
+                                                                                  ev);
+  else
+    epilogue<MT, MT, WT, WT, SYM, TO, true, true, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <int TILE, bool CHECKS>
