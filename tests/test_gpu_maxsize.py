@@ -1,0 +1,80 @@
+"""GPU checks at the largest block the ABI takes, B = 8192 (one 256 MiB block), where the fp64 oracle
+is too slow to run: properties that hold at any size.  The residual ||X^4 A - I||_F / sqrt(B) of
+every solver is evaluated in fp64 with torch products on the device; the scale estimates are
+checked against bounds and against each other."""
+import pytest
+import torch
+
+import dash_inputs as di
+import matrix_inverse_roots_amd as dash
+from gpu_helpers import DEV, R_FP16, R_FP32, cheb, cn, frob_scale, ndb, power_scale
+
+pytestmark = pytest.mark.gpu
+
+B = 8192
+SHIFT = 1.0  # A = G G^T / B + I: spectrum in about [1, 5] (kappa 5, like the Gram stacks)
+
+
+@pytest.fixture(scope="module")
+def block():
+    G = di.gaussian_torch((B, B), seed=41, device=DEV).double()
+    A64 = G @ G.T.contiguous() / B + SHIFT * torch.eye(B, device=DEV, dtype=torch.float64)
+    A64 = 0.5 * (A64 + A64.T.contiguous())
+    del G
+    A = A64.float().reshape(1, B, B).contiguous()
+    A64 = A.double()[0]
+    V0 = torch.from_numpy(di.start_vectors(B, 32)).to(DEV)
+    yield A, A64, V0
+    del A, A64
+    torch.cuda.empty_cache()
+
+
+def residual64(X, A64):
+    x = X[0].double()
+    x2 = x @ x
+    r = x2 @ x2 @ A64
+    r.diagonal().sub_(1.0)
+    return float(torch.linalg.matrix_norm(r) / B ** 0.5)
+
+
+def test_maxsize_scales(block):
+    A, A64, V0 = block
+    fro = float(torch.linalg.matrix_norm(A64))
+    assert abs(float(frob_scale(A)[0]) - fro) <= 1e-6 * fro
+    s10 = float(power_scale(A, V0, 10)[0])
+    s3 = float(power_scale(A, V0, 3)[0])
+    s16 = float(power_scale(A, V0, 10, dash.DASH_FP16)[0])
+    assert s3 * (1 - 1e-6) <= s10 <= fro          # Rayleigh quotients grow with the steps, below ||A||_2
+    assert s10 > 0.85 * (4 + SHIFT)                 # approaches the Marchenko-Pastur edge 4 + SHIFT
+    assert abs(s16 - s10) <= 2e-3 * s10
+
+
+def test_maxsize_ndb(block):
+    A, A64, V0 = block
+    s = power_scale(A, V0, 10)
+    X, R, _, status = ndb(A, s, 8, 8, want_sqrt=True)
+    assert int(status[0]) == 0
+    assert residual64(X, A64) < R_FP32
+    r = R[0].double()
+    assert float(torch.linalg.matrix_norm(r @ r - A64) / torch.linalg.matrix_norm(A64)) < 1e-4
+
+
+@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP16])
+def test_maxsize_cn(block, prec):
+    A, A64, V0 = block
+    s = power_scale(A, V0, 10, prec)
+    X, _, status = cn(A, s, 8, prec)
+    assert int(status[0]) == 0
+    assert residual64(X, A64) < (R_FP32 if prec == dash.DASH_FP32 else R_FP16)
+    if prec == dash.DASH_FP16:  # mirrored products: exactly symmetric
+        assert torch.equal(X[0], X[0].T)
+
+
+def test_maxsize_cheb(block):
+    A, A64, V0 = block
+    s = power_scale(A, V0, 10)
+    lo = 0.9 * SHIFT / float(s[0])
+    X, status = cheb(A, s, 24, lo, 1.25)
+    assert int(status[0]) == 0
+    assert residual64(X, A64) < R_FP32
+    assert torch.equal(X[0], X[0].T)
