@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// fp16 operands with an exactly symmetric right operand Y (Y^T = Y bitwise), 256 x 256 macro tile.
+// fp16 operands with an exactly symmetric right operand Y (Y^T = Y bitwise), 256 x 256 macro tile,
+// four waves of 128 x 128 or eight waves of 128 x 64.
 // Then column j of Y is row j of Y, so both slices are read as rows of consecutive k with 16-byte
 // loads and no transposition.  The k-step is 32 and the global slices run DEPTH = 4 k-steps ahead
 // of the MFMAs through a ring of registers (two LDS buffers), so each workgroup keeps 128 KiB of
@@ -220,9 +221,13 @@ using IC = std::integral_constant<int, V>;
 
 __device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 1)) & 3; }
 
-template <bool SYM, typename TO, bool CHECKS>
-__global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
-  constexpr int TILE = 256, BK = 32, MT = 4, WT = 128, DEPTH = 4;
+template <bool SYM, typename TO, bool CHECKS, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
+  // NW = 4: 2 x 2 waves of 128 x 128; NW = 8: 2 x 4 waves of 128 x 64 (two waves per SIMD)
+  constexpr int NT = 64 * NW;
+  constexpr int TILE = 256, BK = 32, DEPTH = 4;
+  constexpr int WTM = 128, WTN = TILE / (NW / 2), MTM = WTM / 32, MTN = WTN / 32;
+  constexpr int NP = TILE * BK / 8 / NT;  // 16-byte pieces per thread per operand slice
   constexpr int SLICE = TILE * BK;  // halves of one operand slice
   constexpr int MAIN_BYTES = 2 * 2 * SLICE * 2;
   constexpr int STAGE_BYTES = TILE * (TILE + 8) * 2;  // binary16 output tile staged for 16-byte stores
@@ -239,17 +244,17 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   const _Float16* Y = (const _Float16*)P.Y + off;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int li = lane & 31, h = lane >> 5;
 
-  // per k-step each thread moves 4 pieces of 16 bytes of each slice: piece c = tid + 256 r -> row
+  // per k-step each thread moves NP pieces of 16 bytes of each slice: piece c = tid + NT r -> row
   // c / 4, chunk c % 4 (rows i0.. of X and rows j0.. of Y, k0 .. k0 + 31)
-  f16x8 rx[DEPTH][4], ry[DEPTH][4];
+  f16x8 rx[DEPTH][NP], ry[DEPTH][NP];
   auto gload = [&](auto slot_c, int k0) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + 256 * r;
+    for (int r = 0; r < NP; ++r) {
+      const int c = tid + NT * r;
       const int row = c >> 2, ch = c & 3;
       rx[slot][r] = *(const f16x8*)(X + (int64_t)(i0 + row) * B + k0 + 8 * ch);
       ry[slot][r] = *(const f16x8*)(Y + (int64_t)(j0 + row) * B + k0 + 8 * ch);
@@ -258,8 +263,8 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   auto sstore = [&](auto slot_c, int buf) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + 256 * r;
+    for (int r = 0; r < NP; ++r) {
+      const int c = tid + NT * r;
       const int row = c >> 2, ch = c & 3;
       const int o = buf * SLICE + row * BK + 8 * swz4(row, ch);
       *(f16x8*)&Xs[o] = rx[slot][r];
@@ -267,11 +272,11 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
     }
   };
 
-  f32x16 acc[MT][MT];
+  f32x16 acc[MTM][MTN];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < MT; ++nt)
+    for (int nt = 0; nt < MTN; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
@@ -281,21 +286,21 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int chunk = 2 * h + s;
-      f16x8 av[MT], bv[MT];
+      f16x8 av[MTM], bv[MTN];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * WT + mt * 32 + li;
+      for (int mt = 0; mt < MTM; ++mt) {
+        const int row = wm * WTM + mt * 32 + li;
         av[mt] = *(const f16x8*)&xs[row * BK + 8 * swz4(row, chunk)];
       }
 #pragma unroll
-      for (int nt = 0; nt < MT; ++nt) {
-        const int row = wn * WT + nt * 32 + li;
+      for (int nt = 0; nt < MTN; ++nt) {
+        const int row = wn * WTN + nt * 32 + li;
         bv[nt] = *(const f16x8*)&ys[row * BK + 8 * swz4(row, chunk)];
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < MT; ++nt)
+        for (int nt = 0; nt < MTN; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
     }
   };
@@ -335,9 +340,9 @@ __global__ __launch_bounds__(256) void gemm_f16_ysym_kernel(GemmArgs a) {
   tail_step(IC<2>{}, true);
   tail_step(IC<3>{}, false);
   if constexpr (sizeof(TO) == 2)
-    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue_staged_f16<MTM, MTN, WTM, WTN, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MTM, MTN, WTM, WTN, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <bool SYM, bool CHECKS>
@@ -346,9 +351,11 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t
   a.tdim = a.B / tile;
   a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool half_out = out_prec == DASH_FP16;
+  // binary16 outputs run eight waves (two per SIMD: one wave's barrier and LDS latency are hidden
+  // behind the other's MFMAs); the fp32-output epilogue needs the four-wave kernel's registers
   if (tile == 256 && y_sym)
-    return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS>, a, stream)
-                    : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS>, a, stream);
+    return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8>, a, stream, 512)
+                    : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS, 4>, a, stream);
   if (tile == 256)
     return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16, CHECKS>, a, stream)
                     : launch(gemm_f16_big_kernel<SYM, float, CHECKS>, a, stream);
