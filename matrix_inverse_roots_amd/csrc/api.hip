@@ -228,6 +228,65 @@ dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) 
   return DASH_OK;
 }
 
+
+// Coupled Newton with binary16 iterates (T >= 2), on M_0 = A/s already stored in M0.
+// S_k = (5I - M_k)/4 is never stored: every product that takes S_k reads M_k and maps it as it is
+// staged (operand map -1/4 Z + 5/4 I, the same single rounding a binary16 elementwise pass would
+// apply), and X_1 = S_0 is likewise M_0 mapped.  M_0 stays alive until X_2 has been formed.
+dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* status, const float* coef, void* M0,
+                    Pool& pool, hipStream_t st) {
+  auto mapped = [](Product p, bool mx, bool my) {
+    p.map_x = mx;
+    p.map_y = my;
+    p.map_a = -0.25f;
+    p.map_g = 1.25f;
+    return p;
+  };
+  void* M = M0;
+  void* Xk = nullptr;  // null while X_k = S_0 (k = 1) is M_0 mapped
+  for (int k = 0; k < T; ++k) {
+    if (k == T - 1) {  // X_T = s^{-1/4} X_{T-1} S_{T-1}, fp32 output
+      Epilogue e;
+      e.ia = CO_U;
+      e.coef = coef;
+      e.status = status;
+      Product pr = mapped(prod(Xk ? Xk : M0, M, X), Xk == nullptr, true);
+      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP32, Trans::NN, true, e, st, true));
+      break;
+    }
+    void* S2 = pool.get();
+    if (k == 0) {
+      Product pr = mapped(prod(M, M, S2), true, true);
+      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+    } else {  // X_{k+1} = X_k S_k and S_k^2 in one launch
+      void* Xn = pool.get();
+      Product pr[2] = {mapped(prod(Xk ? Xk : M0, M, Xn), Xk == nullptr, true), mapped(prod(M, M, S2), true, true)};
+      TRY(launch_gemm(pr, 2, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+      pool.put(Xk ? Xk : M0);  // X_k (or M_0, whose last use as X_1 this was) is dead
+      Xk = Xn;
+    }
+    void* S4 = pool.get();
+    {
+      Product pr = prod(S2, S2, S4);
+      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+    }
+    pool.put(S2);
+    Epilogue e;
+    if (monitor) {
+      e.monitor = monitor + (k + 1);
+      e.mon_stride = T;
+    }
+    void* Mn = pool.get();
+    Product pr = prod(M, S4, Mn);
+    TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, e, st, true));
+    if (M != M0) pool.put(M);  // M_0 is released with X_1 above
+    pool.put(S4);
+    M = Mn;
+  }
+  if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
+  return DASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,13 +493,30 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   const int T = iters;
-  // binary16: triangle-only products (the iterates are symmetric polynomials in A and the error
-  // floor is set by binary16 storage); fp32: full products, which keep the fp32 rounding floor of
-  // the iteration lowest at high condition numbers
-  const bool tri = (prec == DASH_FP16);
+  // binary16 (T >= 2, cn_half): triangle-only products, the iterates being symmetric polynomials
+  // in A and the error floor set by binary16 storage; fp32: full products, which keep the fp32
+  // rounding floor of the iteration lowest at high condition numbers
+  const bool tri = false;
   // step 0: M_0 = A/s, S_0 = (5I - M_0)/4, X_1 = S_0;  ||M_0 - I||^2 = 16 ||S_0 - I||^2
   void* S = pool.get();
   void* M = pool.get();
+  if (prec == DASH_FP16 && T > 1) {  // binary16: M_0 only; the S_k are formed inside the products
+    pool.put(S);
+    Affine m0;
+    m0.X = A;
+    m0.D = M;
+    m0.d_prec = DASH_FP16;
+    m0.a = 1.f;
+    m0.ia = CO_R1;
+    m0.coef = coef;
+    if (monitor) {
+      m0.monitor = monitor;
+      m0.mon_stride = T;
+    }
+    // built from the upper triangle of A: every later right operand is then exactly symmetric
+    TRY(launch_sym_affine(m0, N, B, st));
+    return cn_half(N, B, T, X, monitor, status, coef, M, pool, st);
+  }
   {
     Affine s0;
     s0.X = A;
@@ -519,23 +595,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.monitor = monitor + (k + 1);
       e.mon_stride = T;
     }
-    if (prec == DASH_FP16) {
-      // binary16: M_{k+1} is stored first and S_{k+1} formed from the stored M in an elementwise
-      // pass (binary16 products carry no second output)
-      void* Mn = pool.get();
-      Product pr = prod(M, S4, Mn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
-      Affine sn;
-      sn.X = Mn;
-      sn.x_prec = DASH_FP16;
-      sn.D = Sn;
-      sn.d_prec = DASH_FP16;
-      sn.a = -0.25f;
-      sn.g = 1.25f;
-      TRY(launch_affine(sn, N, B, st));
-      pool.put(M);
-      M = Mn;
-    } else if (k + 1 == T - 1) {  // M_T is never needed: write S only, monitor from it
+    if (k + 1 == T - 1) {  // M_T is never needed: write S only, monitor from it
       e.alpha = -0.25f;
       e.gamma = 1.25f;
       e.mon_mul = 16.f;

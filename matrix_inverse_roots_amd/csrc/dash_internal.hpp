@@ -55,6 +55,9 @@ struct Epilogue {
 
 // One batched product over N blocks: D_b = epi(X_b Y_b).  X/Y element type is `in_prec`,
 // D/D2 element type is `out_prec`; C/E are fp32.  Stride between blocks: B*B elements.
+// map_x / map_y (binary16 operands only): the operand enters the product as map_a Z + map_g I,
+// formed while it is staged; map_a must be a power of two (each element is then the exact value
+// rounded once to binary16).
 struct Product {
   const void* X = nullptr;
   const void* Y = nullptr;
@@ -62,6 +65,8 @@ struct Product {
   const float* E = nullptr;
   void* D = nullptr;
   void* D2 = nullptr;
+  bool map_x = false, map_y = false;
+  float map_a = 0.f, map_g = 0.f;
 };
 
 enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed

@@ -41,6 +41,10 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
                      (nprob > 1 && probs[1].C != probs[1].Y) || !probs[0].C || !probs[0].E ||
                      (nprob > 1 && !probs[1].E)))
     return hipErrorInvalidValue;
+  // operand maps exist in the binary16 kernels that stage rows of both operands (the 256-wide tile
+  // with a symmetric right operand, and the 128/64-wide tiles)
+  const bool maps = probs[0].map_x || probs[0].map_y || (nprob > 1 && (probs[1].map_x || probs[1].map_y));
+  if (maps && (in_prec != DASH_FP16 || (B % 256 == 0 && !y_sym))) return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);

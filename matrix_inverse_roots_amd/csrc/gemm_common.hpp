@@ -68,6 +68,23 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmArgs& a, bool sym) {
   return c;
 }
 
+// Operand map of the binary16 products: the 8 consecutive elements Z[row][col0 .. col0 + 7] of a
+// staged chunk become a Z + g I.  a is a power of two (the callers' -1/4), so a z is exact unless it
+// is subnormal, and the diagonal element a z + g is rounded once (an exact a z below the half-ulp
+// of g cannot move the rounding): each result equals the exact value rounded to binary16 once, as
+// an fp32 elementwise pass that stores binary16 would give.  Only chunks that hold a diagonal
+// element take the branch.
+__device__ __forceinline__ f16x8 operand_map(f16x8 v, int row, int col0, float a, float g) {
+  f16x8 r = v * (_Float16)a;
+  const int d = row - col0;
+  if ((unsigned)d < 8u) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q == d) r[q] = r[q] + (_Float16)g;
+  }
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -44,15 +44,17 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
       rb[r] = *(const f16x8*)(Y + (int64_t)(k0 + krow) * B + j0 + 8 * n8);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int k0) {
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
       const int f = tid + 256 * r;
       const int row = f / (BK / 8), c8 = f % (BK / 8);
-      *(f16x8*)&As[buf][row * LD + 8 * c8] = ra[r];
       const int krow = f / (TILE / 8), n8 = f % (TILE / 8);
+      const f16x8 xa = P.map_x ? operand_map(ra[r], i0 + row, k0 + 8 * c8, P.map_a, P.map_g) : ra[r];
+      const f16x8 yb = P.map_y ? operand_map(rb[r], k0 + krow, j0 + 8 * n8, P.map_a, P.map_g) : rb[r];
+      *(f16x8*)&As[buf][row * LD + 8 * c8] = xa;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[buf][(8 * n8 + q) * LD + krow] = rb[r][q];
+      for (int q = 0; q < 8; ++q) Bs[buf][(8 * n8 + q) * LD + krow] = yb[q];
     }
   };
 
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
 
   const int KT = B / BK;
   gload(0);
-  sstore(0);
+  sstore(0, 0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
         for (int nt = 0; nt < MT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    if (kt + 1 < KT) sstore(buf ^ 1, (kt + 1) * BK);
     __syncthreads();
   }
   if constexpr (sizeof(TO) == 2)
@@ -260,15 +262,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
       ry[slot][r] = *(const f16x8*)(Y + (int64_t)(j0 + row) * B + k0 + 8 * ch);
     }
   };
-  auto sstore = [&](auto slot_c, int buf) {
+  auto sstore = [&](auto slot_c, int buf, int k0) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
       const int c = tid + NT * r;
       const int row = c >> 2, ch = c & 3;
       const int o = buf * SLICE + row * BK + 8 * swz4(row, ch);
-      *(f16x8*)&Xs[o] = rx[slot][r];
-      *(f16x8*)&Ys[o] = ry[slot][r];
+      *(f16x8*)&Xs[o] = P.map_x ? operand_map(rx[slot][r], i0 + row, k0 + 8 * ch, P.map_a, P.map_g) : rx[slot][r];
+      *(f16x8*)&Ys[o] = P.map_y ? operand_map(ry[slot][r], j0 + row, k0 + 8 * ch, P.map_a, P.map_g) : ry[slot][r];
     }
   };
 
@@ -314,31 +316,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
     constexpr int slot = decltype(slot_c)::value;  // == kt % DEPTH
     gload(slot_c, (kt + DEPTH) * BK);
     compute(slot & 1);
-    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1, (kt + 1) * BK);
     __syncthreads();
   };
-  auto tail_step = [&](auto slot_c, bool store_next) {
+  auto tail_step = [&](auto slot_c, int kt, bool store_next) {
     constexpr int slot = decltype(slot_c)::value;
     compute(slot & 1);
-    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1, (kt + 1) * BK);
     __syncthreads();
   };
   gload(IC<0>{}, 0);
   gload(IC<1>{}, BK);
   gload(IC<2>{}, 2 * BK);
   gload(IC<3>{}, 3 * BK);
-  sstore(IC<0>{}, 0);
+  sstore(IC<0>{}, 0, 0);
   __syncthreads();
-  for (int kt = 0; kt + DEPTH < KT; kt += DEPTH) {
+  int kt = 0;
+  for (; kt + DEPTH < KT; kt += DEPTH) {
     step(IC<0>{}, kt);
     step(IC<1>{}, kt + 1);
     step(IC<2>{}, kt + 2);
     step(IC<3>{}, kt + 3);
   }
-  tail_step(IC<0>{}, true);
-  tail_step(IC<1>{}, true);
-  tail_step(IC<2>{}, true);
-  tail_step(IC<3>{}, false);
+  tail_step(IC<0>{}, kt, true);
+  tail_step(IC<1>{}, kt + 1, true);
+  tail_step(IC<2>{}, kt + 2, true);
+  tail_step(IC<3>{}, kt + 3, false);
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MTM, MTN, WTM, WTN, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else

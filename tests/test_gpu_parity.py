@@ -182,9 +182,21 @@ def test_cn_reads_only_the_upper_triangle(prec):
         assert np.max(np.abs(Xh - Xh.transpose(0, 2, 1))) < 1e-5 * np.abs(Xh).max()
 
 
-@pytest.mark.parametrize("B", [256, 512])
+@pytest.mark.parametrize("iters", [2, 3])
+def test_cn_fp16_short_runs(tiny, iters):
+    """T = 2 and 3: the first iterate X_1 = S_0 enters the last and the dual products directly."""
+    A, Ad = tiny
+    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10, dash.DASH_FP16)
+    X, _, status = cn(Ad, s, iters, dash.DASH_FP16)
+    X_emul, _ = oracle.cn_inverse_root(A, to_host(s), iters, half_storage=True)
+    assert np.max(rel_err(to_host(X), X_emul)) < 5e-3
+    assert np.all(to_host(status) == 0)
+
+
+@pytest.mark.parametrize("B", [128, 192, 256, 512])
 def test_cn_fp16_wide_tiles(B):
-    """B % 256 == 0 runs the 256 x 256 fp16 product tile; compare with the binary16-storage oracle."""
+    """B % 256 == 0 runs the 256 x 256 fp16 product tile, 128 and 192 the 128/64 tiles; compare with
+    the binary16-storage oracle."""
     A64, _, _ = di.known_spectrum_stack(120 + B, 3, B, 0.2, 1.0)  # kappa 5, like the Gram stacks
     A = A64.astype(np.float32)
     Ad = to_dev(A)
