@@ -50,8 +50,8 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     return gemm::launch_f32(a, trans, sym, stream);
   }
   if (trans != Trans::NN || epi_uses_ce(probs, nprob)) return hipErrorInvalidValue;
-  // binary16 outputs are staged through LDS for wide stores and carry no second output
-  if (out_prec == DASH_FP16 && (probs[0].D2 || (nprob > 1 && probs[1].D2))) return hipErrorInvalidValue;
+  // binary16-operand products carry no second output
+  if (probs[0].D2 || (nprob > 1 && probs[1].D2)) return hipErrorInvalidValue;
   return gemm::launch_f16(a, out_prec, sym, y_sym, stream);
 }
 

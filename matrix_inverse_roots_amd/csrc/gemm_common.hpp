@@ -395,6 +395,79 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
   }
 }
 
+// Epilogue for fp32 outputs of the binary16 products (no C/E operands, no second output: the last
+// coupled-Newton product).  Kept elements are stored straight from the accumulators (lanes 0-31
+// cover 128 contiguous bytes of a row); SYM mirrors through LDS in passes of R tile rows, the
+// transposed rows T[jl][il - p R] written with one 16-byte LDS store per 4 values and read back as
+// 16-byte pieces (a diagonal tile stores everything directly and the mirror then overwrites its
+// strict lower part).  Monitor and status (CHECKS) as in `epilogue`.
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE, int SMEM_BYTES, bool CHECKS>
+__device__ __forceinline__ void epilogue_direct_f32(const GemmArgs& a, const TileCoord& tc, const Product& P,
+                                                    const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
+                                                    char* smem) {
+  constexpr int R = TILE * (TILE + 4) * 4 <= SMEM_BYTES ? TILE
+                    : (TILE * (TILE / 2 + 4) * 4 <= SMEM_BYTES ? TILE / 2 : TILE / 4);
+  constexpr int PITCH = R + 4;
+  static_assert(TILE * PITCH * 4 <= SMEM_BYTES, "mirror staging does not fit in LDS");
+  const Epilogue& e = a.epi;
+  const int B = a.B;
+  const int64_t b = tc.b;
+  const float al = e.alpha * coef_of(e, e.ia, b);
+  const float ga = e.gamma * coef_of(e, e.ig, b);
+  const int li = lane & 31, h = lane >> 5;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const bool diag_tile = SYM && tc.ti == tc.tj;
+  float* T = (float*)smem;
+  float* D = (float*)P.D + b * (int64_t)B * B;
+  float mon = 0.f;
+  bool bad = false;
+#pragma unroll
+  for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int jl = wn * WTN + nt * 32 + li;
+        const bool on_diag = (i0 + il == j0 + jl);
+        const float v = al * acc[mt][nt][r] + (on_diag ? ga : 0.f);
+        D[(int64_t)(i0 + il) * B + j0 + jl] = v;
+        if (CHECKS && !(diag_tile && il > jl)) {
+          bad |= !isfinite(v);
+          if (e.monitor) {
+            const float dd = v - (on_diag ? 1.f : 0.f);
+            mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
+          }
+        }
+      }
+  if (CHECKS && e.monitor) {
+    mon = wave_sum(mon);
+    if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
+  }
+  if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
+  if (!SYM) return;
+  for (int p = 0; p < TILE / R; ++p) {
+    __syncthreads();  // LDS is free: the main loop or the previous read-back is done
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3, one pass
+          const int jl = wn * WTN + nt * 32 + li;
+          if (il0 / R != p) continue;
+          f32x4 pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pk[q] = al * acc[mt][nt][4 * r4 + q] + (i0 + il0 + q == j0 + jl ? ga : 0.f);
+          *(f32x4*)&T[jl * PITCH + (il0 - p * R)] = pk;
+        }
+    __syncthreads();
+    mirror_readback<float, TILE, R, PITCH>(D, T, B, i0, j0, p, diag_tile);
+  }
+}
+
 template <typename K>
 hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream, int threads = 256) {
   const int64_t grid = (int64_t)a.nprob * a.N * a.tiles;

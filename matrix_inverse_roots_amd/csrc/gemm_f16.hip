@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MTM, MTN, WTM, WTN, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MTM, MTN, WTM, WTN, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue_direct_f32<MTM, MTN, WTM, WTN, SYM, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
 }
 
 template <bool SYM, bool CHECKS>
@@ -354,11 +354,11 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t
   a.tdim = a.B / tile;
   a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool half_out = out_prec == DASH_FP16;
-  // binary16 outputs run eight waves (two per SIMD: one wave's barrier and LDS latency are hidden
-  // behind the other's MFMAs); the fp32-output epilogue needs the four-wave kernel's registers
+  // eight waves (two per SIMD: one wave's barrier and LDS latency are hidden behind the other's
+  // MFMAs)
   if (tile == 256 && y_sym)
     return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8>, a, stream, 512)
-                    : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS, 4>, a, stream);
+                    : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS, 8>, a, stream, 512);
   if (tile == 256)
     return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16, CHECKS>, a, stream)
                     : launch(gemm_f16_big_kernel<SYM, float, CHECKS>, a, stream);
