@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "dash_internal.hpp"
@@ -653,55 +654,73 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
     TRY(launch_affine(fin, N, B, st));
     return DASH_OK;
   }
-  // b_d = c_d I,  b_{d-1} = c_{d-1} I + 2 T b_d = c_{d-1} I + c_d (4 A/s - 2 m I)/w
-  {
-    Affine init;
-    init.X = A;
-    init.D = b1;
-    init.a = (float)(4.0 * c[d] / w);
-    init.ia = CO_R1;
-    init.g = (float)(c[d - 1] - 2.0 * c[d] * m / w);
-    init.D2 = b2;
-    init.a2 = 0.f;
-    init.g2 = (float)c[d];
-    init.coef = coef;
-    TRY(launch_affine(init, N, B, st));
-  }
-  // b_k = c_k I + 2 T b_{k+1} - b_{k+2}, written over b_{k+2}
-  for (int k = d - 2; k >= 1; --k) {
+  // b_d = c_d I and b_{d-1} = c_{d-1} I + 2 T b_d = a1 A/s + g1 I are never stored: the first
+  // product reads A mapped to b_{d-1} (its C term rides in with it), b_d enters its gamma, and the
+  // second product takes A itself as E for b_{d-1}.
+  const double a1 = 4.0 * c[d] / w, g1 = c[d - 1] - 2.0 * c[d] * m / w;
+  auto clenshaw = [&](const void* Y, const float* E, void* D, bool last) {
     Epilogue e;
-    e.alpha = (float)(4.0 / w);
-    e.ia = CO_R1;
-    e.beta = (float)(-2.0 * m / w);
-    e.fold_c = true;  // beta / alpha = -(m / 2) s
+    e.fold_c = true;  // beta / alpha = -(m / 2) s for every product
     e.c_over_a = (float)(-0.5 * m);
     e.ic = CO_S;
-    e.delta = -1.f;
-    e.gamma = (float)c[k];
     e.coef = coef;
-    Product pr = prod(A, b1, b2, b1, b2);
-    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, e, st));
-    float* t = b1;
-    b1 = b2;
-    b2 = t;
+    if (last) {  // X = u (c_0 I + T b_1 - b_2)
+      e.alpha = (float)(2.0 / w);
+      e.ia = CO_R1U;
+      e.beta = (float)(-m / w);
+      e.ib = CO_U;
+      e.ig = CO_U;
+      e.id = CO_U;
+      e.status = status;
+    } else {  // b_k = c_k I + 2 T b_{k+1} - b_{k+2}
+      e.alpha = (float)(4.0 / w);
+      e.ia = CO_R1;
+      e.beta = (float)(-2.0 * m / w);
+    }
+    e.delta = -1.f;
+    Product pr = prod(A, Y, D, (const float*)Y, E);
+    return std::make_pair(pr, e);
+  };
+  auto run = [&](std::pair<Product, Epilogue> pe) {
+    return launch_gemm(&pe.first, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, pe.second, st);
+  };
+  auto map_first = [&](Product& p) {  // Y = A read as b_{d-1}
+    p.map_y = true;
+    p.map_a = (float)a1;
+    p.map_ia = CO_R1;
+    p.map_g = (float)g1;
+  };
+  // the first product: k = d - 2 (or the final one when d == 2), E = b_d = c_d I folded into gamma
+  {
+    const bool last = (d == 2);
+    auto pe = clenshaw(A, nullptr, last ? (void*)X : (void*)b2, last);
+    map_first(pe.first);
+    pe.second.gamma = (float)((last ? c[0] : c[d - 2]) - c[d]);
+    TRY(run(pe));
+    if (last) return DASH_OK;
   }
-  // X = u (c_0 I + T b_1 - b_2)
-  Epilogue e;
-  e.alpha = (float)(2.0 / w);
-  e.ia = CO_R1U;
-  e.beta = (float)(-m / w);
-  e.ib = CO_U;
-  e.fold_c = true;  // beta / alpha = (-m/w) s^{-1/4} / ((2/w) s^{-5/4}) = -(m / 2) s
-  e.c_over_a = (float)(-0.5 * m);
-  e.ic = CO_S;
-  e.delta = -1.f;
-  e.id = CO_U;
-  e.gamma = (float)c[0];
-  e.ig = CO_U;
-  e.coef = coef;
-  e.status = status;
-  Product pr = prod(A, b1, X, b1, b2);
-  TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, e, st));
+  // the second product: k = d - 3 (or the final one when d == 3), E = b_{d-1} = a1 A/s + g1 I read
+  // as A with its coefficients (A is symmetric, so its upper-triangle tiles serve as E)
+  {
+    const bool last = (d == 3);
+    auto pe = clenshaw(b2, A, last ? (void*)X : (void*)b1, last);
+    pe.second.delta = (float)(-a1);
+    pe.second.id = last ? CO_R1U : CO_R1;
+    pe.second.gamma = (float)((last ? c[0] : c[d - 3]) - g1);
+    TRY(run(pe));
+    if (last) return DASH_OK;
+  }
+  // b_{d-3} is in b1 and b_{d-2} in b2, i.e. b1 = b_{k+1} and b2 = b_{k+2} for k = d - 4; from here
+  // on b_k is written over b_{k+2}
+  for (int k = d - 4; k >= 1; --k) {
+    auto pe = clenshaw(b1, b2, b2, false);
+    pe.second.gamma = (float)c[k];
+    TRY(run(pe));
+    std::swap(b1, b2);
+  }
+  auto pe = clenshaw(b1, b2, X, true);
+  pe.second.gamma = (float)c[0];
+  TRY(run(pe));
   return DASH_OK;
 }
 

@@ -36,10 +36,11 @@ constexpr int COEF_STRIDE = 8;
 // monitor (optional): monitor[b * mon_stride] += mon_mul * sum over the block of (D - I)^2
 //   (accumulated with atomics; the caller zero-fills it and takes sqrt/ sqrt(B) afterwards).
 // status (optional): status[b] |= 2 when D or D2 holds a non-finite value.
-// fold_c (fp32 triangle-only NN products whose C is their right operand Y and that carry E, i.e.
-// Clenshaw's b_{k+1} and b_{k+2}): D = alpha_b (acc + c_over_a_b C) + delta_b E + gamma_b I, with C
-// added from the staged Y slices inside the product and E loaded during its last k-slice;
-// c_over_a_b = c_over_a * coef[ic] must equal beta_b / alpha_b, and beta/ib are then unused.
+// fold_c (fp32 triangle-only NN products whose C is their right operand Y, i.e. Clenshaw's
+// b_{k+1}): D = alpha_b (acc + c_over_a_b C) + delta_b E + gamma_b I, with C added from the staged
+// (and possibly mapped) Y slices inside the product and E loaded during its last k-slice.  E is
+// required, except in a launch that maps Y, which takes none.  c_over_a_b = c_over_a * coef[ic]
+// must equal beta_b / alpha_b, and beta/ib are then unused.
 struct Epilogue {
   float alpha = 1.f, beta = 0.f, delta = 0.f, gamma = 0.f, alpha2 = 0.f, gamma2 = 0.f;
   int8_t ia = CO_NONE, ib = CO_NONE, id = CO_NONE, ig = CO_NONE, ia2 = CO_NONE, ig2 = CO_NONE;
@@ -55,9 +56,10 @@ struct Epilogue {
 
 // One batched product over N blocks: D_b = epi(X_b Y_b).  X/Y element type is `in_prec`,
 // D/D2 element type is `out_prec`; C/E are fp32.  Stride between blocks: B*B elements.
-// map_x / map_y (binary16 operands only): the operand enters the product as map_a Z + map_g I,
-// formed while it is staged; map_a must be a power of two (each element is then the exact value
-// rounded once to binary16).
+// map_x / map_y: the operand enters the product as a Z + map_g I, a = map_a * coef[map_ia], formed
+// while it is staged.  Binary16 operands (map_ia unused): map_a must be a power of two (each element
+// is then the exact value rounded once to binary16).  fp32 operands: only map_y, in the Clenshaw
+// launches (fold_c), one fma per element.
 struct Product {
   const void* X = nullptr;
   const void* Y = nullptr;
@@ -67,6 +69,7 @@ struct Product {
   void* D2 = nullptr;
   bool map_x = false, map_y = false;
   float map_a = 0.f, map_g = 0.f;
+  int8_t map_ia = CO_NONE;
 };
 
 enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed

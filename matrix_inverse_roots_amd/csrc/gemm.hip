@@ -37,14 +37,20 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
       (epi.alpha != 1.f || epi.ia != CO_NONE || epi.gamma != 0.f || epi_uses_ce(probs, nprob)))
     return hipErrorInvalidValue;
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
-  if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || probs[0].C != probs[0].Y ||
-                     (nprob > 1 && probs[1].C != probs[1].Y) || !probs[0].C || !probs[0].E ||
-                     (nprob > 1 && !probs[1].E)))
+  // and E in every problem, except the launches that map Y, which have none
+  auto fold_ok = [&](const Product& p) { return p.C && p.C == p.Y && (p.map_y ? !p.E : p.E != nullptr); };
+  if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) ||
+                     (nprob > 1 && !fold_ok(probs[1]))))
     return hipErrorInvalidValue;
   // operand maps exist in the binary16 kernels that stage rows of both operands (the 256-wide tile
-  // with a symmetric right operand, and the 128/64-wide tiles)
+  // with a symmetric right operand, and the 128/64-wide tiles) and, for the right operand, in the
+  // fp32 Clenshaw launches
   const bool maps = probs[0].map_x || probs[0].map_y || (nprob > 1 && (probs[1].map_x || probs[1].map_y));
-  if (maps && (in_prec != DASH_FP16 || (B % 256 == 0 && !y_sym))) return hipErrorInvalidValue;
+  const bool map_x = probs[0].map_x || (nprob > 1 && probs[1].map_x);
+  if (maps && in_prec == DASH_FP16 && B % 256 == 0 && !y_sym) return hipErrorInvalidValue;
+  // (fp32: every problem of the launch maps its Y)
+  if (maps && in_prec == DASH_FP32 && (map_x || !epi.fold_c || (nprob > 1 && probs[0].map_y != probs[1].map_y)))
+    return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);

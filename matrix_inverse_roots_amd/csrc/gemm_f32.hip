@@ -17,7 +17,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS, bool CY>
+template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS, bool CY, bool MAPY = false>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BK = 32;
   constexpr int WT = TILE / 2;
@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
       }
     }
   };
-  auto sstore = [&](int buf) {
+  // MAPY (Clenshaw's first product, a launch of its own): Y = A is read as b_{d-1} = a A + g I
+  const float ya = MAPY ? P.map_a * coef_of(a.epi, P.map_ia, tc.b) : 0.f;
+  auto sstore = [&](int buf, int k0) {
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
       const int f = tid + 256 * r;
@@ -76,7 +78,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
       }
       if (!TY) {
         const int krow = f / (TILE / 4), c4 = f % (TILE / 4);
-        *(f32x4*)&Bs[buf][krow * LDB + 4 * c4] = rb[r];
+        f32x4 v = rb[r];
+        if constexpr (MAPY) {
+          const int d = k0 + krow - (j0 + 4 * c4);  // Y[k][j] is on the diagonal when j == k
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], ya, q == d ? P.map_g : 0.f);
+        }
+        *(f32x4*)&Bs[buf][krow * LDB + 4 * c4] = v;
       } else {
         const int row = f / (BK / 4), c4 = f % (BK / 4);
 #pragma unroll
@@ -134,31 +142,33 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
     }
   };
   gload(0);
-  sstore(0);
+  sstore(0, 0);
   __syncthreads();
   float ev[CY ? MT : 1][MT][16];
   if constexpr (CY) {
     for (int kt = 0; kt + 1 < KT; ++kt) {
       gload((kt + 1) * BK);
       compute(kt);
-      sstore((kt + 1) & 1);
+      sstore((kt + 1) & 1, (kt + 1) * BK);
       __syncthreads();
     }
-    // last k-slice: a Clenshaw launch (always with E) loads its E values first, so that their
-    // latency overlaps this slice's MFMAs
-    load_e<MT, MT, WT, WT, TILE>(a, tc, P, wm, wn, lane, ev);
+    // last k-slice: a Clenshaw launch loads its E values first, so that their latency overlaps
+    // this slice's MFMAs (the mapped first product has no E)
+    if constexpr (!MAPY) load_e<MT, MT, WT, WT, TILE>(a, tc, P, wm, wn, lane, ev);
     compute(KT - 1);
     __syncthreads();
   } else {
     for (int kt = 0; kt < KT; ++kt) {
       if (kt + 1 < KT) gload((kt + 1) * BK);
       compute(kt);
-      if (kt + 1 < KT) sstore((kt + 1) & 1);
+      if (kt + 1 < KT) sstore((kt + 1) & 1, (kt + 1) * BK);
       __syncthreads();
     }
   }
   if (CY) P.C = nullptr;  // already in the accumulators
-  if constexpr (CY)
+  if constexpr (CY && MAPY)
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+  else if constexpr (CY)
     epilogue<MT, MT, WT, WT, SYM, TO, false, true, TILE, SMEM_BYTES, CHECKS, true>(a, tc, P, acc, wm, wn, lane, smem,
                                                                                   ev);
   else
@@ -169,7 +179,9 @@ template <int TILE, bool CHECKS>
 hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, bool c_is_y, hipStream_t stream) {
   a.tdim = a.B / TILE;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
+  const bool map_y = a.p0.map_y || (a.nprob > 1 && a.p1.map_y);
   if (trans == Trans::NN) {
+    if (sym && c_is_y && map_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true, true>, a, stream);
     if (sym && c_is_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true>, a, stream);
     if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, false>, a, stream);
     return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false>, a, stream);
