@@ -76,7 +76,7 @@ enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transpose
 
 // Enqueue one or two batched products sharing shape, precision and epilogue scalars (two problems
 // in one launch fill the GPU better).  sym: compute only the upper-triangle tiles and mirror them
-// (exactly symmetric output; C read from the upper triangle).  y_sym: every right operand Y is
+// (exactly symmetric output; C and E read from the upper triangle; no second output D2).  y_sym: every right operand Y is
 // exactly symmetric (Y^T == Y bitwise), so binary16 kernels may read its columns as rows.
 hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_prec in_prec, dash_prec out_prec,
                        Trans trans, bool sym, const Epilogue& epi, hipStream_t stream, bool y_sym = false);

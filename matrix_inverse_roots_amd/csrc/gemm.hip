@@ -32,10 +32,8 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   a.N = N;
   a.B = B;
   a.epi = epi;
-  // a mirrored second output is re-derived from D: D must be the bare accumulator
-  if (sym && nprob >= 1 && (probs[0].D2 || (nprob > 1 && probs[1].D2)) &&
-      (epi.alpha != 1.f || epi.ia != CO_NONE || epi.gamma != 0.f || epi_uses_ce(probs, nprob)))
-    return hipErrorInvalidValue;
+  // triangle-only products write their mirror straight from the accumulators: no second output
+  if (sym && (probs[0].D2 || (nprob > 1 && probs[1].D2))) return hipErrorInvalidValue;
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
   // and E in every problem, except the launches that map Y, which have none
   auto fold_ok = [&](const Product& p) { return p.C && p.C == p.Y && (p.map_y ? !p.E : p.E != nullptr); };

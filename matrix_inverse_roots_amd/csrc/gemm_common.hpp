@@ -101,18 +101,13 @@ __device__ __forceinline__ TO cvt_out(float v) {
 //
 //   D  = alpha acc + beta C + delta E + gamma I,   D2 = alpha2 acc + gamma2 I   (per-block coefficients)
 //
-// SYM (triangle-only products): only tiles ti <= tj run, and within a diagonal tile only i <= j is
-// kept.  Each kept element is stored at (i, j) directly and at (j, i) through LDS (a diagonal tile
-// stores all its elements directly and the mirror then overwrites the strict lower part: stores of
-// one workgroup before and after the barrier are ordered).  In the 32x32
-// accumulator layout a lane's 4 consecutive r are 4 consecutive rows of one column, i.e. 4
-// consecutive entries of a row of the transposed tile, so the transposed tile T[jl][il] is filled
-// with one vector LDS store per 4 values and read back in 16-byte row pieces.  When T fits in
-// `smem` whole (ONE_PASS) it is filled while D is stored; otherwise the tile is mirrored in passes
-// of R rows, recomputed from the products in acc (or from D's values kept in acc when C/E enter
-// D; a second output D2 is then re-derived from D, which requires alpha = 1, gamma = 0 and no C/E,
-// enforced on the host).  The monitor counts off-diagonal
-// kept elements twice under SYM.
+// SYM (triangle-only products, no D2): only tiles ti <= tj run.  Each element is stored at (i, j),
+// and at (j, i) by the same lane: its 4 consecutive r are 4 consecutive rows of one column, i.e. a
+// 16-byte piece of a row of the mirror.  In a diagonal tile the direct stores keep i <= j and the
+// mirror i < j, so no element is written twice.  The monitor counts off-diagonal kept elements
+// twice under SYM.  C/E loads of one row of accumulators are issued before its stores (D may alias
+// E: each lane reads and writes only its own elements, so loading the chunk first is still exact);
+// with E_PRE, E's values come from ev_pre (load_e).
 template <typename TO>
 struct Vec4;
 template <>
@@ -123,24 +118,6 @@ template <>
 struct Vec4<_Float16> {
   typedef _Float16 type __attribute__((ext_vector_type(4)));
 };
-
-// read back R rows-worth of the transposed tile T (pitch PITCH) into Dst rows j0 + jl, columns
-// i0 + p R + c; a diagonal tile writes only its strict lower part (c + p R < jl)
-template <typename TO, int TILE, int R, int PITCH>
-__device__ __forceinline__ void mirror_readback(TO* Dst, const TO* T, int B, int i0, int j0, int p, bool diag_tile) {
-  constexpr int PER16 = 16 / (int)sizeof(TO);  // elements per 16-byte piece
-  typedef TO v16 __attribute__((ext_vector_type(PER16)));
-  for (int g = threadIdx.x; g < TILE * R / PER16; g += blockDim.x) {
-    const int jl = g / (R / PER16), c = (g - jl * (R / PER16)) * PER16;
-    const int il = p * R + c;
-    TO* dst = Dst + (int64_t)(j0 + jl) * B + i0 + il;
-    if (!diag_tile || il + PER16 - 1 < jl) {
-      *(v16*)dst = *(const v16*)&T[jl * PITCH + c];
-    } else if (il < jl) {
-      for (int q = 0; il + q < jl; ++q) dst[q] = T[jl * PITCH + c + q];
-    }
-  }
-}
 
 // E values of a lane's accumulator elements, loaded ahead of the epilogue (E_PRE) so that their
 // latency overlaps the last k-slice of the product.
@@ -165,19 +142,12 @@ __device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, c
 
 // HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
 // that E_PRE takes E's values from ev_pre, loaded by load_e).
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE,
-          int SMEM_BYTES, bool CHECKS, bool E_PRE = false>
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE, bool CHECKS,
+          bool E_PRE = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
-                                         f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane, char* smem,
+                                         const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                          const float (*ev_pre)[MTN][16] = nullptr) {
-  constexpr bool HAS_CE = HAS_C || HAS_E;
   typedef typename Vec4<TO>::type v4;
-  constexpr int PAD = 16 / (int)sizeof(TO);  // keeps every T row 16-byte aligned
-  constexpr bool ONE_PASS = TILE * (TILE + PAD) * (int)sizeof(TO) <= SMEM_BYTES;
-  constexpr int R1 = ONE_PASS ? TILE : (TILE * (TILE / 2 + PAD) * (int)sizeof(TO) <= SMEM_BYTES ? TILE / 2 : TILE / 4);
-  constexpr int R = R1;
-  constexpr int PITCH = R + PAD;
-  static_assert(TILE * PITCH * (int)sizeof(TO) <= SMEM_BYTES, "mirror staging does not fit in LDS");
   const Epilogue& e = a.epi;
   const int B = a.B;
   const int64_t b = tc.b;
@@ -189,18 +159,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   const float al2 = e.alpha2 * coef_of(e, e.ia2, b);
   const float ga2 = e.gamma2 * coef_of(e, e.ig2, b);
   TO* D = (TO*)P.D + off;
-  TO* D2 = P.D2 ? (TO*)P.D2 + off : nullptr;
+  TO* D2 = (!SYM && P.D2) ? (TO*)P.D2 + off : nullptr;
   const float* C = P.C ? P.C + off : nullptr;
   const float* E = P.E ? P.E + off : nullptr;
   const int li = lane & 31, h = lane >> 5;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const bool diag_tile = SYM && tc.ti == tc.tj;
-  TO* T = (TO*)smem;
   float mon = 0.f;
   bool bad = false;
-  // One row of MFMA tiles at a time: all C/E loads of the chunk are issued before any store, so
-  // their latency is paid once per chunk (D may alias E: a lane reads and writes only its own
-  // elements, so loading the chunk first is still exact).
 #pragma unroll
   for (int mt = 0; mt < MTM; ++mt) {
     float cv[MTN][16], ev[MTN][16];
@@ -233,16 +199,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           float v = al * x + be * cv[nt][r] + de * ev[nt][r];
           if (i == j) v += ga;
           pk[q] = cvt_out<TO>(v);
-          if (SYM && !ONE_PASS && HAS_CE) acc[mt][nt][r] = v;  // C/E are not re-read by the passes
-          // a diagonal tile stores its lower part too; the mirror overwrites it after the barrier
           const int64_t idx = (int64_t)i * B + j;
-          D[idx] = cvt_out<TO>(v);
+          if (!diag_tile || il <= jl) D[idx] = pk[q];
           float v2 = 0.f;
           if (D2) {
             v2 = al2 * x + (i == j ? ga2 : 0.f);
             D2[idx] = cvt_out<TO>(v2);
           }
-          if (CHECKS && !(diag_tile && i > j)) {
+          if (CHECKS && !(diag_tile && il > jl)) {
             bad |= !isfinite(v) || (D2 && !isfinite(v2));
             if (e.monitor) {
               const float dd = v - (i == j ? 1.f : 0.f);
@@ -250,7 +214,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
             }
           }
         }
-        if (SYM && ONE_PASS) *(v4*)&T[jl * PITCH + il0] = pk;
+        if (SYM) {
+          TO* md = D + (int64_t)(j0 + jl) * B + i0 + il0;  // mirror row j, columns i .. i + 3
+          if (!diag_tile || il0 + 3 < jl) {
+            *(v4*)md = pk;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (il0 + q < jl) md[q] = pk[q];
+          }
+        }
       }
   }
   if (CHECKS && e.monitor) {
@@ -258,66 +231,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
   if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
-  if (!SYM) return;
-
-  if (ONE_PASS) {
-    __syncthreads();
-    mirror_readback<TO, TILE, R, PITCH>(D, T, B, i0, j0, 0, diag_tile);
-    if (D2) {  // refill T with D2's values (acc still holds the products)
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;
-            const int jl = wn * WTN + nt * 32 + li;
-            v4 pk;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              pk[q] = cvt_out<TO>(al2 * acc[mt][nt][4 * r4 + q] + (il0 + q + i0 == jl + j0 ? ga2 : 0.f));
-            *(v4*)&T[jl * PITCH + il0] = pk;
-          }
-      __syncthreads();
-      mirror_readback<TO, TILE, R, PITCH>(D2, T, B, i0, j0, 0, diag_tile);
-    }
-    return;
-  }
-
-  // multi-pass mirror: pass p covers tile rows [p R, p R + R), T[jl][il - p R]
-  constexpr int PASSES = TILE / R;
-  for (int out = 0; out < (D2 ? 2 : 1); ++out) {
-    TO* Dst = out ? D2 : D;
-    for (int p = 0; p < PASSES; ++p) {
-      __syncthreads();  // LDS is free: the main loop or the previous read-back is done
-#pragma unroll
-      for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;
-            const int jl = wn * WTN + nt * 32 + li;
-            if (il0 / R != p) continue;
-            v4 pk;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bool dg = (il0 + q + i0 == jl + j0);
-              const float x = acc[mt][nt][4 * r4 + q];  // D's value (HAS_CE) or the product
-              float w;
-              if (out)
-                w = al2 * x + (dg ? ga2 : 0.f);  // with HAS_CE, D2 requires D = acc (host check)
-              else
-                w = HAS_CE ? x : al * x + (dg ? ga : 0.f);
-              pk[q] = cvt_out<TO>(w);
-            }
-            *(v4*)&T[jl * PITCH + (il0 - p * R)] = pk;
-          }
-      __syncthreads();
-      mirror_readback<TO, TILE, R, PITCH>(Dst, T, B, i0, j0, p, diag_tile);
-    }
-  }
 }
 
 // Epilogue for binary16 outputs (no C/E operands, no second output).  Kept elements are stored
@@ -392,79 +305,6 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
     } else if (il < jl) {  // the chunk crossing the diagonal: strict upper part only
       for (int q = 0; il + q < jl; ++q) dst[q] = T[jl * PITCH + il + q];
     }
-  }
-}
-
-// Epilogue for fp32 outputs of the binary16 products (no C/E operands, no second output: the last
-// coupled-Newton product).  Kept elements are stored straight from the accumulators (lanes 0-31
-// cover 128 contiguous bytes of a row); SYM mirrors through LDS in passes of R tile rows, the
-// transposed rows T[jl][il - p R] written with one 16-byte LDS store per 4 values and read back as
-// 16-byte pieces (a diagonal tile stores everything directly and the mirror then overwrites its
-// strict lower part).  Monitor and status (CHECKS) as in `epilogue`.
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE, int SMEM_BYTES, bool CHECKS>
-__device__ __forceinline__ void epilogue_direct_f32(const GemmArgs& a, const TileCoord& tc, const Product& P,
-                                                    const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
-                                                    char* smem) {
-  constexpr int R = TILE * (TILE + 4) * 4 <= SMEM_BYTES ? TILE
-                    : (TILE * (TILE / 2 + 4) * 4 <= SMEM_BYTES ? TILE / 2 : TILE / 4);
-  constexpr int PITCH = R + 4;
-  static_assert(TILE * PITCH * 4 <= SMEM_BYTES, "mirror staging does not fit in LDS");
-  const Epilogue& e = a.epi;
-  const int B = a.B;
-  const int64_t b = tc.b;
-  const float al = e.alpha * coef_of(e, e.ia, b);
-  const float ga = e.gamma * coef_of(e, e.ig, b);
-  const int li = lane & 31, h = lane >> 5;
-  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
-  const bool diag_tile = SYM && tc.ti == tc.tj;
-  float* T = (float*)smem;
-  float* D = (float*)P.D + b * (int64_t)B * B;
-  float mon = 0.f;
-  bool bad = false;
-#pragma unroll
-  for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int jl = wn * WTN + nt * 32 + li;
-        const bool on_diag = (i0 + il == j0 + jl);
-        const float v = al * acc[mt][nt][r] + (on_diag ? ga : 0.f);
-        D[(int64_t)(i0 + il) * B + j0 + jl] = v;
-        if (CHECKS && !(diag_tile && il > jl)) {
-          bad |= !isfinite(v);
-          if (e.monitor) {
-            const float dd = v - (on_diag ? 1.f : 0.f);
-            mon += (SYM && !on_diag) ? 2.f * dd * dd : dd * dd;
-          }
-        }
-      }
-  if (CHECKS && e.monitor) {
-    mon = wave_sum(mon);
-    if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
-  }
-  if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
-  if (!SYM) return;
-  for (int p = 0; p < TILE / R; ++p) {
-    __syncthreads();  // LDS is free: the main loop or the previous read-back is done
-#pragma unroll
-    for (int mt = 0; mt < MTM; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < MTN; ++nt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3, one pass
-          const int jl = wn * WTN + nt * 32 + li;
-          if (il0 / R != p) continue;
-          f32x4 pk;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            pk[q] = al * acc[mt][nt][4 * r4 + q] + (i0 + il0 + q == j0 + jl ? ga : 0.f);
-          *(f32x4*)&T[jl * PITCH + (il0 - p * R)] = pk;
-        }
-    __syncthreads();
-    mirror_readback<float, TILE, R, PITCH>(D, T, B, i0, j0, p, diag_tile);
   }
 }
 

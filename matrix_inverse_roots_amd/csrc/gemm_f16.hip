@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
 }
 
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
   if constexpr (sizeof(TO) == 2)
     epilogue_staged_f16<MTM, MTN, WTM, WTN, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
   else
-    epilogue_direct_f32<MTM, MTN, WTM, WTN, SYM, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MTM, MTN, WTM, WTN, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
 }
 
 template <bool SYM, bool CHECKS>

@@ -5,7 +5,9 @@
 // k-slice.  Within one k-step, lane half h of an MFMA takes k = h*16 + s at step s, so each lane
 // reads 16 consecutive k of its X row with 128-bit LDS loads; the Y operand is a single float per
 // lane read straight from a row of the Y tile.  The statistics products read one operand
-// transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them.
+// transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them:
+// a lane's 4 consecutive accumulator rows of one column are a 16-byte piece of a mirror row, which
+// the lane stores itself.
 // CY: the epilogue's C operand is the right operand Y itself (Clenshaw's b_{k+1}), so the C tile
 // rows [i0, i0 + TILE) pass through LDS as k-slices of Y; each wave adds (beta/alpha) C to its
 // accumulators from those slices and the epilogue reads no C from memory.
@@ -167,12 +169,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   }
   if (CY) P.C = nullptr;  // already in the accumulators
   if constexpr (CY && MAPY)
-    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
   else if constexpr (CY)
-    epilogue<MT, MT, WT, WT, SYM, TO, false, true, TILE, SMEM_BYTES, CHECKS, true>(a, tc, P, acc, wm, wn, lane, smem,
-                                                                                  ev);
+    epilogue<MT, MT, WT, WT, SYM, TO, false, true, TILE, CHECKS, true>(a, tc, P, acc, wm, wn, lane, ev);
   else
-    epilogue<MT, MT, WT, WT, SYM, TO, true, true, TILE, SMEM_BYTES, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+    epilogue<MT, MT, WT, WT, SYM, TO, true, true, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
 }
 
 template <int TILE, bool CHECKS>
