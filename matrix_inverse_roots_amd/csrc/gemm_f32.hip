@@ -1,8 +1,8 @@
 // gemm_f32.hip -- batched fp32 B x B products on the 32x32x2 fp32 MFMA.
 //
 // Workgroup = 4 waves (256 threads), macro tile TILE x TILE (128, or 64 when B is not a multiple of
-// 128), wave tile (TILE/2)^2, k-step 32, LDS double buffer with register prefetch of the next
-// k-slice.  Within one k-step, lane half h of an MFMA takes k = h*16 + s at step s, so each lane
+// 128), wave tile (TILE/2)^2, k-step 32, LDS double buffer fed from two register slots, so the next
+// two k-slices are in flight while one is multiplied.  Within one k-step, lane half h of an MFMA takes k = h*16 + s at step s, so each lane
 // reads 16 consecutive k of its X row with 128-bit LDS loads; the Y operand is a single float per
 // lane read straight from a row of the Y tile.  The statistics products read one operand
 // transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them:
@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, h = lane >> 5;
 
-  f32x4 ra[NL], rb[NL];
-  auto gload = [&](int k0) {
+  // two register slots: k-slices kt + 1 and kt + 2 are in flight while slice kt is in LDS
+  f32x4 ra0[NL], rb0[NL], ra1[NL], rb1[NL];
+  auto gload = [&](f32x4 (&ra)[NL], f32x4 (&rb)[NL], int k0) {
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
       const int f = tid + 256 * r;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   };
   // MAPY (Clenshaw's first product, a launch of its own): Y = A is read as b_{d-1} = a A + g I
   const float ya = MAPY ? P.map_a * coef_of(a.epi, P.map_ia, tc.b) : 0.f;
-  auto sstore = [&](int buf, int k0) {
+  auto sstore = [&](const f32x4 (&ra)[NL], const f32x4 (&rb)[NL], int buf, int k0) {
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
       const int f = tid + 256 * r;
@@ -143,30 +144,31 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
       }
     }
   };
-  gload(0);
-  sstore(0, 0);
+  // KT = B / 32 is even; each loop pass runs two k-slices, with the register slots alternating
+  gload(ra0, rb0, 0);
+  sstore(ra0, rb0, 0, 0);
   __syncthreads();
-  float ev[CY ? MT : 1][MT][16];
-  if constexpr (CY) {
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-      gload((kt + 1) * BK);
-      compute(kt);
-      sstore((kt + 1) & 1, (kt + 1) * BK);
-      __syncthreads();
-    }
-    // last k-slice: a Clenshaw launch loads its E values first, so that their latency overlaps
-    // this slice's MFMAs (the mapped first product has no E)
-    if constexpr (!MAPY) load_e<MT, MT, WT, WT, TILE>(a, tc, P, wm, wn, lane, ev);
-    compute(KT - 1);
+  gload(ra1, rb1, BK);
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    gload(ra0, rb0, (kt + 2) * BK);
+    compute(kt);
+    sstore(ra1, rb1, (kt + 1) & 1, (kt + 1) * BK);
     __syncthreads();
-  } else {
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) gload((kt + 1) * BK);
-      compute(kt);
-      if (kt + 1 < KT) sstore((kt + 1) & 1, (kt + 1) * BK);
-      __syncthreads();
-    }
+    gload(ra1, rb1, (kt + 3) * BK);
+    compute(kt + 1);
+    sstore(ra0, rb0, (kt + 2) & 1, (kt + 2) * BK);
+    __syncthreads();
   }
+  compute(kt);
+  sstore(ra1, rb1, (kt + 1) & 1, (kt + 1) * BK);
+  __syncthreads();
+  // last k-slice: a Clenshaw launch loads its E values first, so that their latency overlaps this
+  // slice's MFMAs (the mapped first product has no E)
+  float ev[CY ? MT : 1][MT][16];
+  if constexpr (CY && !MAPY) load_e<MT, MT, WT, WT, TILE>(a, tc, P, wm, wn, lane, ev);
+  compute(kt + 1);
+  __syncthreads();
   if (CY) P.C = nullptr;  // already in the accumulators
   if constexpr (CY && MAPY)
     epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
