@@ -349,6 +349,15 @@ def test_scale_equivariance_bitwise(tiny):
     H1, _ = cheb(Ad, s, 12, 0.02, 1.25)
     H16, _ = cheb(16 * Ad, 16 * s, 12, 0.02, 1.25)
     assert torch.equal(H16 * 2, H1)
+    # binary16 operands: a power-of-two scale shifts every rounding exactly, through the
+    # power-of-two prescale of the half-precision power iteration too
+    V0 = to_dev(di.start_vectors(64, 32))
+    p1 = power_scale(Ad, V0, 10, dash.DASH_FP16)
+    p16 = power_scale(16 * Ad, V0, 10, dash.DASH_FP16)
+    assert torch.equal(p16, 16 * p1)
+    F1, _, _ = cn(Ad, p1, 6, dash.DASH_FP16)
+    F16, _, _ = cn(16 * Ad, p16, 6, dash.DASH_FP16)
+    assert torch.equal(F16 * 2, F1)
 
 
 def test_batch_independence_and_determinism(conditioned):
@@ -364,6 +373,12 @@ def test_batch_independence_and_determinism(conditioned):
     Xp, _, _ = cn(Ad[perm].contiguous(), s[perm].contiguous(), 6)
     Xc, _, _ = cn(Ad, s, 6)
     assert torch.equal(Xp, Xc[perm])
+    Hp, _, _ = cn(Ad[perm].contiguous(), s[perm].contiguous(), 6, dash.DASH_FP16)
+    Hc, _, _ = cn(Ad, s, 6, dash.DASH_FP16)
+    assert torch.equal(Hp, Hc[perm])
+    Cp, _ = cheb(Ad[perm].contiguous(), s[perm].contiguous(), 16, 0.01, 1.25)
+    Cc, _ = cheb(Ad, s, 16, 0.01, 1.25)
+    assert torch.equal(Cp, Cc[perm])
 
 
 def test_bad_blocks_are_flagged_and_isolated(tiny):
@@ -383,8 +398,24 @@ def test_bad_blocks_are_flagged_and_isolated(tiny):
     assert np.array_equal(to_host(stc).astype(int) & 1, [0, 1, 1, 0])
     Xh, sth = cheb(Ad, s, 8, 0.02, 1.25)
     assert np.array_equal(to_host(sth).astype(int) & 1, [0, 1, 1, 0])
+    Xf, _, stf = cn(Ad, s, 5, dash.DASH_FP16)
+    assert np.array_equal(to_host(stf).astype(int) & 1, [0, 1, 1, 0])
+    assert np.all(np.isnan(to_host(Xf)[[1, 2]]))
     # a non-finite input block: flagged as a non-finite output, neighbours untouched
     bad = Ad.clone()
     bad[0, 3, 5] = float("inf")
-    _, _, _, st2 = ndb(bad, frob_scale(Ad), 4, 4)
+    bad[0, 5, 3] = float("inf")  # CN and Chebyshev read the upper triangle only
+    s_ok = frob_scale(Ad)
+    _, _, _, st2 = ndb(bad, s_ok, 4, 4)
     assert np.array_equal(to_host(st2).astype(int) & 2, [2, 0, 0, 0])
+    X_good, _, _ = cn(Ad, s_ok, 5)
+    for prec in (dash.DASH_FP32, dash.DASH_FP16):
+        Xb, _, stb = cn(bad, s_ok, 5, prec)
+        assert np.array_equal(to_host(stb).astype(int) & 2, [2, 0, 0, 0])
+        if prec == dash.DASH_FP32:
+            assert torch.equal(Xb[1:], X_good[1:])
+    Hb, sth2 = cheb(bad, s_ok, 8, 0.02, 1.25)
+    assert np.array_equal(to_host(sth2).astype(int) & 2, [2, 0, 0, 0])
+    # a non-finite block gives a non-finite power-iteration scale; the solver then flags bit 0
+    s_bad = power_scale(bad, to_dev(di.start_vectors(64, 32)), 10)
+    assert not np.isfinite(to_host(s_bad)[0]) and np.all(np.isfinite(to_host(s_bad)[1:]))
