@@ -40,12 +40,10 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) ||
                      (nprob > 1 && !fold_ok(probs[1]))))
     return hipErrorInvalidValue;
-  // operand maps exist in the binary16 kernels that stage rows of both operands (the 256-wide tile
-  // with a symmetric right operand, and the 128/64-wide tiles) and, for the right operand, in the
-  // fp32 Clenshaw launches
+  // operand maps exist in every binary16 kernel and, for the right operand, in the fp32 Clenshaw
+  // launches
   const bool maps = probs[0].map_x || probs[0].map_y || (nprob > 1 && (probs[1].map_x || probs[1].map_y));
   const bool map_x = probs[0].map_x || (nprob > 1 && probs[1].map_x);
-  if (maps && in_prec == DASH_FP16 && B % 256 == 0 && !y_sym) return hipErrorInvalidValue;
   // (fp32: every problem of the launch maps its Y)
   if (maps && in_prec == DASH_FP32 && (map_x || !epi.fold_c || (nprob > 1 && probs[0].map_y != probs[1].map_y)))
     return hipErrorInvalidValue;
