@@ -144,10 +144,12 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // Column partial sums (w.w, v.w, v.v) of this workgroup's rows of W = A V, and the W rows
-// themselves.  acc: the wave's 32 x 32 MFMA tile (rows wave*32.., column li).
-template <int WAVES, bool HALF>
-__device__ __forceinline__ void power_epilogue(const float* V, float* W, float* part_out, const f32x16& acc, int r0,
-                                               int wave, int lane, float invj, int k, float (*red)[3][KV]) {
+// themselves.  acc: the wave's 32 x 32 MFMA tile (rows wave*32.., column li); vm: the iterate V
+// (normalised, as the product used it) at the same 16 elements, captured from LDS when the k-loop
+// staged the wave's own rows.
+template <int WAVES>
+__device__ __forceinline__ void power_epilogue(const float (&vm)[16], float* W, float* part_out, const f32x16& acc,
+                                               int r0, int wave, int lane, float (*red)[3][KV]) {
   const int li = lane & 31, h = lane >> 5, j = li;
   float ww = 0.f, vw = 0.f, vv = 0.f;
 #pragma unroll
@@ -155,8 +157,7 @@ __device__ __forceinline__ void power_epilogue(const float* V, float* W, float* 
     const int i = r0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
     const float w = acc[r];
     W[(int64_t)i * KV + j] = w;
-    float v = (j < k) ? V[(int64_t)i * KV + j] * invj : 0.f;
-    if (HALF) v = (float)(_Float16)v;  // the binary16 iterate the product used
+    const float v = vm[r];
     ww += w * w;
     vw += v * w;
     vv += v * v;
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  auto compute = [&](int buf) {
+  float vm[16];  // V at the wave's own 16 accumulator elements, for the epilogue
+  auto compute = [&](int kt) {
+    const int buf = kt & 1;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const f32x4 av = *(const f32x4*)&As[buf][(wave * 32 + li) * LDA + h * 16 + 4 * s4];
@@ -250,18 +253,22 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv, acc, 0, 0, 0);
       }
     }
+    if (kt * BK == r0 + wave * 32) {  // this slice's V rows are the wave's own rows
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vm[r] = li < a.k ? Vs[buf][(8 * (r >> 2) + 4 * h + (r & 3)) * LDV + li] : 0.f;
+    }
   };
   const int KT = B / BK;
   auto step = [&](auto slot_c, int kt) {
     constexpr int slot = decltype(slot_c)::value;
     gload(slot_c, (kt + DEPTH) * BK);  // slot held slice kt, already in LDS
-    compute(kt & 1);
+    compute(kt);
     sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
   };
   auto tail_step = [&](auto slot_c, int kt, bool store_next) {
     constexpr int slot = decltype(slot_c)::value;
-    compute(kt & 1);
+    compute(kt);
     if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
   };
@@ -295,8 +302,8 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f32(PowerStepArgs<float
     tail_step(IC<2>{}, kt + 2, true);
     tail_step(IC<3>{}, kt + 3, false);
   }
-  power_epilogue<WAVES, false>(V, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0,
-                               wave, lane, inv_s[li], a.k, red);
+  power_epilogue<WAVES>(vm, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave,
+                        lane, red);
 }
 
 // Binary16 operands: A_b prescaled in binary16, V rounded to binary16 as it is staged (transposed,
@@ -356,25 +363,33 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Floa
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  auto compute = [&](int buf) {
+  float vm[16];  // V (binary16, as the product used it) at the wave's own 16 accumulator elements
+  auto compute = [&](int kt) {
+    const int buf = kt & 1;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const f16x8 av = *(const f16x8*)&As[buf][(wave * 32 + li) * LDA + h * 32 + 8 * s];
       const f16x8 bv = *(const f16x8*)&Vs[buf][li * LDV + h * 32 + 8 * s];
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
     }
+    const int off = r0 + wave * 32 - kt * BK;  // the wave's own rows within this slice, if there
+    if ((unsigned)off < (unsigned)BK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        vm[r] = li < a.k ? (float)Vs[buf][li * LDV + off + 8 * (r >> 2) + 4 * h + (r & 3)] : 0.f;
+    }
   };
   const int KT = B / BK;
   auto step = [&](auto slot_c, int kt) {
     constexpr int slot = decltype(slot_c)::value;
     gload(slot_c, (kt + DEPTH) * BK);
-    compute(kt & 1);
+    compute(kt);
     sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
   };
   auto tail_step = [&](auto slot_c, int kt, bool store_next) {
     constexpr int slot = decltype(slot_c)::value;
-    compute(kt & 1);
+    compute(kt);
     if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (kt + 1) & 1);
     __syncthreads();
   };
@@ -407,8 +422,8 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Floa
     tail_step(IC<2>{}, kt + 2, true);
     tail_step(IC<3>{}, kt + 3, false);
   }
-  power_epilogue<WAVES, true>(V, a.W + b * (int64_t)B * KV,
-                              a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave, lane, inv_s[li], a.k, red);
+  power_epilogue<WAVES>(vm, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave,
+                        lane, red);
 }
 
 // s_b = scale_b * max_{j<k} (v.w / v.v) from the last step's partials
