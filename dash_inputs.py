@@ -100,7 +100,8 @@ def llama_weight_shapes(layers: int = 24, d: int = 2048, ffn: int = 8192):
 
 
 def num_tiles(shapes, B: int) -> int:
-    return sum((r // B) * (c // B) for r, c in shapes)
+    """Tiles of a stack of weights of these shapes (edge tiles of non-multiple sides included)."""
+    return sum((-(-r // B)) * (-(-c // B)) for r, c in shapes)
 
 
 # ---------------------------------------------------------------------------------------------------

@@ -322,28 +322,36 @@ def apply(XL, G, XR, threads: int | None = None) -> np.ndarray:
 def stack(grads, B: int) -> np.ndarray:
     """Blockify weight gradients into a (N_G, B, B) stack: weight-major, then tile row, then tile column.
 
-    [PT] Metodologia, item 1 (gradient blocks G_ij are stacked into an (N, B, B) tensor)."""
+    [PT] Metodologia, item 1 (gradient blocks G_ij are stacked into an (N, B, B) tensor).  The pages
+    tile weights into blocks of about 1k and say nothing of edges; here a weight whose sides are not
+    multiples of B gets ceil(rows/B) x ceil(cols/B) tiles and the part of an edge tile that lies
+    outside the weight is zero."""
     tiles = []
     for W in grads:
         W = np.asarray(W)
         rows, cols = W.shape
-        if rows % B or cols % B:
-            raise ValueError("weight shape %s is not divisible by B=%d" % (W.shape, B))
-        for tr in range(rows // B):
-            for tc in range(cols // B):
-                tiles.append(W[tr * B:(tr + 1) * B, tc * B:(tc + 1) * B])
+        if rows < 1 or cols < 1:
+            raise ValueError("empty weight %s" % (W.shape,))
+        for tr in range(-(-rows // B)):
+            for tc in range(-(-cols // B)):
+                part = W[tr * B:(tr + 1) * B, tc * B:(tc + 1) * B]
+                tile = np.zeros((B, B), dtype=W.dtype)
+                tile[:part.shape[0], :part.shape[1]] = part
+                tiles.append(tile)
     return np.stack(tiles)
 
 
 def unstack(U, shapes, B: int):
-    """Inverse of :func:`stack`: scatter (N_G, B, B) tiles back into weights of the given shapes."""
+    """Inverse of :func:`stack`: scatter (N_G, B, B) tiles back into weights of the given shapes
+    (the padding of edge tiles is dropped)."""
     U = np.asarray(U)
     out, t = [], 0
     for rows, cols in shapes:
         W = np.empty((rows, cols), dtype=U.dtype)
-        for tr in range(rows // B):
-            for tc in range(cols // B):
-                W[tr * B:(tr + 1) * B, tc * B:(tc + 1) * B] = U[t]
+        for tr in range(-(-rows // B)):
+            for tc in range(-(-cols // B)):
+                h, w = min(B, rows - tr * B), min(B, cols - tc * B)
+                W[tr * B:tr * B + h, tc * B:tc * B + w] = U[t][:h, :w]
                 t += 1
         out.append(W)
     assert t == U.shape[0]

@@ -431,7 +431,28 @@ def test_stack_order_and_round_trip():
     back = oracle.unstack(S, shapes, B)
     assert all(np.array_equal(a, b) for a, b in zip(back, W))
     with pytest.raises(ValueError):
-        oracle.stack([np.zeros((6, 8))], B)
+        oracle.stack([np.zeros((0, 8))], B)
+
+
+def test_stack_edge_tiles_are_zero_padded():
+    # sides that are not multiples of B: ceil(rows/B) x ceil(cols/B) tiles, zero outside the weight
+    B = 4
+    shapes = [(6, 9), (3, 2), (4, 5)]
+    g = di.rng(64)
+    W = [g.standard_normal(s) for s in shapes]
+    S = oracle.stack(W, B)
+    assert S.shape == (2 * 3 + 1 + 1 * 2, B, B) and di.num_tiles(shapes, B) == 9
+    assert np.array_equal(S[0], W[0][0:4, 0:4])
+    assert np.array_equal(S[2][:4, :1], W[0][0:4, 8:9]) and not S[2][:, 1:].any()
+    assert np.array_equal(S[5][:2, :1], W[0][4:6, 8:9]) and not S[5][2:].any() and not S[5][:, 1:].any()
+    assert np.array_equal(S[6][:3, :2], W[1]) and not S[6][3:].any() and not S[6][:, 2:].any()
+    assert np.array_equal(S[8][:, :1], W[2][:, 4:5]) and not S[8][:, 1:].any()
+    # a padded tile's Gram products keep the padding zero, the valid part is the weight's own
+    L, R = oracle.update_stats(S, 0.0, np.zeros_like(S), np.zeros_like(S))
+    assert np.allclose(L[6][:3, :3], W[1] @ W[1].T) and not L[6][3:].any() and not L[6][:, 3:].any()
+    assert np.allclose(R[6][:2, :2], W[1].T @ W[1]) and not R[6][2:].any() and not R[6][:, 2:].any()
+    back = oracle.unstack(S, shapes, B)
+    assert all(np.array_equal(a, b) for a, b in zip(back, W))
 
 
 def test_llama_shapes_give_1536_tiles():
