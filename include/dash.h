@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   DASH_OK = 0,
   DASH_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad count, parameter out of range */
-  DASH_ERR_SHAPE = 2,       /* B not a multiple of 64 or out of range, weight not divisible by B */
+  DASH_ERR_SHAPE = 2,       /* B not a multiple of 64 or out of range */
   DASH_ERR_WORKSPACE = 3,   /* ws too small or misaligned */
   DASH_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement (e.g. p != 4) */
   DASH_ERR_DEVICE = 5       /* a HIP launch failed */
@@ -73,11 +73,15 @@ typedef struct {
 /* Blockify: copy the B x B tiles of n weight gradients into G_stack, weight-major, then tile row,
  * then tile column ([PT] Metodologia, item 1: gradient blocks G_ij are stacked into an (N, B, B)
  * tensor so one batched call processes them all).
- * grads [host]: n descriptors; every rows and cols must be divisible by B (else DASH_ERR_SHAPE),
- * ld >= cols, ptr and ld*4 16-byte aligned.  G_stack: sum_w (rows_w/B)(cols_w/B) blocks. */
+ * grads [host]: n descriptors, rows >= 1, cols >= 1, ld >= cols, ptr and ld*4 16-byte aligned.  A
+ * weight gives ceil(rows/B) x ceil(cols/B) tiles; where its sides are not multiples of B, the part of
+ * an edge tile outside the weight is zero.  G_stack: sum_w ceil(rows_w/B) ceil(cols_w/B) blocks.
+ * (A zero-padded tile keeps zero rows/columns in its statistics; damping the L/R stack, e.g. an
+ * initial eps I, keeps such blocks positive definite, and apply leaves the padding zero.) */
 dash_status dash_stack(const dash_mat* grads, int32_t n, int32_t B, float* G_stack, void* stream);
 
-/* Inverse of dash_stack: scatter the tiles of U_stack back into n weight-shaped outputs [host]. */
+/* Inverse of dash_stack: scatter the tiles of U_stack back into n weight-shaped outputs [host]
+ * (the same shape rules; the padding of edge tiles is not written anywhere). */
 dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, int32_t n, void* stream);
 
 /* Shampoo statistics ([TG] body: L and R are kept from products of the gradient):

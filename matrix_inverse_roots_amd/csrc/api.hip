@@ -222,8 +222,7 @@ dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) 
   for (int32_t i = 0; i < n; ++i) {
     if (!m[i].ptr || !aligned(m[i].ptr, 16) || m[i].ld % 4 != 0) return DASH_ERR_INVALID_ARG;
     if (m[i].rows < 1 || m[i].cols < 1 || m[i].ld < m[i].cols) return DASH_ERR_INVALID_ARG;
-    if (m[i].rows % B || m[i].cols % B) return DASH_ERR_SHAPE;
-    t += (m[i].rows / B) * (m[i].cols / B);
+    t += ((m[i].rows + B - 1) / B) * ((m[i].cols + B - 1) / B);
   }
   *tiles = t;
   return DASH_OK;

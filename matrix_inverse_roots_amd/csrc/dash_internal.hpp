@@ -134,12 +134,14 @@ struct PowerPlan {
 hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
 size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
 
-// Stack / unstack n weights: the (rows/B) x (cols/B) tiles of each, in order, into consecutive
-// blocks of `stack` (to_stack) or back out of it.  One launch per COPY_GROUP weights.
+// Stack / unstack n weights: the ceil(rows/B) x ceil(cols/B) tiles of each, in order, into
+// consecutive blocks of `stack` (to_stack) or back out of it; the part of an edge tile outside the
+// weight is zero in the stack and not written back.  One launch per COPY_GROUP weights.
 constexpr int COPY_GROUP = 32;
 struct CopyGroup {
   float* ptr[COPY_GROUP];
   int64_t ld[COPY_GROUP];
+  int64_t rows[COPY_GROUP], cols[COPY_GROUP];
   int64_t row_base[COPY_GROUP + 1];  // first stack row (tile * B + r) of weight i in this launch
   int32_t wg_base[COPY_GROUP + 1];   // first workgroup of weight i
   int32_t tiles_c[COPY_GROUP];       // tile columns of weight i

@@ -197,6 +197,9 @@ __global__ void monitor_finish_kernel(float* m, int64_t n, float inv_sqrt_b) {
 // the weight they belong to.  All loads of a thread are issued before its stores, and both are
 // non-temporal: the data is streamed once and is far larger than the caches.  A launch covers up
 // to COPY_GROUP weights; the weight of a workgroup comes from the prefix table in the arguments.
+// Edge tiles of a weight whose sides are not multiples of B: the part outside the weight is zero
+// in the stack and is not written back (a float4 that straddles the last column goes element by
+// element).
 constexpr int COPY_VEC = 4;
 
 template <bool TO_STACK>
@@ -212,9 +215,11 @@ __global__ __launch_bounds__(256) void tile_copy_kernel(CopyGroup g, int B, floa
   const int64_t t0 = row0 / B;
   const unsigned r0 = (unsigned)(row0 - t0 * B);
   const unsigned tiles_c = (unsigned)g.tiles_c[wi];
-  const int64_t ld = g.ld[wi];
+  const int64_t ld = g.ld[wi], rows = g.rows[wi], cols = g.cols[wi];
   f32x4* lin = (f32x4*)(stack + g.row_base[wi] * B) + q0;
-  f32x4* wp[COPY_VEC];
+  float* wp[COPY_VEC];
+  int64_t col[COPY_VEC];
+  bool in_rows[COPY_VEC];
   f32x4 v[COPY_VEC];
 #pragma unroll
   for (int i = 0; i < COPY_VEC; ++i) {
@@ -223,13 +228,51 @@ __global__ __launch_bounds__(256) void tile_copy_kernel(CopyGroup g, int B, floa
     const unsigned rr = r0 + dr, tt = rr / (unsigned)B, r = rr - tt * (unsigned)B;
     const unsigned t = (unsigned)t0 + tt;  // tiles per weight < 2^31 (checked on the host)
     const unsigned tr = t / tiles_c, tc = t - tr * tiles_c;
-    wp[i] = (f32x4*)(g.ptr[wi] + ((int64_t)tr * B + r) * ld + (int64_t)tc * B) + c4;
-    if (q0 + d < total) v[i] = __builtin_nontemporal_load(TO_STACK ? wp[i] : lin + d);
+    const int64_t grow = (int64_t)tr * B + r;
+    col[i] = (int64_t)tc * B + 4 * c4;
+    in_rows[i] = grow < rows;
+    wp[i] = g.ptr[wi] + grow * ld + col[i];
+  }
+  if (rows % B == 0 && cols % B == 0) {  // no edge tiles in this weight
+#pragma unroll
+    for (int i = 0; i < COPY_VEC; ++i) {
+      const unsigned d = i * 256 + threadIdx.x;
+      if (q0 + d < total) v[i] = __builtin_nontemporal_load(TO_STACK ? (const f32x4*)wp[i] : lin + d);
+    }
+#pragma unroll
+    for (int i = 0; i < COPY_VEC; ++i) {
+      const unsigned d = i * 256 + threadIdx.x;
+      if (q0 + d < total) __builtin_nontemporal_store(v[i], TO_STACK ? lin + d : (f32x4*)wp[i]);
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < COPY_VEC; ++i) {
     const unsigned d = i * 256 + threadIdx.x;
-    if (q0 + d < total) __builtin_nontemporal_store(v[i], TO_STACK ? lin + d : wp[i]);
+    if (q0 + d < total) {
+      if (!TO_STACK) {
+        v[i] = __builtin_nontemporal_load(lin + d);
+      } else if (in_rows[i] && col[i] + 3 < cols) {
+        v[i] = __builtin_nontemporal_load((const f32x4*)wp[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[i][e] = (in_rows[i] && col[i] + e < cols) ? wp[i][e] : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < COPY_VEC; ++i) {
+    const unsigned d = i * 256 + threadIdx.x;
+    if (q0 + d >= total) continue;
+    if (TO_STACK) {
+      __builtin_nontemporal_store(v[i], lin + d);
+    } else if (in_rows[i] && col[i] + 3 < cols) {
+      __builtin_nontemporal_store(v[i], (f32x4*)wp[i]);
+    } else if (in_rows[i]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col[i] + e < cols) wp[i][e] = v[i][e];
+    }
   }
 }
 
@@ -284,11 +327,14 @@ hipError_t launch_tile_copy(const dash_mat* w, int n, int B, float* stack, bool 
     g.wg_base[0] = 0;
     for (int j = 0; j < g.n; ++j) {
       const dash_mat& m = w[i0 + j];
-      const int64_t tiles = (m.rows / B) * (m.cols / B);
+      const int64_t tiles_r = (m.rows + B - 1) / B, tiles_c = (m.cols + B - 1) / B;
+      const int64_t tiles = tiles_r * tiles_c;
       if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
       g.ptr[j] = m.ptr;
       g.ld[j] = m.ld;
-      g.tiles_c[j] = (int32_t)(m.cols / B);
+      g.rows[j] = m.rows;
+      g.cols[j] = m.cols;
+      g.tiles_c[j] = (int32_t)tiles_c;
       g.row_base[j + 1] = g.row_base[j] + tiles * B;
       wgs += (tiles * B * (B / 4) + f4_per_wg - 1) / f4_per_wg;
       if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;

@@ -153,8 +153,9 @@ class FakeMat:
 
 def test_stack_argument_errors():
     B = 64
-    assert _status_of(dash.dash_stack, [FakeMat(P, 128, 96)], B, P2) == _lib.DASH_ERR_SHAPE
+    assert _status_of(dash.dash_stack, [FakeMat(P, 128, 96)], 96, P2) == _lib.DASH_ERR_SHAPE   # B % 64
+    assert _status_of(dash.dash_stack, [FakeMat(P, 0, 96)], B, P2) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_stack, [FakeMat(P, 128, 128, ld=64)], B, P2) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_stack, [FakeMat(P + 8, 128, 128)], B, P2) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_stack, [FakeMat(P, 128, 128)], B, None) == _lib.DASH_ERR_INVALID_ARG
-    assert _status_of(dash.dash_unstack, P2, B, [FakeMat(P, 64, 130, ld=132)]) == _lib.DASH_ERR_SHAPE
+    assert _status_of(dash.dash_unstack, P2, B, [FakeMat(P, 64, 130, ld=130)]) == _lib.DASH_ERR_INVALID_ARG

@@ -324,6 +324,72 @@ def test_stack_many_weights(B):
         assert np.all(h[:, :32] == -7.0) and np.all(h[:, 32 + c:] == -7.0)
 
 
+def _views(shapes, fill, pad=8):
+    """Device views of the given shapes with a 16-byte-aligned leading dimension and room around them."""
+    bigs, views = [], []
+    for r, c in shapes:
+        ld = (c + 3) // 4 * 4 + pad
+        big = torch.full((r + 2, ld + 8), fill, device=DEV)
+        bigs.append(big)
+        views.append(big[1:1 + r, 4:4 + c])
+    return bigs, views
+
+
+def test_stack_edge_tiles():
+    """Sides that are not multiples of B: zero-padded edge tiles, weights smaller than a tile,
+    strided views; unstack writes the weight and nothing else."""
+    B = 64
+    shapes = [(100, 70), (3, 5), (64, 130), (200, 4), (130, 257), (64, 64)]
+    W = [di.gaussian(s, 300 + i) for i, s in enumerate(shapes)]
+    _, src = _views(shapes, 0.0)
+    for v, w in zip(src, W):
+        v.copy_(to_dev(w))
+    n = di.num_tiles(shapes, B)
+    S = torch.full((n, B, B), 5.0, device=DEV)  # padding must be written as zeros
+    dash.dash_stack(src, B, S)
+    assert np.array_equal(to_host(S), oracle.stack(W, B).astype(np.float64))
+    bigs, dst = _views(shapes, -7.0)
+    dash.dash_unstack(S, B, dst)
+    for big, w, (r, c) in zip(bigs, W, shapes):
+        h = to_host(big)
+        assert np.array_equal(h[1:1 + r, 4:4 + c], w.astype(np.float64))
+        h[1:1 + r, 4:4 + c] = -7.0
+        assert np.all(h == -7.0)
+
+
+def test_edge_tiles_through_the_step():
+    """A Shampoo step on weights with edge tiles (stack, statistics over damped L/R, Frobenius scale,
+    NDB, apply, unstack) against the oracle's same steps."""
+    B = 64
+    shapes = [(100, 70), (64, 130)]
+    W = [di.gaussian(s, 320 + i) for i, s in enumerate(shapes)]
+    NG = di.num_tiles(shapes, B)
+    _, src = _views(shapes, 0.0)
+    for v, w in zip(src, W):
+        v.copy_(to_dev(w))
+    G = torch.empty((NG, B, B), device=DEV)
+    dash.dash_stack(src, B, G)
+    damp = np.broadcast_to(0.05 * np.eye(B), (NG, B, B)).astype(np.float32)
+    A = to_dev(np.concatenate([damp, damp]))
+    dash.dash_update_stats(G, NG, B, 0.5, A)
+    s = frob_scale(A)
+    X, _, _, _ = ndb(A, s, 8, 8)
+    U = torch.empty_like(G)
+    dash.dash_apply(X[:NG].contiguous(), X[NG:].contiguous(), G, NG, B, U,
+                    ws=dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV))
+    _, dst = _views(shapes, 0.0)
+    dash.dash_unstack(U, B, dst)
+    G_ref = oracle.stack(W, B).astype(np.float64)
+    L_ref, R_ref = oracle.update_stats(G_ref, 0.5, damp.astype(np.float64), damp.astype(np.float64))
+    A_ref = np.concatenate([L_ref, R_ref])
+    assert np.max(rel_err(to_host(A), A_ref)) < 1e-6
+    X_ref, _, _ = oracle.ndb_inverse_root(A_ref, to_host(s), 8, 8)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    U_ref = oracle.unstack(oracle.apply(X_ref[:NG], G_ref, X_ref[NG:]), shapes, B)
+    for v, u in zip(dst, U_ref):
+        assert np.max(rel_err(to_host(v), u)) < ITERATE_TOL
+
+
 def test_stack_strided_rows():
     B = 64
     big = to_dev(di.gaussian((128, 256), 110))
