@@ -494,9 +494,8 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   TRY(launch_coef(s, N, coef, status, st));
   const int T = iters;
   // binary16 (T >= 2, cn_half): triangle-only products, the iterates being symmetric polynomials
-  // in A and the error floor set by binary16 storage; fp32: full products, which keep the fp32
-  // rounding floor of the iteration lowest at high condition numbers
-  const bool tri = false;
+  // in A and the error floor set by binary16 storage; fp32 (below): full products, which keep the
+  // fp32 rounding floor of the iteration lowest at high condition numbers
   // step 0: M_0 = A/s, S_0 = (5I - M_0)/4, X_1 = S_0;  ||M_0 - I||^2 = 16 ||S_0 - I||^2
   void* S = pool.get();
   void* M = pool.get();
@@ -567,17 +566,17 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.coef = coef;
       e.status = status;
       Product pr = prod(Xk, S, X);
-      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, tri, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, false, e, st, true));
       break;
     }
     void* S2 = pool.get();
     if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
       Product pr = prod(S, S, S2);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
       Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
-      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
+      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
       pool.put(Xk);
       pool.put(S);
       Xk = Xn;
@@ -585,7 +584,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     void* S4 = pool.get();
     {
       Product pr = prod(S2, S2, S4);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
     }
     pool.put(S2);
     // M_{k+1} = M_k S^4 and S_{k+1} = (5I - M_{k+1})/4 from the same accumulator
@@ -600,7 +599,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.gamma = 1.25f;
       e.mon_mul = 16.f;
       Product pr = prod(M, S4, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st, true));
       pool.put(M);
       M = nullptr;
     } else {
@@ -609,7 +608,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.alpha2 = -0.25f;
       e.gamma2 = 1.25f;
       Product pr = prod(M, S4, Mn, nullptr, nullptr, Sn);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, tri, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st, true));
       pool.put(M);
       M = Mn;
     }

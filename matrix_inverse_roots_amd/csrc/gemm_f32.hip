@@ -1,16 +1,18 @@
 // gemm_f32.hip -- batched fp32 B x B products on the 32x32x2 fp32 MFMA.
 //
-// Workgroup = 4 waves (256 threads), macro tile TILE x TILE (128, or 64 when B is not a multiple of
-// 128), wave tile (TILE/2)^2, k-step 32, LDS double buffer fed from two register slots, so the next
-// two k-slices are in flight while one is multiplied.  Within one k-step, lane half h of an MFMA takes k = h*16 + s at step s, so each lane
-// reads 16 consecutive k of its X row with 128-bit LDS loads; the Y operand is a single float per
-// lane read straight from a row of the Y tile.  The statistics products read one operand
-// transposed while staging it (TX / TY) and compute only upper-triangle tiles (SYM), mirroring them:
-// a lane's 4 consecutive accumulator rows of one column are a 16-byte piece of a mirror row, which
-// the lane stores itself.
+// Workgroup = 4 waves (256 threads), macro tile TILE x TILE (128, or 64 when B is not a multiple
+// of 128), wave tile (TILE/2)^2, k-step 32, LDS double buffer fed from two register slots, so the
+// next two k-slices are in flight while one is multiplied.  Within one k-step, lane half h of an
+// MFMA takes k = h*16 + s at step s, so each lane reads 16 consecutive k of its X row with 128-bit
+// LDS loads; the Y operand is a single float per lane read straight from a row of the Y tile.
+// The statistics products read one operand transposed while staging it (TX / TY).  Products with
+// a symmetric result (statistics, Clenshaw) compute only upper-triangle tiles (SYM) and mirror
+// them: a lane's 4 consecutive accumulator rows of one column are a 16-byte piece of a mirror row,
+// which the lane stores itself.
 // CY: the epilogue's C operand is the right operand Y itself (Clenshaw's b_{k+1}), so the C tile
 // rows [i0, i0 + TILE) pass through LDS as k-slices of Y; each wave adds (beta/alpha) C to its
-// accumulators from those slices and the epilogue reads no C from memory.
+// accumulators from those slices and the epilogue reads no C from memory.  MAPY: the right operand
+// is staged as a Y + g I with a per-block a (Clenshaw's first b, formed inside the product).
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
