@@ -61,7 +61,8 @@ typedef enum {
   DASH_OP_CN = 2,
   DASH_OP_CHEB = 3,
   DASH_OP_APPLY = 4,
-  DASH_OP_STATS = 5
+  DASH_OP_STATS = 5,
+  DASH_OP_EVD = 6
 } dash_op;
 
 /* A row-major fp32 weight gradient (device memory): element (r, c) at ptr[r * ld + c]. */
@@ -141,6 +142,29 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
 dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,
                                    double hi, float* X, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
+/* Inverse fourth root through an eigendecomposition A_i = Q diag(w) Q^T, X_i = Q diag(w^{-1/4}) Q^T
+ * ([PT] Definição do Problema, item 2, and Resultados Experimentais: the eigendecomposition is the
+ * root solver whose cost the iterations above avoid; [TG] body).  Batched two-sided block Jacobi in
+ * fp32: the columns are cut into blocks of 32; each round pairs the blocks (circle schedule),
+ * diagonalises every 64 x 64 pair sub-problem by scalar Jacobi and applies its rotation to A and to
+ * the eigenvector estimate; a sweep is B/32 - 1 rounds.  Rotations are skipped where
+ * |A_pq| <= 2^-22 sqrt(A_pp A_qq); a matrix is done after a sweep that rotates nothing, and later
+ * sweeps skip it.  No scale s is needed (the method is scale-free).
+ * refine = 1 adds a second pass: the eigenvector estimate Q is re-orthogonalised by one
+ * Newton-Schulz step, H = Q^T A_i Q is formed from the input again, and the sweeps run on H.  This
+ * removes the rounding the first pass accumulates in its working matrix, which dominates the
+ * error at high condition numbers (four more products and a few sweeps on a nearly diagonal H).
+ * A: [N,B,B], symmetric, read in full.  max_sweeps: 1 .. 100 per pass.  X: [N,B,B], exactly
+ * symmetric; it also holds working data during the call, so it must not alias A.
+ * eigvals: NULL or [N,B] receives w (unordered; column j of Q belongs to w_j).
+ * sweeps:  NULL or [N] receives the number of sweeps run per block over both passes (each pass
+ *          ends with a sweep that rotated nothing unless max_sweeps cut it short).
+ * status:  NULL or [N]: bit 0 when an eigenvalue is not finite or not > 0 (X_i is NaN), bit 1 for a
+ *          non-finite output, bit 2 when max_sweeps ended the last pass before it converged. */
+dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine, float* X,
+                                  float* eigvals, int32_t* sweeps, int32_t* status, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Preconditioned update U_t = (XL_t G_t) XR_t for t < NG ([TG] body: the -1/4 powers of L and R
  * precondition the gradient).  XL, XR, G_stack, U_stack are [NG,B,B]; U_stack must not alias the
  * inputs.  ws holds one [NG,B,B] intermediate. */
@@ -161,7 +185,8 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2);
  * upper-triangle tiles of their symmetric results, so they count tdim(tdim+1)/2 of the tdim^2
  * tiles of each product (Coupled-Newton only with binary16 operands).  op and a1/a2: DASH_OP_NDB (iters1, iters2), DASH_OP_CN (iters, -),
  * DASH_OP_CHEB (degree, -), DASH_OP_APPLY (-, -; N = tiles), DASH_OP_STATS (-, -; N = tiles),
- * DASH_OP_SCALE (steps of power iteration, -).  Returns -1 for invalid arguments. */
+ * DASH_OP_SCALE (steps of power iteration, -), DASH_OP_EVD (sweeps, -: the products of that many
+ * full sweeps plus the final X = Y Y^T).  Returns -1 for invalid arguments. */
 double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2);
 
 const char* dash_status_string(dash_status status);

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     DASH_OP_APPLY,
     DASH_OP_CHEB,
     DASH_OP_CN,
+    DASH_OP_EVD,
     DASH_OP_NDB,
     DASH_OP_SCALE,
     DASH_OP_STATS,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     dash_flops,
     dash_inverse_root_cheb,
     dash_inverse_root_cn,
+    dash_inverse_root_evd,
     dash_inverse_root_ndb,
     dash_scale,
     dash_solver_products,

@@ -15,7 +15,7 @@ library_path = os.path.join(_HERE, "libdash.so")
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
 DASH_FP32, DASH_FP16 = 0, 1
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
-DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS = range(6)
+DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD = range(7)
 
 
 class DashError(RuntimeError):
@@ -50,6 +50,7 @@ def library() -> ctypes.CDLL:
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cheb": (st, [vp, vp, i64, i32, i32, f64, f64, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
@@ -172,6 +173,13 @@ def dash_inverse_root_cheb(A, s, N: int, B: int, degree: int, lo: float, hi: flo
     _check("dash_inverse_root_cheb",
            library().dash_inverse_root_cheb(_ptr(A), _ptr(s), N, B, degree, lo, hi, _ptr(X), _ptr(status), _ptr(ws),
                                             _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_evd(A, N: int, B: int, max_sweeps: int, refine: int, X, eigvals=None, sweeps=None, status=None,
+                          ws=None, stream=None):
+    _check("dash_inverse_root_evd",
+           library().dash_inverse_root_evd(_ptr(A), N, B, max_sweeps, refine, _ptr(X), _ptr(eigvals), _ptr(sweeps),
+                                           _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
 
 
 def dash_apply(XL, XR, G_stack, NG: int, B: int, U_stack, ws=None, stream=None):

@@ -61,6 +61,7 @@ size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + 5 * stack_bytes(N, B, D
 size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + 5 * stack_bytes(N, B, p); }
 size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
+size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
 size_t ws_scale(int64_t N, int B, dash_prec p, int k) { return k == 0 ? 0 : power_workspace_bytes(N, B, p); }
 
 Product prod(const void* X, const void* Y, void* D, const float* C = nullptr, const float* E = nullptr,
@@ -343,6 +344,14 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
     case DASH_OP_APPLY: return 2.0 * full;
     case DASH_OP_STATS: return 2.0 * full * tri(DASH_FP32);
     case DASH_OP_SCALE: return a1 < 1 ? -1.0 : 2.0 * B * (double)B * 32.0 * a1 * (double)N;
+    case DASH_OP_EVD: {
+      // per round: P(P-1)/2 off-pair blocks (two 64^3 products) and P * B/64 eigenvector tiles (one);
+      // B/32 - 1 rounds per sweep; then X = Y Y^T (triangle-only)
+      if (a1 < 1) return -1.0;
+      const double P = B / 64, prod64 = 2.0 * 64 * 64 * 64;
+      const double round = (P * (P - 1) / 2 * 2 + P * (B / 64)) * prod64;
+      return a1 * (B / 32 - 1) * round * (double)N + full * tri(DASH_FP32);
+    }
   }
   return -1.0;
 }
@@ -362,6 +371,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
     case DASH_OP_STATS: *bytes = 0; return DASH_OK;
+    case DASH_OP_EVD: *bytes = ws_evd(N, B); return DASH_OK;
   }
   return DASH_ERR_INVALID_ARG;
 }
@@ -719,6 +729,78 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
   auto pe = clenshaw(b1, b2, X, true);
   pe.second.gamma = (float)c[0];
   TRY(run(pe));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine, float* X,
+                                  float* eigvals, int32_t* sweeps, int32_t* status, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!A || !X || A == X || !aligned(A, 16) || !aligned(X, 16) || !valid_N(N)) return DASH_ERR_INVALID_ARG;
+  if (max_sweeps < 1 || max_sweeps > 100 || (refine != 0 && refine != 1)) return DASH_ERR_INVALID_ARG;
+  if ((eigvals && !aligned(eigvals, 4)) || (sweeps && !aligned(sweeps, 4)) || (status && !aligned(status, 4)))
+    return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_evd(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* V = (float*)cv.take((size_t)N * B * B * sizeof(float));
+  float* T = (float*)cv.take((size_t)N * B * B * sizeof(float));
+  JacobiPlan jp;
+  jp.N = N;
+  jp.B = B;
+  jp.max_sweeps = max_sweeps;
+  jp.pass = 0;
+  jp.tol = 0x1p-22f;
+  jp.R = (float*)cv.take((size_t)N * (B / 64) * 64 * 64 * sizeof(float));
+  jp.rot = (int32_t*)cv.take((size_t)N * (B / 64) * sizeof(int32_t));
+  float* scale = (float*)cv.take((size_t)N * B * sizeof(float));
+  jp.flags = (int32_t*)cv.take((size_t)N * 8 * sizeof(int32_t));
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  // pass 1 on a working copy of A held in X, eigenvectors accumulated in V
+  TRY(hipMemcpyAsync(X, A, (size_t)N * B * B * sizeof(float), hipMemcpyDeviceToDevice, st));
+  TRY(launch_identity(V, N, B, st));
+  jp.A = X;
+  jp.V = V;
+  TRY(launch_jacobi(jp, st));
+  EvdFinish fin;
+  fin.N = N;
+  fin.B = B;
+  fin.scale = scale;
+  fin.flags = jp.flags;
+  fin.eigvals = eigvals;
+  fin.sweeps = sweeps;
+  fin.status = status;
+  if (refine) {
+    // V <- V (3I - V^T V) / 2, then H = V^T (A V) from the input A; pass 2 diagonalises H in T and
+    // rotates V, now held in X
+    Epilogue ns;
+    ns.alpha = -0.5f;
+    ns.gamma = 1.5f;
+    Product p1 = prod(V, V, T);
+    TRY(launch_gemm(&p1, 1, N, B, DASH_FP32, DASH_FP32, Trans::TN, true, ns, st));
+    Product p2 = prod(V, T, X);
+    TRY(launch_gemm(&p2, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+    Product p3 = prod(A, X, V);
+    TRY(launch_gemm(&p3, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+    Product p4 = prod(X, V, T);
+    TRY(launch_gemm(&p4, 1, N, B, DASH_FP32, DASH_FP32, Trans::TN, true, Epilogue(), st));
+    jp.pass = 1;
+    jp.A = T;
+    jp.V = X;
+    TRY(launch_jacobi(jp, st));
+    fin.A = T;
+    fin.V = X;
+    fin.Y = V;
+  } else {
+    fin.A = X;
+    fin.V = V;
+    fin.Y = V;
+  }
+  TRY(launch_evd_finish(fin, st));
+  Epilogue e;  // X = Y Y^T, Y = V diag(w^{-1/8}); finite check of the output (status bit 1)
+  e.status = status;
+  Product pr = prod(fin.Y, fin.Y, X);
+  TRY(launch_gemm(&pr, 1, N, B, DASH_FP32, DASH_FP32, Trans::NT, true, e, st));
   return DASH_OK;
 }
 

@@ -134,6 +134,37 @@ struct PowerPlan {
 hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
 size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
 
+// Eigendecomposition-based inverse fourth root (two-sided block Jacobi).  launch_jacobi runs up
+// to max_sweeps sweeps on the matrices A (diagonalised in place), applying every rotation to V
+// too.  Pass 0 starts the per-matrix sweep count, a later pass adds to it.  launch_evd_finish reads
+// the eigenvalues w = diag(A) and writes Y = V diag(w^{-1/8}) (Y may be V).
+struct JacobiPlan {
+  int64_t N;
+  int B, max_sweeps, pass;
+  float tol;
+  float* A;
+  float* V;
+  float* R;         // [N, B/64, 64, 64]
+  int32_t* rot;     // [N, B/64]
+  int32_t* flags;   // [N, 8]
+};
+hipError_t launch_jacobi(const JacobiPlan& plan, hipStream_t stream);
+struct EvdFinish {
+  int64_t N;
+  int B;
+  const float* A;
+  const float* V;
+  float* Y;
+  float* scale;     // [N, B]
+  const int32_t* flags;
+  float* eigvals;   // optional [N,B]
+  int32_t* sweeps;  // optional [N]
+  int32_t* status;  // optional [N]
+};
+hipError_t launch_evd_finish(const EvdFinish& f, hipStream_t stream);
+hipError_t launch_identity(float* V, int64_t N, int B, hipStream_t stream);
+size_t evd_workspace_bytes(int64_t N, int B);
+
 // Stack / unstack n weights: the ceil(rows/B) x ceil(cols/B) tiles of each, in order, into
 // consecutive blocks of `stack` (to_stack) or back out of it; the part of an edge tile outside the
 // weight is zero in the stack and not written back.  One launch per COPY_GROUP weights.

@@ -1,0 +1,437 @@
+// evd.hip -- inverse fourth root through an eigendecomposition A = Q diag(w) Q^T of every block of
+// the stack, by a two-sided block Jacobi method.
+//
+// The eigendecomposition is the root solver that DASH's iterations replace ([PT] Definição do
+// Problema, item 2, and Resultados Experimentais: EVD-based roots are the costly baseline; [TG]
+// body).  Here it is a batched GPU solver of its own:
+//
+// - The B columns are cut into K = B/32 blocks of 32.  A sweep runs K-1 rounds; in each round the
+//   blocks are paired by the circle (round-robin) schedule, so each pair of blocks meets once per
+//   sweep and the K/2 pairs of a round are disjoint.
+// - Pair kernel, one workgroup per (matrix, pair): the 64 x 64 sub-problem S = A[I u J, I u J]
+//   sits in LDS (in fp64) and is diagonalised by scalar cyclic Jacobi (the same circle schedule on its 64
+//   indices: 32 disjoint rotations per inner round, each a classical rotation that zeroes one
+//   off-diagonal pair), until an inner sweep finds every |S_pq| <= tol sqrt(S_pp S_qq).  The
+//   accumulated 64 x 64 rotation R_p goes to the workspace; the diagonalised S goes back to A.
+// - Update kernel, one workgroup per 64 x 64 output: the off-pair blocks become
+//   A_pq <- R_p^T A_pq R_q (mirrored into A_qp), and the eigenvector estimate V <- V R, as
+//   32x32x2 fp32 MFMA products from LDS.
+// - A matrix whose whole sweep needed no rotation is done: later launches return at once for it.
+//   An update whose pair rotations are all the identity is skipped.
+// - Refinement pass (optional, driven from api.hip): V is re-orthogonalised by one Newton-Schulz
+//   step, H = V^T A V is formed from the input A again, and the same sweeps run on H, rotating V.
+//   This discards the rounding that the first pass accumulated in the working matrix over its many
+//   dense rounds, which dominates the error at high condition numbers.
+// - Finally w = diag(A), Y = V diag(w^{-1/8}) and X = Y Y^T (a triangle-only NT product: X comes
+//   out exactly symmetric).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "dash_internal.hpp"
+
+namespace dash {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int JB = 32;         // column block width
+constexpr int JS = 2 * JB;     // sub-problem order: one pair of column blocks
+constexpr int JP = JS + 1;     // LDS row pitch in floats (column walks hit distinct banks)
+constexpr int MAX_INNER = 10;  // scalar Jacobi sweeps per sub-problem
+constexpr int NTH = 256;
+
+// per-matrix flags: done, sweeps of this pass, rotated in sweep (parity), sweeps of earlier passes
+enum { F_DONE = 0, F_SWEEPS = 1, F_ROT = 2, F_PREV = 4, F_STRIDE = 8 };  // F_ROT + (sweep & 1)
+
+// Circle schedule of n players (n even): in round r seat 0 holds player 0 and seat x > 0 holds
+// player 1 + (x - 1 + r) mod (n - 1); seat x plays seat n - 1 - x.  Rounds 0 .. n-2 pair every two
+// players exactly once.
+__device__ __forceinline__ int seat(int x, int r, int n) { return x == 0 ? 0 : 1 + (x - 1 + r) % (n - 1); }
+
+// the two column blocks I < J of pair p in round r (K blocks)
+__device__ __forceinline__ void pair_blocks(int p, int r, int K, int& I, int& J) {
+  const int u = seat(p, r, K), v = seat(K - 1 - p, r, K);
+  I = u < v ? u : v;
+  J = u < v ? v : u;
+}
+
+// global index of entry x (0..63) of a pair's index set
+__device__ __forceinline__ int pidx(int x, int I, int J) { return x < JB ? I * JB + x : J * JB + x - JB; }
+
+struct JacobiArgs {
+  float* A;      // [N, B, B] working copy, diagonalised in place
+  float* V;      // [N, B, B] accumulated rotations
+  float* R;      // [N, P, JS, JS] rotations of the current round
+  int32_t* rot;  // [N, P] pair p of the current round rotated something
+  int32_t* flags;
+  int64_t b0;    // first matrix of this launch
+  int B, K, P, round, sweep;
+  float tol;
+};
+
+// The sub-problem and its accumulated rotation live in LDS in fp64 (fp64 FMA runs at the fp32
+// rate here) and are rounded to fp32 once, when written out: a rotation accumulated in fp32 over the
+// hundreds of plane rotations of one diagonalisation drifts from orthogonality by ~sqrt(count) ulp,
+// and applying such a near-rotation to the off-pair blocks every round moves the eigenvalues.
+__global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
+  __shared__ double S[JS * JP];
+  __shared__ double Q[JS * JP];
+  __shared__ double rot_c[JS / 2], rot_s[JS / 2];
+  __shared__ int rot_p[JS / 2], rot_q[JS / 2];
+  __shared__ int rotated[MAX_INNER];
+  const int64_t b = a.b0 + blockIdx.x / a.P;
+  const int p = (int)(blockIdx.x % a.P);
+  if (a.flags[b * F_STRIDE + F_DONE]) return;
+  int I, J;
+  pair_blocks(p, a.round, a.K, I, J);
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  float* Ab = a.A + b * (int64_t)B * B;
+  for (int e = tid; e < JS * JS / 4; e += NTH) {  // 16-byte pieces never straddle the two halves
+    const int i = e >> 4, c4 = e & 15;
+    const f32x4 v = *(const f32x4*)(Ab + (int64_t)pidx(i, I, J) * B + pidx(4 * c4, I, J));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) S[i * JP + 4 * c4 + q] = v[q];
+  }
+  for (int e = tid; e < JS * JS; e += NTH) {
+    const int i = e >> 6, j = e & 63;
+    Q[i * JP + j] = i == j ? 1.0 : 0.0;
+  }
+  if (tid < MAX_INNER) rotated[tid] = 0;
+  __syncthreads();
+  const double tol = a.tol;
+  for (int sw = 0; sw < MAX_INNER; ++sw) {
+    for (int r = 0; r < JS - 1; ++r) {
+      if (tid < JS / 2) {
+        const int u = seat(tid, r, JS), v = seat(JS - 1 - tid, r, JS);
+        const int pp = u < v ? u : v, qq = u < v ? v : u;
+        const double app = S[pp * JP + pp], aqq = S[qq * JP + qq], apq = S[pp * JP + qq];
+        double c = 1.0, s = 0.0;
+        if (fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+          // the rotation that zeroes entry (pp, qq): t = tan of its angle, the smaller root of
+          // t^2 + 2 theta t - 1 = 0
+          const double th = (aqq - app) / (2.0 * apq);
+          const double t = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(th * th + 1.0));
+          c = 1.0 / sqrt(t * t + 1.0);
+          s = t * c;
+          rotated[sw] = 1;
+        }
+        rot_c[tid] = c;
+        rot_s[tid] = s;
+        rot_p[tid] = pp;
+        rot_q[tid] = qq;
+      }
+      __syncthreads();
+      // S <- J^T S J: one 2 x 2 block (rows of rotation k, columns of rotation l) per item
+      for (int e = tid; e < (JS / 2) * (JS / 2); e += NTH) {
+        const int k = e >> 5, l = e & 31;
+        const int pk = rot_p[k], qk = rot_q[k], pl = rot_p[l], ql = rot_q[l];
+        const double ck = rot_c[k], sk = rot_s[k], cl = rot_c[l], sl = rot_s[l];
+        const double x00 = S[pk * JP + pl], x01 = S[pk * JP + ql];
+        const double x10 = S[qk * JP + pl], x11 = S[qk * JP + ql];
+        const double y00 = cl * x00 - sl * x01, y01 = sl * x00 + cl * x01;  // columns
+        const double y10 = cl * x10 - sl * x11, y11 = sl * x10 + cl * x11;
+        double z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;        // rows
+        double z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
+        if (k == l) z01 = z10 = 0.0;  // the entry the rotation annihilates
+        S[pk * JP + pl] = z00;
+        S[pk * JP + ql] = z01;
+        S[qk * JP + pl] = z10;
+        S[qk * JP + ql] = z11;
+      }
+      // Q <- Q J
+      for (int e = tid; e < JS * (JS / 2); e += NTH) {
+        const int k = e >> 6, i = e & 63;
+        const int pk = rot_p[k], qk = rot_q[k];
+        const double ck = rot_c[k], sk = rot_s[k];
+        const double x0 = Q[i * JP + pk], x1 = Q[i * JP + qk];
+        Q[i * JP + pk] = ck * x0 - sk * x1;
+        Q[i * JP + qk] = sk * x0 + ck * x1;
+      }
+      __syncthreads();
+    }
+    if (!rotated[sw]) break;
+  }
+  if (rotated[0]) {
+    for (int e = tid; e < JS * JS / 4; e += NTH) {
+      const int i = e >> 4, c4 = e & 15;
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (float)S[i * JP + 4 * c4 + q];
+      *(f32x4*)(Ab + (int64_t)pidx(i, I, J) * B + pidx(4 * c4, I, J)) = v;
+    }
+  }
+  float* Rb = a.R + (b * a.P + p) * (int64_t)(JS * JS);
+  for (int e = tid; e < JS * JS / 4; e += NTH) {
+    const int i = e >> 4, c4 = e & 15;
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (float)Q[i * JP + 4 * c4 + q];
+    *(f32x4*)(Rb + i * JS + 4 * c4) = v;
+  }
+  if (tid == 0) {
+    a.rot[b * a.P + p] = rotated[0];
+    if (rotated[0]) atomicOr(&a.flags[b * F_STRIDE + F_ROT + (a.sweep & 1)], 1);
+  }
+}
+
+// out = X Y (both 64 x 64 in LDS, pitch JP; TX: X read transposed) -> the wave's 32 x 32 quadrant
+template <bool TX>
+__device__ __forceinline__ f32x16 mm64(const float* X, const float* Y, int wm, int wn, int li, int h) {
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // lane half h takes k = 32 h + s at step s: the sum over k is the same, each read is one float
+#pragma unroll 8
+  for (int s = 0; s < JB; ++s) {
+    const int k = JB * h + s;
+    const float xa = TX ? X[k * JP + wm * JB + li] : X[(wm * JB + li) * JP + k];
+    const float yb = Y[k * JP + wn * JB + li];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, yb, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// the quadrant back into LDS (element r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32)
+__device__ __forceinline__ void store_quadrant(float* T, const f32x16& acc, int wm, int wn, int li, int h) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) T[(wm * JB + 8 * (r >> 2) + 4 * h + (r & 3)) * JP + wn * JB + li] = acc[r];
+}
+
+__device__ __forceinline__ void load_rot(float* T, const float* Rg, int tid) {
+  for (int e = tid; e < JS * JS / 4; e += NTH) {
+    const int i = e >> 4, c4 = e & 15;
+    const f32x4 v = *(const f32x4*)(Rg + i * JS + 4 * c4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[q];
+  }
+}
+
+// Items of one matrix: P(P-1)/2 off-pair blocks A_pq (p < q), then P * B/64 tiles of V (64 rows
+// by one pair's 64 columns).
+__global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
+  __shared__ float X[JS * JP];
+  __shared__ float R1[JS * JP];
+  __shared__ float R2[JS * JP];
+  const int P = a.P, B = a.B;
+  const int PA = P * (P - 1) / 2;
+  const int per = PA + P * (B / JS);
+  const int64_t b = a.b0 + blockIdx.x / per;
+  int t = (int)(blockIdx.x % per);
+  if (a.flags[b * F_STRIDE + F_DONE]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const float* Rm = a.R + b * P * (int64_t)(JS * JS);
+  if (t < PA) {
+    int p = 0;
+    while (t >= P - 1 - p) {
+      t -= P - 1 - p;
+      ++p;
+    }
+    const int q = p + 1 + t;
+    if (!a.rot[b * P + p] && !a.rot[b * P + q]) return;  // R_p = R_q = I: nothing changes
+    int Ip, Jp, Iq, Jq;
+    pair_blocks(p, a.round, a.K, Ip, Jp);
+    pair_blocks(q, a.round, a.K, Iq, Jq);
+    float* Ab = a.A + b * (int64_t)B * B;
+    for (int e = tid; e < JS * JS / 4; e += NTH) {
+      const int i = e >> 4, c4 = e & 15;
+      const f32x4 v = *(const f32x4*)(Ab + (int64_t)pidx(i, Ip, Jp) * B + pidx(4 * c4, Iq, Jq));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[i * JP + 4 * c4 + r] = v[r];
+    }
+    load_rot(R1, Rm + q * JS * JS, tid);
+    load_rot(R2, Rm + p * JS * JS, tid);
+    __syncthreads();
+    f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // T = A_pq R_q
+    __syncthreads();
+    store_quadrant(X, acc, wm, wn, li, h);
+    __syncthreads();
+    acc = mm64<true>(R2, X, wm, wn, li, h);  // R_p^T T
+    __syncthreads();
+    store_quadrant(X, acc, wm, wn, li, h);
+    __syncthreads();
+    for (int e = tid; e < JS * JS / 4; e += NTH) {
+      const int i = e >> 4, c4 = e & 15;
+      f32x4 v, w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = X[i * JP + 4 * c4 + r];
+        w[r] = X[(4 * c4 + r) * JP + i];
+      }
+      *(f32x4*)(Ab + (int64_t)pidx(i, Ip, Jp) * B + pidx(4 * c4, Iq, Jq)) = v;
+      *(f32x4*)(Ab + (int64_t)pidx(i, Iq, Jq) * B + pidx(4 * c4, Ip, Jp)) = w;
+    }
+  } else {
+    t -= PA;
+    const int rb = t / P, q = t - rb * P;
+    if (!a.rot[b * P + q]) return;
+    int Iq, Jq;
+    pair_blocks(q, a.round, a.K, Iq, Jq);
+    float* Vb = a.V + b * (int64_t)B * B + (int64_t)rb * JS * B;
+    for (int e = tid; e < JS * JS / 4; e += NTH) {
+      const int i = e >> 4, c4 = e & 15;
+      const f32x4 v = *(const f32x4*)(Vb + (int64_t)i * B + pidx(4 * c4, Iq, Jq));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[i * JP + 4 * c4 + r] = v[r];
+    }
+    load_rot(R1, Rm + q * JS * JS, tid);
+    __syncthreads();
+    const f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // V_tile R_q
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = wm * JB + 8 * (r >> 2) + 4 * h + (r & 3);
+      Vb[(int64_t)i * B + pidx(wn * JB + li, Iq, Jq)] = acc[r];
+    }
+  }
+}
+
+// Sweep bookkeeping, one thread per matrix.  sweep == 0: start of a pass (the first pass clears
+// the count of earlier sweeps, a later one adds the previous pass's sweeps to it).  sweep t >= 1
+// (sweep t-1 has completed): a matrix whose sweep t-1 rotated nothing is done; F_SWEEPS counts the
+// sweeps run in this pass.
+__global__ void jacobi_sweep_kernel(int32_t* flags, int64_t N, int sweep, int pass) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= N) return;
+  int32_t* f = flags + b * F_STRIDE;
+  if (sweep == 0) {
+    f[F_PREV] = pass == 0 ? 0 : f[F_PREV] + f[F_SWEEPS];
+    f[F_DONE] = 0;
+    f[F_SWEEPS] = 0;
+    f[F_ROT] = 0;
+    f[F_ROT + 1] = 0;
+    return;
+  }
+  if (!f[F_DONE]) {
+    f[F_SWEEPS] = sweep;
+    if (!f[F_ROT + ((sweep - 1) & 1)]) f[F_DONE] = 1;
+  }
+  f[F_ROT + (sweep & 1)] = 0;
+}
+
+// V <- I for every matrix
+__global__ void identity_kernel(float* V, int64_t N, int B) {
+  const int64_t n4 = N * (int64_t)B * B / 4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t idx = 4 * e;
+    const int64_t in = idx % ((int64_t)B * B);
+    const int i = (int)(in / B), j0 = (int)(in % B);
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (i == j0 + q) ? 1.f : 0.f;
+    *(f32x4*)(V + idx) = v;
+  }
+}
+
+// Per matrix: eigenvalues w_j = A_jj, column scales w_j^{-1/8} (NaN for a w_j that is not finite or
+// not > 0, status bit 0), eigenvalue and sweep outputs, status bit 2 when not converged.
+__global__ __launch_bounds__(256) void evd_finish_kernel(const float* A, int64_t b0, int B, const int32_t* flags,
+                                                         float* scale, float* eigvals, int32_t* sweeps,
+                                                         int32_t* status) {
+  const int64_t b = b0 + blockIdx.x;
+  const float* Ab = A + b * (int64_t)B * B;
+  int bad = 0;
+  for (int j = threadIdx.x; j < B; j += blockDim.x) {
+    const float w = Ab[(int64_t)j * B + j];
+    const bool ok = w > 0.f && isfinite(w);
+    bad |= !ok;
+    // w^{-1/8} as three square roots (each exactly equivariant under w -> 4^k w)
+    scale[b * B + j] = ok ? (float)(1.0 / sqrt(sqrt(sqrt((double)w)))) : __builtin_nanf("");
+    if (eigvals) eigvals[b * B + j] = w;
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) {
+    const int32_t* f = flags + b * F_STRIDE;
+    if (sweeps) sweeps[b] = f[F_PREV] + f[F_SWEEPS];
+    if (status) status[b] |= (bad ? 1 : 0) | (f[F_DONE] ? 0 : 4);
+  }
+}
+
+// Y[b][i][j] = V[b][i][j] * scale[b][j]  (Y may be V)
+__global__ void column_scale_kernel(const float* V, const float* scale, float* Y, int64_t N, int B) {
+  const int64_t n4 = N * (int64_t)B * B / 4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n4; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t idx = 4 * e;
+    const int64_t b = idx / ((int64_t)B * B);
+    const int j0 = (int)(idx % B);
+    const f32x4 v = *(const f32x4*)(V + idx);
+    const f32x4 s = *(const f32x4*)(scale + b * B + j0);
+    *(f32x4*)(Y + idx) = v * s;
+  }
+}
+
+unsigned stream_grid(int64_t n4) {
+  const int64_t g = (n4 + 255) / 256;
+  return (unsigned)(g < 16384 ? g : 16384);
+}
+
+}  // namespace
+
+size_t evd_workspace_bytes(int64_t N, int B) {
+  size_t bytes = 2 * align_up((size_t)N * B * B * sizeof(float), 256);       // V, T
+  bytes += align_up((size_t)N * (B / JS) * JS * JS * sizeof(float), 256);    // R
+  bytes += align_up((size_t)N * (B / JS) * sizeof(int32_t), 256);            // pair flags
+  bytes += align_up((size_t)N * B * sizeof(float), 256);                     // column scales
+  bytes += align_up((size_t)N * F_STRIDE * sizeof(int32_t), 256);            // flags
+  return bytes;
+}
+
+hipError_t launch_identity(float* V, int64_t N, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(identity_kernel, dim3(stream_grid(N * (int64_t)B * B / 4)), dim3(256), 0, stream, V, N, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
+  const int B = p.B;
+  const int K = B / JB, P = B / JS;
+  const int64_t N = p.N;
+  hipError_t err;
+  const unsigned fgrid = (unsigned)((N + 255) / 256);
+  JacobiArgs a;
+  a.A = p.A;
+  a.V = p.V;
+  a.R = p.R;
+  a.rot = p.rot;
+  a.flags = p.flags;
+  a.B = B;
+  a.K = K;
+  a.P = P;
+  a.tol = p.tol;
+  // matrices per launch, so that a grid stays below 2^32 work-items
+  const int64_t max_wg = 0xffffffffLL / NTH;
+  const int64_t per_update = (int64_t)P * (P - 1) / 2 + (int64_t)P * (B / JS);
+  const int64_t chunk = max_wg / per_update;
+  for (int t = 0; t <= p.max_sweeps; ++t) {
+    hipLaunchKernelGGL(jacobi_sweep_kernel, dim3(fgrid), dim3(256), 0, stream, p.flags, N, t, p.pass);
+    if (t == p.max_sweeps) break;
+    a.sweep = t;
+    for (int r = 0; r < K - 1; ++r) {
+      a.round = r;
+      for (int64_t b0 = 0; b0 < N; b0 += chunk) {
+        const int64_t nb = N - b0 < chunk ? N - b0 : chunk;
+        a.b0 = b0;
+        hipLaunchKernelGGL(jacobi_pair_kernel, dim3((unsigned)(nb * P)), dim3(NTH), 0, stream, a);
+        hipLaunchKernelGGL(jacobi_update_kernel, dim3((unsigned)(nb * per_update)), dim3(NTH), 0, stream, a);
+      }
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // the sweep kernel of t == max_sweeps closed the pass (done flag, sweep count)
+  return hipGetLastError();
+}
+
+hipError_t launch_evd_finish(const EvdFinish& f, hipStream_t stream) {
+  const int64_t max_wg = 0xffffffffLL / 256;
+  for (int64_t b0 = 0; b0 < f.N; b0 += max_wg) {
+    const int64_t nb = f.N - b0 < max_wg ? f.N - b0 : max_wg;
+    hipLaunchKernelGGL(evd_finish_kernel, dim3((unsigned)nb), dim3(256), 0, stream, f.A, b0, f.B, f.flags, f.scale,
+                       f.eigvals, f.sweeps, f.status);
+  }
+  hipLaunchKernelGGL(column_scale_kernel, dim3(stream_grid(f.N * (int64_t)f.B * f.B / 4)), dim3(256), 0, stream, f.V,
+                     f.scale, f.Y, f.N, f.B);
+  return hipGetLastError();
+}
+
+}  // namespace dash

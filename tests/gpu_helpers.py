@@ -82,3 +82,15 @@ def cheb(A, s, degree, lo, hi):
     ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=DEV)
     dash.dash_inverse_root_cheb(A, s, N, B, degree, lo, hi, X, status=status, ws=ws)
     return X, status
+
+
+def evd(A, max_sweeps=20, refine=0):
+    """(X, eigenvalues, sweeps, status) of the block-Jacobi eigendecomposition solver."""
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    w = torch.empty((N, B), device=DEV)
+    sweeps = torch.empty(N, dtype=torch.int32, device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=DEV)
+    dash.dash_inverse_root_evd(A, N, B, max_sweeps, refine, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
+    return X, w, sweeps, status

@@ -159,3 +159,26 @@ def test_stack_argument_errors():
     assert _status_of(dash.dash_stack, [FakeMat(P + 8, 128, 128)], B, P2) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_stack, [FakeMat(P, 128, 128)], B, None) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_unstack, P2, B, [FakeMat(P, 64, 130, ld=130)]) == _lib.DASH_ERR_INVALID_ARG
+
+
+def test_evd_argument_errors_and_counts():
+    N, B = 4, 64
+    ws = FakeWs(P3, dash.dash_workspace_size(dash.DASH_OP_EVD, N, B))
+    assert ws.n >= 2 * N * B * B * 4
+    f = dash.dash_inverse_root_evd
+    assert _status_of(f, None, N, B, 10, 0, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG     # null A
+    assert _status_of(f, P, N, B, 10, 0, P, ws=ws) == _lib.DASH_ERR_INVALID_ARG         # X aliases A
+    assert _status_of(f, P, N, B, 0, 0, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG         # max_sweeps < 1
+    assert _status_of(f, P, N, B, 101, 0, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, N, B, 10, 2, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG        # refine not 0/1
+    assert _status_of(f, P, N, 96, 10, 0, P2, ws=ws) == _lib.DASH_ERR_SHAPE
+    assert _status_of(f, P, N, B, 10, 0, P2 + 4, ws=ws) == _lib.DASH_ERR_INVALID_ARG    # misaligned X
+    assert _status_of(f, P, N, B, 10, 0, P2, ws=FakeWs(P3, ws.n - 1)) == _lib.DASH_ERR_WORKSPACE
+    # flops: one full sweep of updates per round (P(P-1)/2 blocks x 2 products + P * B/64 tiles) + Y Y^T
+    Bf, Nf = 256, 3
+    Pp = Bf // 64
+    per_round = (Pp * (Pp - 1) // 2 * 2 + Pp * (Bf // 64)) * 2 * 64 ** 3
+    tri = (Bf // 128) * (Bf // 128 + 1) / 2 / (Bf // 128) ** 2
+    expect = 7 * (Bf // 32 - 1) * per_round * Nf + 2 * Bf ** 3 * Nf * tri
+    assert dash.dash_flops(dash.DASH_OP_EVD, Nf, Bf, dash.DASH_FP32, 7, 0) == pytest.approx(expect)
+    assert dash.dash_flops(dash.DASH_OP_EVD, Nf, Bf, dash.DASH_FP32, 0, 0) == -1.0
