@@ -34,6 +34,7 @@ K_VEC, MPI_STEPS = 32, 10
 CHEB_DEGREE, CHEB_HI = 24, 1.25
 NDB_ITERS = 6      # per call: 30 products per block
 CN_ITERS = 5       # 16 products per block
+EVD_MAX_SWEEPS = 20
 FP32_PEAK_TFLOPS = 157.3
 FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
@@ -48,10 +49,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb"], default="step",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd"], default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
-                        "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles)")
+                        "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
+                        "block-Jacobi eigendecomposition solve")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
@@ -112,6 +114,8 @@ def main():
         return only_cheb(dash, di, torch, dev)
     if args.only in ("cn16", "ndb"):
         return only_solver(dash, di, torch, dev, args.only)
+    if args.only == "evd":
+        return only_evd(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -305,6 +309,46 @@ def only_solver(dash, di, torch, dev, which):
     torch.cuda.synchronize()
     print(json.dumps({"mode": which, "N": N, "B": B, "scale_ms": round(e[0].elapsed_time(e[1]), 3),
                       "solve_ms": round(e[1].elapsed_time(e[2]), 3)}), flush=True)
+
+
+def evd_solve(dash, torch, A, N, B, dev, refine=0):
+    """One eigendecomposition solve; (ms, X, sweeps, status)."""
+    X = torch.empty_like(A)
+    sweeps = torch.empty(N, dtype=torch.int32, device=dev)
+    status = torch.empty(N, dtype=torch.int32, device=dev)
+    ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dash.dash_inverse_root_evd(A, N, B, EVD_MAX_SWEEPS, refine, X, sweeps=sweeps, status=status, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    del ws
+    return e0.elapsed_time(e1), X, sweeps, status
+
+
+def evd_residual(torch, A, X, b):
+    """||X^4 A - I||_F / sqrt(B) of block b, in fp64 on the device (checking only)."""
+    x = X[b].double()
+    x2 = x @ x
+    r = x2 @ x2 @ A[b].double()
+    r.diagonal().sub_(1.0)
+    return float(torch.linalg.matrix_norm(r) / A.shape[1] ** 0.5)
+
+
+def only_evd(dash, di, torch, dev):
+    """The block-Jacobi eigendecomposition solve on the N=3072, B=1024 stack (kappa ~5)."""
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    evd_solve(dash, torch, A[:8].contiguous(), 8, B, dev)  # warm the kernels
+    ms, X, sweeps, status = evd_solve(dash, torch, A, N, B, dev)
+    sw = sweeps.cpu().numpy()
+    print(json.dumps({"mode": "evd", "N": N, "B": B, "ms": round(ms, 2), "blocks_per_s": round(N / (ms * 1e-3), 1),
+                      "sweeps": [int(sw.min()), float(sw.mean()), int(sw.max())],
+                      "status_nonzero": int((status != 0).sum()),
+                      "residual_blocks_0_last": [evd_residual(torch, A, X, 0), evd_residual(torch, A, X, N - 1)]}),
+          flush=True)
 
 
 def traffic_from_counters(fetch_csv, write_csv):

@@ -145,8 +145,8 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
 /* Inverse fourth root through an eigendecomposition A_i = Q diag(w) Q^T, X_i = Q diag(w^{-1/4}) Q^T
  * ([PT] Definição do Problema, item 2, and Resultados Experimentais: the eigendecomposition is the
  * root solver whose cost the iterations above avoid; [TG] body).  Batched two-sided block Jacobi in
- * fp32: the columns are cut into blocks of 32; each round pairs the blocks (circle schedule),
- * diagonalises every 64 x 64 pair sub-problem by scalar Jacobi and applies its rotation to A and to
+ * fp32: the columns are cut into blocks of 32; each round pairs the blocks (circle schedule), runs
+ * one sweep of scalar Jacobi on every 64 x 64 pair sub-problem and applies its rotation to A and to
  * the eigenvector estimate; a sweep is B/32 - 1 rounds.  Rotations are skipped where
  * |A_pq| <= 2^-22 sqrt(A_pp A_qq); a matrix is done after a sweep that rotates nothing, and later
  * sweeps skip it.  No scale s is needed (the method is scale-free).

@@ -9,10 +9,10 @@
 //   blocks are paired by the circle (round-robin) schedule, so each pair of blocks meets once per
 //   sweep and the K/2 pairs of a round are disjoint.
 // - Pair kernel, one workgroup per (matrix, pair): the 64 x 64 sub-problem S = A[I u J, I u J]
-//   sits in LDS (in fp64) and is diagonalised by scalar cyclic Jacobi (the same circle schedule on its 64
-//   indices: 32 disjoint rotations per inner round, each a classical rotation that zeroes one
-//   off-diagonal pair), until an inner sweep finds every |S_pq| <= tol sqrt(S_pp S_qq).  The
-//   accumulated 64 x 64 rotation R_p goes to the workspace; the diagonalised S goes back to A.
+//   sits in LDS (in fp64) and gets one sweep of scalar cyclic Jacobi (the same circle schedule on
+//   its 64 indices: 63 inner rounds of 32 disjoint rotations, each a classical rotation that zeroes
+//   one off-diagonal pair; pairs with |S_pq| <= tol sqrt(S_pp S_qq) are left alone).  The
+//   accumulated 64 x 64 rotation R_p goes to the workspace; the rotated S goes back to A.
 // - Update kernel, one workgroup per 64 x 64 output: the off-pair blocks become
 //   A_pq <- R_p^T A_pq R_q (mirrored into A_qp), and the eigenvector estimate V <- V R, as
 //   32x32x2 fp32 MFMA products from LDS.
@@ -39,8 +39,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int JB = 32;         // column block width
 constexpr int JS = 2 * JB;     // sub-problem order: one pair of column blocks
 constexpr int JP = JS + 1;     // LDS row pitch in floats (column walks hit distinct banks)
-constexpr int MAX_INNER = 10;  // scalar Jacobi sweeps per sub-problem
+// Scalar Jacobi sweeps per visit of a sub-problem.  One sweep per visit (an inexact inner solve)
+// costs about one more outer sweep than diagonalising every sub-problem fully and a quarter of the
+// inner work.
+constexpr int MAX_INNER = 1;
 constexpr int NTH = 256;
+constexpr int TV = JS * JS / 4 / NTH;            // 16-byte pieces per thread of a 64 x 64 fp32 tile
+constexpr int SU = (JS / 2) * (JS / 2) / NTH;    // 2 x 2 blocks of S per thread per inner round
+constexpr int QU = JS * (JS / 2) / NTH;          // (row, rotation) items of Q per thread
+static_assert(TV * NTH * 4 == JS * JS && SU * NTH == (JS / 2) * (JS / 2) && QU * NTH == JS * (JS / 2),
+              "the per-thread item counts must cover the tiles exactly");
 
 // per-matrix flags: done, sweeps of this pass, rotated in sweep (parity), sweeps of earlier passes
 enum { F_DONE = 0, F_SWEEPS = 1, F_ROT = 2, F_PREV = 4, F_STRIDE = 8 };  // F_ROT + (sweep & 1)
@@ -73,13 +81,13 @@ struct JacobiArgs {
 
 // The sub-problem and its accumulated rotation live in LDS in fp64 (fp64 FMA runs at the fp32
 // rate here) and are rounded to fp32 once, when written out: a rotation accumulated in fp32 over the
-// hundreds of plane rotations of one diagonalisation drifts from orthogonality by ~sqrt(count) ulp,
+// thousands of plane rotations of one visit drifts from orthogonality by ~sqrt(count) ulp,
 // and applying such a near-rotation to the off-pair blocks every round moves the eigenvalues.
 __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
   __shared__ double S[JS * JP];
   __shared__ double Q[JS * JP];
-  __shared__ double rot_c[JS / 2], rot_s[JS / 2];
-  __shared__ int rot_p[JS / 2], rot_q[JS / 2];
+  __shared__ double2 rot_cs[JS / 2];  // (c, s) of rotation k
+  __shared__ int2 rot_pq[JS / 2];     // its index pair p < q
   __shared__ int rotated[MAX_INNER];
   const int64_t b = a.b0 + blockIdx.x / a.P;
   const int p = (int)(blockIdx.x % a.P);
@@ -89,14 +97,23 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
   const int tid = threadIdx.x;
   const int B = a.B;
   float* Ab = a.A + b * (int64_t)B * B;
-  for (int e = tid; e < JS * JS / 4; e += NTH) {  // 16-byte pieces never straddle the two halves
-    const int i = e >> 4, c4 = e & 15;
-    const f32x4 v = *(const f32x4*)(Ab + (int64_t)pidx(i, I, J) * B + pidx(4 * c4, I, J));
+  {
+    f32x4 v[TV];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) S[i * JP + 4 * c4 + q] = v[q];
+    for (int u = 0; u < TV; ++u) {  // 16-byte pieces never straddle the two halves
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+      v[u] = *(const f32x4*)(Ab + (int64_t)pidx(i, I, J) * B + pidx(4 * c4, I, J));
+    }
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[i * JP + 4 * c4 + q] = v[u][q];
+    }
   }
-  for (int e = tid; e < JS * JS; e += NTH) {
-    const int i = e >> 6, j = e & 63;
+#pragma unroll
+  for (int u = 0; u < JS * JS / NTH; ++u) {
+    const int e = tid + NTH * u, i = e >> 6, j = e & 63;
     Q[i * JP + j] = i == j ? 1.0 : 0.0;
   }
   if (tid < MAX_INNER) rotated[tid] = 0;
@@ -118,45 +135,76 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
           s = t * c;
           rotated[sw] = 1;
         }
-        rot_c[tid] = c;
-        rot_s[tid] = s;
-        rot_p[tid] = pp;
-        rot_q[tid] = qq;
+        rot_cs[tid] = make_double2(c, s);
+        rot_pq[tid] = make_int2(pp, qq);
       }
       __syncthreads();
-      // S <- J^T S J: one 2 x 2 block (rows of rotation k, columns of rotation l) per item
-      for (int e = tid; e < (JS / 2) * (JS / 2); e += NTH) {
-        const int k = e >> 5, l = e & 31;
-        const int pk = rot_p[k], qk = rot_q[k], pl = rot_p[l], ql = rot_q[l];
-        const double ck = rot_c[k], sk = rot_s[k], cl = rot_c[l], sl = rot_s[l];
-        const double x00 = S[pk * JP + pl], x01 = S[pk * JP + ql];
-        const double x10 = S[qk * JP + pl], x11 = S[qk * JP + ql];
-        const double y00 = cl * x00 - sl * x01, y01 = sl * x00 + cl * x01;  // columns
-        const double y10 = cl * x10 - sl * x11, y11 = sl * x10 + cl * x11;
-        double z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;        // rows
-        double z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
-        if (k == l) z01 = z10 = 0.0;  // the entry the rotation annihilates
-        S[pk * JP + pl] = z00;
-        S[pk * JP + ql] = z01;
-        S[qk * JP + pl] = z10;
-        S[qk * JP + ql] = z11;
+      // S <- J^T S J: one 2 x 2 block (rows of rotation k, columns of rotation l) per item; this
+      // thread's items are l = tid % 32, k = tid / 32 + 8 u.  All loads are issued before the
+      // arithmetic so that their latencies overlap.
+      {
+        const int l = tid & 31, kb = tid >> 5;
+        const int2 pql = rot_pq[l];
+        const double2 csl = rot_cs[l];
+        int2 pqk[SU];
+        double2 csk[SU];
+        double x[SU][4];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          pqk[u] = rot_pq[kb + 8 * u];
+          csk[u] = rot_cs[kb + 8 * u];
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          x[u][0] = S[pqk[u].x * JP + pql.x];
+          x[u][1] = S[pqk[u].x * JP + pql.y];
+          x[u][2] = S[pqk[u].y * JP + pql.x];
+          x[u][3] = S[pqk[u].y * JP + pql.y];
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+          const double cl = csl.x, sl = csl.y, ck = csk[u].x, sk = csk[u].y;
+          const double y00 = cl * x[u][0] - sl * x[u][1], y01 = sl * x[u][0] + cl * x[u][1];  // columns
+          const double y10 = cl * x[u][2] - sl * x[u][3], y11 = sl * x[u][2] + cl * x[u][3];
+          double z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;  // rows
+          double z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
+          if (kb + 8 * u == l) z01 = z10 = 0.0;  // the entry the rotation annihilates
+          S[pqk[u].x * JP + pql.x] = z00;
+          S[pqk[u].x * JP + pql.y] = z01;
+          S[pqk[u].y * JP + pql.x] = z10;
+          S[pqk[u].y * JP + pql.y] = z11;
+        }
       }
-      // Q <- Q J
-      for (int e = tid; e < JS * (JS / 2); e += NTH) {
-        const int k = e >> 6, i = e & 63;
-        const int pk = rot_p[k], qk = rot_q[k];
-        const double ck = rot_c[k], sk = rot_s[k];
-        const double x0 = Q[i * JP + pk], x1 = Q[i * JP + qk];
-        Q[i * JP + pk] = ck * x0 - sk * x1;
-        Q[i * JP + qk] = sk * x0 + ck * x1;
+      // Q <- Q J: items (k, i), row i = tid % 64, k = tid / 64 + 4 u
+      {
+        const int i = tid & 63, kb = tid >> 6;
+        int2 pqk[QU];
+        double2 csk[QU];
+        double x0[QU], x1[QU];
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          pqk[u] = rot_pq[kb + 4 * u];
+          csk[u] = rot_cs[kb + 4 * u];
+        }
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          x0[u] = Q[i * JP + pqk[u].x];
+          x1[u] = Q[i * JP + pqk[u].y];
+        }
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+          Q[i * JP + pqk[u].x] = csk[u].x * x0[u] - csk[u].y * x1[u];
+          Q[i * JP + pqk[u].y] = csk[u].y * x0[u] + csk[u].x * x1[u];
+        }
       }
       __syncthreads();
     }
     if (!rotated[sw]) break;
   }
   if (rotated[0]) {
-    for (int e = tid; e < JS * JS / 4; e += NTH) {
-      const int i = e >> 4, c4 = e & 15;
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
       f32x4 v;
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = (float)S[i * JP + 4 * c4 + q];
@@ -164,8 +212,9 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
     }
   }
   float* Rb = a.R + (b * a.P + p) * (int64_t)(JS * JS);
-  for (int e = tid; e < JS * JS / 4; e += NTH) {
-    const int i = e >> 4, c4 = e & 15;
+#pragma unroll
+  for (int u = 0; u < TV; ++u) {
+    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
     f32x4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = (float)Q[i * JP + 4 * c4 + q];
@@ -200,12 +249,24 @@ __device__ __forceinline__ void store_quadrant(float* T, const f32x16& acc, int 
   for (int r = 0; r < 16; ++r) T[(wm * JB + 8 * (r >> 2) + 4 * h + (r & 3)) * JP + wn * JB + li] = acc[r];
 }
 
-__device__ __forceinline__ void load_rot(float* T, const float* Rg, int tid) {
-  for (int e = tid; e < JS * JS / 4; e += NTH) {
-    const int i = e >> 4, c4 = e & 15;
-    const f32x4 v = *(const f32x4*)(Rg + i * JS + 4 * c4);
+// A 64 x 64 fp32 tile through registers: piece u of this thread is row e/16, columns 4(e%16) ..
+// 4(e%16)+3 of the tile, e = tid + NTH u.  Row i of the tile is at src + row_off(i), its column c
+// at + col(c) (a 16-byte piece never straddles the two 32-column halves of a pair's index set).
+template <typename RowOff, typename Col>
+__device__ __forceinline__ void fetch_tile(f32x4 (&v)[TV], const float* src, RowOff row_off, Col col, int tid) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[q];
+  for (int u = 0; u < TV; ++u) {
+    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+    v[u] = *(const f32x4*)(src + row_off(i) + col(4 * c4));
+  }
+}
+
+__device__ __forceinline__ void stage_tile(float* T, const f32x4 (&v)[TV], int tid) {
+#pragma unroll
+  for (int u = 0; u < TV; ++u) {
+    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[u][q];
   }
 }
 
@@ -236,14 +297,16 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
     pair_blocks(p, a.round, a.K, Ip, Jp);
     pair_blocks(q, a.round, a.K, Iq, Jq);
     float* Ab = a.A + b * (int64_t)B * B;
-    for (int e = tid; e < JS * JS / 4; e += NTH) {
-      const int i = e >> 4, c4 = e & 15;
-      const f32x4 v = *(const f32x4*)(Ab + (int64_t)pidx(i, Ip, Jp) * B + pidx(4 * c4, Iq, Jq));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) X[i * JP + 4 * c4 + r] = v[r];
-    }
-    load_rot(R1, Rm + q * JS * JS, tid);
-    load_rot(R2, Rm + p * JS * JS, tid);
+    auto rot_row = [](int i) { return (int64_t)i * JS; };
+    auto rot_col = [](int c) { return c; };
+    f32x4 va[TV], vq[TV], vp[TV];
+    fetch_tile(va, Ab, [&](int i) { return (int64_t)pidx(i, Ip, Jp) * B; }, [&](int c) { return pidx(c, Iq, Jq); },
+               tid);
+    fetch_tile(vq, Rm + q * JS * JS, rot_row, rot_col, tid);
+    fetch_tile(vp, Rm + p * JS * JS, rot_row, rot_col, tid);
+    stage_tile(X, va, tid);
+    stage_tile(R1, vq, tid);
+    stage_tile(R2, vp, tid);
     __syncthreads();
     f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // T = A_pq R_q
     __syncthreads();
@@ -253,8 +316,9 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
     __syncthreads();
     store_quadrant(X, acc, wm, wn, li, h);
     __syncthreads();
-    for (int e = tid; e < JS * JS / 4; e += NTH) {
-      const int i = e >> 4, c4 = e & 15;
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
       f32x4 v, w;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -271,13 +335,11 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
     int Iq, Jq;
     pair_blocks(q, a.round, a.K, Iq, Jq);
     float* Vb = a.V + b * (int64_t)B * B + (int64_t)rb * JS * B;
-    for (int e = tid; e < JS * JS / 4; e += NTH) {
-      const int i = e >> 4, c4 = e & 15;
-      const f32x4 v = *(const f32x4*)(Vb + (int64_t)i * B + pidx(4 * c4, Iq, Jq));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) X[i * JP + 4 * c4 + r] = v[r];
-    }
-    load_rot(R1, Rm + q * JS * JS, tid);
+    f32x4 vv[TV], vq[TV];
+    fetch_tile(vv, Vb, [&](int i) { return (int64_t)i * B; }, [&](int c) { return pidx(c, Iq, Jq); }, tid);
+    fetch_tile(vq, Rm + q * JS * JS, [](int i) { return (int64_t)i * JS; }, [](int c) { return c; }, tid);
+    stage_tile(X, vv, tid);
+    stage_tile(R1, vq, tid);
     __syncthreads();
     const f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // V_tile R_q
 #pragma unroll
