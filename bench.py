@@ -10,8 +10,8 @@ R statistics form an N=3072, B=1024 stack):
 Inputs are synthetic (seeded N(0, 1e-3^2) gradients, prior statistics G G^T/1024 + 1e-6 I) and are
 resident in HBM before timing starts.  The headline value is stacked blocks per second of the whole
 step.  The JSON line also carries the roofline of the dominant kernel (the fp32 MFMA product),
-the solve-only rates of the other two solver configurations (NDB fp32, CN fp16) and the CPU oracle
-timed on a bounded sample of the same workload.
+the solve-only rates of the other two solver configurations (NDB fp32, CN fp16), of the block-Jacobi
+eigendecomposition they replace, and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-solvers]
 """
@@ -379,7 +379,8 @@ def traffic_from_counters(fetch_csv, write_csv):
 
 
 def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
-    """Solve-only rates: NDB fp32 (6+6 steps, 30 products) and CN p=4 fp16 (5 steps, 16 products)."""
+    """Solve-only rates: NDB fp32 (6+6 steps, 30 products), CN p=4 fp16 (5 steps, 16 products) and the
+    block-Jacobi eigendecomposition (fp32, until a sweep rotates nothing)."""
     A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
     s = torch.empty(N, device=dev)
     res = {}
@@ -427,6 +428,15 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                       "frac_fp16_peak": round(fl / FP16_PEAK_TFLOPS, 4),
                       "scale_fp16_ms": round(scale16_ms, 2),
                       "scale_fp16_hbm_gbs": round(half_bytes / (scale16_ms * 1e-3) / 1e9, 1)}
+    # block-Jacobi eigendecomposition (the root solver the iterations replace), one solve
+    evd_ms, Xe, sweeps, status = evd_solve(dash, torch, A, N, B, dev)
+    sw = sweeps.float()
+    res["evd_fp32"] = {"ms": round(evd_ms, 1), "blocks_per_s": round(N / (evd_ms * 1e-3), 1),
+                       "sweeps_mean": round(float(sw.mean()), 2), "sweeps_max": int(sw.max()),
+                       "status_nonzero": int((status != 0).sum()),
+                       "residual_block0": evd_residual(torch, A, Xe, 0)}
+    del Xe
+    torch.cuda.empty_cache()
     log("solvers: %s" % json.dumps(res))
     del A
     torch.cuda.empty_cache()

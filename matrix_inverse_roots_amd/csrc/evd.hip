@@ -68,13 +68,26 @@ __device__ __forceinline__ void pair_blocks(int p, int r, int K, int& I, int& J)
 // global index of entry x (0..63) of a pair's index set
 __device__ __forceinline__ int pidx(int x, int I, int J) { return x < JB ? I * JB + x : J * JB + x - JB; }
 
+// Workgroup w of a launch over nb matrices with `per` workgroups each.  Workgroups are dealt to the
+// 8 XCDs round-robin (w % 8), so XCD x is given the matrices m = x (mod 8), each one's workgroups
+// in a row: a matrix's rotations and tiles are shared through one L2.  False for the padding
+// workgroups of the last group of 8 matrices.
+__device__ __forceinline__ bool xcd_item(int per, int64_t nb, int64_t& m, int& item) {
+  const int64_t w = blockIdx.x, x = w & 7, slot = w >> 3;
+  m = 8 * (slot / per) + x;
+  item = (int)(slot % per);
+  return m < nb;
+}
+
+inline int64_t xcd_grid(int64_t nb, int64_t per) { return (nb + 7) / 8 * 8 * per; }
+
 struct JacobiArgs {
   float* A;      // [N, B, B] working copy, diagonalised in place
   float* V;      // [N, B, B] accumulated rotations
   float* R;      // [N, P, JS, JS] rotations of the current round
   int32_t* rot;  // [N, P] pair p of the current round rotated something
   int32_t* flags;
-  int64_t b0;    // first matrix of this launch
+  int64_t b0, nb;  // first matrix of this launch, matrices in it
   int B, K, P, round, sweep;
   float tol;
 };
@@ -89,8 +102,11 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
   __shared__ double2 rot_cs[JS / 2];  // (c, s) of rotation k
   __shared__ int2 rot_pq[JS / 2];     // its index pair p < q
   __shared__ int rotated[MAX_INNER];
-  const int64_t b = a.b0 + blockIdx.x / a.P;
-  const int p = (int)(blockIdx.x % a.P);
+  __shared__ int round_rot[2];  // inner round r rotates something (parity of r)
+  int64_t m;
+  int p;
+  if (!xcd_item(a.P, a.nb, m, p)) return;
+  const int64_t b = a.b0 + m;
   if (a.flags[b * F_STRIDE + F_DONE]) return;
   int I, J;
   pair_blocks(p, a.round, a.K, I, J);
@@ -117,10 +133,12 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
     Q[i * JP + j] = i == j ? 1.0 : 0.0;
   }
   if (tid < MAX_INNER) rotated[tid] = 0;
+  if (tid < 2) round_rot[tid] = 0;
   __syncthreads();
   const double tol = a.tol;
   for (int sw = 0; sw < MAX_INNER; ++sw) {
     for (int r = 0; r < JS - 1; ++r) {
+      const int rr = sw * (JS - 1) + r;  // inner round count, for the flag parity
       if (tid < JS / 2) {
         const int u = seat(tid, r, JS), v = seat(JS - 1 - tid, r, JS);
         const int pp = u < v ? u : v, qq = u < v ? v : u;
@@ -134,15 +152,20 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
           c = 1.0 / sqrt(t * t + 1.0);
           s = t * c;
           rotated[sw] = 1;
+          round_rot[rr & 1] = 1;
         }
         rot_cs[tid] = make_double2(c, s);
         rot_pq[tid] = make_int2(pp, qq);
       }
       __syncthreads();
+      // a round whose 32 rotations are all the identity changes nothing; the flag of the next
+      // round was last read before the previous barrier
+      const bool any = round_rot[rr & 1];
+      if (tid == 0) round_rot[(rr + 1) & 1] = 0;
       // S <- J^T S J: one 2 x 2 block (rows of rotation k, columns of rotation l) per item; this
       // thread's items are l = tid % 32, k = tid / 32 + 8 u.  All loads are issued before the
       // arithmetic so that their latencies overlap.
-      {
+      if (any) {
         const int l = tid & 31, kb = tid >> 5;
         const int2 pql = rot_pq[l];
         const double2 csl = rot_cs[l];
@@ -168,7 +191,7 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
           const double y10 = cl * x[u][2] - sl * x[u][3], y11 = sl * x[u][2] + cl * x[u][3];
           double z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;  // rows
           double z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
-          if (kb + 8 * u == l) z01 = z10 = 0.0;  // the entry the rotation annihilates
+          if (kb + 8 * u == l && sl != 0.0) z01 = z10 = 0.0;  // the entry a rotation annihilates
           S[pqk[u].x * JP + pql.x] = z00;
           S[pqk[u].x * JP + pql.y] = z01;
           S[pqk[u].y * JP + pql.x] = z10;
@@ -176,7 +199,7 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
         }
       }
       // Q <- Q J: items (k, i), row i = tid % 64, k = tid / 64 + 4 u
-      {
+      if (any) {
         const int i = tid & 63, kb = tid >> 6;
         int2 pqk[QU];
         double2 csk[QU];
@@ -279,8 +302,10 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
   const int P = a.P, B = a.B;
   const int PA = P * (P - 1) / 2;
   const int per = PA + P * (B / JS);
-  const int64_t b = a.b0 + blockIdx.x / per;
-  int t = (int)(blockIdx.x % per);
+  int64_t m;
+  int t;
+  if (!xcd_item(per, a.nb, m, t)) return;
+  const int64_t b = a.b0 + m;
   if (a.flags[b * F_STRIDE + F_DONE]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
@@ -464,7 +489,7 @@ hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
   // matrices per launch, so that a grid stays below 2^32 work-items
   const int64_t max_wg = 0xffffffffLL / NTH;
   const int64_t per_update = (int64_t)P * (P - 1) / 2 + (int64_t)P * (B / JS);
-  const int64_t chunk = max_wg / per_update;
+  const int64_t chunk = max_wg / per_update / 8 * 8;
   for (int t = 0; t <= p.max_sweeps; ++t) {
     hipLaunchKernelGGL(jacobi_sweep_kernel, dim3(fgrid), dim3(256), 0, stream, p.flags, N, t, p.pass);
     if (t == p.max_sweeps) break;
@@ -474,8 +499,9 @@ hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
       for (int64_t b0 = 0; b0 < N; b0 += chunk) {
         const int64_t nb = N - b0 < chunk ? N - b0 : chunk;
         a.b0 = b0;
-        hipLaunchKernelGGL(jacobi_pair_kernel, dim3((unsigned)(nb * P)), dim3(NTH), 0, stream, a);
-        hipLaunchKernelGGL(jacobi_update_kernel, dim3((unsigned)(nb * per_update)), dim3(NTH), 0, stream, a);
+        a.nb = nb;
+        hipLaunchKernelGGL(jacobi_pair_kernel, dim3((unsigned)xcd_grid(nb, P)), dim3(NTH), 0, stream, a);
+        hipLaunchKernelGGL(jacobi_update_kernel, dim3((unsigned)xcd_grid(nb, per_update)), dim3(NTH), 0, stream, a);
       }
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -140,3 +140,35 @@ def test_full_step_chebyshev(stack):
     assert torch.equal(outs[0][:B, :B], U[0]) and torch.equal(outs[-1][B:, -B:], U[NG - 1])
     del A, X, U, G, grads, outs
     torch.cuda.empty_cache()
+
+
+def test_full_evd(stack):
+    """The block-Jacobi eigendecomposition on the full stack.  The fp64 oracle needs minutes per
+    1024-block, so here the checks are properties of every block: it converged (status 0), its
+    eigenvalues keep the block's trace and Frobenius norm (sum w = tr A, sum w^2 = ||A||_F^2,
+    evaluated in fp64), the residual holds, and X is exactly symmetric."""
+    A, _ = stack
+    X = torch.empty_like(A)
+    w = torch.empty((N, B), device=DEV)
+    sweeps = torch.empty(N, dtype=torch.int32, device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=DEV)
+    dash.dash_inverse_root_evd(A, N, B, 20, 0, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
+    del ws
+    torch.cuda.empty_cache()
+    assert int(status.abs().sum()) == 0
+    assert int(sweeps.max()) < 20
+    for i in range(0, N, 256):
+        a = A[i:i + 256].double()
+        wd = w[i:i + 256].double()
+        tr = torch.diagonal(a, dim1=1, dim2=2).sum(1)
+        fro2 = (a * a).sum((1, 2))
+        assert float(((wd.sum(1) - tr).abs() / tr).max()) < 1e-5
+        assert float((((wd * wd).sum(1) - fro2).abs() / fro2).max()) < 1e-5
+        del a
+    X_h = host(X[SAMPLE])
+    assert np.max(residual(X_h, host(A[SAMPLE]))) < R_FP32
+    assert np.array_equal(X_h, np.swapaxes(X_h, 1, 2))
+    assert residual_all(X, A) < R_FP32
+    del X, w
+    torch.cuda.empty_cache()
