@@ -133,6 +133,26 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
                                  dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* Per-block adaptive variants of the two iterations ([PT] Significância e Alegações, "Direções
+ * Futuras": the authors point to choosing the solver work per block from its conditioning).  Each
+ * block stops iterating as soon as its own monitor is <= tol before a step k >= 1 (the first step
+ * always runs): from then on its iterates pass through the remaining launches unchanged (no products
+ * are computed for it) and its output is formed from them as usual.  A block whose monitor never
+ * reaches tol runs all steps.  The monitor is the same as in the fixed-step calls: ||P_k - I|| for
+ * NDB (each of the two calls stops on its own), ||M_k - I|| = ||X_k^4 A_s - I|| for CN, in
+ * Frobenius norm over sqrt(B).
+ * max_iters*: the step limits (as iters* above).  tol >= 0.  monitor is required ([N, max1 + max2]
+ * for NDB, [N, max_iters] for CN); its entries after a block stopped are 0.
+ * steps: NULL or [N, 2] (NDB: steps run by call 1 and call 2) / [N] (CN): the steps each block ran.
+ * CN: prec == DASH_FP32 only (DASH_FP16 -> DASH_ERR_UNSUPPORTED).  Other arguments as above. */
+dash_status dash_inverse_root_ndb_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t max_iters1,
+                                           int32_t max_iters2, float tol, float* X, float* sqrt_out, float* monitor,
+                                           int32_t* steps, int32_t* status, void* ws, size_t ws_bytes,
+                                           void* stream);
+dash_status dash_inverse_root_cn_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t p,
+                                          int32_t max_iters, float tol, dash_prec prec, float* X, float* monitor,
+                                          int32_t* steps, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
 /* Inverse fourth root by a Chebyshev approximation evaluated with Clenshaw's recurrence
  * ([PT] Metodologia, item 2, "Aproximações de Polinômios de Chebyshev").  The degree-`degree`
  * interpolant p of x^{-1/4} at the Chebyshev points of the first kind on [lo, hi] is applied to

@@ -23,8 +23,10 @@ from ._lib import (  # noqa: F401
     dash_flops,
     dash_inverse_root_cheb,
     dash_inverse_root_cn,
+    dash_inverse_root_cn_adaptive,
     dash_inverse_root_evd,
     dash_inverse_root_ndb,
+    dash_inverse_root_ndb_adaptive,
     dash_scale,
     dash_solver_products,
     dash_stack,

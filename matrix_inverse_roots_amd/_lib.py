@@ -49,6 +49,9 @@ def library() -> ctypes.CDLL:
             "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_ndb_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
+                                                    vp]),
+            "dash_inverse_root_cn_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, st, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cheb": (st, [vp, vp, i64, i32, i32, f64, f64, vp, vp, vp, sz, vp]),
             "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
@@ -166,6 +169,22 @@ def dash_inverse_root_cn(A, s, N: int, B: int, p: int, iters: int, prec: int, X,
     _check("dash_inverse_root_cn",
            library().dash_inverse_root_cn(_ptr(A), _ptr(s), N, B, p, iters, prec, _ptr(X), _ptr(monitor),
                                           _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_ndb_adaptive(A, s, N: int, B: int, max_iters1: int, max_iters2: int, tol: float, X, monitor,
+                                   sqrt_out=None, steps=None, status=None, ws=None, stream=None):
+    _check("dash_inverse_root_ndb_adaptive",
+           library().dash_inverse_root_ndb_adaptive(_ptr(A), _ptr(s), N, B, max_iters1, max_iters2, tol, _ptr(X),
+                                                    _ptr(sqrt_out), _ptr(monitor), _ptr(steps), _ptr(status),
+                                                    _ptr(ws), _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_cn_adaptive(A, s, N: int, B: int, p: int, max_iters: int, tol: float, prec: int, X, monitor,
+                                  steps=None, status=None, ws=None, stream=None):
+    _check("dash_inverse_root_cn_adaptive",
+           library().dash_inverse_root_cn_adaptive(_ptr(A), _ptr(s), N, B, p, max_iters, tol, prec, _ptr(X),
+                                                   _ptr(monitor), _ptr(steps), _ptr(status), _ptr(ws), _nbytes(ws),
+                                                   _stream(stream, A)))
 
 
 def dash_inverse_root_cheb(A, s, N: int, B: int, degree: int, lo: float, hi: float, X, status=None, ws=None,

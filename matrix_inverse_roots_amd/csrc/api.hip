@@ -57,8 +57,9 @@ struct Pool {
   void put(void* p) { free_list.push_back(p); }
 };
 
-size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32); }
-size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + 5 * stack_bytes(N, B, p); }
+size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256); }
+size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32); }
+size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, p); }
 size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
 size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
@@ -90,12 +91,18 @@ struct NdbCtx {
   int32_t* status;
   hipStream_t st;
   Pool* pool;
+  // adaptive stopping (null: every block runs all T steps): a block whose monitor is <= tol before
+  // step k >= 1 keeps its iterates from then on; steps (optional, stride 2) receives the steps run
+  int32_t* freeze = nullptr;
+  float tol = 0.f;
+  int32_t* steps = nullptr;
 };
 
 dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool scaled, int T, int mon_col,
                      bool want_z, float* final_out, float** y_out) {
   // step 0: Z_0 = I so P_0 = M and S_0 = (3I - M)/2; Y_1 = M S_0 = 1.5 M - 0.5 M^2, Z_1 = S_0.
   const bool last = (T == 1);
+  if (c.freeze) TRY(launch_freeze_reset(c.freeze, c.steps, 2, T, c.N, c.st));
   float* Z = nullptr;
   float* Y = nullptr;
   {
@@ -162,8 +169,11 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         e.mon_mul = 4.f;
       }
       Product p = prod(Z, Y, S);
+      p.freeze = c.freeze;  // a stopped block needs no S
       TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
     }
+    if (c.freeze)
+      TRY(launch_freeze_update(c.monitor, c.mon_cols, mon_col + k, c.B, c.tol, c.freeze, c.steps, 2, k, c.N, c.st));
     if (k == T - 1) {
       if (want_z) {  // Z_T = S Z, unscaled into the output
         Epilogue e;
@@ -172,6 +182,8 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         e.coef = c.coef;
         e.status = c.status;
         Product p = prod(S, Z, final_out);
+        p.freeze = c.freeze;
+        p.pass = 2;
         TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
@@ -179,6 +191,8 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         float* Yn = (float*)c.pool->get();
         Epilogue e;
         Product p = prod(Y, S, Yn);
+        p.freeze = c.freeze;
+        p.pass = 1;
         TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
@@ -191,6 +205,9 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     float* Zn = (float*)c.pool->get();
     Epilogue e;
     Product p[2] = {prod(Y, S, Yn), prod(S, Z, Zn)};
+    p[0].freeze = p[1].freeze = c.freeze;
+    p[0].pass = 1;
+    p[1].pass = 2;
     TRY(launch_gemm(p, 2, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
     c.pool->put(Y);
     c.pool->put(Z);
@@ -443,9 +460,19 @@ dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, d
   return DASH_OK;
 }
 
-dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
-                                  int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
-                                  void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// adaptive stopping of an NDB or CN call: tol < 0 runs every step
+struct Stop {
+  float tol = -1.f;
+  int32_t* steps = nullptr;
+};
+
+dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1, int32_t iters2, float* X,
+                     float* sqrt_out, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                     const Stop& stop) {
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (sqrt_out && (!aligned(sqrt_out, 16) || sqrt_out == A || sqrt_out == X)) return DASH_ERR_INVALID_ARG;
@@ -457,6 +484,7 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
   hipStream_t st = as_stream(stream);
   Carver cv{(char*)ws, ws_bytes};
   float* coef = (float*)cv.take(coef_bytes(N));
+  int32_t* freeze = (int32_t*)cv.take(flag_bytes(N));
   Pool pool;
   for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, DASH_FP32)));
   const int cols = iters1 + iters2;
@@ -464,6 +492,11 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
   if (monitor) TRY(launch_fill_f32(monitor, N * cols, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
+  if (stop.tol >= 0.f) {
+    c.freeze = freeze;
+    c.tol = stop.tol;
+    c.steps = stop.steps;
+  }
   float* Y = nullptr;
   dash_status r = ndb_call(c, A, false, true, iters1, 0, false, nullptr, &Y);
   if (r != DASH_OK) return r;
@@ -476,15 +509,41 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
     sq.coef = coef;
     TRY(launch_affine(sq, N, B, st));
   }
+  if (c.steps) c.steps += 1;  // the second call's column
   r = ndb_call(c, Y, true, false, iters2, iters1, true, X, nullptr);
   if (r != DASH_OK) return r;
   if (monitor) TRY(launch_monitor_finish(monitor, N * cols, B, st));
   return DASH_OK;
 }
 
-dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
-                                 dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
-                                 size_t ws_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                  int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return ndb_impl(A, s, N, B, iters1, iters2, X, sqrt_out, monitor, status, ws, ws_bytes, stream, Stop());
+}
+
+dash_status dash_inverse_root_ndb_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t max_iters1,
+                                           int32_t max_iters2, float tol, float* X, float* sqrt_out, float* monitor,
+                                           int32_t* steps, int32_t* status, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (!monitor || !(tol >= 0.f && tol < INFINITY) || (steps && !aligned(steps, 4))) return DASH_ERR_INVALID_ARG;
+  Stop stop;
+  stop.tol = tol;
+  stop.steps = steps;
+  return ndb_impl(A, s, N, B, max_iters1, max_iters2, X, sqrt_out, monitor, status, ws, ws_bytes, stream, stop);
+}
+
+}  // extern "C"
+
+namespace {
+
+dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters, dash_prec prec,
+                    float* X, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                    const Stop& stop) {
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (X == A || iters < 1 || iters > 1000) return DASH_ERR_INVALID_ARG;
@@ -497,12 +556,21 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   hipStream_t st = as_stream(stream);
   Carver cv{(char*)ws, ws_bytes};
   float* coef = (float*)cv.take(coef_bytes(N));
+  int32_t* freeze = (int32_t*)cv.take(flag_bytes(N));
   Pool pool;
   for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, prec)));
   if (status) TRY(launch_fill_i32(status, N, 0, st));
   if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   const int T = iters;
+  // adaptive stopping (fp32): a block whose monitor ||M_k - I|| is <= tol before step k >= 1
+  // keeps X_k from then on
+  if (stop.tol >= 0.f) {
+    if (prec != DASH_FP32) return DASH_ERR_UNSUPPORTED;
+    TRY(launch_freeze_reset(freeze, stop.steps, 1, T, N, st));
+  } else {
+    freeze = nullptr;
+  }
   // binary16 (T >= 2, cn_half): triangle-only products, the iterates being symmetric polynomials
   // in A and the error floor set by binary16 storage; fp32 (below): full products, which keep the
   // fp32 rounding floor of the iteration lowest at high condition numbers
@@ -570,12 +638,16 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   }
   void* Xk = S;  // X_1 = S_0 shares the buffer (both are read-only from here on)
   for (int k = 0; k < T; ++k) {
+    if (freeze && k >= 1)  // monitor column k (||M_k - I||) is complete
+      TRY(launch_freeze_update(monitor, T, k, B, stop.tol, freeze, stop.steps, 1, k, N, st));
     if (k == T - 1) {  // X_T = s^{-1/4} X_{T-1} S_{T-1}
       Epilogue e;
       e.ia = CO_U;
       e.coef = coef;
       e.status = status;
       Product pr = prod(Xk, S, X);
+      pr.freeze = freeze;
+      pr.pass = 1;
       TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, false, e, st, true));
       break;
     }
@@ -586,6 +658,8 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
       Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
+      pr[0].freeze = pr[1].freeze = freeze;
+      pr[0].pass = 1;  // a stopped block keeps X_k and needs no S^2
       TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
       pool.put(Xk);
       pool.put(S);
@@ -594,6 +668,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
     void* S4 = pool.get();
     {
       Product pr = prod(S2, S2, S4);
+      pr.freeze = freeze;
       TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
     }
     pool.put(S2);
@@ -609,6 +684,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.gamma = 1.25f;
       e.mon_mul = 16.f;
       Product pr = prod(M, S4, Sn);
+      pr.freeze = freeze;
       TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st, true));
       pool.put(M);
       M = nullptr;
@@ -618,6 +694,7 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
       e.alpha2 = -0.25f;
       e.gamma2 = 1.25f;
       Product pr = prod(M, S4, Mn, nullptr, nullptr, Sn);
+      pr.freeze = freeze;
       TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st, true));
       pool.put(M);
       M = Mn;
@@ -627,6 +704,26 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
   }
   if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
   return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
+                                 dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return cn_impl(A, s, N, B, p, iters, prec, X, monitor, status, ws, ws_bytes, stream, Stop());
+}
+
+dash_status dash_inverse_root_cn_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t p,
+                                          int32_t max_iters, float tol, dash_prec prec, float* X, float* monitor,
+                                          int32_t* steps, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (!monitor || !(tol >= 0.f && tol < INFINITY) || (steps && !aligned(steps, 4))) return DASH_ERR_INVALID_ARG;
+  Stop stop;
+  stop.tol = tol;
+  stop.steps = steps;
+  return cn_impl(A, s, N, B, p, max_iters, prec, X, monitor, status, ws, ws_bytes, stream, stop);
 }
 
 dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,

@@ -60,6 +60,9 @@ struct Epilogue {
 // while it is staged.  Binary16 operands (map_ia unused): map_a must be a power of two (each element
 // is then the exact value rounded once to binary16).  fp32 operands: only map_y, in the Clenshaw
 // launches (fold_c), one fma per element.
+// freeze (optional, [N], fp32 NN full products only): a block b with freeze[b] != 0 has stopped
+// iterating.  Its product is not computed: pass = 0 writes nothing, pass = 1 / 2 writes the
+// epilogue applied to X_b / Y_b in place of X_b Y_b (the iterate goes through unchanged).
 struct Product {
   const void* X = nullptr;
   const void* Y = nullptr;
@@ -70,6 +73,8 @@ struct Product {
   bool map_x = false, map_y = false;
   float map_a = 0.f, map_g = 0.f;
   int8_t map_ia = CO_NONE;
+  const int32_t* freeze = nullptr;
+  int8_t pass = 0;
 };
 
 enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed
@@ -114,6 +119,14 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 // monitor[i] <- sqrt(monitor[i]) / sqrt(B)
 hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t stream);
+// Stopping rule of the adaptive solvers.  Reset: freeze[b] = 0 and steps[b * steps_stride] = T
+// (steps optional).  Update, after the launch that completed monitor column `col` (a sum of
+// squares, before launch_monitor_finish): a block not yet frozen whose sqrt(sum)/sqrt(B) <= tol is
+// frozen and steps[b * steps_stride] = step.
+hipError_t launch_freeze_reset(int32_t* freeze, int32_t* steps, int steps_stride, int T, int64_t N,
+                               hipStream_t stream);
+hipError_t launch_freeze_update(const float* monitor, int mon_stride, int col, int B, float tol, int32_t* freeze,
+                                int32_t* steps, int steps_stride, int step, int64_t N, hipStream_t stream);
 
 // Scaling kernels.
 hipError_t launch_frobenius(const float* A, int64_t N, int B, float* s, hipStream_t stream);

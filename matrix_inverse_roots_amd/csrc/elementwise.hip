@@ -191,6 +191,25 @@ __global__ void monitor_finish_kernel(float* m, int64_t n, float inv_sqrt_b) {
   if (i < n) m[i] = sqrtf(m[i]) * inv_sqrt_b;
 }
 
+// stopping rule of the adaptive solvers (see launch_freeze_update)
+__global__ void freeze_reset_kernel(int32_t* freeze, int32_t* steps, int steps_stride, int T, int64_t N) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= N) return;
+  freeze[b] = 0;
+  if (steps) steps[b * steps_stride] = T;
+}
+
+__global__ void freeze_update_kernel(const float* monitor, int mon_stride, int col, float inv_sqrt_b, float tol,
+                                     int32_t* freeze, int32_t* steps, int steps_stride, int step, int64_t N) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= N || freeze[b]) return;
+  const float m = sqrtf(monitor[b * mon_stride + col]) * inv_sqrt_b;
+  if (m <= tol) {  // a NaN monitor never freezes: the block runs on and is flagged at the end
+    freeze[b] = 1;
+    if (steps) steps[b * steps_stride] = step;
+  }
+}
+
 // Copy one weight's tiles to (to_stack) or from the stack.  Workgroup = 8 rows of one tile.
 // Stack / unstack.  The stack side of a copy is one linear stream, so each workgroup moves
 // COPY_VEC * 256 consecutive float4 of it and gathers them from (or scatters them to) the rows of
@@ -314,6 +333,20 @@ hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t s
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(monitor_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, monitor, n,
                      (float)(1.0 / sqrt((double)B)));
+  return hipGetLastError();
+}
+
+hipError_t launch_freeze_reset(int32_t* freeze, int32_t* steps, int steps_stride, int T, int64_t N,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(freeze_reset_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, freeze, steps,
+                     steps_stride, T, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_freeze_update(const float* monitor, int mon_stride, int col, int B, float tol, int32_t* freeze,
+                                int32_t* steps, int steps_stride, int step, int64_t N, hipStream_t stream) {
+  hipLaunchKernelGGL(freeze_update_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, monitor,
+                     mon_stride, col, (float)(1.0 / sqrt((double)B)), tol, freeze, steps, steps_stride, step, N);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS, bool CY, bool MAPY = false>
+template <int TILE, int TX, int TY, bool SYM, typename TO, bool CHECKS, bool CY, bool MAPY = false, bool FRZ = false>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   constexpr int BK = 32;
   constexpr int WT = TILE / 2;
@@ -44,6 +44,25 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, h = lane >> 5;
+
+  if constexpr (FRZ) {  // a block that stopped iterating: pass an operand through, or write nothing
+    if (P.freeze && P.freeze[tc.b]) {
+      if (P.pass == 0) return;
+      const float* Z = P.pass == 1 ? X : Y;
+      f32x16 pz[MT][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + wm * WT + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            pz[mt][nt][r] = Z[(int64_t)i * B + j0 + wn * WT + nt * 32 + li];
+          }
+      epilogue<MT, MT, WT, WT, SYM, TO, true, true, TILE, CHECKS>(a, tc, P, pz, wm, wn, lane);
+      return;
+    }
+  }
 
   // two register slots: k-slices kt + 1 and kt + 2 are in flight while slice kt is in LDS
   f32x4 ra0[NL], rb0[NL], ra1[NL], rb1[NL];
@@ -189,6 +208,8 @@ hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, bool c_is_y, hipStre
     if (sym && c_is_y && map_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true, true>, a, stream);
     if (sym && c_is_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true>, a, stream);
     if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, false>, a, stream);
+    if (a.p0.freeze || (a.nprob > 1 && a.p1.freeze))
+      return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false, false, true>, a, stream);
     return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false>, a, stream);
   }
   if (!sym) return hipErrorInvalidValue;

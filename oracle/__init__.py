@@ -25,6 +25,7 @@ _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int)
 
 
 def build(force: bool = True) -> str:
@@ -54,6 +55,9 @@ def _load():
             "orc_ndb": (None, [i, _dp, i, _dp, _dp, _dp]),
             "orc_ndb_inverse_root": (None, [i, _dp, d, i, i, _dp, _dp, _dp]),
             "orc_cn_inverse_root": (None, [i, _dp, d, i, i, _dp, _dp]),
+            "orc_ndb_until": (i, [i, _dp, i, d, _dp, _dp, _dp]),
+            "orc_ndb_inverse_root_until": (None, [i, _dp, d, i, i, d, _dp, _dp, _dp, _ip]),
+            "orc_cn_until": (i, [i, _dp, d, i, i, d, _dp, _dp]),
             "orc_cheb_coeffs": (None, [i, d, d, d, _dp]),
             "orc_clenshaw": (None, [i, _dp, i, _dp, d, d, _dp]),
             "orc_cheb_inverse_root": (None, [i, _dp, d, i, d, d, _dp]),
@@ -249,6 +253,45 @@ def cn_inverse_root(A, s, iters: int, half_storage: bool = False, threads: int |
     _over_blocks(one, N, threads)
     mon = mon[:, :iters]
     return (X[0], mon[0]) if single else (X, mon)
+
+
+def ndb_inverse_root_adaptive(A, s, max1: int, max2: int, tol: float, threads: int | None = None):
+    """Composed NDB root with the per-block stopping rule (each call stops before a step k >= 1 once
+    its monitor is <= tol).  Returns (X, monitor[N, max1+max2] (0 after a stop), steps[N, 2])."""
+    A, single = _as_stack(A)
+    N, n, _ = A.shape
+    s = _per_block(s, N)
+    X = np.empty_like(A)
+    mon = np.zeros((N, max(max1 + max2, 1)))
+    steps = np.zeros((N, 2), dtype=np.int32)
+    lib = _load()
+
+    def one(b):
+        lib.orc_ndb_inverse_root_until(n, _p(A[b]), float(s[b]), int(max1), int(max2), float(tol), _p(X[b]),
+                                       _null(), _p(mon[b]), steps[b].ctypes.data_as(_ip))
+
+    _over_blocks(one, N, threads)
+    mon = mon[:, : max1 + max2]
+    return (X[0], mon[0], steps[0]) if single else (X, mon, steps)
+
+
+def cn_inverse_root_adaptive(A, s, max_iters: int, tol: float, threads: int | None = None):
+    """Coupled-Newton root with the per-block stopping rule.  Returns (X, monitor (0 after a stop),
+    steps[N])."""
+    A, single = _as_stack(A)
+    N, n, _ = A.shape
+    s = _per_block(s, N)
+    X = np.empty_like(A)
+    mon = np.zeros((N, max(max_iters, 1)))
+    steps = np.zeros(N, dtype=np.int32)
+    lib = _load()
+
+    def one(b):
+        steps[b] = lib.orc_cn_until(n, _p(A[b]), float(s[b]), int(max_iters), 0, float(tol), _p(X[b]), _p(mon[b]))
+
+    _over_blocks(one, N, threads)
+    mon = mon[:, :max_iters]
+    return (X[0], mon[0], steps[0]) if single else (X, mon, steps)
 
 
 def cheb_coeffs(degree: int, lo: float, hi: float, expo: float = -0.25) -> np.ndarray:

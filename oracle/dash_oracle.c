@@ -283,7 +283,10 @@ double orc_mpi_half(int n, const double* A, int k, int T, const double* V0, doub
  * no value, so this plain form runs every step in full.
  * monitor[k] (optional) = ||P_k - I||_F / sqrt(n).
  * ---------------------------------------------------------------------------------------------- */
-void orc_ndb(int n, const double* M, int T, double* Y, double* Z, double* monitor) {
+/* Stopping rule of the adaptive variants ([PT] Significância e Alegações, "Direções Futuras": the
+ * solver work chosen per block).  Reading: a block stops before step k >= 1 as soon as its monitor
+ * is <= tol and keeps its iterates; tol < 0 never stops.  orc_ndb_until returns the steps run. */
+int orc_ndb_until(int n, const double* M, int T, double tol, double* Y, double* Z, double* monitor) {
   const size_t nn = (size_t)n * n;
   double* P = (double*)malloc(sizeof(double) * nn);
   double* S = (double*)malloc(sizeof(double) * nn);
@@ -291,9 +294,12 @@ void orc_ndb(int n, const double* M, int T, double* Y, double* Z, double* monito
   double* Zn = (double*)malloc(sizeof(double) * nn);
   memcpy(Y, M, sizeof(double) * nn);
   set_identity(n, Z, 1.0);
-  for (int k = 0; k < T; ++k) {
+  int k = 0;
+  for (; k < T; ++k) {
     orc_matmul(n, Z, Y, P);
-    if (monitor) monitor[k] = dist_to_identity(n, P);
+    const double m = dist_to_identity(n, P);
+    if (monitor) monitor[k] = m;
+    if (tol >= 0.0 && k >= 1 && m <= tol) break;
     for (int i = 0; i < n; ++i)
       for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = (i == j ? 1.5 : 0.0) - 0.5 * P[IDX(i, j, n)];
     orc_matmul(n, Y, S, Yn);
@@ -305,29 +311,43 @@ void orc_ndb(int n, const double* M, int T, double* Y, double* Z, double* monito
   free(S);
   free(Yn);
   free(Zn);
+  return k;
+}
+
+void orc_ndb(int n, const double* M, int T, double* Y, double* Z, double* monitor) {
+  orc_ndb_until(n, M, T, -1.0, Y, Z, monitor);
 }
 
 /* c5: inverse fourth root by two NDB calls.  Reading: the first call on A_s = A/s gives
  * Y = A_s^{1/2}; the second call on that Y gives Z = (A_s^{1/2})^{-1/2} = A_s^{-1/4};
  * X = s^{-1/4} Z.  T1 and T2 count steps per call.  Optional outputs: sqrt_out = s^{1/2} Y
  * (the square root of A, the pages' by-product), monitor[0..T1+T2) as in orc_ndb. */
-void orc_ndb_inverse_root(int n, const double* A, double s, int T1, int T2, double* X, double* sqrt_out,
-                          double* monitor) {
+void orc_ndb_inverse_root_until(int n, const double* A, double s, int T1, int T2, double tol, double* X,
+                                double* sqrt_out, double* monitor, int* steps) {
   const size_t nn = (size_t)n * n;
   double* As = (double*)malloc(sizeof(double) * nn);
   double* Y = (double*)malloc(sizeof(double) * nn);
   double* Z = (double*)malloc(sizeof(double) * nn);
   for (size_t e = 0; e < nn; ++e) As[e] = A[e] / s;
-  orc_ndb(n, As, T1, Y, Z, monitor);
+  const int s1 = orc_ndb_until(n, As, T1, tol, Y, Z, monitor);
   if (sqrt_out)
     for (size_t e = 0; e < nn; ++e) sqrt_out[e] = sqrt(s) * Y[e];
   memcpy(As, Y, sizeof(double) * nn);
-  orc_ndb(n, As, T2, Y, Z, monitor ? monitor + T1 : NULL);
+  const int s2 = orc_ndb_until(n, As, T2, tol, Y, Z, monitor ? monitor + T1 : NULL);
+  if (steps) {
+    steps[0] = s1;
+    steps[1] = s2;
+  }
   const double u = pow(s, -0.25);
   for (size_t e = 0; e < nn; ++e) X[e] = u * Z[e];
   free(As);
   free(Y);
   free(Z);
+}
+
+void orc_ndb_inverse_root(int n, const double* A, double s, int T1, int T2, double* X, double* sqrt_out,
+                          double* monitor) {
+  orc_ndb_inverse_root_until(n, A, s, T1, T2, -1.0, X, sqrt_out, monitor, NULL);
 }
 
 /* ------------------------------------------------------------------------------------------------
@@ -340,7 +360,8 @@ void orc_ndb_inverse_root(int n, const double* A, double s, int T1, int T2, doub
  * operand A_s as well, modelling binary16 operands with exact accumulation (diagnostic mode).
  * monitor[k] (optional) = ||M_k - I||_F / sqrt(n), before step k.
  * ---------------------------------------------------------------------------------------------- */
-void orc_cn_inverse_root(int n, const double* A, double s, int T, int half_storage, double* X, double* monitor) {
+int orc_cn_until(int n, const double* A, double s, int T, int half_storage, double tol, double* X,
+                 double* monitor) {
   const size_t nn = (size_t)n * n;
   double* M = (double*)malloc(sizeof(double) * nn);
   double* S = (double*)malloc(sizeof(double) * nn);
@@ -356,8 +377,11 @@ void orc_cn_inverse_root(int n, const double* A, double s, int T, int half_stora
   for (size_t e = 0; e < nn; ++e) M[e] = A[e] / s;
   STORE16(M);
   set_identity(n, Xk, 1.0);
-  for (int k = 0; k < T; ++k) {
-    if (monitor) monitor[k] = dist_to_identity(n, M);
+  int k = 0;
+  for (; k < T; ++k) {
+    const double m = dist_to_identity(n, M);
+    if (monitor) monitor[k] = m;
+    if (tol >= 0.0 && k >= 1 && m <= tol) break;  /* stopping rule as in orc_ndb_until */
     for (int i = 0; i < n; ++i)
       for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = ((i == j ? 5.0 : 0.0) - M[IDX(i, j, n)]) / 4.0;
     STORE16(S);
@@ -381,6 +405,11 @@ void orc_cn_inverse_root(int n, const double* A, double s, int T, int half_stora
   free(S4);
   free(Xk);
   free(tmp);
+  return k;
+}
+
+void orc_cn_inverse_root(int n, const double* A, double s, int T, int half_storage, double* X, double* monitor) {
+  orc_cn_until(n, A, s, T, half_storage, -1.0, X, monitor);
 }
 
 /* ------------------------------------------------------------------------------------------------

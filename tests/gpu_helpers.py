@@ -94,3 +94,26 @@ def evd(A, max_sweeps=20, refine=0):
     ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=DEV)
     dash.dash_inverse_root_evd(A, N, B, max_sweeps, refine, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
     return X, w, sweeps, status
+
+
+def ndb_adaptive(A, s, max1, max2, tol):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    mon = torch.empty((N, max1 + max2), device=DEV)
+    steps = torch.empty((N, 2), dtype=torch.int32, device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=DEV)
+    dash.dash_inverse_root_ndb_adaptive(A, s, N, B, max1, max2, tol, X, mon, steps=steps, status=status, ws=ws)
+    return X, mon, steps, status
+
+
+def cn_adaptive(A, s, max_iters, tol, prec=dash.DASH_FP32):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    mon = torch.empty((N, max_iters), device=DEV)
+    steps = torch.empty(N, dtype=torch.int32, device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=DEV)
+    dash.dash_inverse_root_cn_adaptive(A, s, N, B, 4, max_iters, tol, prec, X, mon, steps=steps, status=status,
+                                       ws=ws)
+    return X, mon, steps, status

@@ -335,6 +335,82 @@ def test_cn_half_storage_residual():
 # c7: Chebyshev / Clenshaw
 # ----------------------------------------------------------------------------------------------
 
+# ---- adaptive stopping rule ([PT] Significância e Alegações, "Direções Futuras"; reading: a call
+# stops before step k >= 1 once its monitor is <= tol)
+
+def _scalar_ndb_monitors(m, T):
+    """Monitors of one NDB call on diag(m), from the scalar recurrence per eigenvalue (plain floats)."""
+    y, z, mons = list(m), [1.0] * len(m), []
+    for _ in range(T):
+        p = [zi * yi for zi, yi in zip(z, y)]
+        mons.append(math.sqrt(sum((pi - 1.0) ** 2 for pi in p) / len(p)))
+        sc = [(3.0 - pi) / 2.0 for pi in p]
+        y = [yi * si for yi, si in zip(y, sc)]
+        z = [si * zi for si, zi in zip(sc, z)]
+    return mons, y
+
+
+def _scalar_cn_monitors(m, T):
+    x, mm, mons = [1.0] * len(m), list(m), []
+    for _ in range(T):
+        mons.append(math.sqrt(sum((mi - 1.0) ** 2 for mi in mm) / len(mm)))
+        sc = [(5.0 - mi) / 4.0 for mi in mm]
+        x = [xi * si for xi, si in zip(x, sc)]
+        mm = [mi * si ** 4 for mi, si in zip(mm, sc)]
+    return mons
+
+
+def _first_below(mons, tol, T):
+    return next((k for k in range(1, T) if mons[k] <= tol), T)
+
+
+def test_adaptive_step_counts_closed_form():
+    """Diagonal blocks: the scalar recurrences give every monitor, hence the step at which each call
+    stops; tol sits midway (in log scale) between two consecutive monitors of the deciding step."""
+    lam = np.exp(np.linspace(np.log(3e-3), 0.0, 48))
+    A = np.diag(lam)
+    T = 25
+    mons1, y = _scalar_ndb_monitors(list(lam), T)
+    k1 = _first_below(mons1, 1e-3, T)
+    tol = math.sqrt(mons1[k1] * mons1[k1 - 1])        # between the last monitor above and the first below
+    X, mon, steps = oracle.ndb_inverse_root_adaptive(A, 1.0, T, T, tol)
+    assert steps[0] == _first_below(mons1, tol, T)
+    y1, _ = _scalar_ndb_monitors(list(lam), steps[0])[1], None
+    mons2, _ = _scalar_ndb_monitors(y1, T)
+    assert steps[1] == _first_below(mons2, tol, T)
+    np.testing.assert_allclose(mon[: steps[0] + 1], mons1[: steps[0] + 1], rtol=1e-9, atol=1e-15)
+    assert np.all(mon[steps[0] + 1:T] == 0.0)
+    monc = _scalar_cn_monitors(list(lam), T)
+    kc = _first_below(monc, 1e-3, T)
+    tolc = math.sqrt(monc[kc] * monc[kc - 1])
+    Xc, monc_o, stc = oracle.cn_inverse_root_adaptive(A, 1.0, T, tolc)
+    assert stc == _first_below(monc, tolc, T)
+    np.testing.assert_allclose(monc_o[: stc + 1], monc[: stc + 1], rtol=1e-9, atol=1e-15)
+
+
+def test_adaptive_equals_fixed_run_of_its_length():
+    """Stopping after k steps leaves exactly the k-step result (bitwise), and the step count is the
+    first k >= 1 whose fixed-run monitor is <= tol; tol < 0 never stops."""
+    A = di.tiny_stack()
+    s = np.array([np.linalg.norm(a) for a in A])
+    tol = 1e-6
+    X, mon, steps = oracle.ndb_inverse_root_adaptive(A, s, 20, 20, tol)
+    for b in range(A.shape[0]):
+        Xf, _, monf = oracle.ndb_inverse_root(A[b], s[b], int(steps[b, 0]), int(steps[b, 1]))
+        assert np.array_equal(X[b], Xf)
+        _, _, mon_full1 = oracle.ndb_inverse_root(A[b], s[b], 20, 1)
+        assert steps[b, 0] == _first_below(list(mon_full1[:20]), tol, 20)
+    Xc, monc, stc = oracle.cn_inverse_root_adaptive(A, s, 20, tol)
+    for b in range(A.shape[0]):
+        Xf, monf = oracle.cn_inverse_root(A[b], s[b], int(stc[b]))
+        assert np.array_equal(Xc[b], Xf)
+        _, mon_full = oracle.cn_inverse_root(A[b], s[b], 20)
+        assert stc[b] == _first_below(list(mon_full), tol, 20)
+    Xn, _, stn = oracle.ndb_inverse_root_adaptive(A, s, 6, 5, -1.0)
+    assert np.all(stn == [6, 5])
+    assert np.array_equal(Xn, oracle.ndb_inverse_root(A, s, 6, 5)[0])
+
+
 @pytest.mark.parametrize("fx", GOLDEN["chebyshev"], ids=lambda f: "%g_%g" % (f["lo"], f["hi"]))
 def test_cheb_coeffs_x2_closed_form(fx):
     c = oracle.cheb_coeffs(2, fx["lo"], fx["hi"], 2.0)
