@@ -49,11 +49,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd"], default="step",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive"], default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
                         "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
-                        "block-Jacobi eigendecomposition solve")
+                        "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
+                        "fixed step counts on a stack of two conditionings")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
@@ -116,6 +117,8 @@ def main():
         return only_solver(dash, di, torch, dev, args.only)
     if args.only == "evd":
         return only_evd(dash, di, torch, dev)
+    if args.only == "adaptive":
+        return only_adaptive(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -349,6 +352,84 @@ def only_evd(dash, di, torch, dev):
                       "status_nonzero": int((status != 0).sum()),
                       "residual_blocks_0_last": [evd_residual(torch, A, X, 0), evd_residual(torch, A, X, N - 1)]}),
           flush=True)
+
+
+ADAPT_TOL = 1e-5
+
+
+def only_adaptive(dash, di, torch, dev):
+    """Per-block stopping on the N=3072, B=1024 stack whose first half is the Gram stack
+    (G G^T/1024 + 1e-6 I, kappa ~5) and second half the same with 1e-8 I (kappa ~500): adaptive NDB
+    and CN (fp32, tol 1e-5) against fixed step counts large enough for every block."""
+    import numpy as np
+
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    A[N // 2:].diagonal(dim1=1, dim2=2).sub_(EPS - 1e-8)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    s = torch.empty(N, device=dev)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    del ws
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=dev)
+    sample = [0, N // 2 - 1, N // 2, N - 1]
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    out = {"mode": "adaptive", "N": N, "B": B, "tol": ADAPT_TOL}
+    # NDB: adaptive with generous limits, then fixed at the largest step counts any block used
+    M1, M2 = 16, 12
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=dev)
+    mon = torch.empty((N, M1 + M2), device=dev)
+    steps = torch.empty((N, 2), dtype=torch.int32, device=dev)
+    run_a = lambda: dash.dash_inverse_root_ndb_adaptive(A, s, N, B, M1, M2, ADAPT_TOL, X, mon, steps=steps,
+                                                        status=status, ws=ws)
+    run_a()
+    ms_a = timed(run_a)
+    st = steps.cpu().numpy()
+    r_a = [evd_residual(torch, A, X, b) for b in sample]
+    T1, T2 = int(st[:, 0].max()), int(st[:, 1].max())
+    run_f = lambda: dash.dash_inverse_root_ndb(A, s, N, B, T1, T2, X, status=status, ws=ws)
+    ms_f = timed(run_f)
+    r_f = [evd_residual(torch, A, X, b) for b in sample]
+    h = N // 2
+    out["ndb_fp32"] = {"adaptive_ms": round(ms_a, 1), "fixed_ms": round(ms_f, 1), "fixed_steps": [T1, T2],
+                       "speedup": round(ms_f / ms_a, 3),
+                       "mean_steps_kappa5": [float(st[:h, 0].mean()), float(st[:h, 1].mean())],
+                       "mean_steps_kappa500": [float(st[h:, 0].mean()), float(st[h:, 1].mean())],
+                       "residual_adaptive": r_a, "residual_fixed": r_f,
+                       "status_nonzero": int((status != 0).sum())}
+    del ws, mon, steps
+    torch.cuda.empty_cache()
+    # CN fp32
+    MC = 20
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_FP32, device=dev)
+    mon = torch.empty((N, MC), device=dev)
+    steps = torch.empty(N, dtype=torch.int32, device=dev)
+    run_a = lambda: dash.dash_inverse_root_cn_adaptive(A, s, N, B, 4, MC, ADAPT_TOL, dash.DASH_FP32, X, mon,
+                                                       steps=steps, status=status, ws=ws)
+    run_a()
+    ms_a = timed(run_a)
+    st = steps.cpu().numpy()
+    r_a = [evd_residual(torch, A, X, b) for b in sample]
+    T = int(st.max())
+    run_f = lambda: dash.dash_inverse_root_cn(A, s, N, B, 4, T, dash.DASH_FP32, X, status=status, ws=ws)
+    ms_f = timed(run_f)
+    r_f = [evd_residual(torch, A, X, b) for b in sample]
+    out["cn_fp32"] = {"adaptive_ms": round(ms_a, 1), "fixed_ms": round(ms_f, 1), "fixed_steps": T,
+                      "speedup": round(ms_f / ms_a, 3), "mean_steps_kappa5": float(st[:h].mean()),
+                      "mean_steps_kappa500": float(st[h:].mean()), "residual_adaptive": r_a, "residual_fixed": r_f,
+                      "status_nonzero": int((status != 0).sum())}
+    print(json.dumps(out), flush=True)
 
 
 def traffic_from_counters(fetch_csv, write_csv):

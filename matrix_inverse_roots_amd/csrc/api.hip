@@ -565,8 +565,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   const int T = iters;
   // adaptive stopping (fp32): a block whose monitor ||M_k - I|| is <= tol before step k >= 1
   // keeps X_k from then on
-  if (stop.tol >= 0.f) {
-    if (prec != DASH_FP32) return DASH_ERR_UNSUPPORTED;
+  if (stop.tol >= 0.f) {  // fp32 only (checked by the caller before anything was enqueued)
     TRY(launch_freeze_reset(freeze, stop.steps, 1, T, N, st));
   } else {
     freeze = nullptr;
@@ -720,6 +719,8 @@ dash_status dash_inverse_root_cn_adaptive(const float* A, const float* s, int64_
                                           int32_t max_iters, float tol, dash_prec prec, float* X, float* monitor,
                                           int32_t* steps, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   if (!monitor || !(tol >= 0.f && tol < INFINITY) || (steps && !aligned(steps, 4))) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (prec == DASH_FP16) return DASH_ERR_UNSUPPORTED;
   Stop stop;
   stop.tol = tol;
   stop.steps = steps;

@@ -68,6 +68,23 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmArgs& a, bool sym) {
   return c;
 }
 
+// Block-interleaved variant for launches whose blocks carry unequal work (some blocks of an adaptive
+// solve have stopped): XCD x takes the blocks b = x (mod 8), each with all of its (problem, tile)
+// items in a row, so stopped and running blocks spread evenly over the XCDs whatever their order
+// in the stack.  The grid is padded to a multiple of 8 blocks (launch_interleaved); false for the
+// padding.  Full (non-triangle) products only.
+__device__ __forceinline__ bool decode_tile_interleaved(const GemmArgs& a, TileCoord& c) {
+  const int64_t w = blockIdx.x, x = w & 7, slot = w >> 3;
+  const int64_t per_block = (int64_t)a.nprob * a.tiles;
+  c.b = 8 * (slot / per_block) + x;
+  const int item = (int)(slot % per_block);
+  c.prob = item / a.tiles;
+  const int t = item - c.prob * a.tiles;
+  c.ti = t / a.tdim;
+  c.tj = t - c.ti * a.tdim;
+  return c.b < a.N;
+}
+
 // Operand map of the binary16 products: the 8 consecutive elements Z[row][col0 .. col0 + 7] of a
 // staged chunk become a Z + g I.  a is a power of two (the callers' -1/4), so a z is exact unless it
 // is subnormal, and the diagonal element a z + g is rounded once (an exact a z below the half-ulp
@@ -313,6 +330,14 @@ hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream, int threads =
   const int64_t grid = (int64_t)a.nprob * a.N * a.tiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename K>
+hipError_t launch_interleaved(K kernel, const GemmArgs& a, hipStream_t stream) {
+  const int64_t grid = (a.N + 7) / 8 * 8 * a.nprob * a.tiles;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -34,7 +34,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   float(*As)[TILE * LDA] = reinterpret_cast<float(*)[TILE * LDA]>(smem);
   float(*Bs)[BK * LDB] = reinterpret_cast<float(*)[BK * LDB]>(smem + 2 * TILE * LDA * 4);
 
-  const TileCoord tc = decode_tile(a, SYM);
+  TileCoord tc;
+  if constexpr (FRZ) {
+    if (!decode_tile_interleaved(a, tc)) return;
+  } else {
+    tc = decode_tile(a, SYM);
+  }
   Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -209,7 +214,7 @@ hipError_t dispatch_f32(GemmArgs& a, Trans trans, bool sym, bool c_is_y, hipStre
     if (sym && c_is_y) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, true>, a, stream);
     if (sym) return launch(gemm_f32_kernel<TILE, 0, 0, true, float, CHECKS, false>, a, stream);
     if (a.p0.freeze || (a.nprob > 1 && a.p1.freeze))
-      return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false, false, true>, a, stream);
+      return launch_interleaved(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false, false, true>, a, stream);
     return launch(gemm_f32_kernel<TILE, 0, 0, false, float, CHECKS, false>, a, stream);
   }
   if (!sym) return hipErrorInvalidValue;

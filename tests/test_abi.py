@@ -182,3 +182,21 @@ def test_evd_argument_errors_and_counts():
     expect = 7 * (Bf // 32 - 1) * per_round * Nf + 2 * Bf ** 3 * Nf * tri
     assert dash.dash_flops(dash.DASH_OP_EVD, Nf, Bf, dash.DASH_FP32, 7, 0) == pytest.approx(expect)
     assert dash.dash_flops(dash.DASH_OP_EVD, Nf, Bf, dash.DASH_FP32, 0, 0) == -1.0
+
+
+def test_adaptive_argument_errors():
+    N, B = 4, 64
+    ws = FakeWs(P3, 1 << 30)
+    f = dash.dash_inverse_root_ndb_adaptive
+    assert _status_of(f, P, P2, N, B, 8, 8, 1e-5, 5 * P, None, ws=ws) == _lib.DASH_ERR_INVALID_ARG    # no monitor
+    assert _status_of(f, P, P2, N, B, 8, 8, -1.0, 5 * P, 6 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG   # tol < 0
+    assert _status_of(f, P, P2, N, B, 8, 8, float("nan"), 5 * P, 6 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, N, B, 0, 8, 1e-5, 5 * P, 6 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG   # max1 < 1
+    assert _status_of(f, P, P2, N, B, 8, 8, 1e-5, 5 * P, 6 * P,
+                      ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
+    g = dash.dash_inverse_root_cn_adaptive
+    assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, dash.DASH_FP32, 5 * P, None, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, dash.DASH_FP16, 5 * P, 6 * P,
+                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                          # fp16 not adaptive
+    assert _status_of(g, P, P2, N, B, 3, 8, 1e-5, dash.DASH_FP32, 5 * P, 6 * P,
+                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                          # p != 4
