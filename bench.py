@@ -429,6 +429,31 @@ def only_adaptive(dash, di, torch, dev):
                       "speedup": round(ms_f / ms_a, 3), "mean_steps_kappa5": float(st[:h].mean()),
                       "mean_steps_kappa500": float(st[h:].mean()), "residual_adaptive": r_a, "residual_fixed": r_f,
                       "status_nonzero": int((status != 0).sum())}
+    del ws, mon, steps
+    torch.cuda.empty_cache()
+    # CN with binary16 iterates after binary16 power-iteration scaling, stopped at the fp16 gate
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP16, K_VEC, MPI_STEPS, V0, s, ws)
+    del ws
+    MC, tol16 = 16, 5e-3
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_FP16, device=dev)
+    mon = torch.empty((N, MC), device=dev)
+    steps = torch.empty(N, dtype=torch.int32, device=dev)
+    run_a = lambda: dash.dash_inverse_root_cn_adaptive(A, s, N, B, 4, MC, tol16, dash.DASH_FP16, X, mon,
+                                                       steps=steps, status=status, ws=ws)
+    run_a()
+    ms_a = timed(run_a)
+    st = steps.cpu().numpy()
+    r_a = [evd_residual(torch, A, X, b) for b in sample]
+    T = int(st.max())
+    run_f = lambda: dash.dash_inverse_root_cn(A, s, N, B, 4, T, dash.DASH_FP16, X, status=status, ws=ws)
+    run_f()
+    ms_f = timed(run_f)
+    r_f = [evd_residual(torch, A, X, b) for b in sample]
+    out["cn_fp16"] = {"tol": tol16, "adaptive_ms": round(ms_a, 1), "fixed_ms": round(ms_f, 1), "fixed_steps": T,
+                      "speedup": round(ms_f / ms_a, 3), "mean_steps_kappa5": float(st[:h].mean()),
+                      "mean_steps_kappa500": float(st[h:].mean()), "residual_adaptive": r_a, "residual_fixed": r_f,
+                      "status_nonzero": int((status != 0).sum())}
     print(json.dumps(out), flush=True)
 
 

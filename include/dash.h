@@ -144,7 +144,9 @@ dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int3
  * max_iters*: the step limits (as iters* above).  tol >= 0.  monitor is required ([N, max1 + max2]
  * for NDB, [N, max_iters] for CN); its entries after a block stopped are 0.
  * steps: NULL or [N, 2] (NDB: steps run by call 1 and call 2) / [N] (CN): the steps each block ran.
- * CN: prec == DASH_FP32 only (DASH_FP16 -> DASH_ERR_UNSUPPORTED).  Other arguments as above. */
+ * CN takes both precisions (with binary16 iterates a stopped block's X_k is the stored binary16
+ * iterate, so its output carries one binary16 rounding more than a fixed run ending at step k).
+ * Other arguments as above. */
 dash_status dash_inverse_root_ndb_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t max_iters1,
                                            int32_t max_iters2, float tol, float* X, float* sqrt_out, float* monitor,
                                            int32_t* steps, int32_t* status, void* ws, size_t ws_bytes,

@@ -251,8 +251,10 @@ dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) 
 // S_k = (5I - M_k)/4 is never stored: every product that takes S_k reads M_k and maps it as it is
 // staged (operand map -1/4 Z + 5/4 I, the same single rounding a binary16 elementwise pass would
 // apply), and X_1 = S_0 is likewise M_0 mapped.  M_0 stays alive until X_2 has been formed.
+// freeze (optional, adaptive): a block whose monitor ||M_k - I|| is <= tol before step k >= 1 keeps
+// X_k from then on (its later products are skipped or pass X through).
 dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* status, const float* coef, void* M0,
-                    Pool& pool, hipStream_t st) {
+                    Pool& pool, hipStream_t st, int32_t* freeze, float tol, int32_t* steps) {
   auto mapped = [](Product p, bool mx, bool my) {
     p.map_x = mx;
     p.map_y = my;
@@ -260,15 +262,22 @@ dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* 
     p.map_g = 1.25f;
     return p;
   };
+  auto frozen = [&](Product p, int8_t pass) {
+    p.freeze = freeze;
+    p.pass = pass;
+    return p;
+  };
   void* M = M0;
   void* Xk = nullptr;  // null while X_k = S_0 (k = 1) is M_0 mapped
   for (int k = 0; k < T; ++k) {
+    if (freeze && k >= 1)  // monitor column k (||M_k - I||) is complete
+      TRY(launch_freeze_update(monitor, T, k, B, tol, freeze, steps, 1, k, N, st));
     if (k == T - 1) {  // X_T = s^{-1/4} X_{T-1} S_{T-1}, fp32 output
       Epilogue e;
       e.ia = CO_U;
       e.coef = coef;
       e.status = status;
-      Product pr = mapped(prod(Xk ? Xk : M0, M, X), Xk == nullptr, true);
+      Product pr = frozen(mapped(prod(Xk ? Xk : M0, M, X), Xk == nullptr, true), 1);
       TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP32, Trans::NN, true, e, st, true));
       break;
     }
@@ -278,14 +287,15 @@ dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* 
       TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S_k and S_k^2 in one launch
       void* Xn = pool.get();
-      Product pr[2] = {mapped(prod(Xk ? Xk : M0, M, Xn), Xk == nullptr, true), mapped(prod(M, M, S2), true, true)};
+      Product pr[2] = {frozen(mapped(prod(Xk ? Xk : M0, M, Xn), Xk == nullptr, true), 1),
+                       frozen(mapped(prod(M, M, S2), true, true), 0)};
       TRY(launch_gemm(pr, 2, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
       pool.put(Xk ? Xk : M0);  // X_k (or M_0, whose last use as X_1 this was) is dead
       Xk = Xn;
     }
     void* S4 = pool.get();
     {
-      Product pr = prod(S2, S2, S4);
+      Product pr = frozen(prod(S2, S2, S4), 0);
       TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
     }
     pool.put(S2);
@@ -295,7 +305,7 @@ dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* 
       e.mon_stride = T;
     }
     void* Mn = pool.get();
-    Product pr = prod(M, S4, Mn);
+    Product pr = frozen(prod(M, S4, Mn), 0);
     TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, e, st, true));
     if (M != M0) pool.put(M);  // M_0 is released with X_1 above
     pool.put(S4);
@@ -563,9 +573,9 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   const int T = iters;
-  // adaptive stopping (fp32): a block whose monitor ||M_k - I|| is <= tol before step k >= 1
-  // keeps X_k from then on
-  if (stop.tol >= 0.f) {  // fp32 only (checked by the caller before anything was enqueued)
+  // adaptive stopping: a block whose monitor ||M_k - I|| is <= tol before step k >= 1 keeps X_k
+  // from then on
+  if (stop.tol >= 0.f) {
     TRY(launch_freeze_reset(freeze, stop.steps, 1, T, N, st));
   } else {
     freeze = nullptr;
@@ -591,7 +601,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
     }
     // built from the upper triangle of A: every later right operand is then exactly symmetric
     TRY(launch_sym_affine(m0, N, B, st));
-    return cn_half(N, B, T, X, monitor, status, coef, M, pool, st);
+    return cn_half(N, B, T, X, monitor, status, coef, M, pool, st, freeze, stop.tol, stop.steps);
   }
   {
     Affine s0;
@@ -719,8 +729,6 @@ dash_status dash_inverse_root_cn_adaptive(const float* A, const float* s, int64_
                                           int32_t max_iters, float tol, dash_prec prec, float* X, float* monitor,
                                           int32_t* steps, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   if (!monitor || !(tol >= 0.f && tol < INFINITY) || (steps && !aligned(steps, 4))) return DASH_ERR_INVALID_ARG;
-  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
-  if (prec == DASH_FP16) return DASH_ERR_UNSUPPORTED;
   Stop stop;
   stop.tol = tol;
   stop.steps = steps;

@@ -60,7 +60,8 @@ struct Epilogue {
 // while it is staged.  Binary16 operands (map_ia unused): map_a must be a power of two (each element
 // is then the exact value rounded once to binary16).  fp32 operands: only map_y, in the Clenshaw
 // launches (fold_c), one fma per element.
-// freeze (optional, [N], fp32 NN full products only): a block b with freeze[b] != 0 has stopped
+// freeze (optional, [N]; fp32 full NN products and binary16 triangle-only NN products): a block b
+// with freeze[b] != 0 has stopped
 // iterating.  Its product is not computed: pass = 0 writes nothing, pass = 1 / 2 writes the
 // epilogue applied to X_b / Y_b in place of X_b Y_b (the iterate goes through unchanged).
 struct Product {

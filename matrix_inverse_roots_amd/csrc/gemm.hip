@@ -47,9 +47,9 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // (fp32: every problem of the launch maps its Y)
   if (maps && in_prec == DASH_FP32 && (map_x || !epi.fold_c || (nprob > 1 && probs[0].map_y != probs[1].map_y)))
     return hipErrorInvalidValue;
-  // frozen blocks are handled by the fp32 full NN kernel only
+  // stopped blocks are handled by the fp32 full NN kernel and the binary16 triangle-only kernels
   const bool frz = probs[0].freeze || (nprob > 1 && probs[1].freeze);
-  if (frz && (in_prec != DASH_FP32 || sym || trans != Trans::NN || epi.fold_c)) return hipErrorInvalidValue;
+  if (frz && (trans != Trans::NN || epi.fold_c || (in_prec == DASH_FP32) == sym)) return hipErrorInvalidValue;
   if (probs[0].pass < 0 || probs[0].pass > 2 || (nprob > 1 && (probs[1].pass < 0 || probs[1].pass > 2)))
     return hipErrorInvalidValue;
   if (in_prec == DASH_FP32) {

@@ -45,6 +45,22 @@ struct TileCoord {
   int ti, tj;
 };
 
+// (row, column) of tile t of a block: all tiles row by row, or the upper triangle row by row (sym)
+__device__ __forceinline__ void tile_rc(const GemmArgs& a, bool sym, int t, int& ti, int& tj) {
+  if (sym) {
+    int r = 0;
+    while (t >= a.tdim - r) {
+      t -= a.tdim - r;
+      ++r;
+    }
+    ti = r;
+    tj = r + t;
+  } else {
+    ti = t / a.tdim;
+    tj = t - ti * a.tdim;
+  }
+}
+
 __device__ __forceinline__ TileCoord decode_tile(const GemmArgs& a, bool sym) {
   const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t per_prob = a.N * a.tiles;
@@ -52,19 +68,7 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmArgs& a, bool sym) {
   c.prob = (int)(lid / per_prob);
   const int64_t rem = lid - (int64_t)c.prob * per_prob;
   c.b = rem / a.tiles;
-  int t = (int)(rem - c.b * a.tiles);
-  if (sym) {
-    int ti = 0;
-    while (t >= a.tdim - ti) {
-      t -= a.tdim - ti;
-      ++ti;
-    }
-    c.ti = ti;
-    c.tj = ti + t;
-  } else {
-    c.ti = t / a.tdim;
-    c.tj = t - c.ti * a.tdim;
-  }
+  tile_rc(a, sym, (int)(rem - c.b * a.tiles), c.ti, c.tj);
   return c;
 }
 
@@ -72,16 +76,14 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmArgs& a, bool sym) {
 // solve have stopped): XCD x takes the blocks b = x (mod 8), each with all of its (problem, tile)
 // items in a row, so stopped and running blocks spread evenly over the XCDs whatever their order
 // in the stack.  The grid is padded to a multiple of 8 blocks (launch_interleaved); false for the
-// padding.  Full (non-triangle) products only.
-__device__ __forceinline__ bool decode_tile_interleaved(const GemmArgs& a, TileCoord& c) {
+// padding.
+__device__ __forceinline__ bool decode_tile_interleaved(const GemmArgs& a, bool sym, TileCoord& c) {
   const int64_t w = blockIdx.x, x = w & 7, slot = w >> 3;
   const int64_t per_block = (int64_t)a.nprob * a.tiles;
   c.b = 8 * (slot / per_block) + x;
   const int item = (int)(slot % per_block);
   c.prob = item / a.tiles;
-  const int t = item - c.prob * a.tiles;
-  c.ti = t / a.tdim;
-  c.tj = t - c.ti * a.tdim;
+  tile_rc(a, sym, item - c.prob * a.tiles, c.ti, c.tj);
   return c.b < a.N;
 }
 
@@ -334,11 +336,38 @@ hipError_t launch(K kernel, const GemmArgs& a, hipStream_t stream, int threads =
 }
 
 template <typename K>
-hipError_t launch_interleaved(K kernel, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_interleaved(K kernel, const GemmArgs& a, hipStream_t stream, int threads = 256) {
   const int64_t grid = (a.N + 7) / 8 * 8 * a.nprob * a.tiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
+}
+
+// A stopped block of an adaptive solve (binary16 operands): the accumulators take the operand that
+// passes through (X for pass 1, Y for pass 2) at the tile's positions, mapped exactly as the product
+// would have staged it (operand_map's arithmetic, element by element).
+template <int MTM, int MTN, int WTM, int WTN>
+__device__ __forceinline__ void pass_tile_f16(const Product& P, const _Float16* X, const _Float16* Y, int B, int i0,
+                                              int j0, int wm, int wn, int lane, f32x16 (&acc)[MTM][MTN]) {
+  const _Float16* Z = P.pass == 1 ? X : Y;
+  const bool map = P.pass == 1 ? P.map_x : P.map_y;
+  const _Float16 ma = (_Float16)P.map_a, mg = (_Float16)P.map_g;
+  const int li = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = j0 + wn * WTN + nt * 32 + li;
+        _Float16 z = Z[(int64_t)i * B + j];
+        if (map) {
+          z = z * ma;
+          if (i == j) z = z + mg;
+        }
+        acc[mt][nt][r] = (float)z;
+      }
 }
 
 // kernel launchers of the two precisions

@@ -10,7 +10,7 @@ namespace dash {
 namespace gemm {
 namespace {
 
-template <int TILE, bool SYM, typename TO, bool CHECKS>
+template <int TILE, bool SYM, typename TO, bool CHECKS, bool FRZ = false>
 __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   constexpr int BK = 64;
   constexpr int WT = TILE / 2;
@@ -22,7 +22,12 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   _Float16(*As)[TILE * LD] = reinterpret_cast<_Float16(*)[TILE * LD]>(smem);
   _Float16(*Bs)[TILE * LD] = reinterpret_cast<_Float16(*)[TILE * LD]>(smem + 2 * TILE * LD * 2);
 
-  const TileCoord tc = decode_tile(a, SYM);
+  TileCoord tc;
+  if constexpr (FRZ) {
+    if (!decode_tile_interleaved(a, SYM, tc)) return;
+  } else {
+    tc = decode_tile(a, SYM);
+  }
   const Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -32,6 +37,19 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, h = lane >> 5;
+
+  if constexpr (FRZ) {  // a block that stopped iterating: pass an operand through, or write nothing
+    if (P.freeze && P.freeze[tc.b]) {
+      if (P.pass == 0) return;
+      f32x16 pz[MT][MT];
+      pass_tile_f16<MT, MT, WT, WT>(P, X, Y, B, i0, j0, wm, wn, lane, pz);
+      if constexpr (sizeof(TO) == 2)
+        epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, pz, wm, wn, lane, smem);
+      else
+        epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, pz, wm, wn, lane);
+      return;
+    }
+  }
 
   f16x8 ra[NL], rb[NL];
   auto gload = [&](int k0) {
@@ -114,7 +132,7 @@ using IC = std::integral_constant<int, V>;
 
 __device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 1)) & 3; }
 
-template <bool SYM, typename TO, bool CHECKS, int NW>
+template <bool SYM, typename TO, bool CHECKS, int NW, bool FRZ = false>
 __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
   // NW = 4: 2 x 2 waves of 128 x 128; NW = 8: 2 x 4 waves of 128 x 64 (two waves per SIMD)
   constexpr int NT = 64 * NW;
@@ -129,7 +147,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
   _Float16* Xs = (_Float16*)smem;  // [2][SLICE]
   _Float16* Ys = Xs + 2 * SLICE;   // [2][SLICE]
 
-  const TileCoord tc = decode_tile(a, SYM);
+  TileCoord tc;
+  if constexpr (FRZ) {
+    if (!decode_tile_interleaved(a, SYM, tc)) return;
+  } else {
+    tc = decode_tile(a, SYM);
+  }
   const Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -139,6 +162,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int li = lane & 31, h = lane >> 5;
+
+  if constexpr (FRZ) {  // a block that stopped iterating: pass an operand through, or write nothing
+    if (P.freeze && P.freeze[tc.b]) {
+      if (P.pass == 0) return;
+      f32x16 pz[MTM][MTN];
+      pass_tile_f16<MTM, MTN, WTM, WTN>(P, X, Y, B, i0, j0, wm, wn, lane, pz);
+      if constexpr (sizeof(TO) == 2)
+        epilogue_staged_f16<MTM, MTN, WTM, WTN, SYM, TILE, CHECKS>(a, tc, P, pz, wm, wn, lane, smem);
+      else
+        epilogue<MTM, MTN, WTM, WTN, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, pz, wm, wn, lane);
+      return;
+    }
+  }
 
   // per k-step each thread moves NP pieces of 16 bytes of each slice: piece c = tid + NT r -> row
   // c / 4, chunk c % 4 (rows i0.. of X and rows j0.. of Y, k0 .. k0 + 31)
@@ -248,6 +284,19 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t
   const bool half_out = out_prec == DASH_FP16;
   // eight waves (two per SIMD: one wave's barrier and LDS latency are hidden behind the other's
   // MFMAs)
+  // launches that carry stopped blocks of an adaptive solve (triangle-only products only)
+  if constexpr (SYM) {
+    if (a.p0.freeze || (a.nprob > 1 && a.p1.freeze)) {
+      if (tile == 256)
+        return half_out ? launch_interleaved(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8, true>, a, stream, 512)
+                        : launch_interleaved(gemm_f16_ysym_kernel<SYM, float, CHECKS, 8, true>, a, stream, 512);
+      if (tile == 128)
+        return half_out ? launch_interleaved(gemm_f16_kernel<128, SYM, _Float16, CHECKS, true>, a, stream)
+                        : launch_interleaved(gemm_f16_kernel<128, SYM, float, CHECKS, true>, a, stream);
+      return half_out ? launch_interleaved(gemm_f16_kernel<64, SYM, _Float16, CHECKS, true>, a, stream)
+                      : launch_interleaved(gemm_f16_kernel<64, SYM, float, CHECKS, true>, a, stream);
+    }
+  }
   if (tile == 256)
     return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8>, a, stream, 512)
                     : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS, 8>, a, stream, 512);

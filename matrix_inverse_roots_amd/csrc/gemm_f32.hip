@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
 
   TileCoord tc;
   if constexpr (FRZ) {
-    if (!decode_tile_interleaved(a, tc)) return;
+    if (!decode_tile_interleaved(a, SYM, tc)) return;
   } else {
     tc = decode_tile(a, SYM);
   }

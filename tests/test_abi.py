@@ -196,7 +196,6 @@ def test_adaptive_argument_errors():
                       ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
     g = dash.dash_inverse_root_cn_adaptive
     assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, dash.DASH_FP32, 5 * P, None, ws=ws) == _lib.DASH_ERR_INVALID_ARG
-    assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, dash.DASH_FP16, 5 * P, 6 * P,
-                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                          # fp16 not adaptive
+    assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, 7, 5 * P, 6 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG  # bad prec
     assert _status_of(g, P, P2, N, B, 3, 8, 1e-5, dash.DASH_FP32, 5 * P, 6 * P,
                       ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                          # p != 4

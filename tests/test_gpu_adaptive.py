@@ -111,7 +111,7 @@ def test_cn_adaptive_mixed_stack(mixed, tol):
     assert np.all(residual(X, A) <= max(2 * tol, R_FP32))
 
 
-def test_cn_adaptive_zero_tol_is_the_fixed_call_and_fp16_unsupported(mixed):
+def test_cn_adaptive_zero_tol_is_the_fixed_call(mixed):
     A, s = mixed
     Xa, mon, steps, _ = cn_adaptive(to_dev(A), to_dev(s), 9, 0.0)
     Xf, _, _ = cn(to_dev(A), to_dev(s), 9)
@@ -119,6 +119,28 @@ def test_cn_adaptive_zero_tol_is_the_fixed_call_and_fp16_unsupported(mixed):
     mon, steps = to_host(mon), to_host(steps).astype(int)
     for b in range(len(A)):
         stopped_only_at_exact_fixed_points(mon[b], steps[b], 9)
-    with pytest.raises(dash.DashError) as ei:
-        cn_adaptive(to_dev(A), to_dev(s), 9, 1e-4, dash.DASH_FP16)
-    assert ei.value.status == dash._lib.DASH_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B16", [128, 256])
+def test_cn_adaptive_binary16(B16):
+    """Binary16 iterates (128- and 256-wide tile kernels): the rule on the GPU's own monitors; each
+    block's result equals the fixed binary16 run of its length up to the one binary16 rounding of
+    the stored X_k, and (for condition numbers up to 100) the exact fp64 oracle run of its length to
+    binary16 accuracy, with the residual at the monitor's level."""
+    A = np.concatenate([di.known_spectrum_stack(200 + i, 1, B16, lm, 1.0)[0] for i, lm in enumerate(LAM_MIN)])
+    A = A.astype(np.float32)
+    s = np.ones(len(A), dtype=np.float32)
+    T, tol = 20, 1e-2
+    X, mon, steps, status = cn_adaptive(to_dev(A), to_dev(s), T, tol, dash.DASH_FP16)
+    assert (to_host(status) == 0).all()
+    mon, steps, X = to_host(mon), to_host(steps).astype(int), to_host(X)
+    for b in range(len(A)):
+        check_rule(mon[b], steps[b], tol, T)
+        Xf16, _, _ = cn(to_dev(A[b:b + 1]), to_dev(s[b:b + 1]), int(steps[b]), dash.DASH_FP16)
+        assert rel_err(X[b], to_host(Xf16)[0])[0] <= 2e-3
+        if LAM_MIN[b] >= 1e-2:  # binary16 storage error grows with the condition number
+            Xo, _ = oracle.cn_inverse_root(A[b], 1.0, int(steps[b]))
+            assert rel_err(X[b], Xo)[0] <= 5e-3
+    assert np.all(np.diff(steps) >= 0) and steps[0] < steps[-1]
+    well = np.array(LAM_MIN) >= 1e-2  # where binary16 storage keeps the monitor close to the residual
+    assert np.all(residual(X[well], A[well]) <= 2.5 * tol)
