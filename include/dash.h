@@ -119,6 +119,22 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
                                   int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* NDB with binary16 iterates and an fp32 correction ([PT] Resultados Experimentais: NDB in FP16/BF16
+ * was unstable in the authors' runs; [PT] Significância e Alegações, "Direções Futuras": stabilising
+ * NDB in lower precision with error correction is named as future work).  The two composed NDB calls
+ * run as in dash_inverse_root_ndb, with binary16 operands and fp32 accumulation, every stored
+ * iterate rounded to binary16 once (M = A_i/s_i included; the second call's last Z is kept in fp32).
+ * Then up to `refine` guarded correction steps against A_s = A_i/s_i in fp32: the candidate is a
+ * Newton step for the inverse fourth root followed by symmetrisation, X_c = sym(X (5I - X^4 A_s)/4),
+ * and a block takes it only if it lowers the block's residual ||X^4 A_s - I||_F (four fp32 products
+ * per step and three to start); at its first candidate that does not, the block keeps its X and
+ * stops correcting (the Newton step is contractive for well-conditioned blocks, kappa of order 10,
+ * and diverges beyond).  X_i = s_i^{-1/4} X.  0 <= refine <= 16.  Workspace: dash_workspace_size(DASH_OP_NDB, ...,
+ * DASH_FP16, ...).  Other arguments as for dash_inverse_root_ndb (no square-root output). */
+dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, int32_t refine, float* X, float* monitor, int32_t* status,
+                                       void* ws, size_t ws_bytes, void* stream);
+
 /* Inverse p-th root by the Coupled-Newton iteration, p = 4 ([PT] Definição do Problema, item 2;
  * [TG] body, "CN - Coupled Newton Iteration"; fp16 operands per [PT] Resultados Experimentais).
  * On M_0 = A_i / s_i, X_0 = I: S = (5I - M)/4, X <- X S, M <- M S^4 (S^4 = (S S)(S S));

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     dash_inverse_root_evd,
     dash_inverse_root_ndb,
     dash_inverse_root_ndb_adaptive,
+    dash_inverse_root_ndb_half,
     dash_scale,
     dash_solver_products,
     dash_stack,

@@ -49,6 +49,7 @@ def library() -> ctypes.CDLL:
             "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_ndb_half": (st, [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
                                                     vp]),
             "dash_inverse_root_cn_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, st, vp, vp, vp, vp, vp, sz, vp]),
@@ -169,6 +170,14 @@ def dash_inverse_root_cn(A, s, N: int, B: int, p: int, iters: int, prec: int, X,
     _check("dash_inverse_root_cn",
            library().dash_inverse_root_cn(_ptr(A), _ptr(s), N, B, p, iters, prec, _ptr(X), _ptr(monitor),
                                           _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_ndb_half(A, s, N: int, B: int, iters1: int, iters2: int, refine: int, X, monitor=None,
+                               status=None, ws=None, stream=None):
+    _check("dash_inverse_root_ndb_half",
+           library().dash_inverse_root_ndb_half(_ptr(A), _ptr(s), N, B, iters1, iters2, refine, _ptr(X),
+                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws),
+                                                _stream(stream, A)))
 
 
 def dash_inverse_root_ndb_adaptive(A, s, N: int, B: int, max_iters1: int, max_iters2: int, tol: float, X, monitor,

@@ -59,6 +59,15 @@ struct Pool {
 
 size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256); }
 size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32); }
+// binary16 NDB: six binary16 stacks for the iterates, reused as three fp32 stacks by the correction,
+// and per-block flags and residuals of the guarded correction (at most 16 steps)
+size_t ndb_half_region(int64_t N, int B) {
+  const size_t h6 = 6 * stack_bytes(N, B, DASH_FP16), f3 = 3 * stack_bytes(N, B, DASH_FP32);
+  return h6 > f3 ? h6 : f3;
+}
+size_t ws_ndb_half(int64_t N, int B) {
+  return coef_bytes(N) + 2 * flag_bytes(N) + align_up((size_t)N * 17 * sizeof(float), 256) + ndb_half_region(N, B);
+}
 size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, p); }
 size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
@@ -209,6 +218,101 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     p[0].pass = 1;
     p[1].pass = 2;
     TRY(launch_gemm(p, 2, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+    c.pool->put(Y);
+    c.pool->put(Z);
+    c.pool->put(S);
+    Y = Yn;
+    Z = Zn;
+  }
+  return DASH_OK;
+}
+
+// One NDB call with binary16 iterates (fp32 accumulation) on the binary16 stack M: every stored
+// iterate is rounded to binary16 once, by the epilogue that forms it.  Step 0: S_0 = (3I - M)/2 is
+// Z_1 and Y_1 = M S_0.  Returns Y_T (binary16) in *y_out, or (want_z) writes Z_T in fp32 into
+// final_out, scaled by coef[final_ia], with the finite check into status.  Monitor as in ndb_call.
+dash_status ndb_half_call(const NdbCtx& c, void* M, bool m_from_pool, int T, int mon_col, bool want_z,
+                          float* final_out, int8_t final_ia, void** y_out) {
+  const auto H = DASH_FP16;
+  void* Z = c.pool->get();
+  {
+    Affine s0;
+    s0.X = M;
+    s0.x_prec = H;
+    s0.D = Z;
+    s0.d_prec = H;
+    s0.a = -0.5f;
+    s0.g = 1.5f;
+    if (c.monitor) {  // ||P_0 - I||^2 = 4 ||S_0 - I||^2
+      s0.monitor = c.monitor + mon_col;
+      s0.mon_stride = c.mon_cols;
+      s0.mon_mul = 4.f;
+    }
+    TRY(launch_affine(s0, c.N, c.B, c.st));
+  }
+  if (T == 1 && want_z) {  // Z_1 = S_0
+    Affine fin;
+    fin.X = Z;
+    fin.x_prec = H;
+    fin.D = final_out;
+    fin.a = 1.f;
+    fin.ia = final_ia;
+    fin.coef = c.coef;
+    fin.status = c.status;
+    TRY(launch_affine(fin, c.N, c.B, c.st));
+    c.pool->put(Z);
+    if (m_from_pool) c.pool->put(M);
+    return DASH_OK;
+  }
+  void* Y = c.pool->get();
+  {
+    Product p = prod(M, Z, Y);
+    TRY(launch_gemm(&p, 1, c.N, c.B, H, H, Trans::NN, false, Epilogue(), c.st));
+  }
+  if (m_from_pool) c.pool->put(M);
+  if (T == 1) {
+    c.pool->put(Z);
+    *y_out = Y;
+    return DASH_OK;
+  }
+  for (int k = 1; k < T; ++k) {
+    void* S = c.pool->get();
+    {
+      Epilogue e;  // S = (3I - Z Y) / 2, monitor ||Z Y - I|| = 2 ||S - I||
+      e.alpha = -0.5f;
+      e.gamma = 1.5f;
+      if (c.monitor) {
+        e.monitor = c.monitor + mon_col + k;
+        e.mon_stride = c.mon_cols;
+        e.mon_mul = 4.f;
+      }
+      Product p = prod(Z, Y, S);
+      TRY(launch_gemm(&p, 1, c.N, c.B, H, H, Trans::NN, false, e, c.st));
+    }
+    if (k == T - 1) {
+      if (want_z) {
+        Epilogue e;
+        e.ia = final_ia;
+        e.coef = c.coef;
+        e.status = c.status;
+        Product p = prod(S, Z, final_out);
+        TRY(launch_gemm(&p, 1, c.N, c.B, H, DASH_FP32, Trans::NN, false, e, c.st));
+        c.pool->put(Y);
+      } else {
+        void* Yn = c.pool->get();
+        Product p = prod(Y, S, Yn);
+        TRY(launch_gemm(&p, 1, c.N, c.B, H, H, Trans::NN, false, Epilogue(), c.st));
+        c.pool->put(Y);
+        *y_out = Yn;
+      }
+      c.pool->put(Z);
+      c.pool->put(S);
+      return DASH_OK;
+    }
+    void* Yn = c.pool->get();
+    void* Zn = c.pool->get();
+    Product p[2] = {prod(Y, S, Yn), prod(S, Z, Zn)};
+    TRY(launch_gemm(p, 2, c.N, c.B, H, H, Trans::NN, false, Epilogue(), c.st));
     c.pool->put(Y);
     c.pool->put(Z);
     c.pool->put(S);
@@ -393,7 +497,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
       if (k_or_degree < 0 || k_or_degree > 32) return DASH_ERR_INVALID_ARG;
       *bytes = ws_scale(N, B, prec, k_or_degree);
       return DASH_OK;
-    case DASH_OP_NDB: *bytes = ws_ndb(N, B); return DASH_OK;
+    case DASH_OP_NDB: *bytes = prec == DASH_FP16 ? ws_ndb_half(N, B) : ws_ndb(N, B); return DASH_OK;
     case DASH_OP_CN: *bytes = ws_cn(N, B, prec); return DASH_OK;
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
@@ -529,6 +633,109 @@ dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32
 }  // namespace
 
 extern "C" {
+
+dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, int32_t refine, float* X, float* monitor, int32_t* status,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (X == A || iters1 < 1 || iters2 < 1 || iters1 > 1000 || iters2 > 1000 || refine < 0 || refine > 16)
+    return DASH_ERR_INVALID_ARG;
+  if ((monitor && !aligned(monitor, 4)) || (status && !aligned(status, 4))) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_ndb_half(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  int32_t* freeze = (int32_t*)cv.take(flag_bytes(N));
+  int32_t* accept = (int32_t*)cv.take(flag_bytes(N));
+  float* res = (float*)cv.take((size_t)N * 17 * sizeof(float));  // residual sums of squares per step
+  char* region = (char*)cv.take(ndb_half_region(N, B));
+  Pool pool;
+  for (int q = 1; q < 6; ++q) pool.put(region + q * stack_bytes(N, B, DASH_FP16));
+  void* M = region;  // M = h(A / s), the first call's input (not from the pool)
+  const int cols = iters1 + iters2;
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  if (monitor) TRY(launch_fill_f32(monitor, N * cols, 0.f, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  {
+    Affine m;
+    m.X = A;
+    m.D = M;
+    m.d_prec = DASH_FP16;
+    m.a = 1.f;
+    m.ia = CO_R1;
+    m.coef = coef;
+    TRY(launch_affine(m, N, B, st));
+  }
+  NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
+  void* Y = nullptr;
+  dash_status r = ndb_half_call(c, M, false, iters1, 0, false, nullptr, CO_NONE, &Y);
+  if (r != DASH_OK) return r;
+  // the second call's Z_T in fp32: unscaled into X when there is no correction, else the
+  // correction's start
+  r = ndb_half_call(c, Y, true, iters2, iters1, true, X, refine ? CO_NONE : CO_U, nullptr);
+  if (r != DASH_OK) return r;
+  if (monitor) TRY(launch_monitor_finish(monitor, N * cols, B, st));
+  if (!refine) return DASH_OK;
+  // Guarded correction in fp32 against A_s = A / s.  T(X) = (5I - X^4 A_s)/4 carries the residual
+  // ||X^4 A_s - I||^2 = 16 ||T(X) - I||^2 in its epilogue.  A step forms the candidate
+  // sym(X T(X)), evaluates T of it, and a block takes it only if its residual went down; a block
+  // whose residual did not is left at its best X and skips the remaining steps.
+  float* R[3] = {(float*)region, (float*)(region + stack_bytes(N, B, DASH_FP32)),
+                 (float*)(region + 2 * stack_bytes(N, B, DASH_FP32))};
+  TRY(launch_fill_i32(freeze, N, 0, st));
+  TRY(launch_fill_f32(res, N * 17, 0.f, st));
+  auto evaluate = [&](const float* Xe, float* Tout, float* W0, float* W1, int col) -> dash_status {
+    Product p1 = prod(Xe, Xe, W0);
+    p1.freeze = freeze;
+    TRY(launch_gemm(&p1, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+    Product p2 = prod(W0, W0, W1);
+    p2.freeze = freeze;
+    TRY(launch_gemm(&p2, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+    Epilogue e;
+    e.alpha = -0.25f;
+    e.ia = CO_R1;
+    e.gamma = 1.25f;
+    e.coef = coef;
+    e.monitor = res + col;
+    e.mon_stride = 17;
+    e.mon_mul = 16.f;
+    Product p3 = prod(W1, A, Tout);
+    p3.freeze = freeze;
+    TRY(launch_gemm(&p3, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, e, st));
+    return DASH_OK;
+  };
+  float* Tx = R[2];  // T(X)
+  if ((r = evaluate(X, Tx, R[0], R[1], 0)) != DASH_OK) return r;
+  for (int q = 0; q < refine; ++q) {
+    float* Wc = R[0];  // candidate X T(X), then its symmetrised form in Xc
+    float* Xc = R[1];
+    Product p4 = prod(X, Tx, Wc);
+    p4.freeze = freeze;
+    TRY(launch_gemm(&p4, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+    Affine sym;
+    sym.X = Wc;
+    sym.D = Xc;
+    sym.a = 1.f;
+    TRY(launch_sym_affine(sym, N, B, st));
+    // T of the candidate: X_c^2 into R[0] (free again), X_c^4 into the old T(X), T(X_c) into R[0]
+    if ((r = evaluate(Xc, Wc, Wc, Tx, q + 1)) != DASH_OK) return r;
+    TRY(launch_accept(res, 17, q, freeze, accept, Xc, X, N, B, st));
+    // the accepted blocks' T is now in R[0]; the next step reads T from there
+    std::swap(R[0], R[2]);
+    Tx = R[2];
+  }
+  Affine fin;  // X = s^{-1/4} X, finite check (status bit 1)
+  fin.X = X;
+  fin.D = X;
+  fin.a = 1.f;
+  fin.ia = CO_U;
+  fin.coef = coef;
+  fin.status = status;
+  TRY(launch_affine(fin, N, B, st));
+  return DASH_OK;
+}
 
 dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
                                   int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,

@@ -126,6 +126,11 @@ hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t s
 // frozen and steps[b * steps_stride] = step.
 hipError_t launch_freeze_reset(int32_t* freeze, int32_t* steps, int steps_stride, int T, int64_t N,
                                hipStream_t stream);
+// Guarded correction step (binary16 NDB): per block, take the candidate src[b] into dst[b] when its
+// residual (monitor column q + 1) is below the current one (column q), else stop the block
+// (freeze[b] = 1).  accept: [N] scratch.
+hipError_t launch_accept(const float* mon, int mon_stride, int q, int32_t* freeze, int32_t* accept, const float* src,
+                         float* dst, int64_t N, int B, hipStream_t stream);
 hipError_t launch_freeze_update(const float* monitor, int mon_stride, int col, int B, float tol, int32_t* freeze,
                                 int32_t* steps, int steps_stride, int step, int64_t N, hipStream_t stream);
 

@@ -336,6 +336,43 @@ hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t s
   return hipGetLastError();
 }
 
+// Guarded correction: block b takes its candidate (accept[b] = 1) when the candidate's residual
+// (monitor column q + 1, a sum of squares) is below the current one (column q); otherwise it stops
+// correcting (freeze[b] = 1).  Stopped blocks are left alone.
+__global__ void accept_kernel(const float* mon, int mon_stride, int q, int32_t* freeze, int32_t* accept, int64_t N) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= N) return;
+  int32_t ok = 0;
+  if (!freeze[b]) {
+    ok = mon[b * mon_stride + q + 1] < mon[b * mon_stride + q];  // NaN compares false: stop
+    if (!ok) freeze[b] = 1;
+  }
+  accept[b] = ok;
+}
+
+// dst[b] = src[b] for the blocks with accept[b] != 0
+__global__ __launch_bounds__(256) void masked_copy_kernel(const float* src, float* dst, const int32_t* accept, int B) {
+  const int64_t chunks = (int64_t)B * B / AFF_CHUNK;
+  const int64_t b = blockIdx.x / chunks;
+  if (!accept[b]) return;
+  const int64_t base = b * (int64_t)B * B + (blockIdx.x - b * chunks) * AFF_CHUNK;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t e = base + 4 * (threadIdx.x + 256 * r);
+    *(f32x4*)(dst + e) = *(const f32x4*)(src + e);
+  }
+}
+
+hipError_t launch_accept(const float* mon, int mon_stride, int q, int32_t* freeze, int32_t* accept, const float* src,
+                         float* dst, int64_t N, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, mon, mon_stride, q,
+                     freeze, accept, N);
+  const int64_t grid = N * ((int64_t)B * B / AFF_CHUNK);
+  if ((int64_t)B * B % AFF_CHUNK != 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(masked_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, accept, B);
+  return hipGetLastError();
+}
+
 hipError_t launch_freeze_reset(int32_t* freeze, int32_t* steps, int steps_stride, int T, int64_t N,
                                hipStream_t stream) {
   hipLaunchKernelGGL(freeze_reset_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, freeze, steps,

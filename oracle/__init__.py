@@ -58,6 +58,7 @@ def _load():
             "orc_ndb_until": (i, [i, _dp, i, d, _dp, _dp, _dp]),
             "orc_ndb_inverse_root_until": (None, [i, _dp, d, i, i, d, _dp, _dp, _dp, _ip]),
             "orc_cn_until": (i, [i, _dp, d, i, i, d, _dp, _dp]),
+            "orc_ndb_half_inverse_root": (None, [i, _dp, d, i, i, i, _dp]),
             "orc_cheb_coeffs": (None, [i, d, d, d, _dp]),
             "orc_clenshaw": (None, [i, _dp, i, _dp, d, d, _dp]),
             "orc_cheb_inverse_root": (None, [i, _dp, d, i, d, d, _dp]),
@@ -292,6 +293,22 @@ def cn_inverse_root_adaptive(A, s, max_iters: int, tol: float, threads: int | No
     _over_blocks(one, N, threads)
     mon = mon[:, :max_iters]
     return (X[0], mon[0], steps[0]) if single else (X, mon, steps)
+
+
+def ndb_half_inverse_root(A, s, iters1: int, iters2: int, refine: int = 0, threads: int | None = None):
+    """Composed NDB root with binary16 iterates, then `refine` Newton correction steps against A_s
+    (each followed by symmetrisation).  Returns X (N, B, B)."""
+    A, single = _as_stack(A)
+    N, n, _ = A.shape
+    s = _per_block(s, N)
+    X = np.empty_like(A)
+    lib = _load()
+
+    def one(b):
+        lib.orc_ndb_half_inverse_root(n, _p(A[b]), float(s[b]), int(iters1), int(iters2), int(refine), _p(X[b]))
+
+    _over_blocks(one, N, threads)
+    return X[0] if single else X
 
 
 def cheb_coeffs(degree: int, lo: float, hi: float, expo: float = -0.25) -> np.ndarray:

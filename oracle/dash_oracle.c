@@ -351,6 +351,106 @@ void orc_ndb_inverse_root(int n, const double* A, double s, int T1, int T2, doub
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * NDB with binary16 iterates and an fp32-precision correction ([PT] Resultados Experimentais: NDB in
+ * FP16/BF16 was found unstable; [PT] Significância e Alegações, "Direções Futuras": stabilising NDB
+ * in lower precision with error correction is named as future work).  Reading: the products are
+ * exact (fp32 accumulation on the GPU) and every stored iterate is rounded to binary16:
+ *     M = h(A/s);  call(M, T): S = h(1.5 I - 0.5 M), Z = S, Y = h(M S);
+ *                  for k = 1 .. T-1: S = h(1.5 I - 0.5 Z Y), Y = h(Y S), Z = h(S Z),
+ * composed as for c5 (call 1 on M gives Y, call 2 on that Y gives Z), except that the last Z of
+ * call 2 is kept unrounded.  Then up to `refine` guarded correction steps against the unrounded
+ * A_s = A/s: the candidate is a Newton step for the inverse fourth root followed by symmetrisation,
+ *     X_c = sym(X (5 I - X^4 A_s) / 4),   sym(W) = (W + W^T) / 2,
+ * taken only if it lowers the residual ||X^4 A_s - I||_F; at the first candidate that does not, the
+ * correction stops (the Newton step is not contractive for every spectrum).  X = s^{-1/4} X.
+ * h() rounds to binary16 (orc_round_binary16).
+ * ---------------------------------------------------------------------------------------------- */
+static void round16_all(size_t nn, double* x) {
+  for (size_t e = 0; e < nn; ++e) x[e] = orc_round_binary16(x[e]);
+}
+
+/* one binary16 NDB call; *Yout / *Zout receive Y_T / Z_T (Z_T unrounded when keep_z_exact) */
+static void ndb_half_call(int n, const double* M, int T, int keep_z_exact, double* Y, double* Z) {
+  const size_t nn = (size_t)n * n;
+  double* S = (double*)malloc(sizeof(double) * nn);
+  double* P = (double*)malloc(sizeof(double) * nn);
+  double* T1 = (double*)malloc(sizeof(double) * nn);
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = (i == j ? 1.5 : 0.0) - 0.5 * M[IDX(i, j, n)];
+  round16_all(nn, S);
+  memcpy(Z, S, sizeof(double) * nn);
+  orc_matmul(n, M, S, Y);
+  round16_all(nn, Y);
+  for (int k = 1; k < T; ++k) {
+    orc_matmul(n, Z, Y, P);
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = (i == j ? 1.5 : 0.0) - 0.5 * P[IDX(i, j, n)];
+    round16_all(nn, S);
+    orc_matmul(n, Y, S, T1);
+    round16_all(nn, T1);
+    memcpy(Y, T1, sizeof(double) * nn);
+    orc_matmul(n, S, Z, T1);
+    if (!(keep_z_exact && k == T - 1)) round16_all(nn, T1);
+    memcpy(Z, T1, sizeof(double) * nn);
+  }
+  free(S);
+  free(P);
+  free(T1);
+}
+
+void orc_ndb_half_inverse_root(int n, const double* A, double s, int T1, int T2, int refine, double* X) {
+  const size_t nn = (size_t)n * n;
+  double* As = (double*)malloc(sizeof(double) * nn);
+  double* M = (double*)malloc(sizeof(double) * nn);
+  double* Y = (double*)malloc(sizeof(double) * nn);
+  double* Z = (double*)malloc(sizeof(double) * nn);
+  double* X2 = (double*)malloc(sizeof(double) * nn);
+  double* X4 = (double*)malloc(sizeof(double) * nn);
+  double* Mr = (double*)malloc(sizeof(double) * nn);
+  for (size_t e = 0; e < nn; ++e) As[e] = A[e] / s;
+  for (size_t e = 0; e < nn; ++e) M[e] = orc_round_binary16(As[e]);
+  ndb_half_call(n, M, T1, 0, Y, Z);
+  memcpy(M, Y, sizeof(double) * nn);
+  ndb_half_call(n, M, T2, 1, Y, Z);
+  /* T = (5I - X^4 A_s)/4 of the current X (in Mr) and its residual ||X^4 A_s - I|| = 4 ||T - I|| */
+  double* Xc = (double*)malloc(sizeof(double) * nn);
+  double* Tc = (double*)malloc(sizeof(double) * nn);
+#define EVAL_T(Xin, Tout, rout)                                                                    \
+  do {                                                                                             \
+    orc_matmul(n, (Xin), (Xin), X2);                                                               \
+    orc_matmul(n, X2, X2, X4);                                                                     \
+    orc_matmul(n, X4, As, (Tout));                                                                 \
+    for (int i = 0; i < n; ++i)                                                                    \
+      for (int j = 0; j < n; ++j) (Tout)[IDX(i, j, n)] = ((i == j ? 5.0 : 0.0) - (Tout)[IDX(i, j, n)]) / 4.0; \
+    (rout) = 4.0 * dist_to_identity(n, (Tout));                                                    \
+  } while (0)
+  double r_cur = 0.0, r_c = 0.0;
+  if (refine > 0) EVAL_T(Z, Mr, r_cur);
+  for (int r = 0; r < refine; ++r) {
+    orc_matmul(n, Z, Mr, X2);
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < n; ++j) Xc[IDX(i, j, n)] = 0.5 * (X2[IDX(i, j, n)] + X2[IDX(j, i, n)]);
+    EVAL_T(Xc, Tc, r_c);
+    if (!(r_c < r_cur)) break;
+    memcpy(Z, Xc, sizeof(double) * nn);
+    memcpy(Mr, Tc, sizeof(double) * nn);
+    r_cur = r_c;
+  }
+#undef EVAL_T
+  free(Xc);
+  free(Tc);
+  const double u = pow(s, -0.25);
+  for (size_t e = 0; e < nn; ++e) X[e] = u * Z[e];
+  free(As);
+  free(M);
+  free(Y);
+  free(Z);
+  free(X2);
+  free(X4);
+  free(Mr);
+}
+
+/* ------------------------------------------------------------------------------------------------
  * c6: Coupled-Newton iteration for the inverse p-th root, p = 4 ([PT] Definição do Problema,
  * item 2; [TG] body, "CN - Coupled Newton Iteration").
  * Reading: the coupled Newton iteration of Guo and Higham (2006) with c = 1, on A_s = A/s:

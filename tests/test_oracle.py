@@ -335,6 +335,97 @@ def test_cn_half_storage_residual():
 # c7: Chebyshev / Clenshaw
 # ----------------------------------------------------------------------------------------------
 
+# ---- NDB with binary16 iterates and fp32 correction (reading: stored iterates rounded to binary16,
+# exact products; correction X <- sym(X (5I - X^4 A_s)/4))
+
+def _scalar_ndb_half(m, T, keep_last):
+    h = lambda x: float(np.float16(x))
+    z = h(1.5 - 0.5 * m)
+    y = h(m * z)
+    for k in range(1, T):
+        sc = h(1.5 - 0.5 * (z * y))
+        y = h(y * sc)
+        z = sc * z if (keep_last and k == T - 1) else h(sc * z)
+    return y, z
+
+
+def test_ndb_half_diagonal_matches_scalar_recurrence():
+    """On diagonal blocks every product is an exact product of binary16 numbers, so the scalar
+    recurrence with the same roundings (numpy float16, round to nearest even) gives the oracle's
+    result exactly; so does the scalar correction step."""
+    lam = np.exp(np.linspace(np.log(0.05), 0.0, 16))
+    s = 1.3
+    for T1, T2, refine in ((6, 6, 0), (5, 4, 2), (1, 1, 1)):
+        X = oracle.ndb_half_inverse_root(np.diag(lam), s, T1, T2, refine)
+        assert np.count_nonzero(X - np.diag(np.diag(X))) == 0
+        xs, ms = [], []
+        for l in lam:
+            m = l / s
+            y, _ = _scalar_ndb_half(float(np.float16(m)), T1, False)
+            _, x = _scalar_ndb_half(y, T2, True)
+            xs.append(x)
+            ms.append(m)
+
+        def tvals(xv):  # T = (5 - x^4 m)/4 per entry, and the block's residual 4 ||T - 1||_F / sqrt(n)
+            t = [(5.0 - ((xi * xi) * (xi * xi)) * mi) / 4.0 for xi, mi in zip(xv, ms)]
+            return t, 4.0 * math.sqrt(sum((ti - 1.0) ** 2 for ti in t) / len(t))
+
+        t, r_cur = tvals(xs)
+        for _ in range(refine):  # guarded: a step is taken only if the residual goes down
+            xc = [xi * ti for xi, ti in zip(xs, t)]
+            tc, r_c = tvals(xc)
+            if not r_c < r_cur:
+                break
+            xs, t, r_cur = xc, tc, r_c
+        for i in range(len(lam)):
+            assert X[i, i] == s ** -0.25 * xs[i]
+
+
+def test_ndb_half_guard_stops_a_diverging_correction():
+    """At kappa ~25-35 the plain Newton correction diverges (the residual grows step by step, as the
+    unguarded steps computed here show); the guarded correction then never ends worse than its
+    start."""
+    A = di.tiny_stack().astype(np.float64)
+    s = np.linalg.eigvalsh(A)[:, -1] * 1.02
+    X0 = oracle.ndb_half_inverse_root(A, s, 6, 6, 0)
+    Xg = oracle.ndb_half_inverse_root(A, s, 6, 6, 4)
+    diverged = 0
+    for b in range(A.shape[0]):
+        As = A[b] / s[b]
+        x = X0[b] * s[b] ** 0.25
+        rs = []
+        for _ in range(3):
+            rs.append(np.linalg.norm(np.linalg.matrix_power(x, 4) @ As - np.eye(64)))
+            x = x @ ((5 * np.eye(64) - np.linalg.matrix_power(x, 4) @ As) / 4)
+            x = 0.5 * (x + x.T)
+        r_g = np.linalg.norm(np.linalg.matrix_power(Xg[b], 4) @ A[b] - np.eye(64))
+        assert r_g <= rs[0] * (1 + 1e-12)
+        diverged += rs[2] > rs[0]
+    assert diverged >= 1
+
+
+def test_ndb_half_residual_and_correction():
+    """Binary16 NDB meets the binary16 gate at kappa ~5, and each correction step lowers the
+    residual and the distance to the exact root."""
+    g = di.rng(77)
+    G = g.standard_normal((96, 96)) * 1e-3
+    A = G @ G.T / 96 + 1e-6 * np.eye(96)
+    s = np.linalg.eigvalsh(A)[-1] * 1.02
+    exact = oracle.inverse_root_evd(A)
+    prev_r, prev_e = None, None
+    for refine in range(4):
+        X = oracle.ndb_half_inverse_root(A, s, 6, 6, refine)
+        X2 = X @ X
+        r = np.linalg.norm(X2 @ X2 @ A - np.eye(96)) / np.sqrt(96)
+        e = np.linalg.norm(X - exact) / np.linalg.norm(exact)
+        if refine == 0:
+            assert r < 5e-3
+        else:
+            assert r < prev_r and e < prev_e
+            assert np.array_equal(X, X.T)
+        prev_r, prev_e = r, e
+
+
 # ---- adaptive stopping rule ([PT] Significância e Alegações, "Direções Futuras"; reading: a call
 # stops before step k >= 1 once its monitor is <= tol)
 
