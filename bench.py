@@ -49,12 +49,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive"], default="step",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16"], default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
                         "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
                         "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
-                        "fixed step counts on a stack of two conditionings")
+                        "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
+                        "iterates and 0-2 correction steps")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
@@ -119,6 +120,8 @@ def main():
         return only_evd(dash, di, torch, dev)
     if args.only == "adaptive":
         return only_adaptive(dash, di, torch, dev)
+    if args.only == "ndb16":
+        return only_ndb16(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -354,6 +357,48 @@ def only_evd(dash, di, torch, dev):
           flush=True)
 
 
+def only_ndb16(dash, di, torch, dev):
+    """NDB (6 + 6 steps) with binary16 iterates on the N=3072, B=1024 Gram stack after fp32
+    power-iteration scaling, with 0, 1 and 2 guarded fp32 correction steps, beside fp32 NDB."""
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    s = torch.empty(N, device=dev)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    del ws
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=dev)
+    sample = [0, N // 2, N - 1]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    out = {"mode": "ndb16", "N": N, "B": B, "iters": [NDB_ITERS, NDB_ITERS]}
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP16, device=dev)
+    for refine in (0, 1, 2):
+        ms = timed(lambda: dash.dash_inverse_root_ndb_half(A, s, N, B, NDB_ITERS, NDB_ITERS, refine, X,
+                                                           status=status, ws=ws))
+        out["refine%d" % refine] = {"ms": round(ms, 1), "blocks_per_s": round(N / (ms * 1e-3), 1),
+                                    "residual": [evd_residual(torch, A, X, b) for b in sample],
+                                    "status_nonzero": int((status != 0).sum())}
+    del ws
+    torch.cuda.empty_cache()
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=dev)
+    ms = timed(lambda: dash.dash_inverse_root_ndb(A, s, N, B, NDB_ITERS, NDB_ITERS, X, status=status, ws=ws))
+    out["ndb_fp32"] = {"ms": round(ms, 1), "blocks_per_s": round(N / (ms * 1e-3), 1),
+                       "residual": [evd_residual(torch, A, X, b) for b in sample]}
+    print(json.dumps(out), flush=True)
+
+
 ADAPT_TOL = 1e-5
 
 
@@ -485,8 +530,9 @@ def traffic_from_counters(fetch_csv, write_csv):
 
 
 def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
-    """Solve-only rates: NDB fp32 (6+6 steps, 30 products), CN p=4 fp16 (5 steps, 16 products) and the
-    block-Jacobi eigendecomposition (fp32, until a sweep rotates nothing)."""
+    """Solve-only rates: NDB fp32 (6+6 steps, 30 products), CN p=4 fp16 (5 steps, 16 products), NDB with
+    binary16 iterates and one guarded fp32 correction, and the block-Jacobi eigendecomposition (fp32,
+    until a sweep rotates nothing)."""
     A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
     s = torch.empty(N, device=dev)
     res = {}
@@ -534,6 +580,17 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                       "frac_fp16_peak": round(fl / FP16_PEAK_TFLOPS, 4),
                       "scale_fp16_ms": round(scale16_ms, 2),
                       "scale_fp16_hbm_gbs": round(half_bytes / (scale16_ms * 1e-3) / 1e9, 1)}
+    # NDB with binary16 iterates and one guarded fp32 correction step (after the fp32 scale)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    del ws
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP16, device=dev)
+    nh_ms = timed(lambda: dash.dash_inverse_root_ndb_half(A, s, N, B, NDB_ITERS, NDB_ITERS, 1, X, ws=ws))
+    del ws
+    torch.cuda.empty_cache()
+    res["ndb_fp16_refine1"] = {"iters": [NDB_ITERS, NDB_ITERS], "correction_steps": 1, "ms": round(nh_ms, 2),
+                               "blocks_per_s": round(N / (nh_ms * 1e-3), 1),
+                               "residual_block0": evd_residual(torch, A, X, 0)}
     # block-Jacobi eigendecomposition (the root solver the iterations replace), one solve
     evd_ms, Xe, sweeps, status = evd_solve(dash, torch, A, N, B, dev)
     sw = sweeps.float()

@@ -117,6 +117,116 @@ __global__ __launch_bounds__(256) void gemm_f16_kernel(GemmArgs a) {
 
 
 // ------------------------------------------------------------------------------------------------
+// fp16 operands with a general right operand (NDB with binary16 iterates), 256 x 256 macro tile
+// (B % 256 == 0), no operand maps.  Four waves as 2 x 2, wave tile 128 x 128
+// (4 x 4 accumulators of 32 x 32, held in the accumulation registers at one wave per SIMD).  Every
+// thread stages 8 pieces of the X slice (256 rows x 64 k, 16-byte loads) and one 8 (k) x 8 (n)
+// sub-block of the Y slice, loaded as eight 16-byte row pieces and transposed in registers, so both
+// LDS tiles hold rows of 64 consecutive k.  LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+// (row ^ row/8) & 7, which keeps both the MFMA reads (8 consecutive rows, one chunk) and the
+// transposed writes (rows 8 apart, one chunk) free of bank conflicts.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row ^ (row >> 3))) & 7; }
+
+template <bool SYM, typename TO, bool CHECKS>
+__global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
+  constexpr int TILE = 256, BK = 64, MT = 4, WT = 128;
+  // double-buffered X and Y slices (128 KiB); a little more so a mirrored binary16 tile fits whole
+  constexpr int MAIN_BYTES = 2 * 2 * TILE * BK * 2;
+  constexpr int STAGE_BYTES = TILE * (TILE + 8) * 2;  // binary16 output tile staged for 16-byte stores
+  constexpr int SMEM_BYTES = MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  _Float16(*As)[TILE * BK] = reinterpret_cast<_Float16(*)[TILE * BK]>(smem);
+  _Float16(*Bs)[TILE * BK] = reinterpret_cast<_Float16(*)[TILE * BK]>(smem + 2 * TILE * BK * 2);
+
+  const TileCoord tc = decode_tile(a, SYM);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const _Float16* X = (const _Float16*)P.X + off;
+  const _Float16* Y = (const _Float16*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int kb = tid >> 5, nb = tid & 31;  // this thread's 8 x 8 sub-block of the Y slice
+
+  // X slice: 8 pieces of 16 bytes, piece c = tid + 256 r -> row c / 8, chunk c % 8.
+  // Y slice: k rows 8 kb .. 8 kb + 7, n columns 8 nb .. 8 nb + 7, transposed in registers.
+  f16x8 lx[8], ly[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      lx[r] = *(const f16x8*)(X + (int64_t)(i0 + (c >> 3)) * B + k0 + 8 * (c & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ly[q] = *(const f16x8*)(Y + (int64_t)(k0 + 8 * kb + q) * B + j0 + 8 * nb);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c >> 3;
+      *(f16x8*)&As[buf][row * BK + 8 * swz(row, c & 7)] = lx[r];
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      f16x8 col;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) col[q] = ly[q][n];
+      const int row = 8 * nb + n;
+      *(f16x8*)&Bs[buf][row * BK + 8 * swz(row, kb)] = col;
+    }
+  };
+
+  f32x16 acc[MT][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  const int KT = B / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const _Float16* as = As[buf];
+    const _Float16* bs = Bs[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int chunk = 4 * h + s;
+      f16x8 av[MT], bv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * WT + mt * 32 + li;
+        av[mt] = *(const f16x8*)&as[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int nt = 0; nt < MT; ++nt) {
+        const int row = wn * WT + nt * 32 + li;
+        bv[nt] = *(const f16x8*)&bs[row * BK + 8 * swz(row, chunk)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < MT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  if constexpr (sizeof(TO) == 2)
+    epilogue_staged_f16<MT, MT, WT, WT, SYM, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane, smem);
+  else
+    epilogue<MT, MT, WT, WT, SYM, TO, false, false, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
+}
+
+// ------------------------------------------------------------------------------------------------
 // fp16 operands with an exactly symmetric right operand Y (Y^T = Y bitwise), 256 x 256 macro tile,
 // four waves of 128 x 128 or eight waves of 128 x 64.
 // Then column j of Y is row j of Y, so both slices are read as rows of consecutive k with 16-byte
@@ -277,8 +387,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
 
 template <bool SYM, bool CHECKS>
 hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t stream) {
-  // the 256-wide tile needs an exactly symmetric right operand (its columns are read as rows)
-  const int tile = (a.B % 256 == 0 && y_sym) ? 256 : (a.B % 128 == 0 ? 128 : 64);
+  // 256-wide tiles: the kernel that reads an exactly symmetric right operand's columns as rows, or
+  // the one that transposes a general right operand while staging it (no operand maps)
+  const bool maps = a.p0.map_x || a.p0.map_y || (a.nprob > 1 && (a.p1.map_x || a.p1.map_y));
+  const bool frz = a.p0.freeze || (a.nprob > 1 && a.p1.freeze);
+  const int tile = (a.B % 256 == 0 && (y_sym || (!maps && !frz))) ? 256 : (a.B % 128 == 0 ? 128 : 64);
   a.tdim = a.B / tile;
   a.tiles = SYM ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool half_out = out_prec == DASH_FP16;
@@ -286,8 +399,8 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t
   // MFMAs)
   // launches that carry stopped blocks of an adaptive solve (triangle-only products only)
   if constexpr (SYM) {
-    if (a.p0.freeze || (a.nprob > 1 && a.p1.freeze)) {
-      if (tile == 256)
+    if (frz) {
+      if (tile == 256)  // frz launches take 256-wide tiles only with a symmetric right operand
         return half_out ? launch_interleaved(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8, true>, a, stream, 512)
                         : launch_interleaved(gemm_f16_ysym_kernel<SYM, float, CHECKS, 8, true>, a, stream, 512);
       if (tile == 128)
@@ -297,6 +410,9 @@ hipError_t dispatch_f16(GemmArgs& a, dash_prec out_prec, bool y_sym, hipStream_t
                       : launch_interleaved(gemm_f16_kernel<64, SYM, float, CHECKS, true>, a, stream);
     }
   }
+  if (tile == 256 && !y_sym)
+    return half_out ? launch(gemm_f16_big_kernel<SYM, _Float16, CHECKS>, a, stream)
+                    : launch(gemm_f16_big_kernel<SYM, float, CHECKS>, a, stream);
   if (tile == 256)
     return half_out ? launch(gemm_f16_ysym_kernel<SYM, _Float16, CHECKS, 8>, a, stream, 512)
                     : launch(gemm_f16_ysym_kernel<SYM, float, CHECKS, 8>, a, stream, 512);
