@@ -49,13 +49,15 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16"], default="step",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "libref"],
+                   default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
                         "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
                         "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
-                        "iterates and 0-2 correction steps")
+                        "iterates and 0-2 correction steps; libref: the vendor library's binary16 "
+                        "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
     return p.parse_args()
@@ -122,6 +124,8 @@ def main():
         return only_adaptive(dash, di, torch, dev)
     if args.only == "ndb16":
         return only_ndb16(dash, di, torch, dev)
+    if args.only == "libref":
+        return only_libref(torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -315,6 +319,38 @@ def only_solver(dash, di, torch, dev, which):
     torch.cuda.synchronize()
     print(json.dumps({"mode": which, "N": N, "B": B, "scale_ms": round(e[0].elapsed_time(e[1]), 3),
                       "solve_ms": round(e[1].elapsed_time(e[2]), 3)}), flush=True)
+
+
+def only_libref(torch, dev):
+    """Calibration, not part of the path: the vendor library's binary16 batched product
+    (torch.bmm, contiguous operands, fp32 accumulation) on the N=3072, B=1024 stack shape, timed as
+    one 3072-product call and as two 1536-product calls.  Every tile is computed (2 B^3 flop per
+    product); the triangle-only products of the binary16 solvers compute 10 of 16 tiles."""
+    B = BLOCK
+    N = 2 * 1536
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    X = (torch.randn(N, B, B, device=dev, generator=g) * 0.03).half()
+    Y = (torch.randn(N, B, B, device=dev, generator=g) * 0.03).half()
+    D = torch.empty_like(X)
+    out = {"mode": "libref", "N": N, "B": B}
+    for chunk in (N, N // 2):
+        def run():
+            for i in range(0, N, chunk):
+                torch.bmm(X[i:i + chunk], Y[i:i + chunk], out=D[i:i + chunk])
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        tf = 2.0 * B ** 3 * N / (ms * 1e-3) / 1e12
+        out["chunk_%d" % chunk] = {"ms_per_product": round(ms, 3), "tflops": round(tf, 1),
+                                   "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
 
 
 def evd_solve(dash, torch, A, N, B, dev, refine=0):
