@@ -51,7 +51,10 @@ typedef enum {
   DASH_ERR_DEVICE = 5       /* a HIP launch failed */
 } dash_status;
 
-typedef enum { DASH_FP32 = 0, DASH_FP16 = 1 } dash_prec; /* operand precision; accumulation is fp32 */
+/* operand precision; accumulation is fp32.  DASH_BF16 (bfloat16 operands: 8-bit significand, the
+ * exponent range of fp32) is accepted by the half-precision solvers (dash_inverse_root_cn,
+ * dash_inverse_root_ndb_lowp) and their workspace/flop queries; dash_scale takes DASH_FP32 or DASH_FP16. */
+typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
 
@@ -135,14 +138,24 @@ dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N
                                        int32_t iters2, int32_t refine, float* X, float* monitor, int32_t* status,
                                        void* ws, size_t ws_bytes, void* stream);
 
+/* The same with the iterates' 2-byte format chosen by prec: DASH_FP16 (binary16; identical to
+ * dash_inverse_root_ndb_half) or DASH_BF16 (bfloat16: 8-bit significand, fp32's exponent range;
+ * [PT] Resultados Experimentais name FP16/BF16 NDB together).  Products accumulate in fp32 and
+ * every stored iterate is rounded to that format once.  Workspace: dash_workspace_size(DASH_OP_NDB,
+ * ..., prec, ...).  Any other prec -> DASH_ERR_INVALID_ARG. */
+dash_status dash_inverse_root_ndb_lowp(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, dash_prec prec, int32_t refine, float* X, float* monitor,
+                                       int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
 /* Inverse p-th root by the Coupled-Newton iteration, p = 4 ([PT] Definição do Problema, item 2;
  * [TG] body, "CN - Coupled Newton Iteration"; fp16 operands per [PT] Resultados Experimentais).
  * On M_0 = A_i / s_i, X_0 = I: S = (5I - M)/4, X <- X S, M <- M S^4 (S^4 = (S S)(S S));
- * X_i = s_i^{-1/4} X_iters.  4*iters - 4 products.  prec == DASH_FP16 stores every iterate in
- * binary16 and accumulates in fp32; X is always written in fp32.  p != 4 -> DASH_ERR_UNSUPPORTED.
- * Only the upper triangle of A_i is read (the start terms are built from it, mirrored).  With
- * binary16 operands every iterate (a polynomial in A_i) is kept exactly symmetric: each product
- * computes only its upper-triangle tiles and mirrors them, and X_i comes out exactly symmetric.
+ * X_i = s_i^{-1/4} X_iters.  4*iters - 4 products.  prec == DASH_FP16 (DASH_BF16) stores every
+ * iterate in binary16 (bfloat16) and accumulates in fp32; X is always written in fp32.  p != 4 ->
+ * DASH_ERR_UNSUPPORTED.  Only the upper triangle of A_i is read (the start terms are built from it,
+ * mirrored).  With 2-byte operands every iterate (a polynomial in A_i) is kept exactly symmetric:
+ * each product computes only its upper-triangle tiles and mirrors them, and X_i comes out exactly
+ * symmetric.
  * fp32 runs full products, which keep the fp32 rounding floor lowest at high condition numbers.
  * monitor: NULL or [N, iters] receives ||M_k - I||_F / sqrt(B) before step k. */
 dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,

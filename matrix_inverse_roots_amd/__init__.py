@@ -6,6 +6,7 @@ passes their pointers and the current HIP stream through ctypes, and raises :cla
 a non-OK status.  There is no CPU fallback: if the library is missing, importing a call raises.
 """
 from ._lib import (  # noqa: F401
+    DASH_BF16,
     DASH_FP16,
     DASH_FP32,
     DASH_OP_APPLY,
@@ -28,6 +29,7 @@ from ._lib import (  # noqa: F401
     dash_inverse_root_ndb,
     dash_inverse_root_ndb_adaptive,
     dash_inverse_root_ndb_half,
+    dash_inverse_root_ndb_lowp,
     dash_scale,
     dash_solver_products,
     dash_stack,

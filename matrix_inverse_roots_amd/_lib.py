@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdash.so")
 
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
-DASH_FP32, DASH_FP16 = 0, 1
+DASH_FP32, DASH_FP16, DASH_BF16 = 0, 1, 2
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
 DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD = range(7)
 
@@ -50,6 +50,7 @@ def library() -> ctypes.CDLL:
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_half": (st, [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_ndb_lowp": (st, [vp, vp, i64, i32, i32, i32, st, i32, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz,
                                                     vp]),
             "dash_inverse_root_cn_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, st, vp, vp, vp, vp, vp, sz, vp]),
@@ -176,6 +177,14 @@ def dash_inverse_root_ndb_half(A, s, N: int, B: int, iters1: int, iters2: int, r
                                status=None, ws=None, stream=None):
     _check("dash_inverse_root_ndb_half",
            library().dash_inverse_root_ndb_half(_ptr(A), _ptr(s), N, B, iters1, iters2, refine, _ptr(X),
+                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws),
+                                                _stream(stream, A)))
+
+
+def dash_inverse_root_ndb_lowp(A, s, N: int, B: int, iters1: int, iters2: int, prec: int, refine: int, X,
+                               monitor=None, status=None, ws=None, stream=None):
+    _check("dash_inverse_root_ndb_lowp",
+           library().dash_inverse_root_ndb_lowp(_ptr(A), _ptr(s), N, B, iters1, iters2, prec, refine, _ptr(X),
                                                 _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws),
                                                 _stream(stream, A)))
 

@@ -28,7 +28,9 @@ bool valid_B(int32_t B) { return B >= 64 && B <= 8192 && B % 64 == 0; }
 bool valid_N(int64_t N) { return N >= 1 && N <= MAX_N; }
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-size_t elem_size(dash_prec p) { return p == DASH_FP16 ? 2 : 4; }
+size_t elem_size(dash_prec p) { return p == DASH_FP32 ? 4 : 2; }
+// 2-byte operand formats of the half-precision solvers
+bool half_prec(dash_prec p) { return p == DASH_FP16 || p == DASH_BF16; }
 size_t stack_bytes(int64_t N, int B, dash_prec p) { return align_up((size_t)N * B * B * elem_size(p), 256); }
 size_t coef_bytes(int64_t N) { return align_up((size_t)N * COEF_STRIDE * sizeof(float), 256); }
 
@@ -227,13 +229,12 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
   return DASH_OK;
 }
 
-// One NDB call with binary16 iterates (fp32 accumulation) on the binary16 stack M: every stored
-// iterate is rounded to binary16 once, by the epilogue that forms it.  Step 0: S_0 = (3I - M)/2 is
+// One NDB call with 2-byte iterates H (binary16 or bfloat16; fp32 accumulation) on the stack M in
+// that format: every stored iterate is rounded to H once, by the epilogue that forms it.  Step 0: S_0 = (3I - M)/2 is
 // Z_1 and Y_1 = M S_0.  Returns Y_T (binary16) in *y_out, or (want_z) writes Z_T in fp32 into
 // final_out, scaled by coef[final_ia], with the finite check into status.  Monitor as in ndb_call.
-dash_status ndb_half_call(const NdbCtx& c, void* M, bool m_from_pool, int T, int mon_col, bool want_z,
+dash_status ndb_half_call(const NdbCtx& c, dash_prec H, void* M, bool m_from_pool, int T, int mon_col, bool want_z,
                           float* final_out, int8_t final_ia, void** y_out) {
-  const auto H = DASH_FP16;
   void* Z = c.pool->get();
   {
     Affine s0;
@@ -351,14 +352,15 @@ dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) 
 }
 
 
-// Coupled Newton with binary16 iterates (T >= 2), on M_0 = A/s already stored in M0.
+// Coupled Newton with 2-byte iterates H (binary16 or bfloat16; T >= 2), on M_0 = A/s already stored
+// in M0 in that format.
 // S_k = (5I - M_k)/4 is never stored: every product that takes S_k reads M_k and maps it as it is
 // staged (operand map -1/4 Z + 5/4 I, the same single rounding a binary16 elementwise pass would
 // apply), and X_1 = S_0 is likewise M_0 mapped.  M_0 stays alive until X_2 has been formed.
 // freeze (optional, adaptive): a block whose monitor ||M_k - I|| is <= tol before step k >= 1 keeps
 // X_k from then on (its later products are skipped or pass X through).
-dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* status, const float* coef, void* M0,
-                    Pool& pool, hipStream_t st, int32_t* freeze, float tol, int32_t* steps) {
+dash_status cn_half(dash_prec H, int64_t N, int B, int T, float* X, float* monitor, int32_t* status, const float* coef,
+                    void* M0, Pool& pool, hipStream_t st, int32_t* freeze, float tol, int32_t* steps) {
   auto mapped = [](Product p, bool mx, bool my) {
     p.map_x = mx;
     p.map_y = my;
@@ -382,25 +384,25 @@ dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* 
       e.coef = coef;
       e.status = status;
       Product pr = frozen(mapped(prod(Xk ? Xk : M0, M, X), Xk == nullptr, true), 1);
-      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP32, Trans::NN, true, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, H, DASH_FP32, Trans::NN, true, e, st, true));
       break;
     }
     void* S2 = pool.get();
     if (k == 0) {
       Product pr = mapped(prod(M, M, S2), true, true);
-      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, H, H, Trans::NN, true, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S_k and S_k^2 in one launch
       void* Xn = pool.get();
       Product pr[2] = {frozen(mapped(prod(Xk ? Xk : M0, M, Xn), Xk == nullptr, true), 1),
                        frozen(mapped(prod(M, M, S2), true, true), 0)};
-      TRY(launch_gemm(pr, 2, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+      TRY(launch_gemm(pr, 2, N, B, H, H, Trans::NN, true, Epilogue(), st, true));
       pool.put(Xk ? Xk : M0);  // X_k (or M_0, whose last use as X_1 this was) is dead
       Xk = Xn;
     }
     void* S4 = pool.get();
     {
       Product pr = frozen(prod(S2, S2, S4), 0);
-      TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, H, H, Trans::NN, true, Epilogue(), st, true));
     }
     pool.put(S2);
     Epilogue e;
@@ -410,7 +412,7 @@ dash_status cn_half(int64_t N, int B, int T, float* X, float* monitor, int32_t* 
     }
     void* Mn = pool.get();
     Product pr = frozen(prod(M, S4, Mn), 0);
-    TRY(launch_gemm(&pr, 1, N, B, DASH_FP16, DASH_FP16, Trans::NN, true, e, st, true));
+    TRY(launch_gemm(&pr, 1, N, B, H, H, Trans::NN, true, e, st, true));
     if (M != M0) pool.put(M);  // M_0 is released with X_1 above
     pool.put(S4);
     M = Mn;
@@ -453,11 +455,11 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2) {
 }
 
 double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2) {
-  if (!valid_N(N) || !valid_B(B) || (prec != DASH_FP32 && prec != DASH_FP16)) return -1.0;
+  if (!valid_N(N) || !valid_B(B) || (prec != DASH_FP32 && !half_prec(prec))) return -1.0;
   const double full = 2.0 * B * B * (double)B * (double)N;
   // fraction of the tiles a triangle-only product computes, for the tile width the kernels use
   auto tri = [&](dash_prec p) {
-    const int tile = (p == DASH_FP16 && B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64);
+    const int tile = (half_prec(p) && B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64);
     const double t = B / tile;
     return (t * (t + 1) / 2) / (t * t);
   };
@@ -468,7 +470,7 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
       return n < 0 ? -1.0 : n * full;
     case DASH_OP_CN:
       n = dash_solver_products(op, a1, 0);
-      return n < 0 ? -1.0 : n * full * (prec == DASH_FP16 ? tri(prec) : 1.0);
+      return n < 0 ? -1.0 : n * full * (half_prec(prec) ? tri(prec) : 1.0);
     case DASH_OP_CHEB:
       n = dash_solver_products(op, a1, 0);
       return n < 0 ? -1.0 : n * full * tri(DASH_FP32);
@@ -491,13 +493,14 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
                                 size_t* bytes) {
   if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
-  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
   switch (op) {
     case DASH_OP_SCALE:
+      if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;
       if (k_or_degree < 0 || k_or_degree > 32) return DASH_ERR_INVALID_ARG;
       *bytes = ws_scale(N, B, prec, k_or_degree);
       return DASH_OK;
-    case DASH_OP_NDB: *bytes = prec == DASH_FP16 ? ws_ndb_half(N, B) : ws_ndb(N, B); return DASH_OK;
+    case DASH_OP_NDB: *bytes = half_prec(prec) ? ws_ndb_half(N, B) : ws_ndb(N, B); return DASH_OK;
     case DASH_OP_CN: *bytes = ws_cn(N, B, prec); return DASH_OK;
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
@@ -551,6 +554,7 @@ dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, d
     return DASH_OK;
   }
   if (how != DASH_SCALE_POWER) return DASH_ERR_INVALID_ARG;
+  if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;  // power iteration streams fp32 or binary16 operands
   if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
   if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !V0 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256) || ws_bytes < power_workspace_bytes(N, B, prec)) return DASH_ERR_WORKSPACE;
@@ -630,15 +634,14 @@ dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32
   return DASH_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
-                                       int32_t iters2, int32_t refine, float* X, float* monitor, int32_t* status,
-                                       void* ws, size_t ws_bytes, void* stream) {
+// NDB with 2-byte iterates H and the guarded fp32 correction (dash_inverse_root_ndb_half /
+// dash_inverse_root_ndb_lowp)
+dash_status ndb_lowp_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1, int32_t iters2,
+                          dash_prec H, int32_t refine, float* X, float* monitor, int32_t* status, void* ws,
+                          size_t ws_bytes, void* stream) {
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
+  if (!half_prec(H)) return DASH_ERR_INVALID_ARG;
   if (X == A || iters1 < 1 || iters2 < 1 || iters1 > 1000 || iters2 > 1000 || refine < 0 || refine > 16)
     return DASH_ERR_INVALID_ARG;
   if ((monitor && !aligned(monitor, 4)) || (status && !aligned(status, 4))) return DASH_ERR_INVALID_ARG;
@@ -652,7 +655,7 @@ dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N
   float* res = (float*)cv.take((size_t)N * 17 * sizeof(float));  // residual sums of squares per step
   char* region = (char*)cv.take(ndb_half_region(N, B));
   Pool pool;
-  for (int q = 1; q < 6; ++q) pool.put(region + q * stack_bytes(N, B, DASH_FP16));
+  for (int q = 1; q < 6; ++q) pool.put(region + q * stack_bytes(N, B, H));
   void* M = region;  // M = h(A / s), the first call's input (not from the pool)
   const int cols = iters1 + iters2;
   if (status) TRY(launch_fill_i32(status, N, 0, st));
@@ -662,7 +665,7 @@ dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N
     Affine m;
     m.X = A;
     m.D = M;
-    m.d_prec = DASH_FP16;
+    m.d_prec = H;
     m.a = 1.f;
     m.ia = CO_R1;
     m.coef = coef;
@@ -670,11 +673,11 @@ dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N
   }
   NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
   void* Y = nullptr;
-  dash_status r = ndb_half_call(c, M, false, iters1, 0, false, nullptr, CO_NONE, &Y);
+  dash_status r = ndb_half_call(c, H, M, false, iters1, 0, false, nullptr, CO_NONE, &Y);
   if (r != DASH_OK) return r;
   // the second call's Z_T in fp32: unscaled into X when there is no correction, else the
   // correction's start
-  r = ndb_half_call(c, Y, true, iters2, iters1, true, X, refine ? CO_NONE : CO_U, nullptr);
+  r = ndb_half_call(c, H, Y, true, iters2, iters1, true, X, refine ? CO_NONE : CO_U, nullptr);
   if (r != DASH_OK) return r;
   if (monitor) TRY(launch_monitor_finish(monitor, N * cols, B, st));
   if (!refine) return DASH_OK;
@@ -737,6 +740,22 @@ dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N
   return DASH_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+dash_status dash_inverse_root_ndb_half(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, int32_t refine, float* X, float* monitor, int32_t* status,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  return ndb_lowp_impl(A, s, N, B, iters1, iters2, DASH_FP16, refine, X, monitor, status, ws, ws_bytes, stream);
+}
+
+dash_status dash_inverse_root_ndb_lowp(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, dash_prec prec, int32_t refine, float* X, float* monitor,
+                                       int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return ndb_lowp_impl(A, s, N, B, iters1, iters2, prec, refine, X, monitor, status, ws, ws_bytes, stream);
+}
+
 dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
                                   int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
                                   void* ws, size_t ws_bytes, void* stream) {
@@ -764,7 +783,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (X == A || iters < 1 || iters > 1000) return DASH_ERR_INVALID_ARG;
-  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
   if (monitor && !aligned(monitor, 4)) return DASH_ERR_INVALID_ARG;
   if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
@@ -793,12 +812,12 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   // step 0: M_0 = A/s, S_0 = (5I - M_0)/4, X_1 = S_0;  ||M_0 - I||^2 = 16 ||S_0 - I||^2
   void* S = pool.get();
   void* M = pool.get();
-  if (prec == DASH_FP16 && T > 1) {  // binary16: M_0 only; the S_k are formed inside the products
+  if (half_prec(prec) && T > 1) {  // 2-byte iterates: M_0 only; the S_k are formed inside the products
     pool.put(S);
     Affine m0;
     m0.X = A;
     m0.D = M;
-    m0.d_prec = DASH_FP16;
+    m0.d_prec = prec;
     m0.a = 1.f;
     m0.ia = CO_R1;
     m0.coef = coef;
@@ -808,7 +827,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
     }
     // built from the upper triangle of A: every later right operand is then exactly symmetric
     TRY(launch_sym_affine(m0, N, B, st));
-    return cn_half(N, B, T, X, monitor, status, coef, M, pool, st, freeze, stop.tol, stop.steps);
+    return cn_half(prec, N, B, T, X, monitor, status, coef, M, pool, st, freeze, stop.tol, stop.steps);
   }
   {
     Affine s0;

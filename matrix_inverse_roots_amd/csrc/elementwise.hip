@@ -51,6 +51,14 @@ __device__ __forceinline__ float co(const float* coef, int idx, int64_t b) {
 __device__ __forceinline__ void store4(void* D, dash_prec p, int64_t e, f32x4 v) {
   if (p == DASH_FP32) {
     *(f32x4*)((float*)D + e) = v;
+  } else if (p == DASH_BF16) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    b4 bv;
+    bv[0] = (__bf16)v[0];
+    bv[1] = (__bf16)v[1];
+    bv[2] = (__bf16)v[2];
+    bv[3] = (__bf16)v[3];
+    *(b4*)((__bf16*)D + e) = bv;
   } else {
     f16x4 hv;
     hv[0] = (_Float16)v[0];
@@ -82,6 +90,10 @@ __global__ __launch_bounds__(256) void affine_kernel(Affine op, int64_t N, int B
     if (op.X) {
       if (op.x_prec == DASH_FP32) {
         x = *(const f32x4*)((const float*)op.X + e);
+      } else if (op.x_prec == DASH_BF16) {
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        const b4 bx = *(const b4*)((const __bf16*)op.X + e);
+        x = f32x4{(float)bx[0], (float)bx[1], (float)bx[2], (float)bx[3]};
       } else {
         const f16x4 hx = *(const f16x4*)((const _Float16*)op.X + e);
         x = f32x4{(float)hx[0], (float)hx[1], (float)hx[2], (float)hx[3]};

@@ -5,7 +5,7 @@
 // matrix products).  One launch covers one or two batched products (grid = problems x blocks x
 // tiles) and fuses the affine combination the iteration needs, D = a*acc + b*C + d*E + g*I, with
 // per-block coefficients read on the device (gemm_common.hpp).  The kernels are in gemm_f32.hip
-// (fp32 operands) and gemm_f16.hip (binary16 operands, fp32 accumulation).
+// (fp32 operands) and gemm_f16.hip (binary16 or bfloat16 operands, fp32 accumulation).
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
@@ -56,10 +56,13 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);
   }
+  // 2-byte operands (binary16 or bfloat16): output in fp32 or in the operand format
+  if ((in_prec != DASH_FP16 && in_prec != DASH_BF16) || (out_prec != DASH_FP32 && out_prec != in_prec))
+    return hipErrorInvalidValue;
   if (trans != Trans::NN || epi_uses_ce(probs, nprob)) return hipErrorInvalidValue;
   // binary16-operand products carry no second output
   if (probs[0].D2 || (nprob > 1 && probs[1].D2)) return hipErrorInvalidValue;
-  return gemm::launch_f16(a, out_prec, sym, y_sym, stream);
+  return gemm::launch_f16(a, in_prec, out_prec, sym, y_sym, stream);
 }
 
 }  // namespace dash

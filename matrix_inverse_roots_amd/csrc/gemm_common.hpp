@@ -13,6 +13,29 @@ namespace gemm {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The 2-byte operand formats of the half-precision products: binary16 (_Float16) and bfloat16
+// (__bf16).  Both multiply on the 32x32x16 MFMA with fp32 accumulation; v8 is the operand of one
+// lane (8 consecutive k), v4 four consecutive elements of a row.
+template <typename TE>
+struct Half;
+template <>
+struct Half<_Float16> {
+  typedef f16x8 v8;
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Half<__bf16> {
+  typedef bf16x8 v8;
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
 
 struct GemmArgs {
   Product p0, p1;
@@ -87,19 +110,21 @@ __device__ __forceinline__ bool decode_tile_interleaved(const GemmArgs& a, bool 
   return c.b < a.N;
 }
 
-// Operand map of the binary16 products: the 8 consecutive elements Z[row][col0 .. col0 + 7] of a
-// staged chunk become a Z + g I.  a is a power of two (the callers' -1/4), so a z is exact unless it
-// is subnormal, and the diagonal element a z + g is rounded once (an exact a z below the half-ulp
-// of g cannot move the rounding): each result equals the exact value rounded to binary16 once, as
-// an fp32 elementwise pass that stores binary16 would give.  Only chunks that hold a diagonal
-// element take the branch.
-__device__ __forceinline__ f16x8 operand_map(f16x8 v, int row, int col0, float a, float g) {
-  f16x8 r = v * (_Float16)a;
+// Operand map of the half-precision products: the 8 consecutive elements Z[row][col0 .. col0 + 7]
+// of a staged chunk become a Z + g I.  a is a power of two (the callers' -1/4 and -1/2), so a z is
+// exact unless it is subnormal, and the diagonal element a z + g (g = 5/4 or 3/2, exact in both
+// formats) is rounded once (an exact a z below the half-ulp of g cannot move the rounding): each
+// result equals the exact value rounded to the operand format once, as an fp32 elementwise pass
+// that stores that format would give.  Only chunks that hold a diagonal element take the branch.
+template <typename TE>
+__device__ __forceinline__ typename Half<TE>::v8 operand_map(typename Half<TE>::v8 v, int row, int col0, float a,
+                                                             float g) {
+  typename Half<TE>::v8 r = v * (TE)a;
   const int d = row - col0;
   if ((unsigned)d < 8u) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if (q == d) r[q] = r[q] + (_Float16)g;
+      if (q == d) r[q] = r[q] + (TE)g;
   }
   return r;
 }
@@ -260,11 +285,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
 // 16-byte rows (a diagonal tile stores everything directly and the mirror then overwrites its
 // strict lower part).  Monitor and status (CHECKS) as in `epilogue`.  smem: TILE * (TILE + 8)
 // halves when SYM.
-template <int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE, bool CHECKS>
+template <typename TE, int MTM, int MTN, int WTM, int WTN, bool SYM, int TILE, bool CHECKS>
 __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                                     const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                                     char* smem) {
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  typedef typename Half<TE>::v4 h4;
+  typedef typename Half<TE>::v8 h8;
   constexpr int PITCH = TILE + 8;
   const Epilogue& e = a.epi;
   const int B = a.B;
@@ -275,8 +301,8 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
   const int li = lane & 31, h = lane >> 5;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const bool diag_tile = SYM && tc.ti == tc.tj;
-  _Float16* T = (_Float16*)smem;
-  _Float16* D = (_Float16*)P.D + off;
+  TE* T = (TE*)smem;
+  TE* D = (TE*)P.D + off;
   float mon = 0.f;
   bool bad = false;
 #pragma unroll
@@ -287,13 +313,13 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
       for (int r4 = 0; r4 < 4; ++r4) {
         const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3
         const int jl = wn * WTN + nt * 32 + li;
-        f16x4 pk;
+        h4 pk;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int il = il0 + q;
           const bool on_diag = (i0 + il == j0 + jl);
           const float v = al * acc[mt][nt][4 * r4 + q] + (on_diag ? ga : 0.f);
-          const _Float16 hv = (_Float16)v;
+          const TE hv = (TE)v;
           pk[q] = hv;
           // a diagonal tile stores its lower part too; the mirror overwrites it after the barrier
           D[(int64_t)(i0 + il) * B + j0 + jl] = hv;
@@ -305,7 +331,7 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
             }
           }
         }
-        if (SYM) *(f16x4*)&T[jl * PITCH + il0] = pk;
+        if (SYM) *(h4*)&T[jl * PITCH + il0] = pk;
       }
   if (CHECKS && e.monitor) {
     mon = wave_sum(mon);
@@ -318,9 +344,9 @@ __device__ __forceinline__ void epilogue_staged_f16(const GemmArgs& a, const Til
   for (int g = threadIdx.x; g < TILE * TILE / 8; g += nthreads) {
     const int jl = g / (TILE / 8), c8 = g - jl * (TILE / 8);
     const int il = 8 * c8;
-    _Float16* dst = D + (int64_t)(j0 + jl) * B + i0 + il;  // mirror element (j, i) = value at (i, j)
+    TE* dst = D + (int64_t)(j0 + jl) * B + i0 + il;  // mirror element (j, i) = value at (i, j)
     if (!diag_tile || il + 7 < jl) {
-      *(f16x8*)dst = *(const f16x8*)&T[jl * PITCH + il];
+      *(h8*)dst = *(const h8*)&T[jl * PITCH + il];
     } else if (il < jl) {  // the chunk crossing the diagonal: strict upper part only
       for (int q = 0; il + q < jl; ++q) dst[q] = T[jl * PITCH + il + q];
     }
@@ -346,12 +372,12 @@ hipError_t launch_interleaved(K kernel, const GemmArgs& a, hipStream_t stream, i
 // A stopped block of an adaptive solve (binary16 operands): the accumulators take the operand that
 // passes through (X for pass 1, Y for pass 2) at the tile's positions, mapped exactly as the product
 // would have staged it (operand_map's arithmetic, element by element).
-template <int MTM, int MTN, int WTM, int WTN>
-__device__ __forceinline__ void pass_tile_f16(const Product& P, const _Float16* X, const _Float16* Y, int B, int i0,
+template <typename TE, int MTM, int MTN, int WTM, int WTN>
+__device__ __forceinline__ void pass_tile_f16(const Product& P, const TE* X, const TE* Y, int B, int i0,
                                               int j0, int wm, int wn, int lane, f32x16 (&acc)[MTM][MTN]) {
-  const _Float16* Z = P.pass == 1 ? X : Y;
+  const TE* Z = P.pass == 1 ? X : Y;
   const bool map = P.pass == 1 ? P.map_x : P.map_y;
-  const _Float16 ma = (_Float16)P.map_a, mg = (_Float16)P.map_g;
+  const TE ma = (TE)P.map_a, mg = (TE)P.map_g;
   const int li = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int mt = 0; mt < MTM; ++mt)
@@ -361,7 +387,7 @@ __device__ __forceinline__ void pass_tile_f16(const Product& P, const _Float16* 
       for (int r = 0; r < 16; ++r) {
         const int i = i0 + wm * WTM + mt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int j = j0 + wn * WTN + nt * 32 + li;
-        _Float16 z = Z[(int64_t)i * B + j];
+        TE z = Z[(int64_t)i * B + j];
         if (map) {
           z = z * ma;
           if (i == j) z = z + mg;
@@ -372,7 +398,7 @@ __device__ __forceinline__ void pass_tile_f16(const Product& P, const _Float16* 
 
 // kernel launchers of the two precisions
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
-hipError_t launch_f16(GemmArgs& a, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
+hipError_t launch_f16(GemmArgs& a, dash_prec in_prec, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

@@ -48,6 +48,7 @@ def _load():
             "orc_matmul": (None, [i, _dp, _dp, _dp]),
             "orc_frobenius": (d, [i, _dp]),
             "orc_round_binary16": (d, [d]),
+            "orc_round_bfloat16": (d, [d]),
             "orc_jacobi_eigh": (i, [i, _dp, _dp, _dp, i]),
             "orc_power_evd": (i, [i, _dp, d, _dp]),
             "orc_mpi": (d, [i, _dp, i, i, _dp, _dp]),
@@ -59,6 +60,7 @@ def _load():
             "orc_ndb_inverse_root_until": (None, [i, _dp, d, i, i, d, _dp, _dp, _dp, _ip]),
             "orc_cn_until": (i, [i, _dp, d, i, i, d, _dp, _dp]),
             "orc_ndb_half_inverse_root": (None, [i, _dp, d, i, i, i, _dp]),
+            "orc_ndb_lowp_inverse_root": (None, [i, _dp, d, i, i, i, i, _dp]),
             "orc_cheb_coeffs": (None, [i, d, d, d, _dp]),
             "orc_clenshaw": (None, [i, _dp, i, _dp, d, d, _dp]),
             "orc_cheb_inverse_root": (None, [i, _dp, d, i, d, d, _dp]),
@@ -136,6 +138,17 @@ def round_binary16(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     f = _load().orc_round_binary16
     return np.array([f(float(v)) for v in x.reshape(-1)]).reshape(x.shape)
+
+
+def round_bfloat16(x) -> np.ndarray:
+    """Elementwise round-to-nearest-even to bfloat16, returned as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    f = _load().orc_round_bfloat16
+    return np.array([f(float(v)) for v in x.reshape(-1)]).reshape(x.shape)
+
+
+# storage formats of the low-precision models
+_FORMATS = {None: 0, "binary16": 1, "bfloat16": 2}
 
 
 def frobenius(A) -> np.ndarray:
@@ -238,8 +251,12 @@ def ndb_inverse_root(A, s, iters1: int, iters2: int, threads: int | None = None,
     return X, R, mon
 
 
-def cn_inverse_root(A, s, iters: int, half_storage: bool = False, threads: int | None = None):
-    """A^{-1/4} by the Coupled-Newton p=4 iteration (c6).  Returns (X, monitor[N, iters])."""
+def cn_inverse_root(A, s, iters: int, half_storage: bool = False, threads: int | None = None,
+                    storage: str | None = None):
+    """A^{-1/4} by the Coupled-Newton p=4 iteration (c6).  Returns (X, monitor[N, iters]).
+    storage: None (exact), "binary16" or "bfloat16" rounds every stored iterate to that format
+    (half_storage=True is "binary16")."""
+    fmt = _FORMATS[storage if storage is not None else ("binary16" if half_storage else None)]
     A, single = _as_stack(A)
     N, n, _ = A.shape
     s = _per_block(s, N)
@@ -248,8 +265,7 @@ def cn_inverse_root(A, s, iters: int, half_storage: bool = False, threads: int |
     lib = _load()
 
     def one(b):
-        lib.orc_cn_inverse_root(n, _p(A[b]), float(s[b]), int(iters), int(bool(half_storage)), _p(X[b]),
-                                _p(mon[b]))
+        lib.orc_cn_inverse_root(n, _p(A[b]), float(s[b]), int(iters), fmt, _p(X[b]), _p(mon[b]))
 
     _over_blocks(one, N, threads)
     mon = mon[:, :iters]
@@ -295,9 +311,12 @@ def cn_inverse_root_adaptive(A, s, max_iters: int, tol: float, threads: int | No
     return (X[0], mon[0], steps[0]) if single else (X, mon, steps)
 
 
-def ndb_half_inverse_root(A, s, iters1: int, iters2: int, refine: int = 0, threads: int | None = None):
-    """Composed NDB root with binary16 iterates, then `refine` Newton correction steps against A_s
-    (each followed by symmetrisation).  Returns X (N, B, B)."""
+def ndb_half_inverse_root(A, s, iters1: int, iters2: int, refine: int = 0, threads: int | None = None,
+                          storage: str = "binary16"):
+    """Composed NDB root with 2-byte iterates (storage "binary16" or "bfloat16"), then `refine`
+    guarded Newton correction steps against A_s (each followed by symmetrisation).  Returns X."""
+    fmt = _FORMATS[storage]
+    assert fmt > 0
     A, single = _as_stack(A)
     N, n, _ = A.shape
     s = _per_block(s, N)
@@ -305,7 +324,8 @@ def ndb_half_inverse_root(A, s, iters1: int, iters2: int, refine: int = 0, threa
     lib = _load()
 
     def one(b):
-        lib.orc_ndb_half_inverse_root(n, _p(A[b]), float(s[b]), int(iters1), int(iters2), int(refine), _p(X[b]))
+        lib.orc_ndb_lowp_inverse_root(n, _p(A[b]), float(s[b]), int(iters1), int(iters2), fmt, int(refine),
+                                      _p(X[b]))
 
     _over_blocks(one, N, threads)
     return X[0] if single else X

@@ -85,6 +85,28 @@ double orc_round_binary16(double x) {
   return copysign(r, x);
 }
 
+/* Round x to the nearest bfloat16 value (ties to even) and return it as a double.  Written from
+ * the bfloat16 format definition: 8 significant bits and the exponent range of binary32 (normal
+ * exponents -126..127, subnormal quantum 2^-133, largest finite (2 - 2^-7) 2^127). */
+double orc_round_bfloat16(double x) {
+  if (isnan(x)) return x;
+  const double ax = fabs(x);
+  if (ax >= ldexp(2.0 - ldexp(1.0, -8), 127)) return copysign(INFINITY, x); /* halfway to 2^128 and above */
+  if (ax == 0.0) return x;
+  int ex;
+  frexp(ax, &ex);
+  int e = ex - 1;
+  if (e < -126) e = -126;
+  const double quantum = ldexp(1.0, e - 7);
+  const double r = nearbyint(ax / quantum) * quantum; /* default mode: ties to even */
+  return copysign(r, x);
+}
+
+/* storage formats of the low-precision models: 0 exact, 1 binary16, 2 bfloat16 */
+static double round_fmt(int fmt, double x) {
+  return fmt == 1 ? orc_round_binary16(x) : (fmt == 2 ? orc_round_bfloat16(x) : x);
+}
+
 /* ------------------------------------------------------------------------------------------------
  * c1: exact root by cyclic Jacobi eigendecomposition.
  * The eigendecomposition is the default root solver of Distributed Shampoo ([PT] Definição do
@@ -363,34 +385,36 @@ void orc_ndb_inverse_root(int n, const double* A, double s, int T1, int T2, doub
  *     X_c = sym(X (5 I - X^4 A_s) / 4),   sym(W) = (W + W^T) / 2,
  * taken only if it lowers the residual ||X^4 A_s - I||_F; at the first candidate that does not, the
  * correction stops (the Newton step is not contractive for every spectrum).  X = s^{-1/4} X.
- * h() rounds to binary16 (orc_round_binary16).
+ * h() rounds to the storage format: binary16 (orc_round_binary16), or bfloat16
+ * (orc_round_bfloat16) in orc_ndb_lowp_inverse_root with fmt = 2 (the pages name FP16 and BF16
+ * NDB together).
  * ---------------------------------------------------------------------------------------------- */
-static void round16_all(size_t nn, double* x) {
-  for (size_t e = 0; e < nn; ++e) x[e] = orc_round_binary16(x[e]);
+static void round_all(int fmt, size_t nn, double* x) {
+  for (size_t e = 0; e < nn; ++e) x[e] = round_fmt(fmt, x[e]);
 }
 
-/* one binary16 NDB call; *Yout / *Zout receive Y_T / Z_T (Z_T unrounded when keep_z_exact) */
-static void ndb_half_call(int n, const double* M, int T, int keep_z_exact, double* Y, double* Z) {
+/* one low-precision NDB call; *Yout / *Zout receive Y_T / Z_T (Z_T unrounded when keep_z_exact) */
+static void ndb_half_call(int n, int fmt, const double* M, int T, int keep_z_exact, double* Y, double* Z) {
   const size_t nn = (size_t)n * n;
   double* S = (double*)malloc(sizeof(double) * nn);
   double* P = (double*)malloc(sizeof(double) * nn);
   double* T1 = (double*)malloc(sizeof(double) * nn);
   for (int i = 0; i < n; ++i)
     for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = (i == j ? 1.5 : 0.0) - 0.5 * M[IDX(i, j, n)];
-  round16_all(nn, S);
+  round_all(fmt, nn, S);
   memcpy(Z, S, sizeof(double) * nn);
   orc_matmul(n, M, S, Y);
-  round16_all(nn, Y);
+  round_all(fmt, nn, Y);
   for (int k = 1; k < T; ++k) {
     orc_matmul(n, Z, Y, P);
     for (int i = 0; i < n; ++i)
       for (int j = 0; j < n; ++j) S[IDX(i, j, n)] = (i == j ? 1.5 : 0.0) - 0.5 * P[IDX(i, j, n)];
-    round16_all(nn, S);
+    round_all(fmt, nn, S);
     orc_matmul(n, Y, S, T1);
-    round16_all(nn, T1);
+    round_all(fmt, nn, T1);
     memcpy(Y, T1, sizeof(double) * nn);
     orc_matmul(n, S, Z, T1);
-    if (!(keep_z_exact && k == T - 1)) round16_all(nn, T1);
+    if (!(keep_z_exact && k == T - 1)) round_all(fmt, nn, T1);
     memcpy(Z, T1, sizeof(double) * nn);
   }
   free(S);
@@ -398,7 +422,7 @@ static void ndb_half_call(int n, const double* M, int T, int keep_z_exact, doubl
   free(T1);
 }
 
-void orc_ndb_half_inverse_root(int n, const double* A, double s, int T1, int T2, int refine, double* X) {
+void orc_ndb_lowp_inverse_root(int n, const double* A, double s, int T1, int T2, int fmt, int refine, double* X) {
   const size_t nn = (size_t)n * n;
   double* As = (double*)malloc(sizeof(double) * nn);
   double* M = (double*)malloc(sizeof(double) * nn);
@@ -408,10 +432,10 @@ void orc_ndb_half_inverse_root(int n, const double* A, double s, int T1, int T2,
   double* X4 = (double*)malloc(sizeof(double) * nn);
   double* Mr = (double*)malloc(sizeof(double) * nn);
   for (size_t e = 0; e < nn; ++e) As[e] = A[e] / s;
-  for (size_t e = 0; e < nn; ++e) M[e] = orc_round_binary16(As[e]);
-  ndb_half_call(n, M, T1, 0, Y, Z);
+  for (size_t e = 0; e < nn; ++e) M[e] = round_fmt(fmt, As[e]);
+  ndb_half_call(n, fmt, M, T1, 0, Y, Z);
   memcpy(M, Y, sizeof(double) * nn);
-  ndb_half_call(n, M, T2, 1, Y, Z);
+  ndb_half_call(n, fmt, M, T2, 1, Y, Z);
   /* T = (5I - X^4 A_s)/4 of the current X (in Mr) and its residual ||X^4 A_s - I|| = 4 ||T - I|| */
   double* Xc = (double*)malloc(sizeof(double) * nn);
   double* Tc = (double*)malloc(sizeof(double) * nn);
@@ -450,14 +474,19 @@ void orc_ndb_half_inverse_root(int n, const double* A, double s, int T1, int T2,
   free(Mr);
 }
 
+void orc_ndb_half_inverse_root(int n, const double* A, double s, int T1, int T2, int refine, double* X) {
+  orc_ndb_lowp_inverse_root(n, A, s, T1, T2, 1, refine, X);
+}
+
 /* ------------------------------------------------------------------------------------------------
  * c6: Coupled-Newton iteration for the inverse p-th root, p = 4 ([PT] Definição do Problema,
  * item 2; [TG] body, "CN - Coupled Newton Iteration").
  * Reading: the coupled Newton iteration of Guo and Higham (2006) with c = 1, on A_s = A/s:
  *     X_0 = I, M_0 = A_s;   S = ((p+1) I - M_k) / p,  X_{k+1} = X_k S,  M_{k+1} = M_k S^p,
  * with S^4 formed as (S S)(S S).  X_T -> A_s^{-1/4}; X = s^{-1/4} X_T.
- * half_storage != 0 rounds every stored iterate (S, S^2, S^4, M, X) to binary16 and the input
- * operand A_s as well, modelling binary16 operands with exact accumulation (diagnostic mode).
+ * half_storage (a storage format: 0 exact, 1 binary16, 2 bfloat16) rounds every stored iterate
+ * (S, S^2, S^4, M, X) and the input operand A_s to that format, modelling 2-byte operands with
+ * exact accumulation.
  * monitor[k] (optional) = ||M_k - I||_F / sqrt(n), before step k.
  * ---------------------------------------------------------------------------------------------- */
 int orc_cn_until(int n, const double* A, double s, int T, int half_storage, double tol, double* X,
@@ -472,7 +501,7 @@ int orc_cn_until(int n, const double* A, double s, int T, int half_storage, doub
 #define STORE16(buf)                                                   \
   do {                                                                 \
     if (half_storage)                                                  \
-      for (size_t e_ = 0; e_ < nn; ++e_) (buf)[e_] = orc_round_binary16((buf)[e_]); \
+      for (size_t e_ = 0; e_ < nn; ++e_) (buf)[e_] = round_fmt(half_storage, (buf)[e_]); \
   } while (0)
   for (size_t e = 0; e < nn; ++e) M[e] = A[e] / s;
   STORE16(M);

@@ -199,3 +199,28 @@ def test_adaptive_argument_errors():
     assert _status_of(g, P, P2, N, B, 4, 8, 1e-5, 7, 5 * P, 6 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG  # bad prec
     assert _status_of(g, P, P2, N, B, 3, 8, 1e-5, dash.DASH_FP32, 5 * P, 6 * P,
                       ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                          # p != 4
+
+
+def test_bfloat16_queries_and_argument_errors():
+    """bfloat16 operands: the half-precision solvers' queries match binary16 (same 2-byte stacks, same
+    tile counts); power-iteration scaling and other precisions are refused before any launch."""
+    N, B = 16, 256
+    for op in (dash.DASH_OP_CN, dash.DASH_OP_NDB):
+        assert (dash.dash_workspace_size(op, N, B, dash.DASH_BF16)
+                == dash.dash_workspace_size(op, N, B, dash.DASH_FP16))
+    assert (dash.dash_flops(dash.DASH_OP_CN, N, B, dash.DASH_BF16, 5, 0)
+            == dash.dash_flops(dash.DASH_OP_CN, N, B, dash.DASH_FP16, 5, 0))
+    with pytest.raises(dash.DashError) as ei:
+        dash.dash_workspace_size(dash.DASH_OP_SCALE, N, B, dash.DASH_BF16, 32)
+    assert ei.value.status == _lib.DASH_ERR_UNSUPPORTED
+    assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_BF16, 32, 10, P2, P3,
+                      ws=FakeWs(4 * P, 1 << 30)) == _lib.DASH_ERR_UNSUPPORTED
+    ws = FakeWs(P3, dash.dash_workspace_size(dash.DASH_OP_NDB, 4, 64, dash.DASH_BF16))
+    f = dash.dash_inverse_root_ndb_lowp
+    assert _status_of(f, P, P2, 4, 64, 6, 6, dash.DASH_FP32, 0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, 4, 64, 6, 6, 7, 0, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(f, P, P2, 4, 64, 6, 6, dash.DASH_BF16, 17, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert (_status_of(f, P, P2, 4, 64, 6, 6, dash.DASH_BF16, 0, 5 * P, ws=FakeWs(P3, ws.n - 1))
+            == _lib.DASH_ERR_WORKSPACE)
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, 4, 64, 4, 5, 3, 5 * P,
+                      ws=FakeWs(P3, 1 << 30)) == _lib.DASH_ERR_INVALID_ARG

@@ -54,6 +54,34 @@ def test_round_binary16_matches_numpy():
     assert math.isnan(oracle.round_binary16(np.array([np.nan]))[0])
 
 
+def _bf16(x):
+    """Library bfloat16 rounding (torch, round to nearest even from binary32) of float32-exact values."""
+    import torch
+
+    x = np.asarray(x, dtype=np.float64)
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x, equal_nan=True)
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_round_bfloat16_matches_library():
+    """bfloat16 rounding against torch's conversion on float32-exact values over the whole exponent
+    range, ties to even, the overflow threshold and the subnormal range."""
+    g = di.rng(13)
+    vals = list((g.standard_normal(3000) * np.exp(g.uniform(-95, 88, 3000))).astype(np.float32))
+    ulp1 = 2.0 ** -7
+    big = 2.0 ** 127
+    vals += [0.0, -0.0, 1.0, 1 + ulp1 / 2, 1 + 3 * ulp1 / 2, -(1 + ulp1 / 2), 257.0, 259.0,
+             (2 - ulp1) * big, (2 - 2.0 ** -8 - 2.0 ** -23) * big, 2.0 ** -126, 2.0 ** -133,
+             3 * 2.0 ** -134, 2.0 ** -135, 2.0 ** -126 * (1 - 2.0 ** -8)]
+    x = np.array(vals, dtype=np.float64)
+    assert np.array_equal(oracle.round_bfloat16(x), _bf16(x))
+    assert oracle.round_bfloat16(np.array([1 + ulp1 / 2]))[0] == 1.0  # tie to the even neighbour
+    assert oracle.round_bfloat16(np.array([1 + 3 * ulp1 / 2]))[0] == 1 + 2 * ulp1
+    top = oracle.round_bfloat16(np.array([(2 - 2.0 ** -8) * big, (2 - 2.0 ** -8) * big * (1 - 2.0 ** -30)]))
+    assert math.isinf(top[0]) and top[1] == (2 - ulp1) * big  # halfway to 2^128 overflows, below it does not
+    assert math.isnan(oracle.round_bfloat16(np.array([np.nan]))[0])
+
+
 # ----------------------------------------------------------------------------------------------
 # c1: exact root by Jacobi eigendecomposition
 # ----------------------------------------------------------------------------------------------
@@ -338,8 +366,10 @@ def test_cn_half_storage_residual():
 # ---- NDB with binary16 iterates and fp32 correction (reading: stored iterates rounded to binary16,
 # exact products; correction X <- sym(X (5I - X^4 A_s)/4))
 
-def _scalar_ndb_half(m, T, keep_last):
-    h = lambda x: float(np.float16(x))
+_ROUND = {"binary16": lambda x: float(np.float16(x)), "bfloat16": lambda x: float(_bf16([x])[0])}
+
+
+def _scalar_ndb_half(m, T, keep_last, h):
     z = h(1.5 - 0.5 * m)
     y = h(m * z)
     for k in range(1, T):
@@ -349,20 +379,24 @@ def _scalar_ndb_half(m, T, keep_last):
     return y, z
 
 
-def test_ndb_half_diagonal_matches_scalar_recurrence():
-    """On diagonal blocks every product is an exact product of binary16 numbers, so the scalar
-    recurrence with the same roundings (numpy float16, round to nearest even) gives the oracle's
-    result exactly; so does the scalar correction step."""
-    lam = np.exp(np.linspace(np.log(0.05), 0.0, 16))
-    s = 1.3
+@pytest.mark.parametrize("storage", ["binary16", "bfloat16"])
+def test_ndb_half_diagonal_matches_scalar_recurrence(storage):
+    """On diagonal blocks every product is an exact product of 2-byte numbers, so the scalar
+    recurrence with the same roundings (numpy float16, or torch's bfloat16 conversion, both round to
+    nearest even; every rounded value is exact in float32, so neither rounds twice) gives the
+    oracle's result exactly; so does the scalar correction step.  s is a power of two and the
+    eigenvalues are float32 numbers, so A/s is exact before its first rounding."""
+    h = _ROUND[storage]
+    lam = np.exp(np.linspace(np.log(0.05), 0.0, 16)).astype(np.float32).astype(np.float64)
+    s = 2.0
     for T1, T2, refine in ((6, 6, 0), (5, 4, 2), (1, 1, 1)):
-        X = oracle.ndb_half_inverse_root(np.diag(lam), s, T1, T2, refine)
+        X = oracle.ndb_half_inverse_root(np.diag(lam), s, T1, T2, refine, storage=storage)
         assert np.count_nonzero(X - np.diag(np.diag(X))) == 0
         xs, ms = [], []
         for l in lam:
             m = l / s
-            y, _ = _scalar_ndb_half(float(np.float16(m)), T1, False)
-            _, x = _scalar_ndb_half(y, T2, True)
+            y, _ = _scalar_ndb_half(h(m), T1, False, h)
+            _, x = _scalar_ndb_half(y, T2, True, h)
             xs.append(x)
             ms.append(m)
 
@@ -379,6 +413,30 @@ def test_ndb_half_diagonal_matches_scalar_recurrence():
             xs, t, r_cur = xc, tc, r_c
         for i in range(len(lam)):
             assert X[i, i] == s ** -0.25 * xs[i]
+
+
+@pytest.mark.parametrize("storage", ["binary16", "bfloat16"])
+def test_cn_storage_diagonal_matches_scalar_recurrence(storage):
+    """Coupled Newton with 2-byte storage on diagonal blocks: each diagonal entry follows the scalar
+    recurrence S = h((5 - m)/4), x = h(x S) (the last x unrounded), m = h(m h(h(S S)^2)), all
+    products exact in float64 (and in float32 before rounding)."""
+    h = _ROUND[storage]
+    lam = np.exp(np.linspace(np.log(0.02), 0.0, 12)).astype(np.float32).astype(np.float64)
+    s = 2.0
+    T = 6
+    X, mon = oracle.cn_inverse_root(np.diag(lam), s, T, storage=storage)
+    assert np.count_nonzero(X - np.diag(np.diag(X))) == 0
+    for i, l in enumerate(lam):
+        m, x = h(l / s), 1.0
+        for k in range(T):
+            sk = h((5.0 - m) / 4.0)
+            x = x * sk if k == T - 1 else h(x * sk)
+            s2 = h(sk * sk)
+            m = h(m * h(s2 * s2))
+        assert X[i, i] == s ** -0.25 * x
+    # the exact iteration differs: the storage rounding is what the model adds
+    X_exact, _ = oracle.cn_inverse_root(np.diag(lam), s, T)
+    assert not np.array_equal(X, X_exact)
 
 
 def test_ndb_half_guard_stops_a_diverging_correction():
