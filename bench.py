@@ -49,14 +49,15 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "libref"],
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "bf16", "libref"],
                    default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
                         "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
                         "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
-                        "iterates and 0-2 correction steps; libref: the vendor library's binary16 "
+                        "iterates and 0-2 correction steps; bf16: CN and NDB with bfloat16 iterates "
+                        "beside binary16; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
@@ -126,6 +127,8 @@ def main():
         return only_ndb16(dash, di, torch, dev)
     if args.only == "libref":
         return only_libref(torch, dev)
+    if args.only == "bf16":
+        return only_bf16(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -435,6 +438,56 @@ def only_ndb16(dash, di, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def only_bf16(dash, di, torch, dev):
+    """CN (5 steps) and NDB (6 + 6 steps, 0 and 1 guarded fp32 correction steps) with bfloat16
+    iterates on the N=3072, B=1024 Gram stack, each beside the same call with binary16 iterates,
+    after fp32 power-iteration scaling."""
+    B = BLOCK
+    N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    s = torch.empty(N, device=dev)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    del ws
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=dev)
+    sample = [0, N // 2, N - 1]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    out = {"mode": "bf16", "N": N, "B": B}
+    for name, prec in (("bf16", dash.DASH_BF16), ("fp16", dash.DASH_FP16)):
+        ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=dev)
+        ms = timed(lambda: dash.dash_inverse_root_cn(A, s, N, B, 4, CN_ITERS, prec, X, status=status, ws=ws))
+        fl = dash.dash_flops(dash.DASH_OP_CN, N, B, prec, CN_ITERS, 0) / (ms * 1e-3) / 1e12
+        out["cn_" + name] = {"iters": CN_ITERS, "ms": round(ms, 2), "blocks_per_s": round(N / (ms * 1e-3), 1),
+                             "tflops": round(fl, 1), "frac_peak": round(fl / FP16_PEAK_TFLOPS, 4),
+                             "residual": [evd_residual(torch, A, X, b) for b in sample],
+                             "status_nonzero": int((status != 0).sum())}
+        del ws
+        torch.cuda.empty_cache()
+        ws = dash.workspace(dash.DASH_OP_NDB, N, B, prec, device=dev)
+        for refine in (0, 1):
+            ms = timed(lambda: dash.dash_inverse_root_ndb_lowp(A, s, N, B, NDB_ITERS, NDB_ITERS, prec, refine, X,
+                                                               status=status, ws=ws))
+            out["ndb_%s_refine%d" % (name, refine)] = {
+                "ms": round(ms, 1), "blocks_per_s": round(N / (ms * 1e-3), 1),
+                "residual": [evd_residual(torch, A, X, b) for b in sample],
+                "status_nonzero": int((status != 0).sum())}
+        del ws
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 ADAPT_TOL = 1e-5
 
 
@@ -566,9 +619,9 @@ def traffic_from_counters(fetch_csv, write_csv):
 
 
 def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
-    """Solve-only rates: NDB fp32 (6+6 steps, 30 products), CN p=4 fp16 (5 steps, 16 products), NDB with
-    binary16 iterates and one guarded fp32 correction, and the block-Jacobi eigendecomposition (fp32,
-    until a sweep rotates nothing)."""
+    """Solve-only rates: NDB fp32 (6+6 steps, 30 products), CN p=4 fp16 and bf16 (5 steps, 16 products),
+    NDB with binary16 iterates and one guarded fp32 correction, and the block-Jacobi eigendecomposition
+    (fp32, until a sweep rotates nothing)."""
     A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
     s = torch.empty(N, device=dev)
     res = {}
@@ -616,6 +669,15 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                       "frac_fp16_peak": round(fl / FP16_PEAK_TFLOPS, 4),
                       "scale_fp16_ms": round(scale16_ms, 2),
                       "scale_fp16_hbm_gbs": round(half_bytes / (scale16_ms * 1e-3) / 1e9, 1)}
+    # CN with bfloat16 iterates (same binary16 power-iteration scale)
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_BF16, device=dev)
+    cnb_ms = timed(lambda: dash.dash_inverse_root_cn(A, s, N, B, 4, CN_ITERS, dash.DASH_BF16, X, ws=ws))
+    del ws
+    torch.cuda.empty_cache()
+    fl = dash.dash_flops(dash.DASH_OP_CN, N, B, dash.DASH_BF16, CN_ITERS, 0) / (cnb_ms * 1e-3) / 1e12
+    res["cn_bf16"] = {"iters": CN_ITERS, "ms": round(cnb_ms, 2), "blocks_per_s": round(N / (cnb_ms * 1e-3), 1),
+                      "tflops": round(fl, 2), "frac_bf16_peak": round(fl / FP16_PEAK_TFLOPS, 4),
+                      "residual_block0": evd_residual(torch, A, X, 0)}
     # NDB with binary16 iterates and one guarded fp32 correction step (after the fp32 scale)
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
