@@ -38,7 +38,7 @@ EVD_MAX_SWEEPS = 20
 FP32_PEAK_TFLOPS = 157.3
 FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-PRODUCT_KERNEL = "gemm_f32_kernel<128, 0, 0, true, float, false, true, false>"
+PRODUCT_KERNEL = "gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>"
 
 
 def parse():
