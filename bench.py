@@ -103,8 +103,8 @@ def main():
     if args.traffic_from:
         return traffic_from_counters(*args.traffic_from)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every block of the stack is independent, and multi-GPU runs "
-              "are not part of this build (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: every block of the stack is independent, and the benchmark "
+              "runs on a single GPU only (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

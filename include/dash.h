@@ -47,7 +47,7 @@ typedef enum {
   DASH_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad count, parameter out of range */
   DASH_ERR_SHAPE = 2,       /* B not a multiple of 64 or out of range */
   DASH_ERR_WORKSPACE = 3,   /* ws too small or misaligned */
-  DASH_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement (e.g. p != 4) */
+  DASH_ERR_UNSUPPORTED = 4, /* a valid request the library does not implement (e.g. p != 4) */
   DASH_ERR_DEVICE = 5       /* a HIP launch failed */
 } dash_status;
 
