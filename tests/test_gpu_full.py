@@ -100,6 +100,60 @@ def test_full_cn_fp16(stack):
     torch.cuda.empty_cache()
 
 
+def test_full_ndb_half_refine1(stack):
+    """Binary16 NDB (6 + 6 steps) with one guarded fp32 correction step, as the bench's solver entry:
+    the binary16 storage model on sampled blocks (tolerance 2e-3, fp32 accumulation against exact
+    products) and the fp32 residual gate on every block."""
+    A, V0 = stack
+    s = scale(A, V0, dash.DASH_FP32)
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP16, device=DEV)
+    dash.dash_inverse_root_ndb_half(A, s, N, B, 6, 6, 1, X, status=status, ws=ws)
+    del ws
+    torch.cuda.empty_cache()
+    assert int(status.abs().sum()) == 0
+    idx = SAMPLE + ORACLE_SAMPLE
+    A_h = host(A[idx])
+    s_h = host(s)[idx]
+    X_h = host(X[idx])
+    assert np.max(residual(X_h, A_h)) < R_FP32
+    k = len(SAMPLE)
+    X_ref = oracle.ndb_half_inverse_root(A_h[k:], s_h[k:], 6, 6, 1)
+    assert np.max(rel_err(X_h[k:], X_ref)) < 2e-3
+    assert residual_all(X, A) < R_FP32
+    del X
+    torch.cuda.empty_cache()
+
+
+def test_full_cn_bf16(stack):
+    """CN (5 steps) with bfloat16 iterates after the fp32 scale: the bfloat16 storage model on sampled
+    blocks and the bfloat16 residual gate 4e-2 (the binary16 gate scaled by the 8x unit roundoff) on
+    every block."""
+    A, V0 = stack
+    s = scale(A, V0, dash.DASH_FP32)
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_BF16, device=DEV)
+    dash.dash_inverse_root_cn(A, s, N, B, 4, 5, dash.DASH_BF16, X, status=status, ws=ws)
+    del ws
+    torch.cuda.empty_cache()
+    assert int(status.abs().sum()) == 0
+    idx = SAMPLE + ORACLE_SAMPLE
+    A_h = host(A[idx])
+    s_h = host(s)[idx]
+    X_h = host(X[idx])
+    r_bf16 = 8 * R_FP16
+    assert np.max(residual(X_h, A_h)) < r_bf16
+    assert np.array_equal(X_h, np.swapaxes(X_h, 1, 2))
+    k = len(SAMPLE)
+    X_ref, _ = oracle.cn_inverse_root(A_h[k:], s_h[k:], 5, storage="bfloat16")
+    assert np.max(rel_err(X_h[k:], X_ref)) < 8 * 5e-3
+    assert residual_all(X, A) < r_bf16
+    del X
+    torch.cuda.empty_cache()
+
+
 def test_full_step_chebyshev(stack):
     """stack -> EMA stats -> power scale -> Chebyshev d=24 -> apply -> unstack on the full workload."""
     A0, V0 = stack
