@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "bf16", "libref"],
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "bf16", "freq",
+                                      "libref"],
                    default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
@@ -57,7 +58,8 @@ def parse():
                         "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
                         "iterates and 0-2 correction steps; bf16: CN and NDB with bfloat16 iterates "
-                        "beside binary16; libref: the vendor library's binary16 "
+                        "beside binary16; freq: the step at update frequencies f = 1, 2, 4, 8, each step "
+                        "refreshing the roots of 1/f of the stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
@@ -129,6 +131,8 @@ def main():
         return only_libref(torch, dev)
     if args.only == "bf16":
         return only_bf16(dash, di, torch, dev)
+    if args.only == "freq":
+        return only_freq(dash, di, torch, dev)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -485,6 +489,62 @@ def only_bf16(dash, di, torch, dev):
                 "status_nonzero": int((status != 0).sum())}
         del ws
         torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
+def only_freq(dash, di, torch, dev):
+    """The optimizer step at preconditioner update frequency f = 1, 2, 4, 8.  Every step stacks the
+    gradients, updates every statistic, applies the current roots to every tile and unstacks; the
+    roots are refreshed round-robin, step i scaling and solving (Chebyshev d=24) the contiguous
+    stack slice [(i mod f) N/f, (i mod f + 1) N/f), so each block is refreshed once every f steps
+    and every step does the same work.  Timed over two full rotations after one."""
+    B = BLOCK
+    shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
+    NG = di.num_tiles(shapes, B)
+    N = 2 * NG
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(di.SEED_GRADS)
+    grads = [torch.randn(sh, generator=gen, device=dev) * 1e-3 for sh in shapes]
+    updates = [torch.empty(sh, device=dev) for sh in shapes]
+    A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    G_stack = torch.empty((NG, B, B), device=dev)
+    U_stack = torch.empty((NG, B, B), device=dev)
+    X = torch.empty((N, B, B), device=dev)
+    s = torch.empty(N, device=dev)
+    ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, device=dev)
+    ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
+    lo = BETA * EPS / float(s.max().item())
+    dash.dash_inverse_root_cheb(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, X, ws=ws_cheb)  # roots of step 0
+    torch.cuda.synchronize()
+
+    def step(i, f):
+        n = N // f
+        o = (i % f) * n
+        dash.dash_stack(grads, B, G_stack)
+        dash.dash_update_stats(G_stack, NG, B, BETA, A)
+        dash.dash_scale(A[o:o + n], n, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s[o:o + n],
+                        ws_scale)
+        dash.dash_inverse_root_cheb(A[o:o + n], s[o:o + n], n, B, CHEB_DEGREE, lo, CHEB_HI, X[o:o + n], ws=ws_cheb)
+        dash.dash_apply(X[:NG], X[NG:], G_stack, NG, B, U_stack, ws_apply)
+        dash.dash_unstack(U_stack, B, updates)
+
+    out = {"mode": "freq", "N": N, "B": B, "solver": "chebyshev-clenshaw d=%d fp32" % CHEB_DEGREE}
+    for f in (1, 2, 4, 8):
+        for i in range(f):
+            step(i, f)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(2 * f):
+            step(i, f)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (2 * f)
+        out["f%d" % f] = {"ms_per_step": round(ms, 1), "blocks_refreshed_per_step": N // f,
+                          "steps_per_s": round(1e3 / ms, 2)}
     print(json.dumps(out), flush=True)
 
 
