@@ -447,6 +447,31 @@ def test_batch_independence_and_determinism(conditioned):
     assert torch.equal(Cp, Cc[perm])
 
 
+def test_stack_slices_solve_like_the_whole_stack(conditioned):
+    """Round-robin refresh at update frequency f > 1 passes a slice of the stack (a pointer offset)
+    to the scale and the solver: the slice's roots equal the whole stack's for those blocks, bit for
+    bit, and the blocks outside the slice are left untouched."""
+    A, Ad = conditioned
+    N, B = Ad.shape[0], Ad.shape[1]
+    V0 = to_dev(di.start_vectors(B, 32))
+    s_all = power_scale(Ad, V0, 10)
+    X_all, _ = cheb(Ad, s_all, 12, 0.01, 1.25)
+    f = 4
+    n = N // f
+    X = torch.full_like(Ad, 7.0)
+    s = torch.zeros(N, device=DEV)
+    ws_s = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 32, device=DEV)
+    ws_c = dash.workspace(dash.DASH_OP_CHEB, N, B, device=DEV)
+    for i in (1, 3):
+        o = i * n
+        dash.dash_scale(Ad[o:o + n], n, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, V0, s[o:o + n], ws_s)
+        dash.dash_inverse_root_cheb(Ad[o:o + n], s[o:o + n], n, B, 12, 0.01, 1.25, X[o:o + n], ws=ws_c)
+        assert torch.equal(s[o:o + n], s_all[o:o + n])
+        assert torch.equal(X[o:o + n], X_all[o:o + n])
+    for i in (0, 2):
+        assert bool((X[i * n:(i + 1) * n] == 7.0).all())
+
+
 def test_bad_blocks_are_flagged_and_isolated(tiny):
     A, Ad = tiny
     s = frob_scale(Ad).clone()
