@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
     p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "bf16", "freq",
-                                      "libref"],
+                                      "c2", "libref"],
                    default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
@@ -59,7 +59,8 @@ def parse():
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
                         "iterates and 0-2 correction steps; bf16: CN and NDB with bfloat16 iterates "
                         "beside binary16; freq: the step at update frequencies f = 1, 2, 4, 8, each step "
-                        "refreshing the roots of 1/f of the stack; libref: the vendor library's binary16 "
+                        "refreshing the roots of 1/f of the stack; c2: steps to reach the residual 1e-3 "
+                        "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
@@ -133,6 +134,8 @@ def main():
         return only_bf16(dash, di, torch, dev)
     if args.only == "freq":
         return only_freq(dash, di, torch, dev)
+    if args.only == "c2":
+        return print(json.dumps(c2_steps_to_tolerance(dash, di, torch, dev)), flush=True)
     B = BLOCK
     shapes = di.llama_weight_shapes(LAYERS, D_MODEL, FFN)
     NG = di.num_tiles(shapes, B)
@@ -548,6 +551,53 @@ def only_freq(dash, di, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+C2_TOL = 1e-3
+C2_MAX_STEPS = 40
+
+
+def c2_residual(torch, A, X):
+    """max over blocks of ||X^4 A - I||_F / sqrt(B), in fp64 on the device (checking only)."""
+    x = X.double()
+    x2 = torch.matmul(x, x)
+    r = torch.matmul(torch.matmul(x2, x2), A.double())
+    r.diagonal(dim1=1, dim2=2).sub_(1.0)
+    return float((torch.linalg.matrix_norm(r) / A.shape[1] ** 0.5).max())
+
+
+def c2_steps_to_tolerance(dash, di, torch, dev):
+    """The conditioned stack (16 blocks of 256 x 256, kappa 1e4): for NDB (T + T steps) and CN p=4
+    (T steps), each after power-iteration (32 vectors, 10 steps) and after Frobenius scaling, the
+    smallest T <= 40 with residual <= 1e-3 on every block (None if not reached)."""
+    A = torch.from_numpy(di.conditioned_stack()[0]).to(dev)
+    N, B = A.shape[0], A.shape[1]
+    V0 = torch.from_numpy(di.start_vectors(B, K_VEC)).to(dev)
+    scales = {}
+    s = torch.empty(N, device=dev)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
+    scales["power"] = s.clone()
+    dash.dash_scale(A, N, B, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None)
+    scales["frobenius"] = s.clone()
+    X = torch.empty_like(A)
+    ws_ndb = dash.workspace(dash.DASH_OP_NDB, N, B, device=dev)
+    ws_cn = dash.workspace(dash.DASH_OP_CN, N, B, device=dev)
+    out = {"mode": "c2", "N": N, "B": B, "tol": C2_TOL, "max_steps": C2_MAX_STEPS}
+    for name, sc in scales.items():
+        for solver in ("ndb", "cn"):
+            found, r_at = None, None
+            for T in range(1, C2_MAX_STEPS + 1):
+                if solver == "ndb":
+                    dash.dash_inverse_root_ndb(A, sc, N, B, T, T, X, ws=ws_ndb)
+                else:
+                    dash.dash_inverse_root_cn(A, sc, N, B, 4, T, dash.DASH_FP32, X, ws=ws_cn)
+                r = c2_residual(torch, A, X)
+                if r <= C2_TOL:
+                    found, r_at = T, r
+                    break
+            out["%s_%s" % (solver, name)] = {"steps": found, "residual": r_at}
+    return out
+
+
 ADAPT_TOL = 1e-5
 
 
@@ -749,6 +799,9 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     res["ndb_fp16_refine1"] = {"iters": [NDB_ITERS, NDB_ITERS], "correction_steps": 1, "ms": round(nh_ms, 2),
                                "blocks_per_s": round(N / (nh_ms * 1e-3), 1),
                                "residual_block0": evd_residual(torch, A, X, 0)}
+    # steps to the residual 1e-3 on the kappa 1e4 stack, for each solver and scaling
+    c2 = c2_steps_to_tolerance(dash, di, torch, dev)
+    res["c2_steps_to_1e-3"] = {k: v["steps"] for k, v in c2.items() if isinstance(v, dict)}
     # block-Jacobi eigendecomposition (the root solver the iterations replace), one solve
     evd_ms, Xe, sweeps, status = evd_solve(dash, torch, A, N, B, dev)
     sw = sweeps.float()

@@ -510,3 +510,39 @@ def test_bad_blocks_are_flagged_and_isolated(tiny):
     # a non-finite block gives a non-finite power-iteration scale; the solver then flags bit 0
     s_bad = power_scale(bad, to_dev(di.start_vectors(64, 32)), 10)
     assert not np.isfinite(to_host(s_bad)[0]) and np.all(np.isfinite(to_host(s_bad)[1:]))
+
+
+def test_c2_steps_to_tolerance():
+    """Steps to reach the residual 1e-3 on every block of the kappa 1e4 stack, for NDB and CN after
+    power-iteration and Frobenius scaling (the counts bench.py --only c2 reports): every count is
+    reached, and the oracle's fp64 iteration with the GPU's scale agrees to one step (it has not
+    converged two steps earlier and has one step later)."""
+    import importlib.util
+    import os
+
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    res = bench.c2_steps_to_tolerance(dash, di, torch, DEV)
+    A, Ad = di.conditioned_stack()[0], to_dev(di.conditioned_stack()[0])
+    V0 = to_dev(di.start_vectors(256, 32))
+    scales = {"power": to_host(power_scale(Ad, V0, 10)), "frobenius": to_host(frob_scale(Ad))}
+    for key, rec in res.items():
+        if not isinstance(rec, dict):
+            continue
+        solver, name = key.split("_")
+        T = rec["steps"]
+        assert T is not None and rec["residual"] <= 1e-3, key
+        s = scales[name]
+
+        def oracle_residual(t):
+            if solver == "ndb":
+                X, _, _ = oracle.ndb_inverse_root(A, s, t, t)
+            else:
+                X, _ = oracle.cn_inverse_root(A, s, t)
+            return residual(X, A).max()
+
+        if T >= 3:
+            assert oracle_residual(T - 2) > 1e-3, key
+        assert oracle_residual(T + 1) <= 1e-3, key
