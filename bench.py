@@ -799,6 +799,11 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     res["ndb_fp16_refine1"] = {"iters": [NDB_ITERS, NDB_ITERS], "correction_steps": 1, "ms": round(nh_ms, 2),
                                "blocks_per_s": round(N / (nh_ms * 1e-3), 1),
                                "residual_block0": evd_residual(torch, A, X, 0)}
+    # Frobenius scaling: one read of the stack
+    fro_ms = timed(lambda: dash.dash_scale(A, N, B, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None))
+    res["frobenius_scale"] = {"ms": round(fro_ms, 3),
+                              "hbm_gbs": round(4.0 * B * B * N / (fro_ms * 1e-3) / 1e9, 1),
+                              "frac_hbm_peak": round(4.0 * B * B * N / (fro_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # steps to the residual 1e-3 on the kappa 1e4 stack, for each solver and scaling
     c2 = c2_steps_to_tolerance(dash, di, torch, dev)
     res["c2_steps_to_1e-3"] = {k: v["steps"] for k, v in c2.items() if isinstance(v, dict)}
