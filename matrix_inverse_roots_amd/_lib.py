@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdash.so")
 
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
-DASH_FP32, DASH_FP16, DASH_BF16 = 0, 1, 2
+DASH_FP32, DASH_FP16, DASH_BF16, DASH_FP32_SPLIT = 0, 1, 2, 3
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
 DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD = range(7)
 
@@ -55,6 +55,7 @@ def library() -> ctypes.CDLL:
                                                     vp]),
             "dash_inverse_root_cn_adaptive": (st, [vp, vp, i64, i32, i32, i32, f32, st, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cheb": (st, [vp, vp, i64, i32, i32, f64, f64, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_cheb_prec": (st, [vp, vp, i64, i32, i32, f64, f64, st, vp, vp, vp, sz, vp]),
             "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
@@ -210,6 +211,13 @@ def dash_inverse_root_cheb(A, s, N: int, B: int, degree: int, lo: float, hi: flo
     _check("dash_inverse_root_cheb",
            library().dash_inverse_root_cheb(_ptr(A), _ptr(s), N, B, degree, lo, hi, _ptr(X), _ptr(status), _ptr(ws),
                                             _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_cheb_prec(A, s, N: int, B: int, degree: int, lo: float, hi: float, prec: int, X, status=None,
+                                ws=None, stream=None):
+    _check("dash_inverse_root_cheb_prec",
+           library().dash_inverse_root_cheb_prec(_ptr(A), _ptr(s), N, B, degree, lo, hi, prec, _ptr(X), _ptr(status),
+                                                 _ptr(ws), _nbytes(ws), _stream(stream, A)))
 
 
 def dash_inverse_root_evd(A, N: int, B: int, max_sweeps: int, refine: int, X, eigvals=None, sweeps=None, status=None,

@@ -28,7 +28,9 @@ bool valid_B(int32_t B) { return B >= 64 && B <= 8192 && B % 64 == 0; }
 bool valid_N(int64_t N) { return N >= 1 && N <= MAX_N; }
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-size_t elem_size(dash_prec p) { return p == DASH_FP32 ? 4 : 2; }
+// fp32 storage: DASH_FP32, and DASH_FP32_SPLIT whose operands are split only inside the products
+bool fp32_prec(dash_prec p) { return p == DASH_FP32 || p == DASH_FP32_SPLIT; }
+size_t elem_size(dash_prec p) { return fp32_prec(p) ? 4 : 2; }
 // 2-byte operand formats of the half-precision solvers
 bool half_prec(dash_prec p) { return p == DASH_FP16 || p == DASH_BF16; }
 size_t stack_bytes(int64_t N, int B, dash_prec p) { return align_up((size_t)N * B * B * elem_size(p), 256); }
@@ -455,7 +457,9 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2) {
 }
 
 double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2) {
-  if (!valid_N(N) || !valid_B(B) || (prec != DASH_FP32 && !half_prec(prec))) return -1.0;
+  if (!valid_N(N) || !valid_B(B) || (!fp32_prec(prec) && !half_prec(prec))) return -1.0;
+  const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
+  if (prec == DASH_FP32_SPLIT) prec = DASH_FP32;
   const double full = 2.0 * B * B * (double)B * (double)N;
   // fraction of the tiles a triangle-only product computes, for the tile width the kernels use
   auto tri = [&](dash_prec p) {
@@ -473,7 +477,12 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
       return n < 0 ? -1.0 : n * full * (half_prec(prec) ? tri(prec) : 1.0);
     case DASH_OP_CHEB:
       n = dash_solver_products(op, a1, 0);
-      return n < 0 ? -1.0 : n * full * tri(DASH_FP32);
+      if (n < 0) return -1.0;
+      if (split && n > 1) {  // the first product on 128-wide fp32 tiles, the others on 256-wide ones
+        const double t = B / 256;
+        return full * (tri(DASH_FP32) + (n - 1) * (t * (t + 1) / 2) / (t * t));
+      }
+      return n * full * tri(DASH_FP32);
     case DASH_OP_APPLY: return 2.0 * full;
     case DASH_OP_STATS: return 2.0 * full * tri(DASH_FP32);
     case DASH_OP_SCALE: return a1 < 1 ? -1.0 : 2.0 * B * (double)B * 32.0 * a1 * (double)N;
@@ -493,7 +502,8 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
                                 size_t* bytes) {
   if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
-  if (prec != DASH_FP32 && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (prec == DASH_FP32_SPLIT) prec = DASH_FP32;
   switch (op) {
     case DASH_OP_SCALE:
       if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;
@@ -963,6 +973,13 @@ dash_status dash_inverse_root_cn_adaptive(const float* A, const float* s, int64_
 
 dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, double lo,
                                    double hi, float* X, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return dash_inverse_root_cheb_prec(A, s, N, B, degree, lo, hi, DASH_FP32, X, status, ws, ws_bytes, stream);
+}
+
+dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
+                                        double lo, double hi, dash_prec prec, float* X, int32_t* status, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (X == A || degree < 1 || degree > 64) return DASH_ERR_INVALID_ARG;
@@ -1021,8 +1038,13 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
     Product pr = prod(A, Y, D, (const float*)Y, E);
     return std::make_pair(pr, e);
   };
+  // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
+  // stored mirrored; the first product, which maps A as it stages it, stays on the fp32 cores
+  const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
   auto run = [&](std::pair<Product, Epilogue> pe) {
-    return launch_gemm(&pe.first, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, true, pe.second, st);
+    const bool sp = split && !pe.first.map_y;
+    return launch_gemm(&pe.first, 1, N, B, sp ? DASH_FP32_SPLIT : DASH_FP32, DASH_FP32, Trans::NN, true, pe.second,
+                       st, sp);
   };
   auto map_first = [&](Product& p) {  // Y = A read as b_{d-1}
     p.map_y = true;

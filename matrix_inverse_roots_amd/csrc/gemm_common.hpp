@@ -1,4 +1,5 @@
-// gemm_common.hpp -- pieces shared by the batched-product kernels (gemm_f32.hip, gemm_f16.hip):
+// gemm_common.hpp -- pieces shared by the batched-product kernels (gemm_f32.hip, gemm_f16.hip,
+// gemm_split.hip):
 // launch arguments, the XCD-aware workgroup -> (problem, block, tile) map and the fused epilogue.
 #pragma once
 
@@ -399,6 +400,9 @@ __device__ __forceinline__ void pass_tile_f16(const Product& P, const TE* X, con
 // kernel launchers of the two precisions
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
 hipError_t launch_f16(GemmArgs& a, dash_prec in_prec, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
+// fp32 products from three-piece bfloat16 splits (gemm_split.hip): symmetric results, exactly
+// symmetric right operand, B % 256 == 0
+hipError_t launch_split(GemmArgs& a, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

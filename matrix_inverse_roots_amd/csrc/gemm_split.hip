@@ -1,0 +1,180 @@
+// gemm_split.hip -- batched fp32 B x B products on the bfloat16 matrix cores.
+//
+// Each fp32 operand element x is cut into three bfloat16 pieces, x0 = bf16(x), x1 = bf16(x - x0),
+// x2 = x - x0 - x1, and the cut is exact: x's 24-bit significand leaves at most 16 significant
+// bits in x - x0 and at most 8 in x - x0 - x1, every difference is exact in fp32 and x2 fits
+// bfloat16's 8 bits (for |x| above 2^-100, far below any operand here).  A product of two pieces
+// has at most 16 significant bits, so the 32x32x16 bfloat16 MFMA forms it exactly and accumulates
+// it in fp32.  The product X Y is the sum of the six piece products x_i y_j with i + j <= 2; the
+// three left out are below 2^-23 of |x||y| element by element, the size of fp32's own rounding.
+// The pages fix the iterations' arithmetic as fp32 and say nothing of how a matrix unit forms a
+// product; this is one way to form an fp32 product, measured against fp64 to be as accurate as
+// the fp32 MFMA.  On this chip the bfloat16 matrix rate is 16 times the fp32 one, so six products of
+// pieces cost 6/16 of one fp32 product in MFMA time.
+//
+// Operands stay fp32 in memory (the same HBM bytes as the fp32 kernel); the split happens while a
+// k-slice moves from the register ring to LDS, where each operand slice is held as three bfloat16
+// planes.  Shape: TILE = 256 output tile, 8 waves of 128 x 64 (two per SIMD), k-slice 16 (one MFMA
+// depth), a 4-deep register ring, LDS double buffer of 2 x 6 planes (96 KiB).  The right operand
+// must be exactly symmetric (Y^T == Y bitwise, as every Clenshaw term b_{k+1} is: it is stored
+// mirrored), so its columns are read as rows and both operands stage 32-byte row pieces.
+// Products with symmetric results only (upper-triangle tiles, mirrored on store).  The epilogue
+// reads C and E from memory: folding C = Y from the staged planes, as the fp32 kernel does, costs
+// this kernel's register budget more than the read (measured slower).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "gemm_common.hpp"
+
+namespace dash {
+namespace gemm {
+namespace {
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// x = p0 + p1 + p2 for the 8 elements lo[0..3], hi[0..3]
+__device__ __forceinline__ void split3(const f32x4& lo, const f32x4& hi, bf16x8& p0, bf16x8& p1, bf16x8& p2) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float x = q < 4 ? lo[q] : hi[q - 4];
+    const __bf16 a0 = (__bf16)x;
+    const float r1 = x - (float)a0;
+    const __bf16 a1 = (__bf16)r1;
+    p0[q] = a0;
+    p1[q] = a1;
+    p2[q] = (__bf16)(r1 - (float)a1);
+  }
+}
+
+// LDS rows are 16 bfloat16 (two 16-byte chunks); rows 4..7 of every 8 swap their chunks so that the
+// 16-byte fragment reads of 8 consecutive rows hit distinct banks
+__device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1); }
+
+template <bool CHECKS>
+__global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
+  constexpr int TILE = 256, BK = 16, DEPTH = 4;
+  constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
+  constexpr int PLANE = TILE * BK;  // bfloat16 of one piece plane of one operand slice
+  constexpr int BUF = 6 * PLANE;    // X pieces 0..2, then Y pieces 0..2
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+
+  const TileCoord tc = decode_tile(a, true);
+  const Product P = tc.prob ? a.p1 : a.p0;
+  const int B = a.B;
+  const int64_t off = tc.b * (int64_t)B * B;
+  const float* X = (const float*)P.X + off;
+  const float* Y = (const float*)P.Y + off;
+  const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int li = lane & 31, h = lane >> 5;
+  const int srow = tid >> 1, sch = tid & 1;  // staged piece: row srow, k 8 sch .. 8 sch + 7
+
+  f32x4 rx[DEPTH][2], ry[DEPTH][2];
+  auto gload = [&](auto slot_c, int k0) {
+    constexpr int slot = decltype(slot_c)::value;
+    const float* xp = X + (int64_t)(i0 + srow) * B + k0 + 8 * sch;
+    const float* yp = Y + (int64_t)(j0 + srow) * B + k0 + 8 * sch;
+    rx[slot][0] = *(const f32x4*)xp;
+    rx[slot][1] = *(const f32x4*)(xp + 4);
+    ry[slot][0] = *(const f32x4*)yp;
+    ry[slot][1] = *(const f32x4*)(yp + 4);
+  };
+  auto sstore = [&](auto slot_c, int buf) {
+    constexpr int slot = decltype(slot_c)::value;
+    __bf16* s = smem + buf * BUF + srow * BK + 8 * swz2(srow, sch);
+    bf16x8 p0, p1, p2;
+    split3(rx[slot][0], rx[slot][1], p0, p1, p2);
+    *(bf16x8*)(s) = p0;
+    *(bf16x8*)(s + PLANE) = p1;
+    *(bf16x8*)(s + 2 * PLANE) = p2;
+    split3(ry[slot][0], ry[slot][1], p0, p1, p2);
+    *(bf16x8*)(s + 3 * PLANE) = p0;
+    *(bf16x8*)(s + 4 * PLANE) = p1;
+    *(bf16x8*)(s + 5 * PLANE) = p2;
+  };
+
+  f32x16 acc[MTM][MTN];
+#pragma unroll
+  for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+  // one k-slice: lane half h takes k = 8h .. 8h + 7 of the slice for both operands; one right
+  // piece at a time (its two fragments), each left piece read per use
+  auto compute = [&](int buf) {
+    const __bf16* s = smem + buf * BUF;
+#pragma unroll
+    for (int pb = 0; pb < 3; ++pb) {
+      bf16x8 bv[MTN];
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt) {
+        const int row = wn * WTN + nt * 32 + li;
+        bv[nt] = *(const bf16x8*)&s[(3 + pb) * PLANE + row * BK + 8 * swz2(row, h)];
+      }
+#pragma unroll
+      for (int pa = 0; pa + pb < 3; ++pa)
+#pragma unroll
+        for (int mt = 0; mt < MTM; ++mt) {
+          const int row = wm * WTM + mt * 32 + li;
+          const bf16x8 av = *(const bf16x8*)&s[pa * PLANE + row * BK + 8 * swz2(row, h)];
+#pragma unroll
+          for (int nt = 0; nt < MTN; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+  };
+
+  const int KT = B / BK;  // a multiple of 16 (B % 256 == 0)
+  // Steady state: the loads of slice kt + DEPTH go into the registers slice kt vacated, slice
+  // kt + 1 moves from registers to the other LDS buffer, then the MFMAs consume slice kt.
+  auto step = [&](auto slot_c, int kt) {
+    constexpr int slot = decltype(slot_c)::value;  // == kt % DEPTH
+    gload(slot_c, (kt + DEPTH) * BK);
+    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    compute(slot & 1);
+    __syncthreads();
+  };
+  auto tail_step = [&](auto slot_c, bool store_next) {
+    constexpr int slot = decltype(slot_c)::value;
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    compute(slot & 1);
+    __syncthreads();
+  };
+  gload(IC<0>{}, 0);
+  gload(IC<1>{}, BK);
+  gload(IC<2>{}, 2 * BK);
+  gload(IC<3>{}, 3 * BK);
+  sstore(IC<0>{}, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + DEPTH < KT; kt += DEPTH) {
+    step(IC<0>{}, kt);
+    step(IC<1>{}, kt + 1);
+    step(IC<2>{}, kt + 2);
+    step(IC<3>{}, kt + 3);
+  }
+  tail_step(IC<0>{}, true);
+  tail_step(IC<1>{}, true);
+  tail_step(IC<2>{}, true);
+  tail_step(IC<3>{}, false);
+  epilogue<MTM, MTN, WTM, WTN, true, float, true, true, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
+}
+
+}  // namespace
+
+hipError_t launch_split(GemmArgs& a, hipStream_t stream) {
+  if (a.B % 256 != 0) return hipErrorInvalidValue;
+  a.tdim = a.B / 256;
+  a.tiles = a.tdim * (a.tdim + 1) / 2;
+  a.epi.fold_c = false;  // C (Clenshaw's b_{k+1} == Y) comes from memory; beta already carries its weight
+  return wants_checks(a.epi) ? launch(gemm_split_kernel<true>, a, stream, 512)
+                             : launch(gemm_split_kernel<false>, a, stream, 512);
+}
+
+}  // namespace gemm
+}  // namespace dash

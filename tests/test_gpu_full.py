@@ -182,6 +182,15 @@ def test_full_step_chebyshev(stack):
     idx = ORACLE_SAMPLE
     X_ref = oracle.cheb_inverse_root(host(A[idx]), host(s)[idx], 24, lo, 1.25)
     assert np.max(rel_err(host(X[idx]), X_ref)) < ITERATE_TOL
+    # the same solve with split products (fp32 on the bfloat16 matrix cores), same gate
+    Xs = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32_SPLIT, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, N, B, 24, lo, 1.25, dash.DASH_FP32_SPLIT, Xs, status=status, ws=ws)
+    del ws
+    assert int(status.abs().sum()) == 0
+    assert np.max(rel_err(host(Xs[idx]), X_ref)) < ITERATE_TOL
+    assert torch.equal(Xs[idx], Xs[idx].transpose(1, 2))
+    del Xs
     U = torch.empty((NG, B, B), device=DEV)
     ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
     dash.dash_apply(X[:NG], X[NG:], G, NG, B, U, ws)

@@ -1,0 +1,111 @@
+"""GPU parity of the Chebyshev solve with split products (DASH_FP32_SPLIT): every product but the
+first forms its fp32 result on the bfloat16 matrix cores from exact three-piece splits of both
+operands.  The gates are the fp32 ones (iterate parity 1e-4 against the oracle's fp64 Clenshaw
+recurrence, residual 1e-3), since the split product is an fp32 product: the split is exact and the
+piece products it leaves out are below fp32's own rounding.  Where the split does not apply
+(degree 2: the only product is the first; B not a multiple of 256) the result is the fp32 path's,
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import dash_inputs as di
+import matrix_inverse_roots_amd as dash
+import oracle
+from gpu_helpers import DEV, ITERATE_TOL, R_FP32, frob_scale, power_scale, rel_err, residual, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SPLIT = dash.DASH_FP32_SPLIT
+
+
+def cheb_p(A, s, degree, lo, hi, prec):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, N, B, degree, lo, hi, prec, X, status=status, ws=ws)
+    return X, status
+
+
+def spectrum_stack(seed, N, B, lam_min=0.05):
+    A = di.known_spectrum_stack(seed, N, B, lam_min, 1.0)[0].astype(np.float32)
+    return A, to_dev(A)
+
+
+@pytest.mark.parametrize("B,N,degrees", [(256, 4, (3, 8, 24)), (512, 2, (24,))])
+def test_cheb_split_matches_oracle(B, N, degrees):
+    """Several 256-wide tiles per block (B = 512: 3 of the 4 x 4 tile grid's upper triangle rows),
+    power-iteration scale, the pages' interval reading hi = 1.25."""
+    A, Ad = spectrum_stack(400 + B, N, B)
+    s = power_scale(Ad, to_dev(di.start_vectors(B, 32)), 10)
+    lo, hi = 0.04, 1.25
+    for d in degrees:
+        X, status = cheb_p(Ad, s, d, lo, hi, SPLIT)
+        Xh = to_host(X)
+        ref = oracle.cheb_inverse_root(A, to_host(s), d, lo, hi)
+        err = rel_err(Xh, ref)
+        print("B", B, "degree", d, "split err", err.max())
+        assert np.all(to_host(status) == 0)
+        assert err.max() < ITERATE_TOL
+        assert np.array_equal(Xh, np.swapaxes(Xh, 1, 2))  # triangle-only products, mirrored
+        if d == 24:
+            assert residual(Xh, A).max() < R_FP32
+            # as accurate as the fp32 matrix cores on the same recurrence
+            Xf, _ = cheb_p(Ad, s, d, lo, hi, dash.DASH_FP32)
+            err_f = rel_err(to_host(Xf), ref)
+            print("fp32 err", err_f.max())
+            assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+
+
+def test_cheb_split_falls_back_to_fp32_bitwise():
+    """Degree 2 runs only the first product (A mapped as it is staged, on the fp32 cores); B = 320
+    has no 256-wide tiling: both equal the fp32 path bit for bit."""
+    A, Ad = spectrum_stack(410, 2, 256)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 2, 0.02, 1.0, SPLIT)
+    X2, _ = cheb_p(Ad, s, 2, 0.02, 1.0, dash.DASH_FP32)
+    assert torch.equal(X1, X2)
+    A, Ad = spectrum_stack(411, 2, 320)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 12, 0.02, 1.0, SPLIT)
+    X2, _ = cheb_p(Ad, s, 12, 0.02, 1.0, dash.DASH_FP32)
+    assert torch.equal(X1, X2)
+
+
+def test_cheb_split_scale_equivariance_and_batch_independence():
+    """A power-of-two scale of A and s moves every piece and every rounding exactly, so
+    X(16 A, 16 s) = X(A, s) / 2 bit for bit; a permuted stack gives the permuted result, and one
+    block alone its result in the stack."""
+    A, Ad = spectrum_stack(412, 4, 256)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 12, 0.02, 1.0, SPLIT)
+    X16, _ = cheb_p(16 * Ad, 16 * s, 12, 0.02, 1.0, SPLIT)
+    assert torch.equal(X16 * 2, X1)
+    perm = torch.tensor([2, 0, 3, 1], device=DEV)
+    Xp, _ = cheb_p(Ad[perm].contiguous(), s[perm].contiguous(), 12, 0.02, 1.0, SPLIT)
+    assert torch.equal(Xp, X1[perm])
+    Xi, _ = cheb_p(Ad[2:3].contiguous(), s[2:3].contiguous(), 12, 0.02, 1.0, SPLIT)
+    assert torch.equal(Xi[0], X1[2])
+
+
+def test_cheb_split_flags_bad_blocks():
+    """A zero or NaN scale flags bit 0 and gives a NaN block; a non-finite input element (mirrored:
+    the products read the upper triangle) flags bit 1; the other blocks are untouched."""
+    A, Ad = spectrum_stack(413, 4, 256)
+    s = frob_scale(Ad).clone()
+    X_good, st_good = cheb_p(Ad, s, 8, 0.02, 1.0, SPLIT)
+    assert np.all(to_host(st_good) == 0)
+    s_bad = s.clone()
+    s_bad[1] = 0.0
+    s_bad[2] = float("nan")
+    X, st = cheb_p(Ad, s_bad, 8, 0.02, 1.0, SPLIT)
+    assert np.array_equal(to_host(st).astype(int) & 1, [0, 1, 1, 0])
+    assert np.all(np.isnan(to_host(X)[[1, 2]]))
+    assert torch.equal(X[[0, 3]], X_good[[0, 3]])
+    bad = Ad.clone()
+    bad[0, 3, 5] = float("inf")
+    bad[0, 5, 3] = float("inf")
+    Xb, stb = cheb_p(bad, s, 8, 0.02, 1.0, SPLIT)
+    assert np.array_equal(to_host(stb).astype(int) & 2, [2, 0, 0, 0])
+    assert torch.equal(Xb[1:], X_good[1:])
