@@ -38,7 +38,12 @@ EVD_MAX_SWEEPS = 20
 FP32_PEAK_TFLOPS = 157.3
 FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-PRODUCT_KERNEL = "gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>"
+# the Clenshaw product kernel of each product arithmetic, and the sources its traffic record is keyed to
+PRODUCT_KERNELS = {
+    "split": ("gemm_split_kernel<false>", ("gemm_common.hpp", "gemm_split.hip")),
+    "fp32": ("gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>", ("gemm_common.hpp", "gemm_f32.hip")),
+}
+SPLIT_PIECE_PRODUCTS = 6  # bfloat16 piece products per fp32 product in the split kernel
 
 
 def parse():
@@ -62,8 +67,13 @@ def parse():
                         "refreshing the roots of 1/f of the stack; c2: steps to reach the residual 1e-3 "
                         "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
+    p.add_argument("--cheb-prec", choices=["split", "fp32"], default="split",
+                   help="arithmetic of the Chebyshev products: split (fp32 products formed from exact "
+                        "three-piece bfloat16 splits on the bfloat16 matrix cores) or fp32 (the fp32 "
+                        "matrix cores)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                   help="write profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb")
+                   help="update profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb "
+                        "(for the --cheb-prec kernel)")
     return p.parse_args()
 
 
@@ -79,24 +89,23 @@ def cpu_threads():
     return max(1, n)
 
 
-PRODUCT_SOURCES = ("gemm_common.hpp", "gemm_f32.hip")
 
 
-def product_source_sha():
-    """sha256 over the sources of the fp32 product kernel (its epilogue and its body)."""
+def product_source_sha(prec):
+    """sha256 over the sources of a Clenshaw product kernel (its epilogue and its body)."""
     h = hashlib.sha256()
-    for name in PRODUCT_SOURCES:
+    for name in PRODUCT_KERNELS[prec][1]:
         h.update(open(os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
 
-def traffic_record():
+def traffic_record(prec):
     """Measured HBM bytes per product launch, if recorded for the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    if rec.get("product_source_sha256") != product_source_sha():
+    rec = json.load(open(path)).get(PRODUCT_KERNELS[prec][0])
+    if rec is None or rec.get("product_source_sha256") != product_source_sha(prec):
         return None
     return rec
 
@@ -104,7 +113,7 @@ def traffic_record():
 def main():
     args = parse()
     if args.traffic_from:
-        return traffic_from_counters(*args.traffic_from)
+        return traffic_from_counters(*args.traffic_from, args.cheb_prec)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every block of the stack is independent, and the benchmark "
               "runs on a single GPU only (run with --gpus 1)", file=sys.stderr)
@@ -119,7 +128,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.only == "cheb":
-        return only_cheb(dash, di, torch, dev)
+        return only_cheb(dash, di, torch, dev, args)
     if args.only in ("cn16", "ndb"):
         return only_solver(dash, di, torch, dev, args.only)
     if args.only == "evd":
@@ -154,7 +163,8 @@ def main():
     X = torch.empty((N, B, B), device=dev)
     s = torch.empty(N, device=dev)
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, device=dev)
+    cheb_prec = dash.DASH_FP32_SPLIT if args.cheb_prec == "split" else dash.DASH_FP32
+    ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
     # one interval for every block: hi = 1.25 above the power-iteration estimate, lo from the
     # damping floor of the statistics relative to the largest scale (taken once, before timing)
@@ -176,7 +186,7 @@ def main():
         mark(2)
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
         mark(3)
-        dash.dash_inverse_root_cheb(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, X, ws=ws_cheb)
+        dash.dash_inverse_root_cheb_prec(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
         mark(4)
         dash.dash_apply(X[:NG], X[NG:], G_stack, NG, B, U_stack, ws_apply)
         mark(5)
@@ -199,16 +209,35 @@ def main():
                 for i, p in enumerate(phases)}
     value = N / (wall / args.steps)
 
-    # dominant kernel: the fp32 product of the Clenshaw solve (d-1 launches per call, each one
-    # batched triangle-only product over all N blocks); its launch time from the events around the
-    # solve.  Flops are counted per computed tile (dash_flops).
+    # dominant kernel: the product of the Clenshaw solve (d-1 launches per call, each one batched
+    # triangle-only product over all N blocks); its launch time from the events around the solve.
+    # With split products the first product (A mapped into b_{d-1} as it is staged) runs on the fp32
+    # kernel: its time, from a degree-2 solve (that product alone), is taken out.  Flops are counted
+    # per computed tile (dash_flops).
     cheb_products = dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)
-    cheb_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32, CHEB_DEGREE, 0)
-    flop_per_launch = cheb_flop / cheb_products
+    cheb_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, cheb_prec, CHEB_DEGREE, 0)
+    kernel_name = PRODUCT_KERNELS[args.cheb_prec][0]
+    if args.cheb_prec == "split":
+        first_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32, 2, 0)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        dash.dash_inverse_root_cheb_prec(A, s, N, B, 2, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
+        e[0].record(stream)
+        for _ in range(3):
+            dash.dash_inverse_root_cheb_prec(A, s, N, B, 2, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        first_ms = e[0].elapsed_time(e[1]) / 3
+        launches = cheb_products - 1
+        flop_per_launch = (cheb_flop - first_flop) / launches
+        launch_ms = (phase_ms["cheb"] - first_ms) / launches
+    else:
+        first_ms = None
+        launches = cheb_products
+        flop_per_launch = cheb_flop / cheb_products
+        launch_ms = phase_ms["cheb"] / cheb_products
     tri = flop_per_launch / (2.0 * B ** 3 * N)
-    launch_ms = phase_ms["cheb"] / cheb_products
-    achieved = flop_per_launch / (launch_ms * 1e-3) / 1e12
-    rec = traffic_record()
+    fp32_equiv = flop_per_launch / (launch_ms * 1e-3) / 1e12
+    rec = traffic_record(args.cheb_prec)
     traffic, traffic_detail = None, None
     if rec is not None:
         # algorithmic bytes of one Clenshaw product launch: read A and b_{k+1} (operands), the upper
@@ -216,10 +245,24 @@ def main():
         traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
         traffic_detail = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
                           "algorithmic_bytes": 4.0 * B * B * N * (3 + tri), "source": "profiles/traffic.json"}
-    roofline = {"kernel": PRODUCT_KERNEL, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                "traffic": traffic, "traffic_detail": traffic_detail, "flop_per_launch": flop_per_launch,
-                "tiles_computed_fraction": round(tri, 4), "avg_launch_ms": round(launch_ms, 3)}
+    if args.cheb_prec == "split":
+        # the matrix cores run six bfloat16 piece products per fp32 product: the roof is the dense
+        # bfloat16 MFMA peak, against the piece products' flops
+        achieved = SPLIT_PIECE_PRODUCTS * fp32_equiv
+        roofline = {"kernel": kernel_name, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
+                    "flop_accounting": "bf16 MFMA flops of the six piece products per fp32 product",
+                    "fp32_product_tflops": round(fp32_equiv, 2),
+                    "fp32_product_frac_of_fp32_peak": round(fp32_equiv / FP32_PEAK_TFLOPS, 4)}
+    else:
+        achieved = fp32_equiv
+        roofline = {"kernel": kernel_name, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4)}
+    roofline.update({"traffic": traffic, "traffic_detail": traffic_detail, "flop_per_launch": flop_per_launch,
+                     "launches_per_step": launches, "tiles_computed_fraction": round(tri, 4),
+                     "avg_launch_ms": round(launch_ms, 3)})
+    if first_ms is not None:
+        roofline["first_product_ms"] = round(first_ms, 3)
 
     step_flop = (cheb_flop
                  + dash.dash_flops(dash.DASH_OP_STATS, NG, B, dash.DASH_FP32, 0, 0)
@@ -234,7 +277,7 @@ def main():
         "unstack_hbm_gbs": round(8.0 * B * B * NG / (phase_ms["unstack"] * 1e-3) / 1e9, 1),
         "cheb_interval": [lo, CHEB_HI],
     }
-    log("step %.1f ms, %.0f blocks/s, product %.2f TFLOP/s" % (ms_step, value, achieved))
+    log("step %.1f ms, %.0f blocks/s, product %.2f TFLOP/s (%s)" % (ms_step, value, achieved, args.cheb_prec))
     del ws_cheb, ws_apply, U_stack, G_stack
     torch.cuda.empty_cache()
 
@@ -261,7 +304,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama-2048 Shampoo step f=1: stack, EMA stats, power-iteration scale, "
                                "Chebyshev d=24 A^-1/4, apply, unstack",
-                   "N": N, "B": B, "tiles": NG, "solver": "chebyshev-clenshaw d=24 fp32",
+                   "N": N, "B": B, "tiles": NG,
+                   "solver": "chebyshev-clenshaw d=24 fp32" + (
+                       ", products formed from exact three-piece bfloat16 splits on the matrix cores"
+                       if args.cheb_prec == "split" else ", fp32 matrix cores"),
                    "scale": "power iteration k=32 T=10 fp32", "beta": BETA},
         "roofline": roofline,
         "breakdown": breakdown,
@@ -274,7 +320,7 @@ def main():
 REF_COPY_BYTES = 4 << 30  # dash_stack of 64 weights of 4096 x 4096 fp32: reads and writes 4 GiB
 
 
-def only_cheb(dash, di, torch, dev):
+def only_cheb(dash, di, torch, dev, args):
     """The run that HBM traffic counters are collected on: a plain copy of known size (dash_stack of
     4 GiB, float4 loads and stores like the product kernel) and then one degree-24 Clenshaw solve on
     the N=3072, B=1024 stack."""
@@ -288,7 +334,8 @@ def only_cheb(dash, di, torch, dev):
     lo = BETA * EPS / float(s.max().item())
     del ws
     X = torch.empty_like(A)
-    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=dev)
+    prec = dash.DASH_FP32_SPLIT if args.cheb_prec == "split" else dash.DASH_FP32
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
     ref = [torch.ones((4096, 4096), device=dev) for _ in range(REF_COPY_BYTES // (4096 * 4096 * 4))]
     ref_stack = torch.empty((REF_COPY_BYTES // (B * B * 4), B, B), device=dev)
     torch.cuda.synchronize()
@@ -296,10 +343,10 @@ def only_cheb(dash, di, torch, dev):
     e[0].record()
     dash.dash_stack(ref, B, ref_stack)
     e[1].record()
-    dash.dash_inverse_root_cheb(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, X, ws=ws)
+    dash.dash_inverse_root_cheb_prec(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, prec, X, ws=ws)
     e[2].record()
     torch.cuda.synchronize()
-    print(json.dumps({"mode": "cheb", "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
+    print(json.dumps({"mode": "cheb", "cheb_prec": args.cheb_prec, "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
                       "ref_copy_ms": round(e[0].elapsed_time(e[1]), 3), "cheb_ms": round(e[1].elapsed_time(e[2]), 3),
                       "products": dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)}), flush=True)
 
@@ -701,29 +748,37 @@ def only_adaptive(dash, di, torch, dev):
     print(json.dumps(out), flush=True)
 
 
-def traffic_from_counters(fetch_csv, write_csv):
-    """Write profiles/traffic.json from two rocprofv3 --pmc runs of `bench.py --only cheb`
-    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads for
-    the 4 GiB reference copy (the tile_copy dispatches of dash_stack in the same run)."""
+def traffic_from_counters(fetch_csv, write_csv, prec):
+    """Update profiles/traffic.json from two rocprofv3 --pmc runs of `bench.py --only cheb
+    --cheb-prec <prec>` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    what it reads for the 4 GiB reference copy (the tile_copy dispatches of dash_stack in the same
+    run).  One record per product kernel, keyed by its name."""
     import csv
 
+    kernel = PRODUCT_KERNELS[prec][0]
     out = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         ref = sum(float(r["Counter_Value"]) for r in rows if "tile_copy_kernel" in r["Kernel_Name"]) * 1024
-        gemm = [float(r["Counter_Value"]) * 1024 for r in rows if PRODUCT_KERNEL in r["Kernel_Name"]]
+        gemm = [float(r["Counter_Value"]) * 1024 for r in rows if kernel in r["Kernel_Name"]]
         factor = REF_COPY_BYTES / ref
         key = "fetch" if counter == "FETCH_SIZE" else "write"
         out[key + "_raw_bytes_per_launch"] = sum(gemm) / len(gemm)
         out[key + "_scale_factor"] = factor
         out[key + "_bytes_per_launch"] = factor * sum(gemm) / len(gemm)
         out[key + "_launches"] = len(gemm)
-    out["product_source_sha256"] = product_source_sha()
-    out["kernel"] = PRODUCT_KERNEL
-    out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb; "
-                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb")
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(out, f, indent=1)
+    out["product_source_sha256"] = product_source_sha(prec)
+    out["kernel"] = kernel
+    out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb --cheb-prec %s; "
+                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb --cheb-prec %s"
+                      % (prec, prec))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    recs = json.load(open(path)) if os.path.exists(path) else {}
+    if "kernel" in recs:  # a single record of the older layout
+        recs = {recs["kernel"]: recs}
+    recs[kernel] = out
+    with open(path, "w") as f:
+        json.dump(recs, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
 
@@ -799,6 +854,16 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     res["ndb_fp16_refine1"] = {"iters": [NDB_ITERS, NDB_ITERS], "correction_steps": 1, "ms": round(nh_ms, 2),
                                "blocks_per_s": round(N / (nh_ms * 1e-3), 1),
                                "residual_block0": evd_residual(torch, A, X, 0)}
+    # Chebyshev d=24 solve-only, fp32 matrix cores against split products (same power-iteration scale)
+    lo = BETA * EPS / float(s.max().item())
+    for name, prec in (("cheb_fp32", dash.DASH_FP32), ("cheb_split", dash.DASH_FP32_SPLIT)):
+        ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
+        ch_ms = timed(lambda: dash.dash_inverse_root_cheb_prec(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, prec, X, ws=ws))
+        del ws
+        torch.cuda.empty_cache()
+        fl = dash.dash_flops(dash.DASH_OP_CHEB, N, B, prec, CHEB_DEGREE, 0) / (ch_ms * 1e-3) / 1e12
+        res[name] = {"degree": CHEB_DEGREE, "ms": round(ch_ms, 2), "blocks_per_s": round(N / (ch_ms * 1e-3), 1),
+                     "fp32_product_tflops": round(fl, 2), "residual_block0": evd_residual(torch, A, X, 0)}
     # Frobenius scaling: one read of the stack
     fro_ms = timed(lambda: dash.dash_scale(A, N, B, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None))
     res["frobenius_scale"] = {"ms": round(fro_ms, 3),
