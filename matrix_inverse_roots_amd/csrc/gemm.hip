@@ -38,13 +38,9 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
   // and E in every problem, except the launches that map Y, which have none
   auto fold_ok = [&](const Product& p) { return p.C && p.C == p.Y && (p.map_y ? !p.E : p.E != nullptr); };
-  if (epi.fold_c && in_prec == DASH_FP32_SPLIT) {
-    for (int i = 0; i < nprob; ++i)
-      if (probs[i].C != probs[i].Y) return hipErrorInvalidValue;
-  } else if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) ||
-                            (nprob > 1 && !fold_ok(probs[1])))) {
+  if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) ||
+                     (nprob > 1 && !fold_ok(probs[1]))))
     return hipErrorInvalidValue;
-  }
   // operand maps exist in every binary16 kernel and, for the right operand, in the fp32 Clenshaw
   // launches
   const bool maps = probs[0].map_x || probs[0].map_y || (nprob > 1 && (probs[1].map_x || probs[1].map_y));
@@ -62,10 +58,11 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     return gemm::launch_f32(a, trans, sym, stream);
   }
   // fp32 operands split into bfloat16 pieces: symmetric products of an exactly symmetric right
-  // operand, 256-wide tiles, no operand maps, stopped blocks or second output (fold_c is accepted
-  // and C read from memory, with beta already set to its weight as every fold_c caller does)
+  // operand, 256-wide tiles, no operand maps, stopped blocks or second output; C is read from
+  // memory with its (beta, ib) weight, never folded
   if (in_prec == DASH_FP32_SPLIT) {
-    if (out_prec != DASH_FP32 || !sym || !y_sym || trans != Trans::NN || maps || frz || B % 256 != 0)
+    if (out_prec != DASH_FP32 || !sym || !y_sym || trans != Trans::NN || maps || frz || epi.fold_c ||
+        B % 256 != 0)
       return hipErrorInvalidValue;
     return gemm::launch_split(a, stream);
   }

@@ -171,7 +171,6 @@ hipError_t launch_split(GemmArgs& a, hipStream_t stream) {
   if (a.B % 256 != 0) return hipErrorInvalidValue;
   a.tdim = a.B / 256;
   a.tiles = a.tdim * (a.tdim + 1) / 2;
-  a.epi.fold_c = false;  // C (Clenshaw's b_{k+1} == Y) comes from memory; beta already carries its weight
   return wants_checks(a.epi) ? launch(gemm_split_kernel<true>, a, stream, 512)
                              : launch(gemm_split_kernel<false>, a, stream, 512);
 }
