@@ -817,6 +817,17 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     res["ndb_fp32"] = {"iters": [NDB_ITERS, NDB_ITERS], "products_per_block": prods, "ms": round(ndb_ms, 2),
                        "blocks_per_s": round(N / (ndb_ms * 1e-3), 1), "tflops": round(fl, 2),
                        "frac_fp32_peak": round(fl / FP32_PEAK_TFLOPS, 4), "scale_ms": round(scale_ms, 2)}
+    # NDB with split products (fp32 products on the bfloat16 matrix cores), same scale
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP32_SPLIT, device=dev)
+    nds_ms = timed(lambda: dash.dash_inverse_root_ndb_prec(A, s, N, B, NDB_ITERS, NDB_ITERS, dash.DASH_FP32_SPLIT, X,
+                                                           ws=ws))
+    del ws
+    torch.cuda.empty_cache()
+    fl = dash.dash_flops(dash.DASH_OP_NDB, N, B, dash.DASH_FP32_SPLIT, NDB_ITERS, NDB_ITERS) / (nds_ms * 1e-3) / 1e12
+    res["ndb_split"] = {"iters": [NDB_ITERS, NDB_ITERS], "ms": round(nds_ms, 2),
+                        "blocks_per_s": round(N / (nds_ms * 1e-3), 1), "fp32_product_tflops": round(fl, 2),
+                        "bf16_mfma_frac": round(SPLIT_PIECE_PRODUCTS * fl / FP16_PEAK_TFLOPS, 4),
+                        "residual_block0": evd_residual(torch, A, X, 0)}
     # CN fp16 after binary16 power-iteration scaling
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, K_VEC, device=dev)
     scale16_ms = timed(lambda: dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP16, K_VEC,

@@ -56,7 +56,8 @@ typedef enum {
  * dash_inverse_root_ndb_lowp) and their workspace/flop queries; dash_scale takes DASH_FP32 or DASH_FP16.
  * DASH_FP32_SPLIT: fp32 operands, iterates and results, with each product formed on the bfloat16
  * matrix cores from an exact three-piece split of both operands (six piece products, fp32
- * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec, by
+ * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec and
+ * dash_inverse_root_ndb_prec, by
  * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts the 256-wide
  * tiles of the split products). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3 } dash_prec;
@@ -126,6 +127,16 @@ dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, d
 dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
                                   int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/* dash_inverse_root_ndb with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix
+ * cores; the same as dash_inverse_root_ndb) or DASH_FP32_SPLIT (every product formed from exact
+ * three-piece bfloat16 splits of its fp32 operands on the bfloat16 matrix cores, 256 x 256 tiles,
+ * when B % 256 == 0; with other B the fp32 matrix cores).  Iterates stay fp32 and are never
+ * symmetrised.  Same arguments, workspace and results contract otherwise; DASH_ERR_INVALID_ARG for
+ * any other prec. */
+dash_status dash_inverse_root_ndb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, dash_prec prec, float* X, float* sqrt_out, float* monitor,
+                                       int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /* NDB with binary16 iterates and an fp32 correction ([PT] Resultados Experimentais: NDB in FP16/BF16
  * was unstable in the authors' runs; [PT] Significância e Alegações, "Direções Futuras": stabilising

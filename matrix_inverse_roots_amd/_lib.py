@@ -48,6 +48,7 @@ def library() -> ctypes.CDLL:
             "dash_update_stats": (st, [vp, i64, i32, f32, vp, vp]),
             "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_ndb_prec": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_half": (st, [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_lowp": (st, [vp, vp, i64, i32, i32, i32, st, i32, vp, vp, vp, vp, sz, vp]),
@@ -165,6 +166,13 @@ def dash_inverse_root_ndb(A, s, N: int, B: int, iters1: int, iters2: int, X, sqr
     _check("dash_inverse_root_ndb",
            library().dash_inverse_root_ndb(_ptr(A), _ptr(s), N, B, iters1, iters2, _ptr(X), _ptr(sqrt_out),
                                            _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+
+
+def dash_inverse_root_ndb_prec(A, s, N: int, B: int, iters1: int, iters2: int, prec: int, X, sqrt_out=None,
+                               monitor=None, status=None, ws=None, stream=None):
+    _check("dash_inverse_root_ndb_prec",
+           library().dash_inverse_root_ndb_prec(_ptr(A), _ptr(s), N, B, iters1, iters2, prec, _ptr(X), _ptr(sqrt_out),
+                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
 
 
 def dash_inverse_root_cn(A, s, N: int, B: int, p: int, iters: int, prec: int, X, monitor=None, status=None,

@@ -109,12 +109,16 @@ struct NdbCtx {
   int32_t* freeze = nullptr;
   float tol = 0.f;
   int32_t* steps = nullptr;
+  // products formed from three-piece bfloat16 splits (DASH_FP32_SPLIT) where the shape allows
+  bool split = false;
 };
 
 dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool scaled, int T, int mon_col,
                      bool want_z, float* final_out, float** y_out) {
   // step 0: Z_0 = I so P_0 = M and S_0 = (3I - M)/2; Y_1 = M S_0 = 1.5 M - 0.5 M^2, Z_1 = S_0.
   const bool last = (T == 1);
+  // every product is a general one (NDB iterates are never symmetrised)
+  const dash_prec PP = (c.split && !c.freeze && c.B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
   if (c.freeze) TRY(launch_freeze_reset(c.freeze, c.steps, 2, T, c.N, c.st));
   float* Z = nullptr;
   float* Y = nullptr;
@@ -150,7 +154,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     e.ib = scaled ? CO_R1 : CO_NONE;
     e.coef = c.coef;
     Product p = prod(M, M, Y, M);
-    TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+    TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
   }
   if (m_from_pool) c.pool->put((void*)M);
   if (last) {
@@ -183,7 +187,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
       }
       Product p = prod(Z, Y, S);
       p.freeze = c.freeze;  // a stopped block needs no S
-      TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+      TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
     }
     if (c.freeze)
       TRY(launch_freeze_update(c.monitor, c.mon_cols, mon_col + k, c.B, c.tol, c.freeze, c.steps, 2, k, c.N, c.st));
@@ -197,7 +201,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         Product p = prod(S, Z, final_out);
         p.freeze = c.freeze;
         p.pass = 2;
-        TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+        TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
       } else {  // Y_T = Y S
@@ -206,7 +210,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         Product p = prod(Y, S, Yn);
         p.freeze = c.freeze;
         p.pass = 1;
-        TRY(launch_gemm(&p, 1, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+        TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
         *y_out = Yn;
@@ -221,7 +225,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     p[0].freeze = p[1].freeze = c.freeze;
     p[0].pass = 1;
     p[1].pass = 2;
-    TRY(launch_gemm(p, 2, c.N, c.B, DASH_FP32, DASH_FP32, Trans::NN, false, e, c.st));
+    TRY(launch_gemm(p, 2, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
     c.pool->put(Y);
     c.pool->put(Z);
     c.pool->put(S);
@@ -600,7 +604,8 @@ struct Stop {
 
 dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1, int32_t iters2, float* X,
                      float* sqrt_out, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream,
-                     const Stop& stop) {
+                     const Stop& stop, dash_prec prec = DASH_FP32) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (sqrt_out && (!aligned(sqrt_out, 16) || sqrt_out == A || sqrt_out == X)) return DASH_ERR_INVALID_ARG;
@@ -620,6 +625,7 @@ dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32
   if (monitor) TRY(launch_fill_f32(monitor, N * cols, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
+  c.split = prec == DASH_FP32_SPLIT;
   if (stop.tol >= 0.f) {
     c.freeze = freeze;
     c.tol = stop.tol;
@@ -770,6 +776,12 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
                                   int32_t iters2, float* X, float* sqrt_out, float* monitor, int32_t* status,
                                   void* ws, size_t ws_bytes, void* stream) {
   return ndb_impl(A, s, N, B, iters1, iters2, X, sqrt_out, monitor, status, ws, ws_bytes, stream, Stop());
+}
+
+dash_status dash_inverse_root_ndb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,
+                                       int32_t iters2, dash_prec prec, float* X, float* sqrt_out, float* monitor,
+                                       int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return ndb_impl(A, s, N, B, iters1, iters2, X, sqrt_out, monitor, status, ws, ws_bytes, stream, Stop(), prec);
 }
 
 dash_status dash_inverse_root_ndb_adaptive(const float* A, const float* s, int64_t N, int32_t B, int32_t max_iters1,

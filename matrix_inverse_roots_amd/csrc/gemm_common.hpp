@@ -186,9 +186,10 @@ __device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, c
 }
 
 // HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
-// that E_PRE takes E's values from ev_pre, loaded by load_e).
+// that E_PRE takes E's values from ev_pre, loaded by load_e).  HAS_D2: the launch may carry a second
+// output (full products only).
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE, bool CHECKS,
-          bool E_PRE = false>
+          bool E_PRE = false, bool HAS_D2 = true>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                          const float (*ev_pre)[MTN][16] = nullptr) {
@@ -204,7 +205,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   const float al2 = e.alpha2 * coef_of(e, e.ia2, b);
   const float ga2 = e.gamma2 * coef_of(e, e.ig2, b);
   TO* D = (TO*)P.D + off;
-  TO* D2 = (!SYM && P.D2) ? (TO*)P.D2 + off : nullptr;
+  TO* D2 = (HAS_D2 && !SYM && P.D2) ? (TO*)P.D2 + off : nullptr;
   const float* C = P.C ? P.C + off : nullptr;
   const float* E = P.E ? P.E + off : nullptr;
   const int li = lane & 31, h = lane >> 5;
@@ -400,9 +401,9 @@ __device__ __forceinline__ void pass_tile_f16(const Product& P, const TE* X, con
 // kernel launchers of the two precisions
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
 hipError_t launch_f16(GemmArgs& a, dash_prec in_prec, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
-// fp32 products from three-piece bfloat16 splits (gemm_split.hip): symmetric results, exactly
-// symmetric right operand, B % 256 == 0
-hipError_t launch_split(GemmArgs& a, hipStream_t stream);
+// fp32 products from three-piece bfloat16 splits (gemm_split.hip), B % 256 == 0: symmetric results
+// of an exactly symmetric right operand (sym), or general products (every tile, any right operand)
+hipError_t launch_split(GemmArgs& a, bool sym, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

@@ -15,12 +15,16 @@
 // Operands stay fp32 in memory (the same HBM bytes as the fp32 kernel); the split happens while a
 // k-slice moves from the register ring to LDS, where each operand slice is held as three bfloat16
 // planes.  Shape: TILE = 256 output tile, 8 waves of 128 x 64 (two per SIMD), k-slice 16 (one MFMA
-// depth), a 4-deep register ring, LDS double buffer of 2 x 6 planes (96 KiB).  The right operand
-// must be exactly symmetric (Y^T == Y bitwise, as every Clenshaw term b_{k+1} is: it is stored
-// mirrored), so its columns are read as rows and both operands stage 32-byte row pieces.
-// Products with symmetric results only (upper-triangle tiles, mirrored on store).  The epilogue
-// reads C and E from memory: folding C = Y from the staged planes, as the fp32 kernel does, costs
-// this kernel's register budget more than the read (measured slower).
+// depth), a 4-deep register ring, LDS double buffer of 2 x 6 planes (96 KiB).  Both operands sit in
+// LDS as rows of 16 consecutive k per output row (X) or output column (Y).
+// SYM (symmetric results: Chebyshev): upper-triangle tiles, mirrored on store; the right operand
+// must then be exactly symmetric (Y^T == Y bitwise, as every Clenshaw term b_{k+1} is: it is stored
+// mirrored), so its columns are read as rows with 32-byte row loads.  YT (general right operand:
+// NDB): every tile; each thread loads 8 consecutive k of one Y column with scalar loads (the lanes
+// of a wave read 64 consecutive columns, 256 contiguous bytes per load) and stores them as that
+// column's 16-byte LDS row piece.  The epilogue reads C and E from memory: folding C = Y from the
+// staged planes, as the fp32 kernel does, costs this kernel's register budget more than the read
+// (measured slower).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -48,11 +52,15 @@ __device__ __forceinline__ void split3(const f32x4& lo, const f32x4& hi, bf16x8&
   }
 }
 
+// Word 3 of a raw buffer resource on this architecture: 32-bit data format, no swizzle, byte
+// offsets (the loads here are untyped).
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
 // LDS rows are 16 bfloat16 (two 16-byte chunks); rows 4..7 of every 8 swap their chunks so that the
 // 16-byte fragment reads of 8 consecutive rows hit distinct banks
 __device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1); }
 
-template <bool CHECKS>
+template <bool CHECKS, bool SYM, bool YT>
 __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 16, DEPTH = 4;
   constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
@@ -60,7 +68,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int BUF = 6 * PLANE;    // X pieces 0..2, then Y pieces 0..2
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
 
-  const TileCoord tc = decode_tile(a, true);
+  const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
   const int B = a.B;
   const int64_t off = tc.b * (int64_t)B * B;
@@ -71,16 +79,39 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   const int wm = wave >> 2, wn = wave & 3;
   const int li = lane & 31, h = lane >> 5;
   const int srow = tid >> 1, sch = tid & 1;  // staged piece: row srow, k 8 sch .. 8 sch + 7
+  const int ycol = tid & 255, ykh = tid >> 8;  // YT: column ycol, k 8 ykh .. 8 ykh + 7
+  const int yrow = YT ? ycol : srow, ych = YT ? ykh : sch;  // the Y piece's LDS row and chunk
+
+  // YT: Y's block as a buffer (out-of-range reads return 0; every offset here is in range), the
+  // lane's column and k-half as a 32-bit byte offset
+  __amdgpu_buffer_rsrc_t yrs;
+  int yvoff = 0;
+  if constexpr (YT) {
+    // the block's address is the same in every lane; say so, or every load becomes a loop over
+    // the distinct descriptors of the wave
+    const uint64_t ya = (uint64_t)Y;
+    const uint64_t yu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ya >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ya);
+    yrs = __builtin_amdgcn_make_buffer_rsrc((void*)yu, (short)0, B * B * 4, BUFFER_RSRC_WORD3);
+    yvoff = (8 * ykh * B + j0 + ycol) * 4;
+  }
 
   f32x4 rx[DEPTH][2], ry[DEPTH][2];
   auto gload = [&](auto slot_c, int k0) {
     constexpr int slot = decltype(slot_c)::value;
     const float* xp = X + (int64_t)(i0 + srow) * B + k0 + 8 * sch;
-    const float* yp = Y + (int64_t)(j0 + srow) * B + k0 + 8 * sch;
     rx[slot][0] = *(const f32x4*)xp;
     rx[slot][1] = *(const f32x4*)(xp + 4);
-    ry[slot][0] = *(const f32x4*)yp;
-    ry[slot][1] = *(const f32x4*)(yp + 4);
+    if constexpr (YT) {  // row k0 + 8 ykh + q: the wave-uniform part of the offset in a scalar
+#pragma unroll
+      for (int q = 0; q < 8; ++q)  // (the load returns the word's bits as an integer)
+        ry[slot][q >> 2][q & 3] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(yrs, yvoff, (k0 + q) * B * 4, 0));
+    } else {
+      const float* yp = Y + (int64_t)(j0 + srow) * B + k0 + 8 * sch;
+      ry[slot][0] = *(const f32x4*)yp;
+      ry[slot][1] = *(const f32x4*)(yp + 4);
+    }
   };
   auto sstore = [&](auto slot_c, int buf) {
     constexpr int slot = decltype(slot_c)::value;
@@ -90,10 +121,11 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
     *(bf16x8*)(s) = p0;
     *(bf16x8*)(s + PLANE) = p1;
     *(bf16x8*)(s + 2 * PLANE) = p2;
+    __bf16* t = smem + buf * BUF + 3 * PLANE + yrow * BK + 8 * swz2(yrow, ych);
     split3(ry[slot][0], ry[slot][1], p0, p1, p2);
-    *(bf16x8*)(s + 3 * PLANE) = p0;
-    *(bf16x8*)(s + 4 * PLANE) = p1;
-    *(bf16x8*)(s + 5 * PLANE) = p2;
+    *(bf16x8*)(t) = p0;
+    *(bf16x8*)(t + PLANE) = p1;
+    *(bf16x8*)(t + 2 * PLANE) = p2;
   };
 
   f32x16 acc[MTM][MTN];
@@ -162,17 +194,21 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   tail_step(IC<1>{}, true);
   tail_step(IC<2>{}, true);
   tail_step(IC<3>{}, false);
-  epilogue<MTM, MTN, WTM, WTN, true, float, true, true, TILE, CHECKS>(a, tc, P, acc, wm, wn, lane);
+  epilogue<MTM, MTN, WTM, WTN, SYM, float, true, true, TILE, CHECKS, false, false>(a, tc, P, acc, wm, wn, lane);
 }
 
 }  // namespace
 
-hipError_t launch_split(GemmArgs& a, hipStream_t stream) {
+hipError_t launch_split(GemmArgs& a, bool sym, hipStream_t stream) {
   if (a.B % 256 != 0) return hipErrorInvalidValue;
   a.tdim = a.B / 256;
-  a.tiles = a.tdim * (a.tdim + 1) / 2;
-  return wants_checks(a.epi) ? launch(gemm_split_kernel<true>, a, stream, 512)
-                             : launch(gemm_split_kernel<false>, a, stream, 512);
+  a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
+  const bool checks = wants_checks(a.epi);
+  if (sym)
+    return checks ? launch(gemm_split_kernel<true, true, false>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, false>, a, stream, 512);
+  return checks ? launch(gemm_split_kernel<true, false, true>, a, stream, 512)
+                : launch(gemm_split_kernel<false, false, true>, a, stream, 512);
 }
 
 }  // namespace gemm

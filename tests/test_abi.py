@@ -226,9 +226,10 @@ def test_bfloat16_queries_and_argument_errors():
                       ws=FakeWs(P3, 1 << 30)) == _lib.DASH_ERR_INVALID_ARG
 
 def test_split_precision_queries_and_argument_errors():
-    """DASH_FP32_SPLIT: the workspace of the fp32 Chebyshev solve; dash_flops counts the first
-    product on 128-wide tiles and the others on 256-wide ones (fp32 tiles when B % 256 != 0); only
-    dash_inverse_root_cheb_prec takes it, and that entry takes nothing else but DASH_FP32."""
+    """DASH_FP32_SPLIT: the workspace of the fp32 solves; dash_flops counts the first Chebyshev
+    product on 128-wide tiles and the others on 256-wide ones (fp32 tiles when B % 256 != 0) and
+    NDB's full products as fp32's; only the *_prec solver entries take it, and they take nothing
+    else but DASH_FP32."""
     for B in (256, 320, 1024):
         assert dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32_SPLIT) == \
             dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32)
@@ -249,5 +250,14 @@ def test_split_precision_queries_and_argument_errors():
                       ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
     assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 3, dash.DASH_FP32_SPLIT, 5 * P,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    h = dash.dash_inverse_root_ndb_prec
+    for prec in (dash.DASH_FP16, dash.DASH_BF16, 7):
+        assert _status_of(h, P, P2, N, B, 5, 5, prec, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(h, P, P2, N, B, 0, 5, dash.DASH_FP32_SPLIT, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(h, P, P2, N, 96, 5, 5, dash.DASH_FP32_SPLIT, 5 * P, ws=ws) == _lib.DASH_ERR_SHAPE
+    assert _status_of(h, P, P2, N, B, 5, 5, dash.DASH_FP32_SPLIT, 5 * P,
+                      ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
+    assert dash.dash_flops(dash.DASH_OP_NDB, 3, 1024, dash.DASH_FP32_SPLIT, 6, 6) == \
+        dash.dash_flops(dash.DASH_OP_NDB, 3, 1024, dash.DASH_FP32, 6, 6)
     assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32_SPLIT, 8, 10, P2, P3,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
