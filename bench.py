@@ -54,12 +54,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "evd", "adaptive", "ndb16", "bf16", "freq",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "ndbsplit", "evd", "adaptive", "ndb16", "bf16", "freq",
                                       "c2", "libref"],
                    default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
-                        "(the run that HBM traffic counters are collected on); cn16 / ndb: one "
-                        "CN fp16 / NDB fp32 solve with its scaling (for kernel profiles); evd: one "
+                        "(the run that HBM traffic counters are collected on); cn16 / ndb / ndbsplit: "
+                        "one CN fp16 / NDB fp32 / NDB split-product solve with its scaling (for kernel "
+                        "profiles); evd: one "
                         "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
                         "iterates and 0-2 correction steps; bf16: CN and NDB with bfloat16 iterates "
@@ -129,7 +130,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.only == "cheb":
         return only_cheb(dash, di, torch, dev, args)
-    if args.only in ("cn16", "ndb"):
+    if args.only in ("cn16", "ndb", "ndbsplit"):
         return only_solver(dash, di, torch, dev, args.only)
     if args.only == "evd":
         return only_evd(dash, di, torch, dev)
@@ -352,7 +353,8 @@ def only_cheb(dash, di, torch, dev, args):
 
 
 def only_solver(dash, di, torch, dev, which):
-    """One scaled solve on the N=3072, B=1024 stack: CN p=4 fp16 (5 steps) or NDB fp32 (6+6 steps)."""
+    """One scaled solve on the N=3072, B=1024 stack: CN p=4 fp16 (5 steps), NDB fp32 (6+6 steps) on
+    the fp32 matrix cores, or NDB with split products (ndbsplit)."""
     B = BLOCK
     N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
     A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
@@ -370,8 +372,9 @@ def only_solver(dash, di, torch, dev, which):
         ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=dev)
         dash.dash_inverse_root_cn(A, s, N, B, 4, CN_ITERS, prec, X, ws=ws)
     else:
-        ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=dev)
-        dash.dash_inverse_root_ndb(A, s, N, B, NDB_ITERS, NDB_ITERS, X, ws=ws)
+        nprec = dash.DASH_FP32_SPLIT if which == "ndbsplit" else dash.DASH_FP32
+        ws = dash.workspace(dash.DASH_OP_NDB, N, B, nprec, device=dev)
+        dash.dash_inverse_root_ndb_prec(A, s, N, B, NDB_ITERS, NDB_ITERS, nprec, X, ws=ws)
     e[2].record()
     torch.cuda.synchronize()
     print(json.dumps({"mode": which, "N": N, "B": B, "scale_ms": round(e[0].elapsed_time(e[1]), 3),
