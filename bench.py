@@ -40,7 +40,7 @@ FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 # the Clenshaw product kernel of each product arithmetic, and the sources its traffic record is keyed to
 PRODUCT_KERNELS = {
-    "split": ("gemm_split_kernel<false>", ("gemm_common.hpp", "gemm_split.hip")),
+    "split": ("gemm_split_kernel<false, true, false, false>", ("gemm_common.hpp", "gemm_split.hip")),
     "fp32": ("gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>", ("gemm_common.hpp", "gemm_f32.hip")),
 }
 SPLIT_PIECE_PRODUCTS = 6  # bfloat16 piece products per fp32 product in the split kernel
@@ -68,13 +68,13 @@ def parse():
                         "refreshing the roots of 1/f of the stack; c2: steps to reach the residual 1e-3 "
                         "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
-    p.add_argument("--cheb-prec", choices=["split", "fp32"], default="split",
-                   help="arithmetic of the Chebyshev products: split (fp32 products formed from exact "
-                        "three-piece bfloat16 splits on the bfloat16 matrix cores) or fp32 (the fp32 "
-                        "matrix cores)")
+    p.add_argument("--prec", choices=["split", "fp32"], default="split",
+                   help="arithmetic of the step's fp32 products (statistics, Chebyshev, apply): split "
+                        "(fp32 products formed from exact three-piece bfloat16 splits on the bfloat16 "
+                        "matrix cores) or fp32 (the fp32 matrix cores)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="update profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb "
-                        "(for the --cheb-prec kernel)")
+                        "(for the --prec kernel)")
     return p.parse_args()
 
 
@@ -114,7 +114,7 @@ def traffic_record(prec):
 def main():
     args = parse()
     if args.traffic_from:
-        return traffic_from_counters(*args.traffic_from, args.cheb_prec)
+        return traffic_from_counters(*args.traffic_from, args.prec)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every block of the stack is independent, and the benchmark "
               "runs on a single GPU only (run with --gpus 1)", file=sys.stderr)
@@ -164,7 +164,7 @@ def main():
     X = torch.empty((N, B, B), device=dev)
     s = torch.empty(N, device=dev)
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    cheb_prec = dash.DASH_FP32_SPLIT if args.cheb_prec == "split" else dash.DASH_FP32
+    cheb_prec = dash.DASH_FP32_SPLIT if args.prec == "split" else dash.DASH_FP32  # every product of the step
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
     # one interval for every block: hi = 1.25 above the power-iteration estimate, lo from the
@@ -183,13 +183,13 @@ def main():
         mark(0)
         dash.dash_stack(grads, B, G_stack)
         mark(1)
-        dash.dash_update_stats(G_stack, NG, B, BETA, A)
+        dash.dash_update_stats_prec(G_stack, NG, B, BETA, cheb_prec, A)
         mark(2)
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
         mark(3)
         dash.dash_inverse_root_cheb_prec(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
         mark(4)
-        dash.dash_apply(X[:NG], X[NG:], G_stack, NG, B, U_stack, ws_apply)
+        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, cheb_prec, U_stack, ws_apply)
         mark(5)
         dash.dash_unstack(U_stack, B, updates)
         mark(6)
@@ -217,8 +217,8 @@ def main():
     # per computed tile (dash_flops).
     cheb_products = dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)
     cheb_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, cheb_prec, CHEB_DEGREE, 0)
-    kernel_name = PRODUCT_KERNELS[args.cheb_prec][0]
-    if args.cheb_prec == "split":
+    kernel_name = PRODUCT_KERNELS[args.prec][0]
+    if args.prec == "split":
         first_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32, 2, 0)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         dash.dash_inverse_root_cheb_prec(A, s, N, B, 2, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
@@ -238,7 +238,7 @@ def main():
         launch_ms = phase_ms["cheb"] / cheb_products
     tri = flop_per_launch / (2.0 * B ** 3 * N)
     fp32_equiv = flop_per_launch / (launch_ms * 1e-3) / 1e12
-    rec = traffic_record(args.cheb_prec)
+    rec = traffic_record(args.prec)
     traffic, traffic_detail = None, None
     if rec is not None:
         # algorithmic bytes of one Clenshaw product launch: read A and b_{k+1} (operands), the upper
@@ -246,7 +246,7 @@ def main():
         traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
         traffic_detail = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
                           "algorithmic_bytes": 4.0 * B * B * N * (3 + tri), "source": "profiles/traffic.json"}
-    if args.cheb_prec == "split":
+    if args.prec == "split":
         # the matrix cores run six bfloat16 piece products per fp32 product: the roof is the dense
         # bfloat16 MFMA peak, against the piece products' flops
         achieved = SPLIT_PIECE_PRODUCTS * fp32_equiv
@@ -278,7 +278,7 @@ def main():
         "unstack_hbm_gbs": round(8.0 * B * B * NG / (phase_ms["unstack"] * 1e-3) / 1e9, 1),
         "cheb_interval": [lo, CHEB_HI],
     }
-    log("step %.1f ms, %.0f blocks/s, product %.2f TFLOP/s (%s)" % (ms_step, value, achieved, args.cheb_prec))
+    log("step %.1f ms, %.0f blocks/s, product %.2f TFLOP/s (%s)" % (ms_step, value, achieved, args.prec))
     del ws_cheb, ws_apply, U_stack, G_stack
     torch.cuda.empty_cache()
 
@@ -307,8 +307,8 @@ def main():
                                "Chebyshev d=24 A^-1/4, apply, unstack",
                    "N": N, "B": B, "tiles": NG,
                    "solver": "chebyshev-clenshaw d=24 fp32" + (
-                       ", products formed from exact three-piece bfloat16 splits on the matrix cores"
-                       if args.cheb_prec == "split" else ", fp32 matrix cores"),
+                       "; fp32 products (statistics, solve, apply) formed from exact three-piece bfloat16 "
+                       "splits on the matrix cores" if args.prec == "split" else "; fp32 matrix cores"),
                    "scale": "power iteration k=32 T=10 fp32", "beta": BETA},
         "roofline": roofline,
         "breakdown": breakdown,
@@ -335,7 +335,7 @@ def only_cheb(dash, di, torch, dev, args):
     lo = BETA * EPS / float(s.max().item())
     del ws
     X = torch.empty_like(A)
-    prec = dash.DASH_FP32_SPLIT if args.cheb_prec == "split" else dash.DASH_FP32
+    prec = dash.DASH_FP32_SPLIT if args.prec == "split" else dash.DASH_FP32
     ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
     ref = [torch.ones((4096, 4096), device=dev) for _ in range(REF_COPY_BYTES // (4096 * 4096 * 4))]
     ref_stack = torch.empty((REF_COPY_BYTES // (B * B * 4), B, B), device=dev)
@@ -347,7 +347,7 @@ def only_cheb(dash, di, torch, dev, args):
     dash.dash_inverse_root_cheb_prec(A, s, N, B, CHEB_DEGREE, lo, CHEB_HI, prec, X, ws=ws)
     e[2].record()
     torch.cuda.synchronize()
-    print(json.dumps({"mode": "cheb", "cheb_prec": args.cheb_prec, "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
+    print(json.dumps({"mode": "cheb", "cheb_prec": args.prec, "N": N, "B": B, "ref_copy_bytes": REF_COPY_BYTES,
                       "ref_copy_ms": round(e[0].elapsed_time(e[1]), 3), "cheb_ms": round(e[1].elapsed_time(e[2]), 3),
                       "products": dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)}), flush=True)
 
@@ -753,7 +753,7 @@ def only_adaptive(dash, di, torch, dev):
 
 def traffic_from_counters(fetch_csv, write_csv, prec):
     """Update profiles/traffic.json from two rocprofv3 --pmc runs of `bench.py --only cheb
-    --cheb-prec <prec>` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    --prec <prec>` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
     what it reads for the 4 GiB reference copy (the tile_copy dispatches of dash_stack in the same
     run).  One record per product kernel, keyed by its name."""
     import csv
@@ -772,8 +772,8 @@ def traffic_from_counters(fetch_csv, write_csv, prec):
         out[key + "_launches"] = len(gemm)
     out["product_source_sha256"] = product_source_sha(prec)
     out["kernel"] = kernel
-    out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb --cheb-prec %s; "
-                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb --cheb-prec %s"
+    out["command"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py --only cheb --prec %s; "
+                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py --only cheb --prec %s"
                       % (prec, prec))
     path = os.path.join(ROOT, "profiles", "traffic.json")
     recs = json.load(open(path)) if os.path.exists(path) else {}

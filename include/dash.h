@@ -56,8 +56,8 @@ typedef enum {
  * dash_inverse_root_ndb_lowp) and their workspace/flop queries; dash_scale takes DASH_FP32 or DASH_FP16.
  * DASH_FP32_SPLIT: fp32 operands, iterates and results, with each product formed on the bfloat16
  * matrix cores from an exact three-piece split of both operands (six piece products, fp32
- * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec and
- * dash_inverse_root_ndb_prec, by
+ * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec,
+ * dash_inverse_root_ndb_prec, dash_update_stats_prec and dash_apply_prec, by
  * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts the 256-wide
  * tiles of the split products). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3 } dash_prec;
@@ -101,6 +101,13 @@ dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, 
  * preconditioners are stacked into one tensor).  Only the upper triangle of each input block is
  * read; every output block is exactly symmetric.  0 <= beta <= 1. */
 dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float beta, float* A, void* stream);
+
+/* dash_update_stats with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix cores;
+ * the same as dash_update_stats) or DASH_FP32_SPLIT (both products formed from exact three-piece
+ * bfloat16 splits of their fp32 operands on the bfloat16 matrix cores when B % 256 == 0; with
+ * other B the fp32 matrix cores).  DASH_ERR_INVALID_ARG for any other prec. */
+dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
+                                   void* stream);
 
 /* Per-block scale s[N] ([PT] Definição do Problema, item 3, and Metodologia, item 2,
  * "Multi-Power-Iteration"; [TG] body: Rayleigh-quotient estimate of the spectral norm).
@@ -247,6 +254,13 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
  * inputs.  ws holds one [NG,B,B] intermediate. */
 dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B, float* U_stack,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* dash_apply with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix cores; the
+ * same as dash_apply) or DASH_FP32_SPLIT (both products formed from exact three-piece bfloat16
+ * splits of their fp32 operands on the bfloat16 matrix cores when B % 256 == 0; with other B the
+ * fp32 matrix cores).  Same workspace; DASH_ERR_INVALID_ARG for any other prec. */
+dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B,
+                            dash_prec prec, float* U_stack, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for an operation.  k_or_degree: the number of start vectors for
  * DASH_OP_SCALE (power iteration; Frobenius needs 0), ignored otherwise.  bytes [host]. */

@@ -46,6 +46,7 @@ def library() -> ctypes.CDLL:
             "dash_stack": (st, [ctypes.POINTER(DashMat), i32, i32, vp, vp]),
             "dash_unstack": (st, [vp, i32, ctypes.POINTER(DashMat), i32, vp]),
             "dash_update_stats": (st, [vp, i64, i32, f32, vp, vp]),
+            "dash_update_stats_prec": (st, [vp, i64, i32, f32, st, vp, vp]),
             "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_prec": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, vp, sz, vp]),
@@ -59,6 +60,7 @@ def library() -> ctypes.CDLL:
             "dash_inverse_root_cheb_prec": (st, [vp, vp, i64, i32, i32, f64, f64, st, vp, vp, vp, sz, vp]),
             "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
+            "dash_apply_prec": (st, [vp, vp, vp, i64, i32, st, vp, vp, sz, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
             "dash_flops": (f64, [st, i64, i32, st, i32, i32]),
@@ -156,6 +158,11 @@ def dash_update_stats(G_stack, NG: int, B: int, beta: float, A, stream=None):
            library().dash_update_stats(_ptr(G_stack), NG, B, beta, _ptr(A), _stream(stream, A)))
 
 
+def dash_update_stats_prec(G_stack, NG: int, B: int, beta: float, prec: int, A, stream=None):
+    _check("dash_update_stats_prec",
+           library().dash_update_stats_prec(_ptr(G_stack), NG, B, beta, prec, _ptr(A), _stream(stream, A)))
+
+
 def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, ws=None, stream=None):
     _check("dash_scale", library().dash_scale(_ptr(A), N, B, how, prec, k, steps, _ptr(V0), _ptr(s), _ptr(ws),
                                               _nbytes(ws), _stream(stream, A)))
@@ -238,3 +245,9 @@ def dash_inverse_root_evd(A, N: int, B: int, max_sweeps: int, refine: int, X, ei
 def dash_apply(XL, XR, G_stack, NG: int, B: int, U_stack, ws=None, stream=None):
     _check("dash_apply", library().dash_apply(_ptr(XL), _ptr(XR), _ptr(G_stack), NG, B, _ptr(U_stack), _ptr(ws),
                                               _nbytes(ws), _stream(stream, G_stack)))
+
+
+def dash_apply_prec(XL, XR, G_stack, NG: int, B: int, prec: int, U_stack, ws=None, stream=None):
+    _check("dash_apply_prec",
+           library().dash_apply_prec(_ptr(XL), _ptr(XR), _ptr(G_stack), NG, B, prec, _ptr(U_stack), _ptr(ws),
+                                     _nbytes(ws), _stream(stream, G_stack)))

@@ -543,6 +543,12 @@ dash_status dash_unstack(const float* U_stack, int32_t B, const dash_mat* outs, 
 }
 
 dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float beta, float* A, void* stream) {
+  return dash_update_stats_prec(G_stack, NG, B, beta, DASH_FP32, A, stream);
+}
+
+dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
+                                   void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
   if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
   if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
   if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
@@ -552,10 +558,11 @@ dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float
   Epilogue e;
   e.alpha = 1.f - beta;
   e.beta = beta;
+  const dash_prec pp = (prec == DASH_FP32_SPLIT && B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
   Product pl = prod(G_stack, G_stack, L, L);  // G G^T : Y read transposed
-  TRY(launch_gemm(&pl, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NT, true, e, as_stream(stream)));
+  TRY(launch_gemm(&pl, 1, NG, B, pp, DASH_FP32, Trans::NT, true, e, as_stream(stream)));
   Product pr = prod(G_stack, G_stack, R, R);  // G^T G : X read transposed
-  TRY(launch_gemm(&pr, 1, NG, B, DASH_FP32, DASH_FP32, Trans::TN, true, e, as_stream(stream)));
+  TRY(launch_gemm(&pr, 1, NG, B, pp, DASH_FP32, Trans::TN, true, e, as_stream(stream)));
   return DASH_OK;
 }
 
@@ -1175,6 +1182,12 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
 
 dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B, float* U_stack,
                        void* ws, size_t ws_bytes, void* stream) {
+  return dash_apply_prec(XL, XR, G_stack, NG, B, DASH_FP32, U_stack, ws, ws_bytes, stream);
+}
+
+dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B,
+                            dash_prec prec, float* U_stack, void* ws, size_t ws_bytes, void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
   if (!XL || !XR || !G_stack || !U_stack || !valid_N(NG)) return DASH_ERR_INVALID_ARG;
   if (!aligned(XL, 16) || !aligned(XR, 16) || !aligned(G_stack, 16) || !aligned(U_stack, 16))
     return DASH_ERR_INVALID_ARG;
@@ -1183,10 +1196,11 @@ dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, i
   if (!ws || !aligned(ws, 256) || ws_bytes < ws_apply(NG, B)) return DASH_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   float* T = (float*)ws;
+  const dash_prec pp = (prec == DASH_FP32_SPLIT && B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
   Product p1 = prod(XL, G_stack, T);
-  TRY(launch_gemm(&p1, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+  TRY(launch_gemm(&p1, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   Product p2 = prod(T, XR, U_stack);
-  TRY(launch_gemm(&p2, 1, NG, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+  TRY(launch_gemm(&p2, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   return DASH_OK;
 }
 

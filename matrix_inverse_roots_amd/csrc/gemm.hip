@@ -57,14 +57,15 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     if (out_prec != DASH_FP32) return hipErrorInvalidValue;
     return gemm::launch_f32(a, trans, sym, stream);
   }
-  // fp32 operands split into bfloat16 pieces, 256-wide tiles: symmetric products of an exactly
-  // symmetric right operand, or general products; no operand maps, stopped blocks or second
-  // output; C is read from memory with its (beta, ib) weight, never folded
+  // fp32 operands split into bfloat16 pieces, 256-wide tiles: symmetric results of NN with an
+  // exactly symmetric right operand, of NT or of TN, or general NN products; no operand maps,
+  // stopped blocks or second output; C is read from memory with its (beta, ib) weight, never folded
   if (in_prec == DASH_FP32_SPLIT) {
-    if (out_prec != DASH_FP32 || (sym && !y_sym) || trans != Trans::NN || maps || frz || epi.fold_c ||
-        probs[0].D2 || (nprob > 1 && probs[1].D2) || B % 256 != 0)
+    const bool shape_ok = sym ? (trans != Trans::NN || y_sym) : trans == Trans::NN;
+    if (out_prec != DASH_FP32 || !shape_ok || maps || frz || epi.fold_c || probs[0].D2 ||
+        (nprob > 1 && probs[1].D2) || B % 256 != 0)
       return hipErrorInvalidValue;
-    return gemm::launch_split(a, sym, stream);
+    return gemm::launch_split(a, sym, trans, y_sym, stream);
   }
   // 2-byte operands (binary16 or bfloat16): output in fp32 or in the operand format
   if ((in_prec != DASH_FP16 && in_prec != DASH_BF16) || (out_prec != DASH_FP32 && out_prec != in_prec))

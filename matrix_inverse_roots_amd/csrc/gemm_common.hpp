@@ -402,8 +402,8 @@ __device__ __forceinline__ void pass_tile_f16(const Product& P, const TE* X, con
 hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
 hipError_t launch_f16(GemmArgs& a, dash_prec in_prec, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
 // fp32 products from three-piece bfloat16 splits (gemm_split.hip), B % 256 == 0: symmetric results
-// of an exactly symmetric right operand (sym), or general products (every tile, any right operand)
-hipError_t launch_split(GemmArgs& a, bool sym, hipStream_t stream);
+// (sym) of NN with an exactly symmetric right operand, of NT or of TN; general results of NN
+hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

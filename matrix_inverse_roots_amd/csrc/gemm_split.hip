@@ -19,10 +19,12 @@
 // LDS as rows of 16 consecutive k per output row (X) or output column (Y).
 // SYM (symmetric results: Chebyshev): upper-triangle tiles, mirrored on store; the right operand
 // must then be exactly symmetric (Y^T == Y bitwise, as every Clenshaw term b_{k+1} is: it is stored
-// mirrored), so its columns are read as rows with 32-byte row loads.  YT (general right operand:
-// NDB): every tile; each thread loads 8 consecutive k of one Y column with scalar loads (the lanes
-// of a wave read 64 consecutive columns, 256 contiguous bytes per load) and stores them as that
-// column's 16-byte LDS row piece.  The epilogue reads C and E from memory: folding C = Y from the
+// mirrored), so its columns are read as rows with 32-byte row loads; the same staging with a
+// general Y forms X Y^T (the statistics' G G^T).  YT (general right operand: NDB, apply): each
+// thread loads 8 consecutive k of one Y column with scalar loads (the lanes of a wave read 64
+// consecutive columns, 256 contiguous bytes per load) and stores them as that column's 16-byte
+// LDS row piece; XT gathers the left operand's columns the same way (X^T Y, the statistics'
+// G^T G).  The epilogue reads C and E from memory: folding C = Y from the
 // staged planes, as the fp32 kernel does, costs this kernel's register budget more than the read
 // (measured slower).
 #include <hip/hip_runtime.h>
@@ -60,7 +62,7 @@ constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 // 16-byte fragment reads of 8 consecutive rows hit distinct banks
 __device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1); }
 
-template <bool CHECKS, bool SYM, bool YT>
+template <bool CHECKS, bool SYM, bool XT, bool YT>
 __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 16, DEPTH = 4;
   constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
@@ -78,35 +80,49 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int li = lane & 31, h = lane >> 5;
-  const int srow = tid >> 1, sch = tid & 1;  // staged piece: row srow, k 8 sch .. 8 sch + 7
-  const int ycol = tid & 255, ykh = tid >> 8;  // YT: column ycol, k 8 ykh .. 8 ykh + 7
-  const int yrow = YT ? ycol : srow, ych = YT ? ykh : sch;  // the Y piece's LDS row and chunk
+  const int srow = tid >> 1, sch = tid & 1;    // row piece: row srow, k 8 sch .. 8 sch + 7
+  const int gcol = tid & 255, gkh = tid >> 8;  // column gather: column gcol, k 8 gkh .. 8 gkh + 7
+  const int xrow = XT ? gcol : srow, xch = XT ? gkh : sch;  // the pieces' LDS rows and chunks
+  const int yrow = YT ? gcol : srow, ych = YT ? gkh : sch;
 
-  // YT: Y's block as a buffer (out-of-range reads return 0; every offset here is in range), the
-  // lane's column and k-half as a 32-bit byte offset
-  __amdgpu_buffer_rsrc_t yrs;
-  int yvoff = 0;
+  // Column gathers read the operand's block as a buffer (out-of-range reads return 0; every
+  // offset here is in range): the row offset is wave-uniform (a scalar), the lane's column and
+  // k-half a 32-bit byte offset.  The block's address is the same in every lane; say so, or every
+  // load becomes a loop over the distinct descriptors of the wave.
+  auto block_rsrc = [&](const float* p) {
+    const uint64_t a64 = (uint64_t)p;
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a64 >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a64);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, B * B * 4, BUFFER_RSRC_WORD3);
+  };
+  __amdgpu_buffer_rsrc_t xrs, yrs;
+  int xvoff = 0, yvoff = 0;
+  if constexpr (XT) {
+    xrs = block_rsrc(X);
+    xvoff = (8 * gkh * B + i0 + gcol) * 4;
+  }
   if constexpr (YT) {
-    // the block's address is the same in every lane; say so, or every load becomes a loop over
-    // the distinct descriptors of the wave
-    const uint64_t ya = (uint64_t)Y;
-    const uint64_t yu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ya >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ya);
-    yrs = __builtin_amdgcn_make_buffer_rsrc((void*)yu, (short)0, B * B * 4, BUFFER_RSRC_WORD3);
-    yvoff = (8 * ykh * B + j0 + ycol) * 4;
+    yrs = block_rsrc(Y);
+    yvoff = (8 * gkh * B + j0 + gcol) * 4;
   }
 
   f32x4 rx[DEPTH][2], ry[DEPTH][2];
+  auto gather = [&](f32x4 (&r)[2], __amdgpu_buffer_rsrc_t rs, int voff, int k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)  // (the load returns the word's bits as an integer)
+      r[q >> 2][q & 3] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, (k0 + q) * B * 4, 0));
+  };
   auto gload = [&](auto slot_c, int k0) {
     constexpr int slot = decltype(slot_c)::value;
-    const float* xp = X + (int64_t)(i0 + srow) * B + k0 + 8 * sch;
-    rx[slot][0] = *(const f32x4*)xp;
-    rx[slot][1] = *(const f32x4*)(xp + 4);
-    if constexpr (YT) {  // row k0 + 8 ykh + q: the wave-uniform part of the offset in a scalar
-#pragma unroll
-      for (int q = 0; q < 8; ++q)  // (the load returns the word's bits as an integer)
-        ry[slot][q >> 2][q & 3] =
-            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(yrs, yvoff, (k0 + q) * B * 4, 0));
+    if constexpr (XT) {
+      gather(rx[slot], xrs, xvoff, k0);
+    } else {
+      const float* xp = X + (int64_t)(i0 + srow) * B + k0 + 8 * sch;
+      rx[slot][0] = *(const f32x4*)xp;
+      rx[slot][1] = *(const f32x4*)(xp + 4);
+    }
+    if constexpr (YT) {
+      gather(ry[slot], yrs, yvoff, k0);
     } else {
       const float* yp = Y + (int64_t)(j0 + srow) * B + k0 + 8 * sch;
       ry[slot][0] = *(const f32x4*)yp;
@@ -115,7 +131,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   };
   auto sstore = [&](auto slot_c, int buf) {
     constexpr int slot = decltype(slot_c)::value;
-    __bf16* s = smem + buf * BUF + srow * BK + 8 * swz2(srow, sch);
+    __bf16* s = smem + buf * BUF + xrow * BK + 8 * swz2(xrow, xch);
     bf16x8 p0, p1, p2;
     split3(rx[slot][0], rx[slot][1], p0, p1, p2);
     *(bf16x8*)(s) = p0;
@@ -199,16 +215,23 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_split(GemmArgs& a, bool sym, hipStream_t stream) {
+hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStream_t stream) {
   if (a.B % 256 != 0) return hipErrorInvalidValue;
   a.tdim = a.B / 256;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool checks = wants_checks(a.epi);
-  if (sym)
-    return checks ? launch(gemm_split_kernel<true, true, false>, a, stream, 512)
-                  : launch(gemm_split_kernel<false, true, false>, a, stream, 512);
-  return checks ? launch(gemm_split_kernel<true, false, true>, a, stream, 512)
-                : launch(gemm_split_kernel<false, false, true>, a, stream, 512);
+  // symmetric results: NN of an exactly symmetric Y and NT read Y's rows as B's columns; TN
+  // gathers the columns of both operands.  General results: NN with Y's columns gathered.
+  if (sym && (trans == Trans::NT || (trans == Trans::NN && y_sym)))
+    return checks ? launch(gemm_split_kernel<true, true, false, false>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, false, false>, a, stream, 512);
+  if (sym && trans == Trans::TN)
+    return checks ? launch(gemm_split_kernel<true, true, true, true>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, true, true>, a, stream, 512);
+  if (!sym && trans == Trans::NN)
+    return checks ? launch(gemm_split_kernel<true, false, false, true>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, false, false, true>, a, stream, 512);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gemm

@@ -259,5 +259,12 @@ def test_split_precision_queries_and_argument_errors():
                       ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
     assert dash.dash_flops(dash.DASH_OP_NDB, 3, 1024, dash.DASH_FP32_SPLIT, 6, 6) == \
         dash.dash_flops(dash.DASH_OP_NDB, 3, 1024, dash.DASH_FP32, 6, 6)
+    for prec in (dash.DASH_FP16, dash.DASH_BF16, 7):
+        assert _status_of(dash.dash_update_stats_prec, P, N, B, 0.9, prec, P2) == _lib.DASH_ERR_INVALID_ARG
+        assert _status_of(dash.dash_apply_prec, P, P2, P3, N, B, prec, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_update_stats_prec, P, N, B, 1.5, dash.DASH_FP32_SPLIT, P2) == \
+        _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_apply_prec, P, P2, P3, N, B, dash.DASH_FP32_SPLIT, P, ws=ws) == \
+        _lib.DASH_ERR_INVALID_ARG                                                           # U aliases XL
     assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32_SPLIT, 8, 10, P2, P3,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG

@@ -189,3 +189,59 @@ def test_ndb_split_fallback_equivariance_independence_and_flags(conditioned):
     assert np.array_equal(to_host(st).astype(int) & 1, [0, 1, 0, 0])
     assert np.all(np.isnan(to_host(Xb)[1]))
     assert torch.equal(Xb[[0, 2, 3]], X[[0, 2, 3]])
+
+
+# ------------------------------------------------------------------------------------------------
+# statistics (G G^T: Y's rows as columns; G^T G: both operands' columns gathered) and apply
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [256, 512])
+def test_update_stats_split_integers_exact(B):
+    """Small integers: every piece product and every sum is exact in fp32, so the split statistics
+    equal the oracle's exactly, with exactly symmetric blocks."""
+    NG = 2
+    g = di.rng(430 + B)
+    G = g.integers(-3, 4, (NG, B, B)).astype(np.float32)
+    L0 = g.integers(-4, 5, (NG, B, B)).astype(np.float32)
+    L0 = L0 + L0.transpose(0, 2, 1)
+    R0 = g.integers(-4, 5, (NG, B, B)).astype(np.float32)
+    R0 = R0 + R0.transpose(0, 2, 1)
+    A = to_dev(np.concatenate([L0, R0]))
+    dash.dash_update_stats_prec(to_dev(G), NG, B, 0.5, SPLIT, A)
+    out = to_host(A)
+    L_ref, R_ref = oracle.update_stats(G, 0.5, L0, R0)
+    assert np.array_equal(out[:NG], L_ref) and np.array_equal(out[NG:], R_ref)
+
+
+def test_update_stats_split_gaussian():
+    NG, B = 3, 512
+    G = di.gaussian((NG, B, B), 440, 1e-3)
+    L0 = di.tiny_stack(seed=441, N=NG, B=B) * 1e-6
+    R0 = di.tiny_stack(seed=442, N=NG, B=B) * 1e-6
+    A = to_dev(np.concatenate([L0, R0]))
+    dash.dash_update_stats_prec(to_dev(G), NG, B, 0.95, SPLIT, A)
+    out = to_host(A)
+    L_ref, R_ref = oracle.update_stats(G, 0.95, L0, R0)
+    assert np.max(rel_err(out[:NG], L_ref)) < 1e-5 and np.max(rel_err(out[NG:], R_ref)) < 1e-5
+    assert np.array_equal(out, out.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("B", [256, 512, 320])
+def test_apply_split_matches_oracle(B):
+    """General operands on both products; B = 320 runs the fp32 matrix cores (bit for bit the fp32
+    path)."""
+    NG = 3
+    XL, XR, G = (di.gaussian((NG, B, B), seed) for seed in (450, 451, 452))
+    U = torch.empty((NG, B, B), device=DEV)
+    ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, SPLIT, device=DEV)
+    dash.dash_apply_prec(to_dev(XL), to_dev(XR), to_dev(G), NG, B, SPLIT, U, ws)
+    U_ref = oracle.apply(XL, G, XR)
+    assert np.max(rel_err(to_host(U), U_ref)) < 1e-5
+    if B % 256:
+        U2 = torch.empty_like(U)
+        dash.dash_apply(to_dev(XL), to_dev(XR), to_dev(G), NG, B, U2, ws)
+        assert torch.equal(U, U2)
+    # identity preconditioners pass the gradient through exactly (pieces of 1 and 0 are exact)
+    I = torch.eye(B, device=DEV).expand(NG, B, B).contiguous()
+    dash.dash_apply_prec(I, I, to_dev(G), NG, B, SPLIT, U, ws)
+    assert np.array_equal(to_host(U), G.astype(np.float64))
