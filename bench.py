@@ -40,7 +40,7 @@ FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 # the Clenshaw product kernel of each product arithmetic, and the sources its traffic record is keyed to
 PRODUCT_KERNELS = {
-    "split": ("gemm_split_kernel<false, true, false, false>", ("gemm_common.hpp", "gemm_split.hip")),
+    "split": ("gemm_split_kernel<false, true, false, false, true>", ("gemm_common.hpp", "gemm_split.hip")),
     "fp32": ("gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>", ("gemm_common.hpp", "gemm_f32.hip")),
 }
 SPLIT_PIECE_PRODUCTS = 6  # bfloat16 piece products per fp32 product in the split kernel

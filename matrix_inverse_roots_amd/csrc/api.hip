@@ -1060,11 +1060,9 @@ dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t 
   // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
   // stored mirrored; the first product, which maps A as it stages it, stays on the fp32 cores
   const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
-  // (split products read C = b_{k+1} from memory with the weight beta * coef(ib) set above, which
-  // equals the fold's alpha * coef(ia) * c_over_a * s for every product)
+  // (split products fold C = b_{k+1} into A's diagonal: alpha (A - (m s / 2) I) b_{k+1})
   auto run = [&](std::pair<Product, Epilogue> pe) {
     const bool sp = split && !pe.first.map_y;
-    if (sp) pe.second.fold_c = false;
     return launch_gemm(&pe.first, 1, N, B, sp ? DASH_FP32_SPLIT : DASH_FP32, DASH_FP32, Trans::NN, true, pe.second,
                        st, sp);
   };

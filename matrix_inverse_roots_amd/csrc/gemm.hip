@@ -38,8 +38,8 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
   // and E in every problem, except the launches that map Y, which have none
   auto fold_ok = [&](const Product& p) { return p.C && p.C == p.Y && (p.map_y ? !p.E : p.E != nullptr); };
-  if (epi.fold_c && (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) ||
-                     (nprob > 1 && !fold_ok(probs[1]))))
+  if (epi.fold_c && in_prec != DASH_FP32_SPLIT &&
+      (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) || (nprob > 1 && !fold_ok(probs[1]))))
     return hipErrorInvalidValue;
   // operand maps exist in every binary16 kernel and, for the right operand, in the fp32 Clenshaw
   // launches
@@ -59,10 +59,15 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   }
   // fp32 operands split into bfloat16 pieces, 256-wide tiles: symmetric results of NN with an
   // exactly symmetric right operand, of NT or of TN, or general NN products; no operand maps,
-  // stopped blocks or second output; C is read from memory with its (beta, ib) weight, never folded
+  // stopped blocks or second output.  C is read from memory with its (beta, ib) weight, or, with
+  // fold_c (symmetric NN only, C == Y in every problem), enters as (c_over_a coef[ic]) added to
+  // X's diagonal: alpha coef[ia] (X + c I) Y
   if (in_prec == DASH_FP32_SPLIT) {
     const bool shape_ok = sym ? (trans != Trans::NN || y_sym) : trans == Trans::NN;
-    if (out_prec != DASH_FP32 || !shape_ok || maps || frz || epi.fold_c || probs[0].D2 ||
+    bool fold_ok_split = !epi.fold_c || (sym && trans == Trans::NN && y_sym);
+    for (int i = 0; i < nprob; ++i)
+      if (epi.fold_c && probs[i].C != probs[i].Y) fold_ok_split = false;
+    if (out_prec != DASH_FP32 || !shape_ok || maps || frz || !fold_ok_split || probs[0].D2 ||
         (nprob > 1 && probs[1].D2) || B % 256 != 0)
       return hipErrorInvalidValue;
     return gemm::launch_split(a, sym, trans, y_sym, stream);

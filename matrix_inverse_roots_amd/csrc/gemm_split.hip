@@ -24,9 +24,10 @@
 // thread loads 8 consecutive k of one Y column with scalar loads (the lanes of a wave read 64
 // consecutive columns, 256 contiguous bytes per load) and stores them as that column's 16-byte
 // LDS row piece; XT gathers the left operand's columns the same way (X^T Y, the statistics'
-// G^T G).  The epilogue reads C and E from memory: folding C = Y from the
-// staged planes, as the fp32 kernel does, costs this kernel's register budget more than the read
-// (measured slower).
+// G^T G).  The epilogue reads E, and C unless FOLD: when C is Y itself (Clenshaw's b_{k+1}),
+// alpha X Y + beta Y = alpha (X + (beta/alpha) I) Y, so beta/alpha is added to X's diagonal as it
+// is staged (before the split) and no C is read.  (Adding C from the staged Y planes, as the fp32
+// kernel does, spilled registers and measured slower.)
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -62,7 +63,7 @@ constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 // 16-byte fragment reads of 8 consecutive rows hit distinct banks
 __device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1); }
 
-template <bool CHECKS, bool SYM, bool XT, bool YT>
+template <bool CHECKS, bool SYM, bool XT, bool YT, bool FOLD = false>
 __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 16, DEPTH = 4;
   constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
@@ -129,10 +130,21 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
       ry[slot][1] = *(const f32x4*)(yp + 4);
     }
   };
-  auto sstore = [&](auto slot_c, int buf) {
+  // FOLD (C == Y, Clenshaw's b_{k+1}): alpha X Y + beta Y = alpha (X + (beta/alpha) I) Y, so the
+  // C term enters as (beta/alpha) added to X's diagonal before the split, and no C is read
+  const float xc = FOLD ? a.epi.c_over_a * coef_of(a.epi, a.epi.ic, tc.b) : 0.f;
+  auto sstore = [&](auto slot_c, int buf, int k0) {
     constexpr int slot = decltype(slot_c)::value;
     __bf16* s = smem + buf * BUF + xrow * BK + 8 * swz2(xrow, xch);
     bf16x8 p0, p1, p2;
+    if constexpr (FOLD) {  // element q of the piece sits on the diagonal when i0 + row == k0 + 8 ch + q
+      const int d = i0 + srow - k0 - 8 * sch;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rx[slot][0][q] = d == q ? rx[slot][0][q] + xc : rx[slot][0][q];
+        rx[slot][1][q] = d == q + 4 ? rx[slot][1][q] + xc : rx[slot][1][q];
+      }
+    }
     split3(rx[slot][0], rx[slot][1], p0, p1, p2);
     *(bf16x8*)(s) = p0;
     *(bf16x8*)(s + PLANE) = p1;
@@ -183,13 +195,13 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   auto step = [&](auto slot_c, int kt) {
     constexpr int slot = decltype(slot_c)::value;  // == kt % DEPTH
     gload(slot_c, (kt + DEPTH) * BK);
-    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1, (kt + 1) * BK);
     compute(slot & 1);
     __syncthreads();
   };
-  auto tail_step = [&](auto slot_c, bool store_next) {
+  auto tail_step = [&](auto slot_c, int kt, bool store_next) {
     constexpr int slot = decltype(slot_c)::value;
-    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1);
+    if (store_next) sstore(IC<(slot + 1) % DEPTH>{}, (slot + 1) & 1, (kt + 1) * BK);
     compute(slot & 1);
     __syncthreads();
   };
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   gload(IC<1>{}, BK);
   gload(IC<2>{}, 2 * BK);
   gload(IC<3>{}, 3 * BK);
-  sstore(IC<0>{}, 0);
+  sstore(IC<0>{}, 0, 0);
   __syncthreads();
   int kt = 0;
   for (; kt + DEPTH < KT; kt += DEPTH) {
@@ -206,11 +218,11 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
     step(IC<2>{}, kt + 2);
     step(IC<3>{}, kt + 3);
   }
-  tail_step(IC<0>{}, true);
-  tail_step(IC<1>{}, true);
-  tail_step(IC<2>{}, true);
-  tail_step(IC<3>{}, false);
-  epilogue<MTM, MTN, WTM, WTN, SYM, float, true, true, TILE, CHECKS, false, false>(a, tc, P, acc, wm, wn, lane);
+  tail_step(IC<0>{}, kt, true);
+  tail_step(IC<1>{}, kt + 1, true);
+  tail_step(IC<2>{}, kt + 2, true);
+  tail_step(IC<3>{}, kt + 3, false);
+  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false>(a, tc, P, acc, wm, wn, lane);
 }
 
 }  // namespace
@@ -222,6 +234,10 @@ hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStrea
   const bool checks = wants_checks(a.epi);
   // symmetric results: NN of an exactly symmetric Y and NT read Y's rows as B's columns; TN
   // gathers the columns of both operands.  General results: NN with Y's columns gathered.
+  if (sym && trans == Trans::NN && y_sym && a.epi.fold_c)  // C == Y folded into X's diagonal
+    return checks ? launch(gemm_split_kernel<true, true, false, false, true>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, false, false, true>, a, stream, 512);
+  if (a.epi.fold_c) return hipErrorInvalidValue;
   if (sym && (trans == Trans::NT || (trans == Trans::NN && y_sym)))
     return checks ? launch(gemm_split_kernel<true, true, false, false>, a, stream, 512)
                   : launch(gemm_split_kernel<false, true, false, false>, a, stream, 512);
