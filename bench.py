@@ -211,31 +211,14 @@ def main():
     value = N / (wall / args.steps)
 
     # dominant kernel: the product of the Clenshaw solve (d-1 launches per call, each one batched
-    # triangle-only product over all N blocks); its launch time from the events around the solve.
-    # With split products the first product (A mapped into b_{d-1} as it is staged) runs on the fp32
-    # kernel: its time, from a degree-2 solve (that product alone), is taken out.  Flops are counted
-    # per computed tile (dash_flops).
+    # triangle-only product over all N blocks); its launch time from the events around the solve,
+    # which also hold the coefficient kernel.  Flops are counted per computed tile (dash_flops).
     cheb_products = dash.dash_solver_products(dash.DASH_OP_CHEB, CHEB_DEGREE, 0)
     cheb_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, cheb_prec, CHEB_DEGREE, 0)
     kernel_name = PRODUCT_KERNELS[args.prec][0]
-    if args.prec == "split":
-        first_flop = dash.dash_flops(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32, 2, 0)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        dash.dash_inverse_root_cheb_prec(A, s, N, B, 2, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
-        e[0].record(stream)
-        for _ in range(3):
-            dash.dash_inverse_root_cheb_prec(A, s, N, B, 2, lo, CHEB_HI, cheb_prec, X, ws=ws_cheb)
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        first_ms = e[0].elapsed_time(e[1]) / 3
-        launches = cheb_products - 1
-        flop_per_launch = (cheb_flop - first_flop) / launches
-        launch_ms = (phase_ms["cheb"] - first_ms) / launches
-    else:
-        first_ms = None
-        launches = cheb_products
-        flop_per_launch = cheb_flop / cheb_products
-        launch_ms = phase_ms["cheb"] / cheb_products
+    launches = cheb_products
+    flop_per_launch = cheb_flop / cheb_products
+    launch_ms = phase_ms["cheb"] / cheb_products
     tri = flop_per_launch / (2.0 * B ** 3 * N)
     fp32_equiv = flop_per_launch / (launch_ms * 1e-3) / 1e12
     rec = traffic_record(args.prec)
@@ -262,8 +245,6 @@ def main():
     roofline.update({"traffic": traffic, "traffic_detail": traffic_detail, "flop_per_launch": flop_per_launch,
                      "launches_per_step": launches, "tiles_computed_fraction": round(tri, 4),
                      "avg_launch_ms": round(launch_ms, 3)})
-    if first_ms is not None:
-        roofline["first_product_ms"] = round(first_ms, 3)
 
     step_flop = (cheb_flop
                  + dash.dash_flops(dash.DASH_OP_STATS, NG, B, dash.DASH_FP32, 0, 0)

@@ -58,8 +58,8 @@ typedef enum {
  * matrix cores from an exact three-piece split of both operands (six piece products, fp32
  * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec,
  * dash_inverse_root_ndb_prec, dash_update_stats_prec and dash_apply_prec, by
- * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts the 256-wide
- * tiles of the split products). */
+ * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts 256-wide tiles
+ * for degree >= 3 and B % 256 == 0). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
@@ -218,10 +218,10 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
 
 /* dash_inverse_root_cheb with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix
  * cores; the same as dash_inverse_root_cheb) or DASH_FP32_SPLIT (fp32 products formed from exact
- * three-piece bfloat16 splits on the bfloat16 matrix cores, 256 x 256 tiles: every product but the
- * first, which maps A into the recurrence's first term as it stages it, when B % 256 == 0; with
- * other B every product runs on the fp32 matrix cores).  Same arguments, workspace and results
- * contract otherwise; DASH_ERR_INVALID_ARG for any other prec. */
+ * three-piece bfloat16 splits on the bfloat16 matrix cores, 256 x 256 tiles, when B % 256 == 0 and
+ * degree >= 3; the recurrence's C term enters as a shift of A's diagonal; with other B or degree 2
+ * the fp32 matrix cores).  Same arguments, workspace and results contract otherwise;
+ * DASH_ERR_INVALID_ARG for any other prec. */
 dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
                                         double lo, double hi, dash_prec prec, float* X, int32_t* status, void* ws,
                                         size_t ws_bytes, void* stream);

@@ -482,9 +482,9 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
     case DASH_OP_CHEB:
       n = dash_solver_products(op, a1, 0);
       if (n < 0) return -1.0;
-      if (split && n > 1) {  // the first product on 128-wide fp32 tiles, the others on 256-wide ones
+      if (split && n > 1) {  // every product on 256-wide tiles (degree >= 3)
         const double t = B / 256;
-        return full * (tri(DASH_FP32) + (n - 1) * (t * (t + 1) / 2) / (t * t));
+        return full * n * (t * (t + 1) / 2) / (t * t);
       }
       return n * full * tri(DASH_FP32);
     case DASH_OP_APPLY: return 2.0 * full;
@@ -1072,8 +1072,22 @@ dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t 
     p.map_ia = CO_R1;
     p.map_g = (float)g1;
   };
-  // the first product: k = d - 2 (or the final one when d == 2), E = b_d = c_d I folded into gamma
-  {
+  // the first product: k = d - 2 (or the final one when d == 2), E = b_d = c_d I folded into gamma.
+  // With split products (d >= 3): b_{d-1} = a1 A/s + g1 I turns alpha A b + beta b + gamma I into
+  // (alpha a1 / s) (A + c I) A + (gamma + beta g1) I with c = s (g1/a1 - m/2): A times A with the
+  // fold's diagonal term (A read by columns, so A need not be bitwise symmetric)
+  if (split && d >= 3 && a1 != 0.0) {
+    Epilogue e;
+    e.alpha = (float)(4.0 * a1 / w);  // (4/w)(1/s) a1 (1/s)
+    e.ia = CO_R2;
+    e.fold_c = true;
+    e.c_over_a = (float)(g1 / a1 - 0.5 * m);
+    e.ic = CO_S;
+    e.gamma = (float)(c[d - 2] - c[d] - 2.0 * m / w * g1);
+    e.coef = coef;
+    Product pr = prod(A, A, b2, A);
+    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32_SPLIT, DASH_FP32, Trans::NN, true, e, st, false));
+  } else {
     const bool last = (d == 2);
     auto pe = clenshaw(A, nullptr, last ? (void*)X : (void*)b2, last);
     map_first(pe.first);

@@ -58,13 +58,14 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
     return gemm::launch_f32(a, trans, sym, stream);
   }
   // fp32 operands split into bfloat16 pieces, 256-wide tiles: symmetric results of NN with an
-  // exactly symmetric right operand, of NT or of TN, or general NN products; no operand maps,
+  // exactly symmetric right operand or with C == Y folded, of NT or of TN, or general NN
+  // products; no operand maps,
   // stopped blocks or second output.  C is read from memory with its (beta, ib) weight, or, with
   // fold_c (symmetric NN only, C == Y in every problem), enters as (c_over_a coef[ic]) added to
   // X's diagonal: alpha coef[ia] (X + c I) Y
   if (in_prec == DASH_FP32_SPLIT) {
-    const bool shape_ok = sym ? (trans != Trans::NN || y_sym) : trans == Trans::NN;
-    bool fold_ok_split = !epi.fold_c || (sym && trans == Trans::NN && y_sym);
+    const bool shape_ok = sym ? (trans != Trans::NN || y_sym || epi.fold_c) : trans == Trans::NN;
+    bool fold_ok_split = !epi.fold_c || (sym && trans == Trans::NN);
     for (int i = 0; i < nprob; ++i)
       if (epi.fold_c && probs[i].C != probs[i].Y) fold_ok_split = false;
     if (out_prec != DASH_FP32 || !shape_ok || maps || frz || !fold_ok_split || probs[0].D2 ||

@@ -233,10 +233,15 @@ hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStrea
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool checks = wants_checks(a.epi);
   // symmetric results: NN of an exactly symmetric Y and NT read Y's rows as B's columns; TN
-  // gathers the columns of both operands.  General results: NN with Y's columns gathered.
-  if (sym && trans == Trans::NN && y_sym && a.epi.fold_c)  // C == Y folded into X's diagonal
-    return checks ? launch(gemm_split_kernel<true, true, false, false, true>, a, stream, 512)
-                  : launch(gemm_split_kernel<false, true, false, false, true>, a, stream, 512);
+  // gathers the columns of both operands; NN with C == Y folded gathers Y's columns unless Y is
+  // exactly symmetric.  General results: NN with Y's columns gathered.
+  if (sym && trans == Trans::NN && a.epi.fold_c) {  // C == Y folded into X's diagonal
+    if (y_sym)
+      return checks ? launch(gemm_split_kernel<true, true, false, false, true>, a, stream, 512)
+                    : launch(gemm_split_kernel<false, true, false, false, true>, a, stream, 512);
+    return checks ? launch(gemm_split_kernel<true, true, false, true, true>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, false, true, true>, a, stream, 512);
+  }
   if (a.epi.fold_c) return hipErrorInvalidValue;
   if (sym && (trans == Trans::NT || (trans == Trans::NN && y_sym)))
     return checks ? launch(gemm_split_kernel<true, true, false, false>, a, stream, 512)

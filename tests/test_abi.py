@@ -226,16 +226,17 @@ def test_bfloat16_queries_and_argument_errors():
                       ws=FakeWs(P3, 1 << 30)) == _lib.DASH_ERR_INVALID_ARG
 
 def test_split_precision_queries_and_argument_errors():
-    """DASH_FP32_SPLIT: the workspace of the fp32 solves; dash_flops counts the first Chebyshev
-    product on 128-wide tiles and the others on 256-wide ones (fp32 tiles when B % 256 != 0) and
-    NDB's full products as fp32's; only the *_prec solver entries take it, and they take nothing
+    """DASH_FP32_SPLIT: the workspace of the fp32 solves; dash_flops counts the Chebyshev products on
+    256-wide tiles (fp32 tiles when B % 256 != 0 or at degree 2) and NDB's full products as fp32's; only the *_prec solver entries take it, and they take nothing
     else but DASH_FP32."""
     for B in (256, 320, 1024):
         assert dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32_SPLIT) == \
             dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32)
     full = 2.0 * 1024 ** 3 * 3
     f = dash.dash_flops(dash.DASH_OP_CHEB, 3, 1024, dash.DASH_FP32_SPLIT, 24, 0)
-    assert f == pytest.approx(full * (36 / 64 + 22 * 10 / 16), rel=1e-12)
+    assert f == pytest.approx(full * 23 * 10 / 16, rel=1e-12)
+    assert dash.dash_flops(dash.DASH_OP_CHEB, 3, 1024, dash.DASH_FP32_SPLIT, 2, 0) == \
+        dash.dash_flops(dash.DASH_OP_CHEB, 3, 1024, dash.DASH_FP32, 2, 0)  # degree 2: the fp32 cores
     assert dash.dash_flops(dash.DASH_OP_CHEB, 3, 1024, dash.DASH_FP32, 24, 0) == pytest.approx(full * 23 * 36 / 64)
     assert dash.dash_flops(dash.DASH_OP_CHEB, 3, 320, dash.DASH_FP32_SPLIT, 24, 0) == \
         dash.dash_flops(dash.DASH_OP_CHEB, 3, 320, dash.DASH_FP32, 24, 0)

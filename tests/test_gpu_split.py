@@ -1,11 +1,10 @@
-"""GPU parity of the solvers with split products (DASH_FP32_SPLIT): the Chebyshev solve (every product
-but the first) and NDB (every product) form their fp32 products on the bfloat16 matrix cores from
+"""GPU parity of the solvers with split products (DASH_FP32_SPLIT): the Chebyshev solve and NDB form their fp32 products on the bfloat16 matrix cores from
 exact three-piece splits of both operands.  The gates are the fp32 ones (iterate parity 1e-4
 against the oracle's fp64 Clenshaw recurrence or NDB iterates, residual 1e-3), since the split
 product is an fp32 product: the split is exact and the piece products it leaves out are below
 fp32's own rounding.  Where the split does not apply
-(degree 2: the only product is the first; B not a multiple of 256) the result is the fp32 path's,
-bit for bit."""
+(Chebyshev degree 2, whose one product maps A into the recurrence's first term as it stages it; B
+not a multiple of 256) the result is the fp32 path's, bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -60,8 +59,8 @@ def test_cheb_split_matches_oracle(B, N, degrees):
 
 
 def test_cheb_split_falls_back_to_fp32_bitwise():
-    """Degree 2 runs only the first product (A mapped as it is staged, on the fp32 cores); B = 320
-    has no 256-wide tiling: both equal the fp32 path bit for bit."""
+    """Degree 2 runs one product (A mapped as it is staged, on the fp32 cores); B = 320 has no
+    256-wide tiling: both equal the fp32 path bit for bit."""
     A, Ad = spectrum_stack(410, 2, 256)
     s = frob_scale(Ad)
     X1, _ = cheb_p(Ad, s, 2, 0.02, 1.0, SPLIT)
