@@ -78,3 +78,30 @@ def test_maxsize_cheb(block):
     assert int(status[0]) == 0
     assert residual64(X, A64) < R_FP32
     assert torch.equal(X[0], X[0].T)
+
+
+def test_maxsize_split_products(block):
+    """Split products at B = 8192, where the column gathers' 32-bit byte offsets into a 256 MiB block
+    are largest: the Chebyshev solve (every product, the first with A read by columns) and NDB
+    (general products, columns gathered) meet the fp32 residual gate and agree with the fp32
+    matrix cores' results to well within the iterate tolerance."""
+    A, A64, V0 = block
+    s = power_scale(A, V0, 10)
+    lo = 0.9 * SHIFT / float(s[0])
+    X, status = cheb(A, s, 24, lo, 1.25)
+    Xs = torch.empty_like(A)
+    st = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, 1, B, dash.DASH_FP32_SPLIT, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, 1, B, 24, lo, 1.25, dash.DASH_FP32_SPLIT, Xs, status=st, ws=ws)
+    del ws
+    assert int(st[0]) == 0
+    assert residual64(Xs, A64) < R_FP32
+    assert torch.equal(Xs[0], Xs[0].T)
+    assert float(torch.linalg.matrix_norm(Xs[0].double() - X[0].double()) /
+                 torch.linalg.matrix_norm(X[0].double())) < 1e-5
+    Xn = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_NDB, 1, B, dash.DASH_FP32_SPLIT, device=DEV)
+    dash.dash_inverse_root_ndb_prec(A, s, 1, B, 8, 8, dash.DASH_FP32_SPLIT, Xn, status=st, ws=ws)
+    del ws
+    assert int(st[0]) == 0
+    assert residual64(Xn, A64) < R_FP32
