@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "dash_internal.hpp"
+#include "gemm_common.hpp"
 
 namespace dash {
 namespace {
@@ -196,8 +197,11 @@ __global__ __launch_bounds__(64 * WAVES, 3) void power_step_f32(PowerStepArgs<fl
   __shared__ __attribute__((aligned(16))) float Vs[2][BK * LDV];
   __shared__ float inv_s[KV];
   __shared__ float red[WAVES][3][KV];
-  const int64_t b = blockIdx.x / a.RB;
-  const int rb = (int)(blockIdx.x - b * a.RB);
+  // the RB row panels of one block share its iterate V: keep them on one XCD (one L2) by taking
+  // the XCD-contiguous logical id of the product kernels
+  const int64_t lid = gemm::xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = lid / a.RB;
+  const int rb = (int)(lid - b * a.RB);
   const int r0 = rb * RT;
   const int B = a.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
@@ -319,8 +323,11 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Floa
   __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KV * LDV];
   __shared__ float inv_s[KV];
   __shared__ float red[WAVES][3][KV];
-  const int64_t b = blockIdx.x / a.RB;
-  const int rb = (int)(blockIdx.x - b * a.RB);
+  // the RB row panels of one block share its iterate V: keep them on one XCD (one L2) by taking
+  // the XCD-contiguous logical id of the product kernels
+  const int64_t lid = gemm::xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = lid / a.RB;
+  const int rb = (int)(lid - b * a.RB);
   const int r0 = rb * RT;
   const int B = a.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
