@@ -57,7 +57,7 @@ typedef enum {
  * DASH_FP32_SPLIT: fp32 operands, iterates and results, with each product formed on the bfloat16
  * matrix cores from an exact three-piece split of both operands (six piece products, fp32
  * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec,
- * dash_inverse_root_ndb_prec, dash_update_stats_prec and dash_apply_prec, by
+ * dash_inverse_root_ndb_prec, dash_inverse_root_cn, dash_update_stats_prec and dash_apply_prec, by
  * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts 256-wide tiles
  * for degree >= 3 and B % 256 == 0). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3 } dash_prec;
@@ -180,6 +180,9 @@ dash_status dash_inverse_root_ndb_lowp(const float* A, const float* s, int64_t N
  * each product computes only its upper-triangle tiles and mirrors them, and X_i comes out exactly
  * symmetric.
  * fp32 runs full products, which keep the fp32 rounding floor lowest at high condition numbers.
+ * prec == DASH_FP32_SPLIT: fp32 iterates with the products formed from exact three-piece bfloat16
+ * splits on the bfloat16 matrix cores when B % 256 == 0, except the M S^4 launches that also write
+ * S_{k+1} (fp32 cores; dash_inverse_root_cn_adaptive runs every product on the fp32 cores).
  * monitor: NULL or [N, iters] receives ||M_k - I||_F / sqrt(B) before step k. */
 dash_status dash_inverse_root_cn(const float* A, const float* s, int64_t N, int32_t B, int32_t p, int32_t iters,
                                  dash_prec prec, float* X, float* monitor, int32_t* status, void* ws,

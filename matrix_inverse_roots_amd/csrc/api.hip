@@ -812,7 +812,10 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (X == A || iters < 1 || iters > 1000) return DASH_ERR_INVALID_ARG;
-  if (prec != DASH_FP32 && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
+  // split products: fp32 storage, products on the bfloat16 matrix cores where the shape allows
+  const bool split = prec == DASH_FP32_SPLIT;
+  if (split) prec = DASH_FP32;
   if (monitor && !aligned(monitor, 4)) return DASH_ERR_INVALID_ARG;
   if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
@@ -900,6 +903,9 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
     if (monitor) TRY(launch_monitor_finish(monitor, N * T, B, st));
     return DASH_OK;
   }
+  // the fp32 products' arithmetic: the M S^4 launch that also writes S_{k+1} (a second output)
+  // stays on the fp32 cores, as do stopped blocks
+  const dash_prec pp = (split && B % 256 == 0 && !freeze) ? DASH_FP32_SPLIT : DASH_FP32;
   void* Xk = S;  // X_1 = S_0 shares the buffer (both are read-only from here on)
   for (int k = 0; k < T; ++k) {
     if (freeze && k >= 1)  // monitor column k (||M_k - I||) is complete
@@ -912,19 +918,19 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
       Product pr = prod(Xk, S, X);
       pr.freeze = freeze;
       pr.pass = 1;
-      TRY(launch_gemm(&pr, 1, N, B, prec, DASH_FP32, Trans::NN, false, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, pp, DASH_FP32, Trans::NN, false, e, st, true));
       break;
     }
     void* S2 = pool.get();
     if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
       Product pr = prod(S, S, S2);
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, pp, prec, Trans::NN, false, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
       Product pr[2] = {prod(Xk, S, Xn), prod(S, S, S2)};
       pr[0].freeze = pr[1].freeze = freeze;
       pr[0].pass = 1;  // a stopped block keeps X_k and needs no S^2
-      TRY(launch_gemm(pr, 2, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
+      TRY(launch_gemm(pr, 2, N, B, pp, prec, Trans::NN, false, Epilogue(), st, true));
       pool.put(Xk);
       pool.put(S);
       Xk = Xn;
@@ -933,7 +939,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
     {
       Product pr = prod(S2, S2, S4);
       pr.freeze = freeze;
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, Epilogue(), st, true));
+      TRY(launch_gemm(&pr, 1, N, B, pp, prec, Trans::NN, false, Epilogue(), st, true));
     }
     pool.put(S2);
     // M_{k+1} = M_k S^4 and S_{k+1} = (5I - M_{k+1})/4 from the same accumulator
@@ -949,7 +955,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
       e.mon_mul = 16.f;
       Product pr = prod(M, S4, Sn);
       pr.freeze = freeze;
-      TRY(launch_gemm(&pr, 1, N, B, prec, prec, Trans::NN, false, e, st, true));
+      TRY(launch_gemm(&pr, 1, N, B, pp, prec, Trans::NN, false, e, st, true));
       pool.put(M);
       M = nullptr;
     } else {

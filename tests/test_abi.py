@@ -222,7 +222,7 @@ def test_bfloat16_queries_and_argument_errors():
     assert _status_of(f, P, P2, 4, 64, 6, 6, dash.DASH_BF16, 17, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
     assert (_status_of(f, P, P2, 4, 64, 6, 6, dash.DASH_BF16, 0, 5 * P, ws=FakeWs(P3, ws.n - 1))
             == _lib.DASH_ERR_WORKSPACE)
-    assert _status_of(dash.dash_inverse_root_cn, P, P2, 4, 64, 4, 5, 3, 5 * P,
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, 4, 64, 4, 5, 7, 5 * P,
                       ws=FakeWs(P3, 1 << 30)) == _lib.DASH_ERR_INVALID_ARG
 
 def test_split_precision_queries_and_argument_errors():
@@ -249,8 +249,10 @@ def test_split_precision_queries_and_argument_errors():
     assert _status_of(g, P, P2, N, 96, 8, 0.1, 1.0, dash.DASH_FP32_SPLIT, 5 * P, ws=ws) == _lib.DASH_ERR_SHAPE
     assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, dash.DASH_FP32_SPLIT, 5 * P,
                       ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
-    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 3, dash.DASH_FP32_SPLIT, 5 * P,
-                      ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 2, 3, dash.DASH_FP32_SPLIT, 5 * P,
+                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED                                   # p != 4
+    assert dash.dash_workspace_size(dash.DASH_OP_CN, 8, B, dash.DASH_FP32_SPLIT) == \
+        dash.dash_workspace_size(dash.DASH_OP_CN, 8, B, dash.DASH_FP32)
     h = dash.dash_inverse_root_ndb_prec
     for prec in (dash.DASH_FP16, dash.DASH_BF16, 7):
         assert _status_of(h, P, P2, N, B, 5, 5, prec, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG

@@ -244,3 +244,42 @@ def test_apply_split_matches_oracle(B):
     I = torch.eye(B, device=DEV).expand(NG, B, B).contiguous()
     dash.dash_apply_prec(I, I, to_dev(G), NG, B, SPLIT, U, ws)
     assert np.array_equal(to_host(U), G.astype(np.float64))
+
+
+# ------------------------------------------------------------------------------------------------
+# Coupled Newton in fp32 with split products (every product but the M S^4 launches that also write
+# S_{k+1})
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scaling", ["power", "frobenius"])
+def test_cn_split_conditioned(conditioned, scaling):
+    A, Ad = conditioned
+    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    T = 16
+    N = Ad.shape[0]
+    X = torch.empty_like(Ad)
+    mon = torch.empty((N, T), device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CN, N, 256, SPLIT, device=DEV)
+    dash.dash_inverse_root_cn(Ad, s, N, 256, 4, T, SPLIT, X, monitor=mon, status=status, ws=ws)
+    X_ref, mon_ref = oracle.cn_inverse_root(A, to_host(s), T)
+    err = rel_err(to_host(X), X_ref)
+    print(scaling, "CN split err", err.max())
+    assert err.max() < ITERATE_TOL
+    assert residual(to_host(X), A).max() < R_FP32
+    assert np.all(to_host(status) == 0)
+    m = to_host(mon)
+    assert np.max(np.abs(m[:, :4] - mon_ref[:, :4]) / mon_ref[:, :4]) < 1e-3
+
+
+def test_cn_split_fallback_bitwise():
+    """B = 320 has no 256-wide tiling: the fp32 path bit for bit."""
+    A, Ad = spectrum_stack(460, 2, 320)
+    s = frob_scale(Ad)
+    out = []
+    for prec in (SPLIT, dash.DASH_FP32):
+        X = torch.empty_like(Ad)
+        ws = dash.workspace(dash.DASH_OP_CN, 2, 320, prec, device=DEV)
+        dash.dash_inverse_root_cn(Ad, s, 2, 320, 4, 6, prec, X, ws=ws)
+        out.append(X)
+    assert torch.equal(out[0], out[1])
