@@ -71,7 +71,8 @@ typedef enum {
   DASH_OP_CHEB = 3,
   DASH_OP_APPLY = 4,
   DASH_OP_STATS = 5,
-  DASH_OP_EVD = 6
+  DASH_OP_EVD = 6,
+  DASH_OP_ROUTED = 7
 } dash_op;
 
 /* A row-major fp32 weight gradient (device memory): element (r, c) at ptr[r * ld + c]. */
@@ -228,6 +229,74 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
 dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
                                         double lo, double hi, dash_prec prec, float* X, int32_t* status, void* ws,
                                         size_t ws_bytes, void* stream);
+
+/* dash_inverse_root_cheb_prec with an interval of its own for every block, derived on the device
+ * (the host never reads s; [PT] Metodologia, item 2, "Aproximações de Polinômios de Chebyshev":
+ * the pages give no interval, so the library takes it from what bounds each block's spectrum).
+ * Block i's interval, in units of A_i / s_i, is [lo_i, hi] with
+ *   lo_i = max(floor, theta * lam_min[i]) / s_i        (lam_min == NULL: lo_i = floor / s_i).
+ * floor: an absolute lower bound of every block's spectrum (e.g. the damping eps I added to the
+ *   statistics, times beta^t after t EMA updates), >= 0; > 0 when lam_min is NULL.
+ * lam_min: NULL or [N] per-block estimates of the smallest eigenvalue (dash_spectrum_min), of which
+ *   the fraction theta (0 < theta <= 1) is taken as the lower end.
+ * hi: upper end relative to s_i, > 0 (e.g. 1.25 after power-iteration scaling, 1 after Frobenius).
+ * The degree-`degree` interpolant of x^{-1/4} at the Chebyshev points of the first kind of block i's
+ * interval is computed on the device in fp64.  lo_out: NULL or [N] receives lo_i.  A block whose
+ * lo_i is not in (0, hi) gets status bit 0 and a NaN output (as for a bad s_i); so does a block whose
+ * top Chebyshev coefficient underflows fp32 (degree near 64 on an interval with hi/lo_i near 1).
+ * Products, precision, workspace (DASH_OP_CHEB) and results otherwise as dash_inverse_root_cheb_prec. */
+dash_status dash_inverse_root_cheb_blocks(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
+                                          double floor, const float* lam_min, float theta, double hi, dash_prec prec,
+                                          float* X, float* lo_out, int32_t* status, void* ws, size_t ws_bytes,
+                                          void* stream);
+
+/* Estimate of every block's smallest eigenvalue, from above ([PT] Significância e Alegações,
+ * "Direções Futuras": choosing the solver per block from its conditioning needs the bottom of each
+ * block's spectrum; the pages name the largest eigenvalue's power iteration only, so this is the
+ * same iteration on a shifted block).  With sigma_i = hi * s_i (hi > 0; s from dash_scale, so that
+ * sigma_i >= lambda_max(A_i) when hi covers the scale's underestimate), `steps` power-iteration steps
+ * with the k normalised start vectors V0[B,k] run on C_i = sigma_i I - A_i exactly as dash_scale's
+ * (every column renormalised between steps, Rayleigh quotients from the last step) and
+ *   lam_min[i] = sigma_i - max_j mu_j(C_i)   (>= lambda_min(A_i) up to rounding).
+ * The estimate converges slowly where the bottom of the spectrum is dense (an excess of order
+ * hi s_i / steps), and an isolated small eigenvalue may be missed; callers take a fraction of it
+ * and check the result (dash_inverse_root_routed).  fp32, 1 <= k <= 32, steps >= 1.
+ * Workspace: dash_workspace_size(DASH_OP_SCALE, N, B, DASH_FP32, k, ...). */
+dash_status dash_spectrum_min(const float* A, const float* s, int64_t N, int32_t B, double hi, int32_t k,
+                              int32_t steps, const float* V0, float* lam_min, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Stochastic residual of a computed inverse fourth root: for the k normalised columns v_j of V0[B,k],
+ *   r[i] = sqrt( (1/k) sum_j ||(X_i^4 A_i - I) v_j||^2 ),
+ * formed by five fp32 block-times-vectors passes (A_i v, then X_i four times).  For v uniform on the
+ * sphere E ||E v||^2 = ||E||_F^2 / B, so r[i] estimates the residual ||X_i^4 A_i - I||_F / sqrt(B) of
+ * the accuracy gate (relative spread about sqrt(2/k)) at the cost of five reads of the stack.
+ * 1 <= k <= 32.  Workspace: dash_workspace_size(DASH_OP_SCALE, N, B, DASH_FP32, k, ...). */
+dash_status dash_residual_probe(const float* A, const float* X, int64_t N, int32_t B, int32_t k, const float* V0,
+                                float* r, void* ws, size_t ws_bytes, void* stream);
+
+/* Inverse fourth root with the solver chosen per block inside one call ([PT] Significância e
+ * Alegações, "Direções Futuras": dynamic solver selection per block from its conditioning).
+ *   1. lam_i = dash_spectrum_min estimate (est_steps steps; none when est_steps == 0);
+ *   2. every block solved by degree-`degree` Chebyshev on its own interval
+ *      [max(floor, lam_i / 2) / s_i, hi] (dash_inverse_root_cheb_blocks with theta = 1/2);
+ *   3. the residual of every block estimated by dash_residual_probe with V0's k columns;
+ *   4. the blocks whose estimate exceeds tol (or is NaN) solved again by coupled Newton p = 4 in fp32
+ *      on the fp32 matrix cores, at most cn_iters steps, each block stopping once its monitor
+ *      ||M_k - I|| / sqrt(B) (its exact residual) is <= tol / 2; their X_i replaced.
+ * Blocks the estimate makes well conditioned keep the tight interval's accuracy; ill-conditioned
+ * blocks, or blocks whose bottom eigenvalue the estimate overshot, are caught by the probe.
+ * floor >= 0 (> 0 when est_steps == 0), hi > 0, 1 <= k <= 32, 0 <= est_steps, tol > 0,
+ * 2 <= cn_iters <= 64; prec DASH_FP32 or DASH_FP32_SPLIT (the Chebyshev products).
+ * lam_min: NULL or [N] receives the estimates (NaN when est_steps == 0); route: NULL or [N] receives
+ * 0 (Chebyshev) or 1 (coupled Newton); resid: NULL or [N] receives the probe's residual estimate of
+ * the final X_i (five more passes); status: as for the solvers, from the solver that wrote X_i.
+ * Workspace: dash_workspace_size(DASH_OP_ROUTED, N, B, ...). */
+dash_status dash_inverse_root_routed(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
+                                     double floor, double hi, int32_t k, int32_t est_steps, const float* V0,
+                                     float tol, int32_t cn_iters, dash_prec prec, float* X, float* lam_min,
+                                     float* resid, int32_t* route, int32_t* status, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* Inverse fourth root through an eigendecomposition A_i = Q diag(w) Q^T, X_i = Q diag(w^{-1/4}) Q^T
  * ([PT] Definição do Problema, item 2, and Resultados Experimentais: the eigendecomposition is the

@@ -15,7 +15,8 @@ library_path = os.path.join(_HERE, "libdash.so")
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
 DASH_FP32, DASH_FP16, DASH_BF16, DASH_FP32_SPLIT = 0, 1, 2, 3
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
-DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD = range(7)
+(DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD,
+ DASH_OP_ROUTED) = range(8)
 
 
 class DashError(RuntimeError):
@@ -61,6 +62,12 @@ def library() -> ctypes.CDLL:
             "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
             "dash_apply_prec": (st, [vp, vp, vp, i64, i32, st, vp, vp, sz, vp]),
+            "dash_inverse_root_cheb_blocks": (st, [vp, vp, i64, i32, i32, f64, vp, f32, f64, st, vp, vp, vp, vp, sz,
+                                                   vp]),
+            "dash_spectrum_min": (st, [vp, vp, i64, i32, f64, i32, i32, vp, vp, vp, sz, vp]),
+            "dash_residual_probe": (st, [vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_routed": (st, [vp, vp, i64, i32, i32, f64, f64, i32, i32, vp, f32, i32, st, vp, vp, vp,
+                                              vp, vp, vp, sz, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
             "dash_flops": (f64, [st, i64, i32, st, i32, i32]),
@@ -75,22 +82,83 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def _ptr(t):
-    """Device pointer of a tensor (None -> NULL).  Plain integers pass through (tests of the ABI)."""
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    return t.data_ptr()
+class _Args:
+    """Host-side checks of one call's tensor arguments before their pointers reach the library.
 
+    A torch tensor must be a contiguous GPU tensor of the expected dtype, on the same device as the
+    call's other tensors, with at least as many elements as the call touches; a violation raises
+    ValueError and nothing is enqueued.  ``None`` is NULL.  Plain integers and objects that only
+    expose ``data_ptr()`` pass through unchecked as raw device addresses (the ABI tests use them).
+    """
 
-def _stream(stream, *tensors):
-    if stream is not None:
-        return stream if isinstance(stream, int) else stream.cuda_stream
-    import torch
+    def __init__(self, call: str):
+        self.call = call
+        self.device = None
 
-    dev = next((t.device for t in tensors if hasattr(t, "device") and t.device.type == "cuda"), None)
-    return torch.cuda.current_stream(dev).cuda_stream
+    def _tensor(self, t, name):
+        import torch
+
+        if not isinstance(t, torch.Tensor):
+            return False
+        if t.device.type != "cuda":
+            raise ValueError("%s: %s must be a GPU tensor, got one on %s" % (self.call, name, t.device))
+        if self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            raise ValueError("%s: %s is on %s, the call's other tensors on %s" % (self.call, name, t.device,
+                                                                                  self.device))
+        return True
+
+    def ptr(self, t, name, dtype="float32", numel=0):
+        """Pointer of tensor argument `name` of `dtype` ('float32', 'int32' or None for any) holding
+        at least `numel` elements."""
+        if t is None:
+            return None
+        if isinstance(t, int):
+            return t
+        if self._tensor(t, name):
+            import torch
+
+            want = {"float32": torch.float32, "int32": torch.int32}.get(dtype)
+            if want is not None and t.dtype != want:
+                raise ValueError("%s: %s must be %s, got %s" % (self.call, name, dtype, t.dtype))
+            if not t.is_contiguous():
+                raise ValueError("%s: %s must be contiguous" % (self.call, name))
+            if t.numel() < numel:
+                raise ValueError("%s: %s holds %d elements, the call touches %d" % (self.call, name, t.numel(),
+                                                                                     int(numel)))
+        return t.data_ptr()
+
+    def ws(self, t):
+        """Workspace tensor: any dtype, contiguous, on the call's device; its byte size is checked by
+        the library against dash_workspace_size."""
+        if t is None or isinstance(t, int):
+            return t
+        if self._tensor(t, "ws") and not t.is_contiguous():
+            raise ValueError("%s: ws must be contiguous" % self.call)
+        return t.data_ptr()
+
+    def mats(self, ts, name):
+        """dash_mat descriptors of 2-D fp32 GPU matrices with unit column stride."""
+        arr = (DashMat * len(ts))()
+        for i, t in enumerate(ts):
+            if self._tensor(t, "%s[%d]" % (name, i)):
+                import torch
+
+                if t.dim() != 2 or t.dtype != torch.float32 or t.stride(1) != 1:
+                    raise ValueError("%s: %s[%d] must be a 2-D float32 matrix with unit column stride"
+                                     % (self.call, name, i))
+            arr[i].ptr = t.data_ptr()
+            arr[i].rows, arr[i].cols = t.shape
+            arr[i].ld = t.stride(0)
+        return arr
+
+    def stream(self, stream):
+        if stream is not None:
+            return stream if isinstance(stream, int) else stream.cuda_stream
+        import torch
+
+        return torch.cuda.current_stream(self.device).cuda_stream
 
 
 def _check(name, status):
@@ -99,7 +167,13 @@ def _check(name, status):
 
 
 def _nbytes(t):
-    return 0 if t is None else t.numel() * t.element_size()
+    if t is None or isinstance(t, int):
+        return 0
+    return t.numel() * t.element_size()
+
+
+def _tiles(shapes, B):
+    return sum((-(-r // B)) * (-(-c // B)) for r, c in shapes) if B > 0 else 0
 
 
 def dash_status_string(status: int) -> str:
@@ -134,120 +208,209 @@ def workspace(op: int, N: int, B: int, prec: int = DASH_FP32, k_or_degree: int =
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _mats(ts):
-    arr = (DashMat * len(ts))()
-    for i, t in enumerate(ts):
-        arr[i].ptr = _ptr(t)
-        arr[i].rows, arr[i].cols = t.shape
-        arr[i].ld = t.stride(0)
-    return arr
-
-
 def dash_stack(grads, B: int, G_stack, stream=None):
-    arr = _mats(grads)
-    _check("dash_stack", library().dash_stack(arr, len(grads), B, _ptr(G_stack), _stream(stream, G_stack)))
+    a = _Args("dash_stack")
+    arr = a.mats(grads, "grads")
+    n = _tiles([tuple(t.shape) for t in grads], B) * B * B
+    _check("dash_stack", library().dash_stack(arr, len(grads), B, a.ptr(G_stack, "G_stack", numel=n), a.stream(stream)))
 
 
 def dash_unstack(U_stack, B: int, outs, stream=None):
-    arr = _mats(outs)
-    _check("dash_unstack", library().dash_unstack(_ptr(U_stack), B, arr, len(outs), _stream(stream, U_stack)))
+    a = _Args("dash_unstack")
+    arr = a.mats(outs, "outs")
+    n = _tiles([tuple(t.shape) for t in outs], B) * B * B
+    _check("dash_unstack", library().dash_unstack(a.ptr(U_stack, "U_stack", numel=n), B, arr, len(outs),
+                                                  a.stream(stream)))
 
 
 def dash_update_stats(G_stack, NG: int, B: int, beta: float, A, stream=None):
+    a = _Args("dash_update_stats")
     _check("dash_update_stats",
-           library().dash_update_stats(_ptr(G_stack), NG, B, beta, _ptr(A), _stream(stream, A)))
+           library().dash_update_stats(a.ptr(G_stack, "G_stack", numel=NG * B * B), NG, B, beta,
+                                       a.ptr(A, "A", numel=2 * NG * B * B), a.stream(stream)))
 
 
 def dash_update_stats_prec(G_stack, NG: int, B: int, beta: float, prec: int, A, stream=None):
+    a = _Args("dash_update_stats_prec")
     _check("dash_update_stats_prec",
-           library().dash_update_stats_prec(_ptr(G_stack), NG, B, beta, prec, _ptr(A), _stream(stream, A)))
+           library().dash_update_stats_prec(a.ptr(G_stack, "G_stack", numel=NG * B * B), NG, B, beta, prec,
+                                            a.ptr(A, "A", numel=2 * NG * B * B), a.stream(stream)))
 
 
 def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, ws=None, stream=None):
-    _check("dash_scale", library().dash_scale(_ptr(A), N, B, how, prec, k, steps, _ptr(V0), _ptr(s), _ptr(ws),
-                                              _nbytes(ws), _stream(stream, A)))
+    a = _Args("dash_scale")
+    vn = B * k if how == DASH_SCALE_POWER else 0
+    _check("dash_scale", library().dash_scale(a.ptr(A, "A", numel=N * B * B), N, B, how, prec, k, steps,
+                                              a.ptr(V0, "V0", numel=vn), a.ptr(s, "s", numel=N), a.ws(ws),
+                                              _nbytes(ws), a.stream(stream)))
+
+
+def dash_spectrum_min(A, s, N: int, B: int, hi: float, k: int, steps: int, V0, lam_min, ws=None, stream=None):
+    a = _Args("dash_spectrum_min")
+    _check("dash_spectrum_min",
+           library().dash_spectrum_min(a.ptr(A, "A", numel=N * B * B), a.ptr(s, "s", numel=N), N, B, hi, k, steps,
+                                       a.ptr(V0, "V0", numel=B * k), a.ptr(lam_min, "lam_min", numel=N), a.ws(ws),
+                                       _nbytes(ws), a.stream(stream)))
+
+
+def dash_residual_probe(A, X, N: int, B: int, k: int, V0, r, ws=None, stream=None):
+    a = _Args("dash_residual_probe")
+    _check("dash_residual_probe",
+           library().dash_residual_probe(a.ptr(A, "A", numel=N * B * B), a.ptr(X, "X", numel=N * B * B), N, B, k,
+                                         a.ptr(V0, "V0", numel=B * k), a.ptr(r, "r", numel=N), a.ws(ws),
+                                         _nbytes(ws), a.stream(stream)))
+
+
+def _solver_ptrs(a, A, s, X, N, B):
+    return a.ptr(A, "A", numel=N * B * B), a.ptr(s, "s", numel=N), a.ptr(X, "X", numel=N * B * B)
 
 
 def dash_inverse_root_ndb(A, s, N: int, B: int, iters1: int, iters2: int, X, sqrt_out=None, monitor=None,
                           status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_ndb")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_ndb",
-           library().dash_inverse_root_ndb(_ptr(A), _ptr(s), N, B, iters1, iters2, _ptr(X), _ptr(sqrt_out),
-                                           _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_ndb(pA, ps, N, B, iters1, iters2, pX, a.ptr(sqrt_out, "sqrt_out", numel=N * B * B),
+                                           a.ptr(monitor, "monitor", numel=N * (iters1 + iters2)),
+                                           a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                           a.stream(stream)))
 
 
 def dash_inverse_root_ndb_prec(A, s, N: int, B: int, iters1: int, iters2: int, prec: int, X, sqrt_out=None,
                                monitor=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_ndb_prec")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_ndb_prec",
-           library().dash_inverse_root_ndb_prec(_ptr(A), _ptr(s), N, B, iters1, iters2, prec, _ptr(X), _ptr(sqrt_out),
-                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_ndb_prec(pA, ps, N, B, iters1, iters2, prec, pX,
+                                                a.ptr(sqrt_out, "sqrt_out", numel=N * B * B),
+                                                a.ptr(monitor, "monitor", numel=N * (iters1 + iters2)),
+                                                a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                a.stream(stream)))
 
 
 def dash_inverse_root_cn(A, s, N: int, B: int, p: int, iters: int, prec: int, X, monitor=None, status=None,
                          ws=None, stream=None):
+    a = _Args("dash_inverse_root_cn")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_cn",
-           library().dash_inverse_root_cn(_ptr(A), _ptr(s), N, B, p, iters, prec, _ptr(X), _ptr(monitor),
-                                          _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_cn(pA, ps, N, B, p, iters, prec, pX, a.ptr(monitor, "monitor", numel=N * iters),
+                                          a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                          a.stream(stream)))
 
 
 def dash_inverse_root_ndb_half(A, s, N: int, B: int, iters1: int, iters2: int, refine: int, X, monitor=None,
                                status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_ndb_half")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_ndb_half",
-           library().dash_inverse_root_ndb_half(_ptr(A), _ptr(s), N, B, iters1, iters2, refine, _ptr(X),
-                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws),
-                                                _stream(stream, A)))
+           library().dash_inverse_root_ndb_half(pA, ps, N, B, iters1, iters2, refine, pX,
+                                                a.ptr(monitor, "monitor", numel=N * (iters1 + iters2)),
+                                                a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                a.stream(stream)))
 
 
 def dash_inverse_root_ndb_lowp(A, s, N: int, B: int, iters1: int, iters2: int, prec: int, refine: int, X,
                                monitor=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_ndb_lowp")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_ndb_lowp",
-           library().dash_inverse_root_ndb_lowp(_ptr(A), _ptr(s), N, B, iters1, iters2, prec, refine, _ptr(X),
-                                                _ptr(monitor), _ptr(status), _ptr(ws), _nbytes(ws),
-                                                _stream(stream, A)))
+           library().dash_inverse_root_ndb_lowp(pA, ps, N, B, iters1, iters2, prec, refine, pX,
+                                                a.ptr(monitor, "monitor", numel=N * (iters1 + iters2)),
+                                                a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                a.stream(stream)))
 
 
 def dash_inverse_root_ndb_adaptive(A, s, N: int, B: int, max_iters1: int, max_iters2: int, tol: float, X, monitor,
                                    sqrt_out=None, steps=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_ndb_adaptive")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_ndb_adaptive",
-           library().dash_inverse_root_ndb_adaptive(_ptr(A), _ptr(s), N, B, max_iters1, max_iters2, tol, _ptr(X),
-                                                    _ptr(sqrt_out), _ptr(monitor), _ptr(steps), _ptr(status),
-                                                    _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_ndb_adaptive(pA, ps, N, B, max_iters1, max_iters2, tol, pX,
+                                                    a.ptr(sqrt_out, "sqrt_out", numel=N * B * B),
+                                                    a.ptr(monitor, "monitor", numel=N * (max_iters1 + max_iters2)),
+                                                    a.ptr(steps, "steps", "int32", 2 * N),
+                                                    a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                    a.stream(stream)))
 
 
 def dash_inverse_root_cn_adaptive(A, s, N: int, B: int, p: int, max_iters: int, tol: float, prec: int, X, monitor,
                                   steps=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_cn_adaptive")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_cn_adaptive",
-           library().dash_inverse_root_cn_adaptive(_ptr(A), _ptr(s), N, B, p, max_iters, tol, prec, _ptr(X),
-                                                   _ptr(monitor), _ptr(steps), _ptr(status), _ptr(ws), _nbytes(ws),
-                                                   _stream(stream, A)))
+           library().dash_inverse_root_cn_adaptive(pA, ps, N, B, p, max_iters, tol, prec, pX,
+                                                   a.ptr(monitor, "monitor", numel=N * max_iters),
+                                                   a.ptr(steps, "steps", "int32", N),
+                                                   a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                   a.stream(stream)))
 
 
 def dash_inverse_root_cheb(A, s, N: int, B: int, degree: int, lo: float, hi: float, X, status=None, ws=None,
                            stream=None):
+    a = _Args("dash_inverse_root_cheb")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_cheb",
-           library().dash_inverse_root_cheb(_ptr(A), _ptr(s), N, B, degree, lo, hi, _ptr(X), _ptr(status), _ptr(ws),
-                                            _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_cheb(pA, ps, N, B, degree, lo, hi, pX, a.ptr(status, "status", "int32", N),
+                                            a.ws(ws), _nbytes(ws), a.stream(stream)))
 
 
 def dash_inverse_root_cheb_prec(A, s, N: int, B: int, degree: int, lo: float, hi: float, prec: int, X, status=None,
                                 ws=None, stream=None):
+    a = _Args("dash_inverse_root_cheb_prec")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
     _check("dash_inverse_root_cheb_prec",
-           library().dash_inverse_root_cheb_prec(_ptr(A), _ptr(s), N, B, degree, lo, hi, prec, _ptr(X), _ptr(status),
-                                                 _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_cheb_prec(pA, ps, N, B, degree, lo, hi, prec, pX,
+                                                 a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                 a.stream(stream)))
+
+
+def dash_inverse_root_cheb_blocks(A, s, N: int, B: int, degree: int, floor: float, lam_min, theta: float, hi: float,
+                                  prec: int, X, lo_out=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_cheb_blocks")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
+    _check("dash_inverse_root_cheb_blocks",
+           library().dash_inverse_root_cheb_blocks(pA, ps, N, B, degree, floor, a.ptr(lam_min, "lam_min", numel=N),
+                                                   theta, hi, prec, pX, a.ptr(lo_out, "lo_out", numel=N),
+                                                   a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                   a.stream(stream)))
+
+
+def dash_inverse_root_routed(A, s, N: int, B: int, degree: int, floor: float, hi: float, k: int, est_steps: int, V0,
+                             tol: float, cn_iters: int, prec: int, X, lam_min=None, resid=None, route=None,
+                             status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_routed")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
+    _check("dash_inverse_root_routed",
+           library().dash_inverse_root_routed(pA, ps, N, B, degree, floor, hi, k, est_steps,
+                                              a.ptr(V0, "V0", numel=B * k), tol, cn_iters, prec, pX,
+                                              a.ptr(lam_min, "lam_min", numel=N), a.ptr(resid, "resid", numel=N),
+                                              a.ptr(route, "route", "int32", N), a.ptr(status, "status", "int32", N),
+                                              a.ws(ws), _nbytes(ws), a.stream(stream)))
 
 
 def dash_inverse_root_evd(A, N: int, B: int, max_sweeps: int, refine: int, X, eigvals=None, sweeps=None, status=None,
                           ws=None, stream=None):
+    a = _Args("dash_inverse_root_evd")
     _check("dash_inverse_root_evd",
-           library().dash_inverse_root_evd(_ptr(A), N, B, max_sweeps, refine, _ptr(X), _ptr(eigvals), _ptr(sweeps),
-                                           _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream, A)))
+           library().dash_inverse_root_evd(a.ptr(A, "A", numel=N * B * B), N, B, max_sweeps, refine,
+                                           a.ptr(X, "X", numel=N * B * B), a.ptr(eigvals, "eigvals", numel=N * B),
+                                           a.ptr(sweeps, "sweeps", "int32", N), a.ptr(status, "status", "int32", N),
+                                           a.ws(ws), _nbytes(ws), a.stream(stream)))
 
 
 def dash_apply(XL, XR, G_stack, NG: int, B: int, U_stack, ws=None, stream=None):
-    _check("dash_apply", library().dash_apply(_ptr(XL), _ptr(XR), _ptr(G_stack), NG, B, _ptr(U_stack), _ptr(ws),
-                                              _nbytes(ws), _stream(stream, G_stack)))
+    a = _Args("dash_apply")
+    n = NG * B * B
+    _check("dash_apply", library().dash_apply(a.ptr(XL, "XL", numel=n), a.ptr(XR, "XR", numel=n),
+                                              a.ptr(G_stack, "G_stack", numel=n), NG, B,
+                                              a.ptr(U_stack, "U_stack", numel=n), a.ws(ws), _nbytes(ws),
+                                              a.stream(stream)))
 
 
 def dash_apply_prec(XL, XR, G_stack, NG: int, B: int, prec: int, U_stack, ws=None, stream=None):
+    a = _Args("dash_apply_prec")
+    n = NG * B * B
     _check("dash_apply_prec",
-           library().dash_apply_prec(_ptr(XL), _ptr(XR), _ptr(G_stack), NG, B, prec, _ptr(U_stack), _ptr(ws),
-                                     _nbytes(ws), _stream(stream, G_stack)))
+           library().dash_apply_prec(a.ptr(XL, "XL", numel=n), a.ptr(XR, "XR", numel=n),
+                                     a.ptr(G_stack, "G_stack", numel=n), NG, B, prec,
+                                     a.ptr(U_stack, "U_stack", numel=n), a.ws(ws), _nbytes(ws), a.stream(stream)))

@@ -73,10 +73,26 @@ size_t ws_ndb_half(int64_t N, int B) {
   return coef_bytes(N) + 2 * flag_bytes(N) + align_up((size_t)N * 17 * sizeof(float), 256) + ndb_half_region(N, B);
 }
 size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, p); }
-size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
+size_t cheb_tab_bytes(int64_t N);
+size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
 size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
 size_t ws_scale(int64_t N, int B, dash_prec p, int k) { return k == 0 ? 0 : power_workspace_bytes(N, B, p); }
+// routed solve: per-block arrays (estimate, probe result, route, freeze, the second solver's status
+// and monitor), then one region that the estimate, the Chebyshev solve, the probes and the coupled
+// Newton fallback use in turn
+constexpr int ROUTED_MAX_CN_ITERS = 64;
+size_t ws_routed_arrays(int64_t N) {
+  return 2 * align_up((size_t)N * sizeof(float), 256) + 3 * flag_bytes(N) +
+         align_up((size_t)N * ROUTED_MAX_CN_ITERS * sizeof(float), 256);
+}
+size_t ws_routed(int64_t N, int B) {
+  size_t region = ws_cheb(N, B);
+  const size_t cn = ws_cn(N, B, DASH_FP32), pw = power_workspace_bytes(N, B, DASH_FP32);
+  if (cn > region) region = cn;
+  if (pw > region) region = pw;
+  return ws_routed_arrays(N) + region;
+}
 
 Product prod(const void* X, const void* Y, void* D, const float* C = nullptr, const float* E = nullptr,
              void* D2 = nullptr) {
@@ -329,19 +345,135 @@ dash_status ndb_half_call(const NdbCtx& c, dash_prec H, void* M, bool m_from_poo
   return DASH_OK;
 }
 
-// Chebyshev interpolation coefficients of x^{-1/4} on [lo, hi] at the d+1 Chebyshev points of the
-// first kind (the interpolant in the Chebyshev basis of t = (2x - lo - hi)/(hi - lo)).
-void cheb_coefficients(int d, double lo, double hi, std::vector<double>& c) {
-  const double pi = std::acos(-1.0);
-  c.assign(d + 1, 0.0);
-  for (int j = 0; j <= d; ++j) {
-    const double theta = pi * (j + 0.5) / (d + 1);
-    const double x = 0.5 * ((hi - lo) * std::cos(theta) + hi + lo);
-    const double fx = 1.0 / std::sqrt(std::sqrt(x));
-    for (int k = 0; k <= d; ++k) c[k] += fx * std::cos(k * theta);
+// Interval of the Chebyshev solve per block, in units of A_b / s_b: [lo_rel, hi] for every block
+// when lo_rel > 0, else [max(floor, theta lam[b]) / s_b, hi].
+struct ChebInterval {
+  double lo_rel = 0.0, floor = 0.0, hi = 1.0;
+  const float* lam = nullptr;
+  float theta = 1.f;
+};
+
+size_t cheb_tab_bytes(int64_t N) {
+  return align_up((size_t)N * COEF_STRIDE * sizeof(float) * (CHEB_MAX_DEGREE - 1), 256);
+}
+
+// The Clenshaw recurrence on A/s with the per-block plan of launch_cheb_plan: b_{d+1} = b_{d+2} = 0,
+// b_k = c_k I + 2 T b_{k+1} - b_{k+2} (k = d .. 1), X = s^{-1/4} (c_0 I + T b_1 - b_2),
+// T = (2 A/s - (hi + lo) I) / (hi - lo); d - 1 products, each epilogue reading its launch's row of
+// the plan.  b_d and b_{d-1} are never stored: the first product reads A mapped to b_{d-1} (or, with
+// split products, is written as a product of A with itself), and the second takes A as b_{k+2}.
+dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, const ChebInterval& iv,
+                      dash_prec prec, float* X, float* lo_out, int32_t* status, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (X == A || degree < 1 || degree > CHEB_MAX_DEGREE) return DASH_ERR_INVALID_ARG;
+  if ((status && !aligned(status, 4)) || (lo_out && !aligned(lo_out, 4))) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_cheb(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  float* tab = (float*)cv.take(cheb_tab_bytes(N));
+  float* b1 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
+  float* b2 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
+  const int d = degree;
+  // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
+  // stored mirrored; the first product maps A on the fp32 cores unless it can be written as
+  // (alpha a1/s)(A + c I) A (degree >= 3), which the split kernel forms with A read by columns
+  const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
+  const bool split_first = split && d >= 3;
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  {
+    ChebPlan cp;
+    cp.N = N;
+    cp.d = d;
+    cp.split_first = split_first;
+    cp.s = s;
+    cp.coef = coef;
+    cp.lo_rel = iv.lo_rel;
+    cp.floor = iv.floor;
+    cp.lam = iv.lam;
+    cp.theta = iv.theta;
+    cp.hi = iv.hi;
+    cp.tab = tab;
+    cp.lo_out = lo_out;
+    cp.status = status;
+    TRY(launch_cheb_plan(cp, st));
   }
-  for (int k = 0; k <= d; ++k) c[k] *= 2.0 / (d + 1);
-  c[0] *= 0.5;
+  auto row = [&](int q) { return (const float*)(tab + (int64_t)q * N * COEF_STRIDE); };
+  if (d == 1) {
+    Affine fin;
+    fin.X = A;
+    fin.D = X;
+    fin.a = 1.f;
+    fin.ia = CS_ALPHA;
+    fin.g = 1.f;
+    fin.ig = CS_GAMMA;
+    fin.coef = row(0);
+    fin.status = status;
+    TRY(launch_affine(fin, N, B, st));
+    return DASH_OK;
+  }
+  // launch q's epilogue: every coefficient from its row of the plan (C = b_{k+1} folded)
+  auto epi = [&](int q, bool last) {
+    Epilogue e;
+    e.coef = row(q);
+    e.alpha = 1.f;
+    e.ia = CS_ALPHA;
+    e.beta = 1.f;
+    e.ib = CS_BETA;
+    e.gamma = 1.f;
+    e.ig = CS_GAMMA;
+    e.delta = 1.f;
+    e.id = CS_DELTA;
+    e.fold_c = true;
+    e.c_over_a = 1.f;
+    e.ic = CS_COVERA;
+    if (last) e.status = status;
+    return e;
+  };
+  auto run = [&](Product& pr, const Epilogue& e) {
+    const bool sp = split && !pr.map_y;
+    return launch_gemm(&pr, 1, N, B, sp ? DASH_FP32_SPLIT : DASH_FP32, DASH_FP32, Trans::NN, true, e, st, sp);
+  };
+  // the first product: k = d - 2 (or the final one when d == 2); b_{k+2} = b_d = c_d I rides in gamma
+  if (split_first) {
+    Product pr = prod(A, A, b2, A);
+    Epilogue e = epi(0, false);
+    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32_SPLIT, DASH_FP32, Trans::NN, true, e, st, false));
+  } else {
+    const bool last = (d == 2);
+    Product pr = prod(A, A, last ? (void*)X : (void*)b2, A, nullptr);
+    pr.map_y = true;
+    pr.map_a = 1.f;
+    pr.map_ia = CS_MAPA;
+    pr.map_g = 1.f;
+    pr.map_ig = CS_MAPG;
+    TRY(run(pr, epi(0, last)));
+    if (last) return DASH_OK;
+  }
+  // the second product: k = d - 3 (or the final one when d == 3), b_{k+2} = b_{d-1} read as A
+  // (A is symmetric, so its upper-triangle tiles serve)
+  {
+    const bool last = (d == 3);
+    Product pr = prod(A, b2, last ? (void*)X : (void*)b1, b2, A);
+    TRY(run(pr, epi(1, last)));
+    if (last) return DASH_OK;
+  }
+  // b_{d-3} is in b1 and b_{d-2} in b2, i.e. b1 = b_{k+1} and b2 = b_{k+2} for k = d - 4; from here
+  // on b_k is written over b_{k+2}
+  int q = 2;
+  for (int k = d - 4; k >= 1; --k, ++q) {
+    Product pr = prod(A, b1, b2, b1, b2);
+    TRY(run(pr, epi(q, false)));
+    std::swap(b1, b2);
+  }
+  Product pr = prod(A, b1, X, b1, b2);
+  TRY(run(pr, epi(q, true)));
+  return DASH_OK;
 }
 
 dash_status check_mats(const dash_mat* m, int32_t n, int32_t B, int64_t* tiles) {
@@ -490,6 +622,7 @@ double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, 
     case DASH_OP_APPLY: return 2.0 * full;
     case DASH_OP_STATS: return 2.0 * full * tri(DASH_FP32);
     case DASH_OP_SCALE: return a1 < 1 ? -1.0 : 2.0 * B * (double)B * 32.0 * a1 * (double)N;
+    case DASH_OP_ROUTED: return -1.0;  // the work depends on the routing the data decides
     case DASH_OP_EVD: {
       // per round: P(P-1)/2 off-pair blocks (two 64^3 products) and P * B/64 eigenvector tiles (one);
       // B/32 - 1 rounds per sweep; then X = Y Y^T (triangle-only)
@@ -517,6 +650,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
     case DASH_OP_NDB: *bytes = half_prec(prec) ? ws_ndb_half(N, B) : ws_ndb(N, B); return DASH_OK;
     case DASH_OP_CN: *bytes = ws_cn(N, B, prec); return DASH_OK;
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
+    case DASH_OP_ROUTED: *bytes = ws_routed(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
     case DASH_OP_STATS: *bytes = 0; return DASH_OK;
     case DASH_OP_EVD: *bytes = ws_evd(N, B); return DASH_OK;
@@ -607,6 +741,9 @@ namespace {
 struct Stop {
   float tol = -1.f;
   int32_t* steps = nullptr;
+  // routed calls: the caller's freeze array, already set (2 = a block this call must leave alone,
+  // 0 = a block to solve); no reset and no step counts
+  int32_t* freeze_ext = nullptr;
 };
 
 dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1, int32_t iters2, float* X,
@@ -833,7 +970,10 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
   const int T = iters;
   // adaptive stopping: a block whose monitor ||M_k - I|| is <= tol before step k >= 1 keeps X_k
   // from then on
-  if (stop.tol >= 0.f) {
+  if (stop.freeze_ext) {
+    if (T < 2 || stop.tol < 0.f || stop.steps || half_prec(prec)) return DASH_ERR_INVALID_ARG;
+    freeze = stop.freeze_ext;
+  } else if (stop.tol >= 0.f) {
     TRY(launch_freeze_reset(freeze, stop.steps, 1, T, N, st));
   } else {
     freeze = nullptr;
@@ -924,6 +1064,7 @@ dash_status cn_impl(const float* A, const float* s, int64_t N, int32_t B, int32_
     void* S2 = pool.get();
     if (k == 0) {  // X_1 = S_0 needs no product; S_0 stays alive as X_1
       Product pr = prod(S, S, S2);
+      pr.freeze = stop.freeze_ext;  // blocks left to another solver are skipped from the start
       TRY(launch_gemm(&pr, 1, N, B, pp, prec, Trans::NN, false, Epilogue(), st, true));
     } else {  // X_{k+1} = X_k S and S^2 in one launch; X_k and S are dead afterwards
       void* Xn = pool.get();
@@ -1004,126 +1145,26 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
 dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
                                         double lo, double hi, dash_prec prec, float* X, int32_t* status, void* ws,
                                         size_t ws_bytes, void* stream) {
-  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
-  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
-    return DASH_ERR_INVALID_ARG;
-  if (X == A || degree < 1 || degree > 64) return DASH_ERR_INVALID_ARG;
   if (!(std::isfinite(lo) && std::isfinite(hi) && lo > 0.0 && hi > lo)) return DASH_ERR_INVALID_ARG;
-  if (status && !aligned(status, 4)) return DASH_ERR_INVALID_ARG;
-  if (!valid_B(B)) return DASH_ERR_SHAPE;
-  if (!ws || !aligned(ws, 256) || ws_bytes < ws_cheb(N, B)) return DASH_ERR_WORKSPACE;
-  hipStream_t st = as_stream(stream);
-  Carver cv{(char*)ws, ws_bytes};
-  float* coef = (float*)cv.take(coef_bytes(N));
-  float* b1 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
-  float* b2 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
-  if (status) TRY(launch_fill_i32(status, N, 0, st));
-  TRY(launch_coef(s, N, coef, status, st));
-  std::vector<double> c;
-  cheb_coefficients(degree, lo, hi, c);
-  const int d = degree;
-  const double w = hi - lo, m = hi + lo;
-  if (d == 1) {  // X = u (c0 I + c1 T),  T = (2 A/s - m I)/w
-    Affine fin;
-    fin.X = A;
-    fin.D = X;
-    fin.a = (float)(2.0 * c[1] / w);
-    fin.ia = CO_R1U;
-    fin.g = (float)(c[0] - c[1] * m / w);
-    fin.ig = CO_U;
-    fin.coef = coef;
-    fin.status = status;
-    TRY(launch_affine(fin, N, B, st));
-    return DASH_OK;
-  }
-  // b_d = c_d I and b_{d-1} = c_{d-1} I + 2 T b_d = a1 A/s + g1 I are never stored: the first
-  // product reads A mapped to b_{d-1} (its C term rides in with it), b_d enters its gamma, and the
-  // second product takes A itself as E for b_{d-1}.
-  const double a1 = 4.0 * c[d] / w, g1 = c[d - 1] - 2.0 * c[d] * m / w;
-  auto clenshaw = [&](const void* Y, const float* E, void* D, bool last) {
-    Epilogue e;
-    e.fold_c = true;  // beta / alpha = -(m / 2) s for every product
-    e.c_over_a = (float)(-0.5 * m);
-    e.ic = CO_S;
-    e.coef = coef;
-    if (last) {  // X = u (c_0 I + T b_1 - b_2)
-      e.alpha = (float)(2.0 / w);
-      e.ia = CO_R1U;
-      e.beta = (float)(-m / w);
-      e.ib = CO_U;
-      e.ig = CO_U;
-      e.id = CO_U;
-      e.status = status;
-    } else {  // b_k = c_k I + 2 T b_{k+1} - b_{k+2}
-      e.alpha = (float)(4.0 / w);
-      e.ia = CO_R1;
-      e.beta = (float)(-2.0 * m / w);
-    }
-    e.delta = -1.f;
-    Product pr = prod(A, Y, D, (const float*)Y, E);
-    return std::make_pair(pr, e);
-  };
-  // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
-  // stored mirrored; the first product, which maps A as it stages it, stays on the fp32 cores
-  const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
-  // (split products fold C = b_{k+1} into A's diagonal: alpha (A - (m s / 2) I) b_{k+1})
-  auto run = [&](std::pair<Product, Epilogue> pe) {
-    const bool sp = split && !pe.first.map_y;
-    return launch_gemm(&pe.first, 1, N, B, sp ? DASH_FP32_SPLIT : DASH_FP32, DASH_FP32, Trans::NN, true, pe.second,
-                       st, sp);
-  };
-  auto map_first = [&](Product& p) {  // Y = A read as b_{d-1}
-    p.map_y = true;
-    p.map_a = (float)a1;
-    p.map_ia = CO_R1;
-    p.map_g = (float)g1;
-  };
-  // the first product: k = d - 2 (or the final one when d == 2), E = b_d = c_d I folded into gamma.
-  // With split products (d >= 3): b_{d-1} = a1 A/s + g1 I turns alpha A b + beta b + gamma I into
-  // (alpha a1 / s) (A + c I) A + (gamma + beta g1) I with c = s (g1/a1 - m/2): A times A with the
-  // fold's diagonal term (A read by columns, so A need not be bitwise symmetric)
-  if (split && d >= 3 && a1 != 0.0) {
-    Epilogue e;
-    e.alpha = (float)(4.0 * a1 / w);  // (4/w)(1/s) a1 (1/s)
-    e.ia = CO_R2;
-    e.fold_c = true;
-    e.c_over_a = (float)(g1 / a1 - 0.5 * m);
-    e.ic = CO_S;
-    e.gamma = (float)(c[d - 2] - c[d] - 2.0 * m / w * g1);
-    e.coef = coef;
-    Product pr = prod(A, A, b2, A);
-    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32_SPLIT, DASH_FP32, Trans::NN, true, e, st, false));
-  } else {
-    const bool last = (d == 2);
-    auto pe = clenshaw(A, nullptr, last ? (void*)X : (void*)b2, last);
-    map_first(pe.first);
-    pe.second.gamma = (float)((last ? c[0] : c[d - 2]) - c[d]);
-    TRY(run(pe));
-    if (last) return DASH_OK;
-  }
-  // the second product: k = d - 3 (or the final one when d == 3), E = b_{d-1} = a1 A/s + g1 I read
-  // as A with its coefficients (A is symmetric, so its upper-triangle tiles serve as E)
-  {
-    const bool last = (d == 3);
-    auto pe = clenshaw(b2, A, last ? (void*)X : (void*)b1, last);
-    pe.second.delta = (float)(-a1);
-    pe.second.id = last ? CO_R1U : CO_R1;
-    pe.second.gamma = (float)((last ? c[0] : c[d - 3]) - g1);
-    TRY(run(pe));
-    if (last) return DASH_OK;
-  }
-  // b_{d-3} is in b1 and b_{d-2} in b2, i.e. b1 = b_{k+1} and b2 = b_{k+2} for k = d - 4; from here
-  // on b_k is written over b_{k+2}
-  for (int k = d - 4; k >= 1; --k) {
-    auto pe = clenshaw(b1, b2, b2, false);
-    pe.second.gamma = (float)c[k];
-    TRY(run(pe));
-    std::swap(b1, b2);
-  }
-  auto pe = clenshaw(b1, b2, X, true);
-  pe.second.gamma = (float)c[0];
-  TRY(run(pe));
-  return DASH_OK;
+  ChebInterval iv;
+  iv.lo_rel = lo;
+  iv.hi = hi;
+  return cheb_impl(A, s, N, B, degree, iv, prec, X, nullptr, status, ws, ws_bytes, stream);
+}
+
+dash_status dash_inverse_root_cheb_blocks(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
+                                          double floor, const float* lam_min, float theta, double hi, dash_prec prec,
+                                          float* X, float* lo_out, int32_t* status, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  if (!(std::isfinite(floor) && floor >= 0.0 && std::isfinite(hi) && hi > 0.0)) return DASH_ERR_INVALID_ARG;
+  if (lam_min && (!aligned(lam_min, 4) || !(theta > 0.f && theta <= 1.f))) return DASH_ERR_INVALID_ARG;
+  if (!lam_min && !(floor > 0.0)) return DASH_ERR_INVALID_ARG;
+  ChebInterval iv;
+  iv.floor = floor;
+  iv.lam = lam_min;
+  iv.theta = theta;
+  iv.hi = hi;
+  return cheb_impl(A, s, N, B, degree, iv, prec, X, lo_out, status, ws, ws_bytes, stream);
 }
 
 dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine, float* X,
@@ -1219,6 +1260,131 @@ dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_sta
   TRY(launch_gemm(&p1, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   Product p2 = prod(T, XR, U_stack);
   TRY(launch_gemm(&p2, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
+  return DASH_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Spectrum bounds, the residual probe and the routed (two-solver) inverse root
+// ------------------------------------------------------------------------------------------------
+
+dash_status dash_spectrum_min(const float* A, const float* s, int64_t N, int32_t B, double hi, int32_t k,
+                              int32_t steps, const float* V0, float* lam_min, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!A || !s || !V0 || !lam_min || !aligned(A, 16) || !aligned(s, 4) || !aligned(V0, 4) || !aligned(lam_min, 4) ||
+      !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (!(std::isfinite(hi) && hi > 0.0) || k < 1 || k > 32 || steps < 1 || steps > 10000) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < power_workspace_bytes(N, B, DASH_FP32)) return DASH_ERR_WORKSPACE;
+  Carver cv{(char*)ws, ws_bytes};
+  PowerPlan p;
+  p.N = N;
+  p.B = B;
+  p.k = k;
+  p.steps = steps;
+  p.prec = DASH_FP32;
+  p.A = A;
+  p.V0 = V0;
+  p.s = lam_min;
+  const int RB = B / 64;
+  for (int q = 0; q < 2; ++q) p.W[q] = (float*)cv.take((size_t)N * B * 32 * sizeof(float));
+  for (int q = 0; q < 2; ++q) p.part[q] = (float*)cv.take((size_t)N * RB * 3 * 32 * sizeof(float));
+  p.V0p = (float*)cv.take((size_t)B * 32 * sizeof(float));
+  p.coef = (float*)cv.take((size_t)N * COEF_STRIDE * sizeof(float));
+  p.Ah = nullptr;
+  p.shift_s = s;
+  p.shift_mul = (float)hi;
+  TRY(launch_power_iteration(p, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_residual_probe(const float* A, const float* X, int64_t N, int32_t B, int32_t k, const float* V0,
+                                float* r, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !X || !V0 || !r || !aligned(A, 16) || !aligned(X, 16) || !aligned(V0, 4) || !aligned(r, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (k < 1 || k > 32) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < power_workspace_bytes(N, B, DASH_FP32)) return DASH_ERR_WORKSPACE;
+  Carver cv{(char*)ws, ws_bytes};
+  ProbePlan p;
+  p.N = N;
+  p.B = B;
+  p.k = k;
+  p.A = A;
+  p.X = X;
+  p.V0 = V0;
+  p.r = r;
+  const int RB = B / 64;
+  for (int q = 0; q < 2; ++q) p.W[q] = (float*)cv.take((size_t)N * B * 32 * sizeof(float));
+  for (int q = 0; q < 2; ++q) p.part[q] = (float*)cv.take((size_t)N * RB * 3 * 32 * sizeof(float));
+  p.V0p = (float*)cv.take((size_t)B * 32 * sizeof(float));
+  TRY(launch_residual_probe(p, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_root_routed(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
+                                     double floor, double hi, int32_t k, int32_t est_steps, const float* V0,
+                                     float tol, int32_t cn_iters, dash_prec prec, float* X, float* lam_min,
+                                     float* resid, int32_t* route, int32_t* status, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!A || !s || !X || !V0 || X == A || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !aligned(V0, 4) ||
+      !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if ((lam_min && !aligned(lam_min, 4)) || (resid && !aligned(resid, 4)) || (route && !aligned(route, 4)) ||
+      (status && !aligned(status, 4)))
+    return DASH_ERR_INVALID_ARG;
+  if (degree < 1 || degree > CHEB_MAX_DEGREE || !(std::isfinite(floor) && floor >= 0.0) ||
+      !(std::isfinite(hi) && hi > 0.0) || k < 1 || k > 32 || est_steps < 0 || est_steps > 10000 ||
+      !(tol > 0.f && tol < INFINITY) || cn_iters < 2 || cn_iters > ROUTED_MAX_CN_ITERS)
+    return DASH_ERR_INVALID_ARG;
+  if (est_steps == 0 && !(floor > 0.0)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_routed(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* lam = (float*)cv.take((size_t)N * sizeof(float));
+  float* r = (float*)cv.take((size_t)N * sizeof(float));
+  int32_t* rt = (int32_t*)cv.take(flag_bytes(N));
+  if (lam_min) lam = lam_min;
+  if (route) rt = route;
+  int32_t* freeze = (int32_t*)cv.take(flag_bytes(N));
+  int32_t* cn_status = (int32_t*)cv.take(flag_bytes(N));
+  float* monitor = (float*)cv.take((size_t)N * ROUTED_MAX_CN_ITERS * sizeof(float));
+  void* region = cv.p;
+  const size_t region_bytes = cv.left;
+  dash_status rc;
+  // 1. the smallest eigenvalue of every block, estimated from above by the shifted power iteration
+  if (est_steps > 0) {
+    rc = dash_spectrum_min(A, s, N, B, hi, k, est_steps, V0, lam, region, region_bytes, stream);
+    if (rc != DASH_OK) return rc;
+  }
+  // 2. Chebyshev on [max(floor, lam/2)/s, hi] per block
+  ChebInterval iv;
+  iv.floor = floor;
+  iv.lam = est_steps > 0 ? lam : nullptr;
+  iv.theta = 0.5f;
+  iv.hi = hi;
+  rc = cheb_impl(A, s, N, B, degree, iv, prec, X, nullptr, status, region, region_bytes, stream);
+  if (rc != DASH_OK) return rc;
+  // 3. its residual per block, by the probe; 4. blocks above tol (or NaN) go to coupled Newton
+  rc = dash_residual_probe(A, X, N, B, k, V0, r, region, region_bytes, stream);
+  if (rc != DASH_OK) return rc;
+  TRY(launch_route(r, tol, N, rt, freeze, st));
+  // 5. coupled Newton p = 4 (fp32 cores) on the routed blocks only, each stopping once its residual
+  // ||M_k - I|| / sqrt(B) is <= tol / 2; the other blocks' X is left as the Chebyshev solve wrote it
+  Stop stop;
+  stop.tol = 0.5f * tol;
+  stop.freeze_ext = freeze;
+  rc = cn_impl(A, s, N, B, 4, cn_iters, DASH_FP32, X, monitor, cn_status, region, region_bytes, stream, stop);
+  if (rc != DASH_OK) return rc;
+  if (status) TRY(launch_select_i32(cn_status, rt, status, N, st));
+  if (lam_min && est_steps == 0) TRY(launch_fill_f32(lam_min, N, __builtin_nanf(""), st));
+  // 6. the final residual of every block, by the probe
+  if (resid) {
+    rc = dash_residual_probe(A, X, N, B, k, V0, resid, region, region_bytes, stream);
+    if (rc != DASH_OK) return rc;
+  }
   return DASH_OK;
 }
 

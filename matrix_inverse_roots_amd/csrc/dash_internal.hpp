@@ -56,14 +56,17 @@ struct Epilogue {
 
 // One batched product over N blocks: D_b = epi(X_b Y_b).  X/Y element type is `in_prec`,
 // D/D2 element type is `out_prec`; C/E are fp32.  Stride between blocks: B*B elements.
-// map_x / map_y: the operand enters the product as a Z + map_g I, a = map_a * coef[map_ia], formed
-// while it is staged.  Binary16 operands (map_ia unused): map_a must be a power of two (each element
+// map_x / map_y: the operand enters the product as a Z + g I, a = map_a * coef[map_ia] and
+// g = map_g * coef[map_ig] (the fp32 kernel; binary16 kernels take map_g alone), formed while it is
+// staged.  Binary16 operands (map_ia unused): map_a must be a power of two (each element
 // is then the exact value rounded once to binary16).  fp32 operands: only map_y, in the Clenshaw
 // launches (fold_c), one fma per element.
 // freeze (optional, [N]; fp32 full NN products and binary16 triangle-only NN products): a block b
 // with freeze[b] != 0 has stopped
 // iterating.  Its product is not computed: pass = 0 writes nothing, pass = 1 / 2 writes the
 // epilogue applied to X_b / Y_b in place of X_b Y_b (the iterate goes through unchanged).
+// freeze[b] == 2 (fp32 kernel): the block is excluded from the call and nothing is written for it
+// in any pass (a block another solver handles).
 struct Product {
   const void* X = nullptr;
   const void* Y = nullptr;
@@ -73,7 +76,7 @@ struct Product {
   void* D2 = nullptr;
   bool map_x = false, map_y = false;
   float map_a = 0.f, map_g = 0.f;
-  int8_t map_ia = CO_NONE;
+  int8_t map_ia = CO_NONE, map_ig = CO_NONE;
   const int32_t* freeze = nullptr;
   int8_t pass = 0;
 };
@@ -134,6 +137,37 @@ hipError_t launch_accept(const float* mon, int mon_stride, int q, int32_t* freez
 hipError_t launch_freeze_update(const float* monitor, int mon_stride, int col, int B, float tol, int32_t* freeze,
                                 int32_t* steps, int steps_stride, int step, int64_t N, hipStream_t stream);
 
+// Chebyshev/Clenshaw plan, computed on the device per block: the interval [lo_b, hi] of x = A_b/s_b
+// (lo_b = lo_rel when lo_rel > 0, else max(floor, theta lam[b]) / s_b), the degree-d interpolation
+// coefficients of x^{-1/4} on it (fp64), and for every product launch q = 0 .. P-1 (P = max(1, d-1),
+// in launch order) a row of epilogue coefficients tab[(q N + b) COEF_STRIDE + CS_*], each already
+// multiplied by the s-dependent factor of the coefficient table.  A block whose interval is not
+// 0 < lo_b < hi (or whose coefficients are not finite) gets NaN rows and status bit 0.
+enum ChebSlot : int { CS_ALPHA = 0, CS_BETA = 1, CS_GAMMA = 2, CS_DELTA = 3, CS_COVERA = 4, CS_MAPA = 5, CS_MAPG = 6 };
+constexpr int CHEB_MAX_DEGREE = 64;
+struct ChebPlan {
+  int64_t N = 0;
+  int d = 0;
+  bool split_first = false;  // first product in the split kernel's (alpha a1/s)(A + c I) A form
+  const float* s = nullptr;
+  const float* coef = nullptr;  // launch_coef's table
+  double lo_rel = 0.0;
+  double floor = 0.0;
+  const float* lam = nullptr;
+  float theta = 1.f;
+  double hi = 1.0;
+  float* tab = nullptr;      // [P, N, COEF_STRIDE]
+  float* lo_out = nullptr;   // optional [N]
+  int32_t* status = nullptr; // optional [N]
+};
+hipError_t launch_cheb_plan(const ChebPlan& p, hipStream_t stream);
+
+// Routing of a two-solver call: route[b] = 1 (second solver) when r[b] > tol or r[b] is NaN, else
+// 0; freeze[b] = route[b] ? 0 : 2 (blocks the second solver must leave alone).
+hipError_t launch_route(const float* r, float tol, int64_t N, int32_t* route, int32_t* freeze, hipStream_t stream);
+// dst[b] = src[b] where route[b] != 0 (per-block int32 select).
+hipError_t launch_select_i32(const int32_t* src, const int32_t* route, int32_t* dst, int64_t N, hipStream_t stream);
+
 // Scaling kernels.
 hipError_t launch_frobenius(const float* A, int64_t N, int B, float* s, hipStream_t stream);
 struct PowerPlan {
@@ -149,8 +183,28 @@ struct PowerPlan {
   float* V0p;        // [B, 32] normalised start vectors, zero columns from k on
   float* coef;       // [N, COEF_STRIDE] (prescale for binary16)
   _Float16* Ah;      // [N, B, B] binary16 operand (prec == DASH_FP16)
+  // shifted iteration (fp32 only): when shift_s is set, each step forms W = sigma_b V - A V with
+  // sigma_b = shift_mul * shift_s[b], and the result is s[b] = sigma_b - max_j mu_j (the smallest
+  // eigenvalue estimate of A_b from the largest Rayleigh quotient of sigma_b I - A_b)
+  const float* shift_s = nullptr;
+  float shift_mul = 0.f;
 };
 hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
+// Stochastic residual: r[b] = sqrt(mean_{j<k} ||(X_b^4 A_b - I) v_j||^2) over the k normalised
+// start vectors v_j (the columns of V0[B,k]), by five fp32 block-times-vectors passes (A, then X four
+// times).  Workspace pieces as for the power iteration (W, part, V0p).
+struct ProbePlan {
+  int64_t N;
+  int B, k;
+  const float* A;
+  const float* X;
+  const float* V0;
+  float* r;
+  float* W[2];
+  float* part[2];
+  float* V0p;
+};
+hipError_t launch_residual_probe(const ProbePlan& plan, hipStream_t stream);
 size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
 
 // Eigendecomposition-based inverse fourth root (two-sided block Jacobi).  launch_jacobi runs up

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
 
   if constexpr (FRZ) {  // a block that stopped iterating: pass an operand through, or write nothing
     if (P.freeze && P.freeze[tc.b]) {
-      if (P.pass == 0) return;
+      if (P.pass == 0 || P.freeze[tc.b] == 2) return;
       const float* Z = P.pass == 1 ? X : Y;
       f32x16 pz[MT][MT];
 #pragma unroll
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
   };
   // MAPY (Clenshaw's first product, a launch of its own): Y = A is read as b_{d-1} = a A + g I
   const float ya = MAPY ? P.map_a * coef_of(a.epi, P.map_ia, tc.b) : 0.f;
+  const float yg = MAPY ? P.map_g * coef_of(a.epi, P.map_ig, tc.b) : 0.f;
   auto sstore = [&](const f32x4 (&ra)[NL], const f32x4 (&rb)[NL], int buf, int k0) {
 #pragma unroll
     for (int r = 0; r < NL; ++r) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs a) {
         if constexpr (MAPY) {
           const int d = k0 + krow - (j0 + 4 * c4);  // Y[k][j] is on the diagonal when j == k
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], ya, q == d ? P.map_g : 0.f);
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], ya, q == d ? yg : 0.f);
         }
         *(f32x4*)&Bs[buf][krow * LDB + 4 * c4] = v;
       } else {

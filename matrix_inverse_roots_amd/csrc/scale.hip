@@ -128,6 +128,9 @@ struct PowerStepArgs {
   float* W;             // [N, B, KV]
   float* part_out;      // [N, RB, 3, KV]
   int B, k, RB;         // RB = row blocks per block
+  // shifted step: W = sigma_b V - A V with sigma_b = shift_mul * shift_s[b] (shift_s null: W = A V)
+  const float* shift_s;
+  float shift_mul;
 };
 
 // inverse norm of column j of the current V for block b (the start vectors come normalised)
@@ -150,13 +153,13 @@ using IC = std::integral_constant<int, V>;
 // staged the wave's own rows.
 template <int WAVES>
 __device__ __forceinline__ void power_epilogue(const float (&vm)[16], float* W, float* part_out, const f32x16& acc,
-                                               int r0, int wave, int lane, float (*red)[3][KV]) {
+                                               int r0, int wave, int lane, float (*red)[3][KV], float sigma) {
   const int li = lane & 31, h = lane >> 5, j = li;
   float ww = 0.f, vw = 0.f, vv = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int i = r0 + wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    const float w = acc[r];
+    const float w = sigma != 0.f ? fmaf(sigma, vm[r], -acc[r]) : acc[r];
     W[(int64_t)i * KV + j] = w;
     const float v = vm[r];
     ww += w * w;
@@ -307,8 +310,9 @@ __global__ __launch_bounds__(64 * WAVES, 3) void power_step_f32(PowerStepArgs<fl
     tail_step(IC<2>{}, kt + 2, true);
     tail_step(IC<3>{}, kt + 3, false);
   }
+  const float sigma = a.shift_s ? a.shift_mul * a.shift_s[b] : 0.f;
   power_epilogue<WAVES>(vm, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave,
-                        lane, red);
+                        lane, red, sigma);
 }
 
 // Binary16 operands: A_b prescaled in binary16, V rounded to binary16 as it is staged (transposed,
@@ -430,12 +434,15 @@ __global__ __launch_bounds__(64 * WAVES) void power_step_f16(PowerStepArgs<_Floa
     tail_step(IC<2>{}, kt + 2, true);
     tail_step(IC<3>{}, kt + 3, false);
   }
+  const float sigma = a.shift_s ? a.shift_mul * a.shift_s[b] : 0.f;
   power_epilogue<WAVES>(vm, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave,
-                        lane, red);
+                        lane, red, sigma);
 }
 
-// s_b = scale_b * max_{j<k} (v.w / v.v) from the last step's partials
-__global__ void power_finish_kernel(const float* part, int64_t N, int RB, int k, const float* coef, float* s) {
+// s_b = scale_b * max_{j<k} (v.w / v.v) from the last step's partials; for a shifted iteration
+// (shift_s set) s_b = sigma_b - max_j (v.w / v.v)
+__global__ void power_finish_kernel(const float* part, int64_t N, int RB, int k, const float* coef, float* s,
+                                    const float* shift_s, float shift_mul) {
   const int64_t b = blockIdx.x;
   const int j = threadIdx.x;
   float mu = -INFINITY;
@@ -457,7 +464,30 @@ __global__ void power_finish_kernel(const float* part, int64_t N, int RB, int k,
   }
   if (j == 0) {
     const float scale = coef ? coef[b * COEF_STRIDE + CO_P2INV] : 1.f;
-    s[b] = any_nan ? __builtin_nanf("") : mu * scale;
+    const float out = shift_s ? shift_mul * shift_s[b] - mu : mu * scale;
+    s[b] = any_nan ? __builtin_nanf("") : out;
+  }
+}
+
+// r_b = sqrt(mean_{j<k} sum_i (W[i][j] - V0p[i][j])^2): 256 threads, column j = tid % 32, rows
+// tid / 32 + 8 t, reduced in double.
+__global__ __launch_bounds__(256) void probe_finish_kernel(const float* W, const float* V0p, int B, int k, float* r) {
+  const int64_t b = blockIdx.x;
+  const int j = threadIdx.x % KV, part = threadIdx.x / KV;
+  const float* w = W + b * (int64_t)B * KV;
+  double acc = 0.0;
+  if (j < k)
+    for (int i = part; i < B; i += 256 / KV) {
+      const double e = (double)w[(int64_t)i * KV + j] - (double)V0p[(int64_t)i * KV + j];
+      acc += e * e;
+    }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int q = 0; q < 256; ++q) t += red[q];
+    r[b] = (float)sqrt(t / k);
   }
 }
 
@@ -540,6 +570,8 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
       a.B = p.B;
       a.k = p.k;
       a.RB = RB;
+      a.shift_s = p.shift_s;
+      a.shift_mul = p.shift_mul;
     };
     if (p.prec == DASH_FP32) {
       PowerStepArgs<float> a;
@@ -561,7 +593,42 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(power_finish_kernel, dim3((unsigned)p.N), dim3(64), 0, stream, p.part[(p.steps - 1) & 1], p.N,
-                     RB, p.k, coef, p.s);
+                     RB, p.k, coef, p.s, p.shift_s, p.shift_mul);
+  return hipGetLastError();
+}
+
+// Residual probe: W1 = A V, W_{t+1} = X W_t (t = 1 .. 4), unnormalised (no partials are read), then
+// r_b^2 = mean_{j<k} ||W5_j - v_j||^2 with v_j the normalised start vectors.
+hipError_t launch_residual_probe(const ProbePlan& p, hipStream_t stream) {
+  const bool wide = (p.B % 128 == 0);
+  const int RT = wide ? 128 : 64;
+  const int RB = p.B / RT;
+  const int64_t grid = p.N * RB;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipError_t err;
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.B, p.k, p.V0p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int depth = ring_depth(p.B / 32, 4);
+  for (int t = 0; t < 5; ++t) {
+    PowerStepArgs<float> a;
+    a.A = t == 0 ? p.A : p.X;
+    a.Vsrc = t == 0 ? p.V0p : p.W[(t - 1) & 1];
+    a.vstride = t == 0 ? 0 : (int64_t)p.B * KV;
+    a.part_in = nullptr;  // every pass multiplies the previous result as it is
+    a.W = p.W[t & 1];
+    a.part_out = p.part[t & 1];
+    a.B = p.B;
+    a.k = p.k;
+    a.RB = RB;
+    a.shift_s = nullptr;
+    a.shift_mul = 0.f;
+    if (wide)
+      launch_step_depth<float, 4>(depth, dim3((unsigned)grid), stream, a);
+    else
+      launch_step_depth<float, 2>(depth, dim3((unsigned)grid), stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(probe_finish_kernel, dim3((unsigned)p.N), dim3(256), 0, stream, p.W[0], p.V0p, p.B, p.k, p.r);
   return hipGetLastError();
 }
 

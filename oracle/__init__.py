@@ -66,6 +66,9 @@ def _load():
             "orc_cheb_inverse_root": (None, [i, _dp, d, i, d, d, _dp]),
             "orc_update_stats": (None, [i, _dp, d, _dp, _dp]),
             "orc_apply": (None, [i, _dp, _dp, _dp, _dp]),
+            "orc_mpi_shifted": (d, [i, _dp, d, i, i, _dp, _dp]),
+            "orc_residual_probe": (d, [i, _dp, _dp, i, _dp]),
+            "orc_routed_inverse_root": (i, [i, _dp, d, i, d, d, i, i, _dp, d, i, _dp, _dp, _dp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -348,19 +351,92 @@ def clenshaw(As, c, lo: float, hi: float) -> np.ndarray:
     return P
 
 
-def cheb_inverse_root(A, s, degree: int, lo: float, hi: float, threads: int | None = None) -> np.ndarray:
-    """A^{-1/4} by a degree-d Chebyshev interpolant on [lo, hi] of A/s, unscaled by s^{-1/4} (c7)."""
+def cheb_inverse_root(A, s, degree: int, lo, hi: float, threads: int | None = None) -> np.ndarray:
+    """A^{-1/4} by a degree-d Chebyshev interpolant on [lo, hi] of A/s, unscaled by s^{-1/4} (c7).
+    lo: one lower end for every block, or one per block."""
     A, single = _as_stack(A)
     N, n, _ = A.shape
     s = _per_block(s, N)
+    lo = _per_block(lo, N)
     X = np.empty_like(A)
     lib = _load()
 
     def one(b):
-        lib.orc_cheb_inverse_root(n, _p(A[b]), float(s[b]), int(degree), float(lo), float(hi), _p(X[b]))
+        lib.orc_cheb_inverse_root(n, _p(A[b]), float(s[b]), int(degree), float(lo[b]), float(hi), _p(X[b]))
 
     _over_blocks(one, N, threads)
     return X[0] if single else X
+
+
+def cheb_interval_lo(s, floor: float, lam=None, theta: float = 1.0) -> np.ndarray:
+    """Lower end of each block's Chebyshev interval in units of A/s: max(floor, theta lam) / s (the
+    per-block reading of c7's interval)."""
+    s = np.asarray(s, dtype=np.float64).reshape(-1)
+    bottom = np.full(s.shape, float(floor))
+    if lam is not None:
+        bottom = np.fmax(bottom, theta * np.asarray(lam, dtype=np.float64).reshape(-1))  # NaN: the floor
+    return bottom / s
+
+
+def mpi_shifted(A, sigma, V0, steps: int, threads: int | None = None):
+    """Smallest-eigenvalue estimate per block from the power iteration on sigma I - A: returns
+    (lam[N], mu[N,k]) with lam = sigma - max_j mu_j."""
+    A, single = _as_stack(A)
+    V0 = _f64(V0)
+    N, n, _ = A.shape
+    k = V0.shape[1]
+    sig = _per_block(sigma, N)
+    mu = np.empty((N, k))
+    lib = _load()
+
+    def one(b):
+        return lib.orc_mpi_shifted(n, _p(A[b]), float(sig[b]), k, int(steps), _p(V0), _p(mu[b]))
+
+    lam = np.array(_over_blocks(one, N, threads))
+    return (lam[0], mu[0]) if single else (lam, mu)
+
+
+def residual_probe(A, X, V0, threads: int | None = None) -> np.ndarray:
+    """r[N]: sqrt(mean_j ||(X^4 A - I) v_j||^2) over the normalised columns v_j of V0."""
+    A, single = _as_stack(A)
+    X, _ = _as_stack(X)
+    V0 = _f64(V0)
+    N, n, _ = A.shape
+    k = V0.shape[1]
+    lib = _load()
+
+    def one(b):
+        return lib.orc_residual_probe(n, _p(A[b]), _p(X[b]), k, _p(V0))
+
+    r = np.array(_over_blocks(one, N, threads))
+    return r[0] if single else r
+
+
+def routed_inverse_root(A, s, degree: int, floor: float, hi: float, V0, est_steps: int, tol: float, cn_iters: int,
+                        threads: int | None = None):
+    """Per-block solver choice: Chebyshev on [max(floor, lam/2)/s, hi] with lam the shifted power
+    iteration's estimate, kept when the probe's residual is <= tol, else coupled Newton (stopping at
+    tol/2).  Returns (X, route[N], lam[N], r[N]) with r the probe's residual of the Chebyshev result."""
+    A, single = _as_stack(A)
+    V0 = _f64(V0)
+    N, n, _ = A.shape
+    k = V0.shape[1]
+    s = _per_block(s, N)
+    X = np.empty_like(A)
+    lam = np.empty(N)
+    r = np.empty(N)
+    lib = _load()
+
+    def one(b):
+        lp = lam[b:].ctypes.data_as(_dp)
+        rp = r[b:].ctypes.data_as(_dp)
+        return lib.orc_routed_inverse_root(n, _p(A[b]), float(s[b]), int(degree), float(floor), float(hi), k,
+                                           int(est_steps), _p(V0), float(tol), int(cn_iters), _p(X[b]), lp, rp)
+
+    route = np.array(_over_blocks(one, N, threads), dtype=np.int32)
+    if single:
+        return X[0], route[0], lam[0], r[0]
+    return X, route, lam, r
 
 
 # ---------------------------------------------------------------------------------------------

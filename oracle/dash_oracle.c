@@ -611,6 +611,90 @@ void orc_cheb_inverse_root(int n, const double* A, double s, int d, double lo, d
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * Per-block interval bottom and solver choice ([PT] Significância e Alegações, "Direções Futuras":
+ * the solver and its work chosen per block from the block's conditioning; no method is given).
+ * ---------------------------------------------------------------------------------------------- */
+
+/* Estimate of lambda_min(A) from above: the Multi-Power-Iteration of c3 run on C = sigma I - A
+ * (same normalisation, Rayleigh quotients from the last product, max over columns), returning
+ * sigma - max_j mu_j(C).  mu receives the k quotients of C. */
+double orc_mpi_shifted(int n, const double* A, double sigma, int k, int T, const double* V0, double* mu) {
+  const size_t nn = (size_t)n * n;
+  double* C = (double*)malloc(sizeof(double) * nn);
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) C[IDX(i, j, n)] = (i == j ? sigma : 0.0) - A[IDX(i, j, n)];
+  const double top = orc_mpi(n, C, k, T, V0, mu);
+  free(C);
+  return sigma - top;
+}
+
+/* Residual of X as an inverse fourth root of A seen through k probe vectors: with v_j the
+ * normalised columns of V0 (B x k, row-major) and E = X^4 A - I,
+ *     r^2 = (1/k) sum_j ||E v_j||^2,
+ * E v_j formed as X (X (X (X (A v_j)))) - v_j, one matrix-vector product at a time. */
+double orc_residual_probe(int n, const double* A, const double* X, int k, const double* V0) {
+  double* v = (double*)malloc(sizeof(double) * n);
+  double* y = (double*)malloc(sizeof(double) * n);
+  double* z = (double*)malloc(sizeof(double) * n);
+  double total = 0.0;
+  for (int j = 0; j < k; ++j) {
+    double nrm = 0.0;
+    for (int i = 0; i < n; ++i) nrm += V0[IDX(i, j, k)] * V0[IDX(i, j, k)];
+    nrm = sqrt(nrm);
+    for (int i = 0; i < n; ++i) v[i] = V0[IDX(i, j, k)] / nrm;
+    for (int i = 0; i < n; ++i) {  /* y = A v */
+      double acc = 0.0;
+      for (int l = 0; l < n; ++l) acc += A[IDX(i, l, n)] * v[l];
+      y[i] = acc;
+    }
+    for (int rep = 0; rep < 4; ++rep) {  /* y = X y, four times */
+      for (int i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int l = 0; l < n; ++l) acc += X[IDX(i, l, n)] * y[l];
+        z[i] = acc;
+      }
+      memcpy(y, z, sizeof(double) * n);
+    }
+    for (int i = 0; i < n; ++i) total += (y[i] - v[i]) * (y[i] - v[i]);
+  }
+  free(v);
+  free(y);
+  free(z);
+  return sqrt(total / k);
+}
+
+/* One block of the routed inverse root.  Reading of the pages' per-block solver choice:
+ *   lam = orc_mpi_shifted(A, hi s) when est_steps > 0 (else no estimate),
+ *   lo  = max(floor, lam / 2) / s,
+ *   X   = degree-d Chebyshev inverse root of A on [lo, hi] in units of A/s (c7);
+ *   r   = orc_residual_probe(A, X, V0);
+ *   when r > tol (or r is NaN): X = coupled Newton p = 4 (c6) with the stopping rule of
+ *   orc_cn_until at tol / 2 and at most cn_iters steps, and route = 1; else route = 0.
+ * lam_out, r_out receive lam (NaN without an estimate) and r.  Returns route. */
+int orc_routed_inverse_root(int n, const double* A, double s, int d, double floor, double hi, int k,
+                            int est_steps, const double* V0, double tol, int cn_iters, double* X, double* lam_out,
+                            double* r_out) {
+  double lam = NAN;
+  double lo_abs = floor;
+  if (est_steps > 0) {
+    double* mu = (double*)malloc(sizeof(double) * k);
+    lam = orc_mpi_shifted(n, A, hi * s, k, est_steps, V0, mu);
+    free(mu);
+    if (0.5 * lam > lo_abs) lo_abs = 0.5 * lam;
+  }
+  orc_cheb_inverse_root(n, A, s, d, lo_abs / s, hi, X);
+  const double r = orc_residual_probe(n, A, X, k, V0);
+  int route = 0;
+  if (!(r <= tol)) {
+    orc_cn_until(n, A, s, cn_iters, 0, 0.5 * tol, X, NULL);
+    route = 1;
+  }
+  if (lam_out) *lam_out = lam;
+  if (r_out) *r_out = r;
+  return route;
+}
+
+/* ------------------------------------------------------------------------------------------------
  * c8: Shampoo statistics update ([TG] body: two matrices L and R are kept from products of the
  * gradient, and their -1/4 power is taken).  Reading: exponential moving average
  *     L <- beta L + (1 - beta) G G^T,   R <- beta R + (1 - beta) G^T G,   in place.

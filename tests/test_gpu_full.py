@@ -47,6 +47,19 @@ def stack():
     torch.cuda.empty_cache()
 
 
+def tile_of(grads, t):
+    """Tile t of the stacking order (weight-major, then tile row, then tile column), read from the
+    weights on the host."""
+    for w in grads:
+        r, c = w.shape
+        n = (r // B) * (c // B)
+        if t < n:
+            tr, tc = divmod(t, c // B)
+            return host(w[tr * B:(tr + 1) * B, tc * B:(tc + 1) * B])
+        t -= n
+    raise IndexError(t)
+
+
 def scale(A, V0, prec):
     s = torch.empty(N, device=DEV)
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, prec, 32, device=DEV)
@@ -202,6 +215,68 @@ def test_full_step_chebyshev(stack):
     dash.dash_unstack(U, B, outs)
     assert torch.equal(outs[0][:B, :B], U[0]) and torch.equal(outs[-1][B:, -B:], U[NG - 1])
     del A, X, U, G, grads, outs
+    torch.cuda.empty_cache()
+
+
+def test_full_step_bench_sequence(stack):
+    """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics (split
+    products) -> power scale -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
+    (floor_t = 1e-6 * 0.95^t, the damping after t updates; split products) -> apply (split products).
+    Sampled L and R blocks of one tile are recomputed by the oracle from the same starting blocks and
+    gradient tiles through both steps (its own statistics, scale, interval and solve); every sampled
+    block's spectrum (numpy eigvalsh; the oracle's Jacobi needs minutes at B = 1024 and is pinned to
+    it) lies in its interval."""
+    A0, V0 = stack
+    A = A0.clone()
+    split = dash.DASH_FP32_SPLIT
+    t_idx = 700
+    idx = [t_idx, NG + t_idx]
+    L_ref, R_ref = host(A[t_idx]), host(A[NG + t_idx])
+    V0h = host(V0)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(di.SEED_GRADS + 1)
+    flat = torch.empty(sum(r * c for r, c in SHAPES), device=DEV)
+    grads, o = [], 0
+    for r, c in SHAPES:
+        grads.append(flat[o:o + r * c].view(r, c))
+        o += r * c
+    G = torch.empty((NG, B, B), device=DEV)
+    U = torch.empty((NG, B, B), device=DEV)
+    X = torch.empty_like(A)
+    s = torch.empty(N, device=DEV)
+    lo = torch.empty(N, device=DEV)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws_s = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 32, device=DEV)
+    ws_c = dash.workspace(dash.DASH_OP_CHEB, N, B, split, device=DEV)
+    ws_a = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
+    floor = 1e-6
+    for step in range(2):
+        flat.normal_(0.0, 1e-3, generator=gen)
+        floor *= 0.95
+        dash.dash_stack(grads, B, G)
+        dash.dash_update_stats_prec(G, NG, B, 0.95, split, A)
+        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, V0, s, ws_s)
+        dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, split, X, lo_out=lo,
+                                          status=status, ws=ws_c)
+        dash.dash_apply_prec(X[:NG], X[NG:], G, NG, B, split, U, ws_a)
+        # the oracle's copy of the same step for tile t_idx, from the gradient itself
+        G_t = tile_of(grads, t_idx)
+        L_ref, R_ref = oracle.update_stats(G_t, 0.95, L_ref, R_ref)
+    assert int(status.abs().sum()) == 0
+    A_ref = np.stack([L_ref, R_ref])
+    assert np.max(rel_err(host(A[idx]), A_ref)) < 1e-5
+    s_ref, _ = oracle.mpi(A_ref, V0h, 10)
+    assert np.max(np.abs(host(s[idx]) - s_ref) / s_ref) < 1e-5
+    lo_ref = oracle.cheb_interval_lo(s_ref, floor)
+    assert np.max(np.abs(host(lo[idx]) - lo_ref) / lo_ref) < 1e-5
+    for b in range(2):
+        w = np.linalg.eigvalsh(A_ref[b])
+        assert lo_ref[b] * s_ref[b] <= w[0] and w[-1] <= 1.25 * s_ref[b], (b, w[0], w[-1], s_ref[b])
+    X_ref = oracle.cheb_inverse_root(A_ref, s_ref, 24, lo_ref, 1.25)
+    assert np.max(rel_err(host(X[idx]), X_ref)) < ITERATE_TOL
+    U_ref = oracle.apply(X_ref[0], G_t, X_ref[1])
+    assert np.max(rel_err(host(U[t_idx]), U_ref)) < ITERATE_TOL
+    del A, X, U, G, flat, grads, ws_s, ws_c, ws_a
     torch.cuda.empty_cache()
 
 

@@ -249,6 +249,158 @@ def test_mpi_half_precision():
     assert oracle.mpi(np.zeros((8, 8)), np.ones((8, 2)), 3, half=True)[0] == 0.0
 
 
+def _mpi_half_diagonal(a, V0, T, prescale="ceil", round_w=False):
+    """The binary16 power iteration on diag(a), written as its scalar recurrence with numpy's float16
+    (round to nearest even): e = ceil(log2 max a), a_h = fp16(a 2^-e), v = fp16(v0 / |v0|), and per
+    step w = a_h v (exact), mu = 2^e (v.w)/(v.v), v <- fp16(w / |w|).  The planted variants prescale
+    by 2^-floor(log2 max a), or round w before it is normalised."""
+    f16 = lambda x: np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+    m = float(np.max(a))
+    e = math.ceil(math.log2(m)) if prescale == "ceil" else math.floor(math.log2(m))
+    ah = f16(a * 2.0 ** -e)
+    V = f16(V0 / np.linalg.norm(V0, axis=0))
+    for t in range(1, T + 1):
+        W = ah[:, None] * V
+        mu = 2.0 ** e * np.sum(V * W, axis=0) / np.sum(V * V, axis=0)
+        if t < T:
+            if round_w:
+                Wr = f16(W)
+                V = Wr / np.linalg.norm(Wr, axis=0)
+            else:
+                V = f16(W / np.linalg.norm(W, axis=0))
+    return mu.max(), mu
+
+
+def test_mpi_half_diagonal_matches_scalar_recurrence():
+    """Pins where the binary16 power iteration rounds: on a diagonal block every step is the scalar
+    recurrence above.  The block's largest entry 3 has ceil(log2 3) = 2 != floor(log2 3) = 1, and half
+    of its entries lie in [2^-13, 2^-12), which the ceil prescale takes into binary16's subnormal range
+    and the floor prescale does not, so a floor prescale changes the result; so does rounding w before
+    its normalisation."""
+    g = di.rng(61)
+    n, k = 64, 4
+    a = np.concatenate([[3.0], g.uniform(0.1, 2.9, n // 4 - 1), g.uniform(2.0 ** -13, 2.0 ** -12, 3 * n // 4)])
+    a = a[g.permutation(n)]
+    V0 = di.start_vectors(n, k, seed=62).astype(np.float64)
+    for T in (1, 2, 3, 10):
+        s, mu = oracle.mpi(np.diag(a), V0, T, half=True)
+        s_ref, mu_ref = _mpi_half_diagonal(a, V0, T)
+        assert np.allclose(mu, mu_ref, rtol=1e-13, atol=0), T
+        assert abs(s - s_ref) <= 1e-13 * s_ref
+    # the planted variants disagree with the oracle by far more than the pin's tolerance
+    s, mu = oracle.mpi(np.diag(a), V0, 1, half=True)
+    _, mu_floor = _mpi_half_diagonal(a, V0, 1, prescale="floor")
+    assert np.max(np.abs(mu_floor - mu) / mu) > 1e-11
+    for T in (2, 3):
+        s, mu = oracle.mpi(np.diag(a), V0, T, half=True)
+        _, mu_w = _mpi_half_diagonal(a, V0, T, round_w=True)
+        assert np.max(np.abs(mu_w - mu) / mu) > 1e-9, T
+
+
+# ----------------------------------------------------------------------------------------------
+# per-block interval bottom, residual probe and routing
+# ----------------------------------------------------------------------------------------------
+
+def test_mpi_shifted_closed_form_on_diagonal():
+    """On diag(lam) the shifted iteration's Rayleigh quotients have the closed form of the power
+    iteration on diag(c), c = sigma - lam: mu_j = sum c^(2T-1) u_j^2 / sum c^(2T-2) u_j^2, evaluated
+    here in exact rational arithmetic."""
+    from fractions import Fraction
+
+    lam = [Fraction(1, 8), Fraction(1, 2), Fraction(3, 4), Fraction(1, 1), Fraction(5, 4), Fraction(3, 2)]
+    sigma = Fraction(2)
+    U = [[1, 2, -1], [2, 0, 1], [-1, 1, 3], [3, -2, 1], [1, 1, 1], [2, -1, 2]]
+    A = np.diag([float(x) for x in lam])
+    V0 = np.array(U, dtype=np.float64)
+    for T in (1, 3, 7):
+        lam_hat, mu = oracle.mpi_shifted(A, float(sigma), V0, T)
+        exact = []
+        for j in range(3):
+            c = [sigma - x for x in lam]
+            num = sum(ci ** (2 * T - 1) * U[i][j] ** 2 for i, ci in enumerate(c))
+            den = sum(ci ** (2 * T - 2) * U[i][j] ** 2 for i, ci in enumerate(c))
+            exact.append(num / den)
+        assert np.allclose(mu, [float(x) for x in exact], rtol=1e-14, atol=0)
+        assert abs(lam_hat - float(sigma - max(exact))) < 1e-14
+
+
+def test_mpi_shifted_bounds_and_limit():
+    """The estimate lies above lambda_min, falls with every step, and reaches it when the bottom
+    eigenvalue is well separated."""
+    A, _, lam = spd(63, 48, 0.02, 1.0)
+    V0 = di.start_vectors(48, 32, seed=64)
+    prev = np.inf
+    for T in (1, 2, 4, 8, 16):
+        est, _ = oracle.mpi_shifted(A, 1.25, V0, T)
+        assert est >= lam.min() * (1 - 1e-12)
+        assert est <= prev * (1 + 1e-14)
+        prev = est
+    g = di.rng(65)
+    lam2 = np.concatenate([[0.01], g.uniform(0.5, 1.0, 47)])
+    Q = di.haar_orthogonal(g, 48)
+    A2 = (Q * lam2[None, :]) @ Q.T
+    est, _ = oracle.mpi_shifted(0.5 * (A2 + A2.T), 1.25, V0, 200)
+    assert abs(est - 0.01) < 1e-10
+
+
+def test_residual_probe_closed_form_and_expectation():
+    g = di.rng(66)
+    n, k = 40, 6
+    a = g.uniform(0.1, 1.0, n)
+    x = a ** -0.25 * (1.0 + g.uniform(-0.01, 0.01, n))
+    V0 = di.start_vectors(n, k, seed=67).astype(np.float64)
+    # diagonal blocks: E = diag(x^4 a - 1), so ||E v||^2 = sum_i e_i^2 v_i^2 for each unit probe v
+    r = oracle.residual_probe(np.diag(a), np.diag(x), V0)
+    e = x ** 4 * a - 1.0
+    v = V0 / np.sqrt(np.sum(V0 * V0, axis=0))
+    assert abs(r - math.sqrt(np.mean(np.sum((e[:, None] * v) ** 2, axis=0)))) < 1e-14
+    # the exact root (closed form) has no residual
+    A, Q, lam = spd(68, 32, 1e-3, 1.0)
+    X = (Q * lam[None, :] ** -0.25) @ Q.T
+    assert oracle.residual_probe(A, X, di.start_vectors(32, 8, seed=69)) < 1e-11
+    # many probes: the mean of ||E v||^2 over the sphere is ||E||_F^2 / n
+    Xp = X + 1e-3 * (g.standard_normal((32, 32)))
+    E = np.linalg.matrix_power(Xp, 4) @ A - np.eye(32)
+    r_exact = np.linalg.norm(E) / math.sqrt(32)
+    r_many = oracle.residual_probe(A, Xp, g.standard_normal((32, 4000)))
+    assert abs(r_many - r_exact) < 0.05 * r_exact
+
+
+def test_cheb_interval_lo_and_per_block_lower_end():
+    s = np.array([2.0, 4.0, 8.0])
+    lo = oracle.cheb_interval_lo(s, 0.1)
+    assert np.array_equal(lo, [0.05, 0.025, 0.0125])
+    lo = oracle.cheb_interval_lo(s, 0.1, lam=[1.0, 0.1, np.nan], theta=0.5)
+    assert np.allclose(lo, [0.25, 0.025, 0.0125], rtol=0, atol=0)  # a NaN estimate leaves the floor
+    # a per-block lower end gives each block the solve it would get alone
+    A, _, _ = spd(70, 24, 0.05, 1.0)
+    B2, _, _ = spd(71, 24, 0.2, 1.0)
+    X = oracle.cheb_inverse_root(np.stack([A, B2]), [1.0, 1.0], 10, [0.04, 0.15], 1.25)
+    assert np.array_equal(X[0], oracle.cheb_inverse_root(A, 1.0, 10, 0.04, 1.25))
+    assert np.array_equal(X[1], oracle.cheb_inverse_root(B2, 1.0, 10, 0.15, 1.25))
+
+
+def test_routed_inverse_root_routes_and_meets_the_gate():
+    """A well-conditioned block stays with Chebyshev on its estimated interval; a kappa = 1e4 block,
+    whose floor-based interval leaves degree 16 far from the gate, goes to coupled Newton; both meet
+    the fp32 residual gate against the closed-form root."""
+    n = 48
+    A0, Q0, l0 = spd(72, n, 0.25, 1.0)
+    A1, Q1, l1 = spd(73, n, 1e-4, 1.0)
+    A = np.stack([A0, A1])
+    s = np.array([l0.max(), l1.max()]) / 1.02
+    V0 = di.start_vectors(n, 16, seed=74).astype(np.float64)
+    X, route, lam, r = oracle.routed_inverse_root(A, s, 16, 0.9e-4, 1.25, V0, 10, 1e-3, 30)
+    assert list(route) == [0, 1]
+    assert np.all(lam >= np.array([l0.min(), l1.min()]) * (1 - 1e-12))
+    assert r[0] < 1e-5 and r[1] > 1e-3
+    for b, (Q, l) in enumerate(((Q0, l0), (Q1, l1))):
+        Xe = (Q * l[None, :] ** -0.25) @ Q.T
+        E = np.linalg.matrix_power(X[b], 4) @ A[b] - np.eye(n)
+        assert np.linalg.norm(E) / math.sqrt(n) < 1e-3
+        assert rel(X[b], Xe) < 1e-3
+
+
 # ----------------------------------------------------------------------------------------------
 # c4 / c5: Newton-Denman-Beavers
 # ----------------------------------------------------------------------------------------------
