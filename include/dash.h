@@ -250,6 +250,19 @@ dash_status dash_inverse_root_cheb_blocks(const float* A, const float* s, int64_
                                           float* X, float* lo_out, int32_t* status, void* ws, size_t ws_bytes,
                                           void* stream);
 
+/* dash_scale without a caller workspace, for callers that cannot allocate device memory: code under
+ * stream capture, serving loops and harnesses that forbid allocation.  Arguments and results as
+ * dash_scale.  The power iteration's scratch lives in a device array owned by the library,
+ * dash_noalloc_scratch_bytes() bytes (128 MiB) on every GPU the library runs on, held until the
+ * process ends; the call allocates nothing.  A request whose scratch (dash_workspace_size of
+ * DASH_OP_SCALE) exceeds it returns DASH_ERR_WORKSPACE before anything is enqueued (fp32: up to 488
+ * blocks per call at B = 1024, 1954 at B = 256; binary16, which also holds the cast of A: 56 at 1024).  The current device must be the stream's.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (on two streams, or from two threads) race and
+ * must be ordered by the caller.  The Frobenius scale needs no scratch and is passed through. */
+dash_status dash_scale_noalloc(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                               int32_t steps, const float* V0, float* s, void* stream);
+size_t dash_noalloc_scratch_bytes(void);
+
 /* Estimate of every block's smallest eigenvalue, from above ([PT] Significância e Alegações,
  * "Direções Futuras": choosing the solver per block from its conditioning needs the bottom of each
  * block's spectrum; the pages name the largest eigenvalue's power iteration only, so this is the

@@ -68,6 +68,8 @@ def library() -> ctypes.CDLL:
             "dash_residual_probe": (st, [vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_routed": (st, [vp, vp, i64, i32, i32, f64, f64, i32, i32, vp, f32, i32, st, vp, vp, vp,
                                               vp, vp, vp, sz, vp]),
+            "dash_scale_noalloc": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp]),
+            "dash_noalloc_scratch_bytes": (sz, []),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
             "dash_flops": (f64, [st, i64, i32, st, i32, i32]),
@@ -243,6 +245,19 @@ def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s
     _check("dash_scale", library().dash_scale(a.ptr(A, "A", numel=N * B * B), N, B, how, prec, k, steps,
                                               a.ptr(V0, "V0", numel=vn), a.ptr(s, "s", numel=N), a.ws(ws),
                                               _nbytes(ws), a.stream(stream)))
+
+
+def dash_scale_noalloc(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, stream=None):
+    """dash_scale with the library's own scratch: no workspace argument, nothing allocated."""
+    a = _Args("dash_scale_noalloc")
+    vn = B * k if how == DASH_SCALE_POWER else 0
+    _check("dash_scale_noalloc",
+           library().dash_scale_noalloc(a.ptr(A, "A", numel=N * B * B), N, B, how, prec, k, steps,
+                                        a.ptr(V0, "V0", numel=vn), a.ptr(s, "s", numel=N), a.stream(stream)))
+
+
+def dash_noalloc_scratch_bytes() -> int:
+    return library().dash_noalloc_scratch_bytes()
 
 
 def dash_spectrum_min(A, s, N: int, B: int, hi: float, k: int, steps: int, V0, lam_min, ws=None, stream=None):

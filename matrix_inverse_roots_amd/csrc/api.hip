@@ -700,18 +700,33 @@ dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, 
   return DASH_OK;
 }
 
-dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
-                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace dash {
+// Argument checks of dash_scale short of the workspace (shared with dash_scale_noalloc).
+dash_status scale_args_check(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                             int32_t steps, const float* V0, const float* s) {
   if (!A || !s || !aligned(A, 16) || !aligned(s, 4) || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
-  if (how == DASH_SCALE_FROBENIUS) {
-    TRY(launch_frobenius(A, N, B, s, as_stream(stream)));
-    return DASH_OK;
-  }
+  if (how == DASH_SCALE_FROBENIUS) return DASH_OK;
   if (how != DASH_SCALE_POWER) return DASH_ERR_INVALID_ARG;
   if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;  // power iteration streams fp32 or binary16 operands
   if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
   if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !V0 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
+  return DASH_OK;
+}
+}  // namespace dash
+
+extern "C" {
+
+dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream) {
+  const dash_status chk = scale_args_check(A, N, B, how, prec, k, steps, V0, s);
+  if (chk != DASH_OK) return chk;
+  if (how == DASH_SCALE_FROBENIUS) {
+    TRY(launch_frobenius(A, N, B, s, as_stream(stream)));
+    return DASH_OK;
+  }
   if (!ws || !aligned(ws, 256) || ws_bytes < power_workspace_bytes(N, B, prec)) return DASH_ERR_WORKSPACE;
   Carver cv{(char*)ws, ws_bytes};
   PowerPlan p;

@@ -255,4 +255,8 @@ hipError_t launch_tile_copy(const dash_mat* w, int n, int B, float* stack, bool 
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// dash_scale's argument checks short of the workspace (DASH_OK or the status dash_scale returns).
+dash_status scale_args_check(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
+                             int32_t steps, const float* V0, const float* s);
+
 }  // namespace dash
