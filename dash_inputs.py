@@ -87,6 +87,24 @@ def start_vectors(B: int, k: int = 32, seed: int = SEED_START) -> np.ndarray:
     return rng(seed).standard_normal((B, k)).astype(np.float32)
 
 
+def start_pool_counter(B: int, k: int, seed: int) -> np.ndarray:
+    """The (B, k) start pool drawn from a counter-based SplitMix64 stream (Steele, Lea and Flood, 2014):
+    output n of the stream started at `seed` is mix(seed + n * 0x9E3779B97F4A7C15); element e = i k + j
+    takes the top 22 bits u_q of outputs 3e + q (q = 1, 2, 3) and is (u_1 + u_2 + u_3 - 1.5 * 2^22) * 2^-22,
+    exact in fp32.  The GPU library draws the same pool when dash_scale is given no start vectors."""
+    e = np.arange(B * k, dtype=np.uint64)
+    total = np.zeros(B * k, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        for q in (1, 2, 3):
+            z = np.uint64(seed) + (np.uint64(3) * e + np.uint64(q)) * np.uint64(0x9E3779B97F4A7C15)
+            z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+            z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+            z = z ^ (z >> np.uint64(31))
+            total += z >> np.uint64(42)
+    v = (total.astype(np.float32) - np.float32(6291456.0)) * np.float32(2.0 ** -22)
+    return v.reshape(B, k)
+
+
 def gaussian(shape, seed: int, std: float = 1.0) -> np.ndarray:
     return (std * rng(seed).standard_normal(shape)).astype(np.float32)
 

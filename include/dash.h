@@ -112,15 +112,27 @@ dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, 
 
 /* Per-block scale s[N] ([PT] Definição do Problema, item 3, and Metodologia, item 2,
  * "Multi-Power-Iteration"; [TG] body: Rayleigh-quotient estimate of the spectral norm).
- *   DASH_SCALE_FROBENIUS: s_i = ||A_i||_F   (k, steps, V0 and prec ignored; ws may be NULL).
+ *   DASH_SCALE_FROBENIUS: s_i = ||A_i||_F   (k, steps, V0, seed and prec ignored; ws may be NULL).
  *   DASH_SCALE_POWER:     k start vectors (columns of V0[B,k], shared by all blocks, 1 <= k <= 32)
  *     run `steps` >= 1 power-iteration steps in parallel: each step forms W = A_i V, the Rayleigh
  *     quotient of every column comes from the last step, each column is renormalised between
  *     steps, and s_i = max over columns.  prec == DASH_FP16 streams A_i in binary16 prescaled by
  *     2^-ceil(log2 max_j A_i[j][j]) and keeps V in binary16; accumulation stays fp32.
+ *     V0 == NULL: the start pool is drawn on the device from `seed` (dash_start_vectors' values).
  * A block whose scale comes out non-finite or <= 0 is flagged later by the solver. */
 dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
-                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream);
+                       int32_t steps, const float* V0, uint64_t seed, float* s, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* The start pool V0[B,k] (row-major) that dash_scale draws from `seed` when it is given no V0.
+ * Element e = i k + j is a centred sum of three uniforms from a SplitMix64 stream started at seed
+ * (Steele, Lea and Flood, "Fast splittable pseudorandom number generators", 2014: output n is
+ * mix(seed + n 0x9E3779B97F4A7C15) with mix(z) = z ^ (z >> 30), times 0xBF58476D1CE4E5B9, ^ >> 27,
+ * times 0x94D049BB133111EB, ^ >> 31): with u_q the top 22 bits of output 3e + q (q = 1, 2, 3),
+ * V0[e] = (u_1 + u_2 + u_3 - 1.5 * 2^22) * 2^-22, in (-1.5, 1.5), exact in fp32.  The pages give no
+ * distribution for the start vectors; any pool with a component along the top eigenvector serves.
+ * 1 <= k <= 32. */
+dash_status dash_start_vectors(int32_t B, int32_t k, uint64_t seed, float* V0, void* stream);
 
 /* Inverse fourth root by two Newton-Denman-Beavers calls ([PT] Metodologia, item 2,
  * "Iteração de Newton-Denman-Beavers": one call gives the square root and the inverse square root;
@@ -260,7 +272,7 @@ dash_status dash_inverse_root_cheb_blocks(const float* A, const float* s, int64_
  * that GPU's array: calls that overlap on one GPU (on two streams, or from two threads) race and
  * must be ordered by the caller.  The Frobenius scale needs no scratch and is passed through. */
 dash_status dash_scale_noalloc(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
-                               int32_t steps, const float* V0, float* s, void* stream);
+                               int32_t steps, const float* V0, uint64_t seed, float* s, void* stream);
 size_t dash_noalloc_scratch_bytes(void);
 
 /* Estimate of every block's smallest eigenvalue, from above ([PT] Significância e Alegações,

@@ -48,7 +48,8 @@ def library() -> ctypes.CDLL:
             "dash_unstack": (st, [vp, i32, ctypes.POINTER(DashMat), i32, vp]),
             "dash_update_stats": (st, [vp, i64, i32, f32, vp, vp]),
             "dash_update_stats_prec": (st, [vp, i64, i32, f32, st, vp, vp]),
-            "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp, sz, vp]),
+            "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, ctypes.c_uint64, vp, vp, sz, vp]),
+            "dash_start_vectors": (st, [i32, i32, ctypes.c_uint64, vp, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_ndb_prec": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cn": (st, [vp, vp, i64, i32, i32, i32, st, vp, vp, vp, vp, sz, vp]),
@@ -68,7 +69,7 @@ def library() -> ctypes.CDLL:
             "dash_residual_probe": (st, [vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]),
             "dash_inverse_root_routed": (st, [vp, vp, i64, i32, i32, f64, f64, i32, i32, vp, f32, i32, st, vp, vp, vp,
                                               vp, vp, vp, sz, vp]),
-            "dash_scale_noalloc": (st, [vp, i64, i32, st, st, i32, i32, vp, vp, vp]),
+            "dash_scale_noalloc": (st, [vp, i64, i32, st, st, i32, i32, vp, ctypes.c_uint64, vp, vp]),
             "dash_noalloc_scratch_bytes": (sz, []),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
@@ -239,21 +240,30 @@ def dash_update_stats_prec(G_stack, NG: int, B: int, beta: float, prec: int, A, 
                                             a.ptr(A, "A", numel=2 * NG * B * B), a.stream(stream)))
 
 
-def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, ws=None, stream=None):
+def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, ws=None, stream=None, seed: int = 0):
+    """V0 None with power iteration: the start pool drawn on the device from seed."""
     a = _Args("dash_scale")
     vn = B * k if how == DASH_SCALE_POWER else 0
     _check("dash_scale", library().dash_scale(a.ptr(A, "A", numel=N * B * B), N, B, how, prec, k, steps,
-                                              a.ptr(V0, "V0", numel=vn), a.ptr(s, "s", numel=N), a.ws(ws),
+                                              a.ptr(V0, "V0", numel=vn), seed, a.ptr(s, "s", numel=N), a.ws(ws),
                                               _nbytes(ws), a.stream(stream)))
 
 
-def dash_scale_noalloc(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, stream=None):
+def dash_start_vectors(B: int, k: int, seed: int, V0, stream=None):
+    a = _Args("dash_start_vectors")
+    _check("dash_start_vectors", library().dash_start_vectors(B, k, seed, a.ptr(V0, "V0", numel=B * k),
+                                                              a.stream(stream)))
+
+
+def dash_scale_noalloc(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, stream=None,
+                       seed: int = 0):
     """dash_scale with the library's own scratch: no workspace argument, nothing allocated."""
     a = _Args("dash_scale_noalloc")
     vn = B * k if how == DASH_SCALE_POWER else 0
     _check("dash_scale_noalloc",
            library().dash_scale_noalloc(a.ptr(A, "A", numel=N * B * B), N, B, how, prec, k, steps,
-                                        a.ptr(V0, "V0", numel=vn), a.ptr(s, "s", numel=N), a.stream(stream)))
+                                        a.ptr(V0, "V0", numel=vn), seed, a.ptr(s, "s", numel=N),
+                                        a.stream(stream)))
 
 
 def dash_noalloc_scratch_bytes() -> int:

@@ -712,15 +712,23 @@ dash_status scale_args_check(const float* A, int64_t N, int32_t B, dash_scaling 
   if (how != DASH_SCALE_POWER) return DASH_ERR_INVALID_ARG;
   if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;  // power iteration streams fp32 or binary16 operands
   if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
-  if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !V0 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
+  if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
   return DASH_OK;
 }
 }  // namespace dash
 
 extern "C" {
 
+dash_status dash_start_vectors(int32_t B, int32_t k, uint64_t seed, float* V0, void* stream) {
+  if (!V0 || !aligned(V0, 4) || k < 1 || k > 32) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  TRY(launch_start_pool(seed, (int64_t)B * k, V0, as_stream(stream)));
+  return DASH_OK;
+}
+
 dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
-                       int32_t steps, const float* V0, float* s, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t steps, const float* V0, uint64_t seed, float* s, void* ws, size_t ws_bytes,
+                       void* stream) {
   const dash_status chk = scale_args_check(A, N, B, how, prec, k, steps, V0, s);
   if (chk != DASH_OK) return chk;
   if (how == DASH_SCALE_FROBENIUS) {
@@ -737,6 +745,7 @@ dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, d
   p.prec = prec;
   p.A = A;
   p.V0 = V0;
+  p.seed = seed;
   p.s = s;
   const int RB = B / 64;
   for (int q = 0; q < 2; ++q) p.W[q] = (float*)cv.take((size_t)N * B * 32 * sizeof(float));

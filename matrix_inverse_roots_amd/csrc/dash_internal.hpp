@@ -175,7 +175,8 @@ struct PowerPlan {
   int B, k, steps;
   dash_prec prec;
   const float* A;
-  const float* V0;
+  const float* V0;   // [B, k], or null: the pool drawn from seed (launch_start_pool's values)
+  uint64_t seed = 0;
   float* s;
   // workspace pieces
   float* W[2];       // [N, B, 32] fp32 iterates
@@ -199,12 +200,15 @@ struct ProbePlan {
   const float* A;
   const float* X;
   const float* V0;
+  uint64_t seed = 0;
   float* r;
   float* W[2];
   float* part[2];
   float* V0p;
 };
 hipError_t launch_residual_probe(const ProbePlan& plan, hipStream_t stream);
+// The start pool V0[e], e < n, drawn from seed (three SplitMix64 outputs per element, see scale.hip).
+hipError_t launch_start_pool(uint64_t seed, int64_t n, float* V0, hipStream_t stream);
 size_t power_workspace_bytes(int64_t N, int B, dash_prec prec);
 
 // Eigendecomposition-based inverse fourth root (two-sided block Jacobi).  launch_jacobi runs up

@@ -46,16 +46,16 @@ extern "C" {
 size_t dash_noalloc_scratch_bytes(void) { return dash::SCRATCH_BYTES; }
 
 dash_status dash_scale_noalloc(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,
-                               int32_t steps, const float* V0, float* s, void* stream) {
+                               int32_t steps, const float* V0, uint64_t seed, float* s, void* stream) {
   using namespace dash;
   const dash_status chk = scale_args_check(A, N, B, how, prec, k, steps, V0, s);
   if (chk != DASH_OK) return chk;
-  if (how == DASH_SCALE_FROBENIUS) return dash_scale(A, N, B, how, prec, k, steps, V0, s, nullptr, 0, stream);
+  if (how == DASH_SCALE_FROBENIUS) return dash_scale(A, N, B, how, prec, k, steps, V0, seed, s, nullptr, 0, stream);
   // the request must fit the fixed scratch; decided on the host before any device call
   if (power_workspace_bytes(N, B, prec) > SCRATCH_BYTES) return DASH_ERR_WORKSPACE;
   void* ws = device_scratch();
   if (!ws) return DASH_ERR_DEVICE;
-  return dash_scale(A, N, B, how, prec, k, steps, V0, s, ws, SCRATCH_BYTES, stream);
+  return dash_scale(A, N, B, how, prec, k, steps, V0, seed, s, ws, SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -65,17 +65,44 @@ __global__ __launch_bounds__(1024) void frobenius_kernel(const float* A, int B, 
 // Power iteration
 // ------------------------------------------------------------------------------------------------
 
+// Element e of the start pool drawn from `seed` when the caller passes none: three SplitMix64 outputs
+// (Steele, Lea and Flood, 2014: output n of the stream started at `seed` is mix(seed + n * gamma)),
+// n = 3e + 1 .. 3e + 3, keep their top 22 bits; the value is (u0 + u1 + u2 - 1.5 * 2^22) * 2^-22, a
+// centred sum of three uniforms.  Every step is exact in integers and fp32, so the host's copy of the
+// generator gives the same bits.
+__device__ __forceinline__ float pool_value(uint64_t seed, int64_t e) {
+  const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+  uint32_t sum = 0;
+  for (int q = 1; q <= 3; ++q) {
+    uint64_t z = seed + (uint64_t)(3 * e + q) * gamma;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    sum += (uint32_t)(z >> 42);
+  }
+  return ((float)sum - 6291456.0f) * 0x1p-22f;
+}
+
+__device__ __forceinline__ float pool_at(const float* V0, uint64_t seed, int64_t e) {
+  return V0 ? V0[e] : pool_value(seed, e);
+}
+
+__global__ void start_pool_kernel(uint64_t seed, int64_t n, float* V0) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) V0[e] = pool_value(seed, e);
+}
+
 // Start vectors: V0p[B, KV] = V0[:, j] / ||V0[:, j]|| for j < k, zero columns after (so every step
-// reads a [B, KV] iterate with 16-byte loads).  One workgroup: 32 threads per column reduce in
-// double, then all threads write the normalised copy.
-__global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, int B, int k, float* V0p) {
+// reads a [B, KV] iterate with 16-byte loads); V0 null: the pool drawn from seed.  One workgroup: 32
+// threads per column reduce in double, then all threads write the normalised copy.
+__global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, uint64_t seed, int B, int k, float* V0p) {
   const int j = threadIdx.x % KV, part = threadIdx.x / KV;
   __shared__ double sq[32][KV];
   __shared__ float inv[KV];
   double acc = 0.0;
   if (j < k)
     for (int i = part; i < B; i += 32) {
-      const double v = V0[(int64_t)i * k + j];
+      const double v = pool_at(V0, seed, (int64_t)i * k + j);
       acc += v * v;
     }
   sq[part][j] = acc;
@@ -88,7 +115,7 @@ __global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, int B
   __syncthreads();
   for (int e = threadIdx.x; e < B * KV; e += 1024) {
     const int i = e / KV, jj = e % KV;
-    V0p[e] = jj < k ? V0[(int64_t)i * k + jj] * inv[jj] : 0.f;
+    V0p[e] = jj < k ? pool_at(V0, seed, (int64_t)i * k + jj) * inv[jj] : 0.f;
   }
 }
 
@@ -504,6 +531,12 @@ size_t power_workspace_bytes(int64_t N, int B, dash_prec prec) {
   return bytes;
 }
 
+hipError_t launch_start_pool(uint64_t seed, int64_t n, float* V0, hipStream_t stream) {
+  if (n < 1 || n > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(start_pool_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, seed, n, V0);
+  return hipGetLastError();
+}
+
 hipError_t launch_frobenius(const float* A, int64_t N, int B, float* s, hipStream_t stream) {
   if (N > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(frobenius_kernel, dim3((unsigned)N), dim3(1024), 0, stream, A, B, s);
@@ -541,7 +574,7 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   const int64_t grid = p.N * RB;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err;
-  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.B, p.k, p.V0p);
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const float* coef = nullptr;
   if (p.prec == DASH_FP16) {
@@ -606,7 +639,7 @@ hipError_t launch_residual_probe(const ProbePlan& p, hipStream_t stream) {
   const int64_t grid = p.N * RB;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err;
-  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.B, p.k, p.V0p);
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int depth = ring_depth(p.B / 32, 4);
   for (int t = 0; t < 5; ++t) {

@@ -126,8 +126,10 @@ def test_cn_cheb_scale_apply_stats_argument_errors():
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 0, P2, P3,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 10, P2 + 2, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG                                   # V0 misaligned
     assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 10, None, P3,
-                      ws=ws) == _lib.DASH_ERR_INVALID_ARG                                   # V0 missing
+                      ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE                         # V0 NULL: seeded
     assert _status_of(g, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 8, 10, P2, P3,
                       ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
     assert _status_of(g, P, N, B, 5, dash.DASH_FP32, 8, 10, P2, P3, ws=ws) == _lib.DASH_ERR_INVALID_ARG
@@ -271,3 +273,38 @@ def test_split_precision_queries_and_argument_errors():
         _lib.DASH_ERR_INVALID_ARG                                                           # U aliases XL
     assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32_SPLIT, 8, 10, P2, P3,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
+
+
+def test_start_pool_generator_matches_splitmix64_definition():
+    """dash_inputs.start_pool_counter (the host twin of the library's seeded start pool) against
+    SplitMix64 written out with Python integers from its published definition."""
+    import dash_inputs as di
+
+    M = (1 << 64) - 1
+
+    def mix(z):
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        return z ^ (z >> 31)
+
+    for seed in (0, 7, (1 << 64) - 5):
+        pool = di.start_pool_counter(64, 3, seed)
+        for e in (0, 1, 2, 100, 191):
+            u = sum(mix((seed + (3 * e + q) * 0x9E3779B97F4A7C15) & M) >> 42 for q in (1, 2, 3))
+            assert float(pool.reshape(-1)[e]) == (u - 6291456) * 2.0 ** -22
+    assert abs(float(di.start_pool_counter(256, 32, 7).mean())) < 0.05
+
+
+def test_binding_rejects_host_tensors():
+    """The binding checks tensor arguments before any pointer reaches the library: a host tensor is
+    refused with ValueError (no GPU needed)."""
+    import torch
+
+    A = torch.zeros((2, 64, 64))
+    s = torch.zeros(2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dash.dash_inverse_root_ndb(A, s, 2, 64, 3, 3, torch.zeros_like(A))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dash.dash_scale(A, 2, 64, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dash.dash_stack([torch.zeros((64, 64))], 64, P)

@@ -167,3 +167,42 @@ def test_routed_inverse_root_matches_oracle(prec):
     assert np.all(to_host(status) == 0)
     rh = to_host(resid)
     assert np.all(rh < tol)
+
+
+def test_seeded_start_pool_equals_the_host_pool():
+    """dash_scale without start vectors draws the pool on the device from the seed: the pool is the
+    host twin's bit for bit, and the scale equals the one computed from the host pool."""
+    Vd = torch.empty((256, 32), device=DEV)
+    dash.dash_start_vectors(256, 32, 7, Vd)
+    V0 = di.start_pool_counter(256, 32, 7)
+    assert np.array_equal(to_host(Vd), V0.astype(np.float64))
+    A, _, _ = mixed_stack(260, 2, 256, [(0.05, 1.0), (1e-3, 1.0)])
+    N, B = A.shape[0], A.shape[1]
+    Ad = to_dev(A)
+    ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 32, device=DEV)
+    s_seed, s_pool, s_na = (torch.empty(N, device=DEV) for _ in range(3))
+    dash.dash_scale(Ad, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, None, s_seed, ws, seed=7)
+    dash.dash_scale(Ad, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, to_dev(V0), s_pool, ws)
+    dash.dash_scale_noalloc(Ad, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, None, s_na, seed=7)
+    assert torch.equal(s_seed, s_pool) and torch.equal(s_seed, s_na)
+    s_ref, _ = oracle.mpi(A.astype(np.float64), V0, 10)
+    assert np.max(np.abs(to_host(s_seed) - s_ref) / s_ref) < 1e-5
+
+
+def test_binding_rejects_bad_tensor_arguments():
+    """Wrong dtype, too few elements, a non-contiguous view: refused by the binding before any pointer
+    reaches the library."""
+    A = torch.eye(64, device=DEV).repeat(2, 1, 1)
+    s = torch.ones(2, device=DEV)
+    X = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_NDB, 2, 64, device=DEV)
+    with pytest.raises(ValueError, match="float32"):
+        dash.dash_inverse_root_ndb(A.double(), s, 2, 64, 3, 3, X, ws=ws)
+    with pytest.raises(ValueError, match="elements"):
+        dash.dash_inverse_root_ndb(A[:1], s, 2, 64, 3, 3, X, ws=ws)
+    with pytest.raises(ValueError, match="contiguous"):
+        dash.dash_inverse_root_ndb(A.transpose(1, 2), s, 2, 64, 3, 3, X, ws=ws)
+    with pytest.raises(ValueError, match="int32"):
+        dash.dash_inverse_root_ndb(A, s, 2, 64, 3, 3, X, status=torch.zeros(2, device=DEV), ws=ws)
+    with pytest.raises(ValueError, match="unit column stride"):
+        dash.dash_stack([torch.zeros((128, 128), device=DEV).t()[::1, ::2]], 64, torch.empty((2, 64, 64), device=DEV))

@@ -17,13 +17,13 @@ def test_noalloc_refuses_requests_beyond_its_scratch():
     lib = dash.library()
     P = 1 << 20
     # 489 fp32 blocks of 1024 need more than the 128 MiB scratch; refused on the host, no launch
-    assert lib.dash_scale_noalloc(P, 489, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, 2 * P, 3 * P,
+    assert lib.dash_scale_noalloc(P, 489, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, 2 * P, 0, 3 * P,
                                   None) == _lib.DASH_ERR_WORKSPACE
-    assert lib.dash_scale_noalloc(P, 57, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP16, 32, 10, 2 * P, 3 * P,
+    assert lib.dash_scale_noalloc(P, 57, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP16, 32, 10, 2 * P, 0, 3 * P,
                                   None) == _lib.DASH_ERR_WORKSPACE
-    assert lib.dash_scale_noalloc(P, 4, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP32, 33, 10, 2 * P, 3 * P,
+    assert lib.dash_scale_noalloc(P, 4, 1024, dash.DASH_SCALE_POWER, dash.DASH_FP32, 33, 10, 2 * P, 0, 3 * P,
                                   None) == _lib.DASH_ERR_INVALID_ARG
-    assert lib.dash_scale_noalloc(P, 4, 96, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, 2 * P, 3 * P,
+    assert lib.dash_scale_noalloc(P, 4, 96, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, 2 * P, 0, 3 * P,
                                   None) == _lib.DASH_ERR_SHAPE
     assert dash.dash_noalloc_scratch_bytes() == 128 << 20
 
