@@ -95,7 +95,8 @@ __global__ void start_pool_kernel(uint64_t seed, int64_t n, float* V0) {
 // Start vectors: V0p[B, KV] = V0[:, j] / ||V0[:, j]|| for j < k, zero columns after (so every step
 // reads a [B, KV] iterate with 16-byte loads); V0 null: the pool drawn from seed.  One workgroup: 32
 // threads per column reduce in double, then all threads write the normalised copy.
-__global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, uint64_t seed, int B, int k, float* V0p) {
+__global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, uint64_t seed, int B, int k, float* V0p,
+                                                          bool transposed) {
   const int j = threadIdx.x % KV, part = threadIdx.x / KV;
   __shared__ double sq[32][KV];
   __shared__ float inv[KV];
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(1024) void v0_prepare_kernel(const float* V0, uint6
   }
   __syncthreads();
   for (int e = threadIdx.x; e < B * KV; e += 1024) {
-    const int i = e / KV, jj = e % KV;
+    const int i = transposed ? e % B : e / KV, jj = transposed ? e / B : e % KV;
     V0p[e] = jj < k ? pool_at(V0, seed, (int64_t)i * k + jj) * inv[jj] : 0.f;
   }
 }
@@ -340,6 +341,129 @@ __global__ __launch_bounds__(64 * WAVES, 3) void power_step_f32(PowerStepArgs<fl
   const float sigma = a.shift_s ? a.shift_mul * a.shift_s[b] : 0.f;
   power_epilogue<WAVES>(vm, a.W + b * (int64_t)B * KV, a.part_out + (b * a.RB + rb) * 3 * KV, acc, r0, wave,
                         lane, red, sigma);
+}
+
+// Streaming fp32 step for symmetric blocks, B % 128 == 0.  Since A_b is symmetric, W = A_b V is also
+// A_b^T V: output row i is the sum over k of row k of A_b (at column i) times row k of V.  A
+// workgroup of WPG waves covers output rows [i0, i0 + 128 WPG) of one block (the whole block when
+// B <= 1024) and walks k over all B rows of A, so for every k the waves together read one
+// contiguous stretch of row k (4 KiB at B = 1024) instead of 128-byte pieces of 128 rows.  Lane
+// (li, h) of a wave takes A[k][iw + 4 li .. 4 li + 3] (one 16-byte load straight into registers, no
+// LDS, no barrier) as the fp32 MFMA's left operand of four 32-row tiles, tile t's row m being output
+// row iw + 4 m + t, and V[k][li] as the right operand, with k = kb + 8 h + p in the MFMA's slot p of
+// the 16-row block kb (any pairing of rows to slots serves, as long as both operands agree).  The
+// iterates are stored transposed, Vt[j][i] per block: a lane's right operands for one k-block are
+// 8 consecutive floats of its column (two 16-byte loads), and its four tiles' outputs at one
+// accumulator position are four consecutive rows of one column (one 16-byte store).  Each wave's
+// 128 rows are one row block of the partial sums (RB = B / 128), reduced in the wave.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void power_step_stream(
+    PowerStepArgs<float> a) {
+  constexpr int D = 8;  // MFMA slots per k-block of 16 rows
+  const int B = a.B;
+  const int wpg = (int)(blockDim.x >> 6);
+  const int gpb = B / (128 * wpg);  // workgroups per block
+  const int64_t lid = gemm::xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = lid / gpb;
+  const int g = (int)(lid - b * gpb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 31, h = lane >> 5;
+  const int rb = g * wpg + wave;
+  const int iw = rb * 128;
+  const float* A = a.A + b * (int64_t)B * B;
+  const float* Vt = a.Vsrc + b * a.vstride;  // [KV][B]
+  const float inv = col_inv_norm(a, b, li);  // normalisation of column li (0 beyond k)
+  const float* ap = A + (int64_t)(8 * h) * B + iw + 4 * li;  // + (kb + p) B
+  const float* vp = Vt + (int64_t)li * B + 8 * h;              // + kb: slots 0..7 of the lane's half
+  const int KB = B / 16;  // k-blocks of 16 rows; even, since B % 128 == 0
+  f32x4 ra[D];
+  f32x4 vb[2][2];  // right operands of k-blocks kb (vb[kb & 1]) and kb + 1: two 16-byte pieces each
+#pragma unroll
+  for (int p = 0; p < D; ++p) {
+    ra[p] = *(const f32x4*)(ap + (int64_t)p * B);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    vb[q][0] = *(const f32x4*)(vp + 16 * q);
+    vb[q][1] = *(const f32x4*)(vp + 16 * q + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  // one k-block: each A slot is reloaded (with the next block's row) right after the MFMAs that
+  // consumed it, then the block's right operands with those of the block after next; the scheduling
+  // barriers keep the compiler from gathering the loads, and the two right-operand buffers alternate
+  // by position (no register copies, which would wait for the loads)
+  auto block = [&](int kb, auto q_c, bool reload_a, bool reload_v) {
+    constexpr int q = decltype(q_c)::value;
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[p][t], vb[q][p >> 2][p & 3] * inv, acc[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (reload_a) ra[p] = *(const f32x4*)(ap + (int64_t)(16 * (kb + 1) + p) * B);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (reload_v) {
+      vb[q][0] = *(const f32x4*)(vp + 16 * (kb + 2));
+      vb[q][1] = *(const f32x4*)(vp + 16 * (kb + 2) + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kb = 0;
+  for (; kb + 2 < KB; kb += 2) {
+    block(kb, IC<0>{}, true, true);
+    block(kb + 1, IC<1>{}, true, true);
+  }
+  block(kb, IC<0>{}, true, false);
+  block(kb + 1, IC<1>{}, false, false);
+  // epilogue: W rows (transposed store), and the column partial sums (w.w, v.w, v.v) of the wave's
+  // 128 rows
+  const float sigma = a.shift_s ? a.shift_mul * a.shift_s[b] : 0.f;
+  float* Wt = a.W + b * (int64_t)B * KV + (int64_t)li * B;
+  const float* vcol = Vt + (int64_t)li * B;
+  float ww = 0.f, vw = 0.f, vv = 0.f;
+  // two halves of eight rows of tiles: all loads of a half issued before its stores (the stores
+  // could alias them)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+  f32x4 v4s[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const int r = 8 * half + rr;
+    v4s[rr] = *(const f32x4*)(vcol + iw + 4 * (8 * (r >> 2) + 4 * h + (r & 3)));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const int r = 8 * half + rr;
+    const int i = iw + 4 * (8 * (r >> 2) + 4 * h + (r & 3));  // rows i .. i + 3 are the four tiles
+    const f32x4 v4 = v4s[rr];
+    f32x4 w4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float v = v4[t] * inv;
+      const float w = sigma != 0.f ? fmaf(sigma, v, -acc[t][r]) : acc[t][r];
+      w4[t] = w;
+      ww += w * w;
+      vw += v * w;
+      vv += v * v;
+    }
+    *(f32x4*)(Wt + i) = w4;
+  }
+  }
+  ww += __shfl_xor(ww, 32, 64);
+  vw += __shfl_xor(vw, 32, 64);
+  vv += __shfl_xor(vv, 32, 64);
+  if (h == 0) {
+    float* po = a.part_out + (b * a.RB + rb) * 3 * KV;
+    po[li] = ww;
+    po[KV + li] = vw;
+    po[2 * KV + li] = vv;
+  }
 }
 
 // Binary16 operands: A_b prescaled in binary16, V rounded to binary16 as it is staged (transposed,
@@ -574,7 +698,10 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   const int64_t grid = p.N * RB;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err;
-  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p);
+  // fp32 on 128-row blocks: the streaming step (row k of the symmetric block read whole), whose
+  // iterates are stored transposed, [KV][B] per block
+  const bool stream_f32 = p.prec == DASH_FP32 && wide;
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p, stream_f32);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const float* coef = nullptr;
   if (p.prec == DASH_FP16) {
@@ -592,6 +719,11 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   }
   // fp32 slices are 32 wide, binary16 slices 64 wide
   const int depth = p.prec == DASH_FP32 ? ring_depth(p.B / 32, 4) : ring_depth(p.B / 64, 2);
+  // waves per workgroup: the largest of 8, 4, 2, 1 dividing the block's 128-row blocks
+  const int rbs = p.B / 128;
+  const int wpg = !stream_f32 ? 1 : rbs % 8 == 0 ? 8 : rbs % 4 == 0 ? 4 : rbs % 2 == 0 ? 2 : 1;
+  const int64_t sgrid = stream_f32 ? p.N * (p.B / (128 * wpg)) : 0;
+  if (sgrid > 0x7fffffffLL) return hipErrorInvalidValue;
   for (int t = 0; t < p.steps; ++t) {
     const int cur = t & 1;
     auto fill = [&](auto& a) {
@@ -606,14 +738,16 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
       a.shift_s = p.shift_s;
       a.shift_mul = p.shift_mul;
     };
-    if (p.prec == DASH_FP32) {
+    if (stream_f32) {
       PowerStepArgs<float> a;
       a.A = p.A;
       fill(a);
-      if (wide)
-        launch_step_depth<float, 4>(depth, dim3((unsigned)grid), stream, a);
-      else
-        launch_step_depth<float, 2>(depth, dim3((unsigned)grid), stream, a);
+      hipLaunchKernelGGL(power_step_stream, dim3((unsigned)sgrid), dim3(64 * wpg), 0, stream, a);
+    } else if (p.prec == DASH_FP32) {
+      PowerStepArgs<float> a;
+      a.A = p.A;
+      fill(a);
+      launch_step_depth<float, 2>(depth, dim3((unsigned)grid), stream, a);
     } else {
       PowerStepArgs<_Float16> a;
       a.A = p.Ah;
@@ -639,7 +773,7 @@ hipError_t launch_residual_probe(const ProbePlan& p, hipStream_t stream) {
   const int64_t grid = p.N * RB;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t err;
-  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p);
+  hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int depth = ring_depth(p.B / 32, 4);
   for (int t = 0; t < 5; ++t) {
