@@ -81,6 +81,12 @@ typedef struct {
   int64_t rows, cols, ld;
 } dash_mat;
 
+/* A contiguous fp32 vector gradient (device memory) of len elements: a 1-D parameter. */
+typedef struct {
+  float* ptr;
+  int64_t len;
+} dash_vec;
+
 /* Blockify: copy the B x B tiles of n weight gradients into G_stack, weight-major, then tile row,
  * then tile column ([PT] Metodologia, item 1: gradient blocks G_ij are stacked into an (N, B, B)
  * tensor so one batched call processes them all).
@@ -358,6 +364,35 @@ dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, i
  * fp32 matrix cores).  Same workspace; DASH_ERR_INVALID_ARG for any other prec. */
 dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B,
                             dash_prec prec, float* U_stack, void* ws, size_t ws_bytes, void* stream);
+
+/* 1-D parameters (biases, normalisation gains).  A Shampoo preconditioner for an order-k tensor
+ * takes the -1/(2k) power of each mode's statistic, so a vector (k = 1) is preconditioned by the
+ * inverse square root of its one statistic; blocked like the matrices, a vector of len elements is
+ * cut into ceil(len/B) pieces of B (the last zero-padded), piece p keeps L_p <- beta L_p +
+ * (1 - beta) g_p g_p^T (B x B, stacked like the matrix statistics) and its update is L_p^{-1/2} g_p
+ * ([TG] body: Shampoo's preconditioners come from gradient products; the pages treat weight
+ * matrices only, so vectors follow Shampoo's rule for order-1 tensors).
+ * dash_stack_vec: the pieces of n vectors [host descriptors] into g_pieces[P, B], vector-major, P =
+ * sum ceil(len_w / B); ptr 4-byte aligned, len >= 1.  dash_unstack_vec: the first len_w elements of
+ * each vector's pieces back (the padding is not written). */
+dash_status dash_stack_vec(const dash_vec* grads, int32_t n, int32_t B, float* g_pieces, void* stream);
+dash_status dash_unstack_vec(const float* u_pieces, int32_t B, const dash_vec* outs, int32_t n, void* stream);
+
+/* L_p <- beta L_p + (1 - beta) g_p g_p^T for the P pieces g_pieces[P, B]; L [P, B, B] in place (each
+ * block symmetric on input stays exactly symmetric).  0 <= beta <= 1. */
+dash_status dash_update_stats_vec(const float* g_pieces, int64_t P, int32_t B, float beta, float* L, void* stream);
+
+/* Inverse square root by one Newton-Denman-Beavers call ([PT] Metodologia, item 2, "Iteração de
+ * Newton-Denman-Beavers": one call yields the square root and the inverse square root): iters steps
+ * on A_i / s_i give Z ~ (A_i/s_i)^{-1/2}, and X_i = s_i^{-1/2} Z.  3 iters - 3 products (1 for iters
+ * = 1).  prec DASH_FP32 or DASH_FP32_SPLIT (as dash_inverse_root_ndb_prec); monitor NULL or
+ * [N, iters]; workspace dash_workspace_size(DASH_OP_NDB, ...).  Other arguments as
+ * dash_inverse_root_ndb. */
+dash_status dash_inverse_sqrt_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters, dash_prec prec,
+                                  float* X, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* u_p = X_p g_p for p < P (X [P, B, B], g_pieces and u_pieces [P, B]; u must not alias g). */
+dash_status dash_apply_vec(const float* X, const float* g_pieces, int64_t P, int32_t B, float* u_pieces, void* stream);
 
 /* Workspace bytes for an operation.  k_or_degree: the number of start vectors for
  * DASH_OP_SCALE (power iteration; Frobenius needs 0), ignored otherwise.  bytes [host]. */

@@ -30,6 +30,10 @@ class DashMat(ctypes.Structure):
                 ("ld", ctypes.c_int64)]
 
 
+class DashVec(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("len", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -71,6 +75,11 @@ def library() -> ctypes.CDLL:
                                               vp, vp, vp, sz, vp]),
             "dash_scale_noalloc": (st, [vp, i64, i32, st, st, i32, i32, vp, ctypes.c_uint64, vp, vp]),
             "dash_noalloc_scratch_bytes": (sz, []),
+            "dash_stack_vec": (st, [ctypes.POINTER(DashVec), i32, i32, vp, vp]),
+            "dash_unstack_vec": (st, [vp, i32, ctypes.POINTER(DashVec), i32, vp]),
+            "dash_update_stats_vec": (st, [vp, i64, i32, f32, vp, vp]),
+            "dash_inverse_sqrt_ndb": (st, [vp, vp, i64, i32, i32, st, vp, vp, vp, vp, sz, vp]),
+            "dash_apply_vec": (st, [vp, vp, i64, i32, vp, vp]),
             "dash_workspace_size": (st, [st, i64, i32, st, i32, ctypes.POINTER(sz)]),
             "dash_solver_products": (i64, [st, i32, i32]),
             "dash_flops": (f64, [st, i64, i32, st, i32, i32]),
@@ -154,6 +163,19 @@ class _Args:
             arr[i].ptr = t.data_ptr()
             arr[i].rows, arr[i].cols = t.shape
             arr[i].ld = t.stride(0)
+        return arr
+
+    def vecs(self, ts, name):
+        """dash_vec descriptors of contiguous 1-D fp32 GPU vectors."""
+        arr = (DashVec * len(ts))()
+        for i, t in enumerate(ts):
+            if self._tensor(t, "%s[%d]" % (name, i)):
+                import torch
+
+                if t.dim() != 1 or t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("%s: %s[%d] must be a contiguous 1-D float32 vector" % (self.call, name, i))
+            arr[i].ptr = t.data_ptr()
+            arr[i].len = t.shape[0]
         return arr
 
     def stream(self, stream):
@@ -439,3 +461,48 @@ def dash_apply_prec(XL, XR, G_stack, NG: int, B: int, prec: int, U_stack, ws=Non
            library().dash_apply_prec(a.ptr(XL, "XL", numel=n), a.ptr(XR, "XR", numel=n),
                                      a.ptr(G_stack, "G_stack", numel=n), NG, B, prec,
                                      a.ptr(U_stack, "U_stack", numel=n), a.ws(ws), _nbytes(ws), a.stream(stream)))
+
+
+def _pieces(lens, B):
+    return sum(-(-n // B) for n in lens) if B > 0 else 0
+
+
+def dash_stack_vec(grads, B: int, g_pieces, stream=None):
+    """The pieces of B (the last zero-padded) of 1-D gradients into g_pieces[P, B]."""
+    a = _Args("dash_stack_vec")
+    arr = a.vecs(grads, "grads")
+    n = _pieces([t.shape[0] for t in grads], B) * B
+    _check("dash_stack_vec", library().dash_stack_vec(arr, len(grads), B, a.ptr(g_pieces, "g_pieces", numel=n),
+                                                      a.stream(stream)))
+
+
+def dash_unstack_vec(u_pieces, B: int, outs, stream=None):
+    a = _Args("dash_unstack_vec")
+    arr = a.vecs(outs, "outs")
+    n = _pieces([t.shape[0] for t in outs], B) * B
+    _check("dash_unstack_vec", library().dash_unstack_vec(a.ptr(u_pieces, "u_pieces", numel=n), B, arr, len(outs),
+                                                          a.stream(stream)))
+
+
+def dash_update_stats_vec(g_pieces, P: int, B: int, beta: float, L, stream=None):
+    a = _Args("dash_update_stats_vec")
+    _check("dash_update_stats_vec",
+           library().dash_update_stats_vec(a.ptr(g_pieces, "g_pieces", numel=P * B), P, B, beta,
+                                           a.ptr(L, "L", numel=P * B * B), a.stream(stream)))
+
+
+def dash_inverse_sqrt_ndb(A, s, N: int, B: int, iters: int, prec: int, X, monitor=None, status=None, ws=None,
+                          stream=None):
+    a = _Args("dash_inverse_sqrt_ndb")
+    pA, ps, pX = _solver_ptrs(a, A, s, X, N, B)
+    _check("dash_inverse_sqrt_ndb",
+           library().dash_inverse_sqrt_ndb(pA, ps, N, B, iters, prec, pX, a.ptr(monitor, "monitor", numel=N * iters),
+                                           a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                           a.stream(stream)))
+
+
+def dash_apply_vec(X, g_pieces, P: int, B: int, u_pieces, stream=None):
+    a = _Args("dash_apply_vec")
+    _check("dash_apply_vec",
+           library().dash_apply_vec(a.ptr(X, "X", numel=P * B * B), a.ptr(g_pieces, "g_pieces", numel=P * B), P, B,
+                                    a.ptr(u_pieces, "u_pieces", numel=P * B), a.stream(stream)))

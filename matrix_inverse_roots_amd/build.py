@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdash.so")
 SOURCES = ["gemm.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_split.hip", "scale.hip", "elementwise.hip", "evd.hip",
-           "cheb.hip", "api.hip", "noalloc.hip"]
+           "cheb.hip", "vec.hip", "api.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

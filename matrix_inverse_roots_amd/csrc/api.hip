@@ -127,6 +127,9 @@ struct NdbCtx {
   int32_t* steps = nullptr;
   // products formed from three-piece bfloat16 splits (DASH_FP32_SPLIT) where the shape allows
   bool split = false;
+  // the coefficient that unscales the wanted Z into the output: s^{-1/4} for the composed inverse
+  // fourth root, s^{-1/2} for one call's inverse square root
+  int8_t final_ia = CO_U;
 };
 
 dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool scaled, int T, int mon_col,
@@ -179,7 +182,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
       fin.X = Z;
       fin.D = final_out;
       fin.a = 1.f;
-      fin.ia = CO_U;
+      fin.ia = c.final_ia;
       fin.coef = c.coef;
       fin.status = c.status;
       TRY(launch_affine(fin, c.N, c.B, c.st));
@@ -211,7 +214,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
       if (want_z) {  // Z_T = S Z, unscaled into the output
         Epilogue e;
         e.alpha = 1.f;
-        e.ia = CO_U;
+        e.ia = c.final_ia;
         e.coef = c.coef;
         e.status = c.status;
         Product p = prod(S, Z, final_out);
@@ -1409,6 +1412,86 @@ dash_status dash_inverse_root_routed(const float* A, const float* s, int64_t N, 
     rc = dash_residual_probe(A, X, N, B, k, V0, resid, region, region_bytes, stream);
     if (rc != DASH_OK) return rc;
   }
+  return DASH_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 1-D parameters
+// ------------------------------------------------------------------------------------------------
+
+static dash_status check_vecs(const dash_vec* v, int32_t n, int32_t B) {
+  if (!v || n < 1) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i)
+    if (!v[i].ptr || !aligned(v[i].ptr, 4) || v[i].len < 1) return DASH_ERR_INVALID_ARG;
+  return DASH_OK;
+}
+
+dash_status dash_stack_vec(const dash_vec* grads, int32_t n, int32_t B, float* g_pieces, void* stream) {
+  const dash_status chk = check_vecs(grads, n, B);
+  if (chk != DASH_OK) return chk;
+  if (!g_pieces || !aligned(g_pieces, 4)) return DASH_ERR_INVALID_ARG;
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    TRY(launch_vec_copy(grads[i].ptr, grads[i].len, g_pieces + off, B, true, as_stream(stream)));
+    off += (grads[i].len + B - 1) / B * B;
+  }
+  return DASH_OK;
+}
+
+dash_status dash_unstack_vec(const float* u_pieces, int32_t B, const dash_vec* outs, int32_t n, void* stream) {
+  const dash_status chk = check_vecs(outs, n, B);
+  if (chk != DASH_OK) return chk;
+  if (!u_pieces || !aligned(u_pieces, 4)) return DASH_ERR_INVALID_ARG;
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    TRY(launch_vec_copy(outs[i].ptr, outs[i].len, (float*)u_pieces + off, B, false, as_stream(stream)));
+    off += (outs[i].len + B - 1) / B * B;
+  }
+  return DASH_OK;
+}
+
+dash_status dash_update_stats_vec(const float* g_pieces, int64_t P, int32_t B, float beta, float* L, void* stream) {
+  if (!g_pieces || !L || !aligned(g_pieces, 16) || !aligned(L, 16) || !valid_N(P)) return DASH_ERR_INVALID_ARG;
+  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  TRY(launch_vec_stats(g_pieces, P, B, beta, L, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_apply_vec(const float* X, const float* g_pieces, int64_t P, int32_t B, float* u_pieces, void* stream) {
+  if (!X || !g_pieces || !u_pieces || !aligned(X, 16) || !aligned(g_pieces, 16) || !aligned(u_pieces, 4) ||
+      !valid_N(P) || u_pieces == g_pieces)
+    return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  TRY(launch_vec_apply(X, g_pieces, P, B, u_pieces, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_inverse_sqrt_ndb(const float* A, const float* s, int64_t N, int32_t B, int32_t iters, dash_prec prec,
+                                  float* X, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
+    return DASH_ERR_INVALID_ARG;
+  if (X == A || iters < 1 || iters > 1000) return DASH_ERR_INVALID_ARG;
+  if ((monitor && !aligned(monitor, 4)) || (status && !aligned(status, 4))) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_ndb(N, B)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  Carver cv{(char*)ws, ws_bytes};
+  float* coef = (float*)cv.take(coef_bytes(N));
+  (void)cv.take(flag_bytes(N));
+  Pool pool;
+  for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, DASH_FP32)));
+  if (status) TRY(launch_fill_i32(status, N, 0, st));
+  if (monitor) TRY(launch_fill_f32(monitor, N * iters, 0.f, st));
+  TRY(launch_coef(s, N, coef, status, st));
+  NdbCtx c{N, B, coef, monitor, iters, status, st, &pool};
+  c.split = prec == DASH_FP32_SPLIT;
+  c.final_ia = CO_RSQ;  // X = s^{-1/2} Z
+  const dash_status r = ndb_call(c, A, false, true, iters, 0, true, X, nullptr);
+  if (r != DASH_OK) return r;
+  if (monitor) TRY(launch_monitor_finish(monitor, N * iters, B, st));
   return DASH_OK;
 }
 

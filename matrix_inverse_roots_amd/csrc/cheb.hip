@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64) void cheb_plan_kernel(ChebPlan p) {
   const double g1 = d >= 1 ? c[d - 1] - 2.0 * c[d] * m / w : 0.0;
   const int P = d == 1 ? 1 : d - 1;
   for (int q = tid; q < P; q += 64) {
-    float row[COEF_STRIDE] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float row[COEF_STRIDE] = {};
     bool ok = !bad;
     if (d == 1) {  // X = u (c0 I + c1 T), T = (2 A/s - (hi + lo) I) / (hi - lo)
       row[CS_ALPHA] = (float)(2.0 * c[1] / w) * R1U;

@@ -25,9 +25,10 @@ enum CoefIdx : int {
   CO_P2 = 5,    // 2^-e: binary16 prescale of the power iteration
   CO_P2INV = 6, // 2^e
   CO_S = 7,     // s
+  CO_RSQ = 8,   // s^{-1/2}        (unscaling of an inverse square root)
   CO_NONE = -1
 };
-constexpr int COEF_STRIDE = 8;
+constexpr int COEF_STRIDE = 10;
 
 // Epilogue of a batched product acc = X_b Y_b (fp32 accumulation):
 //   D  = alpha_b acc + beta_b C + delta_b E + gamma_b I        (C, E optional fp32 stacks)
@@ -256,6 +257,13 @@ struct CopyGroup {
   int32_t n;
 };
 hipError_t launch_tile_copy(const dash_mat* w, int n, int B, float* stack, bool to_stack, hipStream_t stream);
+
+// 1-D parameters (vec.hip): a vector's pieces of B (the last zero-padded) copied to or from a
+// contiguous run of pieces; the rank-one statistic update L_p <- beta L_p + (1 - beta) g_p g_p^T;
+// u_p = X_p g_p.
+hipError_t launch_vec_copy(float* v, int64_t len, float* pieces, int B, bool to_pieces, hipStream_t stream);
+hipError_t launch_vec_stats(const float* g, int64_t P, int B, float beta, float* L, hipStream_t stream);
+hipError_t launch_vec_apply(const float* X, const float* g, int64_t P, int B, float* u, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

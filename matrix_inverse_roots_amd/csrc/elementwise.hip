@@ -42,6 +42,8 @@ __global__ void coef_kernel(const float* s, int64_t N, float* coef, int32_t* sta
   c[CO_P2] = 1.f;
   c[CO_P2INV] = 1.f;
   c[CO_S] = sv;
+  c[CO_RSQ] = (float)(1.0 / sqrt(sd));
+  c[9] = 0.f;
 }
 
 __device__ __forceinline__ float co(const float* coef, int idx, int64_t b) {

@@ -67,6 +67,9 @@ def _load():
             "orc_update_stats": (None, [i, _dp, d, _dp, _dp]),
             "orc_apply": (None, [i, _dp, _dp, _dp, _dp]),
             "orc_mpi_shifted": (d, [i, _dp, d, i, i, _dp, _dp]),
+            "orc_update_stats_vec": (None, [i, _dp, d, _dp]),
+            "orc_apply_vec": (None, [i, _dp, _dp, _dp]),
+            "orc_ndb_inverse_sqrt": (None, [i, _dp, d, i, _dp]),
             "orc_residual_probe": (d, [i, _dp, _dp, i, _dp]),
             "orc_routed_inverse_root": (i, [i, _dp, d, i, d, d, i, i, _dp, d, i, _dp, _dp, _dp]),
         }
@@ -512,3 +515,73 @@ def unstack(U, shapes, B: int):
         out.append(W)
     assert t == U.shape[0]
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# 1-D parameters: pieces of B, L_p <- beta L_p + (1 - beta) g_p g_p^T, update L_p^{-1/2} g_p
+# ---------------------------------------------------------------------------------------------
+
+def stack_vec(vectors, B: int) -> np.ndarray:
+    """[P, B] pieces of the vectors, vector-major, the last piece of each zero-padded."""
+    out = []
+    for v in vectors:
+        v = _f64(v).reshape(-1)
+        n = -(-v.size // B)
+        pad = np.zeros(n * B)
+        pad[: v.size] = v
+        out.append(pad.reshape(n, B))
+    return np.concatenate(out)
+
+
+def unstack_vec(pieces, lens, B: int):
+    """The vectors of the given lengths back from their pieces."""
+    flat = _f64(pieces).reshape(-1)
+    out, off = [], 0
+    for n in lens:
+        out.append(flat[off:off + n].copy())
+        off += -(-n // B) * B
+    return out
+
+
+def update_stats_vec(g, beta: float, L, threads: int | None = None) -> np.ndarray:
+    """L_p <- beta L_p + (1 - beta) g_p g_p^T for every piece (returns the new stack)."""
+    g = _f64(g)
+    L = _f64(L).copy()
+    P, n = g.shape
+    lib = _load()
+
+    def one(p):
+        lib.orc_update_stats_vec(n, _p(g[p]), float(beta), _p(L[p]))
+
+    _over_blocks(one, P, threads)
+    return L
+
+
+def apply_vec(X, g, threads: int | None = None) -> np.ndarray:
+    """u_p = X_p g_p."""
+    X = _f64(X)
+    g = _f64(g)
+    P, n = g.shape
+    u = np.empty((P, n))
+    lib = _load()
+
+    def one(p):
+        lib.orc_apply_vec(n, _p(X[p]), _p(g[p]), _p(u[p]))
+
+    _over_blocks(one, P, threads)
+    return u
+
+
+def ndb_inverse_sqrt(A, s, iters: int, threads: int | None = None) -> np.ndarray:
+    """A^{-1/2} by one NDB call on A/s (its Z), unscaled by s^{-1/2}."""
+    A, single = _as_stack(A)
+    N, n, _ = A.shape
+    s = _per_block(s, N)
+    X = np.empty_like(A)
+    lib = _load()
+
+    def one(b):
+        lib.orc_ndb_inverse_sqrt(n, _p(A[b]), float(s[b]), int(iters), _p(X[b]))
+
+    _over_blocks(one, N, threads)
+    return X[0] if single else X

@@ -712,6 +712,37 @@ void orc_update_stats(int n, const double* G, double beta, double* L, double* R)
     }
 }
 
+/* 1-D parameters: a vector piece g of length n keeps L <- beta L + (1 - beta) g g^T, and its update is
+ * L^{-1/2} g (Shampoo's exponent -1/(2k) for an order-k tensor, k = 1; the pages treat matrices only). */
+void orc_update_stats_vec(int n, const double* g, double beta, double* L) {
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) L[IDX(i, j, n)] = beta * L[IDX(i, j, n)] + (1.0 - beta) * g[i] * g[j];
+}
+
+/* u = X g. */
+void orc_apply_vec(int n, const double* X, const double* g, double* u) {
+  for (int i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < n; ++j) acc += X[IDX(i, j, n)] * g[j];
+    u[i] = acc;
+  }
+}
+
+/* Inverse square root by one NDB call (c4) on A/s: Z -> (A/s)^{-1/2}, X = s^{-1/2} Z. */
+void orc_ndb_inverse_sqrt(int n, const double* A, double s, int T, double* X) {
+  const size_t nn = (size_t)n * n;
+  double* M = (double*)malloc(sizeof(double) * nn);
+  double* Y = (double*)malloc(sizeof(double) * nn);
+  double* mon = (double*)malloc(sizeof(double) * (T > 0 ? T : 1));
+  for (size_t e = 0; e < nn; ++e) M[e] = A[e] / s;
+  orc_ndb(n, M, T, Y, X, mon);
+  const double r = 1.0 / sqrt(s);
+  for (size_t e = 0; e < nn; ++e) X[e] *= r;
+  free(M);
+  free(Y);
+  free(mon);
+}
+
 /* c9: preconditioned update U = L^{-1/4} G R^{-1/4} = (XL G) XR ([TG] body). */
 void orc_apply(int n, const double* XL, const double* G, const double* XR, double* U) {
   double* T = (double*)malloc(sizeof(double) * (size_t)n * n);

@@ -834,3 +834,45 @@ def test_stack_edge_tiles_are_zero_padded():
 
 def test_llama_shapes_give_1536_tiles():
     assert di.num_tiles(di.llama_weight_shapes(), 1024) == 1536
+
+
+# ----------------------------------------------------------------------------------------------
+# 1-D parameters
+# ----------------------------------------------------------------------------------------------
+
+def test_vec_pieces_round_trip_and_padding():
+    g = di.rng(80)
+    vs = [g.standard_normal(n) for n in (5, 64, 130, 1)]
+    P = oracle.stack_vec(vs, 64)
+    assert P.shape == (1 + 1 + 3 + 1, 64)
+    assert np.array_equal(P[0, :5], vs[0]) and np.all(P[0, 5:] == 0)
+    assert np.array_equal(P[2:5].reshape(-1)[:130], vs[2]) and np.all(P[4, 2:] == 0)
+    back = oracle.unstack_vec(P, [5, 64, 130, 1], 64)
+    assert all(np.array_equal(a, b) for a, b in zip(back, vs))
+
+
+def test_vec_stats_and_apply_exact_on_integers():
+    """Small integers and beta = 1/2 keep every value exact: the rank-one update equals numpy's outer
+    product, the apply numpy's matrix-vector product, and L stays exactly symmetric."""
+    g = di.rng(81)
+    gv = g.integers(-8, 9, (3, 16)).astype(np.float64)
+    L0 = g.integers(-8, 9, (3, 16, 16)).astype(np.float64)
+    L0 = L0 + np.swapaxes(L0, 1, 2)
+    L = oracle.update_stats_vec(gv, 0.5, L0)
+    for p in range(3):
+        assert np.array_equal(L[p], 0.5 * L0[p] + 0.5 * np.outer(gv[p], gv[p]))
+        assert np.array_equal(L[p], L[p].T)
+    X = g.integers(-8, 9, (3, 16, 16)).astype(np.float64)
+    u = oracle.apply_vec(X, gv)
+    assert np.array_equal(u, np.einsum("pij,pj->pi", X, gv))
+    assert np.array_equal(oracle.apply_vec(np.stack([np.eye(16)] * 3), gv), gv)
+
+
+def test_ndb_inverse_sqrt_closed_form():
+    """One NDB call's Z, unscaled by s^{-1/2}, is A^{-1/2} = Q diag(lam^{-1/2}) Q^T (exact rational-free
+    closed form); a power-of-two scale of A and s scales X by the exact power of two."""
+    A, Q, lam = spd(82, 24, 0.05, 1.0)
+    X = oracle.ndb_inverse_sqrt(A, lam.max(), 20)
+    assert rel(X, (Q * lam[None, :] ** -0.5) @ Q.T) < 1e-12
+    X16 = oracle.ndb_inverse_sqrt(16 * A, 16 * lam.max(), 20)
+    assert np.array_equal(4 * X16, X)
