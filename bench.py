@@ -60,8 +60,9 @@ def parse():
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
                         "(the run that HBM traffic counters are collected on); cn16 / ndb / ndbsplit: "
                         "one CN fp16 / NDB fp32 / NDB split-product solve with its scaling (for kernel "
-                        "profiles); evd: one "
-                        "block-Jacobi eigendecomposition solve; adaptive: per-block stopping against "
+                        "profiles); evd: the "
+                        "block-Jacobi eigendecomposition solve in fp32 (with and without the refinement pass) "
+                        "and with binary16 operands in its first pass; adaptive: per-block stopping against "
                         "fixed step counts on a stack of two conditionings; ndb16: NDB with binary16 "
                         "iterates and 0-2 correction steps; bf16: CN and NDB with bfloat16 iterates "
                         "beside binary16; freq: the step at update frequencies f = 1, 2, 4, 8, each step "
@@ -420,8 +421,10 @@ def only_libref(torch, dev):
     print(json.dumps(out), flush=True)
 
 
-def evd_solve(dash, torch, A, N, B, dev, refine=0):
-    """One eigendecomposition solve; (ms, X, sweeps, status)."""
+def evd_solve(dash, torch, A, N, B, dev, refine=0, prec=None):
+    """One eigendecomposition solve (first pass in fp32, or with binary16 operands for prec =
+    DASH_FP16, which needs refine = 1); (ms, X, sweeps, status)."""
+    prec = dash.DASH_FP32 if prec is None else prec
     X = torch.empty_like(A)
     sweeps = torch.empty(N, dtype=torch.int32, device=dev)
     status = torch.empty(N, dtype=torch.int32, device=dev)
@@ -429,7 +432,7 @@ def evd_solve(dash, torch, A, N, B, dev, refine=0):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    dash.dash_inverse_root_evd(A, N, B, EVD_MAX_SWEEPS, refine, X, sweeps=sweeps, status=status, ws=ws)
+    dash.dash_inverse_root_evd_prec(A, N, B, EVD_MAX_SWEEPS, refine, prec, X, sweeps=sweeps, status=status, ws=ws)
     e1.record()
     torch.cuda.synchronize()
     del ws
@@ -450,14 +453,19 @@ def only_evd(dash, di, torch, dev):
     B = BLOCK
     N = 2 * di.num_tiles(di.llama_weight_shapes(LAYERS, D_MODEL, FFN), B)
     A = di.gram_stack_torch(N, B, seed=di.SEED_GRAM, device=dev, std=1e-3, eps=EPS)
-    evd_solve(dash, torch, A[:8].contiguous(), 8, B, dev)  # warm the kernels
-    ms, X, sweeps, status = evd_solve(dash, torch, A, N, B, dev)
-    sw = sweeps.cpu().numpy()
-    print(json.dumps({"mode": "evd", "N": N, "B": B, "ms": round(ms, 2), "blocks_per_s": round(N / (ms * 1e-3), 1),
-                      "sweeps": [int(sw.min()), float(sw.mean()), int(sw.max())],
-                      "status_nonzero": int((status != 0).sum()),
-                      "residual_blocks_0_last": [evd_residual(torch, A, X, 0), evd_residual(torch, A, X, N - 1)]}),
-          flush=True)
+    runs = [("fp32", 0, dash.DASH_FP32), ("fp32_refined", 1, dash.DASH_FP32), ("fp16_refined", 1, dash.DASH_FP16)]
+    for name, refine, prec in runs:
+        evd_solve(dash, torch, A[:8].contiguous(), 8, B, dev, refine, prec)  # warm the kernels
+        ms, X, sweeps, status = evd_solve(dash, torch, A, N, B, dev, refine, prec)
+        sw = sweeps.cpu().numpy()
+        print(json.dumps({"mode": "evd_" + name, "N": N, "B": B, "ms": round(ms, 2),
+                          "blocks_per_s": round(N / (ms * 1e-3), 1),
+                          "sweeps": [int(sw.min()), float(sw.mean()), int(sw.max())],
+                          "status_nonzero": int((status != 0).sum()),
+                          "residual_blocks_0_last": [evd_residual(torch, A, X, 0), evd_residual(torch, A, X, N - 1)]}),
+              flush=True)
+        del X, sweeps, status
+        torch.cuda.empty_cache()
 
 
 def only_ndb16(dash, di, torch, dev):
@@ -912,6 +920,15 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                        "sweeps_mean": round(float(sw.mean()), 2), "sweeps_max": int(sw.max()),
                        "status_nonzero": int((status != 0).sum()),
                        "residual_block0": evd_residual(torch, A, Xe, 0)}
+    del Xe
+    torch.cuda.empty_cache()
+    # the same with binary16 operands in the first pass's products, then the fp32 refinement pass
+    evd_ms, Xe, sweeps, status = evd_solve(dash, torch, A, N, B, dev, refine=1, prec=dash.DASH_FP16)
+    sw = sweeps.float()
+    res["evd_fp16_refined"] = {"ms": round(evd_ms, 1), "blocks_per_s": round(N / (evd_ms * 1e-3), 1),
+                               "sweeps_mean": round(float(sw.mean()), 2), "sweeps_max": int(sw.max()),
+                               "status_nonzero": int((status != 0).sum()),
+                               "residual_block0": evd_residual(torch, A, Xe, 0)}
     del Xe
     torch.cuda.empty_cache()
     # per-block solver choice: on the Gram stack (every block well conditioned) and after one EMA update

@@ -352,6 +352,24 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
                                   float* eigvals, int32_t* sweeps, int32_t* status, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* dash_inverse_root_evd with the arithmetic of its first pass chosen by prec ([PT] Resultados
+ * Experimentais: the eigendecomposition root, like the coupled Newton one, works with FP16 operands).
+ * DASH_FP32: the same as dash_inverse_root_evd.  DASH_FP16 (refine must be 1): in the first pass every
+ * product that rotates the off-pair blocks of A or the eigenvector estimate, M R with R a pair's
+ * accumulated rotation, is formed as M + M (R - I), the correction from binary16 operands on the
+ * binary16 matrix cores with fp32 accumulation, added to the fp32 M; A's tiles are scaled by a
+ * power of two per block first (the largest diagonal entry to at most 1) and R - I is stored in
+ * binary16 with a power-of-two scale per pair.  That pass also solves the 64 x 64 pair sub-problems
+ * in fp32 instead of fp64 and leaves pairs with |A_pq| <= 2^-11 sqrt(A_pp A_qq) alone (binary16's
+ * resolution).  The estimate then gets two Newton-Schulz steps instead of one, and the refinement
+ * pass (fp32 products, fp64 pair sub-problems, fp32 tolerance) forms H from the input again, so the
+ * result keeps fp32 accuracy; the binary16 pass makes the dense sweeps cheaper.  A and the estimate
+ * stay fp32 in memory.  Other arguments, outputs and workspace as dash_inverse_root_evd;
+ * DASH_ERR_INVALID_ARG for another prec or for DASH_FP16 with refine = 0. */
+dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine,
+                                       dash_prec prec, float* X, float* eigvals, int32_t* sweeps, int32_t* status,
+                                       void* ws, size_t ws_bytes, void* stream);
+
 /* Preconditioned update U_t = (XL_t G_t) XR_t for t < NG ([TG] body: the -1/4 powers of L and R
  * precondition the gradient).  XL, XR, G_stack, U_stack are [NG,B,B]; U_stack must not alias the
  * inputs.  ws holds one [NG,B,B] intermediate. */

@@ -65,6 +65,7 @@ def library() -> ctypes.CDLL:
             "dash_inverse_root_cheb": (st, [vp, vp, i64, i32, i32, f64, f64, vp, vp, vp, sz, vp]),
             "dash_inverse_root_cheb_prec": (st, [vp, vp, i64, i32, i32, f64, f64, st, vp, vp, vp, sz, vp]),
             "dash_inverse_root_evd": (st, [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "dash_inverse_root_evd_prec": (st, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dash_apply": (st, [vp, vp, vp, i64, i32, vp, vp, sz, vp]),
             "dash_apply_prec": (st, [vp, vp, vp, i64, i32, st, vp, vp, sz, vp]),
             "dash_inverse_root_cheb_blocks": (st, [vp, vp, i64, i32, i32, f64, vp, f32, f64, st, vp, vp, vp, vp, sz,
@@ -443,6 +444,18 @@ def dash_inverse_root_evd(A, N: int, B: int, max_sweeps: int, refine: int, X, ei
                                            a.ptr(X, "X", numel=N * B * B), a.ptr(eigvals, "eigvals", numel=N * B),
                                            a.ptr(sweeps, "sweeps", "int32", N), a.ptr(status, "status", "int32", N),
                                            a.ws(ws), _nbytes(ws), a.stream(stream)))
+
+
+def dash_inverse_root_evd_prec(A, N: int, B: int, max_sweeps: int, refine: int, prec: int, X, eigvals=None,
+                               sweeps=None, status=None, ws=None, stream=None):
+    a = _Args("dash_inverse_root_evd_prec")
+    _check("dash_inverse_root_evd_prec",
+           library().dash_inverse_root_evd_prec(a.ptr(A, "A", numel=N * B * B), N, B, max_sweeps, refine, prec,
+                                                a.ptr(X, "X", numel=N * B * B),
+                                                a.ptr(eigvals, "eigvals", numel=N * B),
+                                                a.ptr(sweeps, "sweeps", "int32", N),
+                                                a.ptr(status, "status", "int32", N), a.ws(ws), _nbytes(ws),
+                                                a.stream(stream)))
 
 
 def dash_apply(XL, XR, G_stack, NG: int, B: int, U_stack, ws=None, stream=None):

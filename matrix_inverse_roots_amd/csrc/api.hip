@@ -1197,8 +1197,18 @@ dash_status dash_inverse_root_cheb_blocks(const float* A, const float* s, int64_
 dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine, float* X,
                                   float* eigvals, int32_t* sweeps, int32_t* status, void* ws, size_t ws_bytes,
                                   void* stream) {
+  return dash_inverse_root_evd_prec(A, N, B, max_sweeps, refine, DASH_FP32, X, eigvals, sweeps, status, ws, ws_bytes,
+                                    stream);
+}
+
+dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine,
+                                       dash_prec prec, float* X, float* eigvals, int32_t* sweeps, int32_t* status,
+                                       void* ws, size_t ws_bytes, void* stream) {
   if (!A || !X || A == X || !aligned(A, 16) || !aligned(X, 16) || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (max_sweeps < 1 || max_sweeps > 100 || (refine != 0 && refine != 1)) return DASH_ERR_INVALID_ARG;
+  // the binary16 pass only finds the eigenvectors approximately; the fp32 pass must follow it
+  if (prec != DASH_FP32 && !(prec == DASH_FP16 && refine == 1)) return DASH_ERR_INVALID_ARG;
+  const bool half = prec == DASH_FP16;
   if ((eigvals && !aligned(eigvals, 4)) || (sweeps && !aligned(sweeps, 4)) || (status && !aligned(status, 4)))
     return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
@@ -1217,13 +1227,31 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
   jp.rot = (int32_t*)cv.take((size_t)N * (B / 64) * sizeof(int32_t));
   float* scale = (float*)cv.take((size_t)N * B * sizeof(float));
   jp.flags = (int32_t*)cv.take((size_t)N * 8 * sizeof(int32_t));
+  float* coef = (float*)cv.take((size_t)N * COEF_STRIDE * sizeof(float));
+  jp.rsc = (float*)cv.take((size_t)N * (B / 64) * sizeof(float));
   if (status) TRY(launch_fill_i32(status, N, 0, st));
   // pass 1 on a working copy of A held in X, eigenvectors accumulated in V
   TRY(hipMemcpyAsync(X, A, (size_t)N * B * B * sizeof(float), hipMemcpyDeviceToDevice, st));
   TRY(launch_identity(V, N, B, st));
   jp.A = X;
   jp.V = V;
+  if (half) {
+    // pass 1 with fp32 pair sub-problems; rotations below binary16's resolution are left to the
+    // refinement pass, which removes the binary16 rounding of the dense sweeps
+    // the dense working matrix's eigenvalues reach up to B times its largest diagonal entry: that
+    // entry maps to at most 1
+    TRY(launch_half_prescale(A, N, B, coef, st));
+    jp.half = true;
+    jp.pair_f32 = true;
+    jp.coef = coef;
+    jp.tol = 0x1p-11f;
+  }
   TRY(launch_jacobi(jp, st));
+  // pass 2 (if any) in fp32 throughout: its rotations between nearly equal eigenvalues are not small
+  // even when H is nearly diagonal, so binary16 corrections would cost the eigenvectors accuracy
+  jp.half = false;
+  jp.pair_f32 = false;
+  jp.tol = 0x1p-22f;
   EvdFinish fin;
   fin.N = N;
   fin.B = B;
@@ -1233,26 +1261,35 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
   fin.sweeps = sweeps;
   fin.status = status;
   if (refine) {
-    // V <- V (3I - V^T V) / 2, then H = V^T (A V) from the input A; pass 2 diagonalises H in T and
-    // rotates V, now held in X
+    // Newton-Schulz steps Q <- Q (3I - Q^T Q) / 2 on the eigenvector estimate (one after the fp32
+    // pass; two after the binary16 pass, whose estimate is orthogonal only to about 1e-2), then
+    // H = Q^T (A Q) from the input A; pass 2 diagonalises H in T and rotates Q
     Epilogue ns;
     ns.alpha = -0.5f;
     ns.gamma = 1.5f;
-    Product p1 = prod(V, V, T);
-    TRY(launch_gemm(&p1, 1, N, B, DASH_FP32, DASH_FP32, Trans::TN, true, ns, st));
-    Product p2 = prod(V, T, X);
-    TRY(launch_gemm(&p2, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
-    Product p3 = prod(A, X, V);
+    float* Q = V;     // current estimate
+    float* free = X;  // the working copy of pass 1 is no longer needed
+    for (int it = 0; it < (half ? 2 : 1); ++it) {
+      Product p1 = prod(Q, Q, T);
+      TRY(launch_gemm(&p1, 1, N, B, DASH_FP32, DASH_FP32, Trans::TN, true, ns, st));
+      Product p2 = prod(Q, T, free);
+      TRY(launch_gemm(&p2, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
+      float* tmp = Q;
+      Q = free;
+      free = tmp;
+    }
+    Product p3 = prod(A, Q, free);
     TRY(launch_gemm(&p3, 1, N, B, DASH_FP32, DASH_FP32, Trans::NN, false, Epilogue(), st));
-    Product p4 = prod(X, V, T);
+    Product p4 = prod(Q, free, T);
     TRY(launch_gemm(&p4, 1, N, B, DASH_FP32, DASH_FP32, Trans::TN, true, Epilogue(), st));
     jp.pass = 1;
     jp.A = T;
-    jp.V = X;
+    jp.V = Q;
     TRY(launch_jacobi(jp, st));
     fin.A = T;
-    fin.V = X;
-    fin.Y = V;
+    fin.V = Q;
+    // Y = Q diag(w^-1/8) must not be X, the output of the last product
+    fin.Y = Q == X ? free : Q;
   } else {
     fin.A = X;
     fin.V = V;

@@ -192,6 +192,9 @@ struct PowerPlan {
   float shift_mul = 0.f;
 };
 hipError_t launch_power_iteration(const PowerPlan& plan, hipStream_t stream);
+// coef[b][CO_P2] = 2^-e, coef[b][CO_P2INV] = 2^e with e = ceil(log2 max_j A_b[j][j]) (0, 0 when that
+// maximum is not finite and > 0): the largest diagonal entry maps into (1/2, 1]
+hipError_t launch_half_prescale(const float* A, int64_t N, int B, float* coef, hipStream_t stream);
 // Stochastic residual: r[b] = sqrt(mean_{j<k} ||(X_b^4 A_b - I) v_j||^2) over the k normalised
 // start vectors v_j (the columns of V0[B,k]), by five fp32 block-times-vectors passes (A, then X four
 // times).  Workspace pieces as for the power iteration (W, part, V0p).
@@ -224,7 +227,12 @@ struct JacobiPlan {
   float* V;
   float* R;         // [N, B/64, 64, 64]
   int32_t* rot;     // [N, B/64]
+  float* rsc = nullptr;  // with half: [N, B/64] power-of-two scales of the stored R - I
   int32_t* flags;   // [N, 8]
+  bool half = false;            // update products as corrections M (R - I) from binary16 operands (R then
+                                // holds (R - I)^T in binary16, scaled per pair by 1/rsc)
+  bool pair_f32 = false;        // with half: pair sub-problems solved in fp32 instead of fp64
+  const float* coef = nullptr;  // with half: per-block prescale (CO_P2, CO_P2INV), from launch_half_prescale
 };
 hipError_t launch_jacobi(const JacobiPlan& plan, hipStream_t stream);
 struct EvdFinish {

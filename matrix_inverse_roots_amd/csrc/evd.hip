@@ -18,6 +18,9 @@
 //   32x32x2 fp32 MFMA products from LDS.
 // - A matrix whose whole sweep needed no rotation is done: later launches return at once for it.
 //   An update whose pair rotations are all the identity is skipped.
+// - Binary16 first pass (optional): the update products are formed as fp32 corrections M (R - I)
+//   from binary16 operands (fp32 accumulation) and the pair sub-problems are solved in fp32; the
+//   refinement pass below, in fp32, must follow it.
 // - Refinement pass (optional, driven from api.hip): V is re-orthogonalised by one Newton-Schulz
 //   step, H = V^T A V is formed from the input A again, and the same sweeps run on H, rotating V.
 //   This discards the rounding that the first pass accumulated in the working matrix over its many
@@ -35,6 +38,8 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int JB = 32;         // column block width
 constexpr int JS = 2 * JB;     // sub-problem order: one pair of column blocks
@@ -84,11 +89,14 @@ inline int64_t xcd_grid(int64_t nb, int64_t per) { return (nb + 7) / 8 * 8 * per
 struct JacobiArgs {
   float* A;      // [N, B, B] working copy, diagonalised in place
   float* V;      // [N, B, B] accumulated rotations
-  float* R;      // [N, P, JS, JS] rotations of the current round
+  float* R;      // [N, P, JS, JS] rotations of the current round (binary16 pass: R^T in binary16)
   int32_t* rot;  // [N, P] pair p of the current round rotated something
+  float* rsc;    // binary16 pass: [N, P] power-of-two scale of pair p's stored R - I
   int32_t* flags;
+  const float* coef;  // binary16 pass: per-block prescale 2^-e (CO_P2) and 2^e (CO_P2INV)
   int64_t b0, nb;  // first matrix of this launch, matrices in it
   int B, K, P, round, sweep;
+  int half;        // binary16 operands in the update products
   float tol;
 };
 
@@ -96,10 +104,27 @@ struct JacobiArgs {
 // rate here) and are rounded to fp32 once, when written out: a rotation accumulated in fp32 over the
 // thousands of plane rotations of one visit drifts from orthogonality by ~sqrt(count) ulp,
 // and applying such a near-rotation to the off-pair blocks every round moves the eigenvalues.
+// The binary16 pass (its products round every operand to binary16 anyway) keeps them in fp32
+// (T = float): half the LDS bytes per access and twice the workgroups per compute unit.
+template <typename T>
+struct CS {
+  T c, s;
+};
+
+// |a_pq| > tol sqrt(a_pp a_qq): the pair is rotated (fp32: the square roots taken apart, so that the
+// product of two diagonal entries can neither overflow nor underflow)
+__device__ __forceinline__ bool needs_rotation(double app, double aqq, double apq, double tol) {
+  return fabs(apq) > tol * sqrt(fabs(app * aqq));
+}
+__device__ __forceinline__ bool needs_rotation(float app, float aqq, float apq, float tol) {
+  return fabsf(apq) > tol * (sqrtf(fabsf(app)) * sqrtf(fabsf(aqq)));
+}
+
+template <typename T>
 __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
-  __shared__ double S[JS * JP];
-  __shared__ double Q[JS * JP];
-  __shared__ double2 rot_cs[JS / 2];  // (c, s) of rotation k
+  __shared__ T S[JS * JP];
+  __shared__ T Q[JS * JP];
+  __shared__ CS<T> rot_cs[JS / 2];  // (c, s) of rotation k
   __shared__ int2 rot_pq[JS / 2];     // its index pair p < q
   __shared__ int rotated[MAX_INNER];
   __shared__ int round_rot[2];  // inner round r rotates something (parity of r)
@@ -130,31 +155,31 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
 #pragma unroll
   for (int u = 0; u < JS * JS / NTH; ++u) {
     const int e = tid + NTH * u, i = e >> 6, j = e & 63;
-    Q[i * JP + j] = i == j ? 1.0 : 0.0;
+    Q[i * JP + j] = i == j ? T(1) : T(0);
   }
   if (tid < MAX_INNER) rotated[tid] = 0;
   if (tid < 2) round_rot[tid] = 0;
   __syncthreads();
-  const double tol = a.tol;
+  const T tol = a.tol;
   for (int sw = 0; sw < MAX_INNER; ++sw) {
     for (int r = 0; r < JS - 1; ++r) {
       const int rr = sw * (JS - 1) + r;  // inner round count, for the flag parity
       if (tid < JS / 2) {
         const int u = seat(tid, r, JS), v = seat(JS - 1 - tid, r, JS);
         const int pp = u < v ? u : v, qq = u < v ? v : u;
-        const double app = S[pp * JP + pp], aqq = S[qq * JP + qq], apq = S[pp * JP + qq];
-        double c = 1.0, s = 0.0;
-        if (fabs(apq) > tol * sqrt(fabs(app * aqq))) {
+        const T app = S[pp * JP + pp], aqq = S[qq * JP + qq], apq = S[pp * JP + qq];
+        T c = 1, s = 0;
+        if (needs_rotation(app, aqq, apq, tol)) {
           // the rotation that zeroes entry (pp, qq): t = tan of its angle, the smaller root of
-          // t^2 + 2 theta t - 1 = 0
-          const double th = (aqq - app) / (2.0 * apq);
-          const double t = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(th * th + 1.0));
-          c = 1.0 / sqrt(t * t + 1.0);
+          // t^2 + 2 theta t - 1 = 0 (a theta whose square overflows gives t = 0: no rotation)
+          const T th = (aqq - app) / (T(2) * apq);
+          const T t = (th >= T(0) ? T(1) : T(-1)) / (fabs(th) + sqrt(th * th + T(1)));
+          c = T(1) / sqrt(t * t + T(1));
           s = t * c;
           rotated[sw] = 1;
           round_rot[rr & 1] = 1;
         }
-        rot_cs[tid] = make_double2(c, s);
+        rot_cs[tid] = CS<T>{c, s};
         rot_pq[tid] = make_int2(pp, qq);
       }
       __syncthreads();
@@ -168,10 +193,10 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
       if (any) {
         const int l = tid & 31, kb = tid >> 5;
         const int2 pql = rot_pq[l];
-        const double2 csl = rot_cs[l];
+        const CS<T> csl = rot_cs[l];
         int2 pqk[SU];
-        double2 csk[SU];
-        double x[SU][4];
+        CS<T> csk[SU];
+        T x[SU][4];
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
           pqk[u] = rot_pq[kb + 8 * u];
@@ -186,12 +211,12 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
-          const double cl = csl.x, sl = csl.y, ck = csk[u].x, sk = csk[u].y;
-          const double y00 = cl * x[u][0] - sl * x[u][1], y01 = sl * x[u][0] + cl * x[u][1];  // columns
-          const double y10 = cl * x[u][2] - sl * x[u][3], y11 = sl * x[u][2] + cl * x[u][3];
-          double z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;  // rows
-          double z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
-          if (kb + 8 * u == l && sl != 0.0) z01 = z10 = 0.0;  // the entry a rotation annihilates
+          const T cl = csl.c, sl = csl.s, ck = csk[u].c, sk = csk[u].s;
+          const T y00 = cl * x[u][0] - sl * x[u][1], y01 = sl * x[u][0] + cl * x[u][1];  // columns
+          const T y10 = cl * x[u][2] - sl * x[u][3], y11 = sl * x[u][2] + cl * x[u][3];
+          T z00 = ck * y00 - sk * y10, z10 = sk * y00 + ck * y10;  // rows
+          T z01 = ck * y01 - sk * y11, z11 = sk * y01 + ck * y11;
+          if (kb + 8 * u == l && sl != T(0)) z01 = z10 = T(0);  // the entry a rotation annihilates
           S[pqk[u].x * JP + pql.x] = z00;
           S[pqk[u].x * JP + pql.y] = z01;
           S[pqk[u].y * JP + pql.x] = z10;
@@ -202,8 +227,8 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
       if (any) {
         const int i = tid & 63, kb = tid >> 6;
         int2 pqk[QU];
-        double2 csk[QU];
-        double x0[QU], x1[QU];
+        CS<T> csk[QU];
+        T x0[QU], x1[QU];
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
           pqk[u] = rot_pq[kb + 4 * u];
@@ -216,8 +241,8 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
-          Q[i * JP + pqk[u].x] = csk[u].x * x0[u] - csk[u].y * x1[u];
-          Q[i * JP + pqk[u].y] = csk[u].y * x0[u] + csk[u].x * x1[u];
+          Q[i * JP + pqk[u].x] = csk[u].c * x0[u] - csk[u].s * x1[u];
+          Q[i * JP + pqk[u].y] = csk[u].s * x0[u] + csk[u].c * x1[u];
         }
       }
       __syncthreads();
@@ -234,14 +259,54 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
       *(f32x4*)(Ab + (int64_t)pidx(i, I, J) * B + pidx(4 * c4, I, J)) = v;
     }
   }
-  float* Rb = a.R + (b * a.P + p) * (int64_t)(JS * JS);
+  if (a.half) {
+    // (R - I)^T in binary16 (the update kernel reads both of its uses row-wise), scaled by the power
+    // of two 1/rsc that maps its largest entry into (1/2, 1]: entries far below binary16's normal
+    // range would otherwise be lost, and with them the small rotations of a converging block
+    __shared__ float wmax[NTH / 64];
+    float d[TV][4];
+    float mx = 0.f;
 #pragma unroll
-  for (int u = 0; u < TV; ++u) {
-    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
-    f32x4 v;
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (float)Q[i * JP + 4 * c4 + q];
-    *(f32x4*)(Rb + i * JS + 4 * c4) = v;
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * c4 + q;
+        d[u][q] = (float)(Q[c * JP + i] - (c == i ? T(1) : T(0)));
+        mx = fmaxf(mx, fabsf(d[u][q]));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    int ex = 0;
+    if (mx > 0.f && isfinite(mx)) {
+      const float mant = frexpf(mx, &ex);  // mx = mant 2^ex, mant in [1/2, 1)
+      if (mant == 0.5f) --ex;
+    }
+    const float down = ldexpf(1.f, -ex);
+    _Float16* Rh = (_Float16*)a.R + (b * a.P + p) * (int64_t)(JS * JS);
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+      f16x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (_Float16)(d[u][q] * down);
+      *(f16x4*)(Rh + i * JS + 4 * c4) = v;
+    }
+    if (tid == 0) a.rsc[b * a.P + p] = ldexpf(1.f, ex);
+  } else {
+    float* Rb = a.R + (b * a.P + p) * (int64_t)(JS * JS);
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (float)Q[i * JP + 4 * c4 + q];
+      *(f32x4*)(Rb + i * JS + 4 * c4) = v;
+    }
   }
   if (tid == 0) {
     a.rot[b * a.P + p] = rotated[0];
@@ -375,6 +440,177 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
   }
 }
 
+// The binary16 update: the same items as jacobi_update_kernel, each product written as a correction
+// M R = M + M (R - I) whose second term is formed on the binary16 matrix cores (32x32x16, fp32
+// accumulation) from operands rounded to binary16 as they are staged, and added to the fp32 M in
+// the epilogue.  The rounding error of a product is then a binary16 fraction of |M| |R - I|:
+// binary16's unit roundoff while the rotations are large (the first sweeps of a dense block), less
+// as they approach the identity.  It is not small enough for the refinement pass, whose rotations
+// between nearly equal eigenvalues stay large while H is nearly diagonal: that pass runs in fp32.
+// A_pq's operand is first scaled by the block's power-of-two 2^-e (its entries then lie within the
+// largest eigenvalue times 2^-e, far inside the binary16 range); R - I is stored scaled by a power
+// of two per pair (largest entry in (1/2, 1]) and the eigenvector tiles have entries in [-1, 1].  A and V stay fp32 in memory.  Operand
+// tiles sit in LDS row-wise along the summed index, so each lane reads 8 consecutive binary16
+// values per matrix-core step: X[i][k] for the left operand and Y^T[j][k] for the right one.
+constexpr int HP = JS + 8;  // binary16 LDS pitch: 144-byte rows keep 16-byte reads aligned
+
+// out = X Y^T over the 64-long index (X, Yt: 64 x 64 binary16 in LDS, pitch HP) -> the wave's
+// 32 x 32 quadrant.  Lane half h takes k = 32 h + 8 s .. 32 h + 8 s + 7 at step s: both operands use
+// the same k order, so the sum is over every k once.
+__device__ __forceinline__ f32x16 mm64h(const _Float16* X, const _Float16* Yt, int wm, int wn, int li, int h) {
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < JS / 16; ++s) {
+    const f16x8 xa = *(const f16x8*)&X[(wm * JB + li) * HP + JB * h + 8 * s];
+    const f16x8 yb = *(const f16x8*)&Yt[(wn * JB + li) * HP + JB * h + 8 * s];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, yb, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// a 64 x 64 fp32 tile (fetched by fetch_tile) times c, rounded to binary16 into LDS (pitch HP)
+__device__ __forceinline__ void stage_tile_h(_Float16* T, const f32x4 (&v)[TV], float c, int tid) {
+#pragma unroll
+  for (int u = 0; u < TV; ++u) {
+    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+    f16x4 hv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hv[q] = (_Float16)(v[u][q] * c);
+    *(f16x4*)&T[i * HP + 4 * c4] = hv;
+  }
+}
+
+constexpr int HV = JS * JS / 8 / NTH;  // 16-byte pieces per thread of a 64 x 64 binary16 tile
+
+// a 64 x 64 binary16 tile (row pitch JS in memory) through registers into LDS (pitch HP)
+__device__ __forceinline__ void fetch_rot_h(f16x8 (&v)[HV], const _Float16* src, int tid) {
+#pragma unroll
+  for (int u = 0; u < HV; ++u) {
+    const int e = tid + NTH * u, i = e >> 3, c8 = e & 7;
+    v[u] = *(const f16x8*)(src + i * JS + 8 * c8);
+  }
+}
+
+__device__ __forceinline__ void stage_rot_h(_Float16* T, const f16x8 (&v)[HV], int tid) {
+#pragma unroll
+  for (int u = 0; u < HV; ++u) {
+    const int e = tid + NTH * u, i = e >> 3, c8 = e & 7;
+    *(f16x8*)&T[i * HP + 8 * c8] = v[u];
+  }
+}
+
+// the fp32 tile (fetched by fetch_tile) into LDS with pitch JP
+__device__ __forceinline__ void stage_tile_f(float* T, const f32x4 (&v)[TV], int tid) {
+#pragma unroll
+  for (int u = 0; u < TV; ++u) {
+    const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[u][q];
+  }
+}
+
+// row of element r of this lane's accumulator in the wave's quadrant
+__device__ __forceinline__ int acc_row(int r, int wm, int h) { return wm * JB + 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__global__ __launch_bounds__(NTH) void jacobi_update_h_kernel(JacobiArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 X[JS * HP];   // left operand, then T^T
+  __shared__ __attribute__((aligned(16))) _Float16 Rq[JS * HP];  // (R_q - I)^T
+  __shared__ __attribute__((aligned(16))) _Float16 Rp[JS * HP];  // (R_p - I)^T
+  __shared__ float O[JS * JP];                                   // the fp32 input, then the result
+  const int P = a.P, B = a.B;
+  const int PA = P * (P - 1) / 2;
+  const int per = PA + P * (B / JS);
+  int64_t m;
+  int t;
+  if (!xcd_item(per, a.nb, m, t)) return;
+  const int64_t b = a.b0 + m;
+  if (a.flags[b * F_STRIDE + F_DONE]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const _Float16* Rh = (const _Float16*)a.R + b * P * (int64_t)(JS * JS);
+  if (t < PA) {
+    int p = 0;
+    while (t >= P - 1 - p) {
+      t -= P - 1 - p;
+      ++p;
+    }
+    const int q = p + 1 + t;
+    if (!a.rot[b * P + p] && !a.rot[b * P + q]) return;
+    int Ip, Jp, Iq, Jq;
+    pair_blocks(p, a.round, a.K, Ip, Jp);
+    pair_blocks(q, a.round, a.K, Iq, Jq);
+    float* Ab = a.A + b * (int64_t)B * B;
+    const float p2 = a.coef[b * COEF_STRIDE + CO_P2], p2inv = a.coef[b * COEF_STRIDE + CO_P2INV];
+    const float uq = p2inv * a.rsc[b * P + q], up = p2inv * a.rsc[b * P + p];  // powers of two
+    f32x4 va[TV];
+    f16x8 vq[HV], vp[HV];
+    fetch_tile(va, Ab, [&](int i) { return (int64_t)pidx(i, Ip, Jp) * B; }, [&](int c) { return pidx(c, Iq, Jq); },
+               tid);
+    fetch_rot_h(vq, Rh + q * JS * JS, tid);
+    fetch_rot_h(vp, Rh + p * JS * JS, tid);
+    stage_tile_h(X, va, p2, tid);
+    stage_tile_f(O, va, tid);
+    stage_rot_h(Rq, vq, tid);
+    stage_rot_h(Rp, vp, tid);
+    __syncthreads();
+    f32x16 acc = mm64h(X, Rq, wm, wn, li, h);  // 2^-e A_pq (R_q - I) / rsc_q
+    float tv[16];                               // T = A_pq R_q at this lane's elements
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tv[r] = O[acc_row(r, wm, h) * JP + wn * JB + li] + acc[r] * uq;
+    __syncthreads();
+    // (2^-e T)^T into X: element r of this lane is T[wm 32 + 8 (r/4) + 4 h + r%4][wn 32 + li], four
+    // rows in a row per group of r
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f16x4 hv;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) hv[q2] = (_Float16)(tv[4 * g + q2] * p2);
+      *(f16x4*)&X[(wn * JB + li) * HP + wm * JB + 8 * g + 4 * h] = hv;
+    }
+    __syncthreads();
+    acc = mm64h(Rp, X, wm, wn, li, h);  // 2^-e (R_p - I)^T T / rsc_p
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[acc_row(r, wm, h) * JP + wn * JB + li] = tv[r] + acc[r] * up;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TV; ++u) {
+      const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
+      f32x4 v, w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = O[i * JP + 4 * c4 + r];
+        w[r] = O[(4 * c4 + r) * JP + i];
+      }
+      *(f32x4*)(Ab + (int64_t)pidx(i, Ip, Jp) * B + pidx(4 * c4, Iq, Jq)) = v;
+      *(f32x4*)(Ab + (int64_t)pidx(i, Iq, Jq) * B + pidx(4 * c4, Ip, Jp)) = w;
+    }
+  } else {
+    t -= PA;
+    const int rb = t / P, q = t - rb * P;
+    if (!a.rot[b * P + q]) return;
+    int Iq, Jq;
+    pair_blocks(q, a.round, a.K, Iq, Jq);
+    float* Vb = a.V + b * (int64_t)B * B + (int64_t)rb * JS * B;
+    f32x4 vv[TV];
+    f16x8 vq[HV];
+    fetch_tile(vv, Vb, [&](int i) { return (int64_t)i * B; }, [&](int c) { return pidx(c, Iq, Jq); }, tid);
+    fetch_rot_h(vq, Rh + q * JS * JS, tid);
+    stage_tile_h(X, vv, 1.f, tid);
+    stage_tile_f(O, vv, tid);
+    stage_rot_h(Rq, vq, tid);
+    __syncthreads();
+    const f32x16 acc = mm64h(X, Rq, wm, wn, li, h);  // V_tile (R_q - I)
+    const float uq = a.rsc[b * P + q];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = acc_row(r, wm, h);
+      Vb[(int64_t)i * B + pidx(wn * JB + li, Iq, Jq)] = O[i * JP + wn * JB + li] + acc[r] * uq;
+    }
+  }
+}
+
 // Sweep bookkeeping, one thread per matrix.  sweep == 0: start of a pass (the first pass clears
 // the count of earlier sweeps, a later one adds the previous pass's sweeps to it).  sweep t >= 1
 // (sweep t-1 has completed): a matrix whose sweep t-1 rotated nothing is done; F_SWEEPS counts the
@@ -462,6 +698,8 @@ size_t evd_workspace_bytes(int64_t N, int B) {
   bytes += align_up((size_t)N * (B / JS) * sizeof(int32_t), 256);            // pair flags
   bytes += align_up((size_t)N * B * sizeof(float), 256);                     // column scales
   bytes += align_up((size_t)N * F_STRIDE * sizeof(int32_t), 256);            // flags
+  bytes += align_up((size_t)N * COEF_STRIDE * sizeof(float), 256);           // binary16 prescale
+  bytes += align_up((size_t)N * (B / JS) * sizeof(float), 256);              // binary16 R - I scales
   return bytes;
 }
 
@@ -481,11 +719,15 @@ hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
   a.V = p.V;
   a.R = p.R;
   a.rot = p.rot;
+  a.rsc = p.rsc;
   a.flags = p.flags;
   a.B = B;
   a.K = K;
   a.P = P;
   a.tol = p.tol;
+  a.half = p.half ? 1 : 0;
+  a.coef = p.coef;
+  if ((p.half && (!p.coef || !p.rsc)) || (p.pair_f32 && !p.half)) return hipErrorInvalidValue;
   // matrices per launch, so that a grid stays below 2^32 work-items
   const int64_t max_wg = 0xffffffffLL / NTH;
   const int64_t per_update = (int64_t)P * (P - 1) / 2 + (int64_t)P * (B / JS);
@@ -500,8 +742,15 @@ hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
         const int64_t nb = N - b0 < chunk ? N - b0 : chunk;
         a.b0 = b0;
         a.nb = nb;
-        hipLaunchKernelGGL(jacobi_pair_kernel, dim3((unsigned)xcd_grid(nb, P)), dim3(NTH), 0, stream, a);
-        hipLaunchKernelGGL(jacobi_update_kernel, dim3((unsigned)xcd_grid(nb, per_update)), dim3(NTH), 0, stream, a);
+        if (p.pair_f32)
+          hipLaunchKernelGGL(jacobi_pair_kernel<float>, dim3((unsigned)xcd_grid(nb, P)), dim3(NTH), 0, stream, a);
+        else
+          hipLaunchKernelGGL(jacobi_pair_kernel<double>, dim3((unsigned)xcd_grid(nb, P)), dim3(NTH), 0, stream, a);
+        if (p.half)
+          hipLaunchKernelGGL(jacobi_update_h_kernel, dim3((unsigned)xcd_grid(nb, per_update)), dim3(NTH), 0, stream,
+                             a);
+        else
+          hipLaunchKernelGGL(jacobi_update_kernel, dim3((unsigned)xcd_grid(nb, per_update)), dim3(NTH), 0, stream, a);
       }
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -691,6 +691,12 @@ void launch_step_depth(int depth, dim3 grid, hipStream_t stream, const PowerStep
     launch_step<TI, WAVES, 1>(grid, stream, a);
 }
 
+hipError_t launch_half_prescale(const float* A, int64_t N, int B, float* coef, hipStream_t stream) {
+  if (N < 1 || N > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(half_prescale_kernel, dim3((unsigned)N), dim3(256), 0, stream, A, N, B, coef);
+  return hipGetLastError();
+}
+
 hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   const bool wide = (p.B % 128 == 0);
   const int RT = wide ? 128 : 64;

@@ -84,15 +84,20 @@ def cheb(A, s, degree, lo, hi):
     return X, status
 
 
-def evd(A, max_sweeps=20, refine=0):
-    """(X, eigenvalues, sweeps, status) of the block-Jacobi eigendecomposition solver."""
+def evd(A, max_sweeps=20, refine=0, prec=None):
+    """(X, eigenvalues, sweeps, status) of the block-Jacobi eigendecomposition solver (prec None:
+    the fp32 entry point; else the entry point that takes the first pass's precision)."""
     N, B = A.shape[0], A.shape[1]
     X = torch.empty_like(A)
     w = torch.empty((N, B), device=DEV)
     sweeps = torch.empty(N, dtype=torch.int32, device=DEV)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=DEV)
-    dash.dash_inverse_root_evd(A, N, B, max_sweeps, refine, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
+    if prec is None:
+        dash.dash_inverse_root_evd(A, N, B, max_sweeps, refine, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
+    else:
+        dash.dash_inverse_root_evd_prec(A, N, B, max_sweeps, refine, prec, X, eigvals=w, sweeps=sweeps,
+                                        status=status, ws=ws)
     return X, w, sweeps, status
 
 

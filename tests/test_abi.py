@@ -176,6 +176,11 @@ def test_evd_argument_errors_and_counts():
     assert _status_of(f, P, N, 96, 10, 0, P2, ws=ws) == _lib.DASH_ERR_SHAPE
     assert _status_of(f, P, N, B, 10, 0, P2 + 4, ws=ws) == _lib.DASH_ERR_INVALID_ARG    # misaligned X
     assert _status_of(f, P, N, B, 10, 0, P2, ws=FakeWs(P3, ws.n - 1)) == _lib.DASH_ERR_WORKSPACE
+    g = dash.dash_inverse_root_evd_prec
+    assert _status_of(g, P, N, B, 10, 0, _lib.DASH_FP16, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG  # fp16 needs refine
+    for prec in (_lib.DASH_BF16, _lib.DASH_FP32_SPLIT, 7):
+        assert _status_of(g, P, N, B, 10, 1, prec, P2, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(g, P, N, B, 10, 1, _lib.DASH_FP16, P2, ws=FakeWs(P3, ws.n - 1)) == _lib.DASH_ERR_WORKSPACE
     # flops: one full sweep of updates per round (P(P-1)/2 blocks x 2 products + P * B/64 tiles) + Y Y^T
     Bf, Nf = 256, 3
     Pp = Bf // 64
