@@ -59,9 +59,10 @@ __device__ __forceinline__ void split3(const f32x4& lo, const f32x4& hi, bf16x8&
 // offsets (the loads here are untyped).
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 
-// LDS rows are 16 bfloat16 (two 16-byte chunks); rows 4..7 of every 8 swap their chunks so that the
-// 16-byte fragment reads of 8 consecutive rows hit distinct banks
-__device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1); }
+// LDS rows are 16 bfloat16 (two 16-byte chunks); a row swaps its chunks when bit 2 xor bit 3 of its
+// index is set, so that the 16-byte reads of 16 consecutive rows (one chunk each, the lanes the LDS
+// serves together) fall on 16 distinct 16-byte slots of its 64 banks
+__device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1) ^ ((row >> 3) & 1); }
 
 template <bool CHECKS, bool SYM, bool XT, bool YT, bool FOLD = false>
 __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
@@ -69,7 +70,12 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
   constexpr int PLANE = TILE * BK;  // bfloat16 of one piece plane of one operand slice
   constexpr int BUF = 6 * PLANE;    // X pieces 0..2, then Y pieces 0..2
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+  // the two stages of the double buffer are separate arrays: the stores of one stage and the
+  // reads of the other then provably do not alias, so the compiler may interleave the staging of
+  // slice k + 1 (split and LDS stores) with the products of slice k
+  __shared__ __attribute__((aligned(16))) __bf16 stage0[BUF];
+  __shared__ __attribute__((aligned(16))) __bf16 stage1[BUF];
+  auto smem_of = [&](int buf) -> __bf16* { return buf ? stage1 : stage0; };
 
   const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   const float xc = FOLD ? a.epi.c_over_a * coef_of(a.epi, a.epi.ic, tc.b) : 0.f;
   auto sstore = [&](auto slot_c, int buf, int k0) {
     constexpr int slot = decltype(slot_c)::value;
-    __bf16* s = smem + buf * BUF + xrow * BK + 8 * swz2(xrow, xch);
+    __bf16* s = smem_of(buf) + xrow * BK + 8 * swz2(xrow, xch);
     bf16x8 p0, p1, p2;
     if constexpr (FOLD) {  // element q of the piece sits on the diagonal when i0 + row == k0 + 8 ch + q
       const int d = i0 + srow - k0 - 8 * sch;
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
     *(bf16x8*)(s) = p0;
     *(bf16x8*)(s + PLANE) = p1;
     *(bf16x8*)(s + 2 * PLANE) = p2;
-    __bf16* t = smem + buf * BUF + 3 * PLANE + yrow * BK + 8 * swz2(yrow, ych);
+    __bf16* t = smem_of(buf) + 3 * PLANE + yrow * BK + 8 * swz2(yrow, ych);
     split3(ry[slot][0], ry[slot][1], p0, p1, p2);
     *(bf16x8*)(t) = p0;
     *(bf16x8*)(t + PLANE) = p1;
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   // one k-slice: lane half h takes k = 8h .. 8h + 7 of the slice for both operands; one right
   // piece at a time (its two fragments), each left piece read per use
   auto compute = [&](int buf) {
-    const __bf16* s = smem + buf * BUF;
+    const __bf16* s = smem_of(buf);
 #pragma unroll
     for (int pb = 0; pb < 3; ++pb) {
       bf16x8 bv[MTN];
