@@ -196,7 +196,7 @@ def main():
         mark(2)
         dash.dash_update_stats_prec(G_stack, NG, B, BETA, cheb_prec, A)
         mark(3)
-        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
+        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, cheb_prec, K_VEC, MPI_STEPS, V0, s, ws_scale)
         mark(4)
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, state["floor"], None, 1.0, CHEB_HI, cheb_prec, X,
                                           lo_out=lo_dev, ws=ws_cheb)
@@ -313,11 +313,12 @@ def main():
                                "power-iteration scale, Chebyshev d=24 A^-1/4 on per-block intervals, apply, unstack",
                    "N": N, "B": B, "tiles": NG,
                    "solver": "chebyshev-clenshaw d=24 fp32, interval [1e-6*0.95^t/s_i, 1.25] per block",
-                   "product_arithmetic": ("fp32 products (statistics, solve, apply) formed from exact three-piece "
-                                          "bfloat16 splits of both operands: six bfloat16 MFMA piece products per "
-                                          "fp32 product, fp32 accumulation" if args.prec == "split"
+                   "product_arithmetic": ("fp32 products (statistics, scale, solve, apply) formed from exact "
+                                          "three-piece bfloat16 splits of both operands: six bfloat16 MFMA piece "
+                                          "products per fp32 product, fp32 accumulation" if args.prec == "split"
                                           else "fp32 matrix cores (32x32x2 fp32 MFMA)"),
-                   "scale": "power iteration k=32 T=10 fp32", "beta": BETA},
+                   "scale": "power iteration k=32 T=10 fp32" + (" (split products)" if args.prec == "split" else ""),
+                   "beta": BETA},
         "step_accuracy": accuracy,
         "roofline": roofline,
         "breakdown": breakdown,

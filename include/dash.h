@@ -124,6 +124,10 @@ dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, 
  *     quotient of every column comes from the last step, each column is renormalised between
  *     steps, and s_i = max over columns.  prec == DASH_FP16 streams A_i in binary16 prescaled by
  *     2^-ceil(log2 max_j A_i[j][j]) and keeps V in binary16; accumulation stays fp32.
+ *     prec == DASH_FP32_SPLIT (B % 128 == 0): each step's product is formed from exact three-piece
+ *     bfloat16 splits of A_i and V on the bfloat16 matrix cores (six piece products, fp32
+ *     accumulation), an fp32 product at a fraction of the fp32 matrix cores' time; other B run
+ *     the DASH_FP32 step.  Workspace as DASH_FP32.
  *     V0 == NULL: the start pool is drawn on the device from `seed` (dash_start_vectors' values).
  * A block whose scale comes out non-finite or <= 0 is flagged later by the solver. */
 dash_status dash_scale(const float* A, int64_t N, int32_t B, dash_scaling how, dash_prec prec, int32_t k,

@@ -714,7 +714,7 @@ dash_status scale_args_check(const float* A, int64_t N, int32_t B, dash_scaling 
   if (how == DASH_SCALE_FROBENIUS) return DASH_OK;
   if (how != DASH_SCALE_POWER) return DASH_ERR_INVALID_ARG;
   if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;  // power iteration streams fp32 or binary16 operands
-  if (prec != DASH_FP32 && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
+  if (prec != DASH_FP32 && prec != DASH_FP32_SPLIT && prec != DASH_FP16) return DASH_ERR_INVALID_ARG;
   if (k < 1 || k > 32 || steps < 1 || steps > 10000 || !aligned(V0, 4)) return DASH_ERR_INVALID_ARG;
   return DASH_OK;
 }

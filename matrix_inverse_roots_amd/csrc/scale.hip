@@ -356,8 +356,25 @@ __global__ __launch_bounds__(64 * WAVES, 3) void power_step_f32(PowerStepArgs<fl
 // 8 consecutive floats of its column (two 16-byte loads), and its four tiles' outputs at one
 // accumulator position are four consecutive rows of one column (one 16-byte store).  Each wave's
 // 128 rows are one row block of the partial sums (RB = B / 128), reduced in the wave.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void power_step_stream(
-    PowerStepArgs<float> a) {
+// SPLIT: the same operands feed the 32x32x16 bfloat16 MFMA instead: a lane's eight rows kb + 8 h + p
+// of one column are exactly its eight k of that MFMA's left operand (and its eight consecutive
+// iterate values its right operand), each fp32 value cut into three bfloat16 pieces (x0 = bf16(x),
+// x1 = bf16(x - x0), x2 = bf16(x - x0 - x1), an exact cut), and the product is the sum of the six
+// piece products with i + j <= 2, each exact in the fp32 accumulator: fp32 products at 6/16 of the
+// fp32 MFMA time, so the step is left bound by its loads.  The pieces need 24 more registers than
+// four waves per SIMD allow; this form runs two.
+__device__ __forceinline__ void cut3(float x, gemm::bf16x8& p0, gemm::bf16x8& p1, gemm::bf16x8& p2, int i) {
+  const __bf16 x0 = (__bf16)x;
+  const float r1 = x - (float)x0;
+  const __bf16 x1 = (__bf16)r1;
+  p0[i] = x0;
+  p1[i] = x1;
+  p2[i] = (__bf16)(r1 - (float)x1);
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPLIT ? 2 : 4, SPLIT ? 2 : 4))) void
+power_step_stream(PowerStepArgs<float> a) {
   constexpr int D = 8;  // MFMA slots per k-block of 16 rows
   const int B = a.B;
   const int wpg = (int)(blockDim.x >> 6);
@@ -398,14 +415,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // by position (no register copies, which would wait for the loads)
   auto block = [&](int kb, auto q_c, bool reload_a, bool reload_v) {
     constexpr int q = decltype(q_c)::value;
+    if constexpr (SPLIT) {
+      gemm::bf16x8 b0, b1, b2;
 #pragma unroll
-    for (int p = 0; p < D; ++p) {
+      for (int p = 0; p < D; ++p) cut3(vb[q][p >> 2][p & 3] * inv, b0, b1, b2, p);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[p][t], vb[q][p >> 2][p & 3] * inv, acc[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+        gemm::bf16x8 a0, a1, a2;
+#pragma unroll
+        for (int p = 0; p < D; ++p) cut3(ra[p][t], a0, a1, a2, p);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b2, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b0, acc[t], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (reload_a) ra[p] = *(const f32x4*)(ap + (int64_t)(16 * (kb + 1) + p) * B);
+#pragma unroll
+      for (int p = 0; p < D; ++p)
+        if (reload_a) ra[p] = *(const f32x4*)(ap + (int64_t)(16 * (kb + 1) + p) * B);
       __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int p = 0; p < D; ++p) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[p][t], vb[q][p >> 2][p & 3] * inv, acc[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (reload_a) ra[p] = *(const f32x4*)(ap + (int64_t)(16 * (kb + 1) + p) * B);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (reload_v) {
       vb[q][0] = *(const f32x4*)(vp + 16 * (kb + 2));
@@ -706,7 +746,8 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
   hipError_t err;
   // fp32 on 128-row blocks: the streaming step (row k of the symmetric block read whole), whose
   // iterates are stored transposed, [KV][B] per block
-  const bool stream_f32 = p.prec == DASH_FP32 && wide;
+  const bool stream_f32 = p.prec != DASH_FP16 && wide;
+  const bool split = p.prec == DASH_FP32_SPLIT && wide;
   hipLaunchKernelGGL(v0_prepare_kernel, dim3(1), dim3(1024), 0, stream, p.V0, p.seed, p.B, p.k, p.V0p, stream_f32);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const float* coef = nullptr;
@@ -724,7 +765,7 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
     coef = p.coef;
   }
   // fp32 slices are 32 wide, binary16 slices 64 wide
-  const int depth = p.prec == DASH_FP32 ? ring_depth(p.B / 32, 4) : ring_depth(p.B / 64, 2);
+  const int depth = p.prec != DASH_FP16 ? ring_depth(p.B / 32, 4) : ring_depth(p.B / 64, 2);
   // waves per workgroup: the largest of 8, 4, 2, 1 dividing the block's 128-row blocks
   const int rbs = p.B / 128;
   const int wpg = !stream_f32 ? 1 : rbs % 8 == 0 ? 8 : rbs % 4 == 0 ? 4 : rbs % 2 == 0 ? 2 : 1;
@@ -748,8 +789,11 @@ hipError_t launch_power_iteration(const PowerPlan& p, hipStream_t stream) {
       PowerStepArgs<float> a;
       a.A = p.A;
       fill(a);
-      hipLaunchKernelGGL(power_step_stream, dim3((unsigned)sgrid), dim3(64 * wpg), 0, stream, a);
-    } else if (p.prec == DASH_FP32) {
+      if (split)
+        hipLaunchKernelGGL(power_step_stream<true>, dim3((unsigned)sgrid), dim3(64 * wpg), 0, stream, a);
+      else
+        hipLaunchKernelGGL(power_step_stream<false>, dim3((unsigned)sgrid), dim3(64 * wpg), 0, stream, a);
+    } else if (p.prec != DASH_FP16) {
       PowerStepArgs<float> a;
       a.A = p.A;
       fill(a);

@@ -276,7 +276,12 @@ def test_split_precision_queries_and_argument_errors():
         _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_apply_prec, P, P2, P3, N, B, dash.DASH_FP32_SPLIT, P, ws=ws) == \
         _lib.DASH_ERR_INVALID_ARG                                                           # U aliases XL
+    # the scale takes split products (past the precision check, a short workspace is what stops it)
     assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32_SPLIT, 8, 10, P2, P3,
+                      ws=FakeWs(4 * P, 256)) == _lib.DASH_ERR_WORKSPACE
+    assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, dash.DASH_BF16, 8, 10, P2, P3,
+                      ws=ws) == _lib.DASH_ERR_UNSUPPORTED
+    assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, 7, 8, 10, P2, P3,
                       ws=ws) == _lib.DASH_ERR_INVALID_ARG
 
 

@@ -283,3 +283,47 @@ def test_cn_split_fallback_bitwise():
         dash.dash_inverse_root_cn(Ad, s, 2, 320, 4, 6, prec, X, ws=ws)
         out.append(X)
     assert torch.equal(out[0], out[1])
+
+
+# ------------------------------------------------------------------------------------------------
+# power-iteration scale with split products (the streaming step, B % 128 == 0)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,N", [(128, 3), (256, 3), (1024, 2)])
+def test_power_scale_split_matches_oracle(B, N):
+    """The streaming step's products from three-piece bfloat16 splits: s against the oracle's fp64
+    power iteration at the fp32 gate, and within 2e-6 of the fp32 matrix cores' s; k = 5 leaves 27
+    zero columns of the iterate."""
+    A, Ad = spectrum_stack(700 + B, N, B)
+    for k in (32, 5):
+        V0 = di.start_vectors(B, k)
+        s = to_host(power_scale(Ad, to_dev(V0), 10, SPLIT))
+        s_ref, _ = oracle.mpi(A, V0, 10)
+        s32 = to_host(power_scale(Ad, to_dev(V0), 10, dash.DASH_FP32))
+        print("B", B, "k", k, "split rel err", np.max(np.abs(s - s_ref) / s_ref))
+        assert np.max(np.abs(s - s_ref) / s_ref) < 1e-5
+        assert np.max(np.abs(s - s32) / s32) < 2e-6
+
+
+def test_power_scale_split_conditioned_and_fallback(conditioned):
+    """kappa 1e4 at B = 256 against the oracle; B = 192 (no 128-row blocks) runs the fp32 step, bit
+    for bit."""
+    A, Ad = conditioned
+    V0 = di.start_vectors(256, 32)
+    s = to_host(power_scale(Ad, to_dev(V0), 10, SPLIT))
+    s_ref, _ = oracle.mpi(A, V0, 10)
+    assert np.max(np.abs(s - s_ref) / s_ref) < 1e-5
+    A2, Ad2 = spectrum_stack(790, 2, 192)
+    V2 = to_dev(di.start_vectors(192, 32))
+    assert torch.equal(power_scale(Ad2, V2, 10, SPLIT), power_scale(Ad2, V2, 10, dash.DASH_FP32))
+
+
+def test_power_scale_split_equivariance_and_independence():
+    """s(4 A) = 4 s(A) bitwise (the split of 4 x is 4 times the split of x), and a block alone gives
+    the s it gets inside a stack."""
+    A, Ad = spectrum_stack(795, 3, 256)
+    V0 = to_dev(di.start_vectors(256, 32))
+    s1 = power_scale(Ad, V0, 10, SPLIT)
+    s4 = power_scale(4.0 * Ad, V0, 10, SPLIT)
+    assert torch.equal(s4, 4.0 * s1)
+    assert torch.equal(power_scale(Ad[1:2].contiguous(), V0, 10, SPLIT), s1[1:2])
