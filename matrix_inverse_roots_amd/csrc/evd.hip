@@ -298,13 +298,14 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
     }
     if (tid == 0) a.rsc[b * a.P + p] = ldexpf(1.f, ex);
   } else {
+    // R^T, rounded to fp32: the update kernel reads both of its uses row-wise
     float* Rb = a.R + (b * a.P + p) * (int64_t)(JS * JS);
 #pragma unroll
     for (int u = 0; u < TV; ++u) {
       const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
       f32x4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = (float)Q[i * JP + 4 * c4 + q];
+      for (int q = 0; q < 4; ++q) v[q] = (float)Q[(4 * c4 + q) * JP + i];
       *(f32x4*)(Rb + i * JS + 4 * c4) = v;
     }
   }
@@ -314,28 +315,34 @@ __global__ __launch_bounds__(NTH) void jacobi_pair_kernel(JacobiArgs a) {
   }
 }
 
-// out = X Y (both 64 x 64 in LDS, pitch JP; TX: X read transposed) -> the wave's 32 x 32 quadrant
-template <bool TX>
-__device__ __forceinline__ f32x16 mm64(const float* X, const float* Y, int wm, int wn, int li, int h) {
+// The fp32 update products read both operands from LDS rows along the summed index k, 16 bytes at a
+// time: X[i][k] for the left operand, Y^T[j][k] for the right one (the pair kernel stores R^T, and
+// T = A_pq R_q is staged transposed from the accumulators).  Rows are FP = 68 floats: 16-byte reads
+// stay aligned, and the 16 rows the LDS serves together start 4 banks apart, covering its 64 banks.
+constexpr int FP = JS + 4;
+
+// out = X Y^T over the 64-long index (X, Yt: 64 x 64 fp32 in LDS, pitch FP) -> the wave's 32 x 32
+// quadrant, on the 32x32x2 fp32 MFMA: lane half h takes k = 32 h + 4 m + j at step (m, j), one
+// 16-byte read per operand feeding four MFMAs.
+__device__ __forceinline__ f32x16 mm64v(const float* X, const float* Yt, int wm, int wn, int li, int h) {
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  // lane half h takes k = 32 h + s at step s: the sum over k is the same, each read is one float
-#pragma unroll 8
-  for (int s = 0; s < JB; ++s) {
-    const int k = JB * h + s;
-    const float xa = TX ? X[k * JP + wm * JB + li] : X[(wm * JB + li) * JP + k];
-    const float yb = Y[k * JP + wn * JB + li];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, yb, acc, 0, 0, 0);
+  const float* xr = X + (wm * JB + li) * FP;
+  const float* yr = Yt + (wn * JB + li) * FP;
+#pragma unroll
+  for (int m = 0; m < JB / 4; ++m) {
+    const f32x4 xa = *(const f32x4*)(xr + JB * h + 4 * m);
+    const f32x4 yb = *(const f32x4*)(yr + JB * h + 4 * m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[j], yb[j], acc, 0, 0, 0);
   }
   return acc;
 }
 
-// the quadrant back into LDS (element r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32)
-__device__ __forceinline__ void store_quadrant(float* T, const f32x16& acc, int wm, int wn, int li, int h) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) T[(wm * JB + 8 * (r >> 2) + 4 * h + (r & 3)) * JP + wn * JB + li] = acc[r];
-}
+// row of element r of this lane's accumulator in the wave's quadrant (the 32x32 MFMA layout: element
+// r of lane l is row 8(r/4) + 4(l/32) + r%4, column l%32)
+__device__ __forceinline__ int acc_row(int r, int wm, int h) { return wm * JB + 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // A 64 x 64 fp32 tile through registers: piece u of this thread is row e/16, columns 4(e%16) ..
 // 4(e%16)+3 of the tile, e = tid + NTH u.  Row i of the tile is at src + row_off(i), its column c
@@ -349,21 +356,21 @@ __device__ __forceinline__ void fetch_tile(f32x4 (&v)[TV], const float* src, Row
   }
 }
 
-__device__ __forceinline__ void stage_tile(float* T, const f32x4 (&v)[TV], int tid) {
+// the tile (fetched by fetch_tile) into LDS rows of pitch FP
+__device__ __forceinline__ void stage_tile_v(float* T, const f32x4 (&v)[TV], int tid) {
 #pragma unroll
   for (int u = 0; u < TV; ++u) {
     const int e = tid + NTH * u, i = e >> 4, c4 = e & 15;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[u][q];
+    *(f32x4*)&T[i * FP + 4 * c4] = v[u];
   }
 }
 
 // Items of one matrix: P(P-1)/2 off-pair blocks A_pq (p < q), then P * B/64 tiles of V (64 rows
 // by one pair's 64 columns).
 __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
-  __shared__ float X[JS * JP];
-  __shared__ float R1[JS * JP];
-  __shared__ float R2[JS * JP];
+  __shared__ __attribute__((aligned(16))) float X[JS * FP];   // left operand, then T^T
+  __shared__ __attribute__((aligned(16))) float Rq[JS * FP];  // R_q^T, then the result (pitch JP)
+  __shared__ __attribute__((aligned(16))) float Rp[JS * FP];  // R_p^T
   const int P = a.P, B = a.B;
   const int PA = P * (P - 1) / 2;
   const int per = PA + P * (B / JS);
@@ -374,7 +381,9 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
   if (a.flags[b * F_STRIDE + F_DONE]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const float* Rm = a.R + b * P * (int64_t)(JS * JS);
+  const float* Rm = a.R + b * P * (int64_t)(JS * JS);  // R^T of every pair of the round
+  auto rot_row = [](int i) { return (int64_t)i * JS; };
+  auto rot_col = [](int c) { return c; };
   if (t < PA) {
     int p = 0;
     while (t >= P - 1 - p) {
@@ -387,24 +396,31 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
     pair_blocks(p, a.round, a.K, Ip, Jp);
     pair_blocks(q, a.round, a.K, Iq, Jq);
     float* Ab = a.A + b * (int64_t)B * B;
-    auto rot_row = [](int i) { return (int64_t)i * JS; };
-    auto rot_col = [](int c) { return c; };
     f32x4 va[TV], vq[TV], vp[TV];
     fetch_tile(va, Ab, [&](int i) { return (int64_t)pidx(i, Ip, Jp) * B; }, [&](int c) { return pidx(c, Iq, Jq); },
                tid);
     fetch_tile(vq, Rm + q * JS * JS, rot_row, rot_col, tid);
     fetch_tile(vp, Rm + p * JS * JS, rot_row, rot_col, tid);
-    stage_tile(X, va, tid);
-    stage_tile(R1, vq, tid);
-    stage_tile(R2, vp, tid);
+    stage_tile_v(X, va, tid);
+    stage_tile_v(Rq, vq, tid);
+    stage_tile_v(Rp, vp, tid);
     __syncthreads();
-    f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // T = A_pq R_q
+    f32x16 acc = mm64v(X, Rq, wm, wn, li, h);  // T = A_pq R_q
     __syncthreads();
-    store_quadrant(X, acc, wm, wn, li, h);
+    // T^T into X: element r of this lane is T[wm 32 + 8 (r/4) + 4 h + r%4][wn 32 + li], four
+    // consecutive rows per group of r
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) v[q2] = acc[4 * g + q2];
+      *(f32x4*)&X[(wn * JB + li) * FP + wm * JB + 8 * g + 4 * h] = v;
+    }
     __syncthreads();
-    acc = mm64<true>(R2, X, wm, wn, li, h);  // R_p^T T
-    __syncthreads();
-    store_quadrant(X, acc, wm, wn, li, h);
+    acc = mm64v(Rp, X, wm, wn, li, h);  // R_p^T T
+    float* O = Rq;  // R_q^T is dead: the result, pitch JP
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[acc_row(r, wm, h) * JP + wn * JB + li] = acc[r];
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < TV; ++u) {
@@ -412,8 +428,8 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
       f32x4 v, w;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = X[i * JP + 4 * c4 + r];
-        w[r] = X[(4 * c4 + r) * JP + i];
+        v[r] = O[i * JP + 4 * c4 + r];
+        w[r] = O[(4 * c4 + r) * JP + i];
       }
       *(f32x4*)(Ab + (int64_t)pidx(i, Ip, Jp) * B + pidx(4 * c4, Iq, Jq)) = v;
       *(f32x4*)(Ab + (int64_t)pidx(i, Iq, Jq) * B + pidx(4 * c4, Ip, Jp)) = w;
@@ -427,16 +443,13 @@ __global__ __launch_bounds__(NTH) void jacobi_update_kernel(JacobiArgs a) {
     float* Vb = a.V + b * (int64_t)B * B + (int64_t)rb * JS * B;
     f32x4 vv[TV], vq[TV];
     fetch_tile(vv, Vb, [&](int i) { return (int64_t)i * B; }, [&](int c) { return pidx(c, Iq, Jq); }, tid);
-    fetch_tile(vq, Rm + q * JS * JS, [](int i) { return (int64_t)i * JS; }, [](int c) { return c; }, tid);
-    stage_tile(X, vv, tid);
-    stage_tile(R1, vq, tid);
+    fetch_tile(vq, Rm + q * JS * JS, rot_row, rot_col, tid);
+    stage_tile_v(X, vv, tid);
+    stage_tile_v(Rq, vq, tid);
     __syncthreads();
-    const f32x16 acc = mm64<false>(X, R1, wm, wn, li, h);  // V_tile R_q
+    const f32x16 acc = mm64v(X, Rq, wm, wn, li, h);  // V_tile R_q
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = wm * JB + 8 * (r >> 2) + 4 * h + (r & 3);
-      Vb[(int64_t)i * B + pidx(wn * JB + li, Iq, Jq)] = acc[r];
-    }
+    for (int r = 0; r < 16; ++r) Vb[(int64_t)acc_row(r, wm, h) * B + pidx(wn * JB + li, Iq, Jq)] = acc[r];
   }
 }
 
@@ -510,9 +523,6 @@ __device__ __forceinline__ void stage_tile_f(float* T, const f32x4 (&v)[TV], int
     for (int q = 0; q < 4; ++q) T[i * JP + 4 * c4 + q] = v[u][q];
   }
 }
-
-// row of element r of this lane's accumulator in the wave's quadrant
-__device__ __forceinline__ int acc_row(int r, int wm, int h) { return wm * JB + 8 * (r >> 2) + 4 * h + (r & 3); }
 
 __global__ __launch_bounds__(NTH) void jacobi_update_h_kernel(JacobiArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 X[JS * HP];   // left operand, then T^T
