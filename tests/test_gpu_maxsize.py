@@ -44,9 +44,11 @@ def test_maxsize_scales(block):
     s10 = float(power_scale(A, V0, 10)[0])
     s3 = float(power_scale(A, V0, 3)[0])
     s16 = float(power_scale(A, V0, 10, dash.DASH_FP16)[0])
+    s_split = float(power_scale(A, V0, 10, dash.DASH_FP32_SPLIT)[0])
     assert s3 * (1 - 1e-6) <= s10 <= fro          # Rayleigh quotients grow with the steps, below ||A||_2
     assert s10 > 0.85 * (4 + SHIFT)                 # approaches the Marchenko-Pastur edge 4 + SHIFT
     assert abs(s16 - s10) <= 2e-3 * s10
+    assert abs(s_split - s10) <= 2e-6 * s10         # split products: an fp32 product
 
 
 def test_maxsize_ndb(block):
