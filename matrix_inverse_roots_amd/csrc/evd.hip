@@ -12,17 +12,19 @@
 //   sits in LDS (in fp64) and gets one sweep of scalar cyclic Jacobi (the same circle schedule on
 //   its 64 indices: 63 inner rounds of 32 disjoint rotations, each a classical rotation that zeroes
 //   one off-diagonal pair; pairs with |S_pq| <= tol sqrt(S_pp S_qq) are left alone).  The
-//   accumulated 64 x 64 rotation R_p goes to the workspace; the rotated S goes back to A.
+//   accumulated 64 x 64 rotation goes to the workspace transposed (R_p^T), the form the update
+//   kernel reads; the rotated S goes back to A.
 // - Update kernel, one workgroup per 64 x 64 output: the off-pair blocks become
 //   A_pq <- R_p^T A_pq R_q (mirrored into A_qp), and the eigenvector estimate V <- V R, as
-//   32x32x2 fp32 MFMA products from LDS.
+//   32x32x2 fp32 MFMA products from LDS rows along the summed index.
 // - A matrix whose whole sweep needed no rotation is done: later launches return at once for it.
 //   An update whose pair rotations are all the identity is skipped.
 // - Binary16 first pass (optional): the update products are formed as fp32 corrections M (R - I)
 //   from binary16 operands (fp32 accumulation) and the pair sub-problems are solved in fp32; the
 //   refinement pass below, in fp32, must follow it.
-// - Refinement pass (optional, driven from api.hip): V is re-orthogonalised by one Newton-Schulz
-//   step, H = V^T A V is formed from the input A again, and the same sweeps run on H, rotating V.
+// - Refinement pass (optional, driven from api.hip): V is re-orthogonalised by Newton-Schulz steps
+//   (one after an fp32 first pass, two after a binary16 one), H = V^T A V is formed from the input A
+//   again, and the same sweeps run on H, rotating V.
 //   This discards the rounding that the first pass accumulated in the working matrix over its many
 //   dense rounds, which dominates the error at high condition numbers.
 // - Finally w = diag(A), Y = V diag(w^{-1/8}) and X = Y Y^T (a triangle-only NT product: X comes
