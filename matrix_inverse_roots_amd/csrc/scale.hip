@@ -360,9 +360,9 @@ __global__ __launch_bounds__(64 * WAVES, 3) void power_step_f32(PowerStepArgs<fl
 // of one column are exactly its eight k of that MFMA's left operand (and its eight consecutive
 // iterate values its right operand), each fp32 value cut into three bfloat16 pieces (x0 = bf16(x),
 // x1 = bf16(x - x0), x2 = bf16(x - x0 - x1), an exact cut), and the product is the sum of the six
-// piece products with i + j <= 2, each exact in the fp32 accumulator: fp32 products at 6/16 of the
-// fp32 MFMA time, so the step is left bound by its loads.  The pieces need 24 more registers than
-// four waves per SIMD allow; this form runs two.
+// piece products with i + j <= 2, each exact in fp32 before it is accumulated: fp32 products at 6/16
+// of the fp32 MFMA time, so the step is left bound by its loads.  The pieces take the step to 148
+// registers, more than four waves per SIMD allow (128); this form runs two.
 __device__ __forceinline__ void cut3(float x, gemm::bf16x8& p0, gemm::bf16x8& p1, gemm::bf16x8& p2, int i) {
   const __bf16 x0 = (__bf16)x;
   const float r1 = x - (float)x0;
