@@ -220,7 +220,7 @@ def test_full_step_chebyshev(stack):
 
 def test_full_step_bench_sequence(stack):
     """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics (split
-    products) -> power scale -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
+    products) -> power scale (split products) -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
     (floor_t = 1e-6 * 0.95^t, the damping after t updates; split products) -> apply (split products).
     Sampled L and R blocks of one tile are recomputed by the oracle from the same starting blocks and
     gradient tiles through both steps (its own statistics, scale, interval and solve); every sampled
@@ -255,7 +255,7 @@ def test_full_step_bench_sequence(stack):
         floor *= 0.95
         dash.dash_stack(grads, B, G)
         dash.dash_update_stats_prec(G, NG, B, 0.95, split, A)
-        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, 32, 10, V0, s, ws_s)
+        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, split, 32, 10, V0, s, ws_s)
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, split, X, lo_out=lo,
                                           status=status, ws=ws_c)
         dash.dash_apply_prec(X[:NG], X[NG:], G, NG, B, split, U, ws_a)
@@ -280,22 +280,24 @@ def test_full_step_bench_sequence(stack):
     torch.cuda.empty_cache()
 
 
-def test_full_evd(stack):
-    """The block-Jacobi eigendecomposition on the full stack.  The fp64 oracle needs minutes per
-    1024-block, so here the checks are properties of every block: it converged (status 0), its
-    eigenvalues keep the block's trace and Frobenius norm (sum w = tr A, sum w^2 = ||A||_F^2,
-    evaluated in fp64), the residual holds, and X is exactly symmetric."""
+@pytest.mark.parametrize("prec,refine", [(dash.DASH_FP32, 0), (dash.DASH_FP16, 1)])
+def test_full_evd(stack, prec, refine):
+    """The block-Jacobi eigendecomposition on the full stack, in fp32 and with the binary16 first
+    pass (then the fp32 refinement pass).  The fp64 oracle needs minutes per 1024-block, so here the
+    checks are properties of every block: it converged (status 0), its eigenvalues keep the block's
+    trace and Frobenius norm (sum w = tr A, sum w^2 = ||A||_F^2, evaluated in fp64), the residual
+    holds at the fp32 gate, and X is exactly symmetric."""
     A, _ = stack
     X = torch.empty_like(A)
     w = torch.empty((N, B), device=DEV)
     sweeps = torch.empty(N, dtype=torch.int32, device=DEV)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_EVD, N, B, device=DEV)
-    dash.dash_inverse_root_evd(A, N, B, 20, 0, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
+    dash.dash_inverse_root_evd_prec(A, N, B, 20, refine, prec, X, eigvals=w, sweeps=sweeps, status=status, ws=ws)
     del ws
     torch.cuda.empty_cache()
     assert int(status.abs().sum()) == 0
-    assert int(sweeps.max()) < 20
+    assert int(sweeps.max()) < 20 * (1 + refine)
     for i in range(0, N, 256):
         a = A[i:i + 256].double()
         wd = w[i:i + 256].double()
