@@ -345,6 +345,8 @@ dash_status dash_inverse_root_routed(const float* A, const float* s, int64_t N, 
  * Newton-Schulz step, H = Q^T A_i Q is formed from the input again, and the sweeps run on H.  This
  * removes the rounding the first pass accumulates in its working matrix, which dominates the
  * error at high condition numbers (four more products and a few sweeps on a nearly diagonal H).
+ * Since the second pass starts from the input again, the first pass then solves its 64 x 64 pair
+ * sub-problems in fp32; the second pass keeps fp64 ones.
  * A: [N,B,B], symmetric, read in full.  max_sweeps: 1 .. 100 per pass.  X: [N,B,B], exactly
  * symmetric; it also holds working data during the call, so it must not alias A.
  * eigvals: NULL or [N,B] receives w (unordered; column j of Q belongs to w_j).
@@ -363,13 +365,13 @@ dash_status dash_inverse_root_evd(const float* A, int64_t N, int32_t B, int32_t 
  * accumulated rotation, is formed as M + M (R - I), the correction from binary16 operands on the
  * binary16 matrix cores with fp32 accumulation, added to the fp32 M; A's tiles are scaled by a
  * power of two per block first (the largest diagonal entry to at most 1) and R - I is stored in
- * binary16 with a power-of-two scale per pair.  That pass also solves the 64 x 64 pair sub-problems
- * in fp32 instead of fp64 and leaves pairs with |A_pq| <= 2^-11 sqrt(A_pp A_qq) alone (binary16's
- * resolution).  The estimate then gets two Newton-Schulz steps instead of one, and the refinement
- * pass (fp32 products, fp64 pair sub-problems, fp32 tolerance) forms H from the input again, so the
- * result keeps fp32 accuracy; the binary16 pass makes the dense sweeps cheaper.  A and the estimate
- * stay fp32 in memory.  Other arguments, outputs and workspace as dash_inverse_root_evd;
- * DASH_ERR_INVALID_ARG for another prec or for DASH_FP16 with refine = 0. */
+ * binary16 with a power-of-two scale per pair.  Like every first pass that a refinement pass
+ * follows, it solves the 64 x 64 pair sub-problems in fp32; it leaves pairs with
+ * |A_pq| <= 2^-11 sqrt(A_pp A_qq) alone (binary16's resolution).  The estimate then gets two
+ * Newton-Schulz steps instead of one, and the refinement pass (fp32 products, fp64 pair
+ * sub-problems, fp32 tolerance) forms H from the input again, so the result keeps fp32 accuracy.
+ * A and the estimate stay fp32 in memory.  Other arguments, outputs and workspace as
+ * dash_inverse_root_evd; DASH_ERR_INVALID_ARG for another prec or for DASH_FP16 with refine = 0. */
 dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int32_t max_sweeps, int32_t refine,
                                        dash_prec prec, float* X, float* eigvals, int32_t* sweeps, int32_t* status,
                                        void* ws, size_t ws_bytes, void* stream);

@@ -1235,6 +1235,9 @@ dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int
   TRY(launch_identity(V, N, B, st));
   jp.A = X;
   jp.V = V;
+  // a first pass that the refinement pass follows finds the eigenvectors only approximately: its
+  // pair sub-problems run in fp32 (the refinement pass forms H from A again and runs fp64 ones)
+  jp.pair_f32 = refine == 1;
   if (half) {
     // pass 1 with fp32 pair sub-problems; rotations below binary16's resolution are left to the
     // refinement pass, which removes the binary16 rounding of the dense sweeps
@@ -1242,7 +1245,6 @@ dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int
     // entry maps to at most 1
     TRY(launch_half_prescale(A, N, B, coef, st));
     jp.half = true;
-    jp.pair_f32 = true;
     jp.coef = coef;
     jp.tol = 0x1p-11f;
   }

@@ -231,7 +231,8 @@ struct JacobiPlan {
   int32_t* flags;   // [N, 8]
   bool half = false;            // update products as corrections M (R - I) from binary16 operands (R then
                                 // holds (R - I)^T in binary16, scaled per pair by 1/rsc)
-  bool pair_f32 = false;        // with half: pair sub-problems solved in fp32 instead of fp64
+  bool pair_f32 = false;        // pair sub-problems solved in fp32 instead of fp64 (a pass that a refinement
+                                // pass follows)
   const float* coef = nullptr;  // with half: per-block prescale (CO_P2, CO_P2INV), from launch_half_prescale
 };
 hipError_t launch_jacobi(const JacobiPlan& plan, hipStream_t stream);

@@ -20,8 +20,9 @@
 // - A matrix whose whole sweep needed no rotation is done: later launches return at once for it.
 //   An update whose pair rotations are all the identity is skipped.
 // - Binary16 first pass (optional): the update products are formed as fp32 corrections M (R - I)
-//   from binary16 operands (fp32 accumulation) and the pair sub-problems are solved in fp32; the
-//   refinement pass below, in fp32, must follow it.
+//   from binary16 operands (fp32 accumulation); the refinement pass below, in fp32, must follow it.
+// - A first pass that the refinement pass follows solves its pair sub-problems in fp32 (the
+//   refinement pass forms H from the input again and runs fp64 ones).
 // - Refinement pass (optional, driven from api.hip): V is re-orthogonalised by Newton-Schulz steps
 //   (one after an fp32 first pass, two after a binary16 one), H = V^T A V is formed from the input A
 //   again, and the same sweeps run on H, rotating V.
@@ -739,7 +740,7 @@ hipError_t launch_jacobi(const JacobiPlan& p, hipStream_t stream) {
   a.tol = p.tol;
   a.half = p.half ? 1 : 0;
   a.coef = p.coef;
-  if ((p.half && (!p.coef || !p.rsc)) || (p.pair_f32 && !p.half)) return hipErrorInvalidValue;
+  if (p.half && (!p.coef || !p.rsc)) return hipErrorInvalidValue;
   // matrices per launch, so that a grid stays below 2^32 work-items
   const int64_t max_wg = 0xffffffffLL / NTH;
   const int64_t per_update = (int64_t)P * (P - 1) / 2 + (int64_t)P * (B / JS);
