@@ -9,7 +9,9 @@ R statistics form an N=3072, B=1024 stack):
 
 Inputs are synthetic (seeded N(0, 1e-3^2) gradients, prior statistics G G^T/1024 + 1e-6 I) and are
 resident in HBM before timing starts.  The headline value is stacked blocks per second of the whole
-step.  The JSON line also carries the roofline of the dominant kernel (the fp32 MFMA product),
+step.  Every product is an fp32 product: the Chebyshev ones formed on the binary16 matrix cores from
+two-piece splits of both operands (--prec split16, the default), the others from exact three-piece
+bfloat16 splits.  The JSON line also carries the roofline of the dominant kernel (the Clenshaw product),
 the solve-only rates of the other two solver configurations (NDB fp32, CN fp16), of the block-Jacobi
 eigendecomposition they replace, and the CPU oracle timed on a bounded sample of the same workload.
 
@@ -40,10 +42,12 @@ FP16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 # the Clenshaw product kernel of each product arithmetic, and the sources its traffic record is keyed to
 PRODUCT_KERNELS = {
-    "split": ("gemm_split_kernel<false, true, false, false, true>", ("gemm_common.hpp", "gemm_split.hip")),
+    "split16": ("gemm_split_kernel<false, true, false, false, true, true>", ("gemm_common.hpp", "gemm_split.hip")),
+    "split": ("gemm_split_kernel<false, true, false, false, true, false>", ("gemm_common.hpp", "gemm_split.hip")),
     "fp32": ("gemm_f32_kernel<128, 0, 0, true, float, false, true, false, false>", ("gemm_common.hpp", "gemm_f32.hip")),
 }
-SPLIT_PIECE_PRODUCTS = 6  # bfloat16 piece products per fp32 product in the split kernel
+# 2-byte piece products per fp32 product: three-piece bfloat16 split (six), two-piece binary16 (three)
+PIECE_PRODUCTS = {"split": 6, "split16": 3}
 
 
 def parse():
@@ -69,10 +73,11 @@ def parse():
                         "refreshing the roots of 1/f of the stack; c2: steps to reach the residual 1e-3 "
                         "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
-    p.add_argument("--prec", choices=["split", "fp32"], default="split",
-                   help="arithmetic of the step's fp32 products (statistics, Chebyshev, apply): split "
-                        "(fp32 products formed from exact three-piece bfloat16 splits on the bfloat16 "
-                        "matrix cores) or fp32 (the fp32 matrix cores)")
+    p.add_argument("--prec", choices=["split16", "split", "fp32"], default="split16",
+                   help="arithmetic of the step's fp32 products: split16 (the Chebyshev products from "
+                        "two-piece binary16 splits on the binary16 matrix cores; statistics, scale and "
+                        "apply as split), split (every product from exact three-piece bfloat16 splits on "
+                        "the bfloat16 matrix cores) or fp32 (the fp32 matrix cores)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="update profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb "
                         "(for the --prec kernel)")
@@ -172,7 +177,8 @@ def main():
     s = torch.empty(N, device=dev)
     lo_dev = torch.empty(N, device=dev)
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    cheb_prec = dash.DASH_FP32_SPLIT if args.prec == "split" else dash.DASH_FP32  # every product of the step
+    prod_prec = dash.DASH_FP32 if args.prec == "fp32" else dash.DASH_FP32_SPLIT  # statistics, scale, apply
+    cheb_prec = dash.DASH_FP32_SPLIT16 if args.prec == "split16" else prod_prec
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
     torch.cuda.synchronize()
@@ -194,14 +200,14 @@ def main():
         mark(1)
         dash.dash_stack(grads, B, G_stack)
         mark(2)
-        dash.dash_update_stats_prec(G_stack, NG, B, BETA, cheb_prec, A)
+        dash.dash_update_stats_prec(G_stack, NG, B, BETA, prod_prec, A)
         mark(3)
-        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, cheb_prec, K_VEC, MPI_STEPS, V0, s, ws_scale)
+        dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prod_prec, K_VEC, MPI_STEPS, V0, s, ws_scale)
         mark(4)
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, state["floor"], None, 1.0, CHEB_HI, cheb_prec, X,
                                           lo_out=lo_dev, ws=ws_cheb)
         mark(5)
-        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, cheb_prec, U_stack, ws_apply)
+        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, prod_prec, U_stack, ws_apply)
         mark(6)
         dash.dash_unstack(U_stack, B, updates)
         mark(7)
@@ -246,15 +252,17 @@ def main():
         traffic_detail = {"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
                           "algorithmic_bytes": 4.0 * B * B * N * (3 + (B + 1) / (2.0 * B)),
                           "source": "profiles/traffic.json"}
-    if args.prec == "split":
-        # the matrix cores run six bfloat16 piece products per fp32 product: the roof is the dense
-        # bfloat16 MFMA peak, against the piece products' algorithmic flops
-        achieved = SPLIT_PIECE_PRODUCTS * fp32_equiv
+    if args.prec in PIECE_PRODUCTS:
+        # the matrix cores run six bfloat16 (or three binary16) piece products per fp32 product: the
+        # roof is the dense 2-byte MFMA peak, against the piece products' algorithmic flops
+        pieces = PIECE_PRODUCTS[args.prec]
+        achieved = pieces * fp32_equiv
         roofline = {"kernel": kernel_name, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
                     "flop_accounting": "algorithmic: B^2 (B+1) flop per block per symmetric fp32 product, times "
-                                       "the six bfloat16 piece products that form it",
-                    "frac_tiles": round(SPLIT_PIECE_PRODUCTS * fp32_equiv_tiles / FP16_PEAK_TFLOPS, 4),
+                                       "the %s piece products that form it"
+                                       % ("three binary16" if args.prec == "split16" else "six bfloat16"),
+                    "frac_tiles": round(pieces * fp32_equiv_tiles / FP16_PEAK_TFLOPS, 4),
                     "fp32_product_tflops": round(fp32_equiv, 2),
                     "fp32_product_frac_of_fp32_peak": round(fp32_equiv / FP32_PEAK_TFLOPS, 4)}
     else:
@@ -307,17 +315,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 via bf16x3 split" if args.prec == "split" else "f32",
+        "dtype": {"split16": "f32 via f16x2 (Chebyshev) and bf16x3 splits", "split": "f32 via bf16x3 split",
+                  "fp32": "f32"}[args.prec],
         "data": "synthetic",
         "config": {"workload": "llama-2048 Shampoo step f=1 on fresh gradients: stack, EMA stats, "
                                "power-iteration scale, Chebyshev d=24 A^-1/4 on per-block intervals, apply, unstack",
                    "N": N, "B": B, "tiles": NG,
                    "solver": "chebyshev-clenshaw d=24 fp32, interval [1e-6*0.95^t/s_i, 1.25] per block",
-                   "product_arithmetic": ("fp32 products (statistics, scale, solve, apply) formed from exact "
-                                          "three-piece bfloat16 splits of both operands: six bfloat16 MFMA piece "
-                                          "products per fp32 product, fp32 accumulation" if args.prec == "split"
-                                          else "fp32 matrix cores (32x32x2 fp32 MFMA)"),
-                   "scale": "power iteration k=32 T=10 fp32" + (" (split products)" if args.prec == "split" else ""),
+                   "product_arithmetic": {
+                       "split16": "fp32 products, fp32 accumulation; Chebyshev: two-piece binary16 splits of both "
+                                  "operands after a power of two per block (three binary16 MFMA piece products per "
+                                  "fp32 product); statistics, scale, apply: exact three-piece bfloat16 splits (six "
+                                  "bfloat16 MFMA piece products)",
+                       "split": "fp32 products (statistics, scale, solve, apply) formed from exact three-piece "
+                                "bfloat16 splits of both operands: six bfloat16 MFMA piece products per fp32 "
+                                "product, fp32 accumulation",
+                       "fp32": "fp32 matrix cores (32x32x2 fp32 MFMA)"}[args.prec],
+                   "scale": "power iteration k=32 T=10 fp32" + (" (split products)" if args.prec != "fp32" else ""),
                    "beta": BETA},
         "step_accuracy": accuracy,
         "roofline": roofline,
@@ -344,7 +358,7 @@ def only_cheb(dash, di, torch, dev, args):
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
     del ws
     X = torch.empty_like(A)
-    prec = dash.DASH_FP32_SPLIT if args.prec == "split" else dash.DASH_FP32
+    prec = {"split16": dash.DASH_FP32_SPLIT16, "split": dash.DASH_FP32_SPLIT, "fp32": dash.DASH_FP32}[args.prec]
     ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
     ref = [torch.ones((4096, 4096), device=dev) for _ in range(REF_COPY_BYTES // (4096 * 4096 * 4))]
     ref_stack = torch.empty((REF_COPY_BYTES // (B * B * 4), B, B), device=dev)
@@ -585,12 +599,13 @@ def only_freq(dash, di, torch, dev):
     U_stack = torch.empty((NG, B, B), device=dev)
     X = torch.empty((N, B, B), device=dev)
     s = torch.empty(N, device=dev)
-    prec = dash.DASH_FP32_SPLIT
+    prec = dash.DASH_FP32_SPLIT          # statistics and apply
+    cheb_prec = dash.DASH_FP32_SPLIT16   # the Chebyshev products, as in the f = 1 step
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
+    ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
-    dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, EPS, None, 1.0, CHEB_HI, prec, X,
+    dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, EPS, None, 1.0, CHEB_HI, cheb_prec, X,
                                       ws=ws_cheb)  # roots of step 0
     torch.cuda.synchronize()
     state = {"floor": EPS}
@@ -607,11 +622,12 @@ def only_freq(dash, di, torch, dev):
         dash.dash_scale(A[o:o + n], n, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s[o:o + n],
                         ws_scale)
         dash.dash_inverse_root_cheb_blocks(A[o:o + n], s[o:o + n], n, B, CHEB_DEGREE, state["floor"], None, 1.0,
-                                          CHEB_HI, prec, X[o:o + n], ws=ws_cheb)
+                                          CHEB_HI, cheb_prec, X[o:o + n], ws=ws_cheb)
         dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, prec, U_stack, ws_apply)
         dash.dash_unstack(U_stack, B, updates)
 
-    out = {"mode": "freq", "N": N, "B": B, "solver": "chebyshev-clenshaw d=%d fp32 (split products)" % CHEB_DEGREE}
+    out = {"mode": "freq", "N": N, "B": B,
+           "solver": "chebyshev-clenshaw d=%d fp32 (two-piece binary16 products)" % CHEB_DEGREE}
     for f in (1, 2, 4, 8):
         for i in range(f):
             step(i, f)
@@ -856,7 +872,7 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
     fl = dash.dash_flops(dash.DASH_OP_NDB, N, B, dash.DASH_FP32_SPLIT, NDB_ITERS, NDB_ITERS) / (nds_ms * 1e-3) / 1e12
     res["ndb_split"] = {"iters": [NDB_ITERS, NDB_ITERS], "ms": round(nds_ms, 2),
                         "blocks_per_s": round(N / (nds_ms * 1e-3), 1), "fp32_product_tflops": round(fl, 2),
-                        "bf16_mfma_frac": round(SPLIT_PIECE_PRODUCTS * fl / FP16_PEAK_TFLOPS, 4),
+                        "bf16_mfma_frac": round(PIECE_PRODUCTS["split"] * fl / FP16_PEAK_TFLOPS, 4),
                         "residual_block0": evd_residual(torch, A, X, 0)}
     # CN fp16 after binary16 power-iteration scaling
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, K_VEC, device=dev)
@@ -897,7 +913,8 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                                "residual_block0": evd_residual(torch, A, X, 0)}
     # Chebyshev d=24 solve-only, fp32 matrix cores against split products (same power-iteration scale)
     # (the Gram stack carries EPS I: every block's interval is [EPS / s_i, 1.25])
-    for name, prec in (("cheb_fp32", dash.DASH_FP32), ("cheb_split", dash.DASH_FP32_SPLIT)):
+    for name, prec in (("cheb_fp32", dash.DASH_FP32), ("cheb_split", dash.DASH_FP32_SPLIT),
+                       ("cheb_split16", dash.DASH_FP32_SPLIT16)):
         ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=dev)
         ch_ms = timed(lambda: dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, EPS, None, 1.0, CHEB_HI, prec,
                                                                  X, ws=ws))

@@ -59,8 +59,14 @@ typedef enum {
  * accumulation; as accurate as an fp32 product); accepted by dash_inverse_root_cheb_prec,
  * dash_inverse_root_ndb_prec, dash_inverse_root_cn, dash_update_stats_prec and dash_apply_prec, by
  * dash_workspace_size (as DASH_FP32) and by dash_flops (DASH_OP_CHEB then counts 256-wide tiles
- * for degree >= 3 and B % 256 == 0). */
-typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3 } dash_prec;
+ * for degree >= 3 and B % 256 == 0).
+ * DASH_FP32_SPLIT16: fp32 operands, iterates and results, with each product formed on the binary16
+ * matrix cores from two-piece binary16 splits of both operands, each brought near 8 by a power of
+ * two per block first (three piece products, fp32 accumulation; the pieces hold 22 of an fp32
+ * value's 24 significant bits, and the product's error, measured against fp64, is that of an fp32
+ * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec and
+ * dash_inverse_root_cheb_blocks), dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
+typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3, DASH_FP32_SPLIT16 = 4 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
 
@@ -246,8 +252,11 @@ dash_status dash_inverse_root_cheb(const float* A, const float* s, int64_t N, in
  * cores; the same as dash_inverse_root_cheb) or DASH_FP32_SPLIT (fp32 products formed from exact
  * three-piece bfloat16 splits on the bfloat16 matrix cores, 256 x 256 tiles, when B % 256 == 0 and
  * degree >= 3; the recurrence's C term enters as a shift of A's diagonal; with other B or degree 2
- * the fp32 matrix cores).  Same arguments, workspace and results contract otherwise;
- * DASH_ERR_INVALID_ARG for any other prec. */
+ * the fp32 matrix cores) or DASH_FP32_SPLIT16 (the same tiles and shapes with two-piece binary16
+ * splits on the binary16 matrix cores: each product's operands are scaled by a power of two per
+ * block from a bound on their magnitude, max |A_i| from a pass over the stack and max |b_k| from
+ * the launch that wrote b_k; with other B or degree 2 the fp32 matrix cores).  Same arguments,
+ * workspace and results contract otherwise; DASH_ERR_INVALID_ARG for any other prec. */
 dash_status dash_inverse_root_cheb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t degree,
                                         double lo, double hi, dash_prec prec, float* X, int32_t* status, void* ws,
                                         size_t ws_bytes, void* stream);

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libdash.so")
 
 DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_SHAPE, DASH_ERR_WORKSPACE, DASH_ERR_UNSUPPORTED, DASH_ERR_DEVICE = range(6)
-DASH_FP32, DASH_FP16, DASH_BF16, DASH_FP32_SPLIT = 0, 1, 2, 3
+DASH_FP32, DASH_FP16, DASH_BF16, DASH_FP32_SPLIT, DASH_FP32_SPLIT16 = 0, 1, 2, 3, 4
 DASH_SCALE_FROBENIUS, DASH_SCALE_POWER = 0, 1
 (DASH_OP_SCALE, DASH_OP_NDB, DASH_OP_CN, DASH_OP_CHEB, DASH_OP_APPLY, DASH_OP_STATS, DASH_OP_EVD,
  DASH_OP_ROUTED) = range(8)

@@ -74,7 +74,12 @@ size_t ws_ndb_half(int64_t N, int B) {
 }
 size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, p); }
 size_t cheb_tab_bytes(int64_t N);
-size_t ws_cheb(int64_t N, int B) { return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32); }
+// per-block magnitude bounds of the two-piece binary16 Clenshaw products: max |A| and three
+// rotating slots for max |b_k|
+size_t amax_bytes(int64_t N) { return align_up((size_t)N * 4 * sizeof(float), 256); }
+size_t ws_cheb(int64_t N, int B) {
+  return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32) + amax_bytes(N);
+}
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
 size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
 size_t ws_scale(int64_t N, int B, dash_prec p, int k) { return k == 0 ? 0 : power_workspace_bytes(N, B, p); }
@@ -368,7 +373,7 @@ size_t cheb_tab_bytes(int64_t N) {
 dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t degree, const ChebInterval& iv,
                       dash_prec prec, float* X, float* lo_out, int32_t* status, void* ws, size_t ws_bytes,
                       void* stream) {
-  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (X == A || degree < 1 || degree > CHEB_MAX_DEGREE) return DASH_ERR_INVALID_ARG;
@@ -381,12 +386,28 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   float* tab = (float*)cv.take(cheb_tab_bytes(N));
   float* b1 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
   float* b2 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
+  float* amax = (float*)cv.take(amax_bytes(N));
   const int d = degree;
   // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
   // stored mirrored; the first product maps A on the fp32 cores unless it can be written as
   // (alpha a1/s)(A + c I) A (degree >= 3), which the split kernel forms with A read by columns
-  const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
+  const bool split = (prec == DASH_FP32_SPLIT || prec == DASH_FP32_SPLIT16) && B % 256 == 0;
   const bool split_first = split && d >= 3;
+  // two-piece binary16 products (from the first product on, degree >= 3): launch q scales its left
+  // operand A + c I by max |A| + |c| and its right one by max |A| (q = 0) or by the maximum that
+  // launch q - 1 gathered into slot (q - 1) % 3; it gathers its own into slot q % 3 and clears slot
+  // (q + 1) % 3, which launch q - 2 filled and launch q - 1 read
+  const bool h2 = split_first && prec == DASH_FP32_SPLIT16;
+  const dash_prec sp_prec = h2 ? DASH_FP32_SPLIT16 : DASH_FP32_SPLIT;
+  float* amax_a = amax;
+  auto slot = [&](int q) { return amax + N * (1 + q % 3); };
+  auto bounds = [&](Product& pr, int q, bool last) {
+    if (!h2) return;
+    pr.amax_x = amax_a;
+    pr.amax_y = q == 0 ? amax_a : slot(q - 1);
+    pr.amax_d = last ? nullptr : slot(q);
+    pr.amax_zero = last ? nullptr : slot(q + 1);
+  };
   if (status) TRY(launch_fill_i32(status, N, 0, st));
   TRY(launch_coef(s, N, coef, status, st));
   {
@@ -440,13 +461,18 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   };
   auto run = [&](Product& pr, const Epilogue& e) {
     const bool sp = split && !pr.map_y;
-    return launch_gemm(&pr, 1, N, B, sp ? DASH_FP32_SPLIT : DASH_FP32, DASH_FP32, Trans::NN, true, e, st, sp);
+    return launch_gemm(&pr, 1, N, B, sp ? sp_prec : DASH_FP32, DASH_FP32, Trans::NN, true, e, st, sp);
   };
+  if (h2) {
+    TRY(launch_block_amax(A, N, B, amax_a, st));
+    TRY(launch_fill_f32(slot(0), N, 0.f, st));
+  }
   // the first product: k = d - 2 (or the final one when d == 2); b_{k+2} = b_d = c_d I rides in gamma
   if (split_first) {
     Product pr = prod(A, A, b2, A);
+    bounds(pr, 0, false);
     Epilogue e = epi(0, false);
-    TRY(launch_gemm(&pr, 1, N, B, DASH_FP32_SPLIT, DASH_FP32, Trans::NN, true, e, st, false));
+    TRY(launch_gemm(&pr, 1, N, B, sp_prec, DASH_FP32, Trans::NN, true, e, st, false));
   } else {
     const bool last = (d == 2);
     Product pr = prod(A, A, last ? (void*)X : (void*)b2, A, nullptr);
@@ -463,6 +489,7 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   {
     const bool last = (d == 3);
     Product pr = prod(A, b2, last ? (void*)X : (void*)b1, b2, A);
+    bounds(pr, 1, last);
     TRY(run(pr, epi(1, last)));
     if (last) return DASH_OK;
   }
@@ -471,10 +498,12 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   int q = 2;
   for (int k = d - 4; k >= 1; --k, ++q) {
     Product pr = prod(A, b1, b2, b1, b2);
+    bounds(pr, q, false);
     TRY(run(pr, epi(q, false)));
     std::swap(b1, b2);
   }
   Product pr = prod(A, b1, X, b1, b2);
+  bounds(pr, q, true);
   TRY(run(pr, epi(q, true)));
   return DASH_OK;
 }
@@ -596,6 +625,7 @@ int64_t dash_solver_products(dash_op op, int32_t iters1, int32_t iters2) {
 }
 
 double dash_flops(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t a1, int32_t a2) {
+  if (prec == DASH_FP32_SPLIT16) prec = DASH_FP32_SPLIT;  // the same tiles
   if (!valid_N(N) || !valid_B(B) || (!fp32_prec(prec) && !half_prec(prec))) return -1.0;
   const bool split = prec == DASH_FP32_SPLIT && B % 256 == 0;
   if (prec == DASH_FP32_SPLIT) prec = DASH_FP32;
@@ -642,8 +672,8 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
                                 size_t* bytes) {
   if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
-  if (!fp32_prec(prec) && !half_prec(prec)) return DASH_ERR_INVALID_ARG;
-  if (prec == DASH_FP32_SPLIT) prec = DASH_FP32;
+  if (!fp32_prec(prec) && !half_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
+  if (prec == DASH_FP32_SPLIT || prec == DASH_FP32_SPLIT16) prec = DASH_FP32;
   switch (op) {
     case DASH_OP_SCALE:
       if (prec == DASH_BF16) return DASH_ERR_UNSUPPORTED;

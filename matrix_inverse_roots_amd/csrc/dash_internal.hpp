@@ -80,6 +80,13 @@ struct Product {
   int8_t map_ia = CO_NONE, map_ig = CO_NONE;
   const int32_t* freeze = nullptr;
   int8_t pass = 0;
+  // two-piece binary16 products (DASH_FP32_SPLIT16), per block [N]: bounds on |X| and |Y|, the
+  // maximum |D| gathered by atomicMax (must hold 0 when the launch starts; null: not gathered), and
+  // a slot that the launch clears for a later one (null: none)
+  const float* amax_x = nullptr;
+  const float* amax_y = nullptr;
+  float* amax_d = nullptr;
+  float* amax_zero = nullptr;
 };
 
 enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed
@@ -121,6 +128,8 @@ hipError_t launch_coef(const float* s, int64_t N, float* coef, int32_t* status, 
 
 // Fill n floats / int32 with a value (a kernel, never a memset node).
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+// out[b] = max_ij |A_b[i][j]| (NaN elements passed over)
+hipError_t launch_block_amax(const float* A, int64_t N, int B, float* out, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 // monitor[i] <- sqrt(monitor[i]) / sqrt(B)
 hipError_t launch_monitor_finish(float* monitor, int64_t n, int B, hipStream_t stream);

@@ -1,5 +1,6 @@
 // elementwise.hip -- HBM-bound kernels around the products: per-block coefficients, affine
-// identity combinations (solver start terms, casts, unscaling), fills, and stack/unstack copies.
+// identity combinations (solver start terms, casts, unscaling), fills, per-block magnitude bounds,
+// and stack/unstack copies.
 //
 // All of them stream 16-byte vectors with consecutive lanes on consecutive addresses.
 #include <hip/hip_runtime.h>
@@ -190,6 +191,29 @@ __global__ __launch_bounds__(256) void sym_affine_kernel(Affine op, int64_t N, i
   }
 }
 
+// out[b] = max |A_b| over the block's B^2 elements (NaN elements are passed over), one workgroup
+// per block streaming 16-byte vectors
+__global__ __launch_bounds__(512) void block_amax_kernel(const float* A, int B, float* out) {
+  const int64_t b = blockIdx.x;
+  const f32x4* a = (const f32x4*)(A + b * (int64_t)B * B);
+  const int n4 = B * B / 4;
+  float m = 0.f;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < n4; i += 512) {
+    const f32x4 v = a[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[8];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w]);
+    out[b] = m;
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -328,6 +352,12 @@ hipError_t launch_sym_affine(const Affine& op, int64_t N, int B, hipStream_t str
   const int64_t grid = N * (int64_t)nt * (nt + 1) / 2;
   if (B % 64 != 0 || op.x_prec != DASH_FP32 || !op.X || op.status || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sym_affine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, op, N, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_amax(const float* A, int64_t N, int B, float* out, hipStream_t stream) {
+  if (N < 1 || N > 0x7fffffffLL || B % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(block_amax_kernel, dim3((unsigned)N), dim3(512), 0, stream, A, B, out);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // tiles) and fuses the affine combination the iteration needs, D = a*acc + b*C + d*E + g*I, with
 // per-block coefficients read on the device (gemm_common.hpp).  The kernels are in gemm_f32.hip
 // (fp32 operands), gemm_f16.hip (binary16 or bfloat16 operands, fp32 accumulation) and
-// gemm_split.hip (fp32 operands formed on the bfloat16 matrix cores from exact three-piece splits).
+// gemm_split.hip (fp32 operands formed on the bfloat16 matrix cores from exact three-piece splits,
+// or, in the Clenshaw launches, on the binary16 ones from scaled two-piece splits).
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
@@ -38,7 +39,8 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // folding C into the product needs C == Y in every problem of a triangle-only fp32 NN launch
   // and E in every problem, except the launches that map Y, which have none
   auto fold_ok = [&](const Product& p) { return p.C && p.C == p.Y && (p.map_y ? !p.E : p.E != nullptr); };
-  if (epi.fold_c && in_prec != DASH_FP32_SPLIT &&
+  const bool split = in_prec == DASH_FP32_SPLIT || in_prec == DASH_FP32_SPLIT16;
+  if (epi.fold_c && !split &&
       (in_prec != DASH_FP32 || !sym || trans != Trans::NN || !fold_ok(probs[0]) || (nprob > 1 && !fold_ok(probs[1]))))
     return hipErrorInvalidValue;
   // operand maps exist in every binary16 kernel and, for the right operand, in the fp32 Clenshaw
@@ -63,15 +65,20 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // stopped blocks or second output.  C is read from memory with its (beta, ib) weight, or, with
   // fold_c (symmetric NN only, C == Y in every problem), enters as (c_over_a coef[ic]) added to
   // X's diagonal: alpha coef[ia] (X + c I) Y
-  if (in_prec == DASH_FP32_SPLIT) {
+  // two-piece binary16 (DASH_FP32_SPLIT16): the Clenshaw launches alone (symmetric NN, C == Y
+  // folded), with the magnitude bounds of both operands in every problem
+  if (split) {
+    const bool h2 = in_prec == DASH_FP32_SPLIT16;
     const bool shape_ok = sym ? (trans != Trans::NN || y_sym || epi.fold_c) : trans == Trans::NN;
     bool fold_ok_split = !epi.fold_c || (sym && trans == Trans::NN);
-    for (int i = 0; i < nprob; ++i)
+    for (int i = 0; i < nprob; ++i) {
       if (epi.fold_c && probs[i].C != probs[i].Y) fold_ok_split = false;
+      if (h2 && (!probs[i].amax_x || !probs[i].amax_y)) fold_ok_split = false;
+    }
     if (out_prec != DASH_FP32 || !shape_ok || maps || frz || !fold_ok_split || probs[0].D2 ||
-        (nprob > 1 && probs[1].D2) || B % 256 != 0)
+        (nprob > 1 && probs[1].D2) || B % 256 != 0 || (h2 && (!sym || !epi.fold_c || trans != Trans::NN)))
       return hipErrorInvalidValue;
-    return gemm::launch_split(a, sym, trans, y_sym, stream);
+    return gemm::launch_split(a, sym, trans, y_sym, h2, stream);
   }
   // 2-byte operands (binary16 or bfloat16): output in fp32 or in the operand format
   if ((in_prec != DASH_FP16 && in_prec != DASH_BF16) || (out_prec != DASH_FP32 && out_prec != in_prec))

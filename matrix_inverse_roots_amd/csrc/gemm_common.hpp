@@ -187,9 +187,10 @@ __device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, c
 
 // HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
 // that E_PRE takes E's values from ev_pre, loaded by load_e).  HAS_D2: the launch may carry a second
-// output (full products only).
+// output (full products only).  AMAX: the largest stored |D| of the tile goes into P.amax_d[b] by
+// atomicMax on its bits (non-negative floats order as their bit patterns), when P.amax_d is set.
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE, bool CHECKS,
-          bool E_PRE = false, bool HAS_D2 = true>
+          bool E_PRE = false, bool HAS_D2 = true, bool AMAX = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
                                          const float (*ev_pre)[MTN][16] = nullptr) {
@@ -211,7 +212,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   const int li = lane & 31, h = lane >> 5;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const bool diag_tile = SYM && tc.ti == tc.tj;
-  float mon = 0.f;
+  float mon = 0.f, amax = 0.f;
   bool bad = false;
 #pragma unroll
   for (int mt = 0; mt < MTM; ++mt) {
@@ -246,7 +247,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           if (i == j) v += ga;
           pk[q] = cvt_out<TO>(v);
           const int64_t idx = (int64_t)i * B + j;
-          if (!diag_tile || il <= jl) D[idx] = pk[q];
+          if (!diag_tile || il <= jl) {
+            D[idx] = pk[q];
+            if (AMAX) amax = fmaxf(amax, fabsf(v));  // (NaN leaves it unchanged)
+          }
           float v2 = 0.f;
           if (D2) {
             v2 = al2 * x + (i == j ? ga2 : 0.f);
@@ -277,6 +281,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
   if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
+  if (AMAX && P.amax_d) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (lane == 0) atomicMax((unsigned*)&P.amax_d[b], __float_as_uint(amax));
+  }
 }
 
 // Epilogue for binary16 outputs (no C/E operands, no second output).  Kept elements are stored
@@ -403,7 +412,7 @@ hipError_t launch_f32(GemmArgs& a, Trans trans, bool sym, hipStream_t stream);
 hipError_t launch_f16(GemmArgs& a, dash_prec in_prec, dash_prec out_prec, bool sym, bool y_sym, hipStream_t stream);
 // fp32 products from three-piece bfloat16 splits (gemm_split.hip), B % 256 == 0: symmetric results
 // (sym) of NN with an exactly symmetric right operand, of NT or of TN; general results of NN
-hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStream_t stream);
+hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, bool h2, hipStream_t stream);
 
 }  // namespace gemm
 }  // namespace dash

@@ -28,6 +28,19 @@
 // alpha X Y + beta Y = alpha (X + (beta/alpha) I) Y, so beta/alpha is added to X's diagonal as it
 // is staged (before the split) and no C is read.  (Adding C from the staged Y planes, as the fp32
 // kernel does, spilled registers and measured slower.)
+//
+// H2 (two-piece binary16 form, Clenshaw launches): each fp32 element is first brought to binary16's
+// upper range by a power of two per operand and block, x' = 2^e x with e from a bound m on |x|
+// (2^13 <= 2^e m < 2^14), then cut into two binary16 pieces, x0 = f16(x') and x1 = f16(x' - x0) (the
+// difference is exact in fp32), so that x' = x0 + x1 up to binary16's rounding of x1: 2^-22 |x'|,
+// or 2^-25 where x1 falls below binary16's normal range, which is 2^-38 of the block's largest
+// element.  x'y' = x0 y0 + x0 y1 + x1 y0 up to the term x1 y1 (2^-22 |x'||y'|): three binary16 MFMA
+// products into one fp32 accumulator (piece products up to 2^28), which the epilogue multiplies by
+// 2^-(ex + ey).  LDS holds two planes per operand.  The bounds: m_X = max|A| + |c| for the left
+// operand A + c I (max|A| from a pass over the stack before the solve), and for the right operand
+// b_{k+1} the maximum that the launch which wrote it gathered in its epilogue (atomicMax of the
+// stored magnitudes per block); each launch also clears the slot that the launch after next
+// gathers into.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -55,6 +68,34 @@ __device__ __forceinline__ void split3(const f32x4& lo, const f32x4& hi, bf16x8&
   }
 }
 
+// power-of-two exponent e with 2^13 <= 2^e m < 2^14 (m = 0, inf or NaN: 0)
+__device__ __forceinline__ int top_exp(float m) {
+  int e;
+  frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
+  return (m > 0.f && isfinite(m)) ? 14 - e : 0;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// H2 pieces of the 8 elements lo[0..3], hi[0..3] of 2^e x: x0 = f16(x'), x1 = f16(x' - x0).  The
+// difference is formed by one mixed-precision fma of x0 (binary16 source) with -1; m1 holds -1 where
+// the compiler cannot see it, so that it keeps the fma instead of a conversion and a subtraction.
+__device__ __forceinline__ void split2(const f32x4& lo, const f32x4& hi, int e, float m1, f16x8& p0, f16x8& p1) {
+#pragma unroll
+  for (int q = 0; q < 8; q += 2) {
+    const float a = ldexpf(q < 4 ? lo[q] : hi[q - 4], e);
+    const float b = ldexpf(q < 4 ? lo[q + 1] : hi[q - 3], e);
+    const f16x2 h = __builtin_convertvector(f32x2{a, b}, f16x2);
+    const f32x2 r = {__builtin_fmaf((float)h[0], m1, a), __builtin_fmaf((float)h[1], m1, b)};
+    const f16x2 l = __builtin_convertvector(r, f16x2);
+    p0[q] = h[0];
+    p0[q + 1] = h[1];
+    p1[q] = l[0];
+    p1[q + 1] = l[1];
+  }
+}
+
 // Word 3 of a raw buffer resource on this architecture: 32-bit data format, no swizzle, byte
 // offsets (the loads here are untyped).
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
@@ -64,18 +105,21 @@ constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 // serves together) fall on 16 distinct 16-byte slots of its 64 banks
 __device__ __forceinline__ int swz2(int row, int ch) { return ch ^ ((row >> 2) & 1) ^ ((row >> 3) & 1); }
 
-template <bool CHECKS, bool SYM, bool XT, bool YT, bool FOLD = false>
+template <bool CHECKS, bool SYM, bool XT, bool YT, bool FOLD = false, bool H2 = false>
 __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   constexpr int TILE = 256, BK = 16, DEPTH = 4;
   constexpr int WTM = 128, WTN = 64, MTM = 4, MTN = 2;
-  constexpr int PLANE = TILE * BK;  // bfloat16 of one piece plane of one operand slice
-  constexpr int BUF = 6 * PLANE;    // X pieces 0..2, then Y pieces 0..2
+  using TE = std::conditional_t<H2, _Float16, __bf16>;
+  using V8 = typename Half<TE>::v8;
+  constexpr int PLANE = TILE * BK;           // elements of one piece plane of one operand slice
+  constexpr int YP = H2 ? 2 : 3;             // pieces per operand
+  constexpr int BUF = 2 * YP * PLANE;        // X pieces, then Y pieces
   // the two stages of the double buffer are separate arrays: the stores of one stage and the
   // reads of the other then provably do not alias, so the compiler may interleave the staging of
   // slice k + 1 (split and LDS stores) with the products of slice k
-  __shared__ __attribute__((aligned(16))) __bf16 stage0[BUF];
-  __shared__ __attribute__((aligned(16))) __bf16 stage1[BUF];
-  auto smem_of = [&](int buf) -> __bf16* { return buf ? stage1 : stage0; };
+  __shared__ __attribute__((aligned(16))) TE stage0[BUF];
+  __shared__ __attribute__((aligned(16))) TE stage1[BUF];
+  auto smem_of = [&](int buf) -> TE* { return buf ? stage1 : stage0; };
 
   const TileCoord tc = decode_tile(a, SYM);
   const Product P = tc.prob ? a.p1 : a.p0;
@@ -139,11 +183,23 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   // FOLD (C == Y, Clenshaw's b_{k+1}): alpha X Y + beta Y = alpha (X + (beta/alpha) I) Y, so the
   // C term enters as (beta/alpha) added to X's diagonal before the split, and no C is read
   const float xc = FOLD ? a.epi.c_over_a * coef_of(a.epi, a.epi.ic, tc.b) : 0.f;
+  // H2: the operands' power-of-two exponents for this block, and the launch's clearing of the slot
+  // that the launch after next gathers into
+  int ex = 0, ey = 0;
+  float m1 = -1.f;
+  if constexpr (H2) {
+    ex = top_exp(P.amax_x[tc.b] + fabsf(xc));
+    ey = top_exp(P.amax_y[tc.b]);
+    if (P.amax_zero && tc.ti == 0 && tc.tj == 0 && tid == 0) P.amax_zero[tc.b] = 0.f;
+    asm("" : "+s"(m1));  // (no instruction: hides the constant -1 from the optimiser)
+  }
   auto sstore = [&](auto slot_c, int buf, int k0) {
     constexpr int slot = decltype(slot_c)::value;
-    __bf16* s = smem_of(buf) + xrow * BK + 8 * swz2(xrow, xch);
-    bf16x8 p0, p1, p2;
-    if constexpr (FOLD) {  // element q of the piece sits on the diagonal when i0 + row == k0 + 8 ch + q
+    TE* s = smem_of(buf) + xrow * BK + 8 * swz2(xrow, xch);
+    // element q of the piece sits on the diagonal when i0 + row == k0 + 8 ch + q: only the slices
+    // with k0 in (i0 - BK, i0 + TILE) hold diagonal elements of the tile's rows.  H2 skips the others
+    // by a uniform branch (the bfloat16 form measured faster without it)
+    if (FOLD && (!H2 || (k0 + BK > i0 && k0 < i0 + TILE))) {
       const int d = i0 + srow - k0 - 8 * sch;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -151,15 +207,26 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
         rx[slot][1][q] = d == q + 4 ? rx[slot][1][q] + xc : rx[slot][1][q];
       }
     }
-    split3(rx[slot][0], rx[slot][1], p0, p1, p2);
-    *(bf16x8*)(s) = p0;
-    *(bf16x8*)(s + PLANE) = p1;
-    *(bf16x8*)(s + 2 * PLANE) = p2;
-    __bf16* t = smem_of(buf) + 3 * PLANE + yrow * BK + 8 * swz2(yrow, ych);
-    split3(ry[slot][0], ry[slot][1], p0, p1, p2);
-    *(bf16x8*)(t) = p0;
-    *(bf16x8*)(t + PLANE) = p1;
-    *(bf16x8*)(t + 2 * PLANE) = p2;
+    TE* t = smem_of(buf) + YP * PLANE + yrow * BK + 8 * swz2(yrow, ych);
+    if constexpr (H2) {
+      f16x8 p0, p1;
+      split2(rx[slot][0], rx[slot][1], ex, m1, p0, p1);
+      *(f16x8*)(s) = p0;
+      *(f16x8*)(s + PLANE) = p1;
+      split2(ry[slot][0], ry[slot][1], ey, m1, p0, p1);
+      *(f16x8*)(t) = p0;
+      *(f16x8*)(t + PLANE) = p1;
+    } else {
+      bf16x8 p0, p1, p2;
+      split3(rx[slot][0], rx[slot][1], p0, p1, p2);
+      *(bf16x8*)(s) = p0;
+      *(bf16x8*)(s + PLANE) = p1;
+      *(bf16x8*)(s + 2 * PLANE) = p2;
+      split3(ry[slot][0], ry[slot][1], p0, p1, p2);
+      *(bf16x8*)(t) = p0;
+      *(bf16x8*)(t + PLANE) = p1;
+      *(bf16x8*)(t + 2 * PLANE) = p2;
+    }
   };
 
   f32x16 acc[MTM][MTN];
@@ -170,27 +237,56 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
-  // one k-slice: lane half h takes k = 8h .. 8h + 7 of the slice for both operands; one right
-  // piece at a time (its two fragments), each left piece read per use
+  // one k-slice: lane half h takes k = 8h .. 8h + 7 of the slice for both operands.  H2: both
+  // right pieces and both left pieces of the wave's fragments, then x0 y0, x0 y1 and x1 y0.
+  auto compute_h2 = [&](int buf) {
+    const TE* s = smem_of(buf);
+    auto frag = [&](int plane, int row) { return *(const V8*)&s[plane * PLANE + row * BK + 8 * swz2(row, h)]; };
+    V8 y0[MTN], y1[MTN], x0[MTM], x1[MTM];
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt) y0[nt] = frag(2, wn * WTN + nt * 32 + li);
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt) x0[mt] = frag(0, wm * WTM + mt * 32 + li);
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt) y1[nt] = frag(3, wn * WTN + nt * 32 + li);
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt) x1[mt] = frag(1, wm * WTM + mt * 32 + li);
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x0[mt], y0[nt], acc[mt][nt]);
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x0[mt], y1[nt], acc[mt][nt]);
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x1[mt], y0[nt], acc[mt][nt]);
+  };
+  // bfloat16: one right piece at a time (its two fragments), each left piece read per use
   auto compute = [&](int buf) {
-    const __bf16* s = smem_of(buf);
+    if constexpr (H2) {
+      compute_h2(buf);
+      return;
+    }
+    const TE* s = smem_of(buf);
 #pragma unroll
     for (int pb = 0; pb < 3; ++pb) {
-      bf16x8 bv[MTN];
+      V8 bv[MTN];
 #pragma unroll
       for (int nt = 0; nt < MTN; ++nt) {
         const int row = wn * WTN + nt * 32 + li;
-        bv[nt] = *(const bf16x8*)&s[(3 + pb) * PLANE + row * BK + 8 * swz2(row, h)];
+        bv[nt] = *(const V8*)&s[(3 + pb) * PLANE + row * BK + 8 * swz2(row, h)];
       }
 #pragma unroll
       for (int pa = 0; pa + pb < 3; ++pa)
 #pragma unroll
         for (int mt = 0; mt < MTM; ++mt) {
           const int row = wm * WTM + mt * 32 + li;
-          const bf16x8 av = *(const bf16x8*)&s[pa * PLANE + row * BK + 8 * swz2(row, h)];
+          const V8 av = *(const V8*)&s[pa * PLANE + row * BK + 8 * swz2(row, h)];
 #pragma unroll
-          for (int nt = 0; nt < MTN; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[nt], acc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(av, bv[nt], acc[mt][nt]);
         }
     }
   };
@@ -228,16 +324,34 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   tail_step(IC<1>{}, kt + 1, true);
   tail_step(IC<2>{}, kt + 2, true);
   tail_step(IC<3>{}, kt + 3, false);
-  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false>(a, tc, P, acc, wm, wn, lane);
+  if constexpr (H2) {
+    const int es = -ex - ey;
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][nt][r] = ldexpf(acc[mt][nt][r], es);
+  }
+  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2>(a, tc, P, acc, wm, wn, lane);
 }
 
 }  // namespace
 
-hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, hipStream_t stream) {
+hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, bool h2, hipStream_t stream) {
   if (a.B % 256 != 0) return hipErrorInvalidValue;
   a.tdim = a.B / 256;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool checks = wants_checks(a.epi);
+  // two-piece binary16 form: the Clenshaw launches alone (symmetric NN with C == Y folded)
+  if (h2) {
+    if (!sym || trans != Trans::NN || !a.epi.fold_c) return hipErrorInvalidValue;
+    if (y_sym)
+      return checks ? launch(gemm_split_kernel<true, true, false, false, true, true>, a, stream, 512)
+                    : launch(gemm_split_kernel<false, true, false, false, true, true>, a, stream, 512);
+    return checks ? launch(gemm_split_kernel<true, true, false, true, true, true>, a, stream, 512)
+                  : launch(gemm_split_kernel<false, true, false, true, true, true>, a, stream, 512);
+  }
   // symmetric results: NN of an exactly symmetric Y and NT read Y's rows as B's columns; TN
   // gathers the columns of both operands; NN with C == Y folded gathers Y's columns unless Y is
   // exactly symmetric.  General results: NN with Y's columns gathered.

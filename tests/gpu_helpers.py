@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import matrix_inverse_roots_amd as dash
+import oracle
 
 DEV = torch.device("cuda:0")
 
@@ -45,6 +46,18 @@ def power_scale(A, V0, steps=10, prec=dash.DASH_FP32):
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, prec, V0.shape[1], device=DEV)
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prec, V0.shape[1], steps, V0, s, ws)
     return s
+
+
+def host_power_scale(A, V0, steps=10):
+    """The oracle's power-iteration scale per block rounded to fp32, on the device: the scale that a
+    solver test feeds to both its GPU solve and the oracle (no oracle input comes from the HIP path)."""
+    s, _ = oracle.mpi(np.asarray(A, np.float64), np.asarray(V0, np.float64), steps)
+    return to_dev(np.asarray(s, np.float32).reshape(-1))
+
+
+def host_frob_scale(A):
+    """The oracle's Frobenius scale per block rounded to fp32, on the device."""
+    return to_dev(np.asarray(oracle.frobenius(np.asarray(A, np.float64)), np.float32).reshape(-1))
 
 
 def frob_scale(A):

@@ -318,3 +318,32 @@ def test_binding_rejects_host_tensors():
         dash.dash_scale(A, 2, 64, dash.DASH_SCALE_FROBENIUS, dash.DASH_FP32, 0, 0, None, s, None)
     with pytest.raises(ValueError, match="GPU tensor"):
         dash.dash_stack([torch.zeros((64, 64))], 64, P)
+
+
+def test_split16_precision_queries_and_argument_errors():
+    """DASH_FP32_SPLIT16 (two-piece binary16 products): the Chebyshev solves take it, with the
+    workspace of the fp32 solve and DASH_FP32_SPLIT's flop count; every other solver, the statistics,
+    the apply and the scale reject it."""
+    for B in (256, 320, 1024):
+        assert dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32_SPLIT16) == \
+            dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32)
+        for d in (2, 24):
+            assert dash.dash_flops(dash.DASH_OP_CHEB, 3, B, dash.DASH_FP32_SPLIT16, d, 0) == \
+                dash.dash_flops(dash.DASH_OP_CHEB, 3, B, dash.DASH_FP32_SPLIT, d, 0)
+    N, B = 4, 256
+    ws = FakeWs(P3, 1 << 30)
+    S16 = dash.DASH_FP32_SPLIT16
+    g = dash.dash_inverse_root_cheb_prec
+    assert _status_of(g, P, P2, N, B, 0, 0.1, 1.0, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG  # degree 0
+    assert _status_of(g, P, P2, N, 96, 8, 0.1, 1.0, S16, 5 * P, ws=ws) == _lib.DASH_ERR_SHAPE
+    assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, S16, 5 * P, ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
+    # the workspace grew by the magnitude slots (4 N floats): one byte short is refused
+    need = dash.dash_workspace_size(dash.DASH_OP_CHEB, N, B, S16)
+    assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, S16, 5 * P, ws=FakeWs(P3, need - 1)) == _lib.DASH_ERR_WORKSPACE
+    assert _status_of(dash.dash_inverse_root_ndb_prec, P, P2, N, B, 5, 5, S16, 5 * P, ws=ws) == \
+        _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 5, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_update_stats_prec, P, N, B, 0.9, S16, P2) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_apply_prec, P, P2, P3, N, B, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
+    assert _status_of(dash.dash_scale, P, N, B, dash.DASH_SCALE_POWER, S16, 8, 10, P2, P3,
+                      ws=ws) == _lib.DASH_ERR_INVALID_ARG

@@ -15,7 +15,7 @@ import torch
 import dash_inputs as di
 import matrix_inverse_roots_amd as dash
 import oracle
-from gpu_helpers import DEV, R_FP16, cn, cn_adaptive, power_scale, rel_err, residual, to_dev, to_host
+from gpu_helpers import DEV, R_FP16, cn, cn_adaptive, host_power_scale, rel_err, residual, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_cn_bf16_matches_storage_model(B):
     """kappa 5 stacks; B % 256 == 0 runs the 256-wide triangle kernel, 64 and 192 the 64-wide one."""
     A = di.known_spectrum_stack(300 + B, 3, B, 0.2, 1.0)[0].astype(np.float32)
     Ad = to_dev(A)
-    s = power_scale(Ad, to_dev(di.start_vectors(B, 32)), 10)
+    s = host_power_scale(A, di.start_vectors(B, 32))
     X, mon, status = cn(Ad, s, 9, dash.DASH_BF16, want_monitor=True)
     Xh = to_host(X)
     assert np.all(to_host(status) == 0)

@@ -67,9 +67,23 @@ def scale(A, V0, prec):
     return s
 
 
+def pinned_scale(A, V0, prec, idx, tol, half=False):
+    """The GPU scale of every block, checked on the blocks idx against the oracle's power iteration
+    (relative tol), whose values, rounded to fp32, then replace the GPU's there: the solve and the
+    oracle take the same scale on those blocks, and it comes from the oracle.  Returns (s on the
+    device, the oracle's fp32 scale of idx in fp64)."""
+    s = scale(A, V0, prec)
+    s_ref, _ = oracle.mpi(host(A[idx]), host(V0), 10, half=half)
+    assert np.max(np.abs(host(s)[idx] - s_ref) / s_ref) < tol
+    s32 = s_ref.astype(np.float32)
+    s[idx] = torch.from_numpy(s32).to(DEV)
+    return s, s32.astype(np.float64)
+
+
 def test_full_ndb_fp32(stack):
     A, V0 = stack
-    s = scale(A, V0, dash.DASH_FP32)
+    idx = SAMPLE + ORACLE_SAMPLE
+    s, s_h = pinned_scale(A, V0, dash.DASH_FP32, idx, 1e-5)
     X = torch.empty_like(A)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_NDB, N, B, device=DEV)
@@ -77,11 +91,7 @@ def test_full_ndb_fp32(stack):
     del ws
     torch.cuda.empty_cache()
     assert int(status.abs().sum()) == 0
-    idx = SAMPLE + ORACLE_SAMPLE
     A_h = host(A[idx])
-    s_h = host(s)[idx]
-    s_ref, _ = oracle.mpi(A_h, host(V0), 10)
-    assert np.max(np.abs(s_h - s_ref) / s_ref) < 1e-5
     X_h = host(X[idx])
     assert np.max(residual(X_h, A_h)) < R_FP32
     k = len(SAMPLE)
@@ -118,7 +128,8 @@ def test_full_ndb_half_refine1(stack):
     the binary16 storage model on sampled blocks (tolerance 2e-3, fp32 accumulation against exact
     products) and the fp32 residual gate on every block."""
     A, V0 = stack
-    s = scale(A, V0, dash.DASH_FP32)
+    idx = SAMPLE + ORACLE_SAMPLE
+    s, s_h = pinned_scale(A, V0, dash.DASH_FP32, idx, 1e-5)
     X = torch.empty_like(A)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP16, device=DEV)
@@ -126,9 +137,7 @@ def test_full_ndb_half_refine1(stack):
     del ws
     torch.cuda.empty_cache()
     assert int(status.abs().sum()) == 0
-    idx = SAMPLE + ORACLE_SAMPLE
     A_h = host(A[idx])
-    s_h = host(s)[idx]
     X_h = host(X[idx])
     assert np.max(residual(X_h, A_h)) < R_FP32
     k = len(SAMPLE)
@@ -144,7 +153,8 @@ def test_full_cn_bf16(stack):
     blocks and the bfloat16 residual gate 4e-2 (the binary16 gate scaled by the 8x unit roundoff) on
     every block."""
     A, V0 = stack
-    s = scale(A, V0, dash.DASH_FP32)
+    idx = SAMPLE + ORACLE_SAMPLE
+    s, s_h = pinned_scale(A, V0, dash.DASH_FP32, idx, 1e-5)
     X = torch.empty_like(A)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_CN, N, B, dash.DASH_BF16, device=DEV)
@@ -152,9 +162,7 @@ def test_full_cn_bf16(stack):
     del ws
     torch.cuda.empty_cache()
     assert int(status.abs().sum()) == 0
-    idx = SAMPLE + ORACLE_SAMPLE
     A_h = host(A[idx])
-    s_h = host(s)[idx]
     X_h = host(X[idx])
     r_bf16 = 8 * R_FP16
     assert np.max(residual(X_h, A_h)) < r_bf16
@@ -184,21 +192,28 @@ def test_full_step_chebyshev(stack):
     L_ref, R_ref = oracle.update_stats(host(G[sample_t]), 0.95, L_prev, R_prev)
     assert np.max(rel_err(host(A[sample_t]), L_ref)) < 1e-5
     assert np.max(rel_err(host(A[[NG + t for t in sample_t]]), R_ref)) < 1e-5
-    s = scale(A, V0, dash.DASH_FP32)
-    lo = 0.95e-6 / float(s.max())
+    idx = ORACLE_SAMPLE
+    s, s_h = pinned_scale(A, V0, dash.DASH_FP32, idx, 1e-5)
+    lo = 0.95e-6 / float(s_h.max())  # the damping after one update over the sampled blocks' scale
     X = torch.empty_like(A)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws = dash.workspace(dash.DASH_OP_CHEB, N, B, device=DEV)
     dash.dash_inverse_root_cheb(A, s, N, B, 24, lo, 1.25, X, status=status, ws=ws)
     del ws
     assert int(status.abs().sum()) == 0
-    idx = ORACLE_SAMPLE
-    X_ref = oracle.cheb_inverse_root(host(A[idx]), host(s)[idx], 24, lo, 1.25)
+    X_ref = oracle.cheb_inverse_root(host(A[idx]), s_h, 24, lo, 1.25)
     assert np.max(rel_err(host(X[idx]), X_ref)) < ITERATE_TOL
     # the same solve with split products (fp32 on the bfloat16 matrix cores), same gate
     Xs = torch.empty_like(A)
     ws = dash.workspace(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32_SPLIT, device=DEV)
     dash.dash_inverse_root_cheb_prec(A, s, N, B, 24, lo, 1.25, dash.DASH_FP32_SPLIT, Xs, status=status, ws=ws)
+    del ws
+    assert int(status.abs().sum()) == 0
+    assert np.max(rel_err(host(Xs[idx]), X_ref)) < ITERATE_TOL
+    assert torch.equal(Xs[idx], Xs[idx].transpose(1, 2))
+    # and with two-piece binary16 products, same gate
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, dash.DASH_FP32_SPLIT16, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, N, B, 24, lo, 1.25, dash.DASH_FP32_SPLIT16, Xs, status=status, ws=ws)
     del ws
     assert int(status.abs().sum()) == 0
     assert np.max(rel_err(host(Xs[idx]), X_ref)) < ITERATE_TOL
@@ -221,7 +236,8 @@ def test_full_step_chebyshev(stack):
 def test_full_step_bench_sequence(stack):
     """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics (split
     products) -> power scale (split products) -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
-    (floor_t = 1e-6 * 0.95^t, the damping after t updates; split products) -> apply (split products).
+    (floor_t = 1e-6 * 0.95^t, the damping after t updates; two-piece binary16 products) -> apply
+    (split products).
     Sampled L and R blocks of one tile are recomputed by the oracle from the same starting blocks and
     gradient tiles through both steps (its own statistics, scale, interval and solve); every sampled
     block's spectrum (numpy eigvalsh; the oracle's Jacobi needs minutes at B = 1024 and is pinned to
@@ -229,6 +245,7 @@ def test_full_step_bench_sequence(stack):
     A0, V0 = stack
     A = A0.clone()
     split = dash.DASH_FP32_SPLIT
+    cheb_prec = dash.DASH_FP32_SPLIT16
     t_idx = 700
     idx = [t_idx, NG + t_idx]
     L_ref, R_ref = host(A[t_idx]), host(A[NG + t_idx])
@@ -247,7 +264,7 @@ def test_full_step_bench_sequence(stack):
     lo = torch.empty(N, device=DEV)
     status = torch.empty(N, dtype=torch.int32, device=DEV)
     ws_s = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 32, device=DEV)
-    ws_c = dash.workspace(dash.DASH_OP_CHEB, N, B, split, device=DEV)
+    ws_c = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=DEV)
     ws_a = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
     floor = 1e-6
     for step in range(2):
@@ -256,7 +273,7 @@ def test_full_step_bench_sequence(stack):
         dash.dash_stack(grads, B, G)
         dash.dash_update_stats_prec(G, NG, B, 0.95, split, A)
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, split, 32, 10, V0, s, ws_s)
-        dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, split, X, lo_out=lo,
+        dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, cheb_prec, X, lo_out=lo,
                                           status=status, ws=ws_c)
         dash.dash_apply_prec(X[:NG], X[NG:], G, NG, B, split, U, ws_a)
         # the oracle's copy of the same step for tile t_idx, from the gradient itself

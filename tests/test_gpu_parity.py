@@ -12,7 +12,8 @@ import torch
 import dash_inputs as di
 import matrix_inverse_roots_amd as dash
 import oracle
-from gpu_helpers import (DEV, ITERATE_TOL, R_FP16, R_FP32, cheb, cn, frob_scale, ndb, power_scale, rel_err,
+from gpu_helpers import (DEV, ITERATE_TOL, R_FP16, R_FP32, cheb, cn, frob_scale, host_frob_scale, host_power_scale,
+                         ndb, power_scale, rel_err,
                          residual, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -84,7 +85,7 @@ def test_frobenius(tiny, conditioned):
 def test_ndb_tiny_full_stack(tiny):
     A, Ad = tiny
     V0 = di.start_vectors(64, 32)
-    s = power_scale(Ad, to_dev(V0), 10)
+    s = host_power_scale(A, V0)
     X, R, mon, status = ndb(Ad, s, 20, 20, want_sqrt=True, want_monitor=True)
     s_h = to_host(s)
     X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, s_h, 20, 20, want_sqrt=True)
@@ -101,7 +102,7 @@ def test_ndb_tiny_full_stack(tiny):
 @pytest.mark.parametrize("scaling", ["power", "frobenius"])
 def test_ndb_conditioned(conditioned, scaling):
     A, Ad = conditioned
-    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    s = host_power_scale(A, di.start_vectors(256, 32)) if scaling == "power" else host_frob_scale(A)
     T = 16 if scaling == "power" else 18
     X, _, _, status = ndb(Ad, s, T, T)
     X_ref, _, _ = oracle.ndb_inverse_root(A, to_host(s), T, T)
@@ -113,7 +114,7 @@ def test_ndb_conditioned(conditioned, scaling):
 @pytest.mark.parametrize("it1,it2", [(1, 1), (1, 3), (2, 1), (3, 2)])
 def test_ndb_few_steps_match_oracle_iterates(tiny, it1, it2):
     A, Ad = tiny
-    s = frob_scale(Ad)
+    s = host_frob_scale(A)
     X, R, mon, _ = ndb(Ad, s, it1, it2, want_sqrt=True, want_monitor=True)
     X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, to_host(s), it1, it2, want_sqrt=True)
     assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
@@ -128,7 +129,7 @@ def test_ndb_few_steps_match_oracle_iterates(tiny, it1, it2):
 @pytest.mark.parametrize("scaling", ["power", "frobenius"])
 def test_cn_conditioned(conditioned, scaling):
     A, Ad = conditioned
-    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    s = host_power_scale(A, di.start_vectors(256, 32)) if scaling == "power" else host_frob_scale(A)
     T = 16
     X, mon, status = cn(Ad, s, T, want_monitor=True)
     X_ref, mon_ref = oracle.cn_inverse_root(A, to_host(s), T)
@@ -144,7 +145,7 @@ def test_cn_conditioned(conditioned, scaling):
 @pytest.mark.parametrize("iters", [1, 2, 3, 6])
 def test_cn_few_steps_match_oracle_iterates(tiny, iters):
     A, Ad = tiny
-    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10)
+    s = host_power_scale(A, di.start_vectors(64, 32))
     X, mon, _ = cn(Ad, s, iters, want_monitor=True)
     X_ref, mon_ref = oracle.cn_inverse_root(A, to_host(s), iters)
     assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
@@ -153,8 +154,7 @@ def test_cn_few_steps_match_oracle_iterates(tiny, iters):
 
 def test_cn_fp16_tiny(tiny):
     A, Ad = tiny
-    V0 = to_dev(di.start_vectors(64, 32))
-    s = power_scale(Ad, V0, 10, dash.DASH_FP16)
+    s = host_power_scale(A, di.start_vectors(64, 32))
     X, _, status = cn(Ad, s, 8, dash.DASH_FP16)
     Xh = to_host(X)
     assert np.max(residual(Xh, A)) < R_FP16
@@ -186,7 +186,7 @@ def test_cn_reads_only_the_upper_triangle(prec):
 def test_cn_fp16_short_runs(tiny, iters):
     """T = 2 and 3: the first iterate X_1 = S_0 enters the last and the dual products directly."""
     A, Ad = tiny
-    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10, dash.DASH_FP16)
+    s = host_power_scale(A, di.start_vectors(64, 32))
     X, _, status = cn(Ad, s, iters, dash.DASH_FP16)
     X_emul, _ = oracle.cn_inverse_root(A, to_host(s), iters, half_storage=True)
     assert np.max(rel_err(to_host(X), X_emul)) < 5e-3
@@ -200,7 +200,7 @@ def test_cn_fp16_wide_tiles(B):
     A64, _, _ = di.known_spectrum_stack(120 + B, 3, B, 0.2, 1.0)  # kappa 5, like the Gram stacks
     A = A64.astype(np.float32)
     Ad = to_dev(A)
-    s = power_scale(Ad, to_dev(di.start_vectors(B, 32)), 10, dash.DASH_FP16)
+    s = host_power_scale(A, di.start_vectors(B, 32))
     X, mon, status = cn(Ad, s, 9, dash.DASH_FP16, want_monitor=True)
     Xh = to_host(X)
     assert np.max(residual(Xh, A)) < R_FP16
@@ -218,7 +218,7 @@ def test_cn_fp16_wide_tiles(B):
 @pytest.mark.parametrize("degree", [1, 2, 3, 8, 24])
 def test_cheb_tiny(tiny, degree):
     A, Ad = tiny
-    s = power_scale(Ad, to_dev(di.start_vectors(64, 32)), 10)
+    s = host_power_scale(A, di.start_vectors(64, 32))
     lo, hi = 0.02, 1.25
     X, status = cheb(Ad, s, degree, lo, hi)
     X_ref = oracle.cheb_inverse_root(A, to_host(s), degree, lo, hi)
@@ -383,7 +383,9 @@ def test_edge_tiles_through_the_step():
     L_ref, R_ref = oracle.update_stats(G_ref, 0.5, damp.astype(np.float64), damp.astype(np.float64))
     A_ref = np.concatenate([L_ref, R_ref])
     assert np.max(rel_err(to_host(A), A_ref)) < 1e-6
-    X_ref, _, _ = oracle.ndb_inverse_root(A_ref, to_host(s), 8, 8)
+    s_ref = oracle.frobenius(A_ref)  # the oracle's own pipeline, on its own statistics and scale
+    assert np.max(np.abs(to_host(s) - s_ref) / s_ref) < 1e-6
+    X_ref, _, _ = oracle.ndb_inverse_root(A_ref, s_ref, 8, 8)
     assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
     U_ref = oracle.unstack(oracle.apply(X_ref[:NG], G_ref, X_ref[NG:]), shapes, B)
     for v, u in zip(dst, U_ref):
@@ -515,7 +517,7 @@ def test_bad_blocks_are_flagged_and_isolated(tiny):
 def test_c2_steps_to_tolerance():
     """Steps to reach the residual 1e-3 on every block of the kappa 1e4 stack, for NDB and CN after
     power-iteration and Frobenius scaling (the counts bench.py --only c2 reports): every count is
-    reached, and the oracle's fp64 iteration with the GPU's scale agrees to one step (it has not
+    reached, and the oracle's fp64 iteration with its own scale agrees to one step (it has not
     converged two steps earlier and has one step later)."""
     import importlib.util
     import os
@@ -525,9 +527,9 @@ def test_c2_steps_to_tolerance():
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
     res = bench.c2_steps_to_tolerance(dash, di, torch, DEV)
-    A, Ad = di.conditioned_stack()[0], to_dev(di.conditioned_stack()[0])
-    V0 = to_dev(di.start_vectors(256, 32))
-    scales = {"power": to_host(power_scale(Ad, V0, 10)), "frobenius": to_host(frob_scale(Ad))}
+    A = di.conditioned_stack()[0]
+    scales = {"power": oracle.mpi(A.astype(np.float64), di.start_vectors(256, 32), 10)[0],
+              "frobenius": oracle.frobenius(A.astype(np.float64))}
     for key, rec in res.items():
         if not isinstance(rec, dict):
             continue

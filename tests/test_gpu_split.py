@@ -12,7 +12,8 @@ import torch
 import dash_inputs as di
 import matrix_inverse_roots_amd as dash
 import oracle
-from gpu_helpers import DEV, ITERATE_TOL, R_FP32, frob_scale, power_scale, rel_err, residual, to_dev, to_host
+from gpu_helpers import (DEV, ITERATE_TOL, R_FP32, frob_scale, host_frob_scale, host_power_scale, power_scale, rel_err,
+                         residual, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +39,7 @@ def test_cheb_split_matches_oracle(B, N, degrees):
     """Several 256-wide tiles per block (B = 512: 3 of the 4 x 4 tile grid's upper triangle rows),
     power-iteration scale, the pages' interval reading hi = 1.25."""
     A, Ad = spectrum_stack(400 + B, N, B)
-    s = power_scale(Ad, to_dev(di.start_vectors(B, 32)), 10)
+    s = host_power_scale(A, di.start_vectors(B, 32))
     lo, hi = 0.04, 1.25
     for d in degrees:
         X, status = cheb_p(Ad, s, d, lo, hi, SPLIT)
@@ -137,7 +138,7 @@ def test_ndb_split_conditioned(conditioned, scaling):
     """kappa 1e4: the stability case of the non-symmetrised NDB iteration, at the fp32 gates, and as
     accurate as the fp32 matrix cores."""
     A, Ad = conditioned
-    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    s = host_power_scale(A, di.start_vectors(256, 32)) if scaling == "power" else host_frob_scale(A)
     T = 16 if scaling == "power" else 18
     X, _, _, status = ndb_p(Ad, s, T, T, SPLIT)
     X_ref, _, _ = oracle.ndb_inverse_root(A, to_host(s), T, T)
@@ -156,7 +157,7 @@ def test_ndb_split_iterates_sqrt_and_monitor(it1, it2):
     """Several 256-wide tiles per block (B = 512, all 16 tiles): X, the square root and the monitor
     of every step against the oracle's NDB iterates."""
     A, Ad = spectrum_stack(420, 2, 512)
-    s = frob_scale(Ad)
+    s = host_frob_scale(A)
     X, R, mon, status = ndb_p(Ad, s, it1, it2, SPLIT, want_sqrt=True, want_monitor=True)
     X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, to_host(s), it1, it2, want_sqrt=True)
     assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
@@ -254,7 +255,7 @@ def test_apply_split_matches_oracle(B):
 @pytest.mark.parametrize("scaling", ["power", "frobenius"])
 def test_cn_split_conditioned(conditioned, scaling):
     A, Ad = conditioned
-    s = power_scale(Ad, to_dev(di.start_vectors(256, 32)), 10) if scaling == "power" else frob_scale(Ad)
+    s = host_power_scale(A, di.start_vectors(256, 32)) if scaling == "power" else host_frob_scale(A)
     T = 16
     N = Ad.shape[0]
     X = torch.empty_like(Ad)

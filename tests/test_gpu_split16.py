@@ -1,0 +1,164 @@
+"""GPU parity of the Chebyshev solve with two-piece binary16 products (DASH_FP32_SPLIT16): each
+product's operands are brought near 8 by a power of two per block and cut into two binary16 pieces
+(22 of fp32's 24 significant bits), and three piece products accumulate in fp32.  The gates are
+the fp32 ones (iterate parity 1e-4 against the oracle's fp64 Clenshaw recurrence, residual 1e-3),
+and the solve must be as accurate as the one on the fp32 matrix cores (error within 1.5 times
+theirs): the pieces' rounding (2^-22 of an element) is below the error the fp32 accumulation of a
+product already makes.  Where the split does not apply (degree 2, B not a multiple of 256) the
+result is the fp32 path's, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import dash_inputs as di
+import matrix_inverse_roots_amd as dash
+import oracle
+from gpu_helpers import DEV, ITERATE_TOL, R_FP32, frob_scale, host_power_scale, rel_err, residual, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+S16 = dash.DASH_FP32_SPLIT16
+
+
+def cheb_p(A, s, degree, lo, hi, prec):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, prec, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, N, B, degree, lo, hi, prec, X, status=status, ws=ws)
+    return X, status
+
+
+def spectrum_stack(seed, N, B, lam_min=0.05):
+    A = di.known_spectrum_stack(seed, N, B, lam_min, 1.0)[0].astype(np.float32)
+    return A, to_dev(A)
+
+
+def as_accurate_as_fp32(Ad, s, d, lo, hi, ref, err):
+    Xf, _ = cheb_p(Ad, s, d, lo, hi, dash.DASH_FP32)
+    err_f = rel_err(to_host(Xf), ref)
+    print("fp32 err", err_f.max())
+    assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+
+
+@pytest.mark.parametrize("B,N,degrees", [(256, 4, (3, 4, 8, 24)), (512, 2, (24,)), (1024, 1, (24,))])
+def test_cheb_split16_matches_oracle(B, N, degrees):
+    """Several 256-wide tiles per block, power-iteration scale, hi = 1.25; degree 3 (two products:
+    the first and the last), 4 (three: every magnitude slot used once), 8 and 24 (the slots
+    rotate)."""
+    A, Ad = spectrum_stack(460 + B, N, B)
+    s = host_power_scale(A, di.start_vectors(B, 32))
+    lo, hi = 0.04, 1.25
+    for d in degrees:
+        X, status = cheb_p(Ad, s, d, lo, hi, S16)
+        Xh = to_host(X)
+        ref = oracle.cheb_inverse_root(A, to_host(s), d, lo, hi)
+        err = rel_err(Xh, ref)
+        print("B", B, "degree", d, "split16 err", err.max())
+        assert np.all(to_host(status) == 0)
+        assert err.max() < ITERATE_TOL
+        assert np.array_equal(Xh, np.swapaxes(Xh, 1, 2))  # triangle-only products, mirrored
+        if d == 24:
+            assert residual(Xh, A).max() < R_FP32
+            as_accurate_as_fp32(Ad, s, d, lo, hi, ref, err)
+
+
+def test_cheb_split16_wide_magnitudes():
+    """Blocks D A D with D log-uniform over six decades (elements from 1e-12 to 1 of one another,
+    an interval reaching down to 1e-7): the small elements' pieces stay in binary16's normal range
+    after the block's power of two, so the solve keeps the fp32 path's accuracy."""
+    B, N = 256, 2
+    g = di.rng(471)
+    A64 = di.known_spectrum_stack(470, N, B, 0.05, 1.0)[0]
+    D = np.exp(g.uniform(np.log(1e-3), 0.0, (N, B)))
+    A = (D[:, :, None] * A64 * D[:, None, :]).astype(np.float32)
+    A = (A + np.swapaxes(A, 1, 2)) / 2  # exactly symmetric
+    Ad = to_dev(A)
+    lam = np.linalg.eigvalsh(A.astype(np.float64))
+    s = to_dev(lam[:, -1] * 1.01)
+    lo = float(max(1e-7, 0.9 * (lam[:, 0] / (lam[:, -1] * 1.01)).min()))
+    X, status = cheb_p(Ad, s, 24, lo, 1.25, S16)
+    ref = oracle.cheb_inverse_root(A, to_host(s), 24, lo, 1.25)
+    err = rel_err(to_host(X), ref)
+    print("lo", lo, "split16 err", err.max())
+    assert np.all(to_host(status) == 0)
+    as_accurate_as_fp32(Ad, s, 24, lo, 1.25, ref, err)
+
+
+def test_cheb_split16_falls_back_to_fp32_bitwise():
+    """Degree 2 runs one product on the fp32 cores; B = 320 has no 256-wide tiling: both equal the
+    fp32 path bit for bit."""
+    A, Ad = spectrum_stack(472, 2, 256)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 2, 0.02, 1.0, S16)
+    X2, _ = cheb_p(Ad, s, 2, 0.02, 1.0, dash.DASH_FP32)
+    assert torch.equal(X1, X2)
+    A, Ad = spectrum_stack(473, 2, 320)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 12, 0.02, 1.0, S16)
+    X2, _ = cheb_p(Ad, s, 12, 0.02, 1.0, dash.DASH_FP32)
+    assert torch.equal(X1, X2)
+
+
+@pytest.mark.parametrize("e", [4, -40, 40])
+def test_cheb_split16_scale_equivariance_and_batch_independence(e):
+    """A power-of-two scale 2^e of A and s moves each block's power of two by -e and leaves every
+    piece as it was, so X(2^e A, 2^e s) = 2^(-e/4) X(A, s) bit for bit; a permuted stack gives the
+    permuted result, and one block alone its result in the stack (each block's bounds are its own)."""
+    A, Ad = spectrum_stack(474, 4, 256)
+    s = frob_scale(Ad)
+    X1, _ = cheb_p(Ad, s, 12, 0.02, 1.0, S16)
+    Xe, _ = cheb_p(Ad * 2.0 ** e, s * 2.0 ** e, 12, 0.02, 1.0, S16)
+    assert torch.equal(Xe * 2.0 ** (e / 4), X1)
+    perm = torch.tensor([2, 0, 3, 1], device=DEV)
+    Xp, _ = cheb_p(Ad[perm].contiguous(), s[perm].contiguous(), 12, 0.02, 1.0, S16)
+    assert torch.equal(Xp, X1[perm])
+    Xi, _ = cheb_p(Ad[2:3].contiguous(), s[2:3].contiguous(), 12, 0.02, 1.0, S16)
+    assert torch.equal(Xi[0], X1[2])
+
+
+def test_cheb_split16_flags_bad_blocks():
+    """A zero or NaN scale flags bit 0 and gives a NaN block; a non-finite input element flags bit
+    1; the other blocks are untouched (their magnitude bounds are their own)."""
+    A, Ad = spectrum_stack(475, 4, 256)
+    s = frob_scale(Ad).clone()
+    X_good, st_good = cheb_p(Ad, s, 8, 0.02, 1.0, S16)
+    assert np.all(to_host(st_good) == 0)
+    s_bad = s.clone()
+    s_bad[1] = 0.0
+    s_bad[2] = float("nan")
+    X, st = cheb_p(Ad, s_bad, 8, 0.02, 1.0, S16)
+    assert np.array_equal(to_host(st).astype(int) & 1, [0, 1, 1, 0])
+    assert np.all(np.isnan(to_host(X)[[1, 2]]))
+    assert torch.equal(X[[0, 3]], X_good[[0, 3]])
+    bad = Ad.clone()
+    bad[0, 3, 5] = float("inf")
+    bad[0, 5, 3] = float("inf")
+    Xb, stb = cheb_p(bad, s, 8, 0.02, 1.0, S16)
+    assert np.array_equal(to_host(stb).astype(int) & 2, [2, 0, 0, 0])
+    assert torch.equal(Xb[1:], X_good[1:])
+
+
+def test_cheb_split16_per_block_interval_matches_oracle():
+    """dash_inverse_root_cheb_blocks with two-piece products: each block on its own interval
+    [floor / s_i, 1.25], against the oracle on the same intervals."""
+    B, N = 256, 3
+    A, Ad = spectrum_stack(476, N, B, lam_min=0.01)
+    A[1] *= 8.0
+    A[2] *= 0.25
+    Ad = to_dev(A)
+    s = host_power_scale(A, di.start_vectors(B, 32))
+    floor = 0.005
+    X = torch.empty_like(Ad)
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    lo_out = torch.empty(N, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_CHEB, N, B, S16, device=DEV)
+    dash.dash_inverse_root_cheb_blocks(Ad, s, N, B, 24, floor, None, 1.0, 1.25, S16, X, lo_out=lo_out,
+                                       status=status, ws=ws)
+    lo = oracle.cheb_interval_lo(to_host(s), floor)
+    assert np.allclose(to_host(lo_out), lo, rtol=1e-6)
+    ref = oracle.cheb_inverse_root(A, to_host(s), 24, lo, 1.25)
+    err = rel_err(to_host(X), ref)
+    print("per-block split16 err", err)
+    assert np.all(to_host(status) == 0)
+    assert err.max() < ITERATE_TOL
