@@ -74,11 +74,18 @@ size_t ws_ndb_half(int64_t N, int B) {
 }
 size_t ws_cn(int64_t N, int B, dash_prec p) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, p); }
 size_t cheb_tab_bytes(int64_t N);
-// per-block magnitude bounds of the two-piece binary16 Clenshaw products: max |A| and three
-// rotating slots for max |b_k|
-size_t amax_bytes(int64_t N) { return align_up((size_t)N * 4 * sizeof(float), 256); }
+// magnitude bounds of the two-piece binary16 Clenshaw products: max |A| per block, and two
+// alternating sets of per-wave maxima of b_k (8 waves for each of the block's upper-triangle
+// 256-wide tiles)
+int64_t amax_parts(int B) {
+  const int64_t t = B / 256;
+  return t * (t + 1) / 2 * 8;
+}
+size_t amax_bytes(int64_t N, int B) {
+  return align_up((size_t)N * sizeof(float), 256) + 2 * align_up((size_t)N * amax_parts(B) * sizeof(float), 256);
+}
 size_t ws_cheb(int64_t N, int B) {
-  return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32) + amax_bytes(N);
+  return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32) + amax_bytes(N, B);
 }
 size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
 size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
@@ -386,7 +393,9 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   float* tab = (float*)cv.take(cheb_tab_bytes(N));
   float* b1 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
   float* b2 = (float*)cv.take(stack_bytes(N, B, DASH_FP32));
-  float* amax = (float*)cv.take(amax_bytes(N));
+  float* amax_a = (float*)cv.take(align_up((size_t)N * sizeof(float), 256));
+  float* amax_slot[2];
+  for (int i = 0; i < 2; ++i) amax_slot[i] = (float*)cv.take(align_up((size_t)N * amax_parts(B) * sizeof(float), 256));
   const int d = degree;
   // split products need 256-wide tiles and an exactly symmetric right operand: every b_{k+1} is
   // stored mirrored; the first product maps A on the fp32 cores unless it can be written as
@@ -394,19 +403,16 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
   const bool split = (prec == DASH_FP32_SPLIT || prec == DASH_FP32_SPLIT16) && B % 256 == 0;
   const bool split_first = split && d >= 3;
   // two-piece binary16 products (from the first product on, degree >= 3): launch q scales its left
-  // operand A + c I by max |A| + |c| and its right one by max |A| (q = 0) or by the maximum that
-  // launch q - 1 gathered into slot (q - 1) % 3; it gathers its own into slot q % 3 and clears slot
-  // (q + 1) % 3, which launch q - 2 filled and launch q - 1 read
+  // operand A + c I by max |A| + |c| and its right one by max |A| (q = 0) or by the largest of the
+  // per-wave maxima that launch q - 1 stored in set (q - 1) % 2; its own go to set q % 2
   const bool h2 = split_first && prec == DASH_FP32_SPLIT16;
   const dash_prec sp_prec = h2 ? DASH_FP32_SPLIT16 : DASH_FP32_SPLIT;
-  float* amax_a = amax;
-  auto slot = [&](int q) { return amax + N * (1 + q % 3); };
   auto bounds = [&](Product& pr, int q, bool last) {
     if (!h2) return;
     pr.amax_x = amax_a;
-    pr.amax_y = q == 0 ? amax_a : slot(q - 1);
-    pr.amax_d = last ? nullptr : slot(q);
-    pr.amax_zero = last ? nullptr : slot(q + 1);
+    pr.amax_y = q == 0 ? amax_a : amax_slot[(q - 1) % 2];
+    pr.amax_y_parts = q == 0 ? 1 : (int)amax_parts(B);
+    pr.amax_d = last ? nullptr : amax_slot[q % 2];
   };
   if (status) TRY(launch_fill_i32(status, N, 0, st));
   TRY(launch_coef(s, N, coef, status, st));
@@ -463,10 +469,7 @@ dash_status cheb_impl(const float* A, const float* s, int64_t N, int32_t B, int3
     const bool sp = split && !pr.map_y;
     return launch_gemm(&pr, 1, N, B, sp ? sp_prec : DASH_FP32, DASH_FP32, Trans::NN, true, e, st, sp);
   };
-  if (h2) {
-    TRY(launch_block_amax(A, N, B, amax_a, st));
-    TRY(launch_fill_f32(slot(0), N, 0.f, st));
-  }
+  if (h2) TRY(launch_block_amax(A, N, B, amax_a, st));
   // the first product: k = d - 2 (or the final one when d == 2); b_{k+2} = b_d = c_d I rides in gamma
   if (split_first) {
     Product pr = prod(A, A, b2, A);

@@ -80,13 +80,14 @@ struct Product {
   int8_t map_ia = CO_NONE, map_ig = CO_NONE;
   const int32_t* freeze = nullptr;
   int8_t pass = 0;
-  // two-piece binary16 products (DASH_FP32_SPLIT16), per block [N]: bounds on |X| and |Y|, the
-  // maximum |D| gathered by atomicMax (must hold 0 when the launch starts; null: not gathered), and
-  // a slot that the launch clears for a later one (null: none)
+  // two-piece binary16 products (DASH_FP32_SPLIT16): per-block bounds on |X| ([N]) and |Y| (the
+  // largest of amax_y_parts values per block, [N][amax_y_parts]), and where each wave of the
+  // launch stores the largest |D| it wrote ([N][tiles][8]: one value per wave of every tile of the
+  // block, every one written; null: not gathered)
   const float* amax_x = nullptr;
   const float* amax_y = nullptr;
+  int amax_y_parts = 1;
   float* amax_d = nullptr;
-  float* amax_zero = nullptr;
 };
 
 enum class Trans { NN, NT, TN };  // NT: Y read transposed, TN: X read transposed

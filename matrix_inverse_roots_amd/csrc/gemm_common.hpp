@@ -187,13 +187,13 @@ __device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, c
 
 // HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
 // that E_PRE takes E's values from ev_pre, loaded by load_e).  HAS_D2: the launch may carry a second
-// output (full products only).  AMAX: the largest stored |D| of the tile goes into P.amax_d[b] by
-// atomicMax on its bits (non-negative floats order as their bit patterns), when P.amax_d is set.
+// output (full products only).  AMAX: the largest |D| that the wave stored goes to *amax_out (a
+// plain store by lane 0; NaN values are passed over), when amax_out is set.
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE, bool CHECKS,
           bool E_PRE = false, bool HAS_D2 = true, bool AMAX = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
-                                         const float (*ev_pre)[MTN][16] = nullptr) {
+                                         const float (*ev_pre)[MTN][16] = nullptr, float* amax_out = nullptr) {
   typedef typename Vec4<TO>::type v4;
   const Epilogue& e = a.epi;
   const int B = a.B;
@@ -281,10 +281,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
     if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
   }
   if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
-  if (AMAX && P.amax_d) {
+  if (AMAX && amax_out) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    if (lane == 0) atomicMax((unsigned*)&P.amax_d[b], __float_as_uint(amax));
+    if (lane == 0) *amax_out = amax;
   }
 }
 

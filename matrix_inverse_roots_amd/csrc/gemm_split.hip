@@ -38,9 +38,8 @@
 // products into one fp32 accumulator (piece products up to 2^28), which the epilogue multiplies by
 // 2^-(ex + ey).  LDS holds two planes per operand.  The bounds: m_X = max|A| + |c| for the left
 // operand A + c I (max|A| from a pass over the stack before the solve), and for the right operand
-// b_{k+1} the maximum that the launch which wrote it gathered in its epilogue (atomicMax of the
-// stored magnitudes per block); each launch also clears the slot that the launch after next
-// gathers into.
+// b_{k+1} the largest of the per-wave maxima that the launch which wrote it stored in its epilogue
+// (one value per wave of every tile of the block, so no atomics and no clearing).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -183,14 +182,18 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   // FOLD (C == Y, Clenshaw's b_{k+1}): alpha X Y + beta Y = alpha (X + (beta/alpha) I) Y, so the
   // C term enters as (beta/alpha) added to X's diagonal before the split, and no C is read
   const float xc = FOLD ? a.epi.c_over_a * coef_of(a.epi, a.epi.ic, tc.b) : 0.f;
-  // H2: the operands' power-of-two exponents for this block, and the launch's clearing of the slot
-  // that the launch after next gathers into
+  // H2: the operands' power-of-two exponents for this block (every wave reduces the right
+  // operand's per-wave maxima itself)
   int ex = 0, ey = 0;
   float m1 = -1.f;
   if constexpr (H2) {
     ex = top_exp(P.amax_x[tc.b] + fabsf(xc));
-    ey = top_exp(P.amax_y[tc.b]);
-    if (P.amax_zero && tc.ti == 0 && tc.tj == 0 && tid == 0) P.amax_zero[tc.b] = 0.f;
+    const float* yb = P.amax_y + tc.b * P.amax_y_parts;
+    float my = 0.f;
+    for (int p = lane; p < P.amax_y_parts; p += 64) my = fmaxf(my, yb[p]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) my = fmaxf(my, __shfl_xor(my, o, 64));
+    ey = __builtin_amdgcn_readfirstlane(top_exp(my));  // (the same in every lane: keep it scalar)
     asm("" : "+s"(m1));  // (no instruction: hides the constant -1 from the optimiser)
   }
   auto sstore = [&](auto slot_c, int buf, int k0) {
@@ -333,7 +336,14 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][nt][r] = ldexpf(acc[mt][nt][r], es);
   }
-  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2>(a, tc, P, acc, wm, wn, lane);
+  // H2: this wave's slot among the block's per-wave maxima (upper-triangle tile index t, 8 waves)
+  float* amax_out = nullptr;
+  if (H2 && P.amax_d) {
+    const int t = tc.ti * a.tdim - tc.ti * (tc.ti - 1) / 2 + (tc.tj - tc.ti);
+    amax_out = P.amax_d + (tc.b * a.tiles + t) * 8 + wave;
+  }
+  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2>(a, tc, P, acc, wm, wn, lane,
+                                                                                       nullptr, amax_out);
 }
 
 }  // namespace

@@ -337,7 +337,7 @@ def test_split16_precision_queries_and_argument_errors():
     assert _status_of(g, P, P2, N, B, 0, 0.1, 1.0, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG  # degree 0
     assert _status_of(g, P, P2, N, 96, 8, 0.1, 1.0, S16, 5 * P, ws=ws) == _lib.DASH_ERR_SHAPE
     assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, S16, 5 * P, ws=FakeWs(P3, 16)) == _lib.DASH_ERR_WORKSPACE
-    # the workspace grew by the magnitude slots (4 N floats): one byte short is refused
+    # the workspace holds the magnitude bounds too: one byte short is refused
     need = dash.dash_workspace_size(dash.DASH_OP_CHEB, N, B, S16)
     assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, S16, 5 * P, ws=FakeWs(P3, need - 1)) == _lib.DASH_ERR_WORKSPACE
     assert _status_of(dash.dash_inverse_root_ndb_prec, P, P2, N, B, 5, 5, S16, 5 * P, ws=ws) == \
