@@ -188,12 +188,21 @@ __device__ __forceinline__ void load_e(const GemmArgs& a, const TileCoord& tc, c
 // HAS_C / HAS_E: the launch may carry C / E operands (each still optional at run time, except
 // that E_PRE takes E's values from ev_pre, loaded by load_e).  HAS_D2: the launch may carry a second
 // output (full products only).  AMAX: the largest |D| that the wave stored goes to *amax_out (a
-// plain store by lane 0; NaN values are passed over), when amax_out is set.
+// plain store by lane 0; NaN values are passed over), when amax_out is set.  MLDS (SYM, fp32
+// output): the mirror goes through the wave's own MLDS_FLOATS floats of LDS at mlds, one 32 x 32
+// accumulator at a time: the lane's four consecutive rows of a column are one 16-byte row piece of
+// the transposed block, stored to LDS (row pitch 36 floats: the 16 lanes that the LDS serves
+// together fall on distinct banks) and read back as 16-byte pieces of whole 128-byte rows, so each
+// store instruction writes 8 full 128-byte rows of the mirror instead of 32-byte pieces of 32 rows.
+// The wave alone reads what it wrote, so no barrier is needed; the caller's LDS must be free.
+constexpr int MLDS_PITCH = 36, MLDS_FLOATS = 32 * MLDS_PITCH;
 template <int MTM, int MTN, int WTM, int WTN, bool SYM, typename TO, bool HAS_C, bool HAS_E, int TILE, bool CHECKS,
-          bool E_PRE = false, bool HAS_D2 = true, bool AMAX = false>
+          bool E_PRE = false, bool HAS_D2 = true, bool AMAX = false, bool MLDS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc, const Product& P,
                                          const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
-                                         const float (*ev_pre)[MTN][16] = nullptr, float* amax_out = nullptr) {
+                                         const float (*ev_pre)[MTN][16] = nullptr, float* amax_out = nullptr,
+                                         float* mlds = nullptr) {
+  static_assert(!MLDS || (SYM && sizeof(TO) == 4), "the LDS mirror is for fp32 triangle-only products");
   typedef typename Vec4<TO>::type v4;
   const Epilogue& e = a.epi;
   const int B = a.B;
@@ -231,7 +240,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           ev[nt][r] = (HAS_E && E) ? E[idx] : 0.f;
       }
 #pragma unroll
-    for (int nt = 0; nt < MTN; ++nt)
+    for (int nt = 0; nt < MTN; ++nt) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int il0 = wm * WTM + mt * 32 + 8 * r4 + 4 * h;  // rows il0 .. il0 + 3 of the tile
@@ -264,7 +273,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
             }
           }
         }
-        if (SYM) {
+        if (SYM && MLDS) {  // transposed block T[jl - (wn WTN + nt 32)][il - (wm WTM + mt 32)]
+          *(v4*)&mlds[li * MLDS_PITCH + 8 * r4 + 4 * h] = pk;
+        } else if (SYM) {
           TO* md = D + (int64_t)(j0 + jl) * B + i0 + il0;  // mirror row j, columns i .. i + 3
           if (!diag_tile || il0 + 3 < jl) {
             *(v4*)md = pk;
@@ -275,6 +286,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
           }
         }
       }
+      if constexpr (SYM && MLDS) {
+        // rows 8 q + lane / 8 of the transposed 32 x 32 block, 16 bytes (columns 4 (lane % 8) ..)
+        // per lane; on a diagonal tile only the mirror's strict lower part (column < row)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 8 * q + (lane >> 3), cc = 4 * (lane & 7);
+          const v4 t = *(const v4*)&mlds[rr * MLDS_PITCH + cc];
+          const int jl = wn * WTN + nt * 32 + rr, il = wm * WTM + mt * 32 + cc;
+          TO* md = D + (int64_t)(j0 + jl) * B + i0 + il;
+          if (!diag_tile || il + 3 < jl) {
+            *(v4*)md = t;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (il + c < jl) md[c] = t[c];
+          }
+        }
+      }
+    }
   }
   if (CHECKS && e.monitor) {
     mon = wave_sum(mon);

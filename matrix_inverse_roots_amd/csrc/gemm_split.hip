@@ -342,8 +342,11 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
     const int t = tc.ti * a.tdim - tc.ti * (tc.ti - 1) / 2 + (tc.tj - tc.ti);
     amax_out = P.amax_d + (tc.b * a.tiles + t) * 8 + wave;
   }
-  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2>(a, tc, P, acc, wm, wn, lane,
-                                                                                       nullptr, amax_out);
+  // symmetric results mirror through LDS (the stage buffers are free after the loop's last barrier)
+  static_assert(!SYM || 8 * MLDS_FLOATS * sizeof(float) <= 2 * BUF * sizeof(TE), "LDS for the mirror");
+  float* mlds = SYM ? (float*)(wave < 4 ? (void*)stage0 : (void*)stage1) + (wave & 3) * MLDS_FLOATS : nullptr;
+  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2, SYM>(
+      a, tc, P, acc, wm, wn, lane, nullptr, amax_out, mlds);
 }
 
 }  // namespace
