@@ -990,8 +990,9 @@ def all_residuals(torch, np, A, X, B, chunk=64):
 
 
 def routed_entry(dash, torch, np, dev, A, s, X, N, B, V0, floor, timed):
-    """The routed solve (dash_inverse_root_routed, Chebyshev d=24 with split products, coupled Newton
-    for the blocks the probe rejects) after the power-iteration scale: time, routes, residuals."""
+    """The routed solve (dash_inverse_root_routed, Chebyshev d=24 with two-piece binary16 products as in
+    the step, coupled Newton for the blocks the probe rejects) after the power-iteration scale: time,
+    routes, residuals."""
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws)
     del ws
@@ -1000,11 +1001,11 @@ def routed_entry(dash, torch, np, dev, A, s, X, N, B, V0, floor, timed):
     status = torch.empty(N, dtype=torch.int32, device=dev)
     ws = dash.workspace(dash.DASH_OP_ROUTED, N, B, device=dev)
     ms = timed(lambda: dash.dash_inverse_root_routed(A, s, N, B, CHEB_DEGREE, floor, CHEB_HI, K_VEC, ROUTED_EST_STEPS,
-                                                     V0, ROUTED_TOL, ROUTED_CN_ITERS, dash.DASH_FP32_SPLIT, X,
+                                                     V0, ROUTED_TOL, ROUTED_CN_ITERS, dash.DASH_FP32_SPLIT16, X,
                                                      route=route, status=status, ws=ws))
     # one more call with the probe's estimate of the final residual (five more passes, not timed)
     dash.dash_inverse_root_routed(A, s, N, B, CHEB_DEGREE, floor, CHEB_HI, K_VEC, ROUTED_EST_STEPS, V0, ROUTED_TOL,
-                                  ROUTED_CN_ITERS, dash.DASH_FP32_SPLIT, X, resid=resid, route=route, status=status,
+                                  ROUTED_CN_ITERS, dash.DASH_FP32_SPLIT16, X, resid=resid, route=route, status=status,
                                   ws=ws)
     del ws
     torch.cuda.empty_cache()

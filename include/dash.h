@@ -64,8 +64,9 @@ typedef enum {
  * matrix cores from two-piece binary16 splits of both operands, each brought near 8 by a power of
  * two per block first (three piece products, fp32 accumulation; the pieces hold 22 of an fp32
  * value's 24 significant bits, and the product's error, measured against fp64, is that of an fp32
- * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec and
- * dash_inverse_root_cheb_blocks), dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
+ * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec,
+ * dash_inverse_root_cheb_blocks and the Chebyshev step of dash_inverse_root_routed),
+ * dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3, DASH_FP32_SPLIT16 = 4 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
@@ -331,7 +332,8 @@ dash_status dash_residual_probe(const float* A, const float* X, int64_t N, int32
  * Blocks the estimate makes well conditioned keep the tight interval's accuracy; ill-conditioned
  * blocks, or blocks whose bottom eigenvalue the estimate overshot, are caught by the probe.
  * floor >= 0 (> 0 when est_steps == 0), hi > 0, 1 <= k <= 32, 0 <= est_steps, tol > 0,
- * 2 <= cn_iters <= 64; prec DASH_FP32 or DASH_FP32_SPLIT (the Chebyshev products).
+ * 2 <= cn_iters <= 64; prec DASH_FP32, DASH_FP32_SPLIT or DASH_FP32_SPLIT16 (the Chebyshev
+ * products).
  * lam_min: NULL or [N] receives the estimates (NaN when est_steps == 0); route: NULL or [N] receives
  * 0 (Chebyshev) or 1 (coupled Newton); resid: NULL or [N] receives the probe's residual estimate of
  * the final X_i (five more passes); status: as for the solvers, from the solver that wrote X_i.

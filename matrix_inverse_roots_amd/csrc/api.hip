@@ -1426,7 +1426,7 @@ dash_status dash_inverse_root_routed(const float* A, const float* s, int64_t N, 
                                      float tol, int32_t cn_iters, dash_prec prec, float* X, float* lam_min,
                                      float* resid, int32_t* route, int32_t* status, void* ws, size_t ws_bytes,
                                      void* stream) {
-  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
   if (!A || !s || !X || !V0 || X == A || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !aligned(V0, 4) ||
       !valid_N(N))
     return DASH_ERR_INVALID_ARG;

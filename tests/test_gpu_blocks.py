@@ -50,7 +50,7 @@ def cheb_blocks(Ad, s, degree, floor, lam=None, theta=1.0, prec=dash.DASH_FP32):
     return X, lo, status
 
 
-@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP32_SPLIT])
+@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP32_SPLIT, dash.DASH_FP32_SPLIT16])
 @pytest.mark.parametrize("degree", [1, 2, 3, 8, 24])
 def test_cheb_blocks_floor_interval_matches_oracle(prec, degree):
     """Each block's interval [floor / s_i, hi] is derived on the device; blocks of different scales
@@ -139,7 +139,7 @@ def test_residual_probe_matches_oracle():
     assert np.all(got[1:] > 0.5 * exact[1:]) and np.all(got[1:] < 2.0 * exact[1:])
 
 
-@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP32_SPLIT])
+@pytest.mark.parametrize("prec", [dash.DASH_FP32, dash.DASH_FP32_SPLIT, dash.DASH_FP32_SPLIT16])
 def test_routed_inverse_root_matches_oracle(prec):
     """Blocks of kappa ~ 4 stay with Chebyshev on their estimated intervals; kappa 1e4 blocks go to
     coupled Newton.  Routes equal the oracle's, roots meet the iterate-parity and residual gates."""
