@@ -58,12 +58,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-solvers", action="store_true")
     p.add_argument("--cpu-blocks", type=int, default=0, help="oracle sample size (default: threads used)")
-    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "ndbsplit", "evd", "adaptive", "ndb16", "bf16", "freq",
+    p.add_argument("--only", choices=["step", "cheb", "cn16", "ndb", "ndbsplit", "ndbsplit16", "evd", "adaptive", "ndb16", "bf16", "freq",
                                       "c2", "libref"],
                    default="step",
                    help="cheb: one Clenshaw solve on the full stack after a 4 GiB reference copy "
-                        "(the run that HBM traffic counters are collected on); cn16 / ndb / ndbsplit: "
-                        "one CN fp16 / NDB fp32 / NDB split-product solve with its scaling (for kernel "
+                        "(the run that HBM traffic counters are collected on); cn16 / ndb / ndbsplit / ndbsplit16: "
+                        "one CN fp16 / NDB fp32 / NDB split-product / NDB two-piece binary16 solve with its "
+                        "scaling (for kernel "
                         "profiles); evd: the "
                         "block-Jacobi eigendecomposition solve in fp32 (with and without the refinement pass) "
                         "and with binary16 operands in its first pass; adaptive: per-block stopping against "
@@ -136,7 +137,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.only == "cheb":
         return only_cheb(dash, di, torch, dev, args)
-    if args.only in ("cn16", "ndb", "ndbsplit"):
+    if args.only in ("cn16", "ndb", "ndbsplit", "ndbsplit16"):
         return only_solver(dash, di, torch, dev, args.only)
     if args.only == "evd":
         return only_evd(dash, di, torch, dev)
@@ -395,7 +396,7 @@ def only_solver(dash, di, torch, dev, which):
         ws = dash.workspace(dash.DASH_OP_CN, N, B, prec, device=dev)
         dash.dash_inverse_root_cn(A, s, N, B, 4, CN_ITERS, prec, X, ws=ws)
     else:
-        nprec = dash.DASH_FP32_SPLIT if which == "ndbsplit" else dash.DASH_FP32
+        nprec = {"ndbsplit": dash.DASH_FP32_SPLIT, "ndbsplit16": dash.DASH_FP32_SPLIT16}.get(which, dash.DASH_FP32)
         ws = dash.workspace(dash.DASH_OP_NDB, N, B, nprec, device=dev)
         dash.dash_inverse_root_ndb_prec(A, s, N, B, NDB_ITERS, NDB_ITERS, nprec, X, ws=ws)
     e[2].record()
@@ -874,6 +875,17 @@ def run_solvers(dash, di, torch, np, dev, N, B, V0, X, args):
                         "blocks_per_s": round(N / (nds_ms * 1e-3), 1), "fp32_product_tflops": round(fl, 2),
                         "bf16_mfma_frac": round(PIECE_PRODUCTS["split"] * fl / FP16_PEAK_TFLOPS, 4),
                         "residual_block0": evd_residual(torch, A, X, 0)}
+    # NDB with two-piece binary16 products
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, dash.DASH_FP32_SPLIT16, device=dev)
+    nd16_ms = timed(lambda: dash.dash_inverse_root_ndb_prec(A, s, N, B, NDB_ITERS, NDB_ITERS, dash.DASH_FP32_SPLIT16,
+                                                            X, ws=ws))
+    del ws
+    torch.cuda.empty_cache()
+    fl = dash.dash_flops(dash.DASH_OP_NDB, N, B, dash.DASH_FP32_SPLIT16, NDB_ITERS, NDB_ITERS) / (nd16_ms * 1e-3) / 1e12
+    res["ndb_split16"] = {"iters": [NDB_ITERS, NDB_ITERS], "ms": round(nd16_ms, 2),
+                          "blocks_per_s": round(N / (nd16_ms * 1e-3), 1), "fp32_product_tflops": round(fl, 2),
+                          "fp16_mfma_frac": round(PIECE_PRODUCTS["split16"] * fl / FP16_PEAK_TFLOPS, 4),
+                          "residual_block0": evd_residual(torch, A, X, 0)}
     # CN fp16 after binary16 power-iteration scaling
     ws = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP16, K_VEC, device=dev)
     scale16_ms = timed(lambda: dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP16, K_VEC,

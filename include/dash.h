@@ -65,8 +65,8 @@ typedef enum {
  * two per block first (three piece products, fp32 accumulation; the pieces hold 22 of an fp32
  * value's 24 significant bits, and the product's error, measured against fp64, is that of an fp32
  * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec,
- * dash_inverse_root_cheb_blocks and the Chebyshev step of dash_inverse_root_routed),
- * dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
+ * dash_inverse_root_cheb_blocks and the Chebyshev step of dash_inverse_root_routed), by
+ * dash_inverse_root_ndb_prec, and by dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3, DASH_FP32_SPLIT16 = 4 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
@@ -166,9 +166,12 @@ dash_status dash_inverse_root_ndb(const float* A, const float* s, int64_t N, int
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* dash_inverse_root_ndb with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix
- * cores; the same as dash_inverse_root_ndb) or DASH_FP32_SPLIT (every product formed from exact
+ * cores; the same as dash_inverse_root_ndb), DASH_FP32_SPLIT (every product formed from exact
  * three-piece bfloat16 splits of its fp32 operands on the bfloat16 matrix cores, 256 x 256 tiles,
- * when B % 256 == 0; with other B the fp32 matrix cores).  Iterates stay fp32 and are never
+ * when B % 256 == 0; with other B the fp32 matrix cores) or DASH_FP32_SPLIT16 (the same tiles with
+ * two-piece binary16 splits on the binary16 matrix cores, each operand scaled by a power of two per
+ * block from a bound on its magnitude: a pass over A, over each elementwise result, and for each
+ * product's result the per-wave maxima its launch stores).  Iterates stay fp32 and are never
  * symmetrised.  Same arguments, workspace and results contract otherwise; DASH_ERR_INVALID_ARG for
  * any other prec. */
 dash_status dash_inverse_root_ndb_prec(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1,

@@ -62,7 +62,15 @@ struct Pool {
 };
 
 size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256); }
-size_t ws_ndb(int64_t N, int B) { return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32); }
+// NDB with two-piece binary16 products: the input's bound per block, and per-wave maxima of every
+// tile (8 per 256-wide tile of the block) for each of the five iterate stacks
+int64_t ndb_parts(int B) { return (int64_t)(B / 256) * (B / 256) * 8; }
+size_t ndb_bound_bytes(int64_t N, int B) {
+  return align_up((size_t)N * sizeof(float), 256) + 5 * align_up((size_t)N * ndb_parts(B) * sizeof(float), 256);
+}
+size_t ws_ndb(int64_t N, int B) {
+  return coef_bytes(N) + flag_bytes(N) + 5 * stack_bytes(N, B, DASH_FP32) + ndb_bound_bytes(N, B);
+}
 // binary16 NDB: six binary16 stacks for the iterates, reused as three fp32 stacks by the correction,
 // and per-block flags and residuals of the guarded correction (at most 16 steps)
 size_t ndb_half_region(int64_t N, int B) {
@@ -139,6 +147,15 @@ struct NdbCtx {
   int32_t* steps = nullptr;
   // products formed from three-piece bfloat16 splits (DASH_FP32_SPLIT) where the shape allows
   bool split = false;
+  // or from two-piece binary16 splits (DASH_FP32_SPLIT16, B % 256 == 0): every stack an operand
+  // comes from has its magnitude bound here (the input's from a pass over it, the products' from
+  // the per-wave maxima their launches store, the elementwise results' from a pass)
+  struct Bound {
+    const void* buf;
+    float* amax;
+    int parts;
+  };
+  std::vector<Bound>* bounds = nullptr;
   // the coefficient that unscales the wanted Z into the output: s^{-1/4} for the composed inverse
   // fourth root, s^{-1/2} for one call's inverse square root
   int8_t final_ia = CO_U;
@@ -149,7 +166,37 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
   // step 0: Z_0 = I so P_0 = M and S_0 = (3I - M)/2; Y_1 = M S_0 = 1.5 M - 0.5 M^2, Z_1 = S_0.
   const bool last = (T == 1);
   // every product is a general one (NDB iterates are never symmetrised)
-  const dash_prec PP = (c.split && !c.freeze && c.B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
+  const bool h2 = c.bounds && !c.freeze && c.B % 256 == 0;
+  const dash_prec PP = h2 ? DASH_FP32_SPLIT16 : (c.split && !c.freeze && c.B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
+  auto bound = [&](const void* buf) -> NdbCtx::Bound* {
+    for (auto& x : *c.bounds)
+      if (x.buf == buf) return &x;
+    return nullptr;
+  };
+  // a product's operand bounds, and (when it writes a stack that has them) its per-wave maxima
+  auto tag = [&](Product& p) -> bool {
+    if (!h2) return true;
+    const NdbCtx::Bound* bx = bound(p.X);
+    const NdbCtx::Bound* by = bound(p.Y);
+    if (!bx || !by || bx->parts < 1 || by->parts < 1) return false;
+    p.amax_x = bx->amax;
+    p.amax_x_parts = bx->parts;
+    p.amax_y = by->amax;
+    p.amax_y_parts = by->parts;
+    if (NdbCtx::Bound* bd = bound(p.D)) {
+      p.amax_d = bd->amax;
+      bd->parts = (int)ndb_parts(c.B);
+    }
+    return true;
+  };
+  // a stack written by an elementwise kernel: its bound from a pass over it
+  auto pass_bound = [&](const void* buf) -> hipError_t {
+    if (!h2) return hipSuccess;
+    NdbCtx::Bound* bd = bound(buf);
+    if (!bd) return hipErrorInvalidValue;
+    bd->parts = 1;
+    return launch_block_amax((const float*)buf, c.N, c.B, bd->amax, c.st);
+  };
   if (c.freeze) TRY(launch_freeze_reset(c.freeze, c.steps, 2, T, c.N, c.st));
   float* Z = nullptr;
   float* Y = nullptr;
@@ -169,6 +216,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
       Z = (float*)c.pool->get();
       s0.D = Z;
       TRY(launch_affine(s0, c.N, c.B, c.st));
+      if (!last) TRY(pass_bound(Z));
     } else if (c.monitor) {  // only the monitor is wanted from S_0: write it to a scratch buffer
       float* tmp = (float*)c.pool->get();
       s0.D = tmp;
@@ -185,6 +233,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     e.ib = scaled ? CO_R1 : CO_NONE;
     e.coef = c.coef;
     Product p = prod(M, M, Y, M);
+    if (!tag(p)) return DASH_ERR_INVALID_ARG;
     TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
   }
   if (m_from_pool) c.pool->put((void*)M);
@@ -218,6 +267,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
       }
       Product p = prod(Z, Y, S);
       p.freeze = c.freeze;  // a stopped block needs no S
+      if (!tag(p)) return DASH_ERR_INVALID_ARG;
       TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
     }
     if (c.freeze)
@@ -232,6 +282,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         Product p = prod(S, Z, final_out);
         p.freeze = c.freeze;
         p.pass = 2;
+        if (!tag(p)) return DASH_ERR_INVALID_ARG;
         TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
@@ -241,6 +292,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
         Product p = prod(Y, S, Yn);
         p.freeze = c.freeze;
         p.pass = 1;
+        if (!tag(p)) return DASH_ERR_INVALID_ARG;
         TRY(launch_gemm(&p, 1, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
         c.pool->put(Y);
         c.pool->put(Z);
@@ -256,6 +308,7 @@ dash_status ndb_call(const NdbCtx& c, const float* M, bool m_from_pool, bool sca
     p[0].freeze = p[1].freeze = c.freeze;
     p[0].pass = 1;
     p[1].pass = 2;
+    if (!tag(p[0]) || !tag(p[1])) return DASH_ERR_INVALID_ARG;
     TRY(launch_gemm(p, 2, c.N, c.B, PP, DASH_FP32, Trans::NN, false, e, c.st));
     c.pool->put(Y);
     c.pool->put(Z);
@@ -809,7 +862,7 @@ struct Stop {
 dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32_t iters1, int32_t iters2, float* X,
                      float* sqrt_out, float* monitor, int32_t* status, void* ws, size_t ws_bytes, void* stream,
                      const Stop& stop, dash_prec prec = DASH_FP32) {
-  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
   if (!A || !s || !X || !aligned(A, 16) || !aligned(X, 16) || !aligned(s, 4) || !valid_N(N))
     return DASH_ERR_INVALID_ARG;
   if (sqrt_out && (!aligned(sqrt_out, 16) || sqrt_out == A || sqrt_out == X)) return DASH_ERR_INVALID_ARG;
@@ -824,12 +877,23 @@ dash_status ndb_impl(const float* A, const float* s, int64_t N, int32_t B, int32
   int32_t* freeze = (int32_t*)cv.take(flag_bytes(N));
   Pool pool;
   for (int q = 0; q < 5; ++q) pool.put(cv.take(stack_bytes(N, B, DASH_FP32)));
+  // two-piece binary16 products: the bound of A (a pass over it) and of each iterate stack
+  std::vector<NdbCtx::Bound> bounds;
+  const bool h2 = prec == DASH_FP32_SPLIT16 && B % 256 == 0 && stop.tol < 0.f;
+  float* amax_a = (float*)cv.take(align_up((size_t)N * sizeof(float), 256));
+  bounds.push_back({A, amax_a, 1});
+  for (int q = 0; q < 5; ++q)
+    bounds.push_back({pool.free_list[q], (float*)cv.take(align_up((size_t)N * ndb_parts(B) * sizeof(float), 256)), 0});
   const int cols = iters1 + iters2;
   if (status) TRY(launch_fill_i32(status, N, 0, st));
   if (monitor) TRY(launch_fill_f32(monitor, N * cols, 0.f, st));
   TRY(launch_coef(s, N, coef, status, st));
   NdbCtx c{N, B, coef, monitor, cols, status, st, &pool};
   c.split = prec == DASH_FP32_SPLIT;
+  if (h2) {
+    c.bounds = &bounds;
+    TRY(launch_block_amax(A, N, B, amax_a, st));
+  }
   if (stop.tol >= 0.f) {
     c.freeze = freeze;
     c.tol = stop.tol;

@@ -80,13 +80,13 @@ struct Product {
   int8_t map_ia = CO_NONE, map_ig = CO_NONE;
   const int32_t* freeze = nullptr;
   int8_t pass = 0;
-  // two-piece binary16 products (DASH_FP32_SPLIT16): per-block bounds on |X| ([N]) and |Y| (the
-  // largest of amax_y_parts values per block, [N][amax_y_parts]), and where each wave of the
-  // launch stores the largest |D| it wrote ([N][tiles][8]: one value per wave of every tile of the
-  // block, every one written; null: not gathered)
+  // two-piece binary16 products (DASH_FP32_SPLIT16): per-block bounds on |X| and |Y|, each the
+  // largest of amax_*_parts values per block ([N][parts]), and where each wave of the launch
+  // stores the largest |D| it wrote ([N][tiles][8]: one value per wave of every tile of the block,
+  // every one written; null: not gathered)
   const float* amax_x = nullptr;
   const float* amax_y = nullptr;
-  int amax_y_parts = 1;
+  int amax_x_parts = 1, amax_y_parts = 1;
   float* amax_d = nullptr;
 };
 

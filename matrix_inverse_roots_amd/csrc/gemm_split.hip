@@ -39,7 +39,9 @@
 // 2^-(ex + ey).  LDS holds two planes per operand.  The bounds: m_X = max|A| + |c| for the left
 // operand A + c I (max|A| from a pass over the stack before the solve), and for the right operand
 // b_{k+1} the largest of the per-wave maxima that the launch which wrote it stored in its epilogue
-// (one value per wave of every tile of the block, so no atomics and no clearing).
+// (one value per wave of every tile of the block, so no atomics and no clearing).  General NN
+// products (NDB's iterates, the right operand gathered by columns) take the same form, each
+// operand's bound the per-wave maxima of the launch that wrote it, or a pass over it.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -187,13 +189,19 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   int ex = 0, ey = 0;
   float m1 = -1.f;
   if constexpr (H2) {
-    ex = top_exp(P.amax_x[tc.b] + fabsf(xc));
+    const float* xb = P.amax_x + tc.b * P.amax_x_parts;
     const float* yb = P.amax_y + tc.b * P.amax_y_parts;
-    float my = 0.f;
+    float mx = 0.f, my = 0.f;
+    for (int p = lane; p < P.amax_x_parts; p += 64) mx = fmaxf(mx, xb[p]);
     for (int p = lane; p < P.amax_y_parts; p += 64) my = fmaxf(my, yb[p]);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) my = fmaxf(my, __shfl_xor(my, o, 64));
-    ey = __builtin_amdgcn_readfirstlane(top_exp(my));  // (the same in every lane: keep it scalar)
+    for (int o = 32; o > 0; o >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      my = fmaxf(my, __shfl_xor(my, o, 64));
+    }
+    // (the same in every lane: keep them scalar)
+    ex = __builtin_amdgcn_readfirstlane(top_exp(mx + fabsf(xc)));
+    ey = __builtin_amdgcn_readfirstlane(top_exp(my));
     asm("" : "+s"(m1));  // (no instruction: hides the constant -1 from the optimiser)
   }
   auto sstore = [&](auto slot_c, int buf, int k0) {
@@ -336,10 +344,11 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][nt][r] = ldexpf(acc[mt][nt][r], es);
   }
-  // H2: this wave's slot among the block's per-wave maxima (upper-triangle tile index t, 8 waves)
+  // H2: this wave's slot among the block's per-wave maxima (tile index t, 8 waves; symmetric
+  // results number the upper-triangle tiles row by row)
   float* amax_out = nullptr;
   if (H2 && P.amax_d) {
-    const int t = tc.ti * a.tdim - tc.ti * (tc.ti - 1) / 2 + (tc.tj - tc.ti);
+    const int t = SYM ? tc.ti * a.tdim - tc.ti * (tc.ti - 1) / 2 + (tc.tj - tc.ti) : tc.ti * a.tdim + tc.tj;
     amax_out = P.amax_d + (tc.b * a.tiles + t) * 8 + wave;
   }
   // symmetric results mirror through LDS (the stage buffers are free after the loop's last barrier)
@@ -356,9 +365,13 @@ hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, bool h2,
   a.tdim = a.B / 256;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool checks = wants_checks(a.epi);
-  // two-piece binary16 form: the Clenshaw launches alone (symmetric NN with C == Y folded)
+  // two-piece binary16 form: the Clenshaw launches (symmetric NN with C == Y folded) and general NN
+  // products (NDB's iterates)
   if (h2) {
-    if (!sym || trans != Trans::NN || !a.epi.fold_c) return hipErrorInvalidValue;
+    if (trans != Trans::NN || sym != a.epi.fold_c) return hipErrorInvalidValue;
+    if (!sym)
+      return checks ? launch(gemm_split_kernel<true, false, false, true, false, true>, a, stream, 512)
+                    : launch(gemm_split_kernel<false, false, false, true, false, true>, a, stream, 512);
     if (y_sym)
       return checks ? launch(gemm_split_kernel<true, true, false, false, true, true>, a, stream, 512)
                     : launch(gemm_split_kernel<false, true, false, false, true, true>, a, stream, 512);

@@ -321,9 +321,9 @@ def test_binding_rejects_host_tensors():
 
 
 def test_split16_precision_queries_and_argument_errors():
-    """DASH_FP32_SPLIT16 (two-piece binary16 products): the Chebyshev solves take it, with the
-    workspace of the fp32 solve and DASH_FP32_SPLIT's flop count; every other solver, the statistics,
-    the apply and the scale reject it."""
+    """DASH_FP32_SPLIT16 (two-piece binary16 products): the Chebyshev solves and NDB take it, the
+    Chebyshev solve with the workspace of the fp32 solve and DASH_FP32_SPLIT's flop count; CN, the
+    statistics, the apply and the scale reject it."""
     for B in (256, 320, 1024):
         assert dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32_SPLIT16) == \
             dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32)
@@ -340,7 +340,10 @@ def test_split16_precision_queries_and_argument_errors():
     # the workspace holds the magnitude bounds too: one byte short is refused
     need = dash.dash_workspace_size(dash.DASH_OP_CHEB, N, B, S16)
     assert _status_of(g, P, P2, N, B, 8, 0.1, 1.0, S16, 5 * P, ws=FakeWs(P3, need - 1)) == _lib.DASH_ERR_WORKSPACE
-    assert _status_of(dash.dash_inverse_root_ndb_prec, P, P2, N, B, 5, 5, S16, 5 * P, ws=ws) == \
+    # NDB takes it too (past the precision check, a short workspace is what stops it)
+    assert _status_of(dash.dash_inverse_root_ndb_prec, P, P2, N, B, 5, 5, S16, 5 * P, ws=FakeWs(P3, 16)) == \
+        _lib.DASH_ERR_WORKSPACE
+    assert _status_of(dash.dash_inverse_root_ndb_prec, P, P2, N, B, 0, 5, S16, 5 * P, ws=ws) == \
         _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 5, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_update_stats_prec, P, N, B, 0.9, S16, P2) == _lib.DASH_ERR_INVALID_ARG

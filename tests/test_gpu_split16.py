@@ -13,7 +13,8 @@ import torch
 import dash_inputs as di
 import matrix_inverse_roots_amd as dash
 import oracle
-from gpu_helpers import DEV, ITERATE_TOL, R_FP32, frob_scale, host_power_scale, rel_err, residual, to_dev, to_host
+from gpu_helpers import (DEV, ITERATE_TOL, R_FP32, frob_scale, host_frob_scale, host_power_scale, rel_err, residual,
+                         to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +163,84 @@ def test_cheb_split16_per_block_interval_matches_oracle():
     print("per-block split16 err", err)
     assert np.all(to_host(status) == 0)
     assert err.max() < ITERATE_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# NDB with two-piece binary16 products (every product a general one, the right operand gathered by
+# columns; each operand's bound from the launch that wrote it, or a pass over it)
+# ------------------------------------------------------------------------------------------------
+
+def ndb_p(A, s, it1, it2, prec, want_sqrt=False, want_monitor=False):
+    N, B = A.shape[0], A.shape[1]
+    X = torch.empty_like(A)
+    R = torch.empty_like(A) if want_sqrt else None
+    mon = torch.empty((N, it1 + it2), device=DEV) if want_monitor else None
+    status = torch.empty(N, dtype=torch.int32, device=DEV)
+    ws = dash.workspace(dash.DASH_OP_NDB, N, B, prec, device=DEV)
+    dash.dash_inverse_root_ndb_prec(A, s, N, B, it1, it2, prec, X, sqrt_out=R, monitor=mon, status=status, ws=ws)
+    return X, R, mon, status
+
+
+@pytest.fixture(scope="module")
+def conditioned():
+    A, _, _ = di.conditioned_stack()  # N = 16, B = 256, kappa = 1e4
+    return A, to_dev(A)
+
+
+@pytest.mark.parametrize("scaling", ["power", "frobenius"])
+def test_ndb_split16_conditioned(conditioned, scaling):
+    """kappa 1e4: the stability case of the non-symmetrised NDB iteration, at the fp32 gates, and as
+    accurate as the fp32 matrix cores."""
+    A, Ad = conditioned
+    s = host_power_scale(A, di.start_vectors(256, 32)) if scaling == "power" else host_frob_scale(A)
+    T = 16 if scaling == "power" else 18
+    X, _, _, status = ndb_p(Ad, s, T, T, S16)
+    X_ref, _, _ = oracle.ndb_inverse_root(A, to_host(s), T, T)
+    err = rel_err(to_host(X), X_ref)
+    Xf, _, _, _ = ndb_p(Ad, s, T, T, dash.DASH_FP32)
+    err_f = rel_err(to_host(Xf), X_ref)
+    print(scaling, "split16 err", err.max(), "fp32 err", err_f.max())
+    assert err.max() < ITERATE_TOL
+    assert residual(to_host(X), A).max() < R_FP32
+    assert np.all(to_host(status) == 0)
+    assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+
+
+@pytest.mark.parametrize("it1,it2", [(1, 1), (2, 3), (4, 4)])
+def test_ndb_split16_iterates_sqrt_and_monitor(it1, it2):
+    """Several 256-wide tiles per block (B = 512, all 16 tiles): X, the square root and the monitor
+    of every step against the oracle's NDB iterates (one step: the first product alone; two or more:
+    the bounds handed from launch to launch)."""
+    A, Ad = spectrum_stack(480, 2, 512)
+    s = host_frob_scale(A)
+    X, R, mon, status = ndb_p(Ad, s, it1, it2, S16, want_sqrt=True, want_monitor=True)
+    X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, to_host(s), it1, it2, want_sqrt=True)
+    assert np.max(rel_err(to_host(X), X_ref)) < ITERATE_TOL
+    assert np.max(rel_err(to_host(R), R_ref)) < ITERATE_TOL
+    assert np.max(np.abs(to_host(mon) - mon_ref) / mon_ref) < 1e-3
+    assert np.all(to_host(status) == 0)
+
+
+def test_ndb_split16_fallback_equivariance_independence_and_flags(conditioned):
+    """B = 320 has no 256-wide tiling: the fp32 path bit for bit.  At B = 256: X(16 A, 16 s) = X / 2
+    bit for bit (every bound moves by the same power of two), one block alone equals its result in
+    the stack, a bad scale flags bit 0 and leaves the other blocks untouched."""
+    A, Ad = spectrum_stack(481, 2, 320)
+    s = frob_scale(Ad)
+    X1, _, _, _ = ndb_p(Ad, s, 5, 5, S16)
+    X2, _, _, _ = ndb_p(Ad, s, 5, 5, dash.DASH_FP32)
+    assert torch.equal(X1, X2)
+    _, Ad = conditioned
+    Ad = Ad[:4].contiguous()
+    s = frob_scale(Ad)
+    X, _, _, _ = ndb_p(Ad, s, 8, 8, S16)
+    X16, _, _, _ = ndb_p(16 * Ad, 16 * s, 8, 8, S16)
+    assert torch.equal(X16 * 2, X)
+    Xi, _, _, _ = ndb_p(Ad[3:4].contiguous(), s[3:4].contiguous(), 8, 8, S16)
+    assert torch.equal(Xi[0], X[3])
+    s_bad = s.clone()
+    s_bad[1] = float("nan")
+    Xb, _, _, st = ndb_p(Ad, s_bad, 8, 8, S16)
+    assert np.array_equal(to_host(st).astype(int) & 1, [0, 1, 0, 0])
+    assert np.all(np.isnan(to_host(Xb)[1]))
+    assert torch.equal(Xb[[0, 2, 3]], X[[0, 2, 3]])
