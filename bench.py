@@ -75,9 +75,9 @@ def parse():
                         "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--prec", choices=["split16", "split", "fp32"], default="split16",
-                   help="arithmetic of the step's fp32 products: split16 (the Chebyshev products from "
-                        "two-piece binary16 splits on the binary16 matrix cores; statistics, scale and "
-                        "apply as split), split (every product from exact three-piece bfloat16 splits on "
+                   help="arithmetic of the step's fp32 products: split16 (the Chebyshev and apply products "
+                        "from two-piece binary16 splits on the binary16 matrix cores; statistics and scale "
+                        "as split), split (every product from exact three-piece bfloat16 splits on "
                         "the bfloat16 matrix cores) or fp32 (the fp32 matrix cores)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="update profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb "
@@ -178,8 +178,8 @@ def main():
     s = torch.empty(N, device=dev)
     lo_dev = torch.empty(N, device=dev)
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    prod_prec = dash.DASH_FP32 if args.prec == "fp32" else dash.DASH_FP32_SPLIT  # statistics, scale, apply
-    cheb_prec = dash.DASH_FP32_SPLIT16 if args.prec == "split16" else prod_prec
+    prod_prec = dash.DASH_FP32 if args.prec == "fp32" else dash.DASH_FP32_SPLIT  # statistics, scale
+    cheb_prec = dash.DASH_FP32_SPLIT16 if args.prec == "split16" else prod_prec  # Chebyshev, apply
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
     torch.cuda.synchronize()
@@ -208,7 +208,7 @@ def main():
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, state["floor"], None, 1.0, CHEB_HI, cheb_prec, X,
                                           lo_out=lo_dev, ws=ws_cheb)
         mark(5)
-        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, prod_prec, U_stack, ws_apply)
+        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, cheb_prec, U_stack, ws_apply)
         mark(6)
         dash.dash_unstack(U_stack, B, updates)
         mark(7)
@@ -316,7 +316,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"split16": "f32 via f16x2 (Chebyshev) and bf16x3 splits", "split": "f32 via bf16x3 split",
+        "dtype": {"split16": "f32 via f16x2 (Chebyshev, apply) and bf16x3 splits", "split": "f32 via bf16x3 split",
                   "fp32": "f32"}[args.prec],
         "data": "synthetic",
         "config": {"workload": "llama-2048 Shampoo step f=1 on fresh gradients: stack, EMA stats, "
@@ -324,10 +324,10 @@ def main():
                    "N": N, "B": B, "tiles": NG,
                    "solver": "chebyshev-clenshaw d=24 fp32, interval [1e-6*0.95^t/s_i, 1.25] per block",
                    "product_arithmetic": {
-                       "split16": "fp32 products, fp32 accumulation; Chebyshev: two-piece binary16 splits of both "
-                                  "operands after a power of two per block (three binary16 MFMA piece products per "
-                                  "fp32 product); statistics, scale, apply: exact three-piece bfloat16 splits (six "
-                                  "bfloat16 MFMA piece products)",
+                       "split16": "fp32 products, fp32 accumulation; Chebyshev and apply: two-piece binary16 "
+                                  "splits of both operands after a power of two per block (three binary16 MFMA "
+                                  "piece products per fp32 product); statistics, scale: exact three-piece bfloat16 "
+                                  "splits (six bfloat16 MFMA piece products)",
                        "split": "fp32 products (statistics, scale, solve, apply) formed from exact three-piece "
                                 "bfloat16 splits of both operands: six bfloat16 MFMA piece products per fp32 "
                                 "product, fp32 accumulation",
@@ -600,8 +600,8 @@ def only_freq(dash, di, torch, dev):
     U_stack = torch.empty((NG, B, B), device=dev)
     X = torch.empty((N, B, B), device=dev)
     s = torch.empty(N, device=dev)
-    prec = dash.DASH_FP32_SPLIT          # statistics and apply
-    cheb_prec = dash.DASH_FP32_SPLIT16   # the Chebyshev products, as in the f = 1 step
+    prec = dash.DASH_FP32_SPLIT          # statistics
+    cheb_prec = dash.DASH_FP32_SPLIT16   # the Chebyshev and apply products, as in the f = 1 step
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
@@ -624,7 +624,7 @@ def only_freq(dash, di, torch, dev):
                         ws_scale)
         dash.dash_inverse_root_cheb_blocks(A[o:o + n], s[o:o + n], n, B, CHEB_DEGREE, state["floor"], None, 1.0,
                                           CHEB_HI, cheb_prec, X[o:o + n], ws=ws_cheb)
-        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, prec, U_stack, ws_apply)
+        dash.dash_apply_prec(X[:NG], X[NG:], G_stack, NG, B, cheb_prec, U_stack, ws_apply)
         dash.dash_unstack(U_stack, B, updates)
 
     out = {"mode": "freq", "N": N, "B": B,

@@ -66,7 +66,8 @@ typedef enum {
  * value's 24 significant bits, and the product's error, measured against fp64, is that of an fp32
  * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec,
  * dash_inverse_root_cheb_blocks and the Chebyshev step of dash_inverse_root_routed), by
- * dash_inverse_root_ndb_prec, and by dash_workspace_size and dash_flops (as DASH_FP32_SPLIT). */
+ * dash_inverse_root_ndb_prec and dash_apply_prec, and by dash_workspace_size and dash_flops (as
+ * DASH_FP32_SPLIT). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3, DASH_FP32_SPLIT16 = 4 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
@@ -392,14 +393,18 @@ dash_status dash_inverse_root_evd_prec(const float* A, int64_t N, int32_t B, int
 
 /* Preconditioned update U_t = (XL_t G_t) XR_t for t < NG ([TG] body: the -1/4 powers of L and R
  * precondition the gradient).  XL, XR, G_stack, U_stack are [NG,B,B]; U_stack must not alias the
- * inputs.  ws holds one [NG,B,B] intermediate. */
+ * inputs.  ws holds one [NG,B,B] intermediate and the magnitude bounds that DASH_FP32_SPLIT16
+ * uses (dash_workspace_size(DASH_OP_APPLY), the same for every prec). */
 dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B, float* U_stack,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* dash_apply with the products' arithmetic chosen by prec: DASH_FP32 (the fp32 matrix cores; the
  * same as dash_apply) or DASH_FP32_SPLIT (both products formed from exact three-piece bfloat16
  * splits of their fp32 operands on the bfloat16 matrix cores when B % 256 == 0; with other B the
- * fp32 matrix cores).  Same workspace; DASH_ERR_INVALID_ARG for any other prec. */
+ * fp32 matrix cores) or DASH_FP32_SPLIT16 (two-piece binary16 splits on the binary16 matrix cores,
+ * each operand brought near 8 by a power of two per block: passes over XL, G and XR for their
+ * bounds, and the first product's epilogue stores the intermediate's; with B % 256 != 0 the fp32
+ * matrix cores).  Same workspace; DASH_ERR_INVALID_ARG for any other prec. */
 dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B,
                             dash_prec prec, float* U_stack, void* ws, size_t ws_bytes, void* stream);
 

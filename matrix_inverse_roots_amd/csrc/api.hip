@@ -65,6 +65,12 @@ size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256)
 // NDB with two-piece binary16 products: the input's bound per block, and per-wave maxima of every
 // tile (8 per 256-wide tile of the block) for each of the five iterate stacks
 int64_t ndb_parts(int B) { return (int64_t)(B / 256) * (B / 256) * 8; }
+// apply: the intermediate stack T = XL G, and for two-piece binary16 products the bounds of XL, G
+// and XR per block and T's per-wave maxima
+size_t ws_apply(int64_t N, int B) {
+  return stack_bytes(N, B, DASH_FP32) + 3 * align_up((size_t)N * sizeof(float), 256) +
+         align_up((size_t)N * ndb_parts(B) * sizeof(float), 256);
+}
 size_t ndb_bound_bytes(int64_t N, int B) {
   return align_up((size_t)N * sizeof(float), 256) + 5 * align_up((size_t)N * ndb_parts(B) * sizeof(float), 256);
 }
@@ -95,7 +101,6 @@ size_t amax_bytes(int64_t N, int B) {
 size_t ws_cheb(int64_t N, int B) {
   return coef_bytes(N) + cheb_tab_bytes(N) + 2 * stack_bytes(N, B, DASH_FP32) + amax_bytes(N, B);
 }
-size_t ws_apply(int64_t N, int B) { return stack_bytes(N, B, DASH_FP32); }
 size_t ws_evd(int64_t N, int B) { return evd_workspace_bytes(N, B); }
 size_t ws_scale(int64_t N, int B, dash_prec p, int k) { return k == 0 ? 0 : power_workspace_bytes(N, B, p); }
 // routed solve: per-block arrays (estimate, probe result, route, freeze, the second solver's status
@@ -1409,7 +1414,7 @@ dash_status dash_apply(const float* XL, const float* XR, const float* G_stack, i
 
 dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_stack, int64_t NG, int32_t B,
                             dash_prec prec, float* U_stack, void* ws, size_t ws_bytes, void* stream) {
-  if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
+  if (!fp32_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
   if (!XL || !XR || !G_stack || !U_stack || !valid_N(NG)) return DASH_ERR_INVALID_ARG;
   if (!aligned(XL, 16) || !aligned(XR, 16) || !aligned(G_stack, 16) || !aligned(U_stack, 16))
     return DASH_ERR_INVALID_ARG;
@@ -1417,11 +1422,29 @@ dash_status dash_apply_prec(const float* XL, const float* XR, const float* G_sta
   if (!valid_B(B)) return DASH_ERR_SHAPE;
   if (!ws || !aligned(ws, 256) || ws_bytes < ws_apply(NG, B)) return DASH_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
-  float* T = (float*)ws;
-  const dash_prec pp = (prec == DASH_FP32_SPLIT && B % 256 == 0) ? DASH_FP32_SPLIT : DASH_FP32;
+  Carver cv{(char*)ws, ws_bytes};
+  float* T = (float*)cv.take(stack_bytes(NG, B, DASH_FP32));
+  const bool h2 = prec == DASH_FP32_SPLIT16 && B % 256 == 0;
+  const dash_prec pp = h2 ? DASH_FP32_SPLIT16
+                          : ((prec == DASH_FP32_SPLIT || prec == DASH_FP32_SPLIT16) && B % 256 == 0) ? DASH_FP32_SPLIT
+                                                                                                       : DASH_FP32;
   Product p1 = prod(XL, G_stack, T);
-  TRY(launch_gemm(&p1, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   Product p2 = prod(T, XR, U_stack);
+  if (h2) {  // two-piece binary16: passes over XL, G and XR; T's bound from the first launch
+    float* b[3];
+    for (int i = 0; i < 3; ++i) b[i] = (float*)cv.take(align_up((size_t)NG * sizeof(float), 256));
+    float* bt = (float*)cv.take(align_up((size_t)NG * ndb_parts(B) * sizeof(float), 256));
+    TRY(launch_block_amax(XL, NG, B, b[0], st));
+    TRY(launch_block_amax(G_stack, NG, B, b[1], st));
+    TRY(launch_block_amax(XR, NG, B, b[2], st));
+    p1.amax_x = b[0];
+    p1.amax_y = b[1];
+    p1.amax_d = bt;
+    p2.amax_x = bt;
+    p2.amax_x_parts = (int)ndb_parts(B);
+    p2.amax_y = b[2];
+  }
+  TRY(launch_gemm(&p1, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   TRY(launch_gemm(&p2, 1, NG, B, pp, DASH_FP32, Trans::NN, false, Epilogue(), st));
   return DASH_OK;
 }

@@ -244,3 +244,86 @@ def test_ndb_split16_fallback_equivariance_independence_and_flags(conditioned):
     assert np.array_equal(to_host(st).astype(int) & 1, [0, 1, 0, 0])
     assert np.all(np.isnan(to_host(Xb)[1]))
     assert torch.equal(Xb[[0, 2, 3]], X[[0, 2, 3]])
+
+
+# ------------------------------------------------------------------------------------------------
+# The preconditioned update U = (XL G) XR with two-piece binary16 products: passes over XL, G and
+# XR for their bounds, and the first product's epilogue stores the per-wave maxima of T = XL G
+# ------------------------------------------------------------------------------------------------
+
+def apply_p(XL, XR, G, prec):
+    NG, B = G.shape[0], G.shape[1]
+    U = torch.empty_like(G)
+    ws = dash.workspace(dash.DASH_OP_APPLY, NG, B, prec, device=DEV)
+    dash.dash_apply_prec(XL, XR, G, NG, B, prec, U, ws)
+    return U
+
+
+def apply_operands(seed, NG, B):
+    """Gaussian XL and XR, and a gradient stack whose blocks differ by up to seven decades."""
+    XL, XR, G = (di.gaussian((NG, B, B), seed + k) for k in range(3))
+    G = (G * np.array([1.0, 3e-4, 2e3, 1e-4])[:NG, None, None]).astype(np.float32)
+    return XL, XR, G
+
+
+@pytest.mark.parametrize("B,NG", [(256, 4), (512, 3), (1024, 2)])
+def test_apply_split16_matches_oracle(B, NG):
+    """Several 256-wide tiles per block (T's bound is read back from every tile's waves): within
+    1e-5 of the oracle's fp64 products and as accurate as the fp32 matrix cores."""
+    XL, XR, G = apply_operands(490 + B, NG, B)
+    U = to_host(apply_p(to_dev(XL), to_dev(XR), to_dev(G), S16))
+    ref = oracle.apply(XL, G, XR)
+    err = rel_err(U, ref)
+    Uf = to_host(apply_p(to_dev(XL), to_dev(XR), to_dev(G), dash.DASH_FP32))
+    err_f = rel_err(Uf, ref)
+    print("B", B, "split16 err", err.max(), "fp32 err", err_f.max())
+    assert err.max() < 1e-5
+    assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+
+
+def test_apply_split16_wide_magnitudes_and_identity():
+    """Rows of G over six decades (D G): the small rows' pieces stay in binary16's normal range after
+    the block's power of two.  Identity preconditioners: XL = I splits exactly, so U differs from G
+    only by the two roundings of G and T to 22 bits (per block, at most 2^-20 of the block's
+    largest element)."""
+    B, NG = 256, 2
+    XL, XR, G = apply_operands(495, NG, B)
+    D = np.exp(di.rng(496).uniform(np.log(1e-6), 0.0, (NG, B)))
+    G = (D[:, :, None] * G).astype(np.float32)
+    U = to_host(apply_p(to_dev(XL), to_dev(XR), to_dev(G), S16))
+    ref = oracle.apply(XL, G, XR)
+    Uf = to_host(apply_p(to_dev(XL), to_dev(XR), to_dev(G), dash.DASH_FP32))
+    err, err_f = rel_err(U, ref), rel_err(Uf, ref)
+    print("wide split16 err", err.max(), "fp32 err", err_f.max())
+    assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+    I = torch.eye(B, device=DEV).expand(NG, B, B).contiguous()
+    U = to_host(apply_p(I, I, to_dev(G), S16)).astype(np.float64)
+    dev = np.abs(U - G).max(axis=(1, 2)) / np.abs(G).max(axis=(1, 2))
+    print("identity deviation", dev)
+    assert np.all(dev <= 2.0 ** -20)
+
+
+@pytest.mark.parametrize("e", [-40, 40])
+def test_apply_split16_equivariance_independence_and_fallback(e):
+    """U(2^e XL, XR, G) = 2^e U bit for bit (XL's bound and T's maxima move by the same power of
+    two); a permuted stack gives the permuted result and one block alone its result in the stack; a
+    zero gradient block gives a zero block and leaves the others as they were; B = 320 has no
+    256-wide tiling: the fp32 path bit for bit."""
+    XL, XR, G = apply_operands(497, 4, 256)
+    XLd, XRd, Gd = to_dev(XL), to_dev(XR), to_dev(G)
+    U = apply_p(XLd, XRd, Gd, S16)
+    assert torch.equal(apply_p(XLd * 2.0 ** e, XRd, Gd, S16), U * 2.0 ** e)
+    assert torch.equal(apply_p(XLd, XRd, Gd * 2.0 ** e, S16), U * 2.0 ** e)
+    perm = torch.tensor([2, 0, 3, 1], device=DEV)
+    Up = apply_p(XLd[perm].contiguous(), XRd[perm].contiguous(), Gd[perm].contiguous(), S16)
+    assert torch.equal(Up, U[perm])
+    Ui = apply_p(XLd[1:2].contiguous(), XRd[1:2].contiguous(), Gd[1:2].contiguous(), S16)
+    assert torch.equal(Ui[0], U[1])
+    Gz = Gd.clone()
+    Gz[2] = 0
+    Uz = apply_p(XLd, XRd, Gz, S16)
+    assert torch.count_nonzero(Uz[2]) == 0
+    assert torch.equal(Uz[[0, 1, 3]], U[[0, 1, 3]])
+    XL, XR, G = apply_operands(498, 2, 320)
+    args = (to_dev(XL), to_dev(XR), to_dev(G))
+    assert torch.equal(apply_p(*args, S16), apply_p(*args, dash.DASH_FP32))
