@@ -318,6 +318,143 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const TileCoord& tc,
   }
 }
 
+// Word 3 of a raw buffer resource on this architecture: 32-bit data format, no swizzle, byte
+// offsets (the accesses here are untyped).
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
+// Epilogue of the split kernels (fp32 output; C optional when HAS_C, E optional; no second
+// output): the arithmetic of `epilogue` (D = al x + be C + de E, plus ga on the diagonal), with
+// every access through a buffer resource over the block, so that the lane's part of a byte offset
+// is a register, the row's part a scalar and the sub-block's column a constant: a load or store
+// takes no address arithmetic, and the tile's parts differ by uniform branches only.  SYM: the
+// upper-triangle tile and its mirror, staged through the wave's MLDS_FLOATS floats of LDS at mlds
+// as in `epilogue`; on a diagonal tile the 32 x 32 sub-blocks below the diagonal store nothing,
+// those on it store their upper part (row <= column) and mirror their strict upper part, and
+// those above store and mirror everything.  AMAX and CHECKS as in `epilogue`.
+template <int MTM, int MTN, int WTM, int WTN, bool SYM, bool HAS_C, int TILE, bool CHECKS, bool AMAX>
+__device__ __forceinline__ void epilogue_split(const GemmArgs& a, const TileCoord& tc, const Product& P,
+                                               const f32x16 (&acc)[MTM][MTN], int wm, int wn, int lane,
+                                               float* amax_out, float* mlds) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const Epilogue& e = a.epi;
+  const int B = a.B;
+  const int64_t b = tc.b;
+  const int64_t off = b * (int64_t)B * B;
+  const float al = e.alpha * coef_of(e, e.ia, b);
+  const float be = e.beta * coef_of(e, e.ib, b);
+  const float de = e.delta * coef_of(e, e.id, b);
+  const float ga = e.gamma * coef_of(e, e.ig, b);
+  auto rsrc = [&](const void* p) {  // (the block's address is the same in every lane: say so)
+    const uint64_t a64 = (uint64_t)((const float*)p + off);
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a64 >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a64);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, B * B * 4, BUFFER_RSRC_WORD3);
+  };
+  const bool has_c = HAS_C && P.C, has_e = P.E;
+  const __amdgpu_buffer_rsrc_t drs = rsrc(P.D);
+  const __amdgpu_buffer_rsrc_t crs = has_c ? rsrc(P.C) : drs;
+  const __amdgpu_buffer_rsrc_t ers = has_e ? rsrc(P.E) : drs;
+  auto ld = [&](__amdgpu_buffer_rsrc_t rs, int v, int s) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, v, s, 0));
+  };
+  auto st = [&](float x, int v, int s) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), drs, v, s, 0);
+  };
+  const int li = lane & 31, h = lane >> 5;
+  const int swm = __builtin_amdgcn_readfirstlane(wm), swn = __builtin_amdgcn_readfirstlane(wn);
+  const int vlane = (4 * h * B + li) * 4;                     // lane part: row 4 h, column li
+  const int vmir = ((lane >> 3) * B + 4 * (lane & 7)) * 4;    // mirror: row lane / 8, column 4 (lane % 8)
+  const bool diag_tile = SYM && tc.ti == tc.tj;
+  float mon = 0.f, amax = 0.f;
+  bool bad = false;
+#pragma unroll
+  for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < MTN; ++nt) {
+      // the sub-block's tile-local origin (ib, jb) and block-level origin (row0, col0)
+      const int ib = swm * WTM + mt * 32, jb = swn * WTN + nt * 32;
+      if (diag_tile && ib > jb) continue;
+      const int row0 = tc.ti * TILE + ib, col0 = tc.tj * TILE + jb;
+      const bool on_diag = row0 == col0;  // holds the block's diagonal elements (row 4h + rr, column li)
+      const bool masked = SYM && on_diag;
+      float cv[16], ev[16], v[16];
+      // element r: row row0 + rr(r) + 4 h, column col0 + li
+      auto srow = [&](int r) { return ((row0 + 8 * (r >> 2) + (r & 3)) * B + col0) * 4; };
+      if (has_c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cv[r] = ld(crs, vlane, srow(r));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cv[r] = 0.f;
+      }
+      if (has_e) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ev[r] = ld(ers, vlane, srow(r));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ev[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 8 * (r >> 2) + (r & 3) + 4 * h;  // row within the sub-block (column li)
+        float x = al * acc[mt][nt][r] + be * cv[r] + de * ev[r];
+        if (on_diag && il == li) x += ga;
+        v[r] = x;
+        const bool keep = !masked || il <= li;
+        if (masked) {
+          if (keep) st(x, vlane, srow(r));
+        } else {
+          st(x, vlane, srow(r));
+        }
+        if (AMAX && keep) amax = fmaxf(amax, fabsf(x));  // (NaN leaves it unchanged)
+        if (CHECKS && keep) {
+          bad |= !isfinite(x);
+          if (e.monitor) {
+            const bool dg = on_diag && il == li;
+            const float dd = x - (dg ? 1.f : 0.f);
+            mon += (SYM && !dg) ? 2.f * dd * dd : dd * dd;
+          }
+        }
+      }
+      if constexpr (SYM) {
+        // the transposed sub-block through LDS: the lane's four consecutive rows of column li are
+        // row li of the transpose, columns 8 r4 + 4 h ..; read back as rows 8 q + lane / 8,
+        // columns 4 (lane % 8) .. 4 (lane % 8) + 3, stored to row col0 + 8 q + lane / 8 of D
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4v pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pk[q] = v[4 * r4 + q];
+          *(f32x4v*)&mlds[li * MLDS_PITCH + 8 * r4 + 4 * h] = pk;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 8 * q + (lane >> 3), cc = 4 * (lane & 7);
+          const f32x4v t = *(const f32x4v*)&mlds[rr * MLDS_PITCH + cc];
+          const int so = ((col0 + 8 * q) * B + row0) * 4;
+          if (!masked) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), drs, vmir, so, 0);
+          } else {  // only the mirror's strict lower part: column cc + c < row rr
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (cc + c < rr) st(t[c], vmir + 4 * c, so);
+          }
+        }
+      }
+    }
+  if (CHECKS && e.monitor) {
+    mon = wave_sum(mon);
+    if (lane == 0) atomicAdd(&e.monitor[b * e.mon_stride], e.mon_mul * mon);
+  }
+  if (CHECKS && e.status && bad) atomicOr(&e.status[b], 2);
+  if (AMAX && amax_out) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (lane == 0) *amax_out = amax;
+  }
+}
+
 // Epilogue for binary16 outputs (no C/E operands, no second output).  Kept elements are stored
 // straight from the accumulators with 2-byte stores (lanes 0-31 cover 64 contiguous bytes of a
 // row).  SYM mirrors through LDS: in the 32x32 accumulator layout a lane's 4 consecutive r are 4

@@ -97,10 +97,6 @@ __device__ __forceinline__ void split2(const f32x4& lo, const f32x4& hi, int e, 
   }
 }
 
-// Word 3 of a raw buffer resource on this architecture: 32-bit data format, no swizzle, byte
-// offsets (the loads here are untyped).
-constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
-
 // LDS rows are 16 bfloat16 (two 16-byte chunks); a row swaps its chunks when bit 2 xor bit 3 of its
 // index is set, so that the 16-byte reads of 16 consecutive rows (one chunk each, the lanes the LDS
 // serves together) fall on 16 distinct 16-byte slots of its 64 banks
@@ -354,8 +350,7 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   // symmetric results mirror through LDS (the stage buffers are free after the loop's last barrier)
   static_assert(!SYM || 8 * MLDS_FLOATS * sizeof(float) <= 2 * BUF * sizeof(TE), "LDS for the mirror");
   float* mlds = SYM ? (float*)(wave < 4 ? (void*)stage0 : (void*)stage1) + (wave & 3) * MLDS_FLOATS : nullptr;
-  epilogue<MTM, MTN, WTM, WTN, SYM, float, !FOLD, true, TILE, CHECKS, false, false, H2, SYM>(
-      a, tc, P, acc, wm, wn, lane, nullptr, amax_out, mlds);
+  epilogue_split<MTM, MTN, WTM, WTN, SYM, !FOLD, TILE, CHECKS, H2>(a, tc, P, acc, wm, wn, lane, amax_out, mlds);
 }
 
 }  // namespace
