@@ -236,13 +236,16 @@ __global__ __launch_bounds__(256) void gemm_f16_big_kernel(GemmArgs a) {
 // of the MFMAs through a ring of registers (two LDS buffers), so each workgroup keeps 128 KiB of
 // loads in flight: the products of the coupled-Newton iteration are latency-bound otherwise (one
 // workgroup per CU, and the first touch of every operand panel misses L2).
-// LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled by row/2 so that the MFMA reads
-// (8 consecutive rows, one chunk) and the stores (2 rows x 4 chunks) are free of bank conflicts.
+// LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled by bits 2-3 of the row.  The LDS
+// serves a 16-byte access 16 lanes at a time from 64 banks (256 bytes): the MFMA reads (16
+// consecutive rows, one chunk) then fall on 16 distinct 16-byte slots, and so do the stores (4
+// rows x 4 chunks).  (Swizzled by row/2, rows r and r + 8 shared a slot: 2-way conflicts on every
+// fragment read.)
 // ------------------------------------------------------------------------------------------------
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-__device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 1)) & 3; }
+__device__ __forceinline__ int swz4(int row, int chunk) { return (chunk ^ (row >> 2)) & 3; }
 
 template <typename TE, bool SYM, typename TO, bool CHECKS, int NW, bool FRZ = false>
 __global__ __launch_bounds__(64 * NW) void gemm_f16_ysym_kernel(GemmArgs a) {
