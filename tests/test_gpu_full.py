@@ -237,7 +237,7 @@ def test_full_step_bench_sequence(stack):
     """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics (split
     products) -> power scale (split products) -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
     (floor_t = 1e-6 * 0.95^t, the damping after t updates; two-piece binary16 products) -> apply
-    (split products).
+    (two-piece binary16 products).
     Sampled L and R blocks of one tile are recomputed by the oracle from the same starting blocks and
     gradient tiles through both steps (its own statistics, scale, interval and solve); every sampled
     block's spectrum (numpy eigvalsh; the oracle's Jacobi needs minutes at B = 1024 and is pinned to
@@ -275,7 +275,7 @@ def test_full_step_bench_sequence(stack):
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, split, 32, 10, V0, s, ws_s)
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, cheb_prec, X, lo_out=lo,
                                           status=status, ws=ws_c)
-        dash.dash_apply_prec(X[:NG], X[NG:], G, NG, B, split, U, ws_a)
+        dash.dash_apply_prec(X[:NG], X[NG:], G, NG, B, cheb_prec, U, ws_a)
         # the oracle's copy of the same step for tile t_idx, from the gradient itself
         G_t = tile_of(grads, t_idx)
         L_ref, R_ref = oracle.update_stats(G_t, 0.95, L_ref, R_ref)
