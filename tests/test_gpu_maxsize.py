@@ -107,3 +107,44 @@ def test_maxsize_split_products(block):
     del ws
     assert int(st[0]) == 0
     assert residual64(Xn, A64) < R_FP32
+
+
+def test_maxsize_split16_products(block):
+    """Two-piece binary16 products at B = 8192, where the magnitude bounds are longest (4224 per-wave
+    maxima per block for the Chebyshev launches, 8192 for NDB's iterates and the apply's
+    intermediate) and the buffer-addressed epilogue's byte offsets reach 256 MiB: the Chebyshev solve
+    and NDB meet the fp32 residual gate and agree with the fp32 matrix cores' results within 1e-5,
+    and so does the apply X_cheb A X_ndb."""
+    A, A64, V0 = block
+    S16 = dash.DASH_FP32_SPLIT16
+    s = power_scale(A, V0, 10)
+    lo = 0.9 * SHIFT / float(s[0])
+    st = torch.empty(1, dtype=torch.int32, device=DEV)
+
+    def rel(P, Q):
+        return float(torch.linalg.matrix_norm(P[0].double() - Q[0].double()) / torch.linalg.matrix_norm(Q[0].double()))
+
+    X, _ = cheb(A, s, 24, lo, 1.25)
+    Xs = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_CHEB, 1, B, S16, device=DEV)
+    dash.dash_inverse_root_cheb_prec(A, s, 1, B, 24, lo, 1.25, S16, Xs, status=st, ws=ws)
+    del ws
+    assert int(st[0]) == 0
+    assert residual64(Xs, A64) < R_FP32
+    assert torch.equal(Xs[0], Xs[0].T)
+    print("cheb split16 vs fp32", rel(Xs, X))
+    assert rel(Xs, X) < 1e-5
+    del X
+    Xn = torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_NDB, 1, B, S16, device=DEV)
+    dash.dash_inverse_root_ndb_prec(A, s, 1, B, 8, 8, S16, Xn, status=st, ws=ws)
+    del ws
+    assert int(st[0]) == 0
+    assert residual64(Xn, A64) < R_FP32
+    U16, U32 = torch.empty_like(A), torch.empty_like(A)
+    ws = dash.workspace(dash.DASH_OP_APPLY, 1, B, S16, device=DEV)
+    dash.dash_apply_prec(Xs, Xn, A, 1, B, S16, U16, ws)
+    dash.dash_apply_prec(Xs, Xn, A, 1, B, dash.DASH_FP32, U32, ws)
+    del ws
+    print("apply split16 vs fp32", rel(U16, U32))
+    assert rel(U16, U32) < 1e-5
