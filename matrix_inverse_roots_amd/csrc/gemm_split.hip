@@ -126,7 +126,23 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
   const float* Y = (const float*)P.Y + off;
   const int i0 = tc.ti * TILE, j0 = tc.tj * TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  int wm = wave >> 2, wn = wave & 3;
+  // H2, symmetric results: a diagonal tile keeps 36 of its 64 32 x 32 sub-blocks.  There the waves
+  // take the 128 x 64 regions so that the two waves of each SIMD (waves w and w + 4) hold at most 11
+  // kept sub-blocks, and the products of the others are skipped (their values are never stored)
+  unsigned need = 0xffu;
+  if (H2 && SYM && tc.ti == tc.tj) {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    wm = (0xD8 >> w) & 1;          // regions (0,2) (0,3) (0,1) (1,3) (1,2) (0,0) (1,0) (1,1)
+    wn = (17118 >> (2 * w)) & 3;
+    need = 0;
+#pragma unroll
+    for (int mt = 0; mt < MTM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < MTN; ++nt)
+        if (wm * WTM + mt * 32 <= wn * WTN + nt * 32) need |= 1u << (mt * MTN + nt);
+    need = __builtin_amdgcn_readfirstlane(need);
+  }
   const int li = lane & 31, h = lane >> 5;
   const int srow = tid >> 1, sch = tid & 1;    // row piece: row srow, k 8 sch .. 8 sch + 7
   const int gcol = tid & 255, gkh = tid >> 8;  // column gather: column gcol, k 8 gkh .. 8 gkh + 7
@@ -261,15 +277,18 @@ __global__ __launch_bounds__(512) void gemm_split_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x0[mt], y0[nt], acc[mt][nt]);
+      for (int nt = 0; nt < MTN; ++nt)
+        if ((need >> (mt * MTN + nt)) & 1) acc[mt][nt] = Half<TE>::mfma(x0[mt], y0[nt], acc[mt][nt]);
 #pragma unroll
     for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x0[mt], y1[nt], acc[mt][nt]);
+      for (int nt = 0; nt < MTN; ++nt)
+        if ((need >> (mt * MTN + nt)) & 1) acc[mt][nt] = Half<TE>::mfma(x0[mt], y1[nt], acc[mt][nt]);
 #pragma unroll
     for (int mt = 0; mt < MTM; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < MTN; ++nt) acc[mt][nt] = Half<TE>::mfma(x1[mt], y0[nt], acc[mt][nt]);
+      for (int nt = 0; nt < MTN; ++nt)
+        if ((need >> (mt * MTN + nt)) & 1) acc[mt][nt] = Half<TE>::mfma(x1[mt], y0[nt], acc[mt][nt]);
   };
   // bfloat16: one right piece at a time (its two fragments), each left piece read per use
   auto compute = [&](int buf) {
