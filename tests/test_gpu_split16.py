@@ -42,11 +42,13 @@ def as_accurate_as_fp32(Ad, s, d, lo, hi, ref, err):
     assert err.max() <= max(1.5 * err_f.max(), 2e-6)
 
 
-@pytest.mark.parametrize("B,N,degrees", [(256, 4, (3, 4, 8, 24)), (512, 2, (24,)), (1024, 1, (24,))])
+@pytest.mark.parametrize("B,N,degrees", [(256, 4, (3, 4, 8, 24)), (512, 2, (24,)), (768, 2, (5, 24)),
+                                         (1024, 1, (24,))])
 def test_cheb_split16_matches_oracle(B, N, degrees):
     """Several 256-wide tiles per block, power-iteration scale, hi = 1.25; degree 3 (two products:
     the first and the last), 4 (three: every magnitude slot used once), 8 and 24 (the slots
-    rotate)."""
+    rotate).  B = 768: an odd number of tiles per side (6 upper-triangle tiles, 3 diagonal ones
+    whose waves take the balanced regions, 48 k-slices)."""
     A, Ad = spectrum_stack(460 + B, N, B)
     s = host_power_scale(A, di.start_vectors(B, 32))
     lo, hi = 0.04, 1.25
@@ -206,12 +208,12 @@ def test_ndb_split16_conditioned(conditioned, scaling):
     assert err.max() <= max(1.5 * err_f.max(), 2e-6)
 
 
-@pytest.mark.parametrize("it1,it2", [(1, 1), (2, 3), (4, 4)])
-def test_ndb_split16_iterates_sqrt_and_monitor(it1, it2):
-    """Several 256-wide tiles per block (B = 512, all 16 tiles): X, the square root and the monitor
-    of every step against the oracle's NDB iterates (one step: the first product alone; two or more:
-    the bounds handed from launch to launch)."""
-    A, Ad = spectrum_stack(480, 2, 512)
+@pytest.mark.parametrize("it1,it2,B", [(1, 1, 512), (2, 3, 512), (4, 4, 512), (3, 3, 768)])
+def test_ndb_split16_iterates_sqrt_and_monitor(it1, it2, B):
+    """Several 256-wide tiles per block (B = 512, all 16 tiles; B = 768, 9): X, the square root and
+    the monitor of every step against the oracle's NDB iterates (one step: the first product alone;
+    two or more: the bounds handed from launch to launch)."""
+    A, Ad = spectrum_stack(480, 2, B)
     s = host_frob_scale(A)
     X, R, mon, status = ndb_p(Ad, s, it1, it2, S16, want_sqrt=True, want_monitor=True)
     X_ref, R_ref, mon_ref = oracle.ndb_inverse_root(A, to_host(s), it1, it2, want_sqrt=True)
@@ -266,7 +268,7 @@ def apply_operands(seed, NG, B):
     return XL, XR, G
 
 
-@pytest.mark.parametrize("B,NG", [(256, 4), (512, 3), (1024, 2)])
+@pytest.mark.parametrize("B,NG", [(256, 4), (512, 3), (768, 2), (1024, 2)])
 def test_apply_split16_matches_oracle(B, NG):
     """Several 256-wide tiles per block (T's bound is read back from every tile's waves): within
     1e-5 of the oracle's fp64 products and as accurate as the fp32 matrix cores."""
