@@ -75,9 +75,9 @@ def parse():
                         "on the kappa 1e4 stack; libref: the vendor library's binary16 "
                         "batched product (torch.bmm) on the same 3072 x 1024 x 1024 shape, for calibration")
     p.add_argument("--prec", choices=["split16", "split", "fp32"], default="split16",
-                   help="arithmetic of the step's fp32 products: split16 (the Chebyshev and apply products "
-                        "from two-piece binary16 splits on the binary16 matrix cores; statistics and scale "
-                        "as split), split (every product from exact three-piece bfloat16 splits on "
+                   help="arithmetic of the step's fp32 products: split16 (the statistics, Chebyshev and apply "
+                        "products from two-piece binary16 splits on the binary16 matrix cores; the scale as "
+                        "split), split (every product from exact three-piece bfloat16 splits on "
                         "the bfloat16 matrix cores) or fp32 (the fp32 matrix cores)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="update profiles/traffic.json from two rocprofv3 counter CSVs of --only cheb "
@@ -178,10 +178,11 @@ def main():
     s = torch.empty(N, device=dev)
     lo_dev = torch.empty(N, device=dev)
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
-    prod_prec = dash.DASH_FP32 if args.prec == "fp32" else dash.DASH_FP32_SPLIT  # statistics, scale
-    cheb_prec = dash.DASH_FP32_SPLIT16 if args.prec == "split16" else prod_prec  # Chebyshev, apply
+    prod_prec = dash.DASH_FP32 if args.prec == "fp32" else dash.DASH_FP32_SPLIT  # scale
+    cheb_prec = dash.DASH_FP32_SPLIT16 if args.prec == "split16" else prod_prec  # statistics, Chebyshev, apply
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
+    ws_stats = dash.workspace(dash.DASH_OP_STATS, NG, B, cheb_prec, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -201,7 +202,7 @@ def main():
         mark(1)
         dash.dash_stack(grads, B, G_stack)
         mark(2)
-        dash.dash_update_stats_prec(G_stack, NG, B, BETA, prod_prec, A)
+        dash.dash_update_stats_ws(G_stack, NG, B, BETA, cheb_prec, A, ws_stats)
         mark(3)
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, prod_prec, K_VEC, MPI_STEPS, V0, s, ws_scale)
         mark(4)
@@ -294,7 +295,7 @@ def main():
     log("step %.1f ms, %.0f blocks/s, product %.2f TFLOP/s (%s)" % (ms_step, value, achieved, args.prec))
     accuracy = step_accuracy(torch, np, A, X, s, lo_dev, V0, state["floor"], N, NG, B)
     log("step accuracy: %s" % json.dumps(accuracy))
-    del ws_cheb, ws_apply, U_stack, G_stack, flat, grads, updates
+    del ws_cheb, ws_apply, ws_stats, U_stack, G_stack, flat, grads, updates
     torch.cuda.empty_cache()
 
     solvers = None
@@ -316,7 +317,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"split16": "f32 via f16x2 (Chebyshev, apply) and bf16x3 splits", "split": "f32 via bf16x3 split",
+        "dtype": {"split16": "f32 via f16x2 (statistics, Chebyshev, apply) and bf16x3 (scale) splits", "split": "f32 via bf16x3 split",
                   "fp32": "f32"}[args.prec],
         "data": "synthetic",
         "config": {"workload": "llama-2048 Shampoo step f=1 on fresh gradients: stack, EMA stats, "
@@ -324,10 +325,10 @@ def main():
                    "N": N, "B": B, "tiles": NG,
                    "solver": "chebyshev-clenshaw d=24 fp32, interval [1e-6*0.95^t/s_i, 1.25] per block",
                    "product_arithmetic": {
-                       "split16": "fp32 products, fp32 accumulation; Chebyshev and apply: two-piece binary16 "
-                                  "splits of both operands after a power of two per block (three binary16 MFMA "
-                                  "piece products per fp32 product); statistics, scale: exact three-piece bfloat16 "
-                                  "splits (six bfloat16 MFMA piece products)",
+                       "split16": "fp32 products, fp32 accumulation; statistics, Chebyshev and apply: two-piece "
+                                  "binary16 splits of both operands after a power of two per block or tile (three "
+                                  "binary16 MFMA piece products per fp32 product); scale: exact three-piece "
+                                  "bfloat16 splits (six bfloat16 MFMA piece products)",
                        "split": "fp32 products (statistics, scale, solve, apply) formed from exact three-piece "
                                 "bfloat16 splits of both operands: six bfloat16 MFMA piece products per fp32 "
                                 "product, fp32 accumulation",
@@ -600,11 +601,11 @@ def only_freq(dash, di, torch, dev):
     U_stack = torch.empty((NG, B, B), device=dev)
     X = torch.empty((N, B, B), device=dev)
     s = torch.empty(N, device=dev)
-    prec = dash.DASH_FP32_SPLIT          # statistics
-    cheb_prec = dash.DASH_FP32_SPLIT16   # the Chebyshev and apply products, as in the f = 1 step
+    cheb_prec = dash.DASH_FP32_SPLIT16   # the statistics, Chebyshev and apply products, as in the f = 1 step
     ws_scale = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, K_VEC, device=dev)
     ws_cheb = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=dev)
     ws_apply = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=dev)
+    ws_stats = dash.workspace(dash.DASH_OP_STATS, NG, B, cheb_prec, device=dev)
     dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s, ws_scale)
     dash.dash_inverse_root_cheb_blocks(A, s, N, B, CHEB_DEGREE, EPS, None, 1.0, CHEB_HI, cheb_prec, X,
                                       ws=ws_cheb)  # roots of step 0
@@ -619,7 +620,7 @@ def only_freq(dash, di, torch, dev):
         flat.normal_(0.0, 1e-3, generator=gen)
         state["floor"] *= BETA
         dash.dash_stack(grads, B, G_stack)
-        dash.dash_update_stats_prec(G_stack, NG, B, BETA, prec, A)
+        dash.dash_update_stats_ws(G_stack, NG, B, BETA, cheb_prec, A, ws_stats)
         dash.dash_scale(A[o:o + n], n, B, dash.DASH_SCALE_POWER, dash.DASH_FP32, K_VEC, MPI_STEPS, V0, s[o:o + n],
                         ws_scale)
         dash.dash_inverse_root_cheb_blocks(A[o:o + n], s[o:o + n], n, B, CHEB_DEGREE, state["floor"], None, 1.0,

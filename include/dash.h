@@ -66,8 +66,8 @@ typedef enum {
  * value's 24 significant bits, and the product's error, measured against fp64, is that of an fp32
  * product); accepted by the Chebyshev solves (dash_inverse_root_cheb_prec,
  * dash_inverse_root_cheb_blocks and the Chebyshev step of dash_inverse_root_routed), by
- * dash_inverse_root_ndb_prec and dash_apply_prec, and by dash_workspace_size and dash_flops (as
- * DASH_FP32_SPLIT). */
+ * dash_inverse_root_ndb_prec, dash_apply_prec and dash_update_stats_ws, and by dash_workspace_size
+ * and dash_flops (as DASH_FP32_SPLIT). */
 typedef enum { DASH_FP32 = 0, DASH_FP16 = 1, DASH_BF16 = 2, DASH_FP32_SPLIT = 3, DASH_FP32_SPLIT16 = 4 } dash_prec;
 
 typedef enum { DASH_SCALE_FROBENIUS = 0, DASH_SCALE_POWER = 1 } dash_scaling;
@@ -123,6 +123,16 @@ dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float
  * other B the fp32 matrix cores).  DASH_ERR_INVALID_ARG for any other prec. */
 dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
                                    void* stream);
+
+/* dash_update_stats_prec with a caller workspace, for DASH_FP32_SPLIT16: both products formed on the
+ * binary16 matrix cores from two-piece binary16 splits of G, brought near 8 by a power of two per
+ * tile (one pass over G_stack for each tile's bound, kept in ws; with B % 256 != 0 the fp32 matrix
+ * cores and ws unused).  ws: dash_workspace_size(DASH_OP_STATS, NG, B, DASH_FP32_SPLIT16) bytes,
+ * 256-byte aligned.  Any other prec: exactly dash_update_stats_prec (ws unused, may be NULL).
+ * Arguments, results and errors otherwise as dash_update_stats_prec; DASH_ERR_WORKSPACE for a
+ * missing or short ws where it is used. */
+dash_status dash_update_stats_ws(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Per-block scale s[N] ([PT] Definição do Problema, item 3, and Metodologia, item 2,
  * "Multi-Power-Iteration"; [TG] body: Rayleigh-quotient estimate of the spectral norm).
@@ -438,7 +448,9 @@ dash_status dash_inverse_sqrt_ndb(const float* A, const float* s, int64_t N, int
 dash_status dash_apply_vec(const float* X, const float* g_pieces, int64_t P, int32_t B, float* u_pieces, void* stream);
 
 /* Workspace bytes for an operation.  k_or_degree: the number of start vectors for
- * DASH_OP_SCALE (power iteration; Frobenius needs 0), ignored otherwise.  bytes [host]. */
+ * DASH_OP_SCALE (power iteration; Frobenius needs 0), ignored otherwise.  DASH_OP_STATS: 0, or
+ * with DASH_FP32_SPLIT16 the bound per tile that dash_update_stats_ws keeps (N = tiles).
+ * bytes [host]. */
 dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec, int32_t k_or_degree,
                                 size_t* bytes);
 

@@ -52,6 +52,7 @@ def library() -> ctypes.CDLL:
             "dash_unstack": (st, [vp, i32, ctypes.POINTER(DashMat), i32, vp]),
             "dash_update_stats": (st, [vp, i64, i32, f32, vp, vp]),
             "dash_update_stats_prec": (st, [vp, i64, i32, f32, st, vp, vp]),
+            "dash_update_stats_ws": (st, [vp, i64, i32, f32, st, vp, vp, sz, vp]),
             "dash_scale": (st, [vp, i64, i32, st, st, i32, i32, vp, ctypes.c_uint64, vp, vp, sz, vp]),
             "dash_start_vectors": (st, [i32, i32, ctypes.c_uint64, vp, vp]),
             "dash_inverse_root_ndb": (st, [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -261,6 +262,14 @@ def dash_update_stats_prec(G_stack, NG: int, B: int, beta: float, prec: int, A, 
     _check("dash_update_stats_prec",
            library().dash_update_stats_prec(a.ptr(G_stack, "G_stack", numel=NG * B * B), NG, B, beta, prec,
                                             a.ptr(A, "A", numel=2 * NG * B * B), a.stream(stream)))
+
+
+def dash_update_stats_ws(G_stack, NG: int, B: int, beta: float, prec: int, A, ws=None, stream=None):
+    a = _Args("dash_update_stats_ws")
+    _check("dash_update_stats_ws",
+           library().dash_update_stats_ws(a.ptr(G_stack, "G_stack", numel=NG * B * B), NG, B, beta, prec,
+                                          a.ptr(A, "A", numel=2 * NG * B * B), a.ws(ws), _nbytes(ws),
+                                          a.stream(stream)))
 
 
 def dash_scale(A, N: int, B: int, how: int, prec: int, k: int, steps: int, V0, s, ws=None, stream=None, seed: int = 0):

@@ -67,6 +67,8 @@ size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256)
 int64_t ndb_parts(int B) { return (int64_t)(B / 256) * (B / 256) * 8; }
 // apply: the intermediate stack T = XL G, and for two-piece binary16 products the bounds of XL, G
 // and XR per block and T's per-wave maxima
+// statistics with two-piece binary16 products: G's bound per tile
+size_t ws_stats16(int64_t N) { return align_up((size_t)N * sizeof(float), 256); }
 size_t ws_apply(int64_t N, int B) {
   return stack_bytes(N, B, DASH_FP32) + 3 * align_up((size_t)N * sizeof(float), 256) +
          align_up((size_t)N * ndb_parts(B) * sizeof(float), 256);
@@ -734,6 +736,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
   if (!bytes || !valid_N(N)) return DASH_ERR_INVALID_ARG;
   if (!valid_B(B)) return DASH_ERR_SHAPE;
   if (!fp32_prec(prec) && !half_prec(prec) && prec != DASH_FP32_SPLIT16) return DASH_ERR_INVALID_ARG;
+  const bool split16 = prec == DASH_FP32_SPLIT16;
   if (prec == DASH_FP32_SPLIT || prec == DASH_FP32_SPLIT16) prec = DASH_FP32;
   switch (op) {
     case DASH_OP_SCALE:
@@ -746,7 +749,7 @@ dash_status dash_workspace_size(dash_op op, int64_t N, int32_t B, dash_prec prec
     case DASH_OP_CHEB: *bytes = ws_cheb(N, B); return DASH_OK;
     case DASH_OP_ROUTED: *bytes = ws_routed(N, B); return DASH_OK;
     case DASH_OP_APPLY: *bytes = ws_apply(N, B); return DASH_OK;
-    case DASH_OP_STATS: *bytes = 0; return DASH_OK;
+    case DASH_OP_STATS: *bytes = split16 ? ws_stats16(N) : 0; return DASH_OK;
     case DASH_OP_EVD: *bytes = ws_evd(N, B); return DASH_OK;
   }
   return DASH_ERR_INVALID_ARG;
@@ -791,6 +794,33 @@ dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, 
   TRY(launch_gemm(&pl, 1, NG, B, pp, DASH_FP32, Trans::NT, true, e, as_stream(stream)));
   Product pr = prod(G_stack, G_stack, R, R);  // G^T G : X read transposed
   TRY(launch_gemm(&pr, 1, NG, B, pp, DASH_FP32, Trans::TN, true, e, as_stream(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_update_stats_ws(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (prec != DASH_FP32_SPLIT16) return dash_update_stats_prec(G_stack, NG, B, beta, prec, A, stream);
+  if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
+  if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
+  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  if (B % 256 != 0) return dash_update_stats_prec(G_stack, NG, B, beta, DASH_FP32, A, stream);
+  if (!ws || !aligned(ws, 256) || ws_bytes < ws_stats16(NG)) return DASH_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  // both products read G on both sides: one bound per tile serves all four operands
+  float* bound = (float*)ws;
+  TRY(launch_block_amax(G_stack, NG, B, bound, st));
+  float* L = A;
+  float* R = A + NG * (int64_t)B * B;
+  Epilogue e;
+  e.alpha = 1.f - beta;
+  e.beta = beta;
+  Product pl = prod(G_stack, G_stack, L, L);  // G G^T : Y's rows as B's columns
+  pl.amax_x = pl.amax_y = bound;
+  TRY(launch_gemm(&pl, 1, NG, B, DASH_FP32_SPLIT16, DASH_FP32, Trans::NT, true, e, st));
+  Product pr = prod(G_stack, G_stack, R, R);  // G^T G : both operands' columns gathered
+  pr.amax_x = pr.amax_y = bound;
+  TRY(launch_gemm(&pr, 1, NG, B, DASH_FP32_SPLIT16, DASH_FP32, Trans::TN, true, e, st));
   return DASH_OK;
 }
 

@@ -65,8 +65,9 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
   // stopped blocks or second output.  C is read from memory with its (beta, ib) weight, or, with
   // fold_c (symmetric NN only, C == Y in every problem), enters as (c_over_a coef[ic]) added to
   // X's diagonal: alpha coef[ia] (X + c I) Y
-  // two-piece binary16 (DASH_FP32_SPLIT16): the Clenshaw launches (symmetric NN, C == Y folded)
-  // and general NN products, with the magnitude bounds of both operands in every problem
+  // two-piece binary16 (DASH_FP32_SPLIT16): the Clenshaw launches (symmetric NN, C == Y folded),
+  // general NN products, and symmetric NT / TN products (the statistics), with the magnitude bounds
+  // of both operands in every problem
   if (split) {
     const bool h2 = in_prec == DASH_FP32_SPLIT16;
     const bool shape_ok = sym ? (trans != Trans::NN || y_sym || epi.fold_c) : trans == Trans::NN;
@@ -75,8 +76,9 @@ hipError_t launch_gemm(const Product* probs, int nprob, int64_t N, int B, dash_p
       if (epi.fold_c && probs[i].C != probs[i].Y) fold_ok_split = false;
       if (h2 && (!probs[i].amax_x || !probs[i].amax_y)) fold_ok_split = false;
     }
+    const bool h2_ok = (trans == Trans::NN && sym == epi.fold_c) || (trans != Trans::NN && sym && !epi.fold_c);
     if (out_prec != DASH_FP32 || !shape_ok || maps || frz || !fold_ok_split || probs[0].D2 ||
-        (nprob > 1 && probs[1].D2) || B % 256 != 0 || (h2 && (trans != Trans::NN || sym != epi.fold_c)))
+        (nprob > 1 && probs[1].D2) || B % 256 != 0 || (h2 && !h2_ok))
       return hipErrorInvalidValue;
     return gemm::launch_split(a, sym, trans, y_sym, h2, stream);
   }

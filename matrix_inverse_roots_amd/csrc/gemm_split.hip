@@ -379,10 +379,18 @@ hipError_t launch_split(GemmArgs& a, bool sym, Trans trans, bool y_sym, bool h2,
   a.tdim = a.B / 256;
   a.tiles = sym ? a.tdim * (a.tdim + 1) / 2 : a.tdim * a.tdim;
   const bool checks = wants_checks(a.epi);
-  // two-piece binary16 form: the Clenshaw launches (symmetric NN with C == Y folded) and general NN
-  // products (NDB's iterates)
+  // two-piece binary16 form: the Clenshaw launches (symmetric NN with C == Y folded), general NN
+  // products (NDB's iterates, the apply) and the statistics' symmetric G G^T (NT) and G^T G (TN)
   if (h2) {
-    if (trans != Trans::NN || sym != a.epi.fold_c) return hipErrorInvalidValue;
+    if (trans != Trans::NN) {
+      if (!sym || a.epi.fold_c) return hipErrorInvalidValue;
+      if (trans == Trans::NT)
+        return checks ? launch(gemm_split_kernel<true, true, false, false, false, true>, a, stream, 512)
+                      : launch(gemm_split_kernel<false, true, false, false, false, true>, a, stream, 512);
+      return checks ? launch(gemm_split_kernel<true, true, true, true, false, true>, a, stream, 512)
+                    : launch(gemm_split_kernel<false, true, true, true, false, true>, a, stream, 512);
+    }
+    if (sym != a.epi.fold_c) return hipErrorInvalidValue;
     if (!sym)
       return checks ? launch(gemm_split_kernel<true, false, false, true, false, true>, a, stream, 512)
                     : launch(gemm_split_kernel<false, false, false, true, false, true>, a, stream, 512);

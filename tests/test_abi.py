@@ -323,7 +323,8 @@ def test_binding_rejects_host_tensors():
 def test_split16_precision_queries_and_argument_errors():
     """DASH_FP32_SPLIT16 (two-piece binary16 products): the Chebyshev solves and NDB take it, the
     Chebyshev solve with the workspace of the fp32 solve and DASH_FP32_SPLIT's flop count; the apply
-    takes it with the workspace every prec uses; CN, the statistics and the scale reject it."""
+    takes it with the workspace every prec uses; the statistics take it through dash_update_stats_ws
+    (a bound per tile in the workspace); CN, dash_update_stats_prec and the scale reject it."""
     for B in (256, 320, 1024):
         assert dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32_SPLIT16) == \
             dash.dash_workspace_size(dash.DASH_OP_CHEB, 8, B, dash.DASH_FP32)
@@ -347,6 +348,15 @@ def test_split16_precision_queries_and_argument_errors():
         _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_inverse_root_cn, P, P2, N, B, 4, 5, S16, 5 * P, ws=ws) == _lib.DASH_ERR_INVALID_ARG
     assert _status_of(dash.dash_update_stats_prec, P, N, B, 0.9, S16, P2) == _lib.DASH_ERR_INVALID_ARG
+    need = dash.dash_workspace_size(dash.DASH_OP_STATS, N, B, S16)
+    assert need >= 4 * N and need % 256 == 0
+    assert dash.dash_workspace_size(dash.DASH_OP_STATS, N, B, dash.DASH_FP32) == 0
+    w = dash.dash_update_stats_ws
+    assert _status_of(w, P, N, B, 0.9, S16, P2, ws=FakeWs(P3, need - 1)) == _lib.DASH_ERR_WORKSPACE
+    assert _status_of(w, P, N, B, 1.5, S16, P2, ws=FakeWs(P3, need)) == _lib.DASH_ERR_INVALID_ARG  # beta
+    assert _status_of(w, P, N, 96, 0.9, S16, P2, ws=FakeWs(P3, need)) == _lib.DASH_ERR_SHAPE
+    for prec in (dash.DASH_FP16, dash.DASH_BF16, 7):   # other precs: dash_update_stats_prec's answers
+        assert _status_of(w, P, N, B, 0.9, prec, P2) == _lib.DASH_ERR_INVALID_ARG
     need = dash.dash_workspace_size(dash.DASH_OP_APPLY, N, B, S16)
     assert need == dash.dash_workspace_size(dash.DASH_OP_APPLY, N, B, dash.DASH_FP32)
     assert need > N * B * B * 4  # the intermediate and the bounds

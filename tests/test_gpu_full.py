@@ -234,10 +234,10 @@ def test_full_step_chebyshev(stack):
 
 
 def test_full_step_bench_sequence(stack):
-    """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics (split
-    products) -> power scale (split products) -> Chebyshev d=24 on every block's own interval [floor_t / s_i, 1.25]
-    (floor_t = 1e-6 * 0.95^t, the damping after t updates; two-piece binary16 products) -> apply
-    (two-piece binary16 products).
+    """The step bench.py times, over two EMA steps with fresh gradients: stack -> statistics
+    (two-piece binary16 products) -> power scale (split products) -> Chebyshev d=24 on every block's
+    own interval [floor_t / s_i, 1.25] (floor_t = 1e-6 * 0.95^t, the damping after t updates;
+    two-piece binary16 products) -> apply (two-piece binary16 products).
     Sampled L and R blocks of one tile are recomputed by the oracle from the same starting blocks and
     gradient tiles through both steps (its own statistics, scale, interval and solve); every sampled
     block's spectrum (numpy eigvalsh; the oracle's Jacobi needs minutes at B = 1024 and is pinned to
@@ -266,12 +266,13 @@ def test_full_step_bench_sequence(stack):
     ws_s = dash.workspace(dash.DASH_OP_SCALE, N, B, dash.DASH_FP32, 32, device=DEV)
     ws_c = dash.workspace(dash.DASH_OP_CHEB, N, B, cheb_prec, device=DEV)
     ws_a = dash.workspace(dash.DASH_OP_APPLY, NG, B, device=DEV)
+    ws_st = dash.workspace(dash.DASH_OP_STATS, NG, B, cheb_prec, device=DEV)
     floor = 1e-6
     for step in range(2):
         flat.normal_(0.0, 1e-3, generator=gen)
         floor *= 0.95
         dash.dash_stack(grads, B, G)
-        dash.dash_update_stats_prec(G, NG, B, 0.95, split, A)
+        dash.dash_update_stats_ws(G, NG, B, 0.95, cheb_prec, A, ws_st)
         dash.dash_scale(A, N, B, dash.DASH_SCALE_POWER, split, 32, 10, V0, s, ws_s)
         dash.dash_inverse_root_cheb_blocks(A, s, N, B, 24, floor, None, 1.0, 1.25, cheb_prec, X, lo_out=lo,
                                           status=status, ws=ws_c)
@@ -293,7 +294,7 @@ def test_full_step_bench_sequence(stack):
     assert np.max(rel_err(host(X[idx]), X_ref)) < ITERATE_TOL
     U_ref = oracle.apply(X_ref[0], G_t, X_ref[1])
     assert np.max(rel_err(host(U[t_idx]), U_ref)) < ITERATE_TOL
-    del A, X, U, G, flat, grads, ws_s, ws_c, ws_a
+    del A, X, U, G, flat, grads, ws_s, ws_c, ws_a, ws_st
     torch.cuda.empty_cache()
 
 

@@ -329,3 +329,71 @@ def test_apply_split16_equivariance_independence_and_fallback(e):
     XL, XR, G = apply_operands(498, 2, 320)
     args = (to_dev(XL), to_dev(XR), to_dev(G))
     assert torch.equal(apply_p(*args, S16), apply_p(*args, dash.DASH_FP32))
+
+
+# ------------------------------------------------------------------------------------------------
+# Statistics L <- beta L + (1 - beta) G G^T, R <- beta R + (1 - beta) G^T G with two-piece binary16
+# products (dash_update_stats_ws: G's bound per tile in the workspace)
+# ------------------------------------------------------------------------------------------------
+
+def stats_p(G, A, beta, prec):
+    NG, B = G.shape[0], G.shape[1]
+    ws = dash.workspace(dash.DASH_OP_STATS, NG, B, prec, device=DEV)
+    dash.dash_update_stats_ws(G, NG, B, beta, prec, A, ws)
+
+
+def stats_operands(seed, NG, B):
+    """Gradient tiles N(0, 1e-3^2) scaled per tile over four decades, on prior statistics of the
+    bench's size (G G^T / 128 + 1e-4 I, times 1e-6)."""
+    G = (di.gaussian((NG, B, B), seed, 1e-3) * np.array([1.0, 1e-2, 30.0, 1e-1])[:NG, None, None]).astype(np.float32)
+    L0 = (di.tiny_stack(seed=seed + 1, N=NG, B=B) * 1e-6).astype(np.float32)
+    R0 = (di.tiny_stack(seed=seed + 2, N=NG, B=B) * 1e-6).astype(np.float32)
+    return G, L0, R0
+
+
+@pytest.mark.parametrize("B,NG", [(256, 3), (512, 2), (768, 2), (1024, 2)])
+def test_stats_split16_matches_oracle(B, NG):
+    """G G^T (Y's rows read as columns) and G^T G (both operands' columns gathered), triangle-only
+    with the mirror: within 1e-5 of the oracle's fp64 update, as accurate as the fp32 matrix cores,
+    every block exactly symmetric."""
+    G, L0, R0 = stats_operands(520 + B, NG, B)
+    A = to_dev(np.concatenate([L0, R0]))
+    stats_p(to_dev(G), A, 0.95, S16)
+    out = to_host(A)
+    L_ref, R_ref = oracle.update_stats(G, 0.95, L0, R0)
+    ref = np.concatenate([L_ref, R_ref])
+    Af = to_dev(np.concatenate([L0, R0]))
+    dash.dash_update_stats_prec(to_dev(G), NG, B, 0.95, dash.DASH_FP32, Af)
+    err, err_f = rel_err(out, ref), rel_err(to_host(Af), ref)
+    print("B", B, "split16 err", err.max(), "fp32 err", err_f.max())
+    assert err.max() < 1e-5
+    assert err.max() <= max(1.5 * err_f.max(), 2e-6)
+    assert np.array_equal(out, np.swapaxes(out, 1, 2))
+
+
+@pytest.mark.parametrize("e", [-8, 8])
+def test_stats_split16_equivariance_zero_tile_and_fallback(e):
+    """beta = 0: L(2^e G) = 2^(2e) L(G) bit for bit (each tile's power of two moves by e and every
+    piece stays as it was); a zero gradient tile leaves beta L exactly and the other tiles as they
+    were; B = 320 has no 256-wide tiling: the fp32 path bit for bit."""
+    NG, B = 3, 512
+    G, L0, R0 = stats_operands(530, NG, B)
+    Gd = to_dev(G)
+    A0 = to_dev(np.concatenate([L0, R0]))
+    A1, A2 = A0.clone(), A0.clone()
+    stats_p(Gd, A1, 0.0, S16)
+    stats_p(Gd * 2.0 ** e, A2, 0.0, S16)
+    assert torch.equal(A2, A1 * 2.0 ** (2 * e))
+    A3, A4 = A0.clone(), A0.clone()
+    stats_p(Gd, A3, 0.95, S16)
+    Gz = Gd.clone()
+    Gz[1] = 0
+    stats_p(Gz, A4, 0.95, S16)
+    keep = [0, 2, NG, NG + 2]
+    assert torch.equal(A4[keep], A3[keep])
+    assert torch.equal(A4[[1, NG + 1]], A0[[1, NG + 1]] * 0.95)
+    G, L0, R0 = stats_operands(531, 2, 320)
+    A5, A6 = to_dev(np.concatenate([L0, R0])), to_dev(np.concatenate([L0, R0]))
+    stats_p(to_dev(G), A5, 0.95, S16)
+    dash.dash_update_stats(to_dev(G), 2, 320, 0.95, A6)
+    assert torch.equal(A5, A6)
