@@ -65,10 +65,18 @@ size_t flag_bytes(int64_t N) { return align_up((size_t)N * sizeof(int32_t), 256)
 // NDB with two-piece binary16 products: the input's bound per block, and per-wave maxima of every
 // tile (8 per 256-wide tile of the block) for each of the five iterate stacks
 int64_t ndb_parts(int B) { return (int64_t)(B / 256) * (B / 256) * 8; }
-// apply: the intermediate stack T = XL G, and for two-piece binary16 products the bounds of XL, G
-// and XR per block and T's per-wave maxima
 // statistics with two-piece binary16 products: G's bound per tile
 size_t ws_stats16(int64_t N) { return align_up((size_t)N * sizeof(float), 256); }
+// the statistics' arguments short of prec and workspace
+dash_status stats_args_check(const float* G_stack, int64_t NG, int32_t B, float beta, const float* A) {
+  if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
+  if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
+  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
+  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  return DASH_OK;
+}
+// apply: the intermediate stack T = XL G, and for two-piece binary16 products the bounds of XL, G
+// and XR per block and T's per-wave maxima
 size_t ws_apply(int64_t N, int B) {
   return stack_bytes(N, B, DASH_FP32) + 3 * align_up((size_t)N * sizeof(float), 256) +
          align_up((size_t)N * ndb_parts(B) * sizeof(float), 256);
@@ -780,10 +788,8 @@ dash_status dash_update_stats(const float* G_stack, int64_t NG, int32_t B, float
 dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
                                    void* stream) {
   if (!fp32_prec(prec)) return DASH_ERR_INVALID_ARG;
-  if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
-  if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
-  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
-  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  const dash_status chk = stats_args_check(G_stack, NG, B, beta, A);
+  if (chk != DASH_OK) return chk;
   float* L = A;
   float* R = A + NG * (int64_t)B * B;
   Epilogue e;
@@ -800,10 +806,8 @@ dash_status dash_update_stats_prec(const float* G_stack, int64_t NG, int32_t B, 
 dash_status dash_update_stats_ws(const float* G_stack, int64_t NG, int32_t B, float beta, dash_prec prec, float* A,
                                  void* ws, size_t ws_bytes, void* stream) {
   if (prec != DASH_FP32_SPLIT16) return dash_update_stats_prec(G_stack, NG, B, beta, prec, A, stream);
-  if (!G_stack || !A || !aligned(G_stack, 16) || !aligned(A, 16)) return DASH_ERR_INVALID_ARG;
-  if (!valid_N(NG) || !valid_N(2 * NG)) return DASH_ERR_INVALID_ARG;
-  if (!(beta >= 0.f && beta <= 1.f)) return DASH_ERR_INVALID_ARG;
-  if (!valid_B(B)) return DASH_ERR_SHAPE;
+  const dash_status chk = stats_args_check(G_stack, NG, B, beta, A);
+  if (chk != DASH_OK) return chk;
   if (B % 256 != 0) return dash_update_stats_prec(G_stack, NG, B, beta, DASH_FP32, A, stream);
   if (!ws || !aligned(ws, 256) || ws_bytes < ws_stats16(NG)) return DASH_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
