@@ -148,3 +148,21 @@ def test_maxsize_split16_products(block):
     del ws
     print("apply split16 vs fp32", rel(U16, U32))
     assert rel(U16, U32) < 1e-5
+
+
+def test_maxsize_split16_statistics(block):
+    """dash_update_stats_ws with two-piece binary16 products at B = 8192 (G G^T reading G's rows,
+    G^T G gathering its columns at the largest byte offsets): L and R agree with the fp32 matrix
+    cores' update within 1e-5 and are exactly symmetric."""
+    A, _, _ = block
+    G = di.gaussian_torch((1, B, B), seed=43, device=DEV, std=1e-3)
+    S0 = torch.cat([A, A]) * 1e-3
+    S16, S32 = S0.clone(), S0.clone()
+    ws = dash.workspace(dash.DASH_OP_STATS, 1, B, dash.DASH_FP32_SPLIT16, device=DEV)
+    dash.dash_update_stats_ws(G, 1, B, 0.95, dash.DASH_FP32_SPLIT16, S16, ws)
+    dash.dash_update_stats_prec(G, 1, B, 0.95, dash.DASH_FP32, S32)
+    for i in range(2):
+        d = float(torch.linalg.matrix_norm(S16[i].double() - S32[i].double()) / torch.linalg.matrix_norm(S32[i].double()))
+        print("stats block", i, "split16 vs fp32", d)
+        assert d < 1e-5
+        assert torch.equal(S16[i], S16[i].T)
